@@ -1,0 +1,491 @@
+"""Plain float64 CPU oracle of the MXFP8 block-scaled grouped MLP.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg, never by the product.
+
+Every step follows a definition, written out directly:
+
+* MXFP8 block quantization -- one E8M0 power-of-two scale per block of 32
+  consecutive values, 8-bit E4M3 elements ("Efficient MoE training for
+  biological foundation models", Key technical approaches item 2; the Llama 3
+  recipe page, "MXFP8 vs BF16 throughput": MXFP8BlockScaling, E4M3).
+* GroupedLinear over per-expert split_sizes (same article, item 1): each
+  expert's rows are multiplied by that expert's weight; the grouped result is
+  the loop of per-expert products.
+* GroupedLinear -> ScaledSwiGLU -> GroupedLinear with routing-weight scaling,
+  16-bit master weights quantized each step, and the corresponding backward
+  (same article, item 3).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+R1  scale exponent e = floor(log2(amax)) - 8 (8 = exponent of E4M3's largest
+    normal), floor taken exactly from the binary exponent; e clamped to
+    [-127, 127]; E8M0 code = e + 127.
+R2  all-zero block -> e = -127 (scale code 0x00), codes 0x00 (0x80 for -0.0).
+R3  element code = E4M3 round-to-nearest, ties to the even code, of v / 2^e;
+    magnitudes >= 448 saturate to 448 (0x7E), never NaN; E4M3 subnormals kept;
+    the sign bit always follows the input's sign (so -tiny -> 0x80).
+R4  non-finite inputs are outside the contract: the oracle raises.
+R5  rowwise layout: codes [rows, cols] row-major, scales [rows, cols/32];
+    blocks start at column 0; cols must be a multiple of 32.
+R6  columnwise layout = rowwise layout of the transpose; with groups, each
+    group's rows are zero-padded to P = ceil(m/32)*32 and group g occupies
+    columns [sum_{j<g} P_j, + P_g) of a [cols, sum P] matrix; padding codes
+    are 0x00 and do not change amax.
+R7  weights are [out, in]: W1 [E, 2F, H] with gate rows 0..F-1 and up rows
+    F..2F-1, W2 [E, H, F]; no biases.
+R8  A = w_r * silu(g) * u is formed before it is requantized for GEMM2
+    (routing weight applied before requantization).
+R9  backward is straight-through: every GEMM runs on MXFP8 copies -- dA from
+    rowwise dY and columnwise W2, dX from rowwise dH1 and columnwise W1, dW2
+    from columnwise dY and A, dW1 from columnwise dH1 and X; gradients are
+    E4M3 as well.  The SwiGLU backward reads H1 rounded to bf16.
+R10 precisions: products and sums in float64; Y, dX and the saved H1 are
+    rounded to bf16 (nearest-even from float64); dW, dprobs in float64.
+R11 a zero-row expert contributes nothing; its dW is the input dW
+    (accumulate) or zero (overwrite).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+E4M3_MAX = 448.0
+E8M0_BIAS = 127
+
+__all__ = [
+    "BLOCK", "E4M3_MAX", "bf16_bits_to_f64", "e4m3_value", "e8m0_value",
+    "scale_exponent", "e4m3_encode", "quantize_blocks", "quantize_rowwise",
+    "dequantize_rowwise", "padded_sizes", "quantize_colwise", "gemm_group_m",
+    "gemm_group_k", "round_to_bf16", "sigmoid", "silu", "mlp_forward",
+    "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
+    "mlp_backward_wgrad_entries",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """E4M3 code -> value.  1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+    infinities; S.1111.111 is NaN; exponent field 0 is subnormal (m/8 * 2^-6)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> 7) & 1
+    ef = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(ef == 0, (m / 8.0) * 2.0 ** -6,
+                   (1.0 + m / 8.0) * np.exp2((ef - 7).astype(np.float64)))
+    mag = np.where((ef == 15) & ((c & 7) == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def e8m0_value(s) -> np.ndarray:
+    """E8M0 code -> 2^(code - 127); code 0xFF is NaN."""
+    s = np.asarray(s).astype(np.int64)
+    v = np.exp2((s - E8M0_BIAS).astype(np.float64))
+    return np.where(s == 255, np.nan, v)
+
+
+def scale_exponent(amax) -> np.ndarray:
+    """Readings R1/R2: e = floor(log2 amax) - 8 clamped to [-127, 127]; amax = 0 -> -127.
+
+    floor(log2 a) is read off the binary exponent: a = f * 2^x with f in
+    [0.5, 1) gives floor(log2 a) = x - 1 (exact, also for subnormal a)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, x = np.frexp(amax)
+    e = (x.astype(np.int64) - 1) - 8
+    e = np.where(amax == 0.0, -127, e)
+    return np.clip(e, -127, 127)
+
+
+def e4m3_encode(t) -> np.ndarray:
+    """Reading R3: E4M3 code of t by saturating round-to-nearest-even.
+
+    t is float64 and already divided by the block scale.  For |t| in the
+    normal range, |t| = (1 + m/8) * 2^E is solved for the integer m by rounding
+    (|t| / 2^E - 1) * 8 half-to-even (all steps exact in float64); a carry to
+    m = 8 moves to the next binade.  Below 2^-6 the grid is uniform with step
+    2^-9, so the code is round-half-even(|t| * 2^9) (code 8 = 2^-6 is the
+    smallest normal, so the two ranges join).  |t| >= 448 saturates."""
+    t = np.asarray(t, dtype=np.float64)
+    a = np.abs(t)
+    sub = a < 2.0 ** -6
+    code_sub = np.rint(a * 2.0 ** 9)
+    safe = np.where(sub, 1.0, a)
+    _, x = np.frexp(safe)
+    E = x.astype(np.int64) - 1
+    frac = safe / np.exp2(E.astype(np.float64)) - 1.0
+    m = np.rint(frac * 8.0).astype(np.int64)
+    carry = m == 8
+    E = np.where(carry, E + 1, E)
+    m = np.where(carry, 0, m)
+    code_norm = (E + 7) * 8 + m
+    code = np.where(sub, code_sub.astype(np.int64), code_norm)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    code = np.where(np.signbit(t), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# block quantization
+
+def quantize_blocks(v):
+    """Quantize blocks of 32 values along the last axis -> (codes, scale codes).
+
+    Steps: amax over the block; e per R1/R2; t = v / 2^e (exact); code per R3."""
+    v = np.asarray(v, dtype=np.float64)
+    if v.shape[-1] != BLOCK:
+        raise ValueError("last axis must be one 32-value block")
+    if not np.all(np.isfinite(v)):
+        raise ValueError("non-finite input is outside the quantizer's contract")
+    amax = np.max(np.abs(v), axis=-1)
+    e = scale_exponent(amax)
+    t = np.ldexp(v, (-e)[..., None])
+    codes = e4m3_encode(t)
+    return codes, (e + E8M0_BIAS).astype(np.uint8)
+
+
+def quantize_rowwise(x):
+    """Reading R5: rowwise MXFP8 of a [rows, cols] matrix -> (codes, scales)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    codes, scales = quantize_blocks(x.reshape(rows, cols // BLOCK, BLOCK))
+    return codes.reshape(rows, cols), scales.reshape(rows, cols // BLOCK)
+
+
+def dequantize_rowwise(q, s):
+    """value = E4M3(code) * 2^(scale code - 127), per 32-block along a row."""
+    q = np.asarray(q)
+    rows, cols = q.shape
+    vals = e4m3_value(q).reshape(rows, cols // BLOCK, BLOCK)
+    return (vals * e8m0_value(s)[..., None]).reshape(rows, cols)
+
+
+def padded_sizes(sizes) -> np.ndarray:
+    s = np.asarray(sizes, dtype=np.int64)
+    return ((s + BLOCK - 1) // BLOCK) * BLOCK
+
+
+def quantize_colwise(x, group_sizes=None):
+    """Reading R6: columnwise MXFP8 (blocks of 32 consecutive rows per column).
+
+    Each group's rows are zero-padded to a multiple of 32, transposed, and
+    quantized rowwise; group g lands at columns [sum of earlier padded sizes,
+    + its padded size) of the [cols, sum P] result."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if group_sizes is None:
+        group_sizes = [rows]
+    sizes = np.asarray(group_sizes, dtype=np.int64)
+    if sizes.sum() != rows:
+        raise ValueError("group sizes must sum to rows")
+    P = padded_sizes(sizes)
+    q = np.zeros((cols, int(P.sum())), dtype=np.uint8)
+    s = np.zeros((cols, int(P.sum()) // BLOCK), dtype=np.uint8)
+    r0 = 0
+    c0 = 0
+    for m, p in zip(sizes.tolist(), P.tolist()):
+        if p:
+            padded = np.zeros((p, cols))
+            padded[:m] = x[r0:r0 + m]
+            qg, sg = quantize_rowwise(padded.T)
+            q[:, c0:c0 + p] = qg
+            s[:, c0 // BLOCK:(c0 + p) // BLOCK] = sg
+        r0 += m
+        c0 += p
+    return q, s
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM (GroupedLinear over split_sizes)
+
+def gemm_group_m(a_q, a_s, b_q, b_s, sizes):
+    """C = A_g . B_g^T for each group's rows of A (float64, dequantized operands).
+
+    a_q [M, K] rowwise MXFP8 (M = sum of sizes); b_q [G, N, K] one weight per
+    group; returns float64 [M, N]."""
+    A = dequantize_rowwise(a_q, a_s)
+    sizes = np.asarray(sizes, dtype=np.int64)
+    G, N, K = b_q.shape
+    C = np.zeros((A.shape[0], N))
+    r0 = 0
+    for g in range(G):
+        m = int(sizes[g])
+        if m:
+            B = dequantize_rowwise(b_q[g], b_s[g])
+            C[r0:r0 + m] = A[r0:r0 + m] @ B.T
+        r0 += m
+    return C
+
+
+def gemm_group_k(a_q, a_s, b_q, b_s, sizes):
+    """C_g = A[:, K_g] . B[:, K_g]^T, K_g = group g's padded column range.
+
+    a_q [M, sum P], b_q [N, sum P] (columnwise-grouped MXFP8); returns
+    float64 [G, M, N]; a group with no rows gives zeros."""
+    A = dequantize_rowwise(a_q, a_s)
+    B = dequantize_rowwise(b_q, b_s)
+    P = padded_sizes(sizes)
+    C = np.zeros((len(P), A.shape[0], B.shape[0]))
+    k0 = 0
+    for g, p in enumerate(P.tolist()):
+        if p:
+            C[g] = A[:, k0:k0 + p] @ B[:, k0:k0 + p].T
+        k0 += p
+    return C
+
+
+# ---------------------------------------------------------------------------
+# fused MLP
+
+def round_to_bf16(x):
+    """Round float64 to the nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits; with E = floor(log2|x|) (at least -126, the
+    subnormal floor) the grid step is 2^(E-7)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(np.where(a == 0, 1.0, a))
+    E = np.maximum(ex.astype(np.int64) - 1, -126)
+    q = np.exp2((E - 7).astype(np.float64))
+    r = np.rint(a / q) * q
+    r = np.where(r > 3.3895313892515355e38, np.inf, r)
+    return np.copysign(r, x)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    return x * sigmoid(x)
+
+
+def _qdq_row(x, quantize):
+    if not quantize:
+        return np.asarray(x, dtype=np.float64)
+    return dequantize_rowwise(*quantize_rowwise(x))
+
+
+def _qdq_col(x, quantize):
+    """Columnwise quantize-dequantize of one group's [m, cols] matrix, returned
+    in the original [m, cols] orientation."""
+    x = np.asarray(x, dtype=np.float64)
+    if not quantize:
+        return x
+    m = x.shape[0]
+    q, s = quantize_colwise(x)
+    return dequantize_rowwise(q, s)[:, :m].T
+
+
+def _as_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+def _offsets(split_sizes):
+    s = np.asarray(split_sizes, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(s)])
+
+
+def mlp_forward(x, probs, w1, w2, split_sizes, *, quantize=True):
+    """GroupedLinear -> ScaledSwiGLU -> GroupedLinear (article item 3).
+
+    Per expert e with rows X_e and routing weights w:
+      H1 = Xq_e . W1q_e^T; g = H1[:, :F], u = H1[:, F:];
+      A  = w * silu(g) * u   (R8);   Y = Aq . W2q_e^T  (rounded to bf16).
+    x [R,H], w1 [E,2F,H], w2 [E,H,F] as bf16 bits or float; probs [R].
+    quantize=False gives the unquantized float64 MLP (for derivative checks).
+    Returns dict(y, y_exact, h1, h1_bf16, a)."""
+    X = _as_f64(x)
+    p = np.asarray(probs, dtype=np.float64)
+    E = w1.shape[0]
+    F = w1.shape[1] // 2
+    off = _offsets(split_sizes)
+    Xh = _qdq_row(X, quantize)
+    R, H = X.shape
+    H1 = np.zeros((R, 2 * F))
+    A = np.zeros((R, F))
+    Y = np.zeros((R, H))
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        W1h = _qdq_row(_as_f64(w1[e]), quantize)
+        W2h = _qdq_row(_as_f64(w2[e]), quantize)
+        h1 = Xh[r0:r1] @ W1h.T
+        g, u = h1[:, :F], h1[:, F:]
+        a = p[r0:r1, None] * silu(g) * u
+        Y[r0:r1] = _qdq_row(a, quantize) @ W2h.T
+        H1[r0:r1] = h1
+        A[r0:r1] = a
+    return dict(y=round_to_bf16(Y), y_exact=Y, h1=H1, h1_bf16=round_to_bf16(H1), a=A)
+
+
+def _swiglu_backward(dA, g, u, w):
+    """Derivatives of A = w * silu(g) * u:
+    dg = dA*w*u*s*(1 + g*(1-s)),  du = dA*w*silu(g),  dw = sum_f dA*silu(g)*u,
+    with s = sigmoid(g) (silu'(g) = s + g*s*(1-s))."""
+    s = sigmoid(g)
+    sl = g * s
+    dg = dA * w[:, None] * u * s * (1.0 + g * (1.0 - s))
+    du = dA * w[:, None] * sl
+    dw = np.sum(dA * sl * u, axis=1)
+    return dg, du, dw
+
+
+def mlp_backward(x, probs, w1, w2, split_sizes, dy, fwd, *, quantize=True,
+                 dw1_in=None, dw2_in=None):
+    """Backward of mlp_forward (article item 3, "corresponding fused backward op"),
+    straight-through per reading R9.
+
+    fwd is mlp_forward's result (its h1_bf16 and a are used; with quantize=False
+    the exact h1 is used instead).  dw1_in/dw2_in, when given, are accumulated
+    into (fp32 main-grad style); otherwise dW starts from zero.
+    Returns dict(dx, dx_exact, dprobs, dw1, dw2, dh1, da)."""
+    X = _as_f64(x)
+    dY = _as_f64(dy)
+    p = np.asarray(probs, dtype=np.float64)
+    E = w1.shape[0]
+    F = w1.shape[1] // 2
+    R, H = X.shape
+    off = _offsets(split_sizes)
+    h1 = fwd["h1_bf16"] if quantize else fwd["h1"]
+    A = fwd["a"]
+    dX = np.zeros((R, H))
+    dP = np.zeros(R)
+    dH1 = np.zeros((R, 2 * F))
+    dAll = np.zeros((R, F))
+    dW1 = np.zeros(w1.shape) if dw1_in is None else np.array(dw1_in, dtype=np.float64)
+    dW2 = np.zeros(w2.shape) if dw2_in is None else np.array(dw2_in, dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        W1 = _as_f64(w1[e])
+        W2 = _as_f64(w2[e])
+        dA = _qdq_row(dY[r0:r1], quantize) @ _qdq_col(W2, quantize)
+        g, u = h1[r0:r1, :F], h1[r0:r1, F:]
+        dg, du, dw = _swiglu_backward(dA, g, u, p[r0:r1])
+        dh = np.concatenate([dg, du], axis=1)
+        dX[r0:r1] = _qdq_row(dh, quantize) @ _qdq_col(W1, quantize)
+        dW2[e] += _qdq_col(dY[r0:r1], quantize).T @ _qdq_col(A[r0:r1], quantize)
+        dW1[e] += _qdq_col(dh, quantize).T @ _qdq_col(X[r0:r1], quantize)
+        dP[r0:r1] = dw
+        dH1[r0:r1] = dh
+        dAll[r0:r1] = dA
+    return dict(dx=round_to_bf16(dX), dx_exact=dX, dprobs=dP, dw1=dW1, dw2=dW2, dh1=dH1,
+                da=dAll)
+
+
+# ---------------------------------------------------------------------------
+# sampled evaluation at full size (same steps, restricted to chosen outputs)
+
+def _expert_of_rows(split_sizes, rows):
+    off = _offsets(split_sizes)
+    return np.searchsorted(off, np.asarray(rows), side="right") - 1
+
+
+def mlp_forward_rows(x, probs, w1, w2, split_sizes, rows):
+    """Y (bf16-rounded) and A for the selected rows only.
+
+    Rowwise quantization acts on one row at a time, so a row's Y depends only
+    on that row, its routing weight and its expert's weights."""
+    rows = np.asarray(rows, dtype=np.int64)
+    F = w1.shape[1] // 2
+    H = w1.shape[2]
+    ex = _expert_of_rows(split_sizes, rows)
+    Y = np.zeros((len(rows), H))
+    A = np.zeros((len(rows), F))
+    H1 = np.zeros((len(rows), 2 * F))
+    p = np.asarray(probs, dtype=np.float64)
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        r = rows[sel]
+        Xh = _qdq_row(_as_f64(x[r]), True)
+        W1h = _qdq_row(_as_f64(w1[e]), True)
+        h1 = Xh @ W1h.T
+        del W1h
+        a = p[r, None] * silu(h1[:, :F]) * h1[:, F:]
+        W2h = _qdq_row(_as_f64(w2[e]), True)
+        Y[sel] = _qdq_row(a, True) @ W2h.T
+        A[sel] = a
+        H1[sel] = h1
+    return dict(y=round_to_bf16(Y), a=A, h1_bf16=round_to_bf16(H1))
+
+
+def _expert_dh1(x, probs, w1, w2, split_sizes, dy, e, r_sel=None):
+    """dH1 rows of expert e (all its rows, or the positions r_sel within it),
+    from the fwd's bf16 H1 and the straight-through dA.  Also returns dprobs of
+    those rows and the unrounded H1 (from which the forward formed A)."""
+    off = _offsets(split_sizes)
+    r0, r1 = int(off[e]), int(off[e + 1])
+    F = w1.shape[1] // 2
+    idx = np.arange(r0, r1) if r_sel is None else r0 + np.asarray(r_sel)
+    Xh = _qdq_row(_as_f64(x[idx]), True)
+    W1h = _qdq_row(_as_f64(w1[e]), True)
+    h1 = Xh @ W1h.T
+    del W1h
+    hb = round_to_bf16(h1)
+    dA = _qdq_row(_as_f64(dy[idx]), True) @ _qdq_col(_as_f64(w2[e]), True)
+    p = np.asarray(probs, dtype=np.float64)[idx]
+    dg, du, dw = _swiglu_backward(dA, hb[:, :F], hb[:, F:], p)
+    return np.concatenate([dg, du], axis=1), dw, h1
+
+
+def mlp_backward_rows(x, probs, w1, w2, split_sizes, dy, rows):
+    """dX (bf16-rounded) and dprobs for the selected rows only."""
+    rows = np.asarray(rows, dtype=np.int64)
+    off = _offsets(split_sizes)
+    ex = _expert_of_rows(split_sizes, rows)
+    H = w1.shape[2]
+    dX = np.zeros((len(rows), H))
+    dP = np.zeros(len(rows))
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        dh, dw, _ = _expert_dh1(x, probs, w1, w2, split_sizes, dy, e,
+                                rows[sel] - int(off[e]))
+        dX[sel] = _qdq_row(dh, True) @ _qdq_col(_as_f64(w1[e]), True)
+        dP[sel] = dw
+    return dict(dx=round_to_bf16(dX), dprobs=dP)
+
+
+def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
+                               dw1_idx, dw2_idx):
+    """Selected entries of one expert's dW1 (indices (n, h)) and dW2 ((h, f)),
+    from a zero start.  Needs the expert's full dH1 and A columns, so it runs
+    the expert's whole forward/backward restricted to the needed columns."""
+    off = _offsets(split_sizes)
+    r0, r1 = int(off[expert]), int(off[expert + 1])
+    F = w1.shape[1] // 2
+    dw1_idx = np.asarray(dw1_idx, dtype=np.int64).reshape(-1, 2)
+    dw2_idx = np.asarray(dw2_idx, dtype=np.int64).reshape(-1, 2)
+    if r1 == r0:
+        return np.zeros(len(dw1_idx)), np.zeros(len(dw2_idx))
+    dh, _, h1 = _expert_dh1(x, probs, w1, w2, split_sizes, dy, expert)
+    p = np.asarray(probs, dtype=np.float64)[r0:r1]
+    a = p[:, None] * silu(h1[:, :F]) * h1[:, F:]
+    X = _as_f64(x[r0:r1])
+    dY = _as_f64(dy[r0:r1])
+    # columnwise quantization is per column: quantize only the needed columns
+    dhc = _qdq_col(dh[:, np.unique(dw1_idx[:, 0])], True)
+    xc = _qdq_col(X[:, np.unique(dw1_idx[:, 1])], True)
+    n_map = {n: i for i, n in enumerate(np.unique(dw1_idx[:, 0]).tolist())}
+    h_map = {h: i for i, h in enumerate(np.unique(dw1_idx[:, 1]).tolist())}
+    out1 = np.array([dhc[:, n_map[n]] @ xc[:, h_map[h]] for n, h in dw1_idx.tolist()])
+    dyc = _qdq_col(dY[:, np.unique(dw2_idx[:, 0])], True)
+    ac = _qdq_col(a[:, np.unique(dw2_idx[:, 1])], True)
+    h2_map = {h: i for i, h in enumerate(np.unique(dw2_idx[:, 0]).tolist())}
+    f_map = {f: i for i, f in enumerate(np.unique(dw2_idx[:, 1]).tolist())}
+    out2 = np.array([dyc[:, h2_map[h]] @ ac[:, f_map[f]] for h, f in dw2_idx.tolist()])
+    return out1, out2
