@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 grouped-MLP training step on one MI355X (gfx950).
+
+One step = the whole hot path on one batch of seeded synthetic input:
+grouped_mlp_fwd in training mode (quantize X, W1, W2 in both layouts; grouped
+GEMM1 with the fused ScaledSwiGLU / routing-weight / requantize epilogue;
+grouped GEMM2) followed by grouped_mlp_bwd (quantize dY; dgrad2 with the
+fused SwiGLU-backward epilogue; dprobs; wgrad2; dgrad1; wgrad1 accumulated
+into fp32 main grads). Default workload: the Mixtral-8x7B-shaped MoE MLP
+fwd+bwd (4096 tokens, top-2 of 8 experts = 8192 routed rows, hidden 4096,
+ffn 14336). Inputs are resident in HBM before the timed region; no host
+transfer or allocation happens inside it.
+
+Prints ONE JSON line: metric/value (GEMM FLOP of the step per second),
+per-stage times from HIP events recorded on the launch stream, the roofline
+of the dominant kernel, the standalone quantize GB/s (16384 x 4096 bf16,
+both layouts) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 grouped-MLP TFLOP/s (fwd+bwd) and % of MXFP8 MFMA peak; quantize GB/s"
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 / MXFP8 MFMA
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+GEMM_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_gemm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stage_flops(R, H, F):
+    """Algorithmic GEMM FLOP of each GEMM stage (actual routed rows, no padding)."""
+    return {
+        "gemm1_swiglu": 4.0 * R * H * F, "gemm2": 2.0 * R * H * F,
+        "dgrad2_swiglu_bwd": 2.0 * R * H * F, "wgrad2": 2.0 * R * H * F,
+        "dgrad1": 4.0 * R * H * F, "wgrad1": 4.0 * R * H * F,
+    }
+
+
+def traffic_from_profiles(kernel_stage):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter summaries, only if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_stage}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_KERNEL_SRC, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inputs, wl, rows_sample=256):
+    """The oracle (float64 numpy) on a bounded sample of the same workload: the
+    fwd+bwd of one expert restricted to its first rows_sample rows."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    split = inputs["split_sizes"]
+    e = int(np.argmax(split))
+    r0 = int(split[:e].sum())
+    S = int(min(rows_sample, split[e]))
+    sl = slice(r0, r0 + S)
+    x, dy, p = inputs["x"][sl], inputs["dy"][sl], inputs["probs"][sl]
+    w1, w2 = inputs["w1"][e:e + 1], inputs["w2"][e:e + 1]
+    t0 = time.perf_counter()
+    fwd = orc.mlp_forward(x, p, w1, w2, [S])
+    orc.mlp_backward(x, p, w1, w2, [S], dy, fwd)
+    dt = time.perf_counter() - t0
+    flops = 18.0 * S * wl.hidden * wl.ffn
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd+bwd of expert {e} on its first {S} routed rows (H={wl.hidden}, F={wl.ffn}), "
+                      f"{flops / 1e12:.3f} TFLOP in {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_moe_fwd_bwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantize", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md but not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as wlmod
+    import mxfp8_block_scaled_mx_amd as mx
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mx.load()
+    dev = torch.device("cuda:0")
+    wl = wlmod.WORKLOADS[args.workload]
+    if not wl.backward:
+        raise SystemExit("bench.py times the fwd+bwd step; pick a workload with a backward pass")
+
+    log(f"generating inputs for {wl.name} (seed {wl.seed})")
+    t0 = time.perf_counter()
+    inp = wlmod.make_mlp_inputs(wl)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; split_sizes={inp['split_sizes'].tolist()}")
+
+    def to_dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w1, w2, dy = (to_dev_bf16(inp[k]) for k in ("x", "w1", "w2", "dy"))
+    probs = torch.from_numpy(inp["probs"]).to(dev)
+    E, R, H, F = wl.experts, wl.rows, wl.hidden, wl.ffn
+    split = inp["split_sizes"].tolist()
+    runner = mx.MLPRunner(E, R, H, F, split, device=dev)
+    dw1 = torch.zeros((E, 2 * F, H), dtype=torch.float32, device=dev)
+    dw2 = torch.zeros((E, H, F), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        runner.forward(x, probs, w1, w2, training=True)
+        runner.backward(dy, probs, dw1, dw2, accumulate=True)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nf, nb = len(mx.FWD_STAGES) + 1, len(mx.BWD_STAGES) + 1
+    ev_f = [[torch.cuda.Event(enable_timing=True) for _ in range(nf)] for _ in range(args.steps)]
+    ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(nb)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for evs in ev_f + ev_b:          # torch creates the HIP event on first record
+        for e in evs:
+            e.record()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        mx.set_stage_events(ev_f[i])
+        runner.forward(x, probs, w1, w2, training=True)
+        mx.set_stage_events(ev_b[i])
+        runner.backward(dy, probs, dw1, dw2, accumulate=True)
+    end.record()
+    mx.set_stage_events(None)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    stages = {}
+    for names, evs in ((mx.FWD_STAGES, ev_f), (mx.BWD_STAGES, ev_b)):
+        for j, name in enumerate(names):
+            stages[name] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+    flops = stage_flops(R, H, F)
+    step_flops = sum(flops.values())                     # = 18 R H F
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = sum(stages[k] for k in flops)
+    gemm_tflops = step_flops / (gemm_ms * 1e-3) / 1e12
+    dom = max(flops, key=lambda k: stages[k])
+    dom_ach = flops[dom] / (stages[dom] * 1e-3) / 1e12
+    traffic = traffic_from_profiles(dom)
+    roofline = {"bound": "mfma", "achieved": round(dom_ach, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "kernel": dom, "flop_per_launch": flops[dom], "avg_launch_ms": round(stages[dom], 4)}
+    per_gemm = {k: {"ms": round(stages[k], 4),
+                    "tflops": round(flops[k] / (stages[k] * 1e-3) / 1e12, 1),
+                    "frac_mfma_peak": round(flops[k] / (stages[k] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+                for k in flops}
+    log(f"step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; GEMM-only {gemm_tflops:.1f} TFLOP/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8_e4m3",
+        "data": "synthetic (seeded; shapes of the Mixtral-8x7B-shaped MoE MLP)",
+        "config": {"workload": wl.name, "tokens": wl.tokens, "topk": wl.topk, "experts": E,
+                   "rows": R, "hidden": H, "ffn": F, "split_sizes": split,
+                   "step": "grouped_mlp_fwd(training) + grouped_mlp_bwd(fp32 wgrad accumulate)"},
+        "gemm_only": {"tflops": round(gemm_tflops, 1),
+                      "frac_mfma_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "ms": round(gemm_ms, 4)},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "per_gemm": per_gemm,
+        "roofline": roofline,
+    }
+
+    if not args.no_quantize:
+        out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
+        log(f"quantize {out['quantize']['gbps']:.0f} GB/s")
+
+    # free device memory before the CPU leg
+    del runner, dw1, dw2, x, w1, w2, dy
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(inp, wl)
+        log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
+    """mx_quantize on the 16384 x 4096 Student-t tensor (rowwise + columnwise),
+    rotating over 4 distinct 128 MiB inputs so re-reads cannot hit the 256 MB
+    Infinity Cache. Algorithmic bytes: 2 read + 2 * (1 + 1/32) written per element."""
+    bits = wlmod.quantize_tensor_c2()
+    rows, cols = bits.shape
+    base = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [base.clone() for _ in range(copies)]
+    del base
+    L = mx.load()
+    q_row = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s_row = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    stream = mx._stream()
+
+    def call(t):
+        mx._check(L.mx_quantize(mx._ptr(t), mx.MX_BF16, rows, cols, None, 0, mx._ptr(q_row), mx._ptr(s_row),
+                                mx._ptr(q_col), mx._ptr(s_col), stream))
+
+    for i in range(8):
+        call(xs[i % copies])
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    evs[0].record()
+    for i in range(iters):
+        call(xs[i % copies])
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(iters)]
+    algo = rows * cols * 2 + 2 * (rows * cols + rows * cols // 32)
+    med = float(np.median(times))
+    gbps = algo / (med * 1e-3) / 1e9
+    return {"workload": "quantize_16384x4096", "layouts": "rowwise+columnwise", "bytes": algo,
+            "median_ms": round(med, 4), "min_ms": round(float(np.min(times)), 4),
+            "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+
+
+if __name__ == "__main__":
+    main()

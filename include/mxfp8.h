@@ -1,0 +1,236 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 block-scaled grouped-MLP library.
+ *
+ * What the library computes (the pages this follows):
+ *   - MXFP8: 8-bit E4M3 values with one power-of-two (E8M0) scale per block of
+ *     32 consecutive values ("Efficient MoE training for biological foundation
+ *     models", section "Key technical approaches in the recipe", item 2; the
+ *     TransformerEngine Llama 3 recipe page, section "MXFP8 vs BF16 throughput
+ *     on Llama-3.1": MXFP8BlockScaling with E4M3).
+ *   - GroupedLinear: one grouped GEMM over per-expert row counts (split_sizes)
+ *     instead of one launch per expert (same article, item 1).
+ *   - GroupedLinear -> ScaledSwiGLU -> GroupedLinear fused into one forward op
+ *     and one backward op, with the SwiGLU activation and routing-weight
+ *     scaling fused and 16-bit master weights quantized each step (same
+ *     article, item 3).
+ *
+ * Number formats and rounding (readings of what the pages leave open):
+ *   - block scale exponent e = floor(log2(amax)) - 8, clamped to [-127, 127];
+ *     E8M0 scale code = e + 127 (0x00 for an all-zero block);
+ *   - element code = E4M3 (bias 7, no infinities) of v / 2^e by
+ *     round-to-nearest-even, saturating at +-448 (never NaN), subnormals kept,
+ *     sign bit copied from the input (so -0.0 and negative underflow -> 0x80).
+ *   - Non-finite inputs are outside the contract: outputs are unspecified.
+ *
+ * Layouts (all row-major, "ld" = elements between consecutive rows):
+ *   - rowwise MXFP8 of a [rows, cols] matrix: codes uint8 [rows, cols] and
+ *     scales uint8 [rows, cols/32]; block j of row r covers columns
+ *     [32j, 32j+32). cols must be a multiple of 32.
+ *   - columnwise MXFP8 = rowwise MXFP8 of the transpose: codes [cols, P],
+ *     scales [cols, P/32]. With row groups (split_sizes), group g's rows are
+ *     zero-padded to P_g = ceil(m_g/32)*32 and occupy columns
+ *     [sum_{j<g} P_j, + P_g); blocks never straddle groups; padding codes are
+ *     0x00. Without groups, P = ceil(rows/32)*32.
+ *   - The scale matrix of a code matrix with leading dimension ld has leading
+ *     dimension ld/32, and a code offset o (whose column part is a multiple of
+ *     32) corresponds to scale offset o/32.
+ *   - Weights are [out, in]: W1 [E, 2F, H] (gate rows 0..F-1, up rows F..2F-1),
+ *     W2 [E, H, F]; no biases. bf16 arrays are raw IEEE bfloat16 bit patterns.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers unless marked "host". The caller owns all memory; the
+ *     library never allocates, frees or keeps device memory between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronizing. split_sizes are host arrays.
+ *   - Arguments are validated before anything is enqueued. On any non-OK
+ *     status nothing was enqueued and no output was touched; mx_last_error()
+ *     then holds a one-line description (thread-local).
+ *   - No C++ exception crosses this boundary. Calls on different streams may
+ *     run concurrently; calls that write the same buffers must be ordered by
+ *     the caller.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MX_API __attribute__((visibility("default")))
+#else
+#define MX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_EINVAL = 1,       /* null pointer, bad enum value, inconsistent flags */
+  MX_ESHAPE = 2,       /* sizes inconsistent or not multiples of 32 */
+  MX_EALIGN = 3,       /* pointer or leading dimension misaligned */
+  MX_EWORKSPACE = 4,   /* workspace or saved buffer smaller than required */
+  MX_EHIP = 5,         /* a HIP runtime call failed (text in mx_last_error) */
+  MX_EUNSUPPORTED = 6  /* valid request this build does not support */
+} mx_status;
+
+typedef enum mx_dtype { MX_BF16 = 0, MX_F32 = 1 } mx_dtype;
+
+typedef enum mx_group_mode {
+  MX_GROUP_M = 0, /* groups split the rows of A (fprop, dgrad) */
+  MX_GROUP_K = 1  /* groups split the K dimension (wgrad) */
+} mx_group_mode;
+
+/* Largest number of groups (experts) one call accepts. */
+#define MX_MAX_GROUPS 128
+
+/* Name of a status code (static string). */
+MX_API const char* mx_status_string(int status);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+MX_API const char* mx_last_error(void);
+
+/* Library ABI version: 1. */
+MX_API int mx_version(void);
+
+/*
+ * mx_quantize -- MXFP8 quantization of a [rows, cols] matrix (row-major,
+ * contiguous, ld = cols) into the rowwise and/or columnwise layouts.
+ *
+ * Follows the block-scaling definition above (article item 2).
+ *   x            bf16 or f32 input [rows, cols], 16-byte aligned.
+ *   x_dtype      MX_BF16 or MX_F32.
+ *   rows, cols   rows >= 0, cols > 0 and cols % 32 == 0.
+ *   group_sizes  host int64[num_groups] row counts (>= 0) summing to rows, or
+ *                NULL with num_groups == 0 for a single group of all rows.
+ *                Groups only change the columnwise layout.
+ *   q_row,s_row  rowwise codes [rows, cols] (16-byte aligned) and scales
+ *                [rows, cols/32]; both NULL to skip the rowwise copy.
+ *   q_col,s_col  columnwise codes [cols, sumP] (16-byte aligned) and scales
+ *                [cols, sumP/32]; both NULL to skip the columnwise copy.
+ * At least one copy must be requested. Errors: MX_EINVAL (null x, both copies
+ * skipped, half of a pair given, bad dtype), MX_ESHAPE (cols % 32, negative or
+ * inconsistent sizes), MX_EALIGN, MX_EUNSUPPORTED (num_groups > MX_MAX_GROUPS).
+ */
+MX_API mx_status mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                      const int64_t* group_sizes, int32_t num_groups,
+                      uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                      void* stream);
+
+/*
+ * mx_grouped_gemm -- grouped block-scaled GEMM  C = A . B^T  on MXFP8 operands
+ * (GroupedLinear over split_sizes, article item 1; MXFP8 operands, item 2).
+ * Both operands are K-contiguous rowwise MXFP8 (codes + scales); products are
+ * accumulated in fp32.
+ *
+ * mode = MX_GROUP_M (fprop/dgrad): sizes[g] rows of A belong to group g (in
+ *   order, sum = M); group g uses B_g = b + g*b_group_stride (codes, [N, ldb])
+ *   and b_scale + g*b_group_stride/32; C is [M, ldc].
+ * mode = MX_GROUP_K (wgrad): sizes[g] are unpadded row counts; group g
+ *   contracts over columns [sum_{j<g} P_j, + P_g) of A [M, lda] and B [N, ldb]
+ *   (the columnwise-grouped layout, K = sum P); C_g = c + g*c_group_stride is
+ *   [M, ldc]; a group with sizes[g] == 0 writes zeros (accumulate = 0) or
+ *   leaves C_g unchanged (accumulate = 1).
+ *
+ *   a, a_scale   A codes [M, lda] and scales [M, lda/32]; lda % 32 == 0.
+ *   b, b_scale   B codes [N, ldb] (per group in MX_GROUP_M) and scales.
+ *   c            output, c_dtype MX_F32 or MX_BF16 (round to nearest even).
+ *   accumulate   1: C += result (MX_F32 only); 0: C = result.
+ * Requirements: K % 32 == 0, N % 32 == 0, K <= lda, K <= ldb, N <= ldc,
+ * b_group_stride % 32 == 0, a/b 16-byte aligned, c 16-byte aligned and
+ * ldc % 4 == 0, 1 <= num_groups <= MX_MAX_GROUPS.
+ */
+MX_API mx_status mx_grouped_gemm(int32_t mode, int32_t num_groups, const int64_t* sizes,
+                          int64_t M, int64_t N, int64_t K,
+                          const uint8_t* a, const uint8_t* a_scale, int64_t lda,
+                          const uint8_t* b, const uint8_t* b_scale, int64_t ldb,
+                          int64_t b_group_stride,
+                          void* c, int32_t c_dtype, int64_t ldc, int64_t c_group_stride,
+                          int32_t accumulate, void* stream);
+
+/* Shape of one grouped MLP call: R routed rows, E experts, hidden H, ffn F. */
+typedef struct mx_mlp_dims {
+  int32_t num_experts;
+  int64_t rows;
+  int64_t hidden;
+  int64_t ffn;
+} mx_mlp_dims;
+
+/*
+ * grouped_mlp_sizes -- byte sizes of the caller-provided buffers for one
+ * shape and split: fwd_workspace (scratch of grouped_mlp_fwd), saved (what
+ * grouped_mlp_fwd keeps for grouped_mlp_bwd in training) and bwd_workspace
+ * (scratch of grouped_mlp_bwd). Any output pointer may be NULL.
+ * Errors: MX_EINVAL, MX_ESHAPE (H or F not multiples of 32, split mismatch).
+ */
+MX_API mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                            size_t* fwd_workspace, size_t* saved, size_t* bwd_workspace);
+
+/*
+ * grouped_mlp_fwd -- fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
+ * forward (article item 3). For expert e and its rows X_e (routing weight w
+ * per row):
+ *     H1 = Xq_e . W1q_e^T;  g = H1[:, :F], u = H1[:, F:];
+ *     A  = w * silu(g) * u  (fp32, formed before requantization);
+ *     Y  = Aq . W2q_e^T     (bf16, round to nearest even)
+ * where Xq, W1q, W2q, Aq are rowwise MXFP8 copies made inside the call (the
+ * bf16 master weights are quantized on every call).
+ *   split_sizes  host int64[E], >= 0, sum = R; rows are ordered by expert.
+ *   x            bf16 [R, H];  probs f32 [R] routing weights (NULL = all 1).
+ *   w1, w2       bf16 [E, 2F, H] and [E, H, F].
+ *   y            bf16 [R, H] output.
+ *   saved        NULL for inference; otherwise a buffer of `saved` bytes
+ *                (grouped_mlp_sizes) that receives H1 (bf16), the columnwise
+ *                copies of X, A, W1, W2 for grouped_mlp_bwd.
+ *   workspace    fwd_workspace bytes of scratch, 256-byte aligned.
+ * Requires H % 32 == 0, F % 32 == 0 (H % 128 and F % 128 for best speed),
+ * 1 <= E <= MX_MAX_GROUPS. All pointers 16-byte aligned.
+ */
+MX_API mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                          const void* x, const float* probs, const void* w1, const void* w2,
+                          void* y, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * grouped_mlp_bwd -- the corresponding fused backward op (article item 3),
+ * straight-through for quantization; every GEMM runs on MXFP8 copies:
+ *     dA  = dYq_row . colwise(W2_e)          (K = H)
+ *     dg  = dA*w*u*s*(1 + g*(1-s)), du = dA*w*silu(g), s = sigmoid(g),
+ *           with g, u from the saved bf16 H1;  dprobs = sum_f dA*silu(g)*u
+ *     dX  = dH1q_row . colwise(W1_e)         (K = 2F, bf16 out)
+ *     dW2_e (+)= colwise(dY_e)^T . colwise(A_e)    (fp32)
+ *     dW1_e (+)= colwise(dH1_e)^T . colwise(X_e)   (fp32)
+ *   dy           bf16 [R, H];  probs as in the forward (NULL = all 1).
+ *   saved        the buffer filled by grouped_mlp_fwd with the same inputs.
+ *   dx           bf16 [R, H] output.
+ *   dprobs       f32 [R] output, or NULL to skip.
+ *   dw1, dw2     f32 [E, 2F, H] and [E, H, F]; accumulate_wgrad = 1 adds into
+ *                them (fp32 main-grad), 0 overwrites. An expert with no rows
+ *                leaves its dW unchanged (1) or zero (0).
+ *   workspace    bwd_workspace bytes of scratch.
+ */
+MX_API mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                          const void* dy, const float* probs, const void* saved, size_t saved_bytes,
+                          void* dx, float* dprobs, float* dw1, float* dw2, int32_t accumulate_wgrad,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mx_set_stage_events -- optional per-stage timing of the fused MLP calls
+ * (observability only; nothing is computed differently). events points to
+ * `count` hipEvent_t handles owned by the caller, or is NULL to switch timing
+ * off. While set on the calling thread, grouped_mlp_fwd records events[i] on
+ * its stream before stage i and after the last stage (stages: quantize X,
+ * quantize W1, quantize W2, GEMM1 + SwiGLU epilogue, GEMM2 -> 6 events) and
+ * grouped_mlp_bwd does the same for its stages (quantize dY, dgrad2 + SwiGLU
+ * backward epilogue, dprobs reduction, wgrad2, dgrad1, wgrad1 -> 7 events).
+ * Events beyond `count` are not recorded. Errors: MX_EINVAL (count < 0, or
+ * count > 0 with events NULL).
+ */
+MX_API mx_status mx_set_stage_events(void* const* events, int32_t count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

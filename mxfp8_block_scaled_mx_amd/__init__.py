@@ -1,0 +1,317 @@
+"""Python binding of the MI355X MXFP8 grouped-MLP library (libmxfp8.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/mxfp8.h). PyTorch provides device memory
+and the current stream. There is no CPU or PyTorch fallback: if the library
+is missing, load() raises.
+
+Entry points mirror the C ABI: quantize (mx_quantize), grouped_gemm
+(mx_grouped_gemm), grouped_mlp_fwd / grouped_mlp_bwd, plus GroupedMLP, an
+autograd Function over the fused forward/backward pair (GroupedLinear ->
+ScaledSwiGLU -> GroupedLinear with routing-weight scaling: "Efficient MoE
+training for biological foundation models", Key technical approaches item 3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "load", "lib_path", "MXError", "MX_BF16", "MX_F32", "MX_GROUP_M", "MX_GROUP_K",
+    "MAX_GROUPS", "padded_sizes", "quantize", "grouped_gemm", "mlp_sizes",
+    "grouped_mlp_fwd", "grouped_mlp_bwd", "GroupedMLP", "MLPState", "MLPRunner",
+    "set_stage_events", "FWD_STAGES", "BWD_STAGES",
+]
+
+FWD_STAGES = ("quantize_x", "quantize_w1", "quantize_w2", "gemm1_swiglu", "gemm2")
+BWD_STAGES = ("quantize_dy", "dgrad2_swiglu_bwd", "dprobs_reduce", "wgrad2", "dgrad1", "wgrad1")
+
+MX_BF16, MX_F32 = 0, 1
+MX_GROUP_M, MX_GROUP_K = 0, 1
+MAX_GROUPS = 128
+STATUS = {0: "MX_OK", 1: "MX_EINVAL", 2: "MX_ESHAPE", 3: "MX_EALIGN",
+          4: "MX_EWORKSPACE", 5: "MX_EHIP", 6: "MX_EUNSUPPORTED"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "lib", "libmxfp8.so")
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmxfp8.so (build it with mxfp8_block_scaled_mx_amd.build first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run python -m mxfp8_block_scaled_mx_amd.build)")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_status_string.argtypes = [ctypes.c_int]
+    L.mx_last_error.restype = ctypes.c_char_p
+    L.mx_last_error.argtypes = []
+    L.mx_version.restype = ctypes.c_int
+    L.mx_quantize.restype = ctypes.c_int
+    L.mx_quantize.argtypes = [vp, i32, i64, i64, p64, i32, vp, vp, vp, vp, vp]
+    L.mx_grouped_gemm.restype = ctypes.c_int
+    L.mx_grouped_gemm.argtypes = [i32, i32, p64, i64, i64, i64, vp, vp, i64, vp, vp, i64, i64,
+                                  vp, i32, i64, i64, i32, vp]
+    L.grouped_mlp_sizes.restype = ctypes.c_int
+    L.grouped_mlp_sizes.argtypes = [ctypes.POINTER(_Dims), p64, ctypes.POINTER(sz),
+                                    ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.grouped_mlp_fwd.restype = ctypes.c_int
+    L.grouped_mlp_fwd.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.grouped_mlp_bwd.restype = ctypes.c_int
+    L.grouped_mlp_bwd.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
+                                  vp, sz, vp]
+    L.mx_set_stage_events.restype = ctypes.c_int
+    L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise MXError(status, load().mx_last_error().decode())
+
+
+def _i64_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def padded_sizes(sizes):
+    return [(int(m) + 31) // 32 * 32 for m in sizes]
+
+
+def quantize(x: torch.Tensor, group_sizes=None, rowwise: bool = True, colwise: bool = True,
+             stream=None):
+    """MXFP8 of a 2-D bf16/fp32 CUDA tensor -> dict(q_row, s_row, q_col, s_col).
+
+    Rowwise: codes [rows, cols], scales [rows, cols/32]. Columnwise (with
+    optional row groups): codes [cols, sumP], scales [cols, sumP/32]."""
+    L = load()
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    dt = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}[x.dtype]
+    rows, cols = x.shape
+    dev = x.device
+    out = {"q_row": None, "s_row": None, "q_col": None, "s_col": None}
+    if rowwise:
+        out["q_row"] = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        out["s_row"] = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    if colwise:
+        P = sum(padded_sizes(group_sizes if group_sizes is not None else [rows]))
+        out["q_col"] = torch.empty((cols, P), dtype=torch.uint8, device=dev)
+        out["s_col"] = torch.empty((cols, P // 32), dtype=torch.uint8, device=dev)
+    gs = None if group_sizes is None else _i64_array(group_sizes)
+    ng = 0 if group_sizes is None else len(group_sizes)
+    _check(L.mx_quantize(_ptr(x), dt, rows, cols, gs, ng, _ptr(out["q_row"]), _ptr(out["s_row"]),
+                         _ptr(out["q_col"]), _ptr(out["s_col"]), _stream(stream)))
+    return out
+
+
+def grouped_gemm(mode: int, sizes, a_q, a_s, b_q, b_s, *, N: int, K: int, M: int | None = None,
+                 lda: int | None = None, ldb: int | None = None, b_group_stride: int = 0,
+                 out: torch.Tensor | None = None, out_dtype=torch.float32, accumulate: bool = False,
+                 c_group_stride: int | None = None, stream=None):
+    """Grouped block-scaled GEMM C = A . B^T (mx_grouped_gemm).
+
+    MX_GROUP_M: A [M, lda] rows split by sizes, B_g = b_q + g*b_group_stride
+    ([N, ldb]); C [M, N]. MX_GROUP_K: K = sum of padded sizes, C [G, M, N]."""
+    L = load()
+    G = len(sizes)
+    if M is None:
+        M = sum(int(s) for s in sizes) if mode == MX_GROUP_M else a_q.shape[0]
+    lda = a_q.shape[1] if lda is None else lda
+    ldb = b_q.shape[-1] if ldb is None else ldb
+    if out is None:
+        shape = (M, N) if mode == MX_GROUP_M else (G, M, N)
+        out = torch.empty(shape, dtype=out_dtype, device=a_q.device)
+    cdt = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}[out.dtype]
+    if c_group_stride is None:
+        c_group_stride = M * N if mode == MX_GROUP_K else 0
+    _check(L.mx_grouped_gemm(mode, G, _i64_array(sizes), M, N, K, _ptr(a_q), _ptr(a_s), lda,
+                             _ptr(b_q), _ptr(b_s), ldb, b_group_stride, _ptr(out), cdt,
+                             out.shape[-1], c_group_stride, int(accumulate), _stream(stream)))
+    return out
+
+
+def _dims(E, R, H, F):
+    return _Dims(int(E), int(R), int(H), int(F))
+
+
+def mlp_sizes(E: int, R: int, H: int, F: int, split_sizes):
+    """(fwd workspace, saved, bwd workspace) byte sizes for one call."""
+    L = load()
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.grouped_mlp_sizes(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes),
+                               ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)))
+    return f.value, s.value, b.value
+
+
+class MLPState:
+    """What the fused forward keeps for the backward (a caller-owned buffer)."""
+
+    def __init__(self, saved: torch.Tensor, dims, split_sizes):
+        self.saved = saved
+        self.dims = dims
+        self.split_sizes = list(int(s) for s in split_sizes)
+
+
+def _byte_buffer(nbytes: int, device):
+    # 256-byte aligned (the caching allocator aligns to at least 512 bytes)
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def grouped_mlp_fwd(x, probs, w1, w2, split_sizes, *, training: bool = True, workspace=None,
+                    out=None, stream=None):
+    """Fused grouped MLP forward. x [R,H] bf16, w1 [E,2F,H] bf16, w2 [E,H,F] bf16,
+    probs [R] fp32 or None. Returns (y [R,H] bf16, MLPState or None)."""
+    L = load()
+    R, H = x.shape
+    E, F2, _ = w1.shape
+    F = F2 // 2
+    fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
+    if workspace is None or workspace.numel() < fws:
+        workspace = _byte_buffer(fws, x.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x.device) if out is None else out
+    saved = _byte_buffer(sv, x.device) if training else None
+    _check(L.grouped_mlp_fwd(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes), _ptr(x),
+                             _ptr(probs), _ptr(w1), _ptr(w2), _ptr(y), _ptr(saved),
+                             0 if saved is None else saved.numel(), _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
+    state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
+    return y, state
+
+
+def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulate: bool = False,
+                    want_dprobs: bool = True, workspace=None, stream=None):
+    """Fused grouped MLP backward. Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32).
+    With accumulate=True, dw1/dw2 (fp32 main grads) are added into."""
+    L = load()
+    E, R, H, F = state.dims
+    _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
+    if workspace is None or workspace.numel() < bws:
+        workspace = _byte_buffer(bws, dy.device)
+    dev = dy.device
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dprobs = torch.empty((R,), dtype=torch.float32, device=dev) if want_dprobs else None
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, H), dtype=torch.float32, device=dev)
+        accumulate = False if dw2 is None else accumulate
+    if dw2 is None:
+        dw2 = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    _check(L.grouped_mlp_bwd(ctypes.byref(_dims(E, R, H, F)), _i64_array(state.split_sizes),
+                             _ptr(dy), _ptr(probs), _ptr(state.saved), state.saved.numel(),
+                             _ptr(dx), _ptr(dprobs), _ptr(dw1), _ptr(dw2), int(accumulate),
+                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dx, dprobs, dw1, dw2
+
+
+_event_arrays = []   # keeps the handle arrays alive while the library holds them
+
+
+def set_stage_events(events):
+    """Record torch.cuda.Event objects at the stage boundaries of the next fused
+    MLP calls on this thread (events[i] before stage i and after the last);
+    None switches stage timing off."""
+    L = load()
+    if not events:
+        _check(L.mx_set_stage_events(None, 0))
+        _event_arrays.clear()
+        return
+    handles = [e.cuda_event for e in events]
+    if not all(handles):
+        raise ValueError("record each event once before handing it to set_stage_events "
+                         "(torch creates the HIP event on first record)")
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(h) for h in handles])
+    _event_arrays.append(arr)
+    if len(_event_arrays) > 4:
+        del _event_arrays[0]
+    _check(L.mx_set_stage_events(arr, len(events)))
+
+
+class MLPRunner:
+    """Preallocated fused-MLP training step (no allocation per call): owns the
+    workspaces, the saved buffer and the outputs for one shape and split."""
+
+    def __init__(self, E: int, R: int, H: int, F: int, split_sizes, device="cuda"):
+        self.dims = (int(E), int(R), int(H), int(F))
+        self.split = [int(s) for s in split_sizes]
+        fws, sv, bws = mlp_sizes(E, R, H, F, self.split)
+        self.fwd_ws = _byte_buffer(fws, device)
+        self.saved = _byte_buffer(sv, device)
+        self.bwd_ws = _byte_buffer(bws, device)
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.dx = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.dprobs = torch.empty((R,), dtype=torch.float32, device=device)
+        self._c_dims = _dims(E, R, H, F)
+        self._c_split = _i64_array(self.split)
+
+    def forward(self, x, probs, w1, w2, training=True, stream=None):
+        L = load()
+        saved = self.saved if training else None
+        _check(L.grouped_mlp_fwd(ctypes.byref(self._c_dims), self._c_split, _ptr(x), _ptr(probs),
+                                 _ptr(w1), _ptr(w2), _ptr(self.y), _ptr(saved),
+                                 0 if saved is None else saved.numel(), _ptr(self.fwd_ws),
+                                 self.fwd_ws.numel(), _stream(stream)))
+        return self.y
+
+    def backward(self, dy, probs, dw1, dw2, accumulate=True, want_dprobs=True, stream=None):
+        L = load()
+        _check(L.grouped_mlp_bwd(ctypes.byref(self._c_dims), self._c_split, _ptr(dy), _ptr(probs),
+                                 _ptr(self.saved), self.saved.numel(), _ptr(self.dx),
+                                 _ptr(self.dprobs) if want_dprobs else None, _ptr(dw1), _ptr(dw2),
+                                 int(accumulate), _ptr(self.bwd_ws), self.bwd_ws.numel(),
+                                 _stream(stream)))
+        return self.dx, (self.dprobs if want_dprobs else None)
+
+
+class GroupedMLP(torch.autograd.Function):
+    """y = GroupedMLP.apply(x, probs, w1, w2, split_sizes): the fused MXFP8
+    grouped MLP with a fused backward (gradients for x, probs, w1, w2)."""
+
+    @staticmethod
+    def forward(ctx, x, probs, w1, w2, split_sizes):
+        y, state = grouped_mlp_fwd(x.contiguous(), probs, w1.contiguous(), w2.contiguous(),
+                                   list(split_sizes), training=True)
+        ctx.state = state
+        ctx.save_for_backward(probs)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (probs,) = ctx.saved_tensors
+        dx, dprobs, dw1, dw2 = grouped_mlp_bwd(dy.contiguous(), probs, ctx.state,
+                                               want_dprobs=probs is not None)
+        return dx, dprobs, dw1, dw2, None

@@ -1,0 +1,470 @@
+// Host side of the C ABI declared in include/mxfp8.h: argument validation
+// (before anything is enqueued), group/tile planning from the host
+// split_sizes, buffer layout of the fused MLP, and kernel launches on the
+// caller's stream. No device memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "mx_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local void* const* g_events = nullptr;   // optional stage-timing events
+thread_local int32_t g_n_events = 0;
+
+void stage_mark(int i, hipStream_t stream) {
+  if (g_events != nullptr && i < g_n_events && g_events[i] != nullptr)
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(g_events[i]), stream);
+}
+
+mx_status fail(mx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mx_status hip_fail(hipError_t e, const char* what) {
+  return fail(MX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kI32Max = 0x7FFFFFFF;
+
+int64_t pad32(int64_t m) { return (m + 31) / 32 * 32; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- quantize
+mx_status check_groups(const int64_t* sizes, int32_t n, int64_t rows, const char* who) {
+  if (n < 0) return fail(MX_EINVAL, "%s: negative group count", who);
+  if (n > mx::kMaxGroups) return fail(MX_EUNSUPPORTED, "%s: %d groups exceeds the maximum %d", who, n, mx::kMaxGroups);
+  if (n > 0 && sizes == nullptr) return fail(MX_EINVAL, "%s: group sizes pointer is null", who);
+  int64_t s = 0;
+  for (int32_t g = 0; g < n; ++g) {
+    if (sizes[g] < 0) return fail(MX_ESHAPE, "%s: group %d has negative size %lld", who, g, (long long)sizes[g]);
+    s += sizes[g];
+  }
+  if (n > 0 && s != rows) return fail(MX_ESHAPE, "%s: group sizes sum to %lld, expected %lld", who, (long long)s, (long long)rows);
+  return MX_OK;
+}
+
+mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
+                        int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                        hipStream_t stream) {
+  const char* who = "mx_quantize";
+  if (x == nullptr) return fail(MX_EINVAL, "%s: x is null", who);
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return fail(MX_EINVAL, "%s: unsupported dtype %d", who, x_dtype);
+  if ((q_row == nullptr) != (s_row == nullptr)) return fail(MX_EINVAL, "%s: rowwise codes and scales must both be given or both null", who);
+  if ((q_col == nullptr) != (s_col == nullptr)) return fail(MX_EINVAL, "%s: columnwise codes and scales must both be given or both null", who);
+  if (q_row == nullptr && q_col == nullptr) return fail(MX_EINVAL, "%s: no output requested", who);
+  if (rows < 0 || cols <= 0) return fail(MX_ESHAPE, "%s: bad shape [%lld, %lld]", who, (long long)rows, (long long)cols);
+  if (cols % 32) return fail(MX_ESHAPE, "%s: cols=%lld is not a multiple of 32", who, (long long)cols);
+  if (rows > kI32Max || cols > kI32Max) return fail(MX_EUNSUPPORTED, "%s: dimension exceeds 2^31-1", who);
+  if (num_groups == 0 && group_sizes != nullptr) return fail(MX_EINVAL, "%s: group sizes given with num_groups == 0", who);
+  mx_status st = check_groups(group_sizes, num_groups, rows, who);
+  if (st != MX_OK) return st;
+  if (!aligned(x, 16) || (q_row && !aligned(q_row, 16)) || (q_col && !aligned(q_col, 16)))
+    return fail(MX_EALIGN, "%s: x, q_row and q_col must be 16-byte aligned", who);
+
+  mx::QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.q_row = q_row;
+  a.s_row = s_row;
+  a.q_col = q_col;
+  a.s_col = s_col;
+  a.cols = cols;
+  const int n = num_groups > 0 ? num_groups : 1;
+  a.groups.n = n;
+  int64_t r0 = 0, p0 = 0, t0 = 0;
+  for (int g = 0; g < n; ++g) {
+    const int64_t m = num_groups > 0 ? group_sizes[g] : rows;
+    a.groups.row0[g] = (int32_t)r0;
+    a.groups.pcol0[g] = (int32_t)p0;
+    a.groups.tile0[g] = (int32_t)t0;
+    r0 += m;
+    p0 += pad32(m);
+    t0 += cdiv(m, mx::kQuantTileRows);
+  }
+  a.groups.row0[n] = (int32_t)r0;
+  a.groups.pcol0[n] = (int32_t)p0;
+  a.groups.tile0[n] = (int32_t)t0;
+  if (p0 > kI32Max) return fail(MX_EUNSUPPORTED, "%s: padded rows exceed 2^31-1", who);
+  a.ld_col = p0;
+  a.n_col_tiles = (int32_t)cdiv(cols, mx::quant_tile_cols(x_dtype));
+  if (t0 * a.n_col_tiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many tiles", who);
+  hipError_t e = mx::launch_quantize(a, x_dtype, (int)t0, stream);
+  if (e != hipSuccess) return hip_fail(e, "mx_quantize launch");
+  return MX_OK;
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+struct GemmPlan {
+  mx::GemmArgs args;
+  int total_tiles;
+  bool scale_dword;
+};
+
+mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, int64_t N, int64_t K,
+                    const uint8_t* a, const uint8_t* as, int64_t lda, const uint8_t* b, const uint8_t* bs,
+                    int64_t ldb, int64_t b_group_stride, void* c, int32_t c_dtype, int64_t ldc,
+                    int64_t c_group_stride, int32_t accumulate, int epi, int64_t n_rows_b, GemmPlan* plan) {
+  const char* who = "mx_grouped_gemm";
+  if (mode != MX_GROUP_M && mode != MX_GROUP_K) return fail(MX_EINVAL, "%s: bad mode %d", who, mode);
+  if (G < 1) return fail(MX_EINVAL, "%s: need at least one group", who);
+  if (G > mx::kMaxGroups) return fail(MX_EUNSUPPORTED, "%s: %d groups exceeds the maximum %d", who, G, mx::kMaxGroups);
+  if (!sizes) return fail(MX_EINVAL, "%s: sizes is null", who);
+  if (!a || !as || !b || !bs || !c) return fail(MX_EINVAL, "%s: null operand pointer", who);
+  if (c_dtype != MX_F32 && c_dtype != MX_BF16) return fail(MX_EINVAL, "%s: bad output dtype %d", who, c_dtype);
+  if (accumulate && c_dtype != MX_F32) return fail(MX_EUNSUPPORTED, "%s: accumulate needs an fp32 output", who);
+  if (M < 0 || N <= 0 || K < 0) return fail(MX_ESHAPE, "%s: bad sizes M=%lld N=%lld K=%lld", who, (long long)M, (long long)N, (long long)K);
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return fail(MX_EUNSUPPORTED, "%s: dimension exceeds 2^31-1", who);
+  if (K % 32 || N % 32) return fail(MX_ESHAPE, "%s: K and N must be multiples of 32 (K=%lld N=%lld)", who, (long long)K, (long long)N);
+  if (lda % 32 || ldb % 32 || lda < K || ldb < K) return fail(MX_ESHAPE, "%s: lda/ldb must be multiples of 32 and >= K", who);
+  if (ldc < N || ldc % 4) return fail(MX_ESHAPE, "%s: ldc must be >= N and a multiple of 4", who);
+  if (b_group_stride < 0 || b_group_stride % 32) return fail(MX_ESHAPE, "%s: b_group_stride must be a non-negative multiple of 32", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
+  // the kernels address one B group and one 256-row A tile with 32-bit offsets
+  if (N * ldb >= (int64_t(1) << 32) || int64_t(mx::kTileM) * lda >= (int64_t(1) << 32))
+    return fail(MX_EUNSUPPORTED, "%s: one B group or A tile exceeds 4 GiB", who);
+  int64_t sum = 0, sumP = 0;
+  for (int g = 0; g < G; ++g) {
+    if (sizes[g] < 0) return fail(MX_ESHAPE, "%s: group %d has negative size", who, g);
+    sum += sizes[g];
+    sumP += pad32(sizes[g]);
+  }
+  if (mode == MX_GROUP_M && sum != M) return fail(MX_ESHAPE, "%s: sizes sum to %lld, expected M=%lld", who, (long long)sum, (long long)M);
+  if (mode == MX_GROUP_K && sumP != K) return fail(MX_ESHAPE, "%s: padded sizes sum to %lld, expected K=%lld", who, (long long)sumP, (long long)K);
+  if (mode == MX_GROUP_K && c_group_stride < 0) return fail(MX_ESHAPE, "%s: negative c_group_stride", who);
+
+  GemmPlan& p = *plan;
+  memset(&p.args, 0, sizeof(p.args));
+  mx::GemmArgs& A = p.args;
+  A.a = a; A.as = as; A.b = b; A.bs = bs; A.c = c;
+  A.lda = lda; A.ldb = ldb; A.ldc = ldc;
+  A.b_group_stride = b_group_stride;
+  A.c_group_stride = c_group_stride;
+  A.M = (int32_t)M; A.N = (int32_t)N; A.K = (int32_t)K;
+  A.accumulate = accumulate;
+  const int64_t tiles_n = epi == mx::EPI_SWIGLU_FWD ? cdiv(N / 2, mx::kTileN / 2) : cdiv(N, mx::kTileN);
+  A.n_tiles_n = (int32_t)tiles_n;
+  (void)n_rows_b;
+  // slot order: group-M keeps expert order and drops empty groups; group-K puts
+  // the longest contractions first so the tail of the launch is short.
+  std::vector<int> order;
+  for (int g = 0; g < G; ++g)
+    if (mode == MX_GROUP_K || sizes[g] > 0) order.push_back(g);
+  if (mode == MX_GROUP_K)
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return sizes[x] > sizes[y]; });
+  std::vector<int64_t> r0(G + 1, 0), p0(G + 1, 0);
+  for (int g = 0; g < G; ++g) { r0[g + 1] = r0[g] + sizes[g]; p0[g + 1] = p0[g] + pad32(sizes[g]); }
+  int64_t t = 0;
+  A.groups.n = (int32_t)order.size();
+  for (size_t s = 0; s < order.size(); ++s) {
+    const int g = order[s];
+    A.groups.tile0[s] = (int32_t)t;
+    A.groups.gid[s] = g;
+    A.groups.pc0[s] = (int32_t)p0[g];
+    if (mode == MX_GROUP_M) {
+      A.groups.a0[s] = (int32_t)r0[g];
+      A.groups.len[s] = (int32_t)sizes[g];
+      t += cdiv(sizes[g], mx::kTileM) * tiles_n;
+    } else {
+      A.groups.a0[s] = (int32_t)p0[g];
+      A.groups.len[s] = (int32_t)pad32(sizes[g]);
+      t += cdiv(M, mx::kTileM) * tiles_n;
+    }
+  }
+  A.groups.tile0[order.size()] = (int32_t)t;
+  if (t > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many tiles", who);
+  p.total_tiles = (int)t;
+  // whole-dword scale loads: every k tile starts at a multiple of 4 blocks
+  p.scale_dword = mode == MX_GROUP_M && K % 128 == 0 && lda % 128 == 0 && ldb % 128 == 0 &&
+                  b_group_stride % 128 == 0 && aligned(as, 4) && aligned(bs, 4);
+  if (M == 0 || (mode == MX_GROUP_M && sum == 0)) p.total_tiles = 0;
+  return MX_OK;
+}
+
+// ---------------------------------------------------------------- fused MLP plan
+struct MlpLayout {
+  int E;
+  int64_t R, H, F, sumP;
+  std::vector<int64_t> split;
+  // forward workspace
+  size_t xq, xs, w1q, w1s, w2q, w2s, aq, as, fwd_total;
+  // saved for backward
+  size_t xcq, xcs, h1, acq, acs, w1cq, w1cs, w2cq, w2cs, saved_total;
+  // backward workspace
+  size_t dyq, dys, dycq, dycs, dhq, dhs, dhcq, dhcs, part, bwd_total;
+  int64_t n_tiles_f;
+};
+
+size_t take(size_t& cur, size_t bytes) {
+  const size_t at = cur;
+  cur += (bytes + 255) / 256 * 256;
+  return at;
+}
+
+mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, const char* who) {
+  if (!d) return fail(MX_EINVAL, "%s: dims is null", who);
+  if (d->num_experts < 1) return fail(MX_EINVAL, "%s: need at least one expert", who);
+  if (d->num_experts > mx::kMaxGroups) return fail(MX_EUNSUPPORTED, "%s: %d experts exceeds the maximum %d", who, d->num_experts, mx::kMaxGroups);
+  if (!split) return fail(MX_EINVAL, "%s: split_sizes is null", who);
+  if (d->rows < 0 || d->hidden <= 0 || d->ffn <= 0) return fail(MX_ESHAPE, "%s: bad dims", who);
+  if (d->hidden % 32 || d->ffn % 32) return fail(MX_ESHAPE, "%s: hidden and ffn must be multiples of 32", who);
+  if (d->rows > kI32Max || 2 * d->ffn > kI32Max || (int64_t)d->num_experts * 2 * d->ffn > kI32Max ||
+      (int64_t)d->num_experts * d->hidden > kI32Max)
+    return fail(MX_EUNSUPPORTED, "%s: dimensions exceed 2^31-1", who);
+  mx_status st = check_groups(split, d->num_experts, d->rows, who);
+  if (st != MX_OK) return st;
+  L->E = d->num_experts;
+  L->R = d->rows;
+  L->H = d->hidden;
+  L->F = d->ffn;
+  L->split.assign(split, split + d->num_experts);
+  L->sumP = 0;
+  for (int e = 0; e < L->E; ++e) L->sumP += pad32(split[e]);
+  const int64_t R = L->R, H = L->H, F = L->F, E = L->E, P = L->sumP;
+  size_t c = 0;
+  L->xq = take(c, R * H); L->xs = take(c, R * H / 32);
+  L->w1q = take(c, E * 2 * F * H); L->w1s = take(c, E * 2 * F * H / 32);
+  L->w2q = take(c, E * H * F); L->w2s = take(c, E * H * F / 32);
+  L->aq = take(c, R * F); L->as = take(c, R * F / 32);
+  L->fwd_total = c;
+  c = 0;
+  L->xcq = take(c, H * P); L->xcs = take(c, H * P / 32);
+  L->h1 = take(c, R * 2 * F * 2);
+  L->acq = take(c, F * P); L->acs = take(c, F * P / 32);
+  L->w1cq = take(c, H * E * 2 * F); L->w1cs = take(c, H * E * 2 * F / 32);
+  L->w2cq = take(c, F * E * H); L->w2cs = take(c, F * E * H / 32);
+  L->saved_total = c;
+  c = 0;
+  L->n_tiles_f = cdiv(F, mx::kTileN);
+  L->dyq = take(c, R * H); L->dys = take(c, R * H / 32);
+  L->dycq = take(c, H * P); L->dycs = take(c, H * P / 32);
+  L->dhq = take(c, R * 2 * F); L->dhs = take(c, R * 2 * F / 32);
+  L->dhcq = take(c, 2 * F * P); L->dhcs = take(c, 2 * F * P / 32);
+  L->part = take(c, L->n_tiles_f * R * 4);
+  L->bwd_total = c;
+  return MX_OK;
+}
+
+uint8_t* at(void* base, size_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
+const uint8_t* at(const void* base, size_t off) { return reinterpret_cast<const uint8_t*>(base) + off; }
+
+mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, const char* what) {
+  hipError_t e = mx::launch_gemm(mode, epi, p.scale_dword, p.args, p.total_tiles, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(int s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_EINVAL: return "MX_EINVAL";
+    case MX_ESHAPE: return "MX_ESHAPE";
+    case MX_EALIGN: return "MX_EALIGN";
+    case MX_EWORKSPACE: return "MX_EWORKSPACE";
+    case MX_EHIP: return "MX_EHIP";
+    case MX_EUNSUPPORTED: return "MX_EUNSUPPORTED";
+    default: return "MX_UNKNOWN";
+  }
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+mx_status mx_set_stage_events(void* const* events, int32_t count) {
+  g_err[0] = 0;
+  if (count < 0 || (count > 0 && events == nullptr))
+    return fail(MX_EINVAL, "mx_set_stage_events: bad event array");
+  g_events = count > 0 ? events : nullptr;
+  g_n_events = count;
+  return MX_OK;
+}
+
+int mx_version(void) { return 1; }
+
+mx_status mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
+                      int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                      void* stream) {
+  g_err[0] = 0;
+  return quantize_impl(x, x_dtype, rows, cols, group_sizes, num_groups, q_row, s_row, q_col, s_col,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status mx_grouped_gemm(int32_t mode, int32_t num_groups, const int64_t* sizes, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* a, const uint8_t* a_scale, int64_t lda, const uint8_t* b,
+                          const uint8_t* b_scale, int64_t ldb, int64_t b_group_stride, void* c, int32_t c_dtype,
+                          int64_t ldc, int64_t c_group_stride, int32_t accumulate, void* stream) {
+  g_err[0] = 0;
+  GemmPlan p;
+  const int epi = c_dtype == MX_BF16 ? mx::EPI_BF16 : mx::EPI_F32;
+  mx_status st = gemm_plan(mode, num_groups, sizes, M, N, K, a, a_scale, lda, b, b_scale, ldb, b_group_stride, c,
+                           c_dtype, ldc, c_group_stride, accumulate, epi, N, &p);
+  if (st != MX_OK) return st;
+  return run_gemm(p, mode, epi, reinterpret_cast<hipStream_t>(stream), "mx_grouped_gemm launch");
+}
+
+mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes, size_t* fwd_workspace,
+                            size_t* saved, size_t* bwd_workspace) {
+  g_err[0] = 0;
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, "grouped_mlp_sizes");
+  if (st != MX_OK) return st;
+  if (fwd_workspace) *fwd_workspace = L.fwd_total;
+  if (saved) *saved = L.saved_total;
+  if (bwd_workspace) *bwd_workspace = L.bwd_total;
+  return MX_OK;
+}
+
+mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x, const float* probs,
+                          const void* w1, const void* w2, void* y, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream_) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  if (!x || !w1 || !w2 || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+      (saved && !aligned(saved, 256)) || (probs && !aligned(probs, 4)))
+    return fail(MX_EALIGN, "%s: x, w1, w2, y must be 16-byte and workspace/saved 256-byte aligned", who);
+  if (workspace_bytes < L.fwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
+  if (saved && saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int64_t R = L.R, H = L.H, F = L.F;
+  const int E = L.E;
+  std::vector<int64_t> g_w1(E, 2 * F), g_w2(E, H);
+  // plan both GEMMs before launching anything
+  GemmPlan p1, p2;
+  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, 2 * F, H, at(workspace, L.xq), at(workspace, L.xs), H,
+                 at(workspace, L.w1q), at(workspace, L.w1s), H, 2 * F * H, y, MX_BF16, 2 * F, 0, 0,
+                 mx::EPI_SWIGLU_FWD, 2 * F, &p1);
+  if (st != MX_OK) return st;
+  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, H, F, at(workspace, L.aq), at(workspace, L.as), F,
+                 at(workspace, L.w2q), at(workspace, L.w2s), F, H * F, y, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &p2);
+  if (st != MX_OK) return st;
+  mx::GemmArgs& a1 = p1.args;
+  a1.c = nullptr;
+  a1.F = (int32_t)F;
+  a1.ld_col = L.sumP;
+  a1.probs = probs;
+  a1.h1 = saved ? reinterpret_cast<uint16_t*>(at(saved, L.h1)) : nullptr;
+  a1.q_row = at(workspace, L.aq);
+  a1.s_row = at(workspace, L.as);
+  a1.q_col = saved ? at(saved, L.acq) : nullptr;
+  a1.s_col = saved ? at(saved, L.acs) : nullptr;
+  a1.R = (int32_t)R;
+
+  stage_mark(0, stream);
+  st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
+                     saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream);
+  if (st != MX_OK) return st;
+  stage_mark(1, stream);
+  st = quantize_impl(w1, MX_BF16, E * 2 * F, H, g_w1.data(), E, at(workspace, L.w1q), at(workspace, L.w1s),
+                     saved ? at(saved, L.w1cq) : nullptr, saved ? at(saved, L.w1cs) : nullptr, stream);
+  if (st != MX_OK) return st;
+  stage_mark(2, stream);
+  st = quantize_impl(w2, MX_BF16, E * H, F, g_w2.data(), E, at(workspace, L.w2q), at(workspace, L.w2s),
+                     saved ? at(saved, L.w2cq) : nullptr, saved ? at(saved, L.w2cs) : nullptr, stream);
+  if (st != MX_OK) return st;
+  stage_mark(3, stream);
+  st = run_gemm(p1, MX_GROUP_M, mx::EPI_SWIGLU_FWD, stream, "grouped_mlp_fwd gemm1");
+  if (st != MX_OK) return st;
+  stage_mark(4, stream);
+  st = run_gemm(p2, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_fwd gemm2");
+  if (st != MX_OK) return st;
+  stage_mark(5, stream);
+  return MX_OK;
+}
+
+mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy, const float* probs,
+                          const void* saved, size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                          int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream_) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  if (!dy || !saved || !dx || !dw1 || !dw2 || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(saved, 256) ||
+      !aligned(workspace, 256) || (probs && !aligned(probs, 4)) || (dprobs && !aligned(dprobs, 4)))
+    return fail(MX_EALIGN, "%s: dy, dx, dw1, dw2 must be 16-byte and saved/workspace 256-byte aligned", who);
+  if (saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  if (workspace_bytes < L.bwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.bwd_total);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int64_t R = L.R, H = L.H, F = L.F, P = L.sumP;
+  const int E = L.E;
+  GemmPlan pd2, pw2, pd1, pw1;
+  // dA = dY_row . colwise(W2_e): B_e = w2 columnwise [F, E*H] at column e*H
+  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, F, H, at(workspace, L.dyq), at(workspace, L.dys), H,
+                 at(saved, L.w2cq), at(saved, L.w2cs), E * H, H, dx, MX_BF16, F, 0, 0, mx::EPI_SWIGLU_BWD, F, &pd2);
+  if (st != MX_OK) return st;
+  // dW2_e = colwise(dY_e) . colwise(A_e)^T
+  st = gemm_plan(MX_GROUP_K, E, L.split.data(), H, F, P, at(workspace, L.dycq), at(workspace, L.dycs), P,
+                 at(saved, L.acq), at(saved, L.acs), P, 0, dw2, MX_F32, F, H * F, accumulate_wgrad, mx::EPI_F32, F, &pw2);
+  if (st != MX_OK) return st;
+  // dX = dH1_row . colwise(W1_e): B_e = w1 columnwise [H, E*2F] at column e*2F
+  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, H, 2 * F, at(workspace, L.dhq), at(workspace, L.dhs), 2 * F,
+                 at(saved, L.w1cq), at(saved, L.w1cs), E * 2 * F, 2 * F, dx, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &pd1);
+  if (st != MX_OK) return st;
+  // dW1_e = colwise(dH1_e) . colwise(X_e)^T
+  st = gemm_plan(MX_GROUP_K, E, L.split.data(), 2 * F, H, P, at(workspace, L.dhcq), at(workspace, L.dhcs), P,
+                 at(saved, L.xcq), at(saved, L.xcs), P, 0, dw1, MX_F32, H, 2 * F * H, accumulate_wgrad, mx::EPI_F32,
+                 H, &pw1);
+  if (st != MX_OK) return st;
+  mx::GemmArgs& a = pd2.args;
+  a.c = nullptr;
+  a.F = (int32_t)F;
+  a.ld_col = P;
+  a.probs = probs;
+  a.h1 = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(at(saved, L.h1)));
+  a.q_row = at(workspace, L.dhq);
+  a.s_row = at(workspace, L.dhs);
+  a.q_col = at(workspace, L.dhcq);
+  a.s_col = at(workspace, L.dhcs);
+  a.dprobs_part = dprobs ? reinterpret_cast<float*>(at(workspace, L.part)) : nullptr;
+  a.R = (int32_t)R;
+
+  stage_mark(0, stream);
+  st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
+                     at(workspace, L.dycq), at(workspace, L.dycs), stream);
+  if (st != MX_OK) return st;
+  stage_mark(1, stream);
+  st = run_gemm(pd2, MX_GROUP_M, mx::EPI_SWIGLU_BWD, stream, "grouped_mlp_bwd dgrad2");
+  if (st != MX_OK) return st;
+  stage_mark(2, stream);
+  if (dprobs) {
+    hipError_t e = mx::launch_dprobs_reduce(reinterpret_cast<const float*>(at(workspace, L.part)), dprobs,
+                                            (int32_t)R, (int32_t)L.n_tiles_f, stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dprobs");
+  }
+  stage_mark(3, stream);
+  st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad2");
+  if (st != MX_OK) return st;
+  stage_mark(4, stream);
+  st = run_gemm(pd1, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_bwd dgrad1");
+  if (st != MX_OK) return st;
+  stage_mark(5, stream);
+  st = run_gemm(pw1, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad1");
+  if (st != MX_OK) return st;
+  stage_mark(6, stream);
+  return MX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device helpers shared by the MXFP8 kernels (gfx950).
+//
+// The block quantizer here is the one routine used by the standalone quantize
+// kernel and by the GEMM epilogues that requantize fp32 intermediates, so both
+// produce identical codes for identical inputs.
+//
+// MXFP8 block rule (one E8M0 scale per 32 consecutive values, E4M3 elements:
+// "Efficient MoE training for biological foundation models", Key technical
+// approaches item 2), with the scale exponent e = floor(log2 amax) - 8 clamped
+// to [-127, 127] and saturating round-to-nearest-even elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// E8M0 scale code of a block from the bit pattern of its |amax| (finite fp32).
+// floor(log2 amax) = biased exponent - 127 for normal amax, so
+// code = e + 127 = biased - 8, clamped at 0; subnormal or zero amax -> 0.
+__device__ __forceinline__ uint32_t scale_code_from_amax_bits(uint32_t amax_bits) {
+  uint32_t eb = amax_bits >> 23;
+  return eb > 8u ? eb - 8u : 0u;
+}
+
+// 2^(-e) = 2^(127 - code) as an fp32 (always a normal number for code <= 246).
+__device__ __forceinline__ float inv_scale_from_code(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
+__device__ __forceinline__ float clamp448(float t) {
+  return fminf(fmaxf(t, -448.0f), 448.0f);
+}
+
+// Four fp32 values (already divided by the block scale) -> four E4M3 codes in
+// one dword (byte i = value i). The hardware convert rounds to nearest even
+// and keeps the sign of zero; clamping to +-448 first makes it saturating.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float v) {
+  return __float_as_uint(v) & 0x7FFFFFFFu;
+}
+
+// bf16 <-> fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Cross-lane helpers (64-wide wavefront).
+__device__ __forceinline__ uint32_t xor_u32(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, 64);
+}
+__device__ __forceinline__ float xor_f32(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps
+// register-array indices constant however large the body is.
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
+}
+
+}  // namespace mx

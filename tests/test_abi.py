@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status before
+anything is enqueued (all of these return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_mx_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.lib_path()):
+        pytest.skip("library not built")
+    return mx.load()
+
+
+def test_exports_every_declared_symbol(L):
+    decl = re.findall(r"MX_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(HEADER).read())
+    assert set(decl) >= {"mx_quantize", "mx_grouped_gemm", "grouped_mlp_fwd", "grouped_mlp_bwd",
+                         "grouped_mlp_sizes", "mx_status_string", "mx_last_error", "mx_version"}
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.mx_version() == 1
+    assert L.mx_status_string(ESHAPE) == b"MX_ESHAPE"
+
+
+FAKE = ctypes.c_void_p(0x100000)       # never dereferenced: validation fails first
+
+
+def _q(L, x=FAKE, dt=0, rows=64, cols=64, gs=None, ng=0, qr=FAKE, sr=FAKE, qc=None, sc=None):
+    return L.mx_quantize(x, dt, rows, cols, gs, ng, qr, sr, qc, sc, None)
+
+
+def test_quantize_argument_errors(L):
+    assert _q(L, x=None) == EINVAL
+    assert _q(L, dt=7) == EINVAL
+    assert _q(L, qr=None, sr=None) == EINVAL                   # nothing requested
+    assert _q(L, sr=None) == EINVAL                            # half a pair
+    assert _q(L, cols=48) == ESHAPE                            # cols % 32
+    assert _q(L, cols=0) == ESHAPE
+    assert _q(L, rows=-1) == ESHAPE
+    assert _q(L, gs=mx._i64_array([30, 30]), ng=2) == ESHAPE   # sum != rows
+    assert _q(L, gs=mx._i64_array([80, -16]), ng=2) == ESHAPE
+    assert _q(L, gs=mx._i64_array([1] * 200), ng=200, rows=200) == EUNSUPPORTED
+    assert _q(L, x=ctypes.c_void_p(0x100008)) == EALIGN
+    assert b"mx_quantize" in L.mx_last_error()
+
+
+def _g(L, mode=0, G=2, sizes=(32, 32), M=64, N=64, K=64, lda=64, ldb=64, bgs=4096, c_dt=1,
+       ldc=64, cgs=0, acc=0, a=FAKE, c=FAKE):
+    return L.mx_grouped_gemm(mode, G, mx._i64_array(sizes), M, N, K, a, FAKE, lda, FAKE, FAKE, ldb,
+                             bgs, c, c_dt, ldc, cgs, acc, None)
+
+
+def test_gemm_argument_errors(L):
+    assert _g(L, mode=5) == EINVAL
+    assert _g(L, G=0) == EINVAL
+    assert _g(L, G=129, sizes=[0] * 129) == EUNSUPPORTED
+    assert _g(L, a=None) == EINVAL
+    assert _g(L, c_dt=4) == EINVAL
+    assert _g(L, acc=1, c_dt=0) == EUNSUPPORTED                 # bf16 accumulate
+    assert _g(L, K=48) == ESHAPE
+    assert _g(L, N=48, ldc=48) == ESHAPE
+    assert _g(L, lda=32) == ESHAPE                              # lda < K
+    assert _g(L, ldc=32) == ESHAPE
+    assert _g(L, sizes=(32, 16)) == ESHAPE                      # sum != M
+    assert _g(L, bgs=48) == ESHAPE
+    assert _g(L, mode=1, sizes=(40, 20), K=64) == ESHAPE        # sum of padded sizes is 96
+    assert _g(L, a=ctypes.c_void_p(0x100004)) == EALIGN
+
+
+def _dims(E=2, R=64, H=64, F=96):
+    return mx._Dims(E, R, H, F)
+
+
+def test_mlp_sizes_and_errors(L):
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    d = _dims()
+    assert L.grouped_mlp_sizes(ctypes.byref(d), mx._i64_array([40, 24]), ctypes.byref(f),
+                               ctypes.byref(s), ctypes.byref(b)) == OK
+    assert f.value > 0 and s.value > 0 and b.value > 0
+    # sizes grow with R and cover at least the dominant buffers
+    R, H, F, E = 64, 64, 96, 2
+    assert f.value >= E * 2 * F * H + E * H * F + R * H + R * F
+    assert s.value >= R * 2 * F * 2
+    assert L.grouped_mlp_sizes(ctypes.byref(d), mx._i64_array([40, 20]), None, None, None) == ESHAPE
+    assert L.grouped_mlp_sizes(ctypes.byref(_dims(H=48)), mx._i64_array([40, 24]), None, None, None) == ESHAPE
+    assert L.grouped_mlp_sizes(None, mx._i64_array([40, 24]), None, None, None) == EINVAL
+    assert L.grouped_mlp_sizes(ctypes.byref(_dims(E=0)), mx._i64_array([64]), None, None, None) == EINVAL
+    ws = ctypes.c_void_p(0x100000)
+    # workspace too small, then saved too small: rejected before any launch
+    assert L.grouped_mlp_fwd(ctypes.byref(d), mx._i64_array([40, 24]), FAKE, None, FAKE, FAKE, FAKE,
+                             None, 0, ws, f.value - 1, None) == EWORKSPACE
+    assert L.grouped_mlp_fwd(ctypes.byref(d), mx._i64_array([40, 24]), FAKE, None, FAKE, FAKE, FAKE,
+                             ws, s.value - 256, ws, f.value, None) == EWORKSPACE
+    assert L.grouped_mlp_fwd(ctypes.byref(d), mx._i64_array([40, 24]), None, None, FAKE, FAKE, FAKE,
+                             None, 0, ws, f.value, None) == EINVAL
+    assert L.grouped_mlp_fwd(ctypes.byref(d), mx._i64_array([40, 24]), FAKE, None, FAKE, FAKE, FAKE,
+                             None, 0, ctypes.c_void_p(0x100010), f.value, None) == EALIGN
+    assert L.grouped_mlp_bwd(ctypes.byref(d), mx._i64_array([40, 24]), FAKE, None, ws, s.value, FAKE,
+                             None, FAKE, FAKE, 1, ws, b.value - 1, None) == EWORKSPACE
+    assert L.grouped_mlp_bwd(ctypes.byref(d), mx._i64_array([40, 24]), FAKE, None, None, s.value, FAKE,
+                             None, FAKE, FAKE, 1, ws, b.value, None) == EINVAL
+
+
+def test_product_has_no_oracle_dependency():
+    """The product package never imports the test oracle."""
+    pkg = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn

@@ -1,0 +1,144 @@
+"""GPU parity of the fused grouped MLP (grouped_mlp_fwd / grouped_mlp_bwd)
+against the oracle: GroupedLinear -> ScaledSwiGLU -> GroupedLinear with
+routing-weight scaling and its backward ("Efficient MoE training for
+biological foundation models", Key technical approaches item 3).
+
+Bar: normwise relative error <= 2e-2 for Y, dX, dW1, dW2 and dprobs, both
+over the whole output and per expert with rows. Requantized intermediates
+(A, dH1) are computed from fp32 on the GPU and fp64 in the oracle, so a code
+can differ by one step where the two straddle a rounding boundary."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from tests.gpu_util import dev_bf16, dev_f32, rel_norm, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _check_rows(got, want, split, what):
+    assert rel_norm(got, want) <= TOL, what
+    r0 = 0
+    for e, m in enumerate(split):
+        if m:
+            err = rel_norm(got[r0:r0 + m], want[r0:r0 + m])
+            assert err <= TOL, f"{what} expert {e}: {err}"
+        r0 += m
+
+
+def _run(mx, c, training=True, probs=True):
+    x, w1, w2 = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"])
+    p = dev_f32(c["probs"]) if probs else None
+    y, st = mx.grouped_mlp_fwd(x, p, w1, w2, c["split_sizes"].tolist(), training=training)
+    torch.cuda.synchronize()
+    return y, st, p
+
+
+CASES = {
+    "ragged4": dict(seed=30, E=4, H=256, F=384, split=(300, 0, 17, 200)),
+    "two_tiles_ffn": dict(seed=31, E=3, H=512, F=768, split=(257, 33, 190)),
+    "dense_one_expert": dict(seed=32, E=1, H=256, F=512, split=(384,)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward(gpu_lib, name):
+    k = CASES[name]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    y, _, _ = _run(gpu_lib, c, training=False)
+    want = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"])
+    _check_rows(to_np(y), want["y"], k["split"], "y")
+
+
+def test_forward_tiny_workload(gpu_lib):
+    """The tiny MoE workload (256 tokens, top-2 of 4 experts, one expert empty)."""
+    c = wl.make_mlp_inputs(wl.WORKLOADS["tiny_moe_fwd"])
+    y, _, _ = _run(gpu_lib, c, training=False)
+    want = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"])
+    _check_rows(to_np(y), want["y"], c["split_sizes"].tolist(), "y")
+
+
+def test_forward_training_matches_inference(gpu_lib):
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    y1, _, _ = _run(gpu_lib, c, training=False)
+    y2, st, _ = _run(gpu_lib, c, training=True)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert st is not None
+
+
+def test_forward_routing_weight_zero_and_pow2(gpu_lib):
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"], probs="one")
+    y1, _, _ = _run(gpu_lib, c, training=False)
+    c4 = dict(c, probs=np.full_like(c["probs"], 4.0))
+    y4, _, _ = _run(gpu_lib, c4, training=False)
+    # w = 2^k only shifts A's scales, so Y scales exactly
+    assert torch.equal((y1.float() * 4).view(torch.int32), y4.float().view(torch.int32))
+    c0 = dict(c, probs=np.zeros_like(c["probs"]))
+    y0, _, _ = _run(gpu_lib, c0, training=False)
+    assert torch.count_nonzero(y0.float()) == 0
+    # probs=None means weight 1
+    yn, _, _ = _run(gpu_lib, c, training=False, probs=False)
+    assert torch.equal(yn.view(torch.int16), y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["ragged4", "two_tiles_ffn", "dense_one_expert"])
+def test_backward(gpu_lib, name):
+    k = CASES[name]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    y, st, p = _run(gpu_lib, c, training=True)
+    dy = dev_bf16(c["dy"])
+    dx, dprobs, dw1, dw2 = gpu_lib.grouped_mlp_bwd(dy, p, st)
+    torch.cuda.synchronize()
+    fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"])
+    want = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"], c["dy"], fwd)
+    split = list(k["split"])
+    _check_rows(to_np(dx), want["dx"], split, "dx")
+    _check_rows(to_np(dprobs), want["dprobs"], split, "dprobs")
+    g1, g2 = to_np(dw1), to_np(dw2)
+    assert rel_norm(g1, want["dw1"]) <= TOL and rel_norm(g2, want["dw2"]) <= TOL
+    for e, m in enumerate(split):
+        if m:
+            assert rel_norm(g1[e], want["dw1"][e]) <= TOL, f"dw1 expert {e}"
+            assert rel_norm(g2[e], want["dw2"][e]) <= TOL, f"dw2 expert {e}"
+        else:
+            assert np.all(g1[e] == 0) and np.all(g2[e] == 0)
+
+
+def test_backward_accumulates_into_main_grad(gpu_lib):
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    _, st, p = _run(gpu_lib, c, training=True)
+    dy = dev_bf16(c["dy"])
+    E, H, F = k["E"], k["H"], k["F"]
+    base1 = torch.full((E, 2 * F, H), 0.25, device="cuda")
+    base2 = torch.full((E, H, F), -0.5, device="cuda")
+    _, _, dw1, dw2 = gpu_lib.grouped_mlp_bwd(dy, p, st, dw1=base1.clone(), dw2=base2.clone(),
+                                             accumulate=True)
+    _, _, f1, f2 = gpu_lib.grouped_mlp_bwd(dy, p, st)
+    torch.cuda.synchronize()
+    assert torch.allclose(dw1, f1 + base1, rtol=0, atol=1e-6)
+    assert torch.allclose(dw2, f2 + base2, rtol=0, atol=1e-6)
+    assert torch.all(dw1[1] == 0.25) and torch.all(dw2[1] == -0.5)    # empty expert untouched
+
+
+def test_autograd_function(gpu_lib):
+    k = CASES["two_tiles_ffn"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    x = dev_bf16(c["x"]).requires_grad_()
+    w1 = dev_bf16(c["w1"]).requires_grad_()
+    w2 = dev_bf16(c["w2"]).requires_grad_()
+    p = dev_f32(c["probs"]).requires_grad_()
+    y = gpu_lib.GroupedMLP.apply(x, p, w1, w2, list(k["split"]))
+    y.backward(dev_bf16(c["dy"]))
+    torch.cuda.synchronize()
+    fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"])
+    want = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"], c["dy"], fwd)
+    assert rel_norm(to_np(y.detach()), fwd["y"]) <= TOL
+    assert rel_norm(to_np(x.grad), want["dx"]) <= TOL
+    assert rel_norm(to_np(p.grad), want["dprobs"]) <= TOL
+    assert rel_norm(to_np(w1.grad.float()), want["dw1"]) <= TOL
