@@ -76,6 +76,15 @@ __device__ __forceinline__ float xor_f32(float v, int mask) {
 }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Identity move through a VALU DPP instruction (quad_perm 0,1,2,3). Passing
+// accumulator values through it before a plain store keeps the register
+// allocator from treating the accumulators as either-class (AGPR or VGPR)
+// operands of the store, which otherwise makes it evict them inside the
+// main loop.
+__device__ __forceinline__ float vgpr_hop(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xE4, 0xF, 0xF, false));
+}
+
 // Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps
 // register-array indices constant however large the body is.
 template <int I, int N, typename Fn>

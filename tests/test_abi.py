@@ -119,3 +119,12 @@ def test_product_has_no_oracle_dependency():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
+
+
+def test_library_defines_every_kernel_stub(L):
+    """Every kernel the host code launches has its host stub in the library
+    (a host-pass problem in a kernel body silently drops the stub and leaves
+    an undefined symbol that only fails at load time on the GPU machine)."""
+    import subprocess
+    out = subprocess.run(["nm", "-C", "--undefined-only", mx.lib_path()], capture_output=True, text=True).stdout
+    assert "device_stub" not in out, [l for l in out.splitlines() if "device_stub" in l][:5]
