@@ -41,23 +41,39 @@
 
 namespace mx {
 
-constexpr int BM = kTileM, BN = kTileN, BK = kTileK;
+[[maybe_unused]] constexpr int BM = kTileM, BN = kTileN, BK = kTileK;
 constexpr int kThreads = 256;
 constexpr int kBandM = 8;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
 // open; issued through the builtin so the compiler's own waitcnt tracking
 // knows the loads have landed.
-constexpr int kWaitVmcnt0 = 0x0F70;
+[[maybe_unused]] constexpr int kWaitVmcnt0 = 0x0F70;
+// Epilogue staging of columnwise codes in a wave's 32 KB LDS slice: [column]
+// [64 rows] with a 96-byte stride (24 dwords: the 8 columns x 8 quads one
+// ds_write_b32 touches fall in 64 distinct banks); the SwiGLU backward keeps
+// the gate and up halves (128 columns each) kColHalf apart.
+[[maybe_unused]] constexpr int kColStride = 96;
+[[maybe_unused]] constexpr int kColHalf = 128 * kColStride;
 
 struct TileCoord {
   int slot;   // group slot in the table
   int mt, nt; // tile indices within the group
 };
 
+// Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8). Tile
+// ids are handed out in rounds of 8 x kXcdChunk: in each round XCD x takes
+// kXcdChunk consecutive ids, so the tiles running together on one XCD are
+// raster neighbours (they share A and B rows in that XCD's L2) while all XCDs
+// walk the id space at the same pace, which keeps tiles of unequal cost
+// (group-K slots sorted by size) balanced across XCDs. Blocks of the last,
+// partial round keep their own id.
+constexpr int kXcdChunk = 32;
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int round = 8 * kXcdChunk;
+  const int full = total / round * round;
+  if (bid >= full) return bid;
   const int xcd = bid & 7, local = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
+  return (local / kXcdChunk) * round + xcd * kXcdChunk + local % kXcdChunk;
 }
 
 __device__ __forceinline__ TileCoord locate_tile(const GemmGroups& gt, int id, int mode, int M, int n_tiles_n) {
@@ -166,7 +182,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     else
       return (uint32_t)(tc.nt * BN + r0);
   };
-  auto nsub = [&](int s) __attribute__((always_inline)) -> int { return (s < 2 ? 64 * wn + 32 * s : BN / 2 + 64 * wn + 32 * (s - 2)); };
+  // n sub-tile s of this wave: with the SwiGLU pairing s and s+2 are the gate
+  // and up rows of the same 32 ffn columns; otherwise the wave's 4 sub-tiles
+  // are 128 contiguous columns.
+  auto nsub = [&](int s) __attribute__((always_inline)) -> int {
+    if constexpr (EPI == EPI_SWIGLU_FWD) return s < 2 ? 64 * wn + 32 * s : BN / 2 + 64 * wn + 32 * (s - 2);
+    else return (BN / 2) * wn + 32 * s;
+  };
 
   // ---- direct buffer->LDS loads: per k-step each wave fills 8 blocks of 1 KB
   // (8 tile rows) of A and of B; LDS slot = lane, i.e. row r = 8*blk + lane/8
@@ -335,235 +357,324 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   }
 
   // ---------------------------------------------------------------- epilogues
-  // lane holds, for n sub-tile s and m sub-tile mi: m_local = 128*wm + 32*mi + l32,
-  // n_local = nsub(s) + 8*(v/4) + 4*h + (v%4) for v = 0..15.
-  // The per-lane indices are re-derived from an opaque copy of the lane id so
-  // that no epilogue address is computed before (and kept live across) the
-  // main loop.
+  // Lane mapping of the accumulators: for n sub-tile s and m sub-tile mi the
+  // lane holds m_local = 128*wm + 32*mi + l32 and
+  // n_local = nsub(s) + 8*(v/4) + 4*h + v%4 for v = 0..15.
+  // Outputs go through buffer resources based at the wave's first row: the
+  // offsets are 32-bit and rows past the valid ones fall outside the resource,
+  // where stores are dropped and loads return 0. The per-lane indices are
+  // re-derived from an opaque copy of the lane id so that no epilogue address
+  // is computed before (and kept live across) the main loop.
   int lane_e = lane;
   asm volatile("" : "+v"(lane_e));
   {
   const int h = lane_e >> 5;        // shadows of the loop's lane-derived values
   const int l32 = lane_e & 31;
+  const int qb = l32 & 3, qa = l32 >> 2;   // lane within its quad, quad index
   const int tid = wave * 64 + lane_e;
+  const int wrows = max(0, min(BM / 2, a_rows_valid - (BM / 2) * wm));   // valid rows of this wave
+  const int64_t m0 = a_row0 + (BM / 2) * wm;                             // global row of its first row
+  // wave-private 32 KB of LDS: the k-loop's stages are free after its last barrier
+  uint8_t* const slice = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+
+  // 32 E4M3 codes of one row block, 4 dwords per lane (columns 8*vg + 4*h ..
+  // +3): regroup over the half-waves so that lane half h holds columns
+  // 16h .. 16h+15, then store them as one 16-byte run.
+  auto store_row_codes = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, const uint32_t (&q)[4])
+      __attribute__((always_inline)) {
+    const uint32_t r0 = xhalf(q[2], q[0], h), r1 = xhalf(q[3], q[1], h);
+    u32x4 v;
+    if (h) { v.x = r0; v.y = q[2]; v.z = r1; v.w = q[3]; }
+    else   { v.x = q[0]; v.y = r0; v.z = q[1]; v.w = r1; }
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off + 16 * h, 0, 0);
+  };
+  // 32 bf16 values of one row (16 per lane, as above): lanes of the lower half
+  // end with columns 0-7 and 16-23, the upper half with 8-15 and 24-31, so
+  // each of the two stores writes 32 contiguous bytes per row.
+  auto store_row_bf16 = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, const float (&x)[16])
+      __attribute__((always_inline)) {
+    uint32_t p[4][2];
+#pragma unroll
+    for (int vg = 0; vg < 4; ++vg) {
+      p[vg][0] = pack_bf16x2(x[4 * vg], x[4 * vg + 1]);
+      p[vg][1] = pack_bf16x2(x[4 * vg + 2], x[4 * vg + 3]);
+    }
+    const uint32_t e0 = xhalf(p[1][0], p[0][0], h), e1 = xhalf(p[1][1], p[0][1], h);
+    const uint32_t f0 = xhalf(p[3][0], p[2][0], h), f1 = xhalf(p[3][1], p[2][1], h);
+    u32x4 a, b;
+    if (h) { a.x = e0; a.y = e1; a.z = p[1][0]; a.w = p[1][1]; b.x = f0; b.y = f1; b.z = p[3][0]; b.w = p[3][1]; }
+    else   { a.x = p[0][0]; a.y = p[0][1]; a.z = e0; a.w = e1; b.x = p[2][0]; b.y = p[2][1]; b.z = f0; b.w = f1; }
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off + 16 * h, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off + 32 + 16 * h, 0, 0);
+  };
+  // Both MXFP8 layouts of one 32 x 32 block of an fp32 intermediate d (this
+  // lane: row l32 of the block, 16 columns). Rowwise: one scale per row over
+  // the 32 columns (lanes l, l^32), codes stored directly. Columnwise: one
+  // scale per column over the 32 rows (the lanes of a half-wave); the codes are
+  // transposed inside each quad of lanes and staged in LDS as [column][row]
+  // (stride kColStride), to be written out as column runs by flush_cols.
+  auto quantize_block = [&](const float (&d)[16], const __amdgpu_buffer_rsrc_t& rq, uint32_t q_off,
+                            const __amdgpu_buffer_rsrc_t& rs, uint32_t s_off, bool row_store,
+                            uint8_t* stage, const __amdgpu_buffer_rsrc_t& rsc, uint32_t sc_col0,
+                            uint32_t sc_ld, bool col_store) __attribute__((always_inline)) {
+    {
+      uint32_t am = 0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) am = umax(am, abs_bits(d[v]));
+      am = max_halves(am);
+      const uint32_t sc = scale_code_from_amax_bits(am);
+      const float inv = inv_scale_from_code(sc);
+      uint32_t q[4];
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) q[vg] = e4m3x4(d[4 * vg] * inv, d[4 * vg + 1] * inv, d[4 * vg + 2] * inv, d[4 * vg + 3] * inv);
+      if (row_store) {
+        store_row_codes(rq, q_off, q);
+        if (h == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, s_off, 0, 0);
+      }
+    }
+    {
+      uint32_t scv[16];
+      float inv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        scv[v] = scale_code_from_amax_bits(max_lanes32(abs_bits(d[v])));
+        inv[v] = inv_scale_from_code(scv[v]);
+      }
+      // scale of column v is written by lane l32 == v (v < 16)
+      uint32_t ssel = scv[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) ssel = l32 == v ? scv[v] : ssel;
+      if (col_store && l32 < 16)
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)ssel, rsc,
+                                             (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3)) * sc_ld + sc_col0, 0, 0);
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const uint32_t x = e4m3x4(d[4 * vg] * inv[4 * vg], d[4 * vg + 1] * inv[4 * vg + 1],
+                                  d[4 * vg + 2] * inv[4 * vg + 2], d[4 * vg + 3] * inv[4 * vg + 3]);
+        // lane (quad qa, qb) now holds rows 4qa..4qa+3 of column 8vg + 4h + qb
+        const uint32_t y = quad_transpose_bytes(x, qb);
+        *reinterpret_cast<uint32_t*>(stage + (8 * vg + 4 * h + qb) * kColStride + 4 * qa) = y;
+      }
+    }
+  };
+  // Write nj staged columns x 64 rows (16-byte runs, 4 per column) to the
+  // columnwise layout; column jl goes to offset jl * ldq + row_off of rq when
+  // jl < j_valid and the run's first row is below rows_valid.
+  auto flush_cols = [&](const uint8_t* stage, auto nj_c, const __amdgpu_buffer_rsrc_t& rq, uint32_t col_off,
+                        uint32_t ldq, uint32_t row_off, int j_valid, int rows_valid) __attribute__((always_inline)) {
+    constexpr int nj = decltype(nj_c)::value;
+    asm volatile("" ::: "memory");
+    static_for<0, nj / 16>([&](auto it_c) __attribute__((always_inline)) {
+      const int c = decltype(it_c)::value * 64 + lane_e;
+      const int jl = c >> 2, part = c & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + jl * kColStride + 16 * part);
+      if (jl < j_valid && 16 * part < rows_valid)
+        __builtin_amdgcn_raw_buffer_store_b128(v, rq, (uint32_t)(col_off + jl) * ldq + row_off + 16 * part, 0, 0);
+    });
+    asm volatile("" ::: "memory");
+  };
+
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     if (MODE == MX_GROUP_K && klen == 0 && args.accumulate) return;
-    // Direct stores: per instruction, lanes (l, l^32) write 8 consecutive
-    // columns of 32 rows; the 4 column groups of a sub-tile complete each
-    // row's 128-byte (fp32) or 64-byte (bf16) run, which L2 merges.
-    char* cbase = reinterpret_cast<char*>(args.c);
     constexpr int esz = EPI == EPI_F32 ? 4 : 2;
-    if constexpr (MODE == MX_GROUP_K) cbase += (int64_t)g * args.c_group_stride * esz;
-    // accumulate and overwrite are separate code paths so the accumulator
-    // registers never merge with the loaded old values
-    auto store_tile = [&](auto acc_c) __attribute__((always_inline)) {
-      constexpr bool ACC = decltype(acc_c)::value;
+    const uint32_t ldc = (uint32_t)args.ldc;
+    const int64_t col0 = (int64_t)tc.nt * BN + (BN / 2) * wn;
+    const char* cb = reinterpret_cast<const char*>(args.c);
+    if constexpr (MODE == MX_GROUP_K) cb += (int64_t)g * args.c_group_stride * esz;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cb + (m0 * args.ldc + col0) * esz, (int64_t)wrows * args.ldc * esz);
+    auto off = [&](int mi, int s, int vg) __attribute__((always_inline)) -> uint32_t {
+      return ((uint32_t)(32 * mi + l32) * ldc + 32 * s + 8 * vg + 4 * h) * esz;
+    };
+    if constexpr (EPI == EPI_F32) {
+      // accumulate and overwrite are separate code paths so the accumulator
+      // registers never merge with the loaded old values; the old values of a
+      // whole m sub-tile are requested before any of them is used
+      auto store_tile = [&](auto acc_c) __attribute__((always_inline)) {
+        constexpr bool ACC = decltype(acc_c)::value;
+        static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
+          constexpr int mi = decltype(mi_c)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          u32x4 old[4][4];
+          if constexpr (ACC) {
+            static_for<0, 16>([&](auto i_c) __attribute__((always_inline)) {
+              constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
+              old[s][vg] = __builtin_amdgcn_raw_buffer_load_b128(rc, off(mi, s, vg), 0, 0);
+            });
+          }
+          static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            if (col0 + 32 * s < args.N) {
+              static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
+                constexpr int vg = decltype(vg_c)::value;
+                float c[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[i] = vgpr_hop(acc[s][mi][4 * vg + i]);
+                if constexpr (ACC) {
+                  c[0] += __uint_as_float(old[s][vg].x); c[1] += __uint_as_float(old[s][vg].y);
+                  c[2] += __uint_as_float(old[s][vg].z); c[3] += __uint_as_float(old[s][vg].w);
+                }
+                u32x4 o;
+                o.x = __float_as_uint(c[0]); o.y = __float_as_uint(c[1]);
+                o.z = __float_as_uint(c[2]); o.w = __float_as_uint(c[3]);
+                __builtin_amdgcn_raw_buffer_store_b128(o, rc, off(mi, s, vg), 0, 0);
+              });
+            }
+          });
+        });
+      };
+      if (args.accumulate) store_tile(std::true_type{});
+      else store_tile(std::false_type{});
+    } else {
       static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_c)::value;
-        const int ml = 128 * wm + 32 * mi + l32;
-        const bool row_ok = ml < a_rows_valid;
-        const int64_t m = a_row0 + ml;
         static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
           constexpr int s = decltype(s_c)::value;
           __builtin_amdgcn_sched_barrier(0);
-          const int64_t n0 = (int64_t)tc.nt * BN + nsub(s) + 4 * h;
-          if (row_ok && n0 < args.N) {
-            char* rowp = cbase + (m * args.ldc + n0) * esz;
-            static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
-              constexpr int vg = decltype(vg_c)::value;
-              float c0 = acc[s][mi][4 * vg + 0], c1 = acc[s][mi][4 * vg + 1];
-              float c2 = acc[s][mi][4 * vg + 2], c3 = acc[s][mi][4 * vg + 3];
-              if constexpr (EPI == EPI_F32) {
-                c0 = vgpr_hop(c0); c1 = vgpr_hop(c1); c2 = vgpr_hop(c2); c3 = vgpr_hop(c3);
-                float4* p = reinterpret_cast<float4*>(rowp + 8 * vg * 4);
-                if constexpr (ACC) {
-                  const float4 old = *p;
-                  c0 += old.x; c1 += old.y; c2 += old.z; c3 += old.w;
-                }
-                *p = make_float4(c0, c1, c2, c3);
-              } else {
-                uint2 o;
-                o.x = pack_bf16x2(c0, c1);
-                o.y = pack_bf16x2(c2, c3);
-                *reinterpret_cast<uint2*>(rowp + 8 * vg * 2) = o;
-              }
-            });
+          if (col0 + 32 * s < args.N) {
+            float x[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = acc[s][mi][v];
+            store_row_bf16(rc, ((uint32_t)(32 * mi + l32) * ldc + 32 * s) * 2, x);
           }
         });
       });
-    };
-    if (EPI == EPI_F32 && args.accumulate) store_tile(std::true_type{});
-    else store_tile(std::false_type{});
+    }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    // sub-tiles s (gate) and s+2 (up), s = 0,1, cover ffn columns
-    // j = j0(s) + 8*(v/4) + 4*h + v%4 with j0(s) = nt*128 + 64*wn + 32*s.
-    const int F = args.F;
-    const int64_t pc0 = args.groups.pc0[slot];
-    const int64_t ldc = args.ld_col;
-    const int grow_in_group0 = tc.mt * BM;
+    // gate (sub-tile s) and up (s+2), s = 0,1, of ffn columns
+    // j = jw0 + 32*s + 8*(v/4) + 4*h + v%4; a = w * silu(gate) * up.
+    const uint32_t F = (uint32_t)args.F;
+    const int jw0 = tc.nt * (BN / 2) + 64 * wn;
+    const int wrow0 = tc.mt * BM + (BM / 2) * wm;       // first row of the wave inside its group
+    const int len = args.groups.len[slot];
+    const int len_pad = (len + 31) & ~31;               // rows of the group in the columnwise layout
+    const uint32_t ldq = (uint32_t)args.ld_col;
+    const int64_t crow0 = args.groups.pc0[slot] + wrow0;   // columnwise position of the wave's first row
+    const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 ? args.h1 + m0 * 2 * F : nullptr, args.h1 ? (int64_t)wrows * 4 * F : 0);
+    const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * F, (int64_t)wrows * F);
+    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row + m0 * (F / 32), (int64_t)wrows * (F / 32));
+    const bool col_out = args.q_col != nullptr;
+    const __amdgpu_buffer_rsrc_t rqc = make_rsrc(col_out ? args.q_col + (int64_t)jw0 * ldq + crow0 : nullptr,
+                                                 col_out ? (int64_t)64 * ldq : 0);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col + (int64_t)jw0 * (ldq / 32) + crow0 / 32 : nullptr,
+                                                 col_out ? (int64_t)64 * (ldq / 32) : 0);
+    float w[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = 32 * mi + l32;
+      w[mi] = args.probs ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * r, 0, 0))
+                         : (r < wrows ? 1.0f : 0.0f);
+    }
     static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
       constexpr int mi = decltype(mi_c)::value;
-      const int ml = 128 * wm + 32 * mi + l32;
-      const bool row_ok = ml < a_rows_valid;
-      const int64_t m = a_row0 + ml;
-      __builtin_amdgcn_sched_barrier(0);
-      const float w = row_ok ? (args.probs ? args.probs[m] : 1.0f) : 0.0f;
-      const int blk_row = grow_in_group0 + 128 * wm + 32 * mi;  // first row of the 32-row block in the group
-      const bool blk_in_layout = blk_row < args.groups.len[slot];
+      const uint32_t r = 32 * mi + l32;
+      const bool blk_ok = col_out && wrow0 + 32 * mi < len;
       static_for<0, 2>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
-        const int j0 = tc.nt * (BN / 2) + 64 * wn + 32 * s;
-        const bool jblk_ok = j0 < F;           // F % 32 == 0: whole 32-block valid or not
-        float a[16];
+        const bool jok = jw0 + 32 * s < (int)F;          // F % 32 == 0: whole block valid or not
+        float gv[16], uv[16], a[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float gg = vgpr_hop(acc[s][mi][v]), uu = vgpr_hop(acc[s + 2][mi][v]);
-          const float sl = gg / (1.0f + __expf(-gg));
-          a[v] = row_ok ? w * sl * uu : 0.0f;
+          gv[v] = vgpr_hop(acc[s][mi][v]);
+          uv[v] = vgpr_hop(acc[s + 2][mi][v]);
+          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[v]));
+          a[v] = w[mi] * (gv[v] * sig) * uv[v];
         }
-        if (args.h1 != nullptr && row_ok && jblk_ok) {
-#pragma unroll
-          for (int vg = 0; vg < 4; ++vg) {
-            const int64_t j = j0 + 8 * vg + 4 * h;
-            uint2 og, ou;
-            og.x = pack_bf16x2(acc[s][mi][4 * vg], acc[s][mi][4 * vg + 1]);
-            og.y = pack_bf16x2(acc[s][mi][4 * vg + 2], acc[s][mi][4 * vg + 3]);
-            ou.x = pack_bf16x2(acc[s + 2][mi][4 * vg], acc[s + 2][mi][4 * vg + 1]);
-            ou.y = pack_bf16x2(acc[s + 2][mi][4 * vg + 2], acc[s + 2][mi][4 * vg + 3]);
-            *reinterpret_cast<uint2*>(args.h1 + m * 2 * F + j) = og;
-            *reinterpret_cast<uint2*>(args.h1 + m * 2 * F + F + j) = ou;
-          }
+        if (args.h1 != nullptr && jok) {
+          store_row_bf16(rh1, (r * 2 * F + jw0 + 32 * s) * 2, gv);
+          store_row_bf16(rh1, (r * 2 * F + F + jw0 + 32 * s) * 2, uv);
         }
-        // rowwise MXFP8 of A: block = the 32 j's of this sub-tile (lanes l, l^32)
-        {
-          uint32_t am = 0;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) am = umax(am, abs_bits(a[v]));
-          am = umax(am, xor_u32(am, 32));
-          const uint32_t sc = scale_code_from_amax_bits(am);
-          const float inv = inv_scale_from_code(sc);
-          if (row_ok && jblk_ok) {
-#pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
-              const uint32_t q = e4m3x4(a[4 * vg] * inv, a[4 * vg + 1] * inv, a[4 * vg + 2] * inv, a[4 * vg + 3] * inv);
-              *reinterpret_cast<uint32_t*>(args.q_row + m * F + j0 + 8 * vg + 4 * h) = q;
-            }
-            if (h == 0) args.s_row[m * (F / 32) + j0 / 32] = (uint8_t)sc;
-          }
-        }
-        // columnwise MXFP8 of A: block = the 32 rows of this m sub-tile (one lane half)
-        if (args.q_col != nullptr && blk_in_layout && jblk_ok) {
-          static_for<0, 16>([&](auto v_c) __attribute__((always_inline)) {
-            constexpr int v = decltype(v_c)::value;
-            uint32_t am = abs_bits(a[v]);
-            static_for<0, 5>([&](auto k_c) __attribute__((always_inline)) {
-              am = umax(am, xor_u32(am, 1 << decltype(k_c)::value));
-            });
-            const uint32_t sc = scale_code_from_amax_bits(am);
-            const float inv = inv_scale_from_code(sc);
-            const uint32_t q = e4m3x4(a[v] * inv, 0.0f, 0.0f, 0.0f) & 0xFFu;
-            const int64_t j = j0 + 8 * (v >> 2) + 4 * h + (v & 3);
-            args.q_col[j * ldc + pc0 + blk_row + l32] = (uint8_t)q;
-            if (l32 == 0) args.s_col[j * (ldc / 32) + (pc0 + blk_row) / 32] = (uint8_t)sc;
-          });
-        }
+        quantize_block(a, rqr, r * F + jw0 + 32 * s, rsr, r * (F / 32) + (jw0 + 32 * s) / 32, jok,
+                       slice + 32 * s * kColStride + 32 * (mi & 1), rsc, (uint32_t)(32 * s) * (ldq / 32) + mi,
+                       ldq / 32, blk_ok && jok);
       });
+      if constexpr (mi & 1) {
+        if (col_out)
+          flush_cols(slice, std::integral_constant<int, 64>{}, rqc, 0u, ldq, (uint32_t)(64 * (mi >> 1)),
+                     (int)F - jw0, len_pad - wrow0 - 64 * (mi >> 1));
+      }
     });
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // acc = dA for ffn column j = nt*256 + nsub(s) + 8*(v/4) + 4*h + v%4
-    const int F = args.F;
-    const int64_t pc0 = args.groups.pc0[slot];
-    const int64_t ldc = args.ld_col;
-    const int grow_in_group0 = tc.mt * BM;
+    // acc = dA for ffn columns j = jw0 + 32*s + 8*(v/4) + 4*h + v%4 (s = 0..3)
+    __shared__ float red[2 * BM];
+    const uint32_t F = (uint32_t)args.F;
+    const int jw0 = tc.nt * BN + (BN / 2) * wn;
+    const int wrow0 = tc.mt * BM + (BM / 2) * wm;
+    const int len = args.groups.len[slot];
+    const int len_pad = (len + 31) & ~31;
+    const uint32_t ldq = (uint32_t)args.ld_col;
+    const int64_t crow0 = args.groups.pc0[slot] + wrow0;
+    const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 + m0 * 2 * F, (int64_t)wrows * 4 * F);
+    const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * 2 * F, (int64_t)wrows * 2 * F);
+    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row + m0 * (2 * F / 32), (int64_t)wrows * (2 * F / 32));
+    // columnwise dH1: gate half (columns j) and up half (columns F + j)
+    const __amdgpu_buffer_rsrc_t rqc_g = make_rsrc(args.q_col + (int64_t)jw0 * ldq + crow0, (int64_t)128 * ldq);
+    const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)128 * ldq);
+    const __amdgpu_buffer_rsrc_t rsc_g = make_rsrc(args.s_col + (int64_t)jw0 * (ldq / 32) + crow0 / 32, (int64_t)128 * (ldq / 32));
+    const __amdgpu_buffer_rsrc_t rsc_u = make_rsrc(args.s_col + (int64_t)(F + jw0) * (ldq / 32) + crow0 / 32, (int64_t)128 * (ldq / 32));
+    float w[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = 32 * mi + l32;
+      w[mi] = args.probs ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * r, 0, 0))
+                         : (r < wrows ? 1.0f : 0.0f);
+    }
     float dpsum[4];
     static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
       constexpr int mi = decltype(mi_c)::value;
-      const int ml = 128 * wm + 32 * mi + l32;
-      const bool row_ok = ml < a_rows_valid;
-      const int64_t m = a_row0 + ml;
+      const uint32_t r = 32 * mi + l32;
+      const bool blk_ok = wrow0 + 32 * mi < len;
       __builtin_amdgcn_sched_barrier(0);
-      const float w = row_ok ? (args.probs ? args.probs[m] : 1.0f) : 0.0f;
-      const int blk_row = grow_in_group0 + 128 * wm + 32 * mi;
-      const bool blk_in_layout = blk_row < args.groups.len[slot];
+      // gate and up (bf16) of the sub-tile's 4 x 16 columns, all requested
+      // before the first is used
+      u32x2 gl[4][4], ul[4][4];
+      static_for<0, 16>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
+        const uint32_t o = (r * 2 * F + jw0 + 32 * s + 8 * vg + 4 * h) * 2;
+        gl[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o, 0, 0);
+        ul[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o + 2 * F, 0, 0);
+      });
       float dp = 0.0f;
       static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
-        const int j0 = tc.nt * BN + nsub(s);
-        const bool jblk_ok = j0 < F;
+        const bool jok = jw0 + 32 * s < (int)F;
         float dg[16], du[16];
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
-          const int64_t j = j0 + 8 * vg + 4 * h;
-          uint2 gr = make_uint2(0, 0), ur = make_uint2(0, 0);
-          if (row_ok && jblk_ok) {
-            gr = *reinterpret_cast<const uint2*>(args.h1 + m * 2 * F + j);
-            ur = *reinterpret_cast<const uint2*>(args.h1 + m * 2 * F + F + j);
-          }
-          const float gv[4] = {bf16_lo(gr.x), bf16_hi(gr.x), bf16_lo(gr.y), bf16_hi(gr.y)};
-          const float uv[4] = {bf16_lo(ur.x), bf16_hi(ur.x), bf16_lo(ur.y), bf16_hi(ur.y)};
+          const float gv[4] = {bf16_lo(gl[s][vg].x), bf16_hi(gl[s][vg].x), bf16_lo(gl[s][vg].y), bf16_hi(gl[s][vg].y)};
+          const float uv[4] = {bf16_lo(ul[s][vg].x), bf16_hi(ul[s][vg].x), bf16_lo(ul[s][vg].y), bf16_hi(ul[s][vg].y)};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float da = vgpr_hop(acc[s][mi][4 * vg + i]);
-            const float sg = 1.0f / (1.0f + __expf(-gv[i]));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
             const float sl = gv[i] * sg;
-            const float dgv = da * w * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg));
-            const float duv = da * w * sl;
-            const bool ok = row_ok && jblk_ok;
-            dg[4 * vg + i] = ok ? dgv : 0.0f;
-            du[4 * vg + i] = ok ? duv : 0.0f;
-            dp += ok ? da * sl * uv[i] : 0.0f;
+            dg[4 * vg + i] = da * w[mi] * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg));
+            du[4 * vg + i] = da * w[mi] * sl;
+            dp += da * sl * uv[i];
           }
         }
-        // MXFP8 of dg (dH1 columns j) and du (dH1 columns F + j), both layouts
-        static_for<0, 2>([&](auto half_c) __attribute__((always_inline)) {
-          constexpr int half = decltype(half_c)::value;
-          float d[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) d[v] = half == 0 ? dg[v] : du[v];
-          const int64_t jc0 = (half == 0 ? 0 : (int64_t)F) + j0;
-          __builtin_amdgcn_sched_barrier(0);
-          uint32_t am = 0;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) am = umax(am, abs_bits(d[v]));
-          am = umax(am, xor_u32(am, 32));
-          const uint32_t sc = scale_code_from_amax_bits(am);
-          const float inv = inv_scale_from_code(sc);
-          if (row_ok && jblk_ok) {
-#pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
-              const uint32_t q = e4m3x4(d[4 * vg] * inv, d[4 * vg + 1] * inv, d[4 * vg + 2] * inv, d[4 * vg + 3] * inv);
-              *reinterpret_cast<uint32_t*>(args.q_row + m * 2 * F + jc0 + 8 * vg + 4 * h) = q;
-            }
-            if (h == 0) args.s_row[m * (2 * F / 32) + jc0 / 32] = (uint8_t)sc;
-          }
-          if (blk_in_layout && jblk_ok) {
-            static_for<0, 16>([&](auto v_c) __attribute__((always_inline)) {
-              constexpr int v = decltype(v_c)::value;
-              uint32_t amc = abs_bits(d[v]);
-              static_for<0, 5>([&](auto k_c) __attribute__((always_inline)) {
-                amc = umax(amc, xor_u32(amc, 1 << decltype(k_c)::value));
-              });
-              const uint32_t scc = scale_code_from_amax_bits(amc);
-              const float invc = inv_scale_from_code(scc);
-              const uint32_t q = e4m3x4(d[v] * invc, 0.0f, 0.0f, 0.0f) & 0xFFu;
-              const int64_t jc = jc0 + 8 * (v >> 2) + 4 * h + (v & 3);
-              args.q_col[jc * ldc + pc0 + blk_row + l32] = (uint8_t)q;
-              if (l32 == 0) args.s_col[jc * (ldc / 32) + (pc0 + blk_row) / 32] = (uint8_t)scc;
-            });
-          }
-        });
+        uint8_t* st = slice + 32 * s * kColStride + 32 * (mi & 1);
+        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, rsr, r * (2 * F / 32) + (jw0 + 32 * s) / 32, jok,
+                       st, rsc_g, (uint32_t)(32 * s) * (ldq / 32) + mi, ldq / 32, blk_ok && jok);
+        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, rsr, r * (2 * F / 32) + (F + jw0 + 32 * s) / 32, jok,
+                       st + kColHalf, rsc_u, (uint32_t)(32 * s) * (ldq / 32) + mi, ldq / 32, blk_ok && jok);
       });
-      dp += xor_f32(dp, 32);
-      dpsum[mi] = dp;
+      dpsum[mi] = sum_halves(dp);
+      if constexpr (mi & 1) {
+        const uint32_t ro = 64 * (mi >> 1);
+        const int rv = len_pad - wrow0 - 64 * (mi >> 1);
+        flush_cols(slice, std::integral_constant<int, 128>{}, rqc_g, 0u, ldq, ro, (int)F - jw0, rv);
+        flush_cols(slice + kColHalf, std::integral_constant<int, 128>{}, rqc_u, 0u, ldq, ro, (int)F - jw0, rv);
+      }
     });
-    // dprobs partial over this tile's 256 columns: reduce the 2 n-waves via LDS
+    // dprobs partial over this tile's 256 columns: the two n-waves meet in LDS
     if (args.dprobs_part != nullptr) {
-      float* red = reinterpret_cast<float*>(sA0);   // main loop is done (barrier above)
       if (h == 0) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) red[wn * BM + 128 * wm + 32 * mi + l32] = dpsum[mi];
+        for (int mi = 0; mi < 4; ++mi) red[wn * BM + (BM / 2) * wm + 32 * mi + l32] = dpsum[mi];
       }
       __syncthreads();
       if (tid < a_rows_valid) {
