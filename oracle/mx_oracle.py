@@ -463,8 +463,14 @@ def mlp_backward_rows(x, probs, w1, w2, split_sizes, dy, rows):
 def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
                                dw1_idx, dw2_idx):
     """Selected entries of one expert's dW1 (indices (n, h)) and dW2 ((h, f)),
-    from a zero start.  Needs the expert's full dH1 and A columns, so it runs
-    the expert's whole forward/backward restricted to the needed columns."""
+    from a zero start.
+
+    Every quantization on the way is per row over the contraction axis (X, dY,
+    W1 rows) or per column over the expert's rows (W2 over H, dH1, A, X and dY
+    for the weight gradients), so an entry only needs the columns it touches:
+    ffn column c = n mod F of H1 (gate c and up F + c) and dA for dW1, gate
+    and up column f of H1 for dW2, and columns h of X and dY. The arithmetic
+    per column is that of _expert_dh1 / mlp_backward."""
     off = _offsets(split_sizes)
     r0, r1 = int(off[expert]), int(off[expert + 1])
     F = w1.shape[1] // 2
@@ -472,20 +478,39 @@ def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
     dw2_idx = np.asarray(dw2_idx, dtype=np.int64).reshape(-1, 2)
     if r1 == r0:
         return np.zeros(len(dw1_idx)), np.zeros(len(dw2_idx))
-    dh, _, h1 = _expert_dh1(x, probs, w1, w2, split_sizes, dy, expert)
     p = np.asarray(probs, dtype=np.float64)[r0:r1]
-    a = p[:, None] * silu(h1[:, :F]) * h1[:, F:]
-    X = _as_f64(x[r0:r1])
-    dY = _as_f64(dy[r0:r1])
-    # columnwise quantization is per column: quantize only the needed columns
-    dhc = _qdq_col(dh[:, np.unique(dw1_idx[:, 0])], True)
-    xc = _qdq_col(X[:, np.unique(dw1_idx[:, 1])], True)
-    n_map = {n: i for i, n in enumerate(np.unique(dw1_idx[:, 0]).tolist())}
-    h_map = {h: i for i, h in enumerate(np.unique(dw1_idx[:, 1]).tolist())}
+    Xh = _qdq_row(_as_f64(x[r0:r1]), True)
+    dYh = _qdq_row(_as_f64(dy[r0:r1]), True)
+
+    def h1_cols(cs):
+        """Unrounded gate and up columns cs of H1 = Xh . W1h^T."""
+        W1h_g = _qdq_row(_as_f64(w1[expert][cs]), True)
+        W1h_u = _qdq_row(_as_f64(w1[expert][F + cs]), True)
+        return Xh @ W1h_g.T, Xh @ W1h_u.T
+
+    # dW1[n, h] = sum_r dH1c[r, n] * Xc[r, h]
+    c1 = np.unique(dw1_idx[:, 0] % F)
+    g, u = h1_cols(c1)
+    dA = dYh @ _qdq_col(_as_f64(w2[expert][:, c1]), True)
+    dg, du, _ = _swiglu_backward(dA, round_to_bf16(g), round_to_bf16(u), p)
+    dh = np.concatenate([dg, du], axis=1)                     # columns c1, then F + c1
+    dh_pos = {int(c): i for i, c in enumerate(c1.tolist())}
+    dh_pos.update({int(F + c): len(c1) + i for i, c in enumerate(c1.tolist())})
+    n_sel = np.unique(dw1_idx[:, 0])
+    dhc = _qdq_col(dh[:, [dh_pos[int(n)] for n in n_sel]], True)
+    h_sel = np.unique(dw1_idx[:, 1])
+    xc = _qdq_col(_as_f64(x[r0:r1][:, h_sel]), True)
+    n_map = {int(n): i for i, n in enumerate(n_sel.tolist())}
+    h_map = {int(h): i for i, h in enumerate(h_sel.tolist())}
     out1 = np.array([dhc[:, n_map[n]] @ xc[:, h_map[h]] for n, h in dw1_idx.tolist()])
-    dyc = _qdq_col(dY[:, np.unique(dw2_idx[:, 0])], True)
-    ac = _qdq_col(a[:, np.unique(dw2_idx[:, 1])], True)
-    h2_map = {h: i for i, h in enumerate(np.unique(dw2_idx[:, 0]).tolist())}
-    f_map = {f: i for i, f in enumerate(np.unique(dw2_idx[:, 1]).tolist())}
+
+    # dW2[h, f] = sum_r dYc[r, h] * Ac[r, f], A = w * silu(gate) * up (unrounded H1)
+    f_sel = np.unique(dw2_idx[:, 1])
+    g2, u2 = h1_cols(f_sel)
+    ac = _qdq_col(p[:, None] * silu(g2) * u2, True)
+    h2_sel = np.unique(dw2_idx[:, 0])
+    dyc = _qdq_col(_as_f64(dy[r0:r1][:, h2_sel]), True)
+    h2_map = {int(h): i for i, h in enumerate(h2_sel.tolist())}
+    f_map = {int(f): i for i, f in enumerate(f_sel.tolist())}
     out2 = np.array([dyc[:, h2_map[h]] @ ac[:, f_map[f]] for h, f in dw2_idx.tolist()])
     return out1, out2
