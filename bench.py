@@ -34,6 +34,7 @@ METRIC = "MXFP8 grouped-MLP TFLOP/s (fwd+bwd) and % of MXFP8 MFMA peak; quantize
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 GEMM_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_gemm.hip")
+QUANT_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_quantize.hip")
 
 
 def log(msg):
@@ -49,10 +50,32 @@ def stage_flops(R, H, F):
     }
 
 
-def traffic_from_profiles(kernel_stage):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter summaries, only if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_stage}_traffic.txt")
+def stage_bytes(E, R, P, H, F):
+    """Algorithmic HBM bytes of each stage: every operand read once, every
+    output written once (MXFP8 = 1 byte per code + 1 per 32 codes; the
+    columnwise layouts hold P = sum of per-expert row counts padded to 32;
+    fp32 main grads are read and written)."""
+    mx8 = 1.0 + 1.0 / 32
+    return {
+        "quantize_x": 2 * R * H + mx8 * (R * H + H * P),
+        "quantize_w1": 2 * E * 2 * F * H + 2 * mx8 * E * 2 * F * H,
+        "quantize_w2": 2 * E * H * F + 2 * mx8 * E * H * F,
+        "gemm1_swiglu": mx8 * (R * H + E * 2 * F * H) + 4 * R + 2 * R * 2 * F + mx8 * (R * F + F * P),
+        "gemm2": mx8 * (R * F + E * H * F) + 2 * R * H,
+        "quantize_dy": 2 * R * H + mx8 * (R * H + H * P),
+        "dgrad2_swiglu_bwd": mx8 * (R * H + E * F * H) + 2 * R * 2 * F + 4 * R
+                             + mx8 * (R * 2 * F + 2 * F * P) + 4 * R * (F // 256),
+        "dprobs_reduce": 4 * R * (F // 256) + 4 * R,
+        "wgrad2": mx8 * (H * P + F * P) + 2 * 4 * E * H * F,
+        "dgrad1": mx8 * (R * 2 * F + E * H * 2 * F) + 2 * R * H,
+        "wgrad1": mx8 * (2 * F * P + H * P) + 2 * 4 * E * 2 * F * H,
+    }
+
+
+def traffic_from_profiles(workload, stage):
+    """Measured HBM bytes per launch of one stage from the committed rocprofv3
+    counter summary, only if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -60,11 +83,11 @@ def traffic_from_profiles(kernel_stage):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(GEMM_KERNEL_SRC, "rb").read()).hexdigest()
-    if vals.get("source_sha256") != sha:
-        return None
+    for key, src in (("source_sha256", GEMM_KERNEL_SRC), ("quantize_source_sha256", QUANT_KERNEL_SRC)):
+        if vals.get(key) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"{stage}.hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -105,6 +128,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_moe_fwd_bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of a known size (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -121,6 +146,9 @@ def main():
         sys.exit(1)
     mx.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     wl = wlmod.WORKLOADS[args.workload]
     if not wl.backward:
         raise SystemExit("bench.py times the fwd+bwd step; pick a workload with a backward pass")
@@ -177,20 +205,32 @@ def main():
         for j, name in enumerate(names):
             stages[name] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
     flops = stage_flops(R, H, F)
+    P = int(sum((m + 31) // 32 * 32 for m in split))
+    nbytes = stage_bytes(E, R, P, H, F)
     step_flops = sum(flops.values())                     # = 18 R H F
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = sum(stages[k] for k in flops)
     gemm_tflops = step_flops / (gemm_ms * 1e-3) / 1e12
-    dom = max(flops, key=lambda k: stages[k])
-    dom_ach = flops[dom] / (stages[dom] * 1e-3) / 1e12
-    traffic = traffic_from_profiles(dom)
-    roofline = {"bound": "mfma", "achieved": round(dom_ach, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": dom, "flop_per_launch": flops[dom], "avg_launch_ms": round(stages[dom], 4)}
-    per_gemm = {k: {"ms": round(stages[k], 4),
-                    "tflops": round(flops[k] / (stages[k] * 1e-3) / 1e12, 1),
-                    "frac_mfma_peak": round(flops[k] / (stages[k] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-                for k in flops}
+
+    def roof(k):
+        """Bound of stage k: whichever of MFMA time and HBM time at peak is larger."""
+        t = stages[k] * 1e-3
+        fl = flops.get(k, 0.0)
+        if fl / (PEAK_FP8_TFLOPS * 1e12) >= nbytes[k] / (PEAK_HBM_GBPS * 1e9):
+            ach = fl / t / 1e12
+            return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_FP8_TFLOPS, 4)}
+        ach = nbytes[k] / t / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4)}
+
+    dom = max(stages, key=lambda k: stages[k])
+    roofline = dict(roof(dom), traffic=traffic_from_profiles(wl.name, dom), kernel=dom,
+                    algorithmic_flop_per_launch=flops.get(dom, 0.0),
+                    algorithmic_bytes_per_launch=round(nbytes[dom]), avg_launch_ms=round(stages[dom], 4))
+    per_stage = {k: dict(ms=round(stages[k], 4), **roof(k),
+                         tflops=round(flops.get(k, 0.0) / (stages[k] * 1e-3) / 1e12, 1),
+                         gbps=round(nbytes[k] / (stages[k] * 1e-3) / 1e9, 1)) for k in stages}
     log(f"step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; GEMM-only {gemm_tflops:.1f} TFLOP/s")
 
     out = {
@@ -203,8 +243,7 @@ def main():
                    "step": "grouped_mlp_fwd(training) + grouped_mlp_bwd(fp32 wgrad accumulate)"},
         "gemm_only": {"tflops": round(gemm_tflops, 1),
                       "frac_mfma_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "ms": round(gemm_ms, 4)},
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-        "per_gemm": per_gemm,
+        "stages": per_stage,
         "roofline": roofline,
     }
 
@@ -220,6 +259,20 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, wl)
         log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes),
+    reps times: the HBM counters (FETCH_SIZE, WRITE_SIZE) of these dispatches
+    give the factor between counter units and bytes on this machine."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}}),
+          flush=True)
 
 
 def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):

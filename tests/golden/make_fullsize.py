@@ -1,0 +1,90 @@
+"""Expected values for the full-size grouped-MLP parity tests, from the oracle only.
+
+For each full-size workload (inputs regenerated from the workload's seed by
+workloads.make_mlp_inputs) the oracle evaluates a sample of outputs it can
+compute one by one: Y at a few rows of two experts (the largest and the
+smallest non-empty one; the only one for a dense MLP) and, for a workload
+with a backward, dX and dprobs at the same rows and entries of those
+experts' dW1 and dW2 (from a zero start). The sample and the values go to
+fullsize_<workload>.npz beside this script.
+
+    python tests/golden/make_fullsize.py [workload ...]
+
+Each workload takes minutes of CPU (the exact float64 quantizer runs over
+whole expert weight matrices for the sampled rows).
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle as orc  # noqa: E402
+import workloads as wl  # noqa: E402
+
+FULLSIZE = ("llama8b_dense_fwd", "mixtral_moe_fwd", "mixtral_moe_fwd_bwd")
+ROWS_PER_EXPERT = 3
+ENTRIES_PER_EXPERT = 24
+
+
+def golden_path(name: str) -> str:
+    return os.path.join(HERE, f"fullsize_{name}.npz")
+
+
+def make(name: str) -> str:
+    w = wl.WORKLOADS[name]
+    t0 = time.time()
+    c = wl.make_mlp_inputs(w, with_dy=w.backward)
+    split = np.asarray(c["split_sizes"], dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(split)])
+    F, H = w.ffn, w.hidden
+    nonempty = [e for e in range(w.experts) if split[e] > 0]
+    experts = sorted({max(nonempty, key=lambda e: split[e]), min(nonempty, key=lambda e: split[e])})
+    rng = np.random.default_rng(1000 + w.seed)
+    rows = []
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        pick = {r0, r1 - 1}
+        while len(pick) < min(ROWS_PER_EXPERT, r1 - r0):
+            pick.add(int(rng.integers(r0, r1)))
+        rows += sorted(pick)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = dict(workload=np.array(name), split=split, experts=np.asarray(experts, dtype=np.int64), rows=rows)
+
+    f = orc.mlp_forward_rows(c["x"], c["probs"], c["w1"], c["w2"], split, rows)
+    out["y"] = f["y"]
+    print(f"[{name}] forward rows done ({time.time() - t0:.0f} s)", flush=True)
+    if w.backward:
+        b = orc.mlp_backward_rows(c["x"], c["probs"], c["w1"], c["w2"], split, c["dy"], rows)
+        out["dx"], out["dprobs"] = b["dx"], b["dprobs"]
+        print(f"[{name}] backward rows done ({time.time() - t0:.0f} s)", flush=True)
+        i1, v1, i2, v2 = [], [], [], []
+        for e in experts:
+            n = rng.integers(0, 2 * F, ENTRIES_PER_EXPERT)
+            n[: ENTRIES_PER_EXPERT // 2] %= F            # half gate rows, the rest anywhere
+            h = rng.integers(0, H, ENTRIES_PER_EXPERT)
+            d1 = np.stack([n, h], axis=1)
+            d2 = np.stack([rng.integers(0, H, ENTRIES_PER_EXPERT), rng.integers(0, F, ENTRIES_PER_EXPERT)], axis=1)
+            a1, a2 = orc.mlp_backward_wgrad_entries(c["x"], c["probs"], c["w1"], c["w2"], split,
+                                                    c["dy"], e, d1, d2)
+            i1.append(np.concatenate([np.full((len(d1), 1), e), d1], axis=1)); v1.append(a1)
+            i2.append(np.concatenate([np.full((len(d2), 1), e), d2], axis=1)); v2.append(a2)
+        out["dw1_idx"], out["dw1"] = np.concatenate(i1), np.concatenate(v1)
+        out["dw2_idx"], out["dw2"] = np.concatenate(i2), np.concatenate(v2)
+        print(f"[{name}] weight-gradient entries done ({time.time() - t0:.0f} s)", flush=True)
+    path = golden_path(name)
+    np.savez_compressed(path, **out)
+    print(f"[{name}] wrote {path}", flush=True)
+    return path
+
+
+if __name__ == "__main__":
+    for nm in sys.argv[1:] or FULLSIZE:
+        make(nm)
