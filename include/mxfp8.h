@@ -162,7 +162,7 @@ typedef struct mx_mlp_dims {
  * shape and split: fwd_workspace (scratch of grouped_mlp_fwd), saved (what
  * grouped_mlp_fwd keeps for grouped_mlp_bwd in training) and bwd_workspace
  * (scratch of grouped_mlp_bwd). Any output pointer may be NULL.
- * Errors: MX_EINVAL, MX_ESHAPE (H or F not multiples of 32, split mismatch).
+ * Errors: MX_EINVAL, MX_ESHAPE (H or F not multiples of 128, split mismatch).
  */
 MX_API mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes,
                             size_t* fwd_workspace, size_t* saved, size_t* bwd_workspace);
@@ -184,8 +184,10 @@ MX_API mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split
  *                (grouped_mlp_sizes) that receives H1 (bf16), the columnwise
  *                copies of X, A, W1, W2 for grouped_mlp_bwd.
  *   workspace    fwd_workspace bytes of scratch, 256-byte aligned.
- * Requires H % 32 == 0, F % 32 == 0 (H % 128 and F % 128 for best speed),
- * 1 <= E <= MX_MAX_GROUPS. All pointers 16-byte aligned.
+ * Requires H % 128 == 0 and F % 128 == 0 (the internal MXFP8 copies keep
+ * their scales in 128-column steps), 1 <= E <= MX_MAX_GROUPS. All pointers
+ * 16-byte aligned. The layout of the workspace and saved buffers is private
+ * to the library.
  */
 MX_API mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes,
                           const void* x, const float* probs, const void* w1, const void* w2,

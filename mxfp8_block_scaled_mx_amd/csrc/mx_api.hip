@@ -41,6 +41,15 @@ constexpr int64_t kI32Max = 0x7FFFFFFF;
 int64_t pad32(int64_t m) { return (m + 31) / 32 * 32; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// k-tiled scales of a columnwise layout with row groups: first 128-column
+// step of each group (q0[n] = total steps).
+std::vector<int64_t> group_steps(const int64_t* sizes, int32_t n, int64_t rows) {
+  std::vector<int64_t> q0(1, 0);
+  const int ng = n > 0 ? n : 1;
+  for (int g = 0; g < ng; ++g) q0.push_back(q0.back() + cdiv(pad32(n > 0 ? sizes[g] : rows), 128));
+  return q0;
+}
+
 // ---------------------------------------------------------------- quantize
 mx_status check_groups(const int64_t* sizes, int32_t n, int64_t rows, const char* who) {
   if (n < 0) return fail(MX_EINVAL, "%s: negative group count", who);
@@ -55,9 +64,11 @@ mx_status check_groups(const int64_t* sizes, int32_t n, int64_t rows, const char
   return MX_OK;
 }
 
+// tiled: scales of both copies in the k-tiled layout (the fused MLP's
+// internal buffers; needs cols % 128 == 0 for the rowwise copy).
 mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
                         int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool tiled = false) {
   const char* who = "mx_quantize";
   if (x == nullptr) return fail(MX_EINVAL, "%s: x is null", who);
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return fail(MX_EINVAL, "%s: unsupported dtype %d", who, x_dtype);
@@ -96,6 +107,15 @@ mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t co
   a.groups.row0[n] = (int32_t)r0;
   a.groups.pcol0[n] = (int32_t)p0;
   a.groups.tile0[n] = (int32_t)t0;
+  if (tiled) {
+    if (q_row != nullptr && cols % 128) return fail(MX_ESHAPE, "%s: k-tiled scales need cols %% 128 == 0", who);
+    const std::vector<int64_t> q0 = group_steps(group_sizes, num_groups, rows);
+    for (int g = 0; g <= n; ++g) a.groups.q0[g] = (int32_t)q0[g];
+    a.tiled = 1;
+    a.nq_row = (int32_t)(cols / 128);
+    a.nq_col = (int32_t)q0[n];
+    a.rows = (int32_t)rows;
+  }
   if (p0 > kI32Max) return fail(MX_EUNSUPPORTED, "%s: padded rows exceed 2^31-1", who);
   a.ld_col = p0;
   a.n_col_tiles = (int32_t)cdiv(cols, mx::quant_tile_cols(x_dtype));
@@ -150,12 +170,16 @@ mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, in
   A.a = a; A.as = as; A.b = b; A.bs = bs; A.c = c;
   A.lda = lda; A.ldb = ldb; A.ldc = ldc;
   A.b_group_stride = b_group_stride;
+  A.bs_group_stride = b_group_stride / 32;
+  A.sa = mx::row_major_scales(lda);
+  A.sb = mx::row_major_scales(ldb);
+  A.as_bytes = M * (lda / 32);
+  A.bs_bytes = n_rows_b * (ldb / 32);
   A.c_group_stride = c_group_stride;
   A.M = (int32_t)M; A.N = (int32_t)N; A.K = (int32_t)K;
   A.accumulate = accumulate;
   const int64_t tiles_n = epi == mx::EPI_SWIGLU_FWD ? cdiv(N / 2, mx::kTileN / 2) : cdiv(N, mx::kTileN);
   A.n_tiles_n = (int32_t)tiles_n;
-  (void)n_rows_b;
   // slot order: group-M keeps expert order and drops empty groups; group-K puts
   // the longest contractions first so the tail of the launch is short.
   std::vector<int> order;
@@ -192,6 +216,24 @@ mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, in
   return MX_OK;
 }
 
+// Switch a plan of the fused MLP to its k-tiled scale buffers: A scales of
+// a_rows rows with nq_a steps, B scales of b_rows rows (all groups) with nq_b
+// steps, B group g's scales bs_group_stride bytes after group g-1's, and the
+// activation layout's per-expert first steps (group-K contraction steps and
+// the columnwise epilogue outputs).
+void use_k_tiled_scales(GemmPlan& p, int64_t nq_a, int64_t a_rows, int64_t nq_b, int64_t b_rows,
+                        int64_t bs_group_stride, const std::vector<int64_t>& q0_act) {
+  mx::GemmArgs& A = p.args;
+  A.sa = mx::k_tiled_scales(nq_a);
+  A.sb = mx::k_tiled_scales(nq_b);
+  A.as_bytes = cdiv(a_rows, 32) * nq_a * 128;
+  A.bs_bytes = cdiv(b_rows, 32) * nq_b * 128;
+  A.bs_group_stride = bs_group_stride;
+  A.k_tiled = 1;
+  for (int s = 0; s < A.groups.n; ++s) A.groups.q0[s] = (int32_t)q0_act[A.groups.gid[s]];
+  p.scale_dword = true;
+}
+
 // ---------------------------------------------------------------- fused MLP plan
 struct MlpLayout {
   int E;
@@ -204,6 +246,8 @@ struct MlpLayout {
   // backward workspace
   size_t dyq, dys, dycq, dycs, dhq, dhs, dhcq, dhcs, part, bwd_total;
   int64_t n_tiles_f;
+  std::vector<int64_t> q0;   // k-tiled steps of the per-expert columnwise layouts
+  int64_t nq;                // total steps (q0[E])
 };
 
 size_t take(size_t& cur, size_t bytes) {
@@ -218,7 +262,7 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   if (d->num_experts > mx::kMaxGroups) return fail(MX_EUNSUPPORTED, "%s: %d experts exceeds the maximum %d", who, d->num_experts, mx::kMaxGroups);
   if (!split) return fail(MX_EINVAL, "%s: split_sizes is null", who);
   if (d->rows < 0 || d->hidden <= 0 || d->ffn <= 0) return fail(MX_ESHAPE, "%s: bad dims", who);
-  if (d->hidden % 32 || d->ffn % 32) return fail(MX_ESHAPE, "%s: hidden and ffn must be multiples of 32", who);
+  if (d->hidden % 128 || d->ffn % 128) return fail(MX_ESHAPE, "%s: hidden and ffn must be multiples of 128", who);
   if (d->rows > kI32Max || 2 * d->ffn > kI32Max || (int64_t)d->num_experts * 2 * d->ffn > kI32Max ||
       (int64_t)d->num_experts * d->hidden > kI32Max)
     return fail(MX_EUNSUPPORTED, "%s: dimensions exceed 2^31-1", who);
@@ -232,25 +276,30 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   L->sumP = 0;
   for (int e = 0; e < L->E; ++e) L->sumP += pad32(split[e]);
   const int64_t R = L->R, H = L->H, F = L->F, E = L->E, P = L->sumP;
+  L->q0 = group_steps(split, d->num_experts, d->rows);
+  L->nq = L->q0[E];
+  // all scales are k-tiled: a rowwise [rows, K] matrix takes ceil(rows/32)*32*K/32
+  // bytes, a per-expert columnwise [cols, P] one cols/32 * nq * 128
+  const int64_t R32 = cdiv(R, 32) * 32, NQ = L->nq;
   size_t c = 0;
-  L->xq = take(c, R * H); L->xs = take(c, R * H / 32);
+  L->xq = take(c, R * H); L->xs = take(c, R32 * H / 32);
   L->w1q = take(c, E * 2 * F * H); L->w1s = take(c, E * 2 * F * H / 32);
   L->w2q = take(c, E * H * F); L->w2s = take(c, E * H * F / 32);
-  L->aq = take(c, R * F); L->as = take(c, R * F / 32);
+  L->aq = take(c, R * F); L->as = take(c, R32 * F / 32);
   L->fwd_total = c;
   c = 0;
-  L->xcq = take(c, H * P); L->xcs = take(c, H * P / 32);
+  L->xcq = take(c, H * P); L->xcs = take(c, H / 32 * NQ * 128);
   L->h1 = take(c, R * 2 * F * 2);
-  L->acq = take(c, F * P); L->acs = take(c, F * P / 32);
+  L->acq = take(c, F * P); L->acs = take(c, F / 32 * NQ * 128);
   L->w1cq = take(c, H * E * 2 * F); L->w1cs = take(c, H * E * 2 * F / 32);
   L->w2cq = take(c, F * E * H); L->w2cs = take(c, F * E * H / 32);
   L->saved_total = c;
   c = 0;
   L->n_tiles_f = cdiv(F, mx::kTileN);
-  L->dyq = take(c, R * H); L->dys = take(c, R * H / 32);
-  L->dycq = take(c, H * P); L->dycs = take(c, H * P / 32);
-  L->dhq = take(c, R * 2 * F); L->dhs = take(c, R * 2 * F / 32);
-  L->dhcq = take(c, 2 * F * P); L->dhcs = take(c, 2 * F * P / 32);
+  L->dyq = take(c, R * H); L->dys = take(c, R32 * H / 32);
+  L->dycq = take(c, H * P); L->dycs = take(c, H / 32 * NQ * 128);
+  L->dhq = take(c, R * 2 * F); L->dhs = take(c, R32 * 2 * F / 32);
+  L->dhcq = take(c, 2 * F * P); L->dhcs = take(c, 2 * F / 32 * NQ * 128);
   L->part = take(c, L->n_tiles_f * R * 4);
   L->bwd_total = c;
   return MX_OK;
@@ -357,8 +406,12 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, H, F, at(workspace, L.aq), at(workspace, L.as), F,
                  at(workspace, L.w2q), at(workspace, L.w2s), F, H * F, y, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &p2);
   if (st != MX_OK) return st;
+  use_k_tiled_scales(p1, H / 128, R, H / 128, E * 2 * F, 2 * F * H / 32, L.q0);
+  use_k_tiled_scales(p2, F / 128, R, F / 128, E * H, H * F / 32, L.q0);
   mx::GemmArgs& a1 = p1.args;
   a1.c = nullptr;
+  a1.nq_row = (int32_t)(F / 128);
+  a1.nq_col = (int32_t)L.nq;
   a1.F = (int32_t)F;
   a1.ld_col = L.sumP;
   a1.probs = probs;
@@ -371,15 +424,15 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
 
   stage_mark(0, stream);
   st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
-                     saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream);
+                     saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true);
   if (st != MX_OK) return st;
   stage_mark(1, stream);
   st = quantize_impl(w1, MX_BF16, E * 2 * F, H, g_w1.data(), E, at(workspace, L.w1q), at(workspace, L.w1s),
-                     saved ? at(saved, L.w1cq) : nullptr, saved ? at(saved, L.w1cs) : nullptr, stream);
+                     saved ? at(saved, L.w1cq) : nullptr, saved ? at(saved, L.w1cs) : nullptr, stream, true);
   if (st != MX_OK) return st;
   stage_mark(2, stream);
   st = quantize_impl(w2, MX_BF16, E * H, F, g_w2.data(), E, at(workspace, L.w2q), at(workspace, L.w2s),
-                     saved ? at(saved, L.w2cq) : nullptr, saved ? at(saved, L.w2cs) : nullptr, stream);
+                     saved ? at(saved, L.w2cq) : nullptr, saved ? at(saved, L.w2cs) : nullptr, stream, true);
   if (st != MX_OK) return st;
   stage_mark(3, stream);
   st = run_gemm(p1, MX_GROUP_M, mx::EPI_SWIGLU_FWD, stream, "grouped_mlp_fwd gemm1");
@@ -428,8 +481,16 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
                  at(saved, L.xcq), at(saved, L.xcs), P, 0, dw1, MX_F32, H, 2 * F * H, accumulate_wgrad, mx::EPI_F32,
                  H, &pw1);
   if (st != MX_OK) return st;
+  // B of dgrad2 / dgrad1: the columnwise weights [F, E*H] / [H, E*2F], expert
+  // e's k range starting at step e*H/128 / e*2F/128
+  use_k_tiled_scales(pd2, H / 128, R, E * H / 128, F, H, L.q0);
+  use_k_tiled_scales(pw2, L.nq, H, L.nq, F, 0, L.q0);
+  use_k_tiled_scales(pd1, 2 * F / 128, R, E * 2 * F / 128, H, 2 * F, L.q0);
+  use_k_tiled_scales(pw1, L.nq, 2 * F, L.nq, H, 0, L.q0);
   mx::GemmArgs& a = pd2.args;
   a.c = nullptr;
+  a.nq_row = (int32_t)(2 * F / 128);
+  a.nq_col = (int32_t)L.nq;
   a.F = (int32_t)F;
   a.ld_col = P;
   a.probs = probs;
@@ -443,7 +504,7 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
 
   stage_mark(0, stream);
   st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
-                     at(workspace, L.dycq), at(workspace, L.dycs), stream);
+                     at(workspace, L.dycq), at(workspace, L.dycs), stream, true);
   if (st != MX_OK) return st;
   stage_mark(1, stream);
   st = run_gemm(pd2, MX_GROUP_M, mx::EPI_SWIGLU_BWD, stream, "grouped_mlp_bwd dgrad2");

@@ -42,6 +42,7 @@
 namespace mx {
 
 [[maybe_unused]] constexpr int BM = kTileM, BN = kTileN, BK = kTileK;
+static_assert(sizeof(GemmArgs) <= 4096, "kernel arguments must fit the 4 KB kernarg segment");
 constexpr int kThreads = 256;
 constexpr int kBandM = 8;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
@@ -154,7 +155,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     kbeg = 0;
     klen = args.K;
     bq += (int64_t)g * args.b_group_stride;
-    bsc += (int64_t)g * (args.b_group_stride / 32);
+    bsc += (int64_t)g * args.bs_group_stride;
   } else {
     a_row0 = (int64_t)tc.mt * BM;
     a_rows_valid = args.M - tc.mt * BM;
@@ -165,14 +166,18 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   if (a_rows_valid > BM) a_rows_valid = BM;
   const int nk = (klen + BK - 1) / BK;
   const uint32_t lda = (uint32_t)args.lda, ldb = (uint32_t)args.ldb;
-  const uint32_t lds_a = lda / 32, lds_b = ldb / 32;
   const int blk_last = (int)((kbeg + klen) / 32) - 1;  // last valid k block (clamp target)
+  const ScaleStrides sa = args.sa, sb = args.sb;
 
   // Operand tiles through buffer resources: rows past the valid ones read as 0.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.a + a_row0 * lda + kbeg, (int64_t)(a_rows_valid - 1) * lda + klen);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(bq + kbeg, (int64_t)(b_rows - 1) * ldb + klen);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(args.as + a_row0 * lds_a, (int64_t)a_rows_valid * lds_a);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bsc, (int64_t)b_rows * lds_b);
+  // Scales: A from the 32-row group of the tile's first row on (rows past the
+  // array read 0); B over the rows of B_g.
+  const int64_t a_grp0 = (a_row0 >> 5) * sa.grp;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(args.as + a_grp0, args.as_bytes - a_grp0);
+  const __amdgpu_buffer_rsrc_t rsb =
+      make_rsrc(bsc, MODE == MX_GROUP_M ? (int64_t)(b_rows >> 5) * sb.grp : args.bs_bytes);
 
   // first B row of tile row block r0 (a multiple of 8 rows): SwiGLU fwd pairs
   // gate rows [nt*128, +128) (tile rows 0..127) with up rows F + the same j
@@ -198,8 +203,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const int lch = (lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1));   // logical chunk this lane fetches
   const uint32_t va_off = (uint32_t)(lane >> 3) * lda + lch * 16;
   const uint32_t vb_off = (uint32_t)(lane >> 3) * ldb + lch * 16;
-  const uint32_t vsa_off = (uint32_t)l32 * lds_a;
-  const uint32_t vsb_off = (uint32_t)l32 * lds_b;
+  // per-lane scale offsets: A row a_row0 + 128*wm + 32*mi + l32 is lane row
+  // la = (a_row0 & 31) + l32 of 32-row group 4*wm + mi past the base
+  const uint32_t la = (uint32_t)(a_row0 & 31) + l32;
+  const uint32_t vsa_off = (la >> 5) * (uint32_t)sa.grp + (la & 31) * (uint32_t)sa.row;
+  const uint32_t vsb_off = (uint32_t)l32 * (uint32_t)sb.row;
+  // first 128-column step of this tile's k range in the scale layout
+  const int q_base = MODE == MX_GROUP_K ? (args.k_tiled ? args.groups.q0[slot] : (int)(kbeg >> 7)) : 0;
 
   v16f acc[4][4];
 #pragma unroll
@@ -219,10 +229,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const int blk0 = (int)((kbeg + k0) / 32);
     const __amdgpu_buffer_rsrc_t& rs = p < 4 ? rsb : rsa;
     const uint32_t voff = p < 4 ? vsb_off : vsa_off;
-    const uint32_t so = p < 4 ? b_row_base(nsub(p)) * lds_b : (uint32_t)(128 * wm + 32 * (p - 4)) * lds_a;
+    const uint32_t so = p < 4 ? (b_row_base(nsub(p)) >> 5) * (uint32_t)sb.grp
+                              : (uint32_t)(4 * wm + (p - 4)) * (uint32_t)sa.grp;
     uint32_t* dst = p < 4 ? sb_n[p] : sa_n[p - 4];
     if constexpr (SVEC) {
-      dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, so + blk0, 0);
+      // the scale word of this k-step: blocks 4q .. 4q+3 of the row
+      const uint32_t qo = (uint32_t)(q_base + (k0 >> 7)) * (uint32_t)(p < 4 ? sb.step : sa.step);
+      dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, so + qo, 0);
       dst[1] = 0;
     } else {
       // per-lane block index: blk0 + h (+2), clamped to the group's last block
@@ -256,11 +269,20 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
     return f;
   };
-  auto take_scales = [&]() __attribute__((always_inline)) {
+  // Hand the loaded scales of k-step kt to the MFMAs. Group-K scale words of a
+  // group's last, partial k-step carry bytes of blocks past the group, which
+  // are cleared (their codes are zero, but a NaN code would still poison the
+  // products).
+  auto take_scales = [&](int kt) __attribute__((always_inline)) {
+    uint32_t m = 0xFFFFFFFFu;
+    if constexpr (MODE == MX_GROUP_K && SVEC) {
+      const int rem = klen - kt * BK;
+      m = rem >= BK ? 0xFFFFFFFFu : (rem <= 0 ? 0u : (1u << (8 * (rem >> 5))) - 1u);
+    }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) { sb_c[s][0] = sb_n[s][0]; sb_c[s][1] = sb_n[s][1]; }
+    for (int s = 0; s < 4; ++s) { sb_c[s][0] = sb_n[s][0] & m; sb_c[s][1] = sb_n[s][1]; }
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) { sa_c[mi][0] = sa_n[mi][0]; sa_c[mi][1] = sa_n[mi][1]; }
+    for (int mi = 0; mi < 4; ++mi) { sa_c[mi][0] = sa_n[mi][0] & m; sa_c[mi][1] = sa_n[mi][1]; }
   };
   // byte-0-aligned scale register of k-step ks: block h (ks 0) or 2+h (ks 1)
   auto scale_of = [&](uint32_t c0, uint32_t c1, int ks) __attribute__((always_inline)) -> int {
@@ -268,44 +290,34 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     else return (int)(ks == 0 ? c0 : c1);
   };
   // MFMAs of one 128-wide k tile (2 MFMA k-steps x 4 m sub-tiles x 4 n
-  // sub-tiles). Fragment reads run one step ahead of the MFMAs that use them:
-  // the next A fragment is read under the current m sub-tile's 4 MFMAs, and
-  // the B fragments of k-step 1 under the last m sub-tile of k-step 0. Peak
-  // fragment registers: 2 x 4 B + 2 A fragments (80 VGPRs).
+  // sub-tiles) in 8 steps of 4 MFMAs. Fragment reads run ahead of the MFMAs
+  // that use them: A fragments two steps ahead (three registers sets), the B
+  // fragments of k-step 1 one per step during k-step 0. Each step also issues
+  // one slice of the next k-step's loads.
   auto compute = [&](const uint8_t* sA, const uint8_t* sB, int kt_next, uint8_t* nA, uint8_t* nB)
       __attribute__((always_inline)) {
-    v8i fb_c[4], fb_n[4], fa_c, fa_n;
+    v8i fb_c[4], fb_n[4], fa[3];
     static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
       constexpr int s = decltype(s_c)::value;
       fb_c[s] = read_frag(sB, nsub(s) + l32, 0);
     });
-    fa_c = read_frag(sA, 128 * wm + l32, 0);
+    fa[0] = read_frag(sA, 128 * wm + l32, 0);
+    fa[1] = read_frag(sA, 128 * wm + 32 + l32, 0);
     static_for<0, 8>([&](auto step_c) __attribute__((always_inline)) {
       constexpr int step = decltype(step_c)::value;
       constexpr int ks = step / 4, mi = step % 4;
       load_part(kt_next, nA, nB, step);
-      if constexpr (step < 7) fa_n = read_frag(sA, 128 * wm + 32 * ((step + 1) % 4) + l32, (step + 1) / 4);
-      if constexpr (step == 3) {
-        static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
-          constexpr int s = decltype(s_c)::value;
-          fb_n[s] = read_frag(sB, nsub(s) + l32, 1);
-        });
-      }
+      if constexpr (step + 2 < 8)
+        fa[(step + 2) % 3] = read_frag(sA, 128 * wm + 32 * ((step + 2) % 4) + l32, (step + 2) / 4);
+      if constexpr (step < 4) fb_n[step] = read_frag(sB, nsub(step) + l32, 1);
       static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         acc[s][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb_c[s], fa_c, acc[s][mi], 0, 0, 0, scale_of(sb_c[s][0], sb_c[s][1], ks), 0,
-            scale_of(sa_c[mi][0], sa_c[mi][1], ks));
+            ks == 0 ? fb_c[s] : fb_n[s], fa[step % 3], acc[s][mi], 0, 0, 0,
+            scale_of(sb_c[s][0], sb_c[s][1], ks), 0, scale_of(sa_c[mi][0], sa_c[mi][1], ks));
       });
       // fence: each step's slice of loads stays with its 4 MFMAs
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (step < 7) fa_c = fa_n;
-      if constexpr (step == 3) {
-        static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
-          constexpr int s = decltype(s_c)::value;
-          fb_c[s] = fb_n[s];
-        });
-      }
     });
   };
   // Zero the chunks of a staged k-step that lie past klen (the k tail of a
@@ -332,7 +344,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     compute(cA, cB, kt + 1, nA, nB);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    take_scales();
+    take_scales(kt + 1);
     __syncthreads();
     if ((klen & (BK - 1)) != 0 && kt + 2 == nk) {
       zero_tail(kt + 1, nA, nB);
@@ -343,7 +355,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   if (nk > 0) {
     load_full(0, sA0, sB0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    take_scales();
+    take_scales(0);
     __syncthreads();
     if ((klen & (BK - 1)) != 0 && nk == 1) {
       zero_tail(0, sA0, sB0);
@@ -413,8 +425,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // scale per column over the 32 rows (the lanes of a half-wave); the codes are
   // transposed inside each quad of lanes and staged in LDS as [column][row]
   // (stride kColStride), to be written out as column runs by flush_cols.
+  // Scales go to the k-tiled layouts: s_off is the rowwise byte of this lane's
+  // row, and the columnwise byte of block column c is sc_col0 + c * sc_ld.
   auto quantize_block = [&](const float (&d)[16], const __amdgpu_buffer_rsrc_t& rq, uint32_t q_off,
-                            const __amdgpu_buffer_rsrc_t& rs, uint32_t s_off, bool row_store,
+                            const __amdgpu_buffer_rsrc_t& rs, uint32_t s_off, bool row_store, bool s_store,
                             uint8_t* stage, const __amdgpu_buffer_rsrc_t& rsc, uint32_t sc_col0,
                             uint32_t sc_ld, bool col_store) __attribute__((always_inline)) {
     {
@@ -427,10 +441,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       uint32_t q[4];
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) q[vg] = e4m3x4(d[4 * vg] * inv, d[4 * vg + 1] * inv, d[4 * vg + 2] * inv, d[4 * vg + 3] * inv);
-      if (row_store) {
-        store_row_codes(rq, q_off, q);
-        if (h == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, s_off, 0, 0);
-      }
+      if (row_store) store_row_codes(rq, q_off, q);
+      if (s_store && h == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, s_off, 0, 0);
     }
     {
       uint32_t scv[16];
@@ -552,12 +564,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
     const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 ? args.h1 + m0 * 2 * F : nullptr, args.h1 ? (int64_t)wrows * 4 * F : 0);
     const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * F, (int64_t)wrows * F);
-    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row + m0 * (F / 32), (int64_t)wrows * (F / 32));
+    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row, (int64_t)((args.R + 31) >> 5) * args.nq_row * 128);
     const bool col_out = args.q_col != nullptr;
     const __amdgpu_buffer_rsrc_t rqc = make_rsrc(col_out ? args.q_col + (int64_t)jw0 * ldq + crow0 : nullptr,
                                                  col_out ? (int64_t)64 * ldq : 0);
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col + (int64_t)jw0 * (ldq / 32) + crow0 / 32 : nullptr,
-                                                 col_out ? (int64_t)64 * (ldq / 32) : 0);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col : nullptr,
+                                                 col_out ? (int64_t)(F >> 5) * args.nq_col * 128 : 0);
+    const uint32_t q0 = (uint32_t)args.groups.q0[slot];
     float w[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -573,21 +586,28 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         const bool jok = jw0 + 32 * s < (int)F;          // F % 32 == 0: whole block valid or not
+        // rows past the group's end are forced to 0 (they share columnwise
+        // blocks with valid rows up to the 32-row padding)
+        const bool rv = r < (uint32_t)wrows;
         float gv[16], uv[16], a[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           gv[v] = vgpr_hop(acc[s][mi][v]);
           uv[v] = vgpr_hop(acc[s + 2][mi][v]);
           const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[v]));
-          a[v] = w[mi] * (gv[v] * sig) * uv[v];
+          a[v] = rv ? w[mi] * (gv[v] * sig) * uv[v] : 0.0f;
         }
         if (args.h1 != nullptr && jok) {
           store_row_bf16(rh1, (r * 2 * F + jw0 + 32 * s) * 2, gv);
           store_row_bf16(rh1, (r * 2 * F + F + jw0 + 32 * s) * 2, uv);
         }
-        quantize_block(a, rqr, r * F + jw0 + 32 * s, rsr, r * (F / 32) + (jw0 + 32 * s) / 32, jok,
-                       slice + 32 * s * kColStride + 32 * (mi & 1), rsc, (uint32_t)(32 * s) * (ldq / 32) + mi,
-                       ldq / 32, blk_ok && jok);
+        const uint32_t m = (uint32_t)m0 + r;             // global row
+        const uint32_t b = (uint32_t)(jw0 + 32 * s) >> 5;   // block of the row
+        const uint32_t bl = ((uint32_t)wrow0 >> 5) + mi;     // block of the column inside the group
+        quantize_block(a, rqr, r * F + jw0 + 32 * s, rsr,
+                       ((m >> 5) * args.nq_row + (b >> 2)) * 128 + (m & 31) * 4 + (b & 3), jok, jok && r < (uint32_t)wrows,
+                       slice + 32 * s * kColStride + 32 * (mi & 1), rsc,
+                       (b * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
       });
       if constexpr (mi & 1) {
         if (col_out)
@@ -608,12 +628,12 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
     const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 + m0 * 2 * F, (int64_t)wrows * 4 * F);
     const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * 2 * F, (int64_t)wrows * 2 * F);
-    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row + m0 * (2 * F / 32), (int64_t)wrows * (2 * F / 32));
+    const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row, (int64_t)((args.R + 31) >> 5) * args.nq_row * 128);
     // columnwise dH1: gate half (columns j) and up half (columns F + j)
     const __amdgpu_buffer_rsrc_t rqc_g = make_rsrc(args.q_col + (int64_t)jw0 * ldq + crow0, (int64_t)128 * ldq);
     const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)128 * ldq);
-    const __amdgpu_buffer_rsrc_t rsc_g = make_rsrc(args.s_col + (int64_t)jw0 * (ldq / 32) + crow0 / 32, (int64_t)128 * (ldq / 32));
-    const __amdgpu_buffer_rsrc_t rsc_u = make_rsrc(args.s_col + (int64_t)(F + jw0) * (ldq / 32) + crow0 / 32, (int64_t)128 * (ldq / 32));
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(args.s_col, (int64_t)(2 * F >> 5) * args.nq_col * 128);
+    const uint32_t q0 = (uint32_t)args.groups.q0[slot];
     float w[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -641,6 +661,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         const bool jok = jw0 + 32 * s < (int)F;
+        const bool rv = r < (uint32_t)wrows;
         float dg[16], du[16];
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
@@ -651,16 +672,21 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
             const float da = vgpr_hop(acc[s][mi][4 * vg + i]);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
             const float sl = gv[i] * sg;
-            dg[4 * vg + i] = da * w[mi] * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg));
-            du[4 * vg + i] = da * w[mi] * sl;
-            dp += da * sl * uv[i];
+            dg[4 * vg + i] = rv ? da * w[mi] * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg)) : 0.0f;
+            du[4 * vg + i] = rv ? da * w[mi] * sl : 0.0f;
+            dp += jok ? da * sl * uv[i] : 0.0f;
           }
         }
         uint8_t* st = slice + 32 * s * kColStride + 32 * (mi & 1);
-        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, rsr, r * (2 * F / 32) + (jw0 + 32 * s) / 32, jok,
-                       st, rsc_g, (uint32_t)(32 * s) * (ldq / 32) + mi, ldq / 32, blk_ok && jok);
-        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, rsr, r * (2 * F / 32) + (F + jw0 + 32 * s) / 32, jok,
-                       st + kColHalf, rsc_u, (uint32_t)(32 * s) * (ldq / 32) + mi, ldq / 32, blk_ok && jok);
+        const uint32_t m = (uint32_t)m0 + r;
+        const uint32_t bg = (uint32_t)(jw0 + 32 * s) >> 5, bu = (uint32_t)(F + jw0 + 32 * s) >> 5;
+        const uint32_t bl = ((uint32_t)wrow0 >> 5) + mi;
+        const uint32_t srow = (m >> 5) * args.nq_row * 128 + (m & 31) * 4;
+        const bool s_ok = jok && r < (uint32_t)wrows;
+        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, rsr, srow + (bg >> 2) * 128 + (bg & 3), jok, s_ok,
+                       st, rsc, (bg * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
+        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, rsr, srow + (bu >> 2) * 128 + (bu & 3), jok, s_ok,
+                       st + kColHalf, rsc, (bu * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
       });
       dpsum[mi] = sum_halves(dp);
       if constexpr (mi & 1) {
@@ -716,8 +742,8 @@ hipError_t launch_gemm(int mode, int epi, bool scale_dword, const GemmArgs& args
     }
   } else {
     switch (epi) {
-      case EPI_F32: return launch_mode_epi<MX_GROUP_K, EPI_F32>(false, args, total_tiles, stream);
-      case EPI_BF16: return launch_mode_epi<MX_GROUP_K, EPI_BF16>(false, args, total_tiles, stream);
+      case EPI_F32: return launch_mode_epi<MX_GROUP_K, EPI_F32>(scale_dword, args, total_tiles, stream);
+      case EPI_BF16: return launch_mode_epi<MX_GROUP_K, EPI_BF16>(scale_dword, args, total_tiles, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -10,12 +10,33 @@ namespace mx {
 
 constexpr int kMaxGroups = MX_MAX_GROUPS;
 
+// Two layouts of the E8M0 scales of a code matrix [rows, K]:
+//  - row-major: byte (r, b) at r * (K/32) + b (the public layout);
+//  - k-tiled: K is cut into groups (the columnwise layouts' per-expert
+//    segments; one group for a rowwise matrix), each group into steps of 128
+//    columns (4 blocks) numbered q = q0(group) + b_local/4 over all groups
+//    (nq steps in total), and byte (r, b) sits at
+//      ((r >> 5) * nq + q) * 128 + (r & 31) * 4 + b_local % 4,
+//    so the scales of 32 consecutive rows for one 128-column step are one
+//    contiguous 128-byte line. Bytes of blocks past a group's end in its last
+//    step are unspecified.
+// Scale address generator used by the kernels for one operand:
+//   step word of row r, step q = (r >> 5) * grp + (r & 31) * row + q * step.
+struct ScaleStrides {
+  int64_t grp;                      // bytes per 32-row group
+  int32_t row;                      // bytes per row inside a group
+  int32_t step;                     // bytes per 128-column step
+};
+inline ScaleStrides row_major_scales(int64_t ld) { return {32 * (ld / 32), (int32_t)(ld / 32), 4}; }
+inline ScaleStrides k_tiled_scales(int64_t nq) { return {nq * 128, 4, 128}; }
+
 // Row groups of a quantize call (kernel argument, passed by value).
 struct QuantGroups {
   int32_t n;                        // number of groups (>= 1)
   int32_t row0[kMaxGroups + 1];     // first row of group g
   int32_t pcol0[kMaxGroups + 1];    // first column of group g in the columnwise layout
   int32_t tile0[kMaxGroups + 1];    // first row-tile of group g (prefix of ceil(m_g/128))
+  int32_t q0[kMaxGroups + 1];       // k-tiled columnwise scales: first 128-column step of group g
 };
 
 struct QuantArgs {
@@ -27,6 +48,10 @@ struct QuantArgs {
   int64_t cols;
   int64_t ld_col;                   // leading dimension of the columnwise codes (sum P)
   int32_t n_col_tiles;
+  int32_t tiled;                    // scales in the k-tiled layout (both copies)
+  int32_t nq_row;                   // k-tiled rowwise scales: cols / 128
+  int32_t nq_col;                   // k-tiled columnwise scales: steps over all groups
+  int32_t rows;                     // total rows (k-tiled rowwise: pad rows up to a multiple of 32 get 0)
   QuantGroups groups;
 };
 
@@ -52,6 +77,7 @@ struct GemmGroups {
   int32_t a0[kMaxGroups];
   int32_t len[kMaxGroups];
   int32_t pc0[kMaxGroups];          // first column of the group in columnwise layouts
+  int32_t q0[kMaxGroups];           // first 128-column step of the group in k-tiled scales
 };
 
 struct GemmArgs {
@@ -61,7 +87,11 @@ struct GemmArgs {
   const uint8_t* bs;
   void* c;
   int64_t lda, ldb, ldc;
-  int64_t b_group_stride;           // codes; scales use b_group_stride/32
+  int64_t b_group_stride;           // codes of consecutive B groups (MX_GROUP_M)
+  int64_t bs_group_stride;          // scales of consecutive B groups (MX_GROUP_M)
+  ScaleStrides sa, sb;              // scale addressing of A and B
+  int32_t k_tiled;                  // scales k-tiled (MX_GROUP_K: steps from groups.q0)
+  int64_t as_bytes, bs_bytes;       // extent of the A and B scale arrays
   int64_t c_group_stride;
   int32_t M;                        // rows of C in MX_GROUP_K (A rows)
   int32_t N;                        // columns of C (B rows); SwiGLU fwd: 2F
@@ -77,6 +107,8 @@ struct GemmArgs {
   uint8_t* s_row;
   uint8_t* q_col;                   // fwd: A columnwise [F, ld_col]; bwd: dH1 [2F, ld_col]
   uint8_t* s_col;
+  int32_t nq_row;                   // k-tiled epilogue scales: steps of the rowwise output
+  int32_t nq_col;                   // k-tiled epilogue scales: steps of the columnwise output
   float* dprobs_part;               // bwd: [n_tiles_n, R] partial sums
   int32_t R;                        // rows of the routed activations
   GemmGroups groups;

@@ -13,6 +13,8 @@
 // LDS row, conflict-free) and writes 32 contiguous code bytes per column.
 // Row tiles restart at each group's first row so columnwise blocks never
 // straddle groups; rows past the group's end are zeros (padding codes 0x00).
+// Scales go to the row-major layout or, for the fused MLP's internal
+// buffers, to the k-tiled layout (see ScaleStrides).
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -44,6 +46,13 @@ template <>
 __device__ __forceinline__ void unpack16<float>(const uint4& raw, float* v) {
   v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
   v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+}
+
+// Offset of the rowwise scale of (row r, block b) in the row-major or
+// k-tiled layout.
+__device__ __forceinline__ int64_t row_scale_offset(const QuantArgs& args, int64_t r, int b) {
+  if (args.tiled) return ((r >> 5) * args.nq_row + (b >> 2)) * 128 + (r & 31) * 4 + (b & 3);
+  return r * (args.cols / 32) + b;
 }
 
 template <typename T>
@@ -108,7 +117,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
         } else {
           *reinterpret_cast<uint32_t*>(qd) = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
         }
-        if ((cc % TPB) == 0) args.s_row[grow * (cols / 32) + col / 32] = (uint8_t)sc;
+        if ((cc % TPB) == 0) args.s_row[row_scale_offset(args, grow, col / 32)] = (uint8_t)sc;
+      } else if (args.tiled && col_ok && (cc % TPB) == 0 && grow >= args.rows && grow < ((args.rows + 31) & ~31)) {
+        // k-tiled: the pad rows of the last 32-row group get scale 0 (2^-127)
+        args.s_row[row_scale_offset(args, grow, col / 32)] = 0;
       }
     }
   }
@@ -153,7 +165,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
     uint8_t* qd = args.q_col + colc * args.ld_col + qc0;
     *reinterpret_cast<uint4*>(qd) = w0;
     *reinterpret_cast<uint4*>(qd + 16) = w1;
-    args.s_col[colc * (args.ld_col / 32) + qc0 / 32] = (uint8_t)sc;
+    if (args.tiled) {
+      const int bl = (tile_r0 + rb * 32) >> 5;       // block index inside the group
+      args.s_col[((colc >> 5) * args.nq_col + args.groups.q0[g] + (bl >> 2)) * 128 + (colc & 31) * 4 + (bl & 3)] =
+          (uint8_t)sc;
+    } else {
+      args.s_col[colc * (args.ld_col / 32) + qc0 / 32] = (uint8_t)sc;
+    }
   }
 }
 

@@ -77,7 +77,7 @@ def test_gemm_argument_errors(L):
     assert _g(L, a=ctypes.c_void_p(0x100004)) == EALIGN
 
 
-def _dims(E=2, R=64, H=64, F=96):
+def _dims(E=2, R=64, H=128, F=128):
     return mx._Dims(E, R, H, F)
 
 
@@ -88,11 +88,12 @@ def test_mlp_sizes_and_errors(L):
                                ctypes.byref(s), ctypes.byref(b)) == OK
     assert f.value > 0 and s.value > 0 and b.value > 0
     # sizes grow with R and cover at least the dominant buffers
-    R, H, F, E = 64, 64, 96, 2
+    R, H, F, E = 64, 128, 128, 2
     assert f.value >= E * 2 * F * H + E * H * F + R * H + R * F
     assert s.value >= R * 2 * F * 2
     assert L.grouped_mlp_sizes(ctypes.byref(d), mx._i64_array([40, 20]), None, None, None) == ESHAPE
     assert L.grouped_mlp_sizes(ctypes.byref(_dims(H=48)), mx._i64_array([40, 24]), None, None, None) == ESHAPE
+    assert L.grouped_mlp_sizes(ctypes.byref(_dims(F=96)), mx._i64_array([40, 24]), None, None, None) == ESHAPE
     assert L.grouped_mlp_sizes(None, mx._i64_array([40, 24]), None, None, None) == EINVAL
     assert L.grouped_mlp_sizes(ctypes.byref(_dims(E=0)), mx._i64_array([64]), None, None, None) == EINVAL
     ws = ctypes.c_void_p(0x100000)
