@@ -38,7 +38,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "lib", "libmxfp8.so")
+    """The built library: lib/libmxfp8.so in the package, or the file named by
+    the MXFP8_AMD_LIB environment variable (another build of the same sources)."""
+    return os.environ.get("MXFP8_AMD_LIB") or os.path.join(_HERE, "lib", "libmxfp8.so")
 
 
 class MXError(RuntimeError):

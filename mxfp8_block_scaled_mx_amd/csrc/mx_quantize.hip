@@ -5,12 +5,15 @@
 // Key technical approaches item 2).
 //
 // Tile: 128 rows x 256 bytes of input (128 bf16 or 64 fp32 columns), 256
-// threads. Each thread loads 16 contiguous bytes per pass (a 16-thread row
-// segment is 256 contiguous bytes, fully coalesced); the 4 (bf16) or 8 (fp32)
-// threads of one 32-block reduce their amax with two or three xor shuffles.
-// The tile is staged in LDS unchanged; the columnwise phase then reads 32
-// values down each column (consecutive lanes read consecutive dwords of one
-// LDS row, conflict-free) and writes 32 contiguous code bytes per column.
+// threads. Each thread issues all 8 of its 16-byte loads first (a 16-thread
+// row segment is 256 contiguous bytes); the 4 (bf16) or 8 (fp32) threads of
+// one 32-block reduce their amax with two or three xor shuffles and store the
+// rowwise codes directly. The tile is staged in LDS unchanged; the columnwise
+// phase reads 32 values down each column (consecutive lanes read consecutive
+// dwords of one LDS row, conflict-free), stages the codes as [column][row] in
+// LDS and writes each column's 128 tile rows as one run. Scales of a row (a
+// column) within the tile are gathered into one word, so the k-tiled layout
+// receives whole 128-byte lines.
 // Row tiles restart at each group's first row so columnwise blocks never
 // straddle groups; rows past the group's end are zeros (padding codes 0x00).
 // Scales go to the row-major layout or, for the fused MLP's internal
@@ -48,131 +51,201 @@ __device__ __forceinline__ void unpack16<float>(const uint4& raw, float* v) {
   v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
 }
 
-// Offset of the rowwise scale of (row r, block b) in the row-major or
-// k-tiled layout.
-__device__ __forceinline__ int64_t row_scale_offset(const QuantArgs& args, int64_t r, int b) {
-  if (args.tiled) return ((r >> 5) * args.nq_row + (b >> 2)) * 128 + (r & 31) * 4 + (b & 3);
-  return r * (args.cols / 32) + b;
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
   constexpr int VPT = QTraits<T>::kVals;
   constexpr int TC = QTraits<T>::kCols;
   constexpr int TR = kQuantTileRows;
-  constexpr int TPB = 32 / VPT;  // threads per 32-block along a row
-  __shared__ __attribute__((aligned(16))) uint8_t tile[TR * 256];
+  constexpr int TPB = 32 / VPT;              // threads per 32-block along a row
+  constexpr int NB = TC / 32;                // 32-blocks per tile row (4 bf16, 2 f32)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TR * 256];   // input tile, as loaded
+  // columnwise codes [column][row], in the input tile's memory once the
+  // columns are in registers; the 16-byte pad per column spreads the 16-byte
+  // writes of consecutive column pairs over the LDS banks
+  constexpr int CST = TR + 16;
+  static_assert(TC * CST <= TR * 256, "columnwise staging must fit the input tile");
+  uint8_t* const ctile = tile;
+  __shared__ uint8_t rs_t[TR * 4];           // rowwise scales [row][block]
+  __shared__ uint8_t cs_t[TC * 4];           // columnwise scales [column][block]
 
   const int tid = threadIdx.x;
-  const int ct = blockIdx.x % args.n_col_tiles;
-  const int rt_global = blockIdx.x / args.n_col_tiles;
+  const int cc = tid & 15;                     // 16-byte chunk within the row segment
+  const int64_t cols = args.cols;
+  const T* x = reinterpret_cast<const T*>(args.x);
 
-  // group of this row tile
-  int g = 0;
-  {
-    int lo = 0, hi = args.groups.n - 1;
-    while (lo < hi) {  // last g with tile0[g] <= rt_global
+  struct Loc {
+    int g, tile_r0, m_g, col_base;
+    int64_t grow0;
+  };
+  auto locate = [&](int t) __attribute__((always_inline)) -> Loc {
+    Loc L;
+    const int ct = t % args.n_col_tiles;
+    const int rt_global = t / args.n_col_tiles;
+    int lo = 0, hi = args.groups.n - 1;        // last group with tile0 <= rt_global
+    while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
       if (args.groups.tile0[mid] <= rt_global) lo = mid; else hi = mid - 1;
     }
-    g = lo;
-  }
-  const int rt = rt_global - args.groups.tile0[g];
-  const int64_t grow0 = args.groups.row0[g];
-  const int m_g = args.groups.row0[g + 1] - args.groups.row0[g];
-  const int tile_r0 = rt * TR;                 // first row of the tile within the group
-  const int64_t cols = args.cols;
-  const int col_base = ct * TC;
-
-  const T* x = reinterpret_cast<const T*>(args.x);
-  const int cc = tid & 15;                     // 16-byte chunk within the row segment
-  const int col = col_base + cc * VPT;
-  const bool col_ok = col < cols;
-
-#pragma unroll 2
-  for (int p = 0; p < TR / 16; ++p) {
-    const int r = p * 16 + (tid >> 4);
-    const bool row_ok = (tile_r0 + r) < m_g;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    const int64_t grow = grow0 + tile_r0 + r;
-    if (row_ok && col_ok) raw = *reinterpret_cast<const uint4*>(x + grow * cols + col);
-    *reinterpret_cast<uint4*>(tile + r * 256 + cc * 16) = raw;
-    if (args.q_row != nullptr) {
-      float v[VPT];
-      unpack16<T>(raw, v);
-      uint32_t am = 0;
+    L.g = lo;
+    L.tile_r0 = (rt_global - args.groups.tile0[lo]) * TR;   // first row of the tile within the group
+    L.grow0 = args.groups.row0[lo];
+    L.m_g = args.groups.row0[lo + 1] - args.groups.row0[lo];
+    L.col_base = ct * TC;
+    return L;
+  };
+  // the tile's 8 x 16 bytes per thread, all requested at once
+  auto load = [&](const Loc& L, uint4 (&raw)[TR / 16]) __attribute__((always_inline)) {
+    const int col = L.col_base + cc * VPT;
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) am = umax(am, abs_bits(v[i]));
+    for (int p = 0; p < TR / 16; ++p) {
+      const int r = p * 16 + (tid >> 4);
+      raw[p] = make_uint4(0, 0, 0, 0);
+      if ((L.tile_r0 + r) < L.m_g && col < cols)
+        raw[p] = *reinterpret_cast<const uint4*>(x + (L.grow0 + L.tile_r0 + r) * cols + col);
+    }
+  };
+  auto process = [&](const Loc& L, const uint4 (&raw)[TR / 16]) __attribute__((always_inline)) {
+    const int g = L.g, tile_r0 = L.tile_r0, m_g = L.m_g, col_base = L.col_base;
+    const int64_t grow0 = L.grow0;
+    const int col = col_base + cc * VPT;
+    const bool col_ok = col < cols;
 #pragma unroll
-      for (int s = 1; s < TPB; s <<= 1) am = umax(am, xor_u32(am, s));
-      const uint32_t sc = scale_code_from_amax_bits(am);
-      const float inv = inv_scale_from_code(sc);
-      if (row_ok && col_ok) {
-        uint8_t* qd = args.q_row + grow * cols + col;
-        if constexpr (VPT == 8) {
-          uint2 w;
-          w.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-          w.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-          *reinterpret_cast<uint2*>(qd) = w;
-        } else {
-          *reinterpret_cast<uint32_t*>(qd) = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    for (int p = 0; p < TR / 16; ++p) {
+      const int r = p * 16 + (tid >> 4);
+      const bool row_ok = (tile_r0 + r) < m_g;
+      const int64_t grow = grow0 + tile_r0 + r;
+      *reinterpret_cast<uint4*>(tile + r * 256 + cc * 16) = raw[p];
+      if (args.q_row != nullptr) {
+        float v[VPT];
+        unpack16<T>(raw[p], v);
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) am = umax(am, abs_bits(v[i]));
+#pragma unroll
+        for (int s = 1; s < TPB; s <<= 1) am = umax(am, xor_u32(am, s));
+        const uint32_t sc = scale_code_from_amax_bits(am);
+        const float inv = inv_scale_from_code(sc);
+        if (row_ok && col_ok) {
+          uint8_t* qd = args.q_row + grow * cols + col;
+          if constexpr (VPT == 8) {
+            uint2 w;
+            w.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            w.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            *reinterpret_cast<uint2*>(qd) = w;
+          } else {
+            *reinterpret_cast<uint32_t*>(qd) = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+          }
         }
-        if ((cc % TPB) == 0) args.s_row[row_scale_offset(args, grow, col / 32)] = (uint8_t)sc;
-      } else if (args.tiled && col_ok && (cc % TPB) == 0 && grow >= args.rows && grow < ((args.rows + 31) & ~31)) {
-        // k-tiled: the pad rows of the last 32-row group get scale 0 (2^-127)
-        args.s_row[row_scale_offset(args, grow, col / 32)] = 0;
+        if ((cc % TPB) == 0) rs_t[r * 4 + cc / TPB] = (uint8_t)sc;
       }
     }
-  }
-  if (args.q_col == nullptr) return;
-  __syncthreads();
+    __syncthreads();
 
-  // columnwise: unit = (column slot, 32-row block); 4 row blocks x 64 slots
-  const int rb = tid >> 6;
-  const int slot = tid & 63;
-  if (tile_r0 + rb * 32 >= m_g) return;        // block entirely past the group: not in the layout
-  const int64_t qc0 = args.groups.pcol0[g] + tile_r0 + rb * 32;
-  constexpr int CPS = 4 / sizeof(T) > 0 ? 4 / (int)sizeof(T) : 1;  // columns per dword
-  float v[CPS][32];
+    // rowwise scales of the tile: one word (the tile's blocks) per row
+    if (args.q_row != nullptr && tid < TR) {
+      const int r = tid;
+      const int64_t grow = grow0 + tile_r0 + r;
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(rs_t + r * 4);
+      const int b0 = col_base / 32;             // first block of the tile in the row
+      if (tile_r0 + r < m_g) {
+        if (args.tiled) {
+          uint8_t* sd = args.s_row + ((grow >> 5) * args.nq_row + (b0 >> 2)) * 128 + (grow & 31) * 4 + (b0 & 3);
+          if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = word;
+          else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)word;
+        } else {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * 256 + slot * 4);
-    if constexpr (CPS == 2) {
-      v[0][i] = bf16_lo(w);
-      v[1][i] = bf16_hi(w);
-    } else {
-      v[0][i] = __uint_as_float(w);
+          for (int j = 0; j < NB; ++j)
+            if (col_base + 32 * j < cols) args.s_row[grow * (cols / 32) + b0 + j] = (uint8_t)(word >> (8 * j));
+        }
+      } else if (args.tiled && grow >= args.rows && grow < ((args.rows + 31) & ~31)) {
+        // k-tiled: the pad rows of the last 32-row group get scale 0 (2^-127)
+        uint8_t* sd = args.s_row + ((grow >> 5) * args.nq_row + (b0 >> 2)) * 128 + (grow & 31) * 4 + (b0 & 3);
+        if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = 0;
+        else *reinterpret_cast<uint16_t*>(sd) = 0;
+      }
     }
-  }
+    if (args.q_col != nullptr) {
+    // columnwise: unit = (column slot, 32-row block); 4 row blocks x 64 slots.
+    // Codes go to ctile[column][row], scales to cs_t[column][block].
+    {
+      const int rb = tid >> 6;
+      const int slot = tid & 63;
+      constexpr int CPS = 4 / sizeof(T) > 0 ? 4 / (int)sizeof(T) : 1;  // columns per dword
+      float v[CPS][32];
 #pragma unroll
-  for (int c = 0; c < CPS; ++c) {
-    const int64_t colc = col_base + slot * CPS + c;
-    if (colc >= cols) continue;
-    uint32_t am = 0;
+      for (int i = 0; i < 32; ++i) {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * 256 + slot * 4);
+        if constexpr (CPS == 2) {
+          v[0][i] = bf16_lo(w);
+          v[1][i] = bf16_hi(w);
+        } else {
+          v[0][i] = __uint_as_float(w);
+        }
+      }
+      __syncthreads();                           // every column read: the tile becomes ctile
 #pragma unroll
-    for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[c][i]));
-    const uint32_t sc = scale_code_from_amax_bits(am);
-    const float inv = inv_scale_from_code(sc);
-    uint4 w0, w1;
-    w0.x = e4m3x4(v[c][0] * inv, v[c][1] * inv, v[c][2] * inv, v[c][3] * inv);
-    w0.y = e4m3x4(v[c][4] * inv, v[c][5] * inv, v[c][6] * inv, v[c][7] * inv);
-    w0.z = e4m3x4(v[c][8] * inv, v[c][9] * inv, v[c][10] * inv, v[c][11] * inv);
-    w0.w = e4m3x4(v[c][12] * inv, v[c][13] * inv, v[c][14] * inv, v[c][15] * inv);
-    w1.x = e4m3x4(v[c][16] * inv, v[c][17] * inv, v[c][18] * inv, v[c][19] * inv);
-    w1.y = e4m3x4(v[c][20] * inv, v[c][21] * inv, v[c][22] * inv, v[c][23] * inv);
-    w1.z = e4m3x4(v[c][24] * inv, v[c][25] * inv, v[c][26] * inv, v[c][27] * inv);
-    w1.w = e4m3x4(v[c][28] * inv, v[c][29] * inv, v[c][30] * inv, v[c][31] * inv);
-    uint8_t* qd = args.q_col + colc * args.ld_col + qc0;
-    *reinterpret_cast<uint4*>(qd) = w0;
-    *reinterpret_cast<uint4*>(qd + 16) = w1;
-    if (args.tiled) {
-      const int bl = (tile_r0 + rb * 32) >> 5;       // block index inside the group
-      args.s_col[((colc >> 5) * args.nq_col + args.groups.q0[g] + (bl >> 2)) * 128 + (colc & 31) * 4 + (bl & 3)] =
-          (uint8_t)sc;
-    } else {
-      args.s_col[colc * (args.ld_col / 32) + qc0 / 32] = (uint8_t)sc;
+      for (int c = 0; c < CPS; ++c) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[c][i]));
+        const uint32_t sc = scale_code_from_amax_bits(am);
+        const float inv = inv_scale_from_code(sc);
+        uint4 w0, w1;
+        w0.x = e4m3x4(v[c][0] * inv, v[c][1] * inv, v[c][2] * inv, v[c][3] * inv);
+        w0.y = e4m3x4(v[c][4] * inv, v[c][5] * inv, v[c][6] * inv, v[c][7] * inv);
+        w0.z = e4m3x4(v[c][8] * inv, v[c][9] * inv, v[c][10] * inv, v[c][11] * inv);
+        w0.w = e4m3x4(v[c][12] * inv, v[c][13] * inv, v[c][14] * inv, v[c][15] * inv);
+        w1.x = e4m3x4(v[c][16] * inv, v[c][17] * inv, v[c][18] * inv, v[c][19] * inv);
+        w1.y = e4m3x4(v[c][20] * inv, v[c][21] * inv, v[c][22] * inv, v[c][23] * inv);
+        w1.z = e4m3x4(v[c][24] * inv, v[c][25] * inv, v[c][26] * inv, v[c][27] * inv);
+        w1.w = e4m3x4(v[c][28] * inv, v[c][29] * inv, v[c][30] * inv, v[c][31] * inv);
+        const int cl = slot * CPS + c;           // column inside the tile
+        *reinterpret_cast<uint4*>(ctile + cl * CST + rb * 32) = w0;
+        *reinterpret_cast<uint4*>(ctile + cl * CST + rb * 32 + 16) = w1;
+        cs_t[cl * 4 + rb] = (uint8_t)sc;
+      }
     }
-  }
+    __syncthreads();
+
+    // Columnwise codes: each column's 128 tile rows are one contiguous run of the
+    // layout; 8 lanes x 16 bytes per column. Blocks past the group's end are not
+    // part of the layout (the next group's columns start there).
+    const int64_t qc0 = args.groups.pcol0[g] + tile_r0;
+#pragma unroll
+    for (int it = 0; it < TC * 8 / 256; ++it) {
+      const int c = it * 256 + tid;
+      const int cl = c >> 3, part = c & 7;
+      const int64_t colc = col_base + cl;
+      const uint4 w = *reinterpret_cast<const uint4*>(ctile + cl * CST + part * 16);
+      if (colc < cols && tile_r0 + 32 * (part >> 1) < m_g)
+        *reinterpret_cast<uint4*>(args.q_col + colc * args.ld_col + qc0 + part * 16) = w;
+    }
+    // columnwise scales: one word (the tile's 4 blocks) per column
+    if (tid < TC) {
+      const int cl = tid;
+      const int64_t colc = col_base + cl;
+      if (colc < cols) {
+        uint32_t word = *reinterpret_cast<const uint32_t*>(cs_t + cl * 4);
+        if (args.tiled) {
+          // blocks past the group's end in its last step are cleared
+          const int nvalid = (m_g - tile_r0 + 31) >> 5;
+          if (nvalid < 4) word &= (1u << (8 * nvalid)) - 1u;
+          *reinterpret_cast<uint32_t*>(args.s_col + ((colc >> 5) * args.nq_col + args.groups.q0[g] + (tile_r0 >> 7)) * 128 +
+                                       (colc & 31) * 4) = word;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (tile_r0 + 32 * j < m_g) args.s_col[colc * (args.ld_col / 32) + qc0 / 32 + j] = (uint8_t)(word >> (8 * j));
+        }
+      }
+    }
+    }
+    };
+
+  const Loc cur = locate(blockIdx.x);
+  uint4 raw[TR / 16];
+  load(cur, raw);
+  process(cur, raw);
 }
 
 hipError_t launch_quantize(const QuantArgs& args, int x_dtype, int total_row_tiles, hipStream_t stream) {
