@@ -234,17 +234,54 @@ void use_k_tiled_scales(GemmPlan& p, int64_t nq_a, int64_t a_rows, int64_t nq_b,
   p.scale_dword = true;
 }
 
+// Number of compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Split-K tail of a plain group-M plan: when the last round of tiles would
+// leave at least half of the CUs idle, each tail tile's k-steps are split
+// into parts that run as separate workgroups, writing fp32 partials to ws;
+// launch_split_reduce then forms C. Returns the number of tail tiles (0: no
+// split; the plan is unchanged).
+size_t split_ws_bytes(int64_t tiles) { return (size_t)std::min<int64_t>(tiles, mx::kMaxSplitTiles) * mx::kMaxSplitParts * mx::kTileM * mx::kTileN * 4; }
+
+int plan_split_tail(GemmPlan& p, int64_t K, float* ws, size_t ws_bytes) {
+  const int n_cu = device_cu_count();
+  const int T = p.total_tiles;
+  if (n_cu <= 0 || T == 0 || K % mx::kTileK) return 0;
+  const int F = T / n_cu * n_cu, R = T - F;
+  if (R == 0 || R > n_cu / 2 || R > mx::kMaxSplitTiles) return 0;
+  const int nk = (int)(K / mx::kTileK);
+  const int S = std::min({mx::kMaxSplitParts, n_cu / R, nk / 4});
+  if (S < 2 || (size_t)R * S * mx::kTileM * mx::kTileN * 4 > ws_bytes) return 0;
+  p.args.split_f = F;
+  p.args.split_s = S;
+  p.args.split_ws = ws;
+  p.total_tiles = F + R * S;
+  return R;
+}
+
 // ---------------------------------------------------------------- fused MLP plan
 struct MlpLayout {
   int E;
   int64_t R, H, F, sumP;
   std::vector<int64_t> split;
   // forward workspace
-  size_t xq, xs, w1q, w1s, w2q, w2s, aq, as, fwd_total;
+  size_t xq, xs, w1q, w1s, w2q, w2s, aq, as, split2, fwd_total;
   // saved for backward
   size_t xcq, xcs, h1, acq, acs, w1cq, w1cs, w2cq, w2cs, saved_total;
   // backward workspace
-  size_t dyq, dys, dycq, dycs, dhq, dhs, dhcq, dhcs, part, bwd_total;
+  size_t dyq, dys, dycq, dycs, dhq, dhs, dhcq, dhcs, part, split1, bwd_total;
+  size_t split2_bytes, split1_bytes;   // split-K tail partials of GEMM2 / dgrad1
   int64_t n_tiles_f;
   std::vector<int64_t> q0;   // k-tiled steps of the per-expert columnwise layouts
   int64_t nq;                // total steps (q0[E])
@@ -286,6 +323,12 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   L->w1q = take(c, E * 2 * F * H); L->w1s = take(c, E * 2 * F * H / 32);
   L->w2q = take(c, E * H * F); L->w2s = take(c, E * H * F / 32);
   L->aq = take(c, R * F); L->as = take(c, R32 * F / 32);
+  // GEMM2 and dgrad1 tiles: sum over experts of ceil(m_e/256) x ceil(H/256)
+  int64_t m_tiles = 0;
+  for (int e = 0; e < L->E; ++e) m_tiles += cdiv(split[e], mx::kTileM);
+  const int64_t h_tiles = m_tiles * cdiv(H, mx::kTileN);
+  L->split2_bytes = L->split1_bytes = split_ws_bytes(h_tiles);
+  L->split2 = take(c, L->split2_bytes);
   L->fwd_total = c;
   c = 0;
   L->xcq = take(c, H * P); L->xcs = take(c, H / 32 * NQ * 128);
@@ -301,6 +344,7 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   L->dhq = take(c, R * 2 * F); L->dhs = take(c, R32 * 2 * F / 32);
   L->dhcq = take(c, 2 * F * P); L->dhcs = take(c, 2 * F / 32 * NQ * 128);
   L->part = take(c, L->n_tiles_f * R * 4);
+  L->split1 = take(c, L->split1_bytes);
   L->bwd_total = c;
   return MX_OK;
 }
@@ -438,8 +482,13 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   st = run_gemm(p1, MX_GROUP_M, mx::EPI_SWIGLU_FWD, stream, "grouped_mlp_fwd gemm1");
   if (st != MX_OK) return st;
   stage_mark(4, stream);
-  st = run_gemm(p2, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_fwd gemm2");
-  if (st != MX_OK) return st;
+  {
+    const int tail = plan_split_tail(p2, F, reinterpret_cast<float*>(at(workspace, L.split2)), L.split2_bytes);
+    st = run_gemm(p2, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_fwd gemm2");
+    if (st != MX_OK) return st;
+    hipError_t e = mx::launch_split_reduce(mx::EPI_BF16, p2.args, tail, stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_fwd gemm2 split reduce");
+  }
   stage_mark(5, stream);
   return MX_OK;
 }
@@ -519,8 +568,13 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad2");
   if (st != MX_OK) return st;
   stage_mark(4, stream);
-  st = run_gemm(pd1, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_bwd dgrad1");
-  if (st != MX_OK) return st;
+  {
+    const int tail = plan_split_tail(pd1, 2 * F, reinterpret_cast<float*>(at(workspace, L.split1)), L.split1_bytes);
+    st = run_gemm(pd1, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_bwd dgrad1");
+    if (st != MX_OK) return st;
+    hipError_t e = mx::launch_split_reduce(mx::EPI_BF16, pd1.args, tail, stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dgrad1 split reduce");
+  }
   stage_mark(5, stream);
   st = run_gemm(pw1, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad1");
   if (st != MX_OK) return st;

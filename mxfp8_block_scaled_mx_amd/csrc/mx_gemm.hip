@@ -136,7 +136,16 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int id = xcd_remap(blockIdx.x, total_tiles);
+  // Work unit of this workgroup: a whole tile, or (split-K tail) part
+  // `part` of tile id's k-steps, written as an fp32 partial tile.
+  int id, part = 0, split_unit = -1;
+  if (args.split_s > 1 && (int)blockIdx.x >= args.split_f) {
+    split_unit = (int)blockIdx.x - args.split_f;
+    id = args.split_f + split_unit / args.split_s;
+    part = split_unit % args.split_s;
+  } else {
+    id = xcd_remap(blockIdx.x, args.split_s > 1 ? args.split_f : total_tiles);
+  }
   const TileCoord tc = locate_tile(args.groups, id, MODE, args.M, args.n_tiles_n);
   const int slot = tc.slot;
   const int g = args.groups.gid[slot];
@@ -164,7 +173,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   }
   b_rows = EPI == EPI_SWIGLU_FWD ? 2 * args.F : args.N;
   if (a_rows_valid > BM) a_rows_valid = BM;
-  const int nk = (klen + BK - 1) / BK;
+  const int nk_all = (klen + BK - 1) / BK;
+  // k-steps [kt_lo, kt_hi) of this work unit
+  const int kt_lo = split_unit >= 0 ? part * nk_all / args.split_s : 0;
+  const int kt_hi = split_unit >= 0 ? (part + 1) * nk_all / args.split_s : nk_all;
   const uint32_t lda = (uint32_t)args.lda, ldb = (uint32_t)args.ldb;
   const int blk_last = (int)((kbeg + klen) / 32) - 1;  // last valid k block (clamp target)
   const ScaleStrides sa = args.sa, sb = args.sb;
@@ -346,26 +358,26 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     take_scales(kt + 1);
     __syncthreads();
-    if ((klen & (BK - 1)) != 0 && kt + 2 == nk) {
+    if ((klen & (BK - 1)) != 0 && kt + 2 == kt_hi) {
       zero_tail(kt + 1, nA, nB);
       __syncthreads();
     }
   };
 
-  if (nk > 0) {
-    load_full(0, sA0, sB0);
+  if (kt_hi > kt_lo) {
+    load_full(kt_lo, sA0, sB0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    take_scales(0);
+    take_scales(kt_lo);
     __syncthreads();
-    if ((klen & (BK - 1)) != 0 && nk == 1) {
-      zero_tail(0, sA0, sB0);
+    if ((klen & (BK - 1)) != 0 && kt_lo + 1 == kt_hi) {
+      zero_tail(kt_lo, sA0, sB0);
       __syncthreads();
     }
   }
-  // k-step kt lives in stage kt & 1
-  for (int kt = 0; kt < nk; kt += 2) {
+  // k-step kt_lo + j lives in stage j & 1
+  for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     kstep(kt, sA0, sB0, sA1, sB1);
-    if (kt + 1 < nk) kstep(kt + 1, sA1, sB1, sA0, sB0);
+    if (kt + 1 < kt_hi) kstep(kt + 1, sA1, sB1, sA0, sB0);
   }
 
   // ---------------------------------------------------------------- epilogues
@@ -488,6 +500,28 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     if (MODE == MX_GROUP_K && klen == 0 && args.accumulate) return;
+    if (MODE == MX_GROUP_M && split_unit >= 0) {
+      // split-K part: the whole 256 x 256 fp32 partial, row-major, into its
+      // workspace slot (the reduce kernel adds the parts and writes C)
+      const __amdgpu_buffer_rsrc_t rw =
+          make_rsrc(args.split_ws + (int64_t)split_unit * BM * BN + (BM / 2) * wm * BN + (BN / 2) * wn,
+                    (int64_t)(BM / 2) * BN * 4);
+      static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
+        constexpr int mi = decltype(mi_c)::value;
+        static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int s = decltype(s_c)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
+            constexpr int vg = decltype(vg_c)::value;
+            u32x4 o;
+            o.x = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 0])); o.y = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 1]));
+            o.z = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 2])); o.w = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 3]));
+            __builtin_amdgcn_raw_buffer_store_b128(o, rw, ((uint32_t)(32 * mi + l32) * BN + 32 * s + 8 * vg + 4 * h) * 4, 0, 0);
+          });
+        });
+      });
+      return;
+    }
     constexpr int esz = EPI == EPI_F32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)args.ldc;
     const int64_t col0 = (int64_t)tc.nt * BN + (BN / 2) * wn;
@@ -721,6 +755,45 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* part, f
   out[r] = s;
 }
 
+// Split-K tail: tile args.split_f + blockIdx.x is the sum of its
+// args.split_s fp32 partials (added in part order); write it as C (bf16, or
+// fp32 with optional accumulate) over the tile's valid rows and columns.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs args) {
+  const int id = args.split_f + (int)blockIdx.x;
+  const TileCoord tc = locate_tile(args.groups, id, MX_GROUP_M, args.M, args.n_tiles_n);
+  const int slot = tc.slot;
+  const int64_t a_row0 = (int64_t)args.groups.a0[slot] + (int64_t)tc.mt * BM;
+  const int rows_valid = min(BM, args.groups.len[slot] - tc.mt * BM);
+  const int64_t col0 = (int64_t)tc.nt * BN;
+  const int S = args.split_s;
+  const float* ws = args.split_ws + (int64_t)blockIdx.x * S * BM * BN;
+  for (int it = 0; it < BM * BN / 1024; ++it) {
+    const int e = it * 1024 + (int)threadIdx.x * 4;
+    const int r = e / BN, c = e % BN;
+    float4 sum = *reinterpret_cast<const float4*>(ws + e);
+    for (int p = 1; p < S; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)p * BM * BN + e);
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    if (r >= rows_valid || col0 + c >= args.N) continue;
+    const int64_t o = (a_row0 + r) * args.ldc + col0 + c;
+    if constexpr (EPI == EPI_BF16) {
+      uint2 w;
+      w.x = pack_bf16x2(sum.x, sum.y);
+      w.y = pack_bf16x2(sum.z, sum.w);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(args.c) + o) = w;
+    } else {
+      float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(args.c) + o);
+      if (args.accumulate) {
+        const float4 old = *d;
+        sum.x += old.x; sum.y += old.y; sum.z += old.z; sum.w += old.w;
+      }
+      *d = sum;
+    }
+  }
+}
+
 template <int MODE, int EPI>
 static hipError_t launch_mode_epi(bool svec, const GemmArgs& args, int total, hipStream_t stream) {
   if (svec)
@@ -747,6 +820,17 @@ hipError_t launch_gemm(int mode, int epi, bool scale_dword, const GemmArgs& args
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_reduce(int epi, const GemmArgs& args, int tail_tiles, hipStream_t stream) {
+  if (tail_tiles == 0) return hipSuccess;
+  if (epi == EPI_BF16)
+    hipLaunchKernelGGL(split_reduce_kernel<EPI_BF16>, dim3(tail_tiles), dim3(256), 0, stream, args);
+  else if (epi == EPI_F32)
+    hipLaunchKernelGGL(split_reduce_kernel<EPI_F32>, dim3(tail_tiles), dim3(256), 0, stream, args);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts, hipStream_t stream) {

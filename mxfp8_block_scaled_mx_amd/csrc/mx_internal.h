@@ -111,11 +111,22 @@ struct GemmArgs {
   int32_t nq_col;                   // k-tiled epilogue scales: steps of the columnwise output
   float* dprobs_part;               // bwd: [n_tiles_n, R] partial sums
   int32_t R;                        // rows of the routed activations
+  // split-K tail (MX_GROUP_M, plain epilogues): workgroups past split_f each
+  // take 1/split_s of the k-steps of tile split_f + (wg - split_f) / split_s
+  // and write an fp32 partial tile to split_ws; split_s <= 1: no split
+  int32_t split_f, split_s;
+  float* split_ws;
   GemmGroups groups;
 };
 
 hipError_t launch_gemm(int mode, int epi, bool scale_dword, const GemmArgs& args, int total_tiles,
                        hipStream_t stream);
+
+// Sum the split-K partials of the tail tiles into C (after launch_gemm).
+hipError_t launch_split_reduce(int epi, const GemmArgs& args, int tail_tiles, hipStream_t stream);
+// Split-K tail bounds: at most this many tail tiles, each in at most this many parts.
+constexpr int kMaxSplitTiles = 128;
+constexpr int kMaxSplitParts = 4;
 
 hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts,
                                 hipStream_t stream);

@@ -41,6 +41,9 @@ CASES = {
     "ragged4": dict(seed=30, E=4, H=256, F=384, split=(300, 0, 17, 200)),
     "two_tiles_ffn": dict(seed=31, E=3, H=512, F=768, split=(257, 33, 190)),
     "dense_one_expert": dict(seed=32, E=1, H=256, F=512, split=(384,)),
+    # GEMM2 (K = F = 1024, 8 k-steps) and dgrad1 (K = 2F) take the split-K
+    # tail path: fewer tiles than half the CUs, each split into k-step parts
+    "split_k_tail": dict(seed=33, E=2, H=256, F=1024, split=(300, 100)),
 }
 
 
@@ -86,7 +89,7 @@ def test_forward_routing_weight_zero_and_pow2(gpu_lib):
     assert torch.equal(yn.view(torch.int16), y1.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["ragged4", "two_tiles_ffn", "dense_one_expert"])
+@pytest.mark.parametrize("name", ["ragged4", "two_tiles_ffn", "dense_one_expert", "split_k_tail"])
 def test_backward(gpu_lib, name):
     k = CASES[name]
     c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
