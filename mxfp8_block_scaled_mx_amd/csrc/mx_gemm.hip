@@ -43,7 +43,17 @@ namespace mx {
 
 [[maybe_unused]] constexpr int BM = kTileM, BN = kTileN, BK = kTileK;
 static_assert(sizeof(GemmArgs) <= 4096, "kernel arguments must fit the 4 KB kernarg segment");
-constexpr int kThreads = 256;
+// Waves: 2 along m (128 rows each) x kWavesN along n. kWavesN = 2: a wave
+// owns 128 x 128 (NS = 4 n sub-tiles of 32, 256 fp32 accumulators in AGPRs),
+// one wave per SIMD. (kWavesN = 4 -- 128 x 64 per wave, two waves per SIMD --
+// is also supported, but at 256 registers per wave the accumulators leave the
+// AGPRs and the loop spills, which makes it slower.)
+constexpr int kWavesN = 2;
+constexpr int kWaves = 2 * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int NS = 8 / kWavesN;             // n sub-tiles of 32 per wave
+constexpr int kWaveN = 256 / kWavesN;       // n columns per wave
+constexpr int kDmaPerWave = 32 / kWaves;    // 1 KB blocks of A (and of B) per wave per k-step
 constexpr int kBandM = 8;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
 // open; issued through the builtin so the compiler's own waitcnt tracking
@@ -52,9 +62,9 @@ constexpr int kBandM = 8;
 // Epilogue staging of columnwise codes in a wave's 32 KB LDS slice: [column]
 // [64 rows] with a 96-byte stride (24 dwords: the 8 columns x 8 quads one
 // ds_write_b32 touches fall in 64 distinct banks); the SwiGLU backward keeps
-// the gate and up halves (128 columns each) kColHalf apart.
+// the gate and up halves (NS * 32 columns each) kColHalf apart.
 [[maybe_unused]] constexpr int kColStride = 96;
-[[maybe_unused]] constexpr int kColHalf = 128 * kColStride;
+[[maybe_unused]] constexpr int kColHalf = NS * 32 * kColStride;
 
 struct TileCoord {
   int slot;   // group slot in the table
@@ -115,7 +125,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 template <int MODE, int EPI, bool SVEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_kernel(GemmArgs args, int total_tiles) {
   // The body uses gfx950-only types and builtins (buffer resources, LDS DMA);
   // the host compilation pass only needs the launch stub.
@@ -132,7 +142,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -199,19 +209,21 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     else
       return (uint32_t)(tc.nt * BN + r0);
   };
-  // n sub-tile s of this wave: with the SwiGLU pairing s and s+2 are the gate
-  // and up rows of the same 32 ffn columns; otherwise the wave's 4 sub-tiles
-  // are 128 contiguous columns.
+  // n sub-tile s of this wave: with the SwiGLU pairing s and s + NS/2 are
+  // the gate and up rows of the same 32 ffn columns; otherwise the wave's NS
+  // sub-tiles are kWaveN contiguous columns.
   auto nsub = [&](int s) __attribute__((always_inline)) -> int {
-    if constexpr (EPI == EPI_SWIGLU_FWD) return s < 2 ? 64 * wn + 32 * s : BN / 2 + 64 * wn + 32 * (s - 2);
-    else return (BN / 2) * wn + 32 * s;
+    if constexpr (EPI == EPI_SWIGLU_FWD)
+      return s < NS / 2 ? (NS / 2) * 32 * wn + 32 * s : BN / 2 + (NS / 2) * 32 * wn + 32 * (s - NS / 2);
+    else return kWaveN * wn + 32 * s;
   };
 
-  // ---- direct buffer->LDS loads: per k-step each wave fills 8 blocks of 1 KB
-  // (8 tile rows) of A and of B; LDS slot = lane, i.e. row r = 8*blk + lane/8
-  // and stored chunk lane%8, which holds logical chunk
-  // (lane%8) ^ ((r >> 1) & 7) = (lane%8) ^ (lane/16) ^ 4*(blk&1), and
-  // blk&1 = wave&1 for every blk this wave loads.
+  // ---- direct buffer->LDS loads: per k-step each wave fills kDmaPerWave
+  // blocks of 1 KB (8 tile rows) of A and of B (block blk = it*kWaves + wave);
+  // LDS slot = lane, i.e. row r = 8*blk + lane/8 and stored chunk lane%8,
+  // which holds logical chunk (lane%8) ^ ((r >> 1) & 7) =
+  // (lane%8) ^ (lane/16) ^ 4*(blk&1), and blk&1 = wave&1 for every blk this
+  // wave loads.
   const int lch = (lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1));   // logical chunk this lane fetches
   const uint32_t va_off = (uint32_t)(lane >> 3) * lda + lch * 16;
   const uint32_t vb_off = (uint32_t)(lane >> 3) * ldb + lch * 16;
@@ -223,30 +235,30 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // first 128-column step of this tile's k range in the scale layout
   const int q_base = MODE == MX_GROUP_K ? (args.k_tiled ? args.groups.q0[slot] : (int)(kbeg >> 7)) : 0;
 
-  v16f acc[4][4];
+  v16f acc[NS][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[s][mi][v] = 0.0f;
 
   // scales: raw words (dword path) or bytes of the next and current k-step
-  uint32_t sb_n[4][2], sa_n[4][2];
-  uint32_t sb_c[4][2], sa_c[4][2];
+  uint32_t sb_n[NS][2], sa_n[4][2];
+  uint32_t sb_c[NS][2], sa_c[4][2];
 
-  // Scale loads of one k-step, in 8 slices (slice p: sub-tile p of B for
-  // p < 4, m sub-tile p-4 of A after), so they spread over the 8 MFMA steps.
+  // Scale loads of one k-step, in slices (slice p: sub-tile p of B for
+  // p < NS, m sub-tile p-NS of A after), spread over the MFMA steps.
   auto load_scale_part = [&](int k0, int p) __attribute__((always_inline)) {
     const int blk0 = (int)((kbeg + k0) / 32);
-    const __amdgpu_buffer_rsrc_t& rs = p < 4 ? rsb : rsa;
-    const uint32_t voff = p < 4 ? vsb_off : vsa_off;
-    const uint32_t so = p < 4 ? (b_row_base(nsub(p)) >> 5) * (uint32_t)sb.grp
-                              : (uint32_t)(4 * wm + (p - 4)) * (uint32_t)sa.grp;
-    uint32_t* dst = p < 4 ? sb_n[p] : sa_n[p - 4];
+    const __amdgpu_buffer_rsrc_t& rs = p < NS ? rsb : rsa;
+    const uint32_t voff = p < NS ? vsb_off : vsa_off;
+    const uint32_t so = p < NS ? (b_row_base(nsub(p)) >> 5) * (uint32_t)sb.grp
+                               : (uint32_t)(4 * wm + (p - NS)) * (uint32_t)sa.grp;
+    uint32_t* dst = p < NS ? sb_n[p] : sa_n[p - NS];
     if constexpr (SVEC) {
       // the scale word of this k-step: blocks 4q .. 4q+3 of the row
-      const uint32_t qo = (uint32_t)(q_base + (k0 >> 7)) * (uint32_t)(p < 4 ? sb.step : sa.step);
+      const uint32_t qo = (uint32_t)(q_base + (k0 >> 7)) * (uint32_t)(p < NS ? sb.step : sa.step);
       dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, so + qo, 0);
       dst[1] = 0;
     } else {
@@ -258,14 +270,18 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   };
   // Slice p (0..7) of the loads of k-step kt: one 1 KB block (8 tile rows) of
   // A and of B into the LDS stage, and one scale slice into registers.
+  // p = 0..7: block p of this wave's A and B blocks (p < kDmaPerWave) and
+  // scale slice p (p < NS + 4).
   auto load_part = [&](int kt, uint8_t* dA, uint8_t* dB, int p) __attribute__((always_inline)) {
     const int k0 = kt * BK;
-    const int blk = p * 4 + wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dA + blk * 1024), 16, va_off,
-                                             (uint32_t)(8 * blk) * lda + k0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dB + blk * 1024), 16, vb_off,
-                                             b_row_base(8 * blk) * ldb + k0, 0, 0);
-    load_scale_part(k0, p);
+    if (p < kDmaPerWave) {
+      const int blk = p * kWaves + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dA + blk * 1024), 16, va_off,
+                                               (uint32_t)(8 * blk) * lda + k0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dB + blk * 1024), 16, vb_off,
+                                               b_row_base(8 * blk) * ldb + k0, 0, 0);
+    }
+    if (p < NS + 4) load_scale_part(k0, p);
   };
   auto load_full = [&](int kt, uint8_t* dA, uint8_t* dB) __attribute__((always_inline)) {
 #pragma unroll
@@ -292,7 +308,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       m = rem >= BK ? 0xFFFFFFFFu : (rem <= 0 ? 0u : (1u << (8 * (rem >> 5))) - 1u);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) { sb_c[s][0] = sb_n[s][0] & m; sb_c[s][1] = sb_n[s][1]; }
+    for (int s = 0; s < NS; ++s) { sb_c[s][0] = sb_n[s][0] & m; sb_c[s][1] = sb_n[s][1]; }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) { sa_c[mi][0] = sa_n[mi][0] & m; sa_c[mi][1] = sa_n[mi][1]; }
   };
@@ -301,15 +317,15 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     if constexpr (SVEC) return (int)(c0 >> (8 * h + 16 * ks));
     else return (int)(ks == 0 ? c0 : c1);
   };
-  // MFMAs of one 128-wide k tile (2 MFMA k-steps x 4 m sub-tiles x 4 n
-  // sub-tiles) in 8 steps of 4 MFMAs. Fragment reads run ahead of the MFMAs
+  // MFMAs of one 128-wide k tile (2 MFMA k-steps x 4 m sub-tiles x NS n
+  // sub-tiles) in 8 steps of NS MFMAs. Fragment reads run ahead of the MFMAs
   // that use them: A fragments two steps ahead (three registers sets), the B
   // fragments of k-step 1 one per step during k-step 0. Each step also issues
   // one slice of the next k-step's loads.
   auto compute = [&](const uint8_t* sA, const uint8_t* sB, int kt_next, uint8_t* nA, uint8_t* nB)
       __attribute__((always_inline)) {
-    v8i fb_c[4], fb_n[4], fa[3];
-    static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+    v8i fb_c[NS], fb_n[NS], fa[3];
+    static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
       constexpr int s = decltype(s_c)::value;
       fb_c[s] = read_frag(sB, nsub(s) + l32, 0);
     });
@@ -321,8 +337,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       load_part(kt_next, nA, nB, step);
       if constexpr (step + 2 < 8)
         fa[(step + 2) % 3] = read_frag(sA, 128 * wm + 32 * ((step + 2) % 4) + l32, (step + 2) / 4);
-      if constexpr (step < 4) fb_n[step] = read_frag(sB, nsub(step) + l32, 1);
-      static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+      if constexpr (step < NS) fb_n[step] = read_frag(sB, nsub(step) + l32, 1);
+      static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         acc[s][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             ks == 0 ? fb_c[s] : fb_n[s], fa[step % 3], acc[s][mi], 0, 0, 0,
@@ -338,8 +354,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const bool ok = kt * BK + lch * 16 < klen;
     if (!ok) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int blk = it * 4 + wave;
+      for (int it = 0; it < kDmaPerWave; ++it) {
+        const int blk = it * kWaves + wave;
         *reinterpret_cast<uint4*>(dA + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(dB + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
       }
@@ -398,8 +414,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const int tid = wave * 64 + lane_e;
   const int wrows = max(0, min(BM / 2, a_rows_valid - (BM / 2) * wm));   // valid rows of this wave
   const int64_t m0 = a_row0 + (BM / 2) * wm;                             // global row of its first row
-  // wave-private 32 KB of LDS: the k-loop's stages are free after its last barrier
-  uint8_t* const slice = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  // wave-private 128 KB / kWaves of LDS: the k-loop's stages (4 x 32 KB) are
+  // free after its last barrier
+  constexpr int kSlice = 4 * BM * BK / kWaves;
+  uint8_t* const slice = [&]() -> uint8_t* {
+    const int a = wave * kSlice / (BM * BK), o = wave * kSlice % (BM * BK);
+    return (a == 0 ? sA0 : a == 1 ? sA1 : a == 2 ? sB0 : sB1) + o;
+  }();
 
   // 32 E4M3 codes of one row block, 4 dwords per lane (columns 8*vg + 4*h ..
   // +3): regroup over the half-waves so that lane half h holds columns
@@ -504,11 +525,11 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       // split-K part: the whole 256 x 256 fp32 partial, row-major, into its
       // workspace slot (the reduce kernel adds the parts and writes C)
       const __amdgpu_buffer_rsrc_t rw =
-          make_rsrc(args.split_ws + (int64_t)split_unit * BM * BN + (BM / 2) * wm * BN + (BN / 2) * wn,
+          make_rsrc(args.split_ws + (int64_t)split_unit * BM * BN + (BM / 2) * wm * BN + kWaveN * wn,
                     (int64_t)(BM / 2) * BN * 4);
       static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_c)::value;
-        static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+        static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
           constexpr int s = decltype(s_c)::value;
           __builtin_amdgcn_sched_barrier(0);
           static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
@@ -524,7 +545,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     }
     constexpr int esz = EPI == EPI_F32 ? 4 : 2;
     const uint32_t ldc = (uint32_t)args.ldc;
-    const int64_t col0 = (int64_t)tc.nt * BN + (BN / 2) * wn;
+    const int64_t col0 = (int64_t)tc.nt * BN + kWaveN * wn;
     const char* cb = reinterpret_cast<const char*>(args.c);
     if constexpr (MODE == MX_GROUP_K) cb += (int64_t)g * args.c_group_stride * esz;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cb + (m0 * args.ldc + col0) * esz, (int64_t)wrows * args.ldc * esz);
@@ -540,14 +561,14 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
           constexpr int mi = decltype(mi_c)::value;
           __builtin_amdgcn_sched_barrier(0);
-          u32x4 old[4][4];
+          u32x4 old[NS][4];
           if constexpr (ACC) {
-            static_for<0, 16>([&](auto i_c) __attribute__((always_inline)) {
+            static_for<0, NS * 4>([&](auto i_c) __attribute__((always_inline)) {
               constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
               old[s][vg] = __builtin_amdgcn_raw_buffer_load_b128(rc, off(mi, s, vg), 0, 0);
             });
           }
-          static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+          static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             if (col0 + 32 * s < args.N) {
               static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
@@ -573,7 +594,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     } else {
       static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_c)::value;
-        static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+        static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
           constexpr int s = decltype(s_c)::value;
           __builtin_amdgcn_sched_barrier(0);
           if (col0 + 32 * s < args.N) {
@@ -586,10 +607,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       });
     }
   } else if constexpr (EPI == EPI_SWIGLU_FWD) {
-    // gate (sub-tile s) and up (s+2), s = 0,1, of ffn columns
+    // gate (sub-tile s) and up (s + NS/2), s < NS/2, of ffn columns
     // j = jw0 + 32*s + 8*(v/4) + 4*h + v%4; a = w * silu(gate) * up.
     const uint32_t F = (uint32_t)args.F;
-    const int jw0 = tc.nt * (BN / 2) + 64 * wn;
+    const int jw0 = tc.nt * (BN / 2) + (NS / 2) * 32 * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;       // first row of the wave inside its group
     const int len = args.groups.len[slot];
     const int len_pad = (len + 31) & ~31;               // rows of the group in the columnwise layout
@@ -601,7 +622,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row, (int64_t)((args.R + 31) >> 5) * args.nq_row * 128);
     const bool col_out = args.q_col != nullptr;
     const __amdgpu_buffer_rsrc_t rqc = make_rsrc(col_out ? args.q_col + (int64_t)jw0 * ldq + crow0 : nullptr,
-                                                 col_out ? (int64_t)64 * ldq : 0);
+                                                 col_out ? (int64_t)(NS / 2) * 32 * ldq : 0);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col : nullptr,
                                                  col_out ? (int64_t)(F >> 5) * args.nq_col * 128 : 0);
     const uint32_t q0 = (uint32_t)args.groups.q0[slot];
@@ -616,7 +637,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       constexpr int mi = decltype(mi_c)::value;
       const uint32_t r = 32 * mi + l32;
       const bool blk_ok = col_out && wrow0 + 32 * mi < len;
-      static_for<0, 2>([&](auto s_c) __attribute__((always_inline)) {
+      static_for<0, NS / 2>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         const bool jok = jw0 + 32 * s < (int)F;          // F % 32 == 0: whole block valid or not
@@ -627,7 +648,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           gv[v] = vgpr_hop(acc[s][mi][v]);
-          uv[v] = vgpr_hop(acc[s + 2][mi][v]);
+          uv[v] = vgpr_hop(acc[s + NS / 2][mi][v]);
           const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[v]));
           a[v] = rv ? w[mi] * (gv[v] * sig) * uv[v] : 0.0f;
         }
@@ -645,15 +666,15 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       });
       if constexpr (mi & 1) {
         if (col_out)
-          flush_cols(slice, std::integral_constant<int, 64>{}, rqc, 0u, ldq, (uint32_t)(64 * (mi >> 1)),
+          flush_cols(slice, std::integral_constant<int, 32 * (NS / 2)>{}, rqc, 0u, ldq, (uint32_t)(64 * (mi >> 1)),
                      (int)F - jw0, len_pad - wrow0 - 64 * (mi >> 1));
       }
     });
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     // acc = dA for ffn columns j = jw0 + 32*s + 8*(v/4) + 4*h + v%4 (s = 0..3)
-    __shared__ float red[2 * BM];
+    __shared__ float red[kWavesN * BM];
     const uint32_t F = (uint32_t)args.F;
-    const int jw0 = tc.nt * BN + (BN / 2) * wn;
+    const int jw0 = tc.nt * BN + kWaveN * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;
     const int len = args.groups.len[slot];
     const int len_pad = (len + 31) & ~31;
@@ -664,8 +685,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * 2 * F, (int64_t)wrows * 2 * F);
     const __amdgpu_buffer_rsrc_t rsr = make_rsrc(args.s_row, (int64_t)((args.R + 31) >> 5) * args.nq_row * 128);
     // columnwise dH1: gate half (columns j) and up half (columns F + j)
-    const __amdgpu_buffer_rsrc_t rqc_g = make_rsrc(args.q_col + (int64_t)jw0 * ldq + crow0, (int64_t)128 * ldq);
-    const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)128 * ldq);
+    const __amdgpu_buffer_rsrc_t rqc_g = make_rsrc(args.q_col + (int64_t)jw0 * ldq + crow0, (int64_t)kWaveN * ldq);
+    const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)kWaveN * ldq);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(args.s_col, (int64_t)(2 * F >> 5) * args.nq_col * 128);
     const uint32_t q0 = (uint32_t)args.groups.q0[slot];
     float w[4];
@@ -683,15 +704,15 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       __builtin_amdgcn_sched_barrier(0);
       // gate and up (bf16) of the sub-tile's 4 x 16 columns, all requested
       // before the first is used
-      u32x2 gl[4][4], ul[4][4];
-      static_for<0, 16>([&](auto i_c) __attribute__((always_inline)) {
+      u32x2 gl[NS][4], ul[NS][4];
+      static_for<0, NS * 4>([&](auto i_c) __attribute__((always_inline)) {
         constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
         const uint32_t o = (r * 2 * F + jw0 + 32 * s + 8 * vg + 4 * h) * 2;
         gl[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o, 0, 0);
         ul[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o + 2 * F, 0, 0);
       });
       float dp = 0.0f;
-      static_for<0, 4>([&](auto s_c) __attribute__((always_inline)) {
+      static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         const bool jok = jw0 + 32 * s < (int)F;
@@ -726,11 +747,11 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       if constexpr (mi & 1) {
         const uint32_t ro = 64 * (mi >> 1);
         const int rv = len_pad - wrow0 - 64 * (mi >> 1);
-        flush_cols(slice, std::integral_constant<int, 128>{}, rqc_g, 0u, ldq, ro, (int)F - jw0, rv);
-        flush_cols(slice + kColHalf, std::integral_constant<int, 128>{}, rqc_u, 0u, ldq, ro, (int)F - jw0, rv);
+        flush_cols(slice, std::integral_constant<int, kWaveN>{}, rqc_g, 0u, ldq, ro, (int)F - jw0, rv);
+        flush_cols(slice + kColHalf, std::integral_constant<int, kWaveN>{}, rqc_u, 0u, ldq, ro, (int)F - jw0, rv);
       }
     });
-    // dprobs partial over this tile's 256 columns: the two n-waves meet in LDS
+    // dprobs partial over this tile's 256 columns: the n-waves meet in LDS
     if (args.dprobs_part != nullptr) {
       if (h == 0) {
 #pragma unroll
@@ -738,7 +759,9 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       }
       __syncthreads();
       if (tid < a_rows_valid) {
-        const float tot = red[tid] + red[BM + tid];
+        float tot = red[tid];
+#pragma unroll
+        for (int w = 1; w < kWavesN; ++w) tot += red[w * BM + tid];
         args.dprobs_part[(int64_t)tc.nt * args.R + a_row0 + tid] = tot;
       }
     }
