@@ -52,13 +52,16 @@ constexpr int kWavesN = 2;
 constexpr int kWaves = 2 * kWavesN;
 constexpr int kThreads = 64 * kWaves;
 constexpr int NS = 8 / kWavesN;             // n sub-tiles of 32 per wave
-constexpr int kWaveN = 256 / kWavesN;       // n columns per wave
-constexpr int kDmaPerWave = 32 / kWaves;    // 1 KB blocks of A (and of B) per wave per k-step
+[[maybe_unused]] constexpr int kWaveN = 256 / kWavesN;      // n columns per wave
+[[maybe_unused]] constexpr int kDmaPerWave = 32 / kWaves;    // 1 KB blocks of A (and of B) per wave per k-step
 constexpr int kBandM = 8;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
 // open; issued through the builtin so the compiler's own waitcnt tracking
 // knows the loads have landed.
 [[maybe_unused]] constexpr int kWaitVmcnt0 = 0x0F70;
+[[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
+// L2 prefetch distance in k-steps (see kstep)
+[[maybe_unused]] constexpr int kPrefetchAhead = 3;
 // Epilogue staging of columnwise codes in a wave's 32 KB LDS slice: [column]
 // [64 rows] with a 96-byte stride (24 dwords: the 8 columns x 8 quads one
 // ds_write_b32 touches fall in 64 distinct banks); the SwiGLU backward keeps
@@ -367,13 +370,34 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // bytes the bounds-checked buffer returns as 0 or data of neighbouring rows,
   // into the stage nobody computes on again. A partial last k-step (group-K
   // tail) gets its out-of-range chunks zeroed after the handoff.
+  // L2 prefetch: once a k-step's loads are issued, each wave touches one
+  // 128-byte line per row of a share of the operand rows of k-step
+  // kt + kPrefetchAhead, so that step's LDS loads hit L2 instead of waiting
+  // for memory. The 32 tiles one XCD runs at a time (8 m-tiles x 4 n-tiles of
+  // the band raster) share A and B blocks, so a tile touches only its share:
+  // A rows [64*(nt%4), +64) (waves 0-1, 32 rows each) and B rows
+  // [32*(mt%8), +32) (waves 2-3, 16 rows each). The loaded words land in a
+  // sink register one k-step later, when the in-order completion of the next
+  // loads has made them ready, so the prefetch never adds a wait.
+  uint32_t pf_sink = 0, pf_last = 0;
+  const uint32_t pf_row = wave < 2 ? (uint32_t)(64 * (tc.nt & 3) + 32 * wave + (lane & 31))
+                                   : (uint32_t)(32 * (tc.mt & 7) + 16 * (wave - 2) + (lane & 15));
+  const uint32_t pf_voff = wave < 2 ? pf_row * lda : b_row_base(pf_row & ~7u) * ldb + (pf_row & 7u) * ldb;
+  auto prefetch = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t k0 = (uint32_t)kt * BK;
+    return wave < 2 ? __builtin_amdgcn_raw_buffer_load_b32(ra, pf_voff, k0, 0)
+                    : __builtin_amdgcn_raw_buffer_load_b32(rb, pf_voff, k0, 0);
+  };
   auto kstep = [&](int kt, const uint8_t* cA, const uint8_t* cB, uint8_t* nA, uint8_t* nB)
       __attribute__((always_inline)) {
     compute(cA, cB, kt + 1, nA, nB);
+    const uint32_t pf_new = prefetch(kt + kPrefetchAhead);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt1);     // all but the prefetch just issued
     take_scales(kt + 1);
     __syncthreads();
+    pf_sink ^= pf_last;
+    pf_last = pf_new;
     if ((klen & (BK - 1)) != 0 && kt + 2 == kt_hi) {
       zero_tail(kt + 1, nA, nB);
       __syncthreads();
@@ -395,6 +419,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     kstep(kt, sA0, sB0, sA1, sB1);
     if (kt + 1 < kt_hi) kstep(kt + 1, sA1, sB1, sA0, sB0);
   }
+
+  asm volatile("" :: "v"(pf_sink ^ pf_last));
 
   // ---------------------------------------------------------------- epilogues
   // Lane mapping of the accumulators: for n sub-tile s and m sub-tile mi the
