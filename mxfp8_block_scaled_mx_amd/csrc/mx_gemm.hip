@@ -67,6 +67,9 @@ constexpr int kBandM = 8;
 // ds_write_b32 touches fall in 64 distinct banks); the SwiGLU backward keeps
 // the gate and up halves (NS * 32 columns each) kColHalf apart.
 [[maybe_unused]] constexpr int kColStride = 96;
+// cache policy of memory touched exactly once (fp32 C of the plain epilogue):
+// non-temporal
+[[maybe_unused]] constexpr int kNonTemporal = 2;
 [[maybe_unused]] constexpr int kColHalf = NS * 32 * kColStride;
 
 struct TileCoord {
@@ -547,26 +550,69 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     if (MODE == MX_GROUP_K && klen == 0 && args.accumulate) return;
+    // fp32 out: the accumulators leave through the wave's LDS slice so that
+    // every store covers whole 128-byte rows. 32 x 32 block (mi, s) is staged
+    // as [row][16-byte chunk] (chunk c of row r at slot c ^ (r & 7), which
+    // keeps both passes free of bank conflicts) and read back so that lane L
+    // holds row 8i + L/8, chunk L%8 for i = 0..3; rd is based at the wave's
+    // first row and column, ld is its row stride in floats, blocks from
+    // column cols_valid on are skipped. Old values of an accumulating store
+    // are read in the same layout. Accumulate and overwrite are separate code
+    // paths so the accumulator registers never merge with the loaded values.
+    const int rr = lane_e >> 3, cc = lane_e & 7;
+    auto store_f32 = [&](const __amdgpu_buffer_rsrc_t& rd, uint32_t ld, int64_t cols_valid, auto acc_c,
+                         auto policy_c) __attribute__((always_inline)) {
+      constexpr bool ACC = decltype(acc_c)::value;
+      constexpr int POL = decltype(policy_c)::value;
+      auto coff = [&](int mi, int s, int i) __attribute__((always_inline)) -> uint32_t {
+        return ((uint32_t)(32 * mi + 8 * i + rr) * ld + 32 * s + 4 * cc) * 4;
+      };
+      static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
+        constexpr int mi = decltype(mi_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 old[NS][4];
+        if constexpr (ACC) {
+          static_for<0, NS * 4>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(j_c)::value / 4, i = decltype(j_c)::value % 4;
+            old[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rd, coff(mi, s, i), 0, POL);
+          });
+        }
+        uint8_t* const st = slice + (mi & 1) * (NS * 4096);
+        static_for<0, NS * 4>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int s = decltype(j_c)::value / 4, vg = decltype(j_c)::value % 4;
+          u32x4 v;
+          v.x = __float_as_uint(acc[s][mi][4 * vg + 0]); v.y = __float_as_uint(acc[s][mi][4 * vg + 1]);
+          v.z = __float_as_uint(acc[s][mi][4 * vg + 2]); v.w = __float_as_uint(acc[s][mi][4 * vg + 3]);
+          const int c = 2 * vg + h;
+          *reinterpret_cast<u32x4*>(st + s * 4096 + l32 * 128 + ((c ^ (l32 & 7)) << 4)) = v;
+        });
+        static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int s = decltype(s_c)::value;
+          if (32 * s < cols_valid) {
+            static_for<0, 4>([&](auto i_c) __attribute__((always_inline)) {
+              constexpr int i = decltype(i_c)::value;
+              u32x4 v = *reinterpret_cast<const u32x4*>(st + s * 4096 + (8 * i + rr) * 128 + ((cc ^ rr) << 4));
+              if constexpr (ACC) {
+                v.x = __float_as_uint(__uint_as_float(v.x) + __uint_as_float(old[s][i].x));
+                v.y = __float_as_uint(__uint_as_float(v.y) + __uint_as_float(old[s][i].y));
+                v.z = __float_as_uint(__uint_as_float(v.z) + __uint_as_float(old[s][i].z));
+                v.w = __float_as_uint(__uint_as_float(v.w) + __uint_as_float(old[s][i].w));
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(v, rd, coff(mi, s, i), 0, POL);
+            });
+          }
+        });
+      });
+    };
+    using plain = std::integral_constant<int, 0>;
+    using once = std::integral_constant<int, kNonTemporal>;
     if (MODE == MX_GROUP_M && split_unit >= 0) {
       // split-K part: the whole 256 x 256 fp32 partial, row-major, into its
       // workspace slot (the reduce kernel adds the parts and writes C)
       const __amdgpu_buffer_rsrc_t rw =
           make_rsrc(args.split_ws + (int64_t)split_unit * BM * BN + (BM / 2) * wm * BN + kWaveN * wn,
                     (int64_t)(BM / 2) * BN * 4);
-      static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
-        constexpr int mi = decltype(mi_c)::value;
-        static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
-          constexpr int s = decltype(s_c)::value;
-          __builtin_amdgcn_sched_barrier(0);
-          static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
-            constexpr int vg = decltype(vg_c)::value;
-            u32x4 o;
-            o.x = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 0])); o.y = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 1]));
-            o.z = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 2])); o.w = __float_as_uint(vgpr_hop(acc[s][mi][4 * vg + 3]));
-            __builtin_amdgcn_raw_buffer_store_b128(o, rw, ((uint32_t)(32 * mi + l32) * BN + 32 * s + 8 * vg + 4 * h) * 4, 0, 0);
-          });
-        });
-      });
+      store_f32(rw, BN, BN, std::false_type{}, plain{});
       return;
     }
     constexpr int esz = EPI == EPI_F32 ? 4 : 2;
@@ -575,48 +621,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const char* cb = reinterpret_cast<const char*>(args.c);
     if constexpr (MODE == MX_GROUP_K) cb += (int64_t)g * args.c_group_stride * esz;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(cb + (m0 * args.ldc + col0) * esz, (int64_t)wrows * args.ldc * esz);
-    auto off = [&](int mi, int s, int vg) __attribute__((always_inline)) -> uint32_t {
-      return ((uint32_t)(32 * mi + l32) * ldc + 32 * s + 8 * vg + 4 * h) * esz;
-    };
     if constexpr (EPI == EPI_F32) {
-      // accumulate and overwrite are separate code paths so the accumulator
-      // registers never merge with the loaded old values; the old values of a
-      // whole m sub-tile are requested before any of them is used
-      auto store_tile = [&](auto acc_c) __attribute__((always_inline)) {
-        constexpr bool ACC = decltype(acc_c)::value;
-        static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
-          constexpr int mi = decltype(mi_c)::value;
-          __builtin_amdgcn_sched_barrier(0);
-          u32x4 old[NS][4];
-          if constexpr (ACC) {
-            static_for<0, NS * 4>([&](auto i_c) __attribute__((always_inline)) {
-              constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
-              old[s][vg] = __builtin_amdgcn_raw_buffer_load_b128(rc, off(mi, s, vg), 0, 0);
-            });
-          }
-          static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
-            constexpr int s = decltype(s_c)::value;
-            if (col0 + 32 * s < args.N) {
-              static_for<0, 4>([&](auto vg_c) __attribute__((always_inline)) {
-                constexpr int vg = decltype(vg_c)::value;
-                float c[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) c[i] = vgpr_hop(acc[s][mi][4 * vg + i]);
-                if constexpr (ACC) {
-                  c[0] += __uint_as_float(old[s][vg].x); c[1] += __uint_as_float(old[s][vg].y);
-                  c[2] += __uint_as_float(old[s][vg].z); c[3] += __uint_as_float(old[s][vg].w);
-                }
-                u32x4 o;
-                o.x = __float_as_uint(c[0]); o.y = __float_as_uint(c[1]);
-                o.z = __float_as_uint(c[2]); o.w = __float_as_uint(c[3]);
-                __builtin_amdgcn_raw_buffer_store_b128(o, rc, off(mi, s, vg), 0, 0);
-              });
-            }
-          });
-        });
-      };
-      if (args.accumulate) store_tile(std::true_type{});
-      else store_tile(std::false_type{});
+      // C is touched once: non-temporal
+      if (args.accumulate) store_f32(rc, ldc, args.N - col0, std::true_type{}, once{});
+      else store_f32(rc, ldc, args.N - col0, std::false_type{}, once{});
     } else {
       static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_c)::value;
