@@ -85,6 +85,8 @@ struct TileCoord {
 // (group-K slots sorted by size) balanced across XCDs. Blocks of the last,
 // partial round keep their own id.
 constexpr int kXcdChunk = 32;
+// words of k-tiled scales per LDS stage: A 16 row groups, B 8 row groups
+[[maybe_unused]] constexpr int kScStage = 768;
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
   constexpr int round = 8 * kXcdChunk;
   const int full = total / round * round;
@@ -130,7 +132,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
 }
 
-template <int MODE, int EPI, bool SVEC>
+// Scale sources: per-lane byte loads (any layout), per-lane dword loads (row
+// layouts whose 4 scales of a k-step are one aligned word), or the k-tiled
+// layout through LDS (one DMA per 256 rows and k-step).
+enum ScaleSource : int { kScByte = 0, kScDword = 1, kScLds = 2 };
+
+template <int MODE, int EPI, int SC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_kernel(GemmArgs args, int total_tiles) {
   // The body uses gfx950-only types and builtins (buffer resources, LDS DMA);
@@ -144,6 +151,9 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t sA1[BM * BK];
   __shared__ __attribute__((aligned(16))) uint8_t sB0[BN * BK];
   __shared__ __attribute__((aligned(16))) uint8_t sB1[BN * BK];
+  // k-tiled scales of the two stages: A words of 16 row groups (the tile's 256
+  // rows from the group of its first row on) and B words of 8 row groups
+  __shared__ __attribute__((aligned(16))) uint32_t sSc[SC == kScLds ? 2 * kScStage : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -262,7 +272,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const uint32_t so = p < NS ? (b_row_base(nsub(p)) >> 5) * (uint32_t)sb.grp
                                : (uint32_t)(4 * wm + (p - NS)) * (uint32_t)sa.grp;
     uint32_t* dst = p < NS ? sb_n[p] : sa_n[p - NS];
-    if constexpr (SVEC) {
+    if constexpr (SC != kScByte) {
       // the scale word of this k-step: blocks 4q .. 4q+3 of the row
       const uint32_t qo = (uint32_t)(q_base + (k0 >> 7)) * (uint32_t)(p < NS ? sb.step : sa.step);
       dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, so + qo, 0);
@@ -287,7 +297,23 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dB + blk * 1024), 16, vb_off,
                                                b_row_base(8 * blk) * ldb + k0, 0, 0);
     }
-    if (p < NS + 4) load_scale_part(k0, p);
+    if constexpr (SC == kScLds) {
+      // one k-step's words of 32 rows are 128 contiguous bytes: waves 0 and 1
+      // fetch A row groups 0-7 and 8-15, wave 2 B row groups 0-7
+      if (p == 0 && wave < 3) {
+        const int st = (kt - kt_lo) & 1;
+        const uint32_t c16 = (uint32_t)(lane & 7) * 16, g = (uint32_t)(lane >> 3);
+        const uint32_t so = (uint32_t)(q_base + kt) * 128;
+        if (wave < 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(sSc + st * kScStage + 256 * wave), 16,
+                                                   (8 * wave + g) * (uint32_t)sa.grp + c16, so, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(sSc + st * kScStage + 512), 16,
+                                                   (b_row_base(32 * g) >> 5) * (uint32_t)sb.grp + c16, so, 0, 0);
+      }
+    } else {
+      if (p < NS + 4) load_scale_part(k0, p);
+    }
   };
   auto load_full = [&](int kt, uint8_t* dA, uint8_t* dB) __attribute__((always_inline)) {
 #pragma unroll
@@ -308,8 +334,17 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // are cleared (their codes are zero, but a NaN code would still poison the
   // products).
   auto take_scales = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (SC == kScLds) {
+      // words of this lane's rows, from the stage of k-step kt (after the
+      // barrier that follows its DMA)
+      const uint32_t* ss = sSc + ((kt - kt_lo) & 1) * kScStage;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) { sa_n[mi][0] = ss[(a_row0 & 31) + 128 * wm + 32 * mi + l32]; sa_n[mi][1] = 0; }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) { sb_n[s][0] = ss[512 + nsub(s) + l32]; sb_n[s][1] = 0; }
+    }
     uint32_t m = 0xFFFFFFFFu;
-    if constexpr (MODE == MX_GROUP_K && SVEC) {
+    if constexpr (MODE == MX_GROUP_K && SC != kScByte) {
       const int rem = klen - kt * BK;
       m = rem >= BK ? 0xFFFFFFFFu : (rem <= 0 ? 0u : (1u << (8 * (rem >> 5))) - 1u);
     }
@@ -320,7 +355,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   };
   // byte-0-aligned scale register of k-step ks: block h (ks 0) or 2+h (ks 1)
   auto scale_of = [&](uint32_t c0, uint32_t c1, int ks) __attribute__((always_inline)) -> int {
-    if constexpr (SVEC) return (int)(c0 >> (8 * h + 16 * ks));
+    if constexpr (SC != kScByte) return (int)(c0 >> (8 * h + 16 * ks));
     else return (int)(ks == 0 ? c0 : c1);
   };
   // MFMAs of one 128-wide k tile (2 MFMA k-steps x 4 m sub-tiles x NS n
@@ -397,8 +432,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const uint32_t pf_new = prefetch(kt + kPrefetchAhead);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt1);     // all but the prefetch just issued
-    take_scales(kt + 1);
-    __syncthreads();
+    if constexpr (SC == kScLds) {
+      __syncthreads();
+      take_scales(kt + 1);
+    } else {
+      take_scales(kt + 1);
+      __syncthreads();
+    }
     pf_sink ^= pf_last;
     pf_last = pf_new;
     if ((klen & (BK - 1)) != 0 && kt + 2 == kt_hi) {
@@ -410,8 +450,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   if (kt_hi > kt_lo) {
     load_full(kt_lo, sA0, sB0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    take_scales(kt_lo);
-    __syncthreads();
+    if constexpr (SC == kScLds) {
+      __syncthreads();
+      take_scales(kt_lo);
+    } else {
+      take_scales(kt_lo);
+      __syncthreads();
+    }
     if ((klen & (BK - 1)) != 0 && kt_lo + 1 == kt_hi) {
       zero_tail(kt_lo, sA0, sB0);
       __syncthreads();
@@ -853,10 +898,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs args) {
 
 template <int MODE, int EPI>
 static hipError_t launch_mode_epi(bool svec, const GemmArgs& args, int total, hipStream_t stream) {
-  if (svec)
-    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, true>), dim3(total), dim3(kThreads), 0, stream, args, total);
-  else
-    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, false>), dim3(total), dim3(kThreads), 0, stream, args, total);
+  if (args.k_tiled) {
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScLds>), dim3(total), dim3(kThreads), 0, stream, args, total);
+  } else if constexpr (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
+    return hipErrorInvalidValue;       // the fused epilogues run on k-tiled scales only
+  } else if (svec) {
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScDword>), dim3(total), dim3(kThreads), 0, stream, args, total);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScByte>), dim3(total), dim3(kThreads), 0, stream, args, total);
+  }
   return hipGetLastError();
 }
 
