@@ -532,12 +532,13 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // scale per column over the 32 rows (the lanes of a half-wave); the codes are
   // transposed inside each quad of lanes and staged in LDS as [column][row]
   // (stride kColStride), to be written out as column runs by flush_cols.
-  // Scales go to the k-tiled layouts: s_off is the rowwise byte of this lane's
-  // row, and the columnwise byte of block column c is sc_col0 + c * sc_ld.
+  // The scale codes come back to the caller, which gathers the bytes that
+  // share a k-tiled word and stores whole words: row_sc is the rowwise code
+  // of this lane's row, col_sc the columnwise code of block column
+  // 8*(l32/4) + 4*h + l32%4 (lanes l32 < 16).
   auto quantize_block = [&](const float (&d)[16], const __amdgpu_buffer_rsrc_t& rq, uint32_t q_off,
-                            const __amdgpu_buffer_rsrc_t& rs, uint32_t s_off, bool row_store, bool s_store,
-                            uint8_t* stage, const __amdgpu_buffer_rsrc_t& rsc, uint32_t sc_col0,
-                            uint32_t sc_ld, bool col_store) __attribute__((always_inline)) {
+                            bool row_store, uint8_t* stage, uint32_t& row_sc, uint32_t& col_sc)
+      __attribute__((always_inline)) {
     {
       uint32_t am = 0;
 #pragma unroll
@@ -549,7 +550,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) q[vg] = e4m3x4(d[4 * vg] * inv, d[4 * vg + 1] * inv, d[4 * vg + 2] * inv, d[4 * vg + 3] * inv);
       if (row_store) store_row_codes(rq, q_off, q);
-      if (s_store && h == 0) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, s_off, 0, 0);
+      row_sc = sc;
     }
     {
       uint32_t scv[16];
@@ -559,13 +560,11 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         scv[v] = scale_code_from_amax_bits(max_lanes32(abs_bits(d[v])));
         inv[v] = inv_scale_from_code(scv[v]);
       }
-      // scale of column v is written by lane l32 == v (v < 16)
+      // scale of column v is kept by lane l32 == v (v < 16)
       uint32_t ssel = scv[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) ssel = l32 == v ? scv[v] : ssel;
-      if (col_store && l32 < 16)
-        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)ssel, rsc,
-                                             (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3)) * sc_ld + sc_col0, 0, 0);
+      col_sc = ssel;
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
         const uint32_t x = e4m3x4(d[4 * vg] * inv[4 * vg], d[4 * vg + 1] * inv[4 * vg + 1],
@@ -712,10 +711,19 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       w[mi] = args.probs ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * r, 0, 0))
                          : (r < wrows ? 1.0f : 0.0f);
     }
+    // Scale words: the wave's NS/2 column blocks are bytes 2*wn .. of one
+    // rowwise word per row, and its 4 row blocks the 4 bytes of one
+    // columnwise word per column (bytes of blocks past the group are 0).
+    const uint32_t b0 = (uint32_t)jw0 >> 5;
+    const bool wave_jok = jw0 < (int)F;                  // F % 128 == 0: all NS/2 blocks valid or none
+    uint32_t csw[NS / 2];
+#pragma unroll
+    for (int s2 = 0; s2 < NS / 2; ++s2) csw[s2] = 0;
     static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
       constexpr int mi = decltype(mi_c)::value;
       const uint32_t r = 32 * mi + l32;
       const bool blk_ok = col_out && wrow0 + 32 * mi < len;
+      uint32_t rsw = 0;
       static_for<0, NS / 2>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -735,20 +743,32 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
           store_row_bf16(rh1, (r * 2 * F + jw0 + 32 * s) * 2, gv);
           store_row_bf16(rh1, (r * 2 * F + F + jw0 + 32 * s) * 2, uv);
         }
-        const uint32_t m = (uint32_t)m0 + r;             // global row
-        const uint32_t b = (uint32_t)(jw0 + 32 * s) >> 5;   // block of the row
-        const uint32_t bl = ((uint32_t)wrow0 >> 5) + mi;     // block of the column inside the group
-        quantize_block(a, rqr, r * F + jw0 + 32 * s, rsr,
-                       ((m >> 5) * args.nq_row + (b >> 2)) * 128 + (m & 31) * 4 + (b & 3), jok, jok && r < (uint32_t)wrows,
-                       slice + 32 * s * kColStride + 32 * (mi & 1), rsc,
-                       (b * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
+        uint32_t rsc_v, csc_v;
+        quantize_block(a, rqr, r * F + jw0 + 32 * s, jok, slice + 32 * s * kColStride + 32 * (mi & 1), rsc_v, csc_v);
+        rsw |= rsc_v << (8 * s);
+        csw[s] |= (blk_ok ? csc_v : 0u) << (8 * mi);
       });
+      {
+        const uint32_t m = (uint32_t)m0 + r;             // global row
+        if (wave_jok && r < (uint32_t)wrows && h == 0)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)rsw, rsr,
+                                                ((m >> 5) * args.nq_row + (b0 >> 2)) * 128 + (m & 31) * 4 + (b0 & 3), 0, 0);
+      }
       if constexpr (mi & 1) {
         if (col_out)
           flush_cols(slice, std::integral_constant<int, 32 * (NS / 2)>{}, rqc, 0u, ldq, (uint32_t)(64 * (mi >> 1)),
                      (int)F - jw0, len_pad - wrow0 - 64 * (mi >> 1));
       }
     });
+    // columnwise scale words: only where the wave has rows of the group (the
+    // word past the group's last k-step belongs to the next group)
+    if (col_out && wave_jok && wrow0 < len && l32 < 16) {
+      const uint32_t c = (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3));
+#pragma unroll
+      for (int s2 = 0; s2 < NS / 2; ++s2)
+        __builtin_amdgcn_raw_buffer_store_b32(csw[s2], rsc,
+                                              ((b0 + s2) * args.nq_col + q0 + ((uint32_t)wrow0 >> 7)) * 128 + c * 4, 0, 0);
+    }
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     // acc = dA for ffn columns j = jw0 + 32*s + 8*(v/4) + 4*h + v%4 (s = 0..3)
     __shared__ float red[kWavesN * BM];
@@ -776,10 +796,21 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
                          : (r < wrows ? 1.0f : 0.0f);
     }
     float dpsum[4];
+    // Scale words: the wave's NS column blocks of the gate (and of the up)
+    // half are the 4 bytes of one rowwise word per row, and its 4 row blocks
+    // the 4 bytes of one columnwise word per column (bytes of blocks past the
+    // group are 0). The columnwise bytes collect in the slice past the
+    // column-code staging, word (half, s, column).
+    const uint32_t bg0 = (uint32_t)jw0 >> 5, bu0 = (uint32_t)(F + jw0) >> 5;
+    const bool wave_jok = jw0 < (int)F;                  // F % 128 == 0: all NS blocks valid or none
+    static_assert(2 * kColHalf + 2 * NS * 32 * 4 <= kSlice, "column scale bytes must fit the wave's slice");
+    uint8_t* const csl = slice + 2 * kColHalf;
+    const uint32_t ccol = (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3));
     static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
       constexpr int mi = decltype(mi_c)::value;
       const uint32_t r = 32 * mi + l32;
       const bool blk_ok = wrow0 + 32 * mi < len;
+      uint32_t rsg = 0, rsu = 0;
       __builtin_amdgcn_sched_barrier(0);
       // gate and up (bf16) of the sub-tile's 4 x 16 columns, all requested
       // before the first is used
@@ -812,16 +843,24 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
           }
         }
         uint8_t* st = slice + 32 * s * kColStride + 32 * (mi & 1);
-        const uint32_t m = (uint32_t)m0 + r;
-        const uint32_t bg = (uint32_t)(jw0 + 32 * s) >> 5, bu = (uint32_t)(F + jw0 + 32 * s) >> 5;
-        const uint32_t bl = ((uint32_t)wrow0 >> 5) + mi;
-        const uint32_t srow = (m >> 5) * args.nq_row * 128 + (m & 31) * 4;
-        const bool s_ok = jok && r < (uint32_t)wrows;
-        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, rsr, srow + (bg >> 2) * 128 + (bg & 3), jok, s_ok,
-                       st, rsc, (bg * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
-        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, rsr, srow + (bu >> 2) * 128 + (bu & 3), jok, s_ok,
-                       st + kColHalf, rsc, (bu * args.nq_col + q0 + (bl >> 2)) * 128 + (bl & 3), 4, blk_ok && jok);
+        uint32_t rg, cg, ru, cu;
+        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, jok, st, rg, cg);
+        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, jok, st + kColHalf, ru, cu);
+        rsg |= rg << (8 * s);
+        rsu |= ru << (8 * s);
+        if (l32 < 16) {
+          csl[(s * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cg : 0u);
+          csl[((NS + s) * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cu : 0u);
+        }
       });
+      {
+        const uint32_t m = (uint32_t)m0 + r;
+        const uint32_t srow = (m >> 5) * args.nq_row * 128 + (m & 31) * 4;
+        if (wave_jok && r < (uint32_t)wrows && h == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(rsg, rsr, srow + (bg0 >> 2) * 128, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(rsu, rsr, srow + (bu0 >> 2) * 128, 0, 0);
+        }
+      }
       dpsum[mi] = sum_halves(dp);
       if constexpr (mi & 1) {
         const uint32_t ro = 64 * (mi >> 1);
@@ -830,6 +869,18 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         flush_cols(slice + kColHalf, std::integral_constant<int, kWaveN>{}, rqc_u, 0u, ldq, ro, (int)F - jw0, rv);
       }
     });
+    // columnwise scale words: only where the wave has rows of the group (the
+    // word past the group's last k-step belongs to the next group)
+    if (wave_jok && wrow0 < len && l32 < 16) {
+      const uint32_t qo = q0 + ((uint32_t)wrow0 >> 7);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const uint32_t wg = *reinterpret_cast<const uint32_t*>(csl + (s2 * 32 + ccol) * 4);
+        const uint32_t wu = *reinterpret_cast<const uint32_t*>(csl + ((NS + s2) * 32 + ccol) * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(wg, rsc, ((bg0 + s2) * args.nq_col + qo) * 128 + ccol * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(wu, rsc, ((bu0 + s2) * args.nq_col + qo) * 128 + ccol * 4, 0, 0);
+      }
+    }
     // dprobs partial over this tile's 256 columns: the n-waves meet in LDS
     if (args.dprobs_part != nullptr) {
       if (h == 0) {
