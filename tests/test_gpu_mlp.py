@@ -44,6 +44,11 @@ CASES = {
     # GEMM2 (K = F = 1024, 8 k-steps) and dgrad1 (K = 2F) take the split-K
     # tail path: fewer tiles than half the CUs, each split into k-step parts
     "split_k_tail": dict(seed=33, E=2, H=256, F=1024, split=(300, 100)),
+    # many small groups around the 32-, 64- and 128-row boundaries (k-tiled
+    # scale words shared by a group's last rows, waves with no rows of their
+    # group) at the smallest hidden size
+    "many_small": dict(seed=34, E=12, H=128, F=256,
+                       split=(1, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129)),
 }
 
 
@@ -89,7 +94,7 @@ def test_forward_routing_weight_zero_and_pow2(gpu_lib):
     assert torch.equal(yn.view(torch.int16), y1.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["ragged4", "two_tiles_ffn", "dense_one_expert", "split_k_tail"])
+@pytest.mark.parametrize("name", ["ragged4", "two_tiles_ffn", "dense_one_expert", "split_k_tail", "many_small"])
 def test_backward(gpu_lib, name):
     k = CASES[name]
     c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
