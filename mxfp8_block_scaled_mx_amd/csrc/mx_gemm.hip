@@ -11,31 +11,37 @@
 // Tiling: 256 (A rows, "m") x 256 (B rows, "n") x 128 (k) per workgroup of
 // 256 threads = 4 waves in 2 (m) x 2 (n), one wave per SIMD so each wave can
 // keep its 256 fp32 accumulators in AGPRs. A wave owns m rows [128*wm, +128)
-// and the four 32-row n sub-tiles {64*wn, 64*wn+32, 128+64*wn, 160+64*wn},
-// i.e. 4 x 4 MFMA tiles of 32x32. The MFMA's first operand is the B tile
-// (n), its second the A tile (m), so each lane ends up with one m row
-// (lane % 32) and 16 n values: 4 runs of 4 consecutive n. With the SwiGLU
-// pairing (tile rows 0..127 = gate rows, 128..255 = the matching up rows)
-// sub-tiles s and s+2 hold gate and up of the same (row, j) in the same
-// accumulator slot, and the 32 j's of one MXFP8 block sit in lanes l, l^32.
+// and four 32-row n sub-tiles: n [128*wn, +128) for the plain epilogues, and
+// {64*wn, 64*wn+32, 128+64*wn, 160+64*wn} with the SwiGLU pairing (tile rows
+// 0..127 = gate rows, 128..255 = the matching up rows), so that sub-tiles s
+// and s+2 hold gate and up of the same (row, j) in the same accumulator slot.
+// The MFMA's first operand is the B tile (n), its second the A tile (m), so
+// each lane ends up with one m row (lane % 32) and 16 n values: 4 runs of 4
+// consecutive n, the 32 n of one MXFP8 block in lanes l and l^32.
 //
 // Operand layout inside the MFMA (pinned on hardware): lane l = row (l%32),
 // half h = l/32 holds k [16h, 16h+16) in bytes 0-15 and k [32+16h, +16) in
 // bytes 16-31 of its 32-byte operand; the scale register of lane l (byte 0)
 // scales k-block h of its row.
 //
-// LDS: double-buffered A and B tiles, 128 bytes per row, 16-byte chunk c of
-// row r stored at chunk (c ^ ((r >> 1) & 7)): the 16 rows one ds_read_b128
-// phase reads (16 lanes x 16 bytes over the 64 banks) then land in 16
-// distinct 16-byte bank groups. Global loads go through registers
-// one k-step ahead of the MFMAs (scalar base + 32-bit per-lane offsets).
-// Scales are read straight from global memory (L2-resident), also one step
-// ahead.
+// Operands: double-buffered A and B stages in LDS, filled straight from
+// global memory by buffer->LDS DMA one k-step ahead, 128 bytes per row with
+// 16-byte chunk c of row r stored at chunk (c ^ ((r >> 1) & 7)), so that
+// fragment reads are free of bank conflicts. Each wave also touches the L2
+// lines of its share of the operand rows three k-steps ahead. Scales come
+// per lane from global memory (row layouts) or, for the k-tiled layout of
+// the fused MLP, by DMA into a small LDS stage beside the operands.
 //
-// Tile order: workgroup ids are first spread evenly over the 8 XCDs (ids that
-// run on one XCD form one contiguous range of tiles, which then share its L2),
-// then mapped to (group, m-tile, n-tile) with m-tiles grouped in bands of 8
-// so the tiles in flight reuse the same A rows and B rows.
+// Tile order: workgroup ids are spread over the 8 XCDs in rounds of 32
+// consecutive tile ids per XCD (the tiles one XCD runs together share A and
+// B rows in its L2), then mapped to (group, m-tile, n-tile) with m-tiles in
+// bands of 8. Plain group-M GEMMs split the tiles of a last, partial round
+// along k (fp32 partials, summed by split_reduce_kernel).
+//
+// Epilogues: fp32 (optionally accumulating) and bf16 C; the fused SwiGLU
+// forward (A = w * silu(g) * u, H1 saved as bf16, A quantized rowwise and
+// columnwise) and backward (dg, du, dprobs partials, dH1 quantized rowwise
+// and columnwise). fp32 C leaves through LDS as whole 128-byte rows.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -284,10 +290,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       dst[1] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff + b1, so, 0);
     }
   };
-  // Slice p (0..7) of the loads of k-step kt: one 1 KB block (8 tile rows) of
-  // A and of B into the LDS stage, and one scale slice into registers.
-  // p = 0..7: block p of this wave's A and B blocks (p < kDmaPerWave) and
-  // scale slice p (p < NS + 4).
+  // Slice p (0..7) of the loads of k-step kt: block p of this wave's 1 KB
+  // blocks (8 tile rows) of A and of B into the LDS stage (p < kDmaPerWave),
+  // and the scales: slice p into registers (p < NS + 4), or for the k-tiled
+  // layout one DMA per wave 0-2 at p = 0 into the LDS scale stage.
   auto load_part = [&](int kt, uint8_t* dA, uint8_t* dB, int p) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     if (p < kDmaPerWave) {
