@@ -208,6 +208,10 @@ mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, in
   }
   A.groups.tile0[order.size()] = (int32_t)t;
   if (t > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many tiles", who);
+  // group-K: every slot has cdiv(M, 256) * tiles_n tiles; when that is a
+  // whole number of 32-tile XCD chunks the kernel interleaves the slots
+  const int64_t per_slot = cdiv(M, mx::kTileM) * tiles_n;
+  A.groups.interleave = mode == MX_GROUP_K && order.size() > 1 && per_slot % 32 == 0 ? 1 : 0;
   p.total_tiles = (int)t;
   // whole-dword scale loads: every k tile starts at a multiple of 4 blocks
   p.scale_dword = mode == MX_GROUP_M && K % 128 == 0 && lda % 128 == 0 && ldb % 128 == 0 &&

@@ -101,15 +101,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (local / kXcdChunk) * round + xcd * kXcdChunk + local % kXcdChunk;
 }
 
+// Slot of a tile id: slots hold consecutive id ranges (tile0), except in an
+// interleaved group-K plan, where chunk q of kXcdChunk ids belongs to slot
+// (q % n + q / n) % n as its chunk q / n. Every n consecutive chunks then
+// cover all slots once, so the tiles running at one time mix contractions of
+// different lengths (their k-loops and their fp32 read-modify-write phases
+// overlap across CUs instead of all CUs computing, then all CUs storing), and
+// the rotation gives every XCD the same mix, while the 32 tiles one XCD runs
+// together still come from one slot and share its operand rows in L2.
 __device__ __forceinline__ TileCoord locate_tile(const GemmGroups& gt, int id, int mode, int M, int n_tiles_n) {
-  int lo = 0, hi = gt.n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (gt.tile0[mid] <= id) lo = mid; else hi = mid - 1;
+  int lo = 0, local;
+  if (mode == MX_GROUP_K && gt.interleave) {
+    const int q = id / kXcdChunk, r = q / gt.n, pos = q - r * gt.n;
+    lo = pos + r % gt.n;
+    if (lo >= gt.n) lo -= gt.n;
+    local = r * kXcdChunk + (id - q * kXcdChunk);
+  } else {
+    int hi = gt.n - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (gt.tile0[mid] <= id) lo = mid; else hi = mid - 1;
+    }
+    local = id - gt.tile0[lo];
   }
   TileCoord t;
   t.slot = lo;
-  const int local = id - gt.tile0[lo];
   const int rows = mode == MX_GROUP_M ? gt.len[lo] : M;
   const int mtiles = (rows + BM - 1) / BM;
   // band raster: kBandM m-tiles x all n-tiles, m fastest inside a band
@@ -617,16 +633,24 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       auto coff = [&](int mi, int s, int i) __attribute__((always_inline)) -> uint32_t {
         return ((uint32_t)(32 * mi + 8 * i + rr) * ld + 32 * s + 4 * cc) * 4;
       };
+      // Old values of an accumulating store: two 32-row blocks in flight (the
+      // loads of block mi + 2 go out as soon as block mi has been added), so
+      // the read latency is exposed once per tile rather than once per block.
+      u32x4 old_e[NS][4], old_o[NS][4];
+      auto load_old = [&](int mi, u32x4 (&o)[NS][4]) __attribute__((always_inline)) {
+        static_for<0, NS * 4>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int s = decltype(j_c)::value / 4, i = decltype(j_c)::value % 4;
+          o[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rd, coff(mi, s, i), 0, POL);
+        });
+      };
+      if constexpr (ACC) {
+        load_old(0, old_e);
+        load_old(1, old_o);
+      }
       static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_c)::value;
         __builtin_amdgcn_sched_barrier(0);
-        u32x4 old[NS][4];
-        if constexpr (ACC) {
-          static_for<0, NS * 4>([&](auto j_c) __attribute__((always_inline)) {
-            constexpr int s = decltype(j_c)::value / 4, i = decltype(j_c)::value % 4;
-            old[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rd, coff(mi, s, i), 0, POL);
-          });
-        }
+        u32x4 (&old)[NS][4] = (mi & 1) ? old_o : old_e;
         uint8_t* const st = slice + (mi & 1) * (NS * 4096);
         static_for<0, NS * 4>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int s = decltype(j_c)::value / 4, vg = decltype(j_c)::value % 4;
@@ -652,6 +676,10 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
             });
           }
         });
+        if constexpr (ACC && mi + 2 < 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_old(mi + 2, old);
+        }
       });
     };
     using plain = std::integral_constant<int, 0>;
@@ -812,21 +840,27 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     static_assert(2 * kColHalf + 2 * NS * 32 * 4 <= kSlice, "column scale bytes must fit the wave's slice");
     uint8_t* const csl = slice + 2 * kColHalf;
     const uint32_t ccol = (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3));
+    // gate and up (bf16) of one 32-row block and 32 columns (16 per lane) are
+    // a unit of 8 loads; a ring of NS units keeps the next NS units in flight
+    // (unit (mi + 1, s) is requested once unit (mi, s) has been used), so the
+    // H1 read latency is exposed once per tile rather than once per row block.
+    u32x2 gl[NS][4], ul[NS][4];
+    auto load_gu = [&](int mi, int s) __attribute__((always_inline)) {
+      const uint32_t r = 32 * mi + l32;
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const uint32_t o = (r * 2 * F + jw0 + 32 * s + 8 * vg + 4 * h) * 2;
+        gl[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o, 0, 0);
+        ul[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o + 2 * F, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NS; ++s) load_gu(0, s);
     static_for<0, 4>([&](auto mi_c) __attribute__((always_inline)) {
       constexpr int mi = decltype(mi_c)::value;
       const uint32_t r = 32 * mi + l32;
       const bool blk_ok = wrow0 + 32 * mi < len;
       uint32_t rsg = 0, rsu = 0;
-      __builtin_amdgcn_sched_barrier(0);
-      // gate and up (bf16) of the sub-tile's 4 x 16 columns, all requested
-      // before the first is used
-      u32x2 gl[NS][4], ul[NS][4];
-      static_for<0, NS * 4>([&](auto i_c) __attribute__((always_inline)) {
-        constexpr int s = decltype(i_c)::value / 4, vg = decltype(i_c)::value % 4;
-        const uint32_t o = (r * 2 * F + jw0 + 32 * s + 8 * vg + 4 * h) * 2;
-        gl[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o, 0, 0);
-        ul[s][vg] = __builtin_amdgcn_raw_buffer_load_b64(rh1, o + 2 * F, 0, 0);
-      });
       float dp = 0.0f;
       static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
@@ -858,6 +892,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
           csl[(s * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cg : 0u);
           csl[((NS + s) * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cu : 0u);
         }
+        if constexpr (mi + 1 < 4) load_gu(mi + 1, s);
       });
       {
         const uint32_t m = (uint32_t)m0 + r;

@@ -72,6 +72,9 @@ enum GemmEpi : int {
 // are (first row, rows) in MX_GROUP_M and (first K column, padded K) in MX_GROUP_K.
 struct GemmGroups {
   int32_t n;
+  // MX_GROUP_K with every slot holding the same number of tiles, a multiple
+  // of 32: chunks of 32 tile ids rotate over the slots (see locate_tile)
+  int32_t interleave;
   int32_t tile0[kMaxGroups + 1];
   int32_t gid[kMaxGroups];
   int32_t a0[kMaxGroups];

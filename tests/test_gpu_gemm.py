@@ -135,12 +135,14 @@ def test_group_m_bf16_out_and_accumulate(gpu_lib):
 
 
 @pytest.mark.parametrize("accumulate", [False, True])
-def test_group_k_wgrad_layout(gpu_lib, accumulate):
+@pytest.mark.parametrize("Mo,No", [(288, 320), (2048, 1024)])
+def test_group_k_wgrad_layout(gpu_lib, accumulate, Mo, No):
     """Columnwise-grouped operands from the oracle's own quantizer, ragged
-    groups including an empty one; fp32 output per group."""
-    rng = np.random.default_rng(6 + accumulate)
+    groups including an empty one; fp32 output per group. At 2048 x 1024 each
+    group has 8 x 4 = 32 tiles, a whole XCD chunk, so the launch interleaves
+    the groups chunk by chunk."""
+    rng = np.random.default_rng(6 + accumulate + Mo)
     sizes = np.array([300, 0, 45, 129])
-    Mo, No = 288, 320
     x = rng.standard_normal((sizes.sum(), Mo))
     y = rng.standard_normal((sizes.sum(), No))
     aq, as_ = orc.quantize_colwise(x, sizes)      # [Mo, sumP]
