@@ -218,6 +218,45 @@ MX_API mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_s
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Cached MXFP8 weights ("quantized initialization" in the Llama 3 recipe
+ * page's MXFP8 throughput section, and the 16-bit master weights of item 3 of
+ * the MoE article): the two weight casts of grouped_mlp_fwd are taken out of
+ * the step. A training loop quantizes its bf16 master weights once after each
+ * optimizer update and runs every forward and backward of that step on the
+ * cached copies, which hold exactly the codes and scales grouped_mlp_fwd
+ * would have made from the same weights, so results are identical.
+ *
+ * grouped_mlp_weight_cache_bytes -- size of the cache for E, H, F (rows and
+ * split are not used). Errors: MX_EINVAL, MX_ESHAPE as grouped_mlp_sizes.
+ *
+ * grouped_mlp_quantize_weights -- cast w1 bf16 [E, 2F, H] and w2 bf16
+ * [E, H, F] into `cache` (caller-owned device buffer, 256-byte aligned, at
+ * least grouped_mlp_weight_cache_bytes), rowwise and columnwise. Async on
+ * `stream`. The cache layout is private to the library; it stays valid until
+ * the caller overwrites or frees it. Errors: MX_EINVAL (null pointers),
+ * MX_EALIGN, MX_EWORKSPACE (cache too small), MX_EHIP.
+ *
+ * grouped_mlp_fwd_cached / grouped_mlp_bwd_cached -- grouped_mlp_fwd and
+ * grouped_mlp_bwd with the weights read from a filled cache instead of being
+ * cast from bf16. Same arguments, buffer sizes and errors otherwise; a
+ * `saved` buffer written by grouped_mlp_fwd_cached holds no weight copies and
+ * must be consumed by grouped_mlp_bwd_cached with the same cache.
+ */
+MX_API mx_status grouped_mlp_weight_cache_bytes(const mx_mlp_dims* dims, size_t* bytes);
+MX_API mx_status grouped_mlp_quantize_weights(const mx_mlp_dims* dims, const void* w1, const void* w2,
+                                              void* cache, size_t cache_bytes, void* stream);
+MX_API mx_status grouped_mlp_fwd_cached(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                        const void* x, const float* probs, const void* cache,
+                                        size_t cache_bytes, void* y, void* saved, size_t saved_bytes,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                        const void* dy, const float* probs, const void* cache,
+                                        size_t cache_bytes, const void* saved, size_t saved_bytes,
+                                        void* dx, float* dprobs, float* dw1, float* dw2,
+                                        int32_t accumulate_wgrad, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * mx_set_stage_events -- optional per-stage timing of the fused MLP calls
  * (observability only; nothing is computed differently). events points to
  * `count` hipEvent_t handles owned by the caller, or is NULL to switch timing

@@ -87,6 +87,15 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_bwd.restype = ctypes.c_int
     L.grouped_mlp_bwd.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
                                   vp, sz, vp]
+    L.grouped_mlp_weight_cache_bytes.restype = ctypes.c_int
+    L.grouped_mlp_weight_cache_bytes.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(sz)]
+    L.grouped_mlp_quantize_weights.restype = ctypes.c_int
+    L.grouped_mlp_quantize_weights.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, sz, vp]
+    L.grouped_mlp_fwd_cached.restype = ctypes.c_int
+    L.grouped_mlp_fwd_cached.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, sz, vp, sz, vp]
+    L.grouped_mlp_bwd_cached.restype = ctypes.c_int
+    L.grouped_mlp_bwd_cached.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp,
+                                         i32, vp, sz, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -240,6 +249,84 @@ def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulat
     return dx, dprobs, dw1, dw2
 
 
+def grouped_mlp_weight_cache_bytes(E: int, H: int, F: int) -> int:
+    """Bytes of the MXFP8 weight cache for E experts, hidden H, ffn F."""
+    L = load()
+    n = ctypes.c_size_t()
+    _check(L.grouped_mlp_weight_cache_bytes(ctypes.byref(_dims(E, 0, H, F)), ctypes.byref(n)))
+    return n.value
+
+
+class WeightCache:
+    """MXFP8 copies of w1 [E,2F,H] and w2 [E,H,F] in both layouts (a
+    caller-owned device buffer filled by grouped_mlp_quantize_weights)."""
+
+    def __init__(self, E: int, H: int, F: int, device="cuda"):
+        self.ehf = (int(E), int(H), int(F))
+        self.buf = _byte_buffer(grouped_mlp_weight_cache_bytes(E, H, F), device)
+
+
+def grouped_mlp_quantize_weights(w1, w2, cache: WeightCache | None = None, stream=None) -> WeightCache:
+    """Cast the bf16 master weights into `cache` (allocated when None); run
+    once after each optimizer update, then use the *_cached calls."""
+    L = load()
+    E, F2, H = w1.shape
+    F = F2 // 2
+    if cache is None:
+        cache = WeightCache(E, H, F, device=w1.device)
+    if cache.ehf != (E, H, F):
+        raise ValueError(f"weight cache is for (E, H, F) = {cache.ehf}, weights are {(E, H, F)}")
+    _check(L.grouped_mlp_quantize_weights(ctypes.byref(_dims(E, 0, H, F)), _ptr(w1), _ptr(w2),
+                                          _ptr(cache.buf), cache.buf.numel(), _stream(stream)))
+    return cache
+
+
+def grouped_mlp_fwd_cached(x, probs, cache: WeightCache, split_sizes, *, training: bool = True,
+                           workspace=None, out=None, stream=None):
+    """grouped_mlp_fwd on the cached MXFP8 weights. Returns (y, MLPState or None)."""
+    L = load()
+    R, H = x.shape
+    E, Hc, F = cache.ehf
+    if Hc != H:
+        raise ValueError(f"x has hidden {H}, the weight cache {Hc}")
+    fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
+    if workspace is None or workspace.numel() < fws:
+        workspace = _byte_buffer(fws, x.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x.device) if out is None else out
+    saved = _byte_buffer(sv, x.device) if training else None
+    _check(L.grouped_mlp_fwd_cached(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes), _ptr(x),
+                                    _ptr(probs), _ptr(cache.buf), cache.buf.numel(), _ptr(y), _ptr(saved),
+                                    0 if saved is None else saved.numel(), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+    state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
+    return y, state
+
+
+def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw1=None, dw2=None,
+                           accumulate: bool = False, want_dprobs: bool = True, workspace=None, stream=None):
+    """grouped_mlp_bwd after grouped_mlp_fwd_cached (same cache).
+    Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
+    L = load()
+    E, R, H, F = state.dims
+    _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
+    if workspace is None or workspace.numel() < bws:
+        workspace = _byte_buffer(bws, dy.device)
+    dev = dy.device
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dprobs = torch.empty((R,), dtype=torch.float32, device=dev) if want_dprobs else None
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, H), dtype=torch.float32, device=dev)
+        accumulate = False if dw2 is None else accumulate
+    if dw2 is None:
+        dw2 = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    _check(L.grouped_mlp_bwd_cached(ctypes.byref(_dims(E, R, H, F)), _i64_array(state.split_sizes),
+                                    _ptr(dy), _ptr(probs), _ptr(cache.buf), cache.buf.numel(),
+                                    _ptr(state.saved), state.saved.numel(), _ptr(dx), _ptr(dprobs),
+                                    _ptr(dw1), _ptr(dw2), int(accumulate), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+    return dx, dprobs, dw1, dw2
+
+
 _event_arrays = []   # keeps the handle arrays alive while the library holds them
 
 
@@ -288,6 +375,33 @@ class MLPRunner:
                                  0 if saved is None else saved.numel(), _ptr(self.fwd_ws),
                                  self.fwd_ws.numel(), _stream(stream)))
         return self.y
+
+    def quantize_weights(self, w1, w2, stream=None):
+        """Fill this runner's weight cache (allocated on first use) from w1, w2."""
+        E, _, H, F = self.dims
+        if getattr(self, "cache", None) is None:
+            self.cache = WeightCache(E, H, F, device=self.y.device)
+        grouped_mlp_quantize_weights(w1, w2, self.cache, stream=stream)
+        return self.cache
+
+    def forward_cached(self, x, probs, training=True, stream=None):
+        L = load()
+        saved = self.saved if training else None
+        _check(L.grouped_mlp_fwd_cached(ctypes.byref(self._c_dims), self._c_split, _ptr(x), _ptr(probs),
+                                        _ptr(self.cache.buf), self.cache.buf.numel(), _ptr(self.y),
+                                        _ptr(saved), 0 if saved is None else saved.numel(),
+                                        _ptr(self.fwd_ws), self.fwd_ws.numel(), _stream(stream)))
+        return self.y
+
+    def backward_cached(self, dy, probs, dw1, dw2, accumulate=True, want_dprobs=True, stream=None):
+        L = load()
+        _check(L.grouped_mlp_bwd_cached(ctypes.byref(self._c_dims), self._c_split, _ptr(dy), _ptr(probs),
+                                        _ptr(self.cache.buf), self.cache.buf.numel(), _ptr(self.saved),
+                                        self.saved.numel(), _ptr(self.dx),
+                                        _ptr(self.dprobs) if want_dprobs else None, _ptr(dw1), _ptr(dw2),
+                                        int(accumulate), _ptr(self.bwd_ws), self.bwd_ws.numel(),
+                                        _stream(stream)))
+        return self.dx, (self.dprobs if want_dprobs else None)
 
     def backward(self, dy, probs, dw1, dw2, accumulate=True, want_dprobs=True, stream=None):
         L = load()

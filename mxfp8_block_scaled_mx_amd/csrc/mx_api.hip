@@ -174,7 +174,9 @@ mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, in
   A.sa = mx::row_major_scales(lda);
   A.sb = mx::row_major_scales(ldb);
   A.as_bytes = M * (lda / 32);
-  A.bs_bytes = n_rows_b * (ldb / 32);
+  // extent of the B scale array: all G groups in group-M, B itself in group-K
+  A.bs_bytes = mode == MX_GROUP_M ? ((int64_t)(G - 1) * b_group_stride + n_rows_b * ldb) / 32
+                                  : n_rows_b * (ldb / 32);
   A.c_group_stride = c_group_stride;
   A.M = (int32_t)M; A.N = (int32_t)N; A.K = (int32_t)K;
   A.accumulate = accumulate;
@@ -356,6 +358,51 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
 uint8_t* at(void* base, size_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
 const uint8_t* at(const void* base, size_t off) { return reinterpret_cast<const uint8_t*>(base) + off; }
 
+// MXFP8 copies of the expert weights, both layouts with k-tiled scales:
+// W1 rowwise [E*2F, H], W2 rowwise [E*H, F], W1 columnwise [H, E*2F] (groups
+// of 2F columns per expert) and W2 columnwise [F, E*H] (groups of H).
+struct WeightCopies {
+  uint8_t *w1q, *w1s, *w2q, *w2s;      // rowwise (forward GEMMs)
+  uint8_t *w1cq, *w1cs, *w2cq, *w2cs;  // columnwise (dgrad GEMMs)
+};
+
+// Layout of a weight cache buffer (grouped_mlp_quantize_weights): the four
+// copies back to back, 256-byte aligned regions; offsets depend on E, H, F only.
+struct WeightCacheLayout {
+  size_t w1q, w1s, w2q, w2s, w1cq, w1cs, w2cq, w2cs, total;
+};
+
+WeightCacheLayout weight_cache_layout(int64_t E, int64_t H, int64_t F) {
+  WeightCacheLayout W;
+  size_t c = 0;
+  W.w1q = take(c, E * 2 * F * H); W.w1s = take(c, E * 2 * F * H / 32);
+  W.w2q = take(c, E * H * F); W.w2s = take(c, E * H * F / 32);
+  W.w1cq = take(c, H * E * 2 * F); W.w1cs = take(c, H * E * 2 * F / 32);
+  W.w2cq = take(c, F * E * H); W.w2cs = take(c, F * E * H / 32);
+  W.total = c;
+  return W;
+}
+
+WeightCopies weight_cache_copies(const WeightCacheLayout& W, void* base) {
+  return {at(base, W.w1q), at(base, W.w1s), at(base, W.w2q), at(base, W.w2s),
+          at(base, W.w1cq), at(base, W.w1cs), at(base, W.w2cq), at(base, W.w2cs)};
+}
+
+// Quantize the bf16 master weights into both MXFP8 layouts (columnwise
+// copies skipped where their pointers are null).
+mx_status quantize_weights_into(const MlpLayout& L, const void* w1, const void* w2, const WeightCopies& wc,
+                                hipStream_t stream, bool marks) {
+  const int64_t H = L.H, F = L.F;
+  const int E = L.E;
+  std::vector<int64_t> g_w1(E, 2 * F), g_w2(E, H);
+  if (marks) stage_mark(1, stream);
+  mx_status st = quantize_impl(w1, MX_BF16, E * 2 * F, H, g_w1.data(), E, wc.w1q, wc.w1s, wc.w1cq, wc.w1cs,
+                               stream, true);
+  if (st != MX_OK) return st;
+  if (marks) stage_mark(2, stream);
+  return quantize_impl(w2, MX_BF16, E * H, F, g_w2.data(), E, wc.w2q, wc.w2s, wc.w2cq, wc.w2cs, stream, true);
+}
+
 mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, const char* what) {
   hipError_t e = mx::launch_gemm(mode, epi, p.scale_dword, p.args, p.total_tiles, stream);
   if (e != hipSuccess) return hip_fail(e, what);
@@ -425,34 +472,28 @@ mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes,
   return MX_OK;
 }
 
-mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x, const float* probs,
-                          const void* w1, const void* w2, void* y, void* saved, size_t saved_bytes,
-                          void* workspace, size_t workspace_bytes, void* stream_) {
-  g_err[0] = 0;
-  const char* who = "grouped_mlp_fwd";
-  MlpLayout L;
-  mx_status st = mlp_layout(dims, split_sizes, &L, who);
-  if (st != MX_OK) return st;
-  if (!x || !w1 || !w2 || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
-  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
-      (saved && !aligned(saved, 256)) || (probs && !aligned(probs, 4)))
-    return fail(MX_EALIGN, "%s: x, w1, w2, y must be 16-byte and workspace/saved 256-byte aligned", who);
-  if (workspace_bytes < L.fwd_total)
-    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
-  if (saved && saved_bytes < L.saved_total)
-    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+}  // extern "C"
+
+namespace {
+
+// The fused forward after argument checks. With wc_cached null the weights
+// are cast from w1/w2 into the workspace (rowwise) and saved (columnwise)
+// copies; otherwise the cached copies are used and w1/w2 are not read.
+mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const void* w1, const void* w2,
+                   const WeightCopies* wc_cached, void* y, void* saved, void* workspace, hipStream_t stream) {
   const int64_t R = L.R, H = L.H, F = L.F;
   const int E = L.E;
-  std::vector<int64_t> g_w1(E, 2 * F), g_w2(E, H);
+  const WeightCopies wc = wc_cached ? *wc_cached
+      : WeightCopies{at(workspace, L.w1q), at(workspace, L.w1s), at(workspace, L.w2q), at(workspace, L.w2s),
+                     saved ? at(saved, L.w1cq) : nullptr, saved ? at(saved, L.w1cs) : nullptr,
+                     saved ? at(saved, L.w2cq) : nullptr, saved ? at(saved, L.w2cs) : nullptr};
   // plan both GEMMs before launching anything
   GemmPlan p1, p2;
-  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, 2 * F, H, at(workspace, L.xq), at(workspace, L.xs), H,
-                 at(workspace, L.w1q), at(workspace, L.w1s), H, 2 * F * H, y, MX_BF16, 2 * F, 0, 0,
-                 mx::EPI_SWIGLU_FWD, 2 * F, &p1);
+  mx_status st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, 2 * F, H, at(workspace, L.xq), at(workspace, L.xs), H,
+                           wc.w1q, wc.w1s, H, 2 * F * H, y, MX_BF16, 2 * F, 0, 0, mx::EPI_SWIGLU_FWD, 2 * F, &p1);
   if (st != MX_OK) return st;
   st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, H, F, at(workspace, L.aq), at(workspace, L.as), F,
-                 at(workspace, L.w2q), at(workspace, L.w2s), F, H * F, y, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &p2);
+                 wc.w2q, wc.w2s, F, H * F, y, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &p2);
   if (st != MX_OK) return st;
   use_k_tiled_scales(p1, H / 128, R, H / 128, E * 2 * F, 2 * F * H / 32, L.q0);
   use_k_tiled_scales(p2, F / 128, R, F / 128, E * H, H * F / 32, L.q0);
@@ -474,14 +515,13 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
                      saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true);
   if (st != MX_OK) return st;
-  stage_mark(1, stream);
-  st = quantize_impl(w1, MX_BF16, E * 2 * F, H, g_w1.data(), E, at(workspace, L.w1q), at(workspace, L.w1s),
-                     saved ? at(saved, L.w1cq) : nullptr, saved ? at(saved, L.w1cs) : nullptr, stream, true);
-  if (st != MX_OK) return st;
-  stage_mark(2, stream);
-  st = quantize_impl(w2, MX_BF16, E * H, F, g_w2.data(), E, at(workspace, L.w2q), at(workspace, L.w2s),
-                     saved ? at(saved, L.w2cq) : nullptr, saved ? at(saved, L.w2cs) : nullptr, stream, true);
-  if (st != MX_OK) return st;
+  if (wc_cached) {
+    stage_mark(1, stream);      // the weight stages are empty
+    stage_mark(2, stream);
+  } else {
+    st = quantize_weights_into(L, w1, w2, wc, stream, true);
+    if (st != MX_OK) return st;
+  }
   stage_mark(3, stream);
   st = run_gemm(p1, MX_GROUP_M, mx::EPI_SWIGLU_FWD, stream, "grouped_mlp_fwd gemm1");
   if (st != MX_OK) return st;
@@ -497,14 +537,108 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   return MX_OK;
 }
 
-mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy, const float* probs,
-                          const void* saved, size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
-                          int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream_) {
+mx_status fwd_checks(const MlpLayout& L, const void* x, const float* probs, const void* y, const void* saved,
+                     size_t saved_bytes, const void* workspace, size_t workspace_bytes, const char* who) {
+  if (!x || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) || (saved && !aligned(saved, 256)) ||
+      (probs && !aligned(probs, 4)))
+    return fail(MX_EALIGN, "%s: x, y must be 16-byte and workspace/saved 256-byte aligned", who);
+  if (workspace_bytes < L.fwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
+  if (saved && saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  return MX_OK;
+}
+
+mx_status cache_checks(const MlpLayout& L, const void* cache, size_t cache_bytes, WeightCacheLayout* W,
+                       const char* who) {
+  *W = weight_cache_layout(L.E, L.H, L.F);
+  if (!cache) return fail(MX_EINVAL, "%s: weight cache is null", who);
+  if (!aligned(cache, 256)) return fail(MX_EALIGN, "%s: weight cache must be 256-byte aligned", who);
+  if (cache_bytes < W->total)
+    return fail(MX_EWORKSPACE, "%s: weight cache %zu bytes < required %zu", who, cache_bytes, W->total);
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x, const float* probs,
+                          const void* w1, const void* w2, void* y, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const char* who = "grouped_mlp_bwd";
+  const char* who = "grouped_mlp_fwd";
   MlpLayout L;
   mx_status st = mlp_layout(dims, split_sizes, &L, who);
   if (st != MX_OK) return st;
+  st = fwd_checks(L, x, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
+  return fwd_impl(L, x, probs, w1, w2, nullptr, y, saved, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_weight_cache_bytes(const mx_mlp_dims* dims, size_t* bytes) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_weight_cache_bytes";
+  if (!bytes) return fail(MX_EINVAL, "%s: bytes is null", who);
+  if (!dims) return fail(MX_EINVAL, "%s: dims is null", who);
+  // the cache does not depend on the routed rows: check the rest with R = 0
+  mx_mlp_dims d = *dims;
+  d.rows = 0;
+  std::vector<int64_t> zeros(d.num_experts > 0 && d.num_experts <= mx::kMaxGroups ? d.num_experts : 1, 0);
+  MlpLayout L;
+  mx_status st = mlp_layout(&d, zeros.data(), &L, who);
+  if (st != MX_OK) return st;
+  *bytes = weight_cache_layout(L.E, L.H, L.F).total;
+  return MX_OK;
+}
+
+mx_status grouped_mlp_quantize_weights(const mx_mlp_dims* dims, const void* w1, const void* w2, void* cache,
+                                       size_t cache_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_quantize_weights";
+  if (!dims) return fail(MX_EINVAL, "%s: dims is null", who);
+  mx_mlp_dims d = *dims;
+  d.rows = 0;
+  std::vector<int64_t> zeros(d.num_experts > 0 && d.num_experts <= mx::kMaxGroups ? d.num_experts : 1, 0);
+  MlpLayout L;
+  mx_status st = mlp_layout(&d, zeros.data(), &L, who);
+  if (st != MX_OK) return st;
+  WeightCacheLayout W;
+  st = cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
+  return quantize_weights_into(L, w1, w2, weight_cache_copies(W, cache), reinterpret_cast<hipStream_t>(stream),
+                               false);
+}
+
+mx_status grouped_mlp_fwd_cached(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x,
+                                 const float* probs, const void* cache, size_t cache_bytes, void* y, void* saved,
+                                 size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd_cached";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = fwd_checks(L, x, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  WeightCacheLayout W;
+  st = cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  const WeightCopies wc = weight_cache_copies(W, const_cast<void*>(cache));
+  return fwd_impl(L, x, probs, nullptr, nullptr, &wc, y, saved, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+mx_status bwd_checks(const MlpLayout& L, const void* dy, const float* probs, const void* saved, size_t saved_bytes,
+                     const void* dx, const float* dprobs, const float* dw1, const float* dw2, const void* workspace,
+                     size_t workspace_bytes, const char* who) {
   if (!dy || !saved || !dx || !dw1 || !dw2 || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
   if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(saved, 256) ||
       !aligned(workspace, 256) || (probs && !aligned(probs, 4)) || (dprobs && !aligned(dprobs, 4)))
@@ -513,13 +647,24 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
     return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
   if (workspace_bytes < L.bwd_total)
     return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.bwd_total);
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return MX_OK;
+}
+
+// The fused backward after argument checks; the columnwise weight copies
+// come from saved (w1c/w2c null) or from a weight cache.
+mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const void* saved,
+                   const WeightCopies* wc_cached, void* dx, float* dprobs, float* dw1, float* dw2,
+                   int32_t accumulate_wgrad, void* workspace, hipStream_t stream) {
   const int64_t R = L.R, H = L.H, F = L.F, P = L.sumP;
   const int E = L.E;
+  const uint8_t* w1cq = wc_cached ? wc_cached->w1cq : at(saved, L.w1cq);
+  const uint8_t* w1cs = wc_cached ? wc_cached->w1cs : at(saved, L.w1cs);
+  const uint8_t* w2cq = wc_cached ? wc_cached->w2cq : at(saved, L.w2cq);
+  const uint8_t* w2cs = wc_cached ? wc_cached->w2cs : at(saved, L.w2cs);
   GemmPlan pd2, pw2, pd1, pw1;
   // dA = dY_row . colwise(W2_e): B_e = w2 columnwise [F, E*H] at column e*H
-  st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, F, H, at(workspace, L.dyq), at(workspace, L.dys), H,
-                 at(saved, L.w2cq), at(saved, L.w2cs), E * H, H, dx, MX_BF16, F, 0, 0, mx::EPI_SWIGLU_BWD, F, &pd2);
+  mx_status st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, F, H, at(workspace, L.dyq), at(workspace, L.dys), H,
+                           w2cq, w2cs, E * H, H, dx, MX_BF16, F, 0, 0, mx::EPI_SWIGLU_BWD, F, &pd2);
   if (st != MX_OK) return st;
   // dW2_e = colwise(dY_e) . colwise(A_e)^T
   st = gemm_plan(MX_GROUP_K, E, L.split.data(), H, F, P, at(workspace, L.dycq), at(workspace, L.dycs), P,
@@ -527,7 +672,7 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   if (st != MX_OK) return st;
   // dX = dH1_row . colwise(W1_e): B_e = w1 columnwise [H, E*2F] at column e*2F
   st = gemm_plan(MX_GROUP_M, E, L.split.data(), R, H, 2 * F, at(workspace, L.dhq), at(workspace, L.dhs), 2 * F,
-                 at(saved, L.w1cq), at(saved, L.w1cs), E * 2 * F, 2 * F, dx, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &pd1);
+                 w1cq, w1cs, E * 2 * F, 2 * F, dx, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &pd1);
   if (st != MX_OK) return st;
   // dW1_e = colwise(dH1_e) . colwise(X_e)^T
   st = gemm_plan(MX_GROUP_K, E, L.split.data(), 2 * F, H, P, at(workspace, L.dhcq), at(workspace, L.dhcs), P,
@@ -584,6 +729,43 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   if (st != MX_OK) return st;
   stage_mark(6, stream);
   return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy, const float* probs,
+                          const void* saved, size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                          int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = bwd_checks(L, dy, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  return bwd_impl(L, dy, probs, saved, nullptr, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy,
+                                 const float* probs, const void* cache, size_t cache_bytes, const void* saved,
+                                 size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                                 int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd_cached";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = bwd_checks(L, dy, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  WeightCacheLayout W;
+  st = cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  const WeightCopies wc = weight_cache_copies(W, const_cast<void*>(cache));
+  return bwd_impl(L, dy, probs, saved, &wc, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
+                  reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -233,11 +233,17 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.a + a_row0 * lda + kbeg, (int64_t)(a_rows_valid - 1) * lda + klen);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(bq + kbeg, (int64_t)(b_rows - 1) * ldb + klen);
   // Scales: A from the 32-row group of the tile's first row on (rows past the
-  // array read 0); B over the rows of B_g.
+  // array read 0); B over the rows of B_g, and never past the end of the
+  // scale array: in the k-tiled columnwise weight layout the groups sit side
+  // by side along k, so B_g's base is g * bs_group_stride into the array
+  // while its rows span the array's full row pitch, and the k-step loaded
+  // past the last one would otherwise reach beyond the array's last byte.
   const int64_t a_grp0 = (a_row0 >> 5) * sa.grp;
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(args.as + a_grp0, args.as_bytes - a_grp0);
   const __amdgpu_buffer_rsrc_t rsb =
-      make_rsrc(bsc, MODE == MX_GROUP_M ? (int64_t)(b_rows >> 5) * sb.grp : args.bs_bytes);
+      make_rsrc(bsc, MODE == MX_GROUP_M ? min((int64_t)(b_rows >> 5) * sb.grp,
+                                              args.bs_bytes - (int64_t)g * args.bs_group_stride)
+                                        : args.bs_bytes);
 
   // first B row of tile row block r0 (a multiple of 8 rows): SwiGLU fwd pairs
   // gate rows [nt*128, +128) (tile rows 0..127) with up rows F + the same j

@@ -112,6 +112,39 @@ def test_mlp_sizes_and_errors(L):
                              None, FAKE, FAKE, 1, ws, b.value, None) == EINVAL
 
 
+def test_weight_cache_sizes_and_errors(L):
+    n = ctypes.c_size_t()
+    E, H, F = 2, 128, 256
+    assert L.grouped_mlp_weight_cache_bytes(ctypes.byref(_dims(E=E, H=H, F=F)), ctypes.byref(n)) == OK
+    codes = 2 * (E * 2 * F * H + E * H * F)          # both layouts of W1 and W2
+    assert codes * (1 + 1 / 32) <= n.value <= codes * (1 + 1 / 32) + 8 * 256
+    assert L.grouped_mlp_weight_cache_bytes(ctypes.byref(_dims(H=96)), ctypes.byref(n)) == ESHAPE
+    assert L.grouped_mlp_weight_cache_bytes(None, ctypes.byref(n)) == EINVAL
+    assert L.grouped_mlp_weight_cache_bytes(ctypes.byref(_dims()), None) == EINVAL
+    d = _dims(E=E, H=H, F=F)
+    cb = ctypes.c_size_t()
+    L.grouped_mlp_weight_cache_bytes(ctypes.byref(d), ctypes.byref(cb))
+    ws = ctypes.c_void_p(0x100000)
+    assert L.grouped_mlp_quantize_weights(ctypes.byref(d), FAKE, FAKE, ws, cb.value - 1, None) == EWORKSPACE
+    assert L.grouped_mlp_quantize_weights(ctypes.byref(d), None, FAKE, ws, cb.value, None) == EINVAL
+    assert L.grouped_mlp_quantize_weights(ctypes.byref(d), FAKE, FAKE, None, cb.value, None) == EINVAL
+    assert L.grouped_mlp_quantize_weights(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x100010), cb.value,
+                                          None) == EALIGN
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    split = mx._i64_array([40, 24])
+    assert L.grouped_mlp_sizes(ctypes.byref(d), split, ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)) == OK
+    assert L.grouped_mlp_fwd_cached(ctypes.byref(d), split, FAKE, None, ws, cb.value - 1, FAKE, None, 0, ws,
+                                    f.value, None) == EWORKSPACE
+    assert L.grouped_mlp_fwd_cached(ctypes.byref(d), split, FAKE, None, None, cb.value, FAKE, None, 0, ws,
+                                    f.value, None) == EINVAL
+    assert L.grouped_mlp_fwd_cached(ctypes.byref(d), split, FAKE, None, ws, cb.value, FAKE, None, 0, ws,
+                                    f.value - 1, None) == EWORKSPACE
+    assert L.grouped_mlp_bwd_cached(ctypes.byref(d), split, FAKE, None, ws, cb.value - 1, ws, s.value, FAKE,
+                                    None, FAKE, FAKE, 1, ws, b.value, None) == EWORKSPACE
+    assert L.grouped_mlp_bwd_cached(ctypes.byref(d), split, FAKE, None, ws, cb.value, None, s.value, FAKE,
+                                    None, FAKE, FAKE, 1, ws, b.value, None) == EINVAL
+
+
 def test_product_has_no_oracle_dependency():
     """The product package never imports the test oracle."""
     pkg = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd")

@@ -79,3 +79,39 @@ def test_fullsize_sampled(gpu_lib, name):
             err = rel_norm(got[m], g[key][m])
             print(f"[fullsize] {name}: {key} expert {e} error {err:.2e}", flush=True)
             assert err <= TOL, f"{key} expert {e}: {err}"
+
+
+def test_fullsize_cached_weights_bit_identical(gpu_lib):
+    """The Mixtral-shaped forward + backward on weights cast once into the
+    weight cache (grouped_mlp_quantize_weights, then the *_cached calls)
+    equals the step that casts the bf16 weights itself, bit for bit, at full
+    size. At this shape the cache is a whole number of 2 MiB pages, so the
+    dgrad GEMMs' loads of the columnwise weight scales must stay inside it."""
+    name = "mixtral_moe_fwd_bwd"
+    w = wl.WORKLOADS[name]
+    print(f"[fullsize] {name} cached weights: generating inputs", flush=True)
+    c = wl.make_mlp_inputs(w, with_dy=True)
+    split = c["split_sizes"].tolist()
+    E, R, H, F = w.experts, w.rows, w.hidden, w.ffn
+    x, w1, w2, dy = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]), dev_bf16(c["dy"])
+    probs = dev_f32(c["probs"])
+    runner = gpu_lib.MLPRunner(E, R, H, F, split)
+    grads = [torch.zeros((E, 2 * F, H), dtype=torch.float32, device="cuda"),
+             torch.zeros((E, H, F), dtype=torch.float32, device="cuda")]
+    print(f"[fullsize] {name} cached weights: reference step", flush=True)
+    y_ref = runner.forward(x, probs, w1, w2, training=True).clone()
+    dx_ref, dp_ref = (t.clone() for t in runner.backward(dy, probs, *grads, accumulate=True))
+    cache_bytes = gpu_lib.grouped_mlp_weight_cache_bytes(E, H, F)
+    assert cache_bytes % (2 << 20) == 0
+    runner.quantize_weights(w1, w2)
+    grads_c = [torch.zeros_like(grads[0]), torch.zeros_like(grads[1])]
+    print(f"[fullsize] {name} cached weights: cached step", flush=True)
+    y = runner.forward_cached(x, probs, training=True)
+    dx, dp = runner.backward_cached(dy, probs, *grads_c, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    assert torch.equal(dx.view(torch.int16), dx_ref.view(torch.int16))
+    assert torch.equal(dp.view(torch.int32), dp_ref.view(torch.int32))
+    for a, b in zip(grads_c, grads):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    print(f"[fullsize] {name} cached weights: bit-identical", flush=True)

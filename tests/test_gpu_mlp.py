@@ -150,3 +150,39 @@ def test_autograd_function(gpu_lib):
     assert rel_norm(to_np(x.grad), want["dx"]) <= TOL
     assert rel_norm(to_np(p.grad), want["dprobs"]) <= TOL
     assert rel_norm(to_np(w1.grad.float()), want["dw1"]) <= TOL
+
+
+@pytest.mark.parametrize("name", ["ragged4", "many_small"])
+def test_cached_weights_match_uncast_path(gpu_lib, name):
+    """grouped_mlp_fwd_cached / grouped_mlp_bwd_cached on weights cast once by
+    grouped_mlp_quantize_weights give bit-identical outputs to the calls that
+    cast the bf16 weights themselves (same codes, same kernels), in training
+    and inference, and the cache survives a second step with another split."""
+    mx = gpu_lib
+    k = CASES[name]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    x, w1, w2, dy = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]), dev_bf16(c["dy"])
+    p = dev_f32(c["probs"])
+    split = c["split_sizes"].tolist()
+    cache = mx.grouped_mlp_quantize_weights(w1, w2)
+
+    def same(a, b):
+        if a.dtype == torch.bfloat16:
+            return torch.equal(a.view(torch.int16), b.view(torch.int16))
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+    for split_now in (split, split[::-1]):
+        y_ref, st_ref = mx.grouped_mlp_fwd(x, p, w1, w2, split_now, training=True)
+        y_c, st_c = mx.grouped_mlp_fwd_cached(x, p, cache, split_now, training=True)
+        y_i, _ = mx.grouped_mlp_fwd_cached(x, p, cache, split_now, training=False)
+        ref = mx.grouped_mlp_bwd(dy, p, st_ref)
+        got = mx.grouped_mlp_bwd_cached(dy, p, st_c, cache)
+        torch.cuda.synchronize()
+        assert same(y_ref, y_c) and same(y_ref, y_i)
+        for a, b, what in zip(ref, got, ("dx", "dprobs", "dw1", "dw2")):
+            assert same(a, b), what
+    # and the cached path against the oracle directly
+    want = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], c["split_sizes"])
+    y_c, _ = mx.grouped_mlp_fwd_cached(x, p, cache, split, training=False)
+    torch.cuda.synchronize()
+    _check_rows(to_np(y_c), want["y"], split, "y (cached weights)")
