@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--workload", default="mixtral_moe_fwd_bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--no-qinit", action="store_true", help="skip the cached-weight (qinit-style) step")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip the forward-only Llama dense and Mixtral-shaped workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of a known size (reference for HBM counters)")
     args = ap.parse_args()
@@ -250,6 +253,34 @@ def main():
     # qinit-style variant: the weights are cast into the MXFP8 weight cache
     # once, outside the timed region (as after an optimizer update), and the
     # step runs grouped_mlp_fwd_cached + grouped_mlp_bwd_cached
+    if not args.no_qinit:
+        measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step_flops, out, torch)
+
+    if not args.no_quantize:
+        out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
+        log(f"quantize {out['quantize']['gbps']:.0f} GB/s")
+
+    # free device memory before the forward-only workloads and the CPU leg
+    del runner, dw1, dw2, x, w1, w2, dy
+    torch.cuda.empty_cache()
+    if not args.no_forward:
+        out["forward_only"] = {}
+        for name in ("llama8b_dense_fwd", "mixtral_moe_fwd"):
+            r = measure_forward(mx, torch, np, wlmod, dev, wlmod.WORKLOADS[name], args.steps, args.warmup)
+            out["forward_only"][name] = r
+            log(f"{name}: forward {r['ms']:.3f} ms -> {r['tflops']:.1f} TFLOP/s; "
+                f"cached weights {r['qinit_style_ms']:.3f} ms -> {r['qinit_style_tflops']:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(inp, wl)
+        log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+def measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step_flops, out, torch):
+    """The training step on weights cast once into the weight cache before the
+    timed region (grouped_mlp_quantize_weights), as after an optimizer update."""
     runner.quantize_weights(w1, w2)
     for _ in range(args.warmup):
         runner.forward_cached(x, probs, training=True)
@@ -268,18 +299,47 @@ def main():
                                   "once by grouped_mlp_quantize_weights before the timed region"}
     log(f"qinit-style step {q_ms:.3f} ms -> {out['qinit_style']['tflops']:.1f} TFLOP/s")
 
-    if not args.no_quantize:
-        out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
-        log(f"quantize {out['quantize']['gbps']:.0f} GB/s")
 
-    # free device memory before the CPU leg
-    del runner, dw1, dw2, x, w1, w2, dy
-    torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(inp, wl)
-        log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
-    print(json.dumps(out), flush=True)
+def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup):
+    """Inference forward (grouped_mlp_fwd without a saved buffer: quantize X
+    and the weights rowwise, GEMM1 + SwiGLU epilogue, GEMM2) on a forward-only
+    workload, then the same with the weights cast once into the weight cache
+    before the timed region (grouped_mlp_fwd_cached). Algorithmic GEMM FLOP:
+    6 R H F."""
+    log(f"generating inputs for {wl.name} (seed {wl.seed})")
+    inp = wlmod.make_mlp_inputs(wl)
+
+    def to_dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w1, w2 = (to_dev_bf16(inp[k]) for k in ("x", "w1", "w2"))
+    probs = torch.from_numpy(inp["probs"]).to(dev)
+    E, R, H, F = wl.experts, wl.rows, wl.hidden, wl.ffn
+    split = inp["split_sizes"].tolist()
+    runner = mx.MLPRunner(E, R, H, F, split, device=dev)
+    flops = 6.0 * R * H * F
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms = timed(lambda: runner.forward(x, probs, w1, w2, training=False))
+    runner.quantize_weights(w1, w2)
+    q_ms = timed(lambda: runner.forward_cached(x, probs, training=False))
+    del runner, x, w1, w2, probs
+    return {"rows": R, "experts": E, "hidden": H, "ffn": F, "split_sizes": split,
+            "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "qinit_style_ms": round(q_ms, 4), "qinit_style_tflops": round(flops / (q_ms * 1e-3) / 1e12, 1),
+            "step": "grouped_mlp_fwd (inference; weights cast in the call) / grouped_mlp_fwd_cached"}
 
 
 def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
@@ -319,18 +379,23 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
     for i in range(8):
         call(xs[i % copies])
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    # batches of back-to-back launches between one pair of events (an event
+    # between every launch would add its own gap to each ~60 us kernel)
+    batches = 5
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
     evs[0].record()
-    for i in range(iters):
-        call(xs[i % copies])
-        evs[i + 1].record()
+    for b in range(batches):
+        for i in range(iters):
+            call(xs[i % copies])
+        evs[b + 1].record()
     torch.cuda.synchronize()
-    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(iters)]
+    times = [evs[b].elapsed_time(evs[b + 1]) / iters for b in range(batches)]
     algo = rows * cols * 2 + 2 * (rows * cols + rows * cols // 32)
     med = float(np.median(times))
     gbps = algo / (med * 1e-3) / 1e9
     return {"workload": "quantize_16384x4096", "layouts": "rowwise+columnwise", "bytes": algo,
             "median_ms": round(med, 4), "min_ms": round(float(np.min(times)), 4),
+            "timing": f"median over {batches} batches of the mean of {iters} back-to-back launches",
             "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
