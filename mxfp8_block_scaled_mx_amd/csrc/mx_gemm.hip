@@ -279,6 +279,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // first 128-column step of this tile's k range in the scale layout
   const int q_base = MODE == MX_GROUP_K ? (args.k_tiled ? args.groups.q0[slot] : (int)(kbeg >> 7)) : 0;
 
+  // valid A rows of this wave's 128 (wave-uniform; <= 0: none)
+  const int wave_rows = __builtin_amdgcn_readfirstlane(a_rows_valid - (BM / 2) * wm);
   v16f acc[NS][4];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -407,12 +409,17 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       if constexpr (step + 2 < 8)
         fa[(step + 2) % 3] = read_frag(sA, 128 * wm + 32 * ((step + 2) % 4) + l32, (step + 2) / 4);
       if constexpr (step < NS) fb_n[step] = read_frag(sB, nsub(step) + l32, 1);
-      static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int s = decltype(s_c)::value;
-        acc[s][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            ks == 0 ? fb_c[s] : fb_n[s], fa[step % 3], acc[s][mi], 0, 0, 0,
-            scale_of(sb_c[s][0], sb_c[s][1], ks), 0, scale_of(sa_c[mi][0], sa_c[mi][1], ks));
-      });
+      // a 32-row block wholly past the tile's valid A rows (the last m-tile
+      // of a group) keeps zero accumulators, which every epilogue masks or
+      // drops anyway: its MFMAs are skipped (wave-uniform branch)
+      if (32 * mi < wave_rows) {
+        static_for<0, NS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int s = decltype(s_c)::value;
+          acc[s][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              ks == 0 ? fb_c[s] : fb_n[s], fa[step % 3], acc[s][mi], 0, 0, 0,
+              scale_of(sb_c[s][0], sb_c[s][1], ks), 0, scale_of(sa_c[mi][0], sa_c[mi][1], ks));
+        });
+      }
       // fence: each step's slice of loads stays with its 4 MFMAs
       __builtin_amdgcn_sched_barrier(0);
     });
