@@ -60,7 +60,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int NS = 8 / kWavesN;             // n sub-tiles of 32 per wave
 [[maybe_unused]] constexpr int kWaveN = 256 / kWavesN;      // n columns per wave
 [[maybe_unused]] constexpr int kDmaPerWave = 32 / kWaves;    // 1 KB blocks of A (and of B) per wave per k-step
-constexpr int kBandM = 8;
+// m-tiles per band of the raster: 8 for group-M (fprop, dgrad); 4 for
+// group-K (wgrad), measured faster there (wgrad1 of the Mixtral-shaped
+// backward 1.99 -> 1.90 ms) while slower for group-M
+__host__ __device__ constexpr int band_m(int mode) { return mode == MX_GROUP_K ? 4 : 8; }
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
 // open; issued through the builtin so the compiler's own waitcnt tracking
 // knows the loads have landed.
@@ -128,7 +131,8 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmGroups& gt, int id, i
   t.slot = lo;
   const int rows = mode == MX_GROUP_M ? gt.len[lo] : M;
   const int mtiles = (rows + BM - 1) / BM;
-  // band raster: kBandM m-tiles x all n-tiles, m fastest inside a band
+  // band raster: band_m(mode) m-tiles x all n-tiles, m fastest inside a band
+  const int kBandM = band_m(mode);
   const int per_band = kBandM * n_tiles_n;
   const int band = local / per_band;
   const int in_band = local - band * per_band;
@@ -446,15 +450,17 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // L2 prefetch: once a k-step's loads are issued, each wave touches one
   // 128-byte line per row of a share of the operand rows of k-step
   // kt + kPrefetchAhead, so that step's LDS loads hit L2 instead of waiting
-  // for memory. The 32 tiles one XCD runs at a time (8 m-tiles x 4 n-tiles of
-  // the band raster) share A and B blocks, so a tile touches only its share:
-  // A rows [64*(nt%4), +64) (waves 0-1, 32 rows each) and B rows
-  // [32*(mt%8), +32) (waves 2-3, 16 rows each). The loaded words land in a
-  // sink register one k-step later, when the in-order completion of the next
-  // loads has made them ready, so the prefetch never adds a wait.
+  // for memory. The 32 tiles one XCD runs at a time (Bm m-tiles x 32/Bm
+  // n-tiles of the band raster, Bm = band_m(MODE)) share A and B blocks, so a
+  // tile touches only its share: A rows [8Bm*(nt%(32/Bm)), +8Bm) (waves 0-1,
+  // half each) and B rows [(256/Bm)*(mt%Bm), +256/Bm) (waves 2-3, half
+  // each). The loaded words land in a sink register one k-step later, when
+  // the in-order completion of the next loads has made them ready, so the
+  // prefetch never adds a wait.
   uint32_t pf_sink = 0, pf_last = 0;
-  const uint32_t pf_row = wave < 2 ? (uint32_t)(64 * (tc.nt & 3) + 32 * wave + (lane & 31))
-                                   : (uint32_t)(32 * (tc.mt & 7) + 16 * (wave - 2) + (lane & 15));
+  constexpr int Bm = band_m(MODE), SA = 8 * Bm, SB = 256 / Bm;
+  const uint32_t pf_row = wave < 2 ? (uint32_t)(SA * (tc.nt % (32 / Bm)) + (SA / 2) * wave + (lane % (SA / 2)))
+                                   : (uint32_t)(SB * (tc.mt % Bm) + (SB / 2) * (wave - 2) + (lane % (SB / 2)));
   const uint32_t pf_voff = wave < 2 ? pf_row * lda : b_row_base(pf_row & ~7u) * ldb + (pf_row & 7u) * ldb;
   auto prefetch = [&](int kt) __attribute__((always_inline)) -> uint32_t {
     const uint32_t k0 = (uint32_t)kt * BK;
