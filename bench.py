@@ -193,6 +193,16 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    # per-stage times: the same steps with stage events set, which runs every
+    # stage on the launch stream in order (no side-stream overlap)
+    log(f"timing {args.steps} steps stage by stage")
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
         mx.set_stage_events(ev_f[i])
         runner.forward(x, probs, w1, w2, training=True)
         mx.set_stage_events(ev_b[i])
@@ -200,8 +210,7 @@ def main():
     end.record()
     mx.set_stage_events(None)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    serial_ms = start.elapsed_time(end) / args.steps
 
     stages = {}
     for names, evs in ((mx.FWD_STAGES, ev_f), (mx.BWD_STAGES, ev_b)):
@@ -244,6 +253,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.tokens, "topk": wl.topk, "experts": E,
                    "rows": R, "hidden": H, "ffn": F, "split_sizes": split,
                    "step": "grouped_mlp_fwd(training) + grouped_mlp_bwd(fp32 wgrad accumulate)"},
+        "serial_ms_per_step": round(serial_ms, 4),
         "gemm_only": {"tflops": round(gemm_tflops, 1),
                       "frac_mfma_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "ms": round(gemm_ms, 4)},
         "stages": per_stage,

@@ -42,6 +42,12 @@
  *     library never allocates, frees or keeps device memory between calls.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronizing. split_sizes are host arrays.
+ *     grouped_mlp_bwd also runs its wgrad stages on a side
+ *     stream the library creates per thread and device (on first use, default
+ *     priority, kept until the process ends): it waits on an event recorded on
+ *     `stream` and `stream` waits on an event recorded after the side work,
+ *     so to the caller all work is ordered on `stream` (also under graph
+ *     capture). `stream` must belong to the current device.
  *   - Arguments are validated before anything is enqueued. On any non-OK
  *     status nothing was enqueued and no output was touched; mx_last_error()
  *     then holds a one-line description (thread-local).
@@ -258,7 +264,9 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
 
 /*
  * mx_set_stage_events -- optional per-stage timing of the fused MLP calls
- * (observability only; nothing is computed differently). events points to
+ * (observability only; the results are the same). While events are set, the
+ * fused MLP calls run every stage on the caller's stream in order, without
+ * the side stream, so each stage's time is its own. events points to
  * `count` hipEvent_t handles owned by the caller, or is NULL to switch timing
  * off. While set on the calling thread, grouped_mlp_fwd records events[i] on
  * its stream before stage i and after the last stage (stages: quantize X,

@@ -22,6 +22,50 @@ void stage_mark(int i, hipStream_t stream) {
     (void)hipEventRecord(reinterpret_cast<hipEvent_t>(g_events[i]), stream);
 }
 
+mx_status fail(mx_status s, const char* fmt, ...);
+mx_status hip_fail(hipError_t e, const char* what);
+
+// Side stream of the calling thread on the current device, with the events
+// that fork it from and join it back into the caller's stream. The fused MLP
+// runs its HBM-bound stages there (the W2 cast, the wgrad GEMMs) beside the
+// MFMA-bound ones; every side launch is ordered after the caller's earlier
+// work and before its later work by these events, so to the caller all work
+// is ordered on its own stream. Created on first use, default priority, kept
+// for the life of the process; one set per thread so that calls from
+// different threads never share an event.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+};
+thread_local SideStream g_side[64];
+
+mx_status side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MX_EUNSUPPORTED, "device index %d out of range", dev);
+  SideStream& sd = g_side[dev];
+  if (sd.s == nullptr) {
+    e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+    if (e != hipSuccess) { sd.s = nullptr; return hip_fail(e, "side stream"); }
+    for (hipEvent_t& v : sd.ev) {
+      e = hipEventCreateWithFlags(&v, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "side stream event");
+    }
+  }
+  *out = &sd;
+  return MX_OK;
+}
+
+// `to` waits for all work enqueued so far on `from` (event ev recorded on from).
+mx_status wait_for(hipStream_t to, hipStream_t from, hipEvent_t ev) {
+  hipError_t e = hipEventRecord(ev, from);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = hipStreamWaitEvent(to, ev, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  return MX_OK;
+}
+
 mx_status fail(mx_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -515,6 +559,8 @@ mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const 
   st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
                      saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true);
   if (st != MX_OK) return st;
+  // (running the W2 cast on the side stream beside GEMM1 was measured: it
+  // slows GEMM1 by more than the cast takes, so the forward stays serial)
   if (wc_cached) {
     stage_mark(1, stream);      // the weight stages are empty
     stage_mark(2, stream);
@@ -700,10 +746,23 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   a.dprobs_part = dprobs ? reinterpret_cast<float*>(at(workspace, L.part)) : nullptr;
   a.R = (int32_t)R;
 
+  // stages overlap on the side stream unless per-stage timing is on: the
+  // wgrad GEMMs (HBM-bound fp32 read-modify-write) run there, wgrad2 beside
+  // dgrad2 and wgrad1 (which needs dH1 from dgrad2) beside dgrad1
+  SideStream* sd = nullptr;
+  if (g_events == nullptr) {
+    st = side_stream(&sd);
+    if (st != MX_OK) return st;
+  }
   stage_mark(0, stream);
   st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
                      at(workspace, L.dycq), at(workspace, L.dycs), stream, true);
   if (st != MX_OK) return st;
+  if (sd != nullptr) {
+    st = wait_for(sd->s, stream, sd->ev[0]);
+    if (st == MX_OK) st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, sd->s, "grouped_mlp_bwd wgrad2");
+    if (st != MX_OK) return st;
+  }
   stage_mark(1, stream);
   st = run_gemm(pd2, MX_GROUP_M, mx::EPI_SWIGLU_BWD, stream, "grouped_mlp_bwd dgrad2");
   if (st != MX_OK) return st;
@@ -713,9 +772,16 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
                                             (int32_t)R, (int32_t)L.n_tiles_f, stream);
     if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dprobs");
   }
+  if (sd != nullptr) {
+    st = wait_for(sd->s, stream, sd->ev[1]);
+    if (st == MX_OK) st = run_gemm(pw1, MX_GROUP_K, mx::EPI_F32, sd->s, "grouped_mlp_bwd wgrad1");
+    if (st != MX_OK) return st;
+  }
   stage_mark(3, stream);
-  st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad2");
-  if (st != MX_OK) return st;
+  if (sd == nullptr) {
+    st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad2");
+    if (st != MX_OK) return st;
+  }
   stage_mark(4, stream);
   {
     const int tail = plan_split_tail(pd1, 2 * F, reinterpret_cast<float*>(at(workspace, L.split1)), L.split1_bytes);
@@ -725,6 +791,7 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
     if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dgrad1 split reduce");
   }
   stage_mark(5, stream);
+  if (sd != nullptr) return wait_for(stream, sd->s, sd->ev[2]);
   st = run_gemm(pw1, MX_GROUP_K, mx::EPI_F32, stream, "grouped_mlp_bwd wgrad1");
   if (st != MX_OK) return st;
   stage_mark(6, stream);

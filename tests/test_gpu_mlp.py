@@ -186,3 +186,31 @@ def test_cached_weights_match_uncast_path(gpu_lib, name):
     y_c, _ = mx.grouped_mlp_fwd_cached(x, p, cache, split, training=False)
     torch.cuda.synchronize()
     _check_rows(to_np(y_c), want["y"], split, "y (cached weights)")
+
+
+def test_backward_on_user_stream_orders_side_work(gpu_lib):
+    """grouped_mlp_bwd runs its wgrad GEMMs on a library side stream forked
+    from and joined back into the caller's stream. Two accumulating calls on
+    a user stream must give exactly twice one call's dW (fp32 doubling is
+    exact): the second call's read-modify-write may start only after the
+    first's, and everything is complete once the user stream is synchronized."""
+    mx = gpu_lib
+    k = CASES["two_tiles_ffn"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    x, w1, w2, dy = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]), dev_bf16(c["dy"])
+    p = dev_f32(c["probs"])
+    split = c["split_sizes"].tolist()
+    E, H, F = k["E"], k["H"], k["F"]
+    user = torch.cuda.Stream()
+    with torch.cuda.stream(user):
+        _, st = mx.grouped_mlp_fwd(x, p, w1, w2, split, training=True, stream=user)
+        once = [torch.zeros((E, 2 * F, H), dtype=torch.float32, device="cuda"),
+                torch.zeros((E, H, F), dtype=torch.float32, device="cuda")]
+        twice = [torch.zeros_like(once[0]), torch.zeros_like(once[1])]
+        dx1, dp1, _, _ = mx.grouped_mlp_bwd(dy, p, st, dw1=once[0], dw2=once[1], accumulate=True, stream=user)
+        for _ in range(2):
+            mx.grouped_mlp_bwd(dy, p, st, dw1=twice[0], dw2=twice[1], accumulate=True, stream=user)
+    user.synchronize()
+    for a, b in zip(twice, once):
+        assert torch.equal(a, 2 * b)
+    assert float(once[0].abs().sum()) > 0 and float(once[1].abs().sum()) > 0
