@@ -80,16 +80,6 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppRowMirror = 0x140;     // lane i <- 15 - i within each row of 16
-constexpr int kDppRowHalfMirror = 0x141; // lane i <- 7 - i within each half row of 8
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
-}
-
 // Half-wave exchange: lanes 0..31 send `lower_sends` to lane l + 32, lanes
 // 32..63 send `upper_sends` to lane l - 32; returns what the lane received.
 // (v_permlane32_swap exchanges the upper half of its first operand with the
@@ -106,25 +96,6 @@ __device__ __forceinline__ uint32_t max_halves(uint32_t v) {
 __device__ __forceinline__ float sum_halves(float v) {
   const u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r.x) + __uint_as_float(r.y);
-}
-// max over the 32 lanes of the caller's half-wave: butterfly inside rows of
-// 16 through DPP, then the two rows of the half through v_permlane16_swap.
-__device__ __forceinline__ uint32_t max_lanes32(uint32_t v) {
-  v = umax(v, dpp_mov<kDppQuadXor1>(v));
-  v = umax(v, dpp_mov<kDppQuadXor2>(v));
-  v = umax(v, dpp_mov<kDppRowHalfMirror>(v));
-  v = umax(v, dpp_mov<kDppRowMirror>(v));
-  const u32x2 r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return umax(r.x, r.y);
-}
-// 4x4 byte transpose inside each quad of lanes: lane b (= lane & 3) holds in
-// byte c the element (b, c); afterwards it holds in byte r the element (r, b).
-// v_perm_b32 picks bytes 0-3 from its second and 4-7 from its first operand.
-__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, int b) {
-  const uint32_t p = dpp_mov<kDppQuadXor1>(x);
-  const uint32_t t = __builtin_amdgcn_perm(p, x, (b & 1) ? 0x03070105u : 0x06020400u);
-  const uint32_t q = dpp_mov<kDppQuadXor2>(t);
-  return __builtin_amdgcn_perm(q, t, (b & 2) ? 0x03020706u : 0x05040100u);
 }
 
 // Identity move through a VALU DPP instruction (quad_perm 0,1,2,3). Passing

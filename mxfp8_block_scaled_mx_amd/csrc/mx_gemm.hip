@@ -71,15 +71,14 @@ __host__ __device__ constexpr int band_m(int mode) { return mode == MX_GROUP_K ?
 [[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
 // L2 prefetch distance in k-steps (see kstep)
 [[maybe_unused]] constexpr int kPrefetchAhead = 3;
-// Epilogue staging of columnwise codes in a wave's 32 KB LDS slice: [column]
-// [64 rows] with a 96-byte stride (24 dwords: the 8 columns x 8 quads one
-// ds_write_b32 touches fall in 64 distinct banks); the SwiGLU backward keeps
-// the gate and up halves (NS * 32 columns each) kColHalf apart.
-[[maybe_unused]] constexpr int kColStride = 96;
+// Epilogue transpose area of a 32 x 32 fp32 block in a wave's LDS slice:
+// [column][row] with 36 floats per column (a multiple of 4 for the 16-byte
+// reads; the 8 lanes of one 16-byte read pass start 4 banks apart)
+[[maybe_unused]] constexpr int kTrStride = 36;
+[[maybe_unused]] constexpr int kTrBytes = 32 * kTrStride * 4;
 // cache policy of memory touched exactly once (fp32 C of the plain epilogue):
 // non-temporal
 [[maybe_unused]] constexpr int kNonTemporal = 2;
-[[maybe_unused]] constexpr int kColHalf = NS * 32 * kColStride;
 
 struct TileCoord {
   int slot;   // group slot in the table
@@ -525,7 +524,6 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   {
   const int h = lane_e >> 5;        // shadows of the loop's lane-derived values
   const int l32 = lane_e & 31;
-  const int qb = l32 & 3, qa = l32 >> 2;   // lane within its quad, quad index
   const int tid = wave * 64 + lane_e;
   const int wrows = max(0, min(BM / 2, a_rows_valid - (BM / 2) * wm));   // valid rows of this wave
   const int64_t m0 = a_row0 + (BM / 2) * wm;                             // global row of its first row
@@ -569,16 +567,20 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   };
   // Both MXFP8 layouts of one 32 x 32 block of an fp32 intermediate d (this
   // lane: row l32 of the block, 16 columns). Rowwise: one scale per row over
-  // the 32 columns (lanes l, l^32), codes stored directly. Columnwise: one
-  // scale per column over the 32 rows (the lanes of a half-wave); the codes are
-  // transposed inside each quad of lanes and staged in LDS as [column][row]
-  // (stride kColStride), to be written out as column runs by flush_cols.
+  // the 32 columns (lanes l, l^32), codes stored directly. Columnwise: the
+  // block is written transposed into the wave's fp32 area tr ([column][row],
+  // kTrStride floats per column) and read back so that lane L holds rows
+  // 16*(L/32) .. +15 of column L%32: the column amax is a local max plus one
+  // exchange with lane L^32, and the 16 codes are 16 consecutive bytes of the
+  // column's run in the columnwise layout, stored at
+  // c_off + (L%32) * ldq + 16*(L/32) of rc when col_store.
   // The scale codes come back to the caller, which gathers the bytes that
   // share a k-tiled word and stores whole words: row_sc is the rowwise code
-  // of this lane's row, col_sc the columnwise code of block column
-  // 8*(l32/4) + 4*h + l32%4 (lanes l32 < 16).
+  // of this lane's row, col_sc the columnwise code of block column l32 (each
+  // column once in the lanes with h == 0).
   auto quantize_block = [&](const float (&d)[16], const __amdgpu_buffer_rsrc_t& rq, uint32_t q_off,
-                            bool row_store, uint8_t* stage, uint32_t& row_sc, uint32_t& col_sc)
+                            bool row_store, float* tr, const __amdgpu_buffer_rsrc_t& rc, uint32_t c_off,
+                            uint32_t ldq, bool col_store, uint32_t& row_sc, uint32_t& col_sc)
       __attribute__((always_inline)) {
     {
       uint32_t am = 0;
@@ -594,45 +596,31 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
       row_sc = sc;
     }
     {
-      uint32_t scv[16];
-      float inv[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        scv[v] = scale_code_from_amax_bits(max_lanes32(abs_bits(d[v])));
-        inv[v] = inv_scale_from_code(scv[v]);
+      for (int vg = 0; vg < 4; ++vg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tr[(8 * vg + 4 * h + i) * kTrStride + l32] = d[4 * vg + i];
+      float cv[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 t = *reinterpret_cast<const float4*>(tr + l32 * kTrStride + 16 * h + 4 * j);
+        cv[4 * j] = t.x; cv[4 * j + 1] = t.y; cv[4 * j + 2] = t.z; cv[4 * j + 3] = t.w;
       }
-      // scale of column v is kept by lane l32 == v (v < 16)
-      uint32_t ssel = scv[0];
+      uint32_t am = 0;
 #pragma unroll
-      for (int v = 1; v < 16; ++v) ssel = l32 == v ? scv[v] : ssel;
-      col_sc = ssel;
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const uint32_t x = e4m3x4(d[4 * vg] * inv[4 * vg], d[4 * vg + 1] * inv[4 * vg + 1],
-                                  d[4 * vg + 2] * inv[4 * vg + 2], d[4 * vg + 3] * inv[4 * vg + 3]);
-        // lane (quad qa, qb) now holds rows 4qa..4qa+3 of column 8vg + 4h + qb
-        const uint32_t y = quad_transpose_bytes(x, qb);
-        *reinterpret_cast<uint32_t*>(stage + (8 * vg + 4 * h + qb) * kColStride + 4 * qa) = y;
-      }
+      for (int v = 0; v < 16; ++v) am = umax(am, abs_bits(cv[v]));
+      am = max_halves(am);
+      const uint32_t sc = scale_code_from_amax_bits(am);
+      const float inv = inv_scale_from_code(sc);
+      u32x4 q;
+      q.x = e4m3x4(cv[0] * inv, cv[1] * inv, cv[2] * inv, cv[3] * inv);
+      q.y = e4m3x4(cv[4] * inv, cv[5] * inv, cv[6] * inv, cv[7] * inv);
+      q.z = e4m3x4(cv[8] * inv, cv[9] * inv, cv[10] * inv, cv[11] * inv);
+      q.w = e4m3x4(cv[12] * inv, cv[13] * inv, cv[14] * inv, cv[15] * inv);
+      if (col_store) __builtin_amdgcn_raw_buffer_store_b128(q, rc, c_off + (uint32_t)l32 * ldq + 16 * h, 0, 0);
+      col_sc = sc;
     }
   };
-  // Write nj staged columns x 64 rows (16-byte runs, 4 per column) to the
-  // columnwise layout; column jl goes to offset jl * ldq + row_off of rq when
-  // jl < j_valid and the run's first row is below rows_valid.
-  auto flush_cols = [&](const uint8_t* stage, auto nj_c, const __amdgpu_buffer_rsrc_t& rq, uint32_t col_off,
-                        uint32_t ldq, uint32_t row_off, int j_valid, int rows_valid) __attribute__((always_inline)) {
-    constexpr int nj = decltype(nj_c)::value;
-    asm volatile("" ::: "memory");
-    static_for<0, nj / 16>([&](auto it_c) __attribute__((always_inline)) {
-      const int c = decltype(it_c)::value * 64 + lane_e;
-      const int jl = c >> 2, part = c & 3;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + jl * kColStride + 16 * part);
-      if (jl < j_valid && 16 * part < rows_valid)
-        __builtin_amdgcn_raw_buffer_store_b128(v, rq, (uint32_t)(col_off + jl) * ldq + row_off + 16 * part, 0, 0);
-    });
-    asm volatile("" ::: "memory");
-  };
-
   if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
     if (MODE == MX_GROUP_K && klen == 0 && args.accumulate) return;
     // fp32 out: the accumulators leave through the wave's LDS slice so that
@@ -744,7 +732,6 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const int jw0 = tc.nt * (BN / 2) + (NS / 2) * 32 * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;       // first row of the wave inside its group
     const int len = args.groups.len[slot];
-    const int len_pad = (len + 31) & ~31;               // rows of the group in the columnwise layout
     const uint32_t ldq = (uint32_t)args.ld_col;
     const int64_t crow0 = args.groups.pc0[slot] + wrow0;   // columnwise position of the wave's first row
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
@@ -797,7 +784,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
           store_row_bf16(rh1, (r * 2 * F + F + jw0 + 32 * s) * 2, uv);
         }
         uint32_t rsc_v, csc_v;
-        quantize_block(a, rqr, r * F + jw0 + 32 * s, jok, slice + 32 * s * kColStride + 32 * (mi & 1), rsc_v, csc_v);
+        quantize_block(a, rqr, r * F + jw0 + 32 * s, jok, reinterpret_cast<float*>(slice), rqc,
+                       (uint32_t)(32 * s) * ldq + 32 * mi, ldq, jok && blk_ok, rsc_v, csc_v);
         rsw |= rsc_v << (8 * s);
         csw[s] |= (blk_ok ? csc_v : 0u) << (8 * mi);
       });
@@ -807,20 +795,15 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
           __builtin_amdgcn_raw_buffer_store_b16((unsigned short)rsw, rsr,
                                                 ((m >> 5) * args.nq_row + (b0 >> 2)) * 128 + (m & 31) * 4 + (b0 & 3), 0, 0);
       }
-      if constexpr (mi & 1) {
-        if (col_out)
-          flush_cols(slice, std::integral_constant<int, 32 * (NS / 2)>{}, rqc, 0u, ldq, (uint32_t)(64 * (mi >> 1)),
-                     (int)F - jw0, len_pad - wrow0 - 64 * (mi >> 1));
-      }
     });
     // columnwise scale words: only where the wave has rows of the group (the
     // word past the group's last k-step belongs to the next group)
-    if (col_out && wave_jok && wrow0 < len && l32 < 16) {
-      const uint32_t c = (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3));
+    if (col_out && wave_jok && wrow0 < len && h == 0) {
 #pragma unroll
       for (int s2 = 0; s2 < NS / 2; ++s2)
         __builtin_amdgcn_raw_buffer_store_b32(csw[s2], rsc,
-                                              ((b0 + s2) * args.nq_col + q0 + ((uint32_t)wrow0 >> 7)) * 128 + c * 4, 0, 0);
+                                              ((b0 + s2) * args.nq_col + q0 + ((uint32_t)wrow0 >> 7)) * 128 + l32 * 4,
+                                              0, 0);
     }
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     // acc = dA for ffn columns j = jw0 + 32*s + 8*(v/4) + 4*h + v%4 (s = 0..3)
@@ -829,7 +812,6 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const int jw0 = tc.nt * BN + kWaveN * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;
     const int len = args.groups.len[slot];
-    const int len_pad = (len + 31) & ~31;
     const uint32_t ldq = (uint32_t)args.ld_col;
     const int64_t crow0 = args.groups.pc0[slot] + wrow0;
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
@@ -853,12 +835,11 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     // half are the 4 bytes of one rowwise word per row, and its 4 row blocks
     // the 4 bytes of one columnwise word per column (bytes of blocks past the
     // group are 0). The columnwise bytes collect in the slice past the
-    // column-code staging, word (half, s, column).
+    // transpose area, word (half, s, column).
     const uint32_t bg0 = (uint32_t)jw0 >> 5, bu0 = (uint32_t)(F + jw0) >> 5;
     const bool wave_jok = jw0 < (int)F;                  // F % 128 == 0: all NS blocks valid or none
-    static_assert(2 * kColHalf + 2 * NS * 32 * 4 <= kSlice, "column scale bytes must fit the wave's slice");
-    uint8_t* const csl = slice + 2 * kColHalf;
-    const uint32_t ccol = (uint32_t)(8 * (l32 >> 2) + 4 * h + (l32 & 3));
+    static_assert(kTrBytes + 2 * NS * 32 * 4 <= kSlice, "column scale bytes must fit the wave's slice");
+    uint8_t* const csl = slice + kTrBytes;
     // gate and up (bf16) of one 32-row block and 32 columns (16 per lane) are
     // a unit of 8 loads; a ring of NS units keeps the next NS units in flight
     // (unit (mi + 1, s) is requested once unit (mi, s) has been used), so the
@@ -901,15 +882,16 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
             dp += jok ? da * sl * uv[i] : 0.0f;
           }
         }
-        uint8_t* st = slice + 32 * s * kColStride + 32 * (mi & 1);
+        float* const tr = reinterpret_cast<float*>(slice);
+        const uint32_t co = (uint32_t)(32 * s) * ldq + 32 * mi;
         uint32_t rg, cg, ru, cu;
-        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, jok, st, rg, cg);
-        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, jok, st + kColHalf, ru, cu);
+        quantize_block(dg, rqr, r * 2 * F + jw0 + 32 * s, jok, tr, rqc_g, co, ldq, jok && blk_ok, rg, cg);
+        quantize_block(du, rqr, r * 2 * F + F + jw0 + 32 * s, jok, tr, rqc_u, co, ldq, jok && blk_ok, ru, cu);
         rsg |= rg << (8 * s);
         rsu |= ru << (8 * s);
-        if (l32 < 16) {
-          csl[(s * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cg : 0u);
-          csl[((NS + s) * 32 + ccol) * 4 + mi] = (uint8_t)(blk_ok ? cu : 0u);
+        if (h == 0) {
+          csl[(s * 32 + l32) * 4 + mi] = (uint8_t)(blk_ok ? cg : 0u);
+          csl[((NS + s) * 32 + l32) * 4 + mi] = (uint8_t)(blk_ok ? cu : 0u);
         }
         if constexpr (mi + 1 < 4) load_gu(mi + 1, s);
       });
@@ -922,23 +904,17 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
         }
       }
       dpsum[mi] = sum_halves(dp);
-      if constexpr (mi & 1) {
-        const uint32_t ro = 64 * (mi >> 1);
-        const int rv = len_pad - wrow0 - 64 * (mi >> 1);
-        flush_cols(slice, std::integral_constant<int, kWaveN>{}, rqc_g, 0u, ldq, ro, (int)F - jw0, rv);
-        flush_cols(slice + kColHalf, std::integral_constant<int, kWaveN>{}, rqc_u, 0u, ldq, ro, (int)F - jw0, rv);
-      }
     });
     // columnwise scale words: only where the wave has rows of the group (the
     // word past the group's last k-step belongs to the next group)
-    if (wave_jok && wrow0 < len && l32 < 16) {
+    if (wave_jok && wrow0 < len && h == 0) {
       const uint32_t qo = q0 + ((uint32_t)wrow0 >> 7);
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
-        const uint32_t wg = *reinterpret_cast<const uint32_t*>(csl + (s2 * 32 + ccol) * 4);
-        const uint32_t wu = *reinterpret_cast<const uint32_t*>(csl + ((NS + s2) * 32 + ccol) * 4);
-        __builtin_amdgcn_raw_buffer_store_b32(wg, rsc, ((bg0 + s2) * args.nq_col + qo) * 128 + ccol * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(wu, rsc, ((bu0 + s2) * args.nq_col + qo) * 128 + ccol * 4, 0, 0);
+        const uint32_t wg = *reinterpret_cast<const uint32_t*>(csl + (s2 * 32 + l32) * 4);
+        const uint32_t wu = *reinterpret_cast<const uint32_t*>(csl + ((NS + s2) * 32 + l32) * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(wg, rsc, ((bg0 + s2) * args.nq_col + qo) * 128 + l32 * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(wu, rsc, ((bu0 + s2) * args.nq_col + qo) * 128 + l32 * 4, 0, 0);
       }
     }
     // dprobs partial over this tile's 256 columns: the n-waves meet in LDS
