@@ -152,6 +152,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
           uint8_t* sd = args.s_row + ((grow >> 5) * args.nq_row + (b0 >> 2)) * 128 + (grow & 31) * 4 + (b0 & 3);
           if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = word;
           else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)word;
+        } else if (NB == 4 && (cols & 127) == 0 && (reinterpret_cast<uintptr_t>(args.s_row) & 3) == 0) {
+          // row-major, whole 128-column tile: its 4 scale bytes as one aligned word
+          *reinterpret_cast<uint32_t*>(args.s_row + grow * (cols / 32) + b0) = word;
         } else {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
@@ -232,6 +235,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
           if (nvalid < 4) word &= (1u << (8 * nvalid)) - 1u;
           *reinterpret_cast<uint32_t*>(args.s_col + ((colc >> 5) * args.nq_col + args.groups.q0[g] + (tile_r0 >> 7)) * 128 +
                                        (colc & 31) * 4) = word;
+        } else if (tile_r0 + 96 < m_g && ((args.ld_col | qc0) & 127) == 0 &&
+                   (reinterpret_cast<uintptr_t>(args.s_col) & 3) == 0) {
+          // row-major, all 4 blocks inside the group: one aligned word
+          *reinterpret_cast<uint32_t*>(args.s_col + colc * (args.ld_col / 32) + qc0 / 32) = word;
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
