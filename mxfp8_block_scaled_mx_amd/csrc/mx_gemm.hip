@@ -395,7 +395,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   // sub-tiles) in 8 steps of NS MFMAs. Fragment reads run ahead of the MFMAs
   // that use them: A fragments two steps ahead (three registers sets), the B
   // fragments of k-step 1 one per step during k-step 0. Each step also issues
-  // one slice of the next k-step's loads.
+  // slices of the next k-step's loads (when: see the step body).
   auto compute = [&](const uint8_t* sA, const uint8_t* sB, int kt_next, uint8_t* nA, uint8_t* nB)
       __attribute__((always_inline)) {
     v8i fb_c[NS], fb_n[NS], fa[3];
@@ -408,7 +408,16 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     static_for<0, 8>([&](auto step_c) __attribute__((always_inline)) {
       constexpr int step = decltype(step_c)::value;
       constexpr int ks = step / 4, mi = step % 4;
-      load_part(kt_next, nA, nB, step);
+      // slice p of the next k-step's loads: at step p (group-K), or two
+      // steps earlier (group-M: slices 0-2 at step 0, slice p at step p-2),
+      // which gives the last slices more time to land before the hand-off
+      // (measured: group-M GEMMs 1.5-3.6% faster, wgrad 1.5% slower)
+      if constexpr (MODE == MX_GROUP_M) {
+        if constexpr (step == 0) { load_part(kt_next, nA, nB, 0); load_part(kt_next, nA, nB, 1); }
+        if constexpr (step + 2 < 8) load_part(kt_next, nA, nB, step + 2);
+      } else {
+        load_part(kt_next, nA, nB, step);
+      }
       if constexpr (step + 2 < 8)
         fa[(step + 2) % 3] = read_frag(sA, 128 * wm + 32 * ((step + 2) % 4) + l32, (step + 2) / 4);
       if constexpr (step < NS) fb_n[step] = read_frag(sB, nsub(step) + l32, 1);
