@@ -44,6 +44,14 @@ R10 precisions: products and sums in float64; Y, dX and the saved H1 are
     rounded to bf16 (nearest-even from float64); dW, dprobs in float64.
 R11 a zero-row expert contributes nothing; its dW is the input dW
     (accumulate) or zero (overwrite).
+R12 token dispatch: the routed rows are the (token, slot) entries of the
+    top-k choices, ordered by expert, then token (the per-expert groups that
+    GroupedLinear takes, item 1); counts per expert are the split_sizes; an
+    entry whose expert lies outside [0, E) is dropped (its perm is -1).
+R13 token combine: y[t] = sum over slots j of the routed output row of
+    (t, j), slots with perm -1 skipped, summed in float64 and rounded once to
+    bf16. The routing weight is already applied inside the MLP (R8), so the
+    combine is unweighted.
 """
 from __future__ import annotations
 
@@ -58,6 +66,7 @@ __all__ = [
     "scale_exponent", "e4m3_encode", "quantize_blocks", "quantize_rowwise",
     "dequantize_rowwise", "padded_sizes", "quantize_colwise", "gemm_group_m",
     "gemm_group_k", "round_to_bf16", "sigmoid", "silu", "mlp_forward",
+    "moe_dispatch", "moe_combine",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
     "mlp_backward_wgrad_entries",
 ]
@@ -514,3 +523,58 @@ def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
     f_map = {int(f): i for i, f in enumerate(f_sel.tolist())}
     out2 = np.array([dyc[:, h2_map[h]] @ ac[:, f_map[f]] for h, f in dw2_idx.tolist()])
     return out1, out2
+
+
+# ---------------------------------------------------------------------------
+# token dispatch and combine around the grouped MLP (R12, R13)
+# ("Efficient MoE training for biological foundation models": "Dense vs. MoE
+# scaling" -- each token activates a few experts and routing adds overhead;
+# "Key technical approaches" item 1 -- GroupedLinear gathers the input tokens
+# of each expert and takes per-expert token counts, split_sizes)
+
+def moe_dispatch(x, topk_idx, topk_w, num_experts):
+    """Gather each token's rows into per-expert groups (R12).
+
+    x: [T, H] (any dtype, copied as is); topk_idx int [T, k]; topk_w [T, k]
+    or None. Returns dict: x_perm [R, H] (R = valid entries), probs_perm
+    float32 [R] (or None), perm int32 [T, k] (routed row of entry (t, j), -1
+    if dropped), row_token int32 [R], counts int64 [E]."""
+    idx = np.asarray(topk_idx)
+    T, k = idx.shape
+    entries = []                       # (t, j) in routed-row order
+    for e in range(num_experts):
+        for t in range(T):
+            for j in range(k):
+                if idx[t, j] == e:
+                    entries.append((t, j))
+    R = len(entries)
+    perm = np.full((T, k), -1, dtype=np.int32)
+    row_token = np.empty(R, dtype=np.int32)
+    for r, (t, j) in enumerate(entries):
+        perm[t, j] = r
+        row_token[r] = t
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for (t, j) in entries:
+        counts[idx[t, j]] += 1
+    x = np.asarray(x)
+    x_perm = x[row_token] if R else np.empty((0,) + x.shape[1:], dtype=x.dtype)
+    probs = None
+    if topk_w is not None:
+        w = np.asarray(topk_w, dtype=np.float32)
+        probs = np.array([w[t, j] for (t, j) in entries], dtype=np.float32)
+    return dict(x_perm=x_perm, probs_perm=probs, perm=perm, row_token=row_token, counts=counts)
+
+
+def moe_combine(y_perm_bits, perm):
+    """y[t] = bf16(sum_j y_perm[perm[t, j]]) over the valid slots (R13).
+    y_perm_bits: bf16 bit patterns [R, H]. Returns the bf16 values [T, H] as
+    float64."""
+    perm = np.asarray(perm)
+    T, k = perm.shape
+    y = bf16_bits_to_f64(y_perm_bits)
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            if perm[t, j] >= 0:
+                out[t] += y[perm[t, j]]
+    return round_to_bf16(out)

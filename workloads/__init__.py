@@ -109,19 +109,28 @@ def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
 # ---------------------------------------------------------------------------
 # routing bookkeeping (produces split_sizes and routing weights)
 
-def route_top2(logits: np.ndarray, bias: np.ndarray):
-    """Top-2 routing of each token.
+def top2_picks(logits: np.ndarray, bias: np.ndarray):
+    """The two experts each token picks (by biased logit, lower index wins ties)
+    and their routing weights (softmax over the two picks).
 
-    Returns (split_sizes int64[E], token_of_row int64[R], probs float32[R]) with
-    rows ordered by (expert, token)."""
-    T, E = logits.shape
+    Returns (idx int32 [T, 2], w float32 [T, 2])."""
     z = logits + bias[None, :]
     order = np.argsort(-z, axis=1, kind="stable")[:, :2]          # lower index wins ties
     sel = np.take_along_axis(z, order, axis=1)                    # [T, 2]
     m = sel.max(axis=1, keepdims=True)
     ex = np.exp(sel - m)
     w = ex / ex.sum(axis=1, keepdims=True)                        # softmax over the two picks
-    expert = order.reshape(-1)
+    return order.astype(np.int32), w.astype(np.float32)
+
+
+def route_top2(logits: np.ndarray, bias: np.ndarray):
+    """Top-2 routing of each token.
+
+    Returns (split_sizes int64[E], token_of_row int64[R], probs float32[R]) with
+    rows ordered by (expert, token)."""
+    T, E = logits.shape
+    order, w = top2_picks(logits, bias)
+    expert = order.reshape(-1).astype(np.int64)
     token = np.repeat(np.arange(T), 2)
     weight = w.reshape(-1)
     key = expert * T + token
@@ -167,6 +176,21 @@ def make_mlp_inputs(wl: Workload, *, with_dy: bool | None = None):
     if with_dy if with_dy is not None else wl.backward:
         out["dy"] = normal_bf16(rng, (R, H), 1e-3)
     return out
+
+
+def make_dispatch_inputs(tokens: int, experts: int, hidden: int, seed: int):
+    """Tokens and top-2 routing for token dispatch / combine: x bf16 bits
+    [T, H] ~ N(0,1), logits N(0,1) plus a per-expert bias N(0,1) (skewed
+    expert loads, as the Mixtral-shaped workloads). Returns dict with x,
+    topk_idx int32 [T, 2], topk_w float32 [T, 2], and y_perm bf16 bits
+    [2T, H] ~ N(0,1) standing in for the MLP's routed output."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (tokens, hidden), 1.0)
+    logits = rng.standard_normal((tokens, experts))
+    bias = rng.standard_normal(experts)
+    idx, w = top2_picks(logits, bias)
+    y_perm = normal_bf16(rng, (2 * tokens, hidden), 1.0)
+    return dict(x=x, topk_idx=idx, topk_w=w, y_perm=y_perm, logits=logits, bias=bias)
 
 
 def quantize_tensor_c2(seed: int = 2, rows: int = 16384, cols: int = 4096):
