@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--no-qinit", action="store_true", help="skip the cached-weight (qinit-style) step")
+    ap.add_argument("--no-moe", action="store_true", help="skip token dispatch / combine")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward-only Llama dense and Mixtral-shaped workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -270,6 +271,11 @@ def main():
         out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
         log(f"quantize {out['quantize']['gbps']:.0f} GB/s")
 
+    if not args.no_moe:
+        out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
+        log(f"dispatch {out['dispatch_combine']['dispatch_gbps']:.0f} GB/s, "
+            f"combine {out['dispatch_combine']['combine_gbps']:.0f} GB/s")
+
     # free device memory before the forward-only workloads and the CPU leg
     del runner, dw1, dw2, x, w1, w2, dy
     torch.cuda.empty_cache()
@@ -308,6 +314,44 @@ def measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step
                           "step": "grouped_mlp_fwd_cached + grouped_mlp_bwd_cached; weights cast "
                                   "once by grouped_mlp_quantize_weights before the timed region"}
     log(f"qinit-style step {q_ms:.3f} ms -> {out['qinit_style']['tflops']:.1f} TFLOP/s")
+
+
+def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096):
+    """Token dispatch and combine for 8192 tokens, top-2 of 8 experts, hidden
+    4096 (the Mixtral-shaped forward workload's routing shape). Algorithmic
+    bytes: dispatch reads x once and writes the 2T routed rows; combine reads
+    the 2T routed rows and writes y (index arrays are negligible)."""
+    c = wlmod.make_dispatch_inputs(T, E, H, seed=60)
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, y_perm = bits(c["x"]), bits(c["y_perm"])
+    idx = torch.from_numpy(c["topk_idx"]).to(dev)
+    w = torch.from_numpy(c["topk_w"]).to(dev)
+    _, _, perm, _, _ = mx.mx_moe_dispatch(x, idx, w, E)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    d_ms = timed(lambda: mx.mx_moe_dispatch(x, idx, w, E))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    c_ms = timed(lambda: mx.mx_moe_combine(y_perm, perm, out=y))
+    d_bytes = (T + 2 * T) * H * 2
+    c_bytes = (2 * T + T) * H * 2
+    return {"tokens": T, "topk": 2, "experts": E, "hidden": H,
+            "dispatch_ms": round(d_ms, 4), "dispatch_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+            "combine_ms": round(c_ms, 4), "combine_gbps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
+            "note": "dispatch time includes the binding's output allocation per call (torch caching allocator)"}
 
 
 def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup):

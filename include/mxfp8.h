@@ -263,6 +263,53 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
                                         size_t workspace_bytes, void* stream);
 
 /*
+ * Token dispatch and combine around the grouped MLP. Each token activates
+ * `topk` experts ("Efficient MoE training for biological foundation
+ * models", Dense vs. MoE scaling), and GroupedLinear takes each expert's
+ * input tokens gathered into one group with per-expert counts, split_sizes
+ * (Key technical approaches, item 1). These calls build that grouping on the
+ * device.
+ *
+ * mx_moe_dispatch_workspace_bytes -- scratch bytes of mx_moe_dispatch
+ * (0 for invalid sizes).
+ *
+ * mx_moe_dispatch -- routed rows ordered by expert, then token.
+ *   x          bf16 [tokens, hidden], hidden % 8 == 0.
+ *   topk_idx   int32 [tokens, topk]: the experts of each token (distinct per
+ *              token). An entry outside [0, num_experts) is dropped: its perm
+ *              is -1 and it takes no routed row.
+ *   topk_w     f32 [tokens, topk] routing weights, or NULL (then probs_perm
+ *              must be NULL too).
+ *   x_perm     bf16 [tokens * topk, hidden]: routed row r holds the row of its
+ *              token. Only the first sum(counts) rows are written.
+ *   probs_perm f32 [tokens * topk]: routing weight of each routed row.
+ *   perm       int32 [tokens, topk]: routed row of entry (t, j), or -1.
+ *   row_token  int32 [tokens * topk]: token of each routed row.
+ *   counts     int64 [num_experts]: rows per expert (split_sizes; copy them to
+ *              the host for grouped_mlp_fwd).
+ *   workspace  at least mx_moe_dispatch_workspace_bytes, 4-byte aligned.
+ * The result is deterministic: no global atomics. With tokens == 0 only
+ * counts (set to 0) and workspace are used; the other pointers may be NULL.
+ * Errors: MX_EINVAL, MX_ESHAPE, MX_EALIGN (x, x_perm 16-byte), MX_EWORKSPACE,
+ * MX_EUNSUPPORTED (num_experts > MX_MAX_GROUPS, tokens * topk >= 2^31).
+ *
+ * mx_moe_combine -- y[t] = sum over the token's slots j with perm[t, j] >= 0
+ * of y_perm[perm[t, j]]. The sum is fp32 in slot order, rounded once to bf16
+ * (nearest even). The routing weights were applied inside the MLP, so the sum
+ * is unweighted. perm must come from mx_moe_dispatch with the same tokens and
+ * topk, and y_perm must hold at least that call's routed rows.
+ *   y_perm bf16 [>= sum(counts), hidden]; y bf16 [tokens, hidden].
+ */
+MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
+MX_API mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                 int64_t tokens, int64_t hidden, int32_t topk, int32_t num_experts,
+                                 void* x_perm, float* probs_perm, int32_t* perm, int32_t* row_token,
+                                 int64_t* counts, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+MX_API mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens,
+                                int64_t hidden, int32_t topk, void* y, void* stream);
+
+/*
  * mx_set_stage_events -- optional per-stage timing of the fused MLP calls
  * (observability only; the results are the same). While events are set, the
  * fused MLP calls run every stage on the caller's stream in order, without

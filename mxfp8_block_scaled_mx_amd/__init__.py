@@ -96,6 +96,12 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_bwd_cached.restype = ctypes.c_int
     L.grouped_mlp_bwd_cached.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp,
                                          i32, vp, sz, vp]
+    L.mx_moe_dispatch_workspace_bytes.restype = sz
+    L.mx_moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
+    L.mx_moe_dispatch.restype = ctypes.c_int
+    L.mx_moe_dispatch.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.mx_moe_combine.restype = ctypes.c_int
+    L.mx_moe_combine.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -325,6 +331,38 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
                                     _ptr(dw1), _ptr(dw2), int(accumulate), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
     return dx, dprobs, dw1, dw2
+
+
+def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None):
+    """Token dispatch (mx_moe_dispatch): x bf16 [T, H], topk_idx int32 [T, k],
+    topk_w fp32 [T, k] or None. Returns (x_perm bf16 [T*k, H], probs_perm fp32
+    [T*k] or None, perm int32 [T, k], row_token int32 [T*k], counts int64 [E]);
+    the first counts.sum() routed rows are valid."""
+    L = load()
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev)
+    probs_perm = torch.empty((T * k,), dtype=torch.float32, device=dev) if topk_w is not None else None
+    perm = torch.empty((T, k), dtype=torch.int32, device=dev)
+    row_token = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    counts = torch.empty((num_experts,), dtype=torch.int64, device=dev)
+    ws = _byte_buffer(L.mx_moe_dispatch_workspace_bytes(T, k, num_experts), dev)
+    _check(L.mx_moe_dispatch(_ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, num_experts, _ptr(x_perm),
+                             _ptr(probs_perm), _ptr(perm), _ptr(row_token), _ptr(counts), _ptr(ws), ws.numel(),
+                             _stream(stream)))
+    return x_perm, probs_perm, perm, row_token, counts
+
+
+def mx_moe_combine(y_perm, perm, out=None, stream=None):
+    """Token combine (mx_moe_combine): y [T, H] bf16, the fp32 sum of each
+    token's routed rows, rounded once to bf16."""
+    L = load()
+    T, k = perm.shape
+    H = y_perm.shape[1]
+    y = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device) if out is None else out
+    _check(L.mx_moe_combine(_ptr(y_perm), _ptr(perm), T, H, k, _ptr(y), _stream(stream)))
+    return y
 
 
 _event_arrays = []   # keeps the handle arrays alive while the library holds them

@@ -835,4 +835,58 @@ mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* split_s
                   reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts) {
+  if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > mx::kMaxGroups) return 0;
+  const int64_t nblk = cdiv(tokens * topk, mx::kMoeBlock);
+  return (size_t)((nblk * num_experts + 1) * 4);
+}
+
+mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* topk_w, int64_t tokens,
+                          int64_t hidden, int32_t topk, int32_t num_experts, void* x_perm, float* probs_perm,
+                          int32_t* perm, int32_t* row_token, int64_t* counts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_moe_dispatch";
+  if (tokens < 0 || hidden <= 0 || hidden % 8) return fail(MX_ESHAPE, "%s: need tokens >= 0 and hidden a positive multiple of 8", who);
+  if (topk < 1 || topk > 64) return fail(MX_EINVAL, "%s: topk %d outside [1, 64]", who, topk);
+  if (num_experts < 1 || num_experts > mx::kMaxGroups)
+    return fail(MX_EUNSUPPORTED, "%s: %d experts outside [1, %d]", who, num_experts, mx::kMaxGroups);
+  if (tokens * topk > kI32Max || tokens * hidden > ((int64_t)1 << 40))
+    return fail(MX_EUNSUPPORTED, "%s: too many routed rows", who);
+  if (!counts || !workspace || (tokens > 0 && (!x || !topk_idx || !x_perm || !perm || !row_token)))
+    return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if ((topk_w == nullptr) != (probs_perm == nullptr))
+    return fail(MX_EINVAL, "%s: topk_w and probs_perm must both be given or both be null", who);
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_idx, 4) || !aligned(perm, 4) ||
+      !aligned(row_token, 4) || !aligned(counts, 8) || !aligned(workspace, 4) || (topk_w && !aligned(topk_w, 4)) ||
+      (probs_perm && !aligned(probs_perm, 4)))
+    return fail(MX_EALIGN, "%s: x and x_perm must be 16-byte aligned, the index arrays 4-byte", who);
+  const size_t need = mx_moe_dispatch_workspace_bytes(tokens, topk, num_experts);
+  if (workspace_bytes < need)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, need);
+  mx::MoeDispatchArgs a;
+  a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w;
+  a.tokens = tokens; a.hidden = hidden; a.topk = topk; a.experts = num_experts;
+  a.x_perm = x_perm; a.probs_perm = probs_perm; a.perm = perm; a.row_token = row_token; a.counts = counts;
+  a.workspace = reinterpret_cast<int32_t*>(workspace);
+  hipError_t e = mx::launch_moe_dispatch(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_moe_dispatch launch");
+  return MX_OK;
+}
+
+mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens, int64_t hidden, int32_t topk,
+                         void* y, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_moe_combine";
+  if (tokens < 0 || hidden <= 0 || hidden % 8) return fail(MX_ESHAPE, "%s: need tokens >= 0 and hidden a positive multiple of 8", who);
+  if (topk < 1 || topk > 64) return fail(MX_EINVAL, "%s: topk %d outside [1, 64]", who, topk);
+  if (tokens * topk > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many routed rows", who);
+  if (tokens > 0 && (!y_perm || !perm || !y)) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(y_perm, 16) || !aligned(y, 16) || !aligned(perm, 4))
+    return fail(MX_EALIGN, "%s: y_perm and y must be 16-byte aligned, perm 4-byte", who);
+  hipError_t e = mx::launch_moe_combine(y_perm, perm, tokens, hidden, topk, y, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_moe_combine launch");
+  return MX_OK;
+}
+
 }  // extern "C"

@@ -134,6 +134,25 @@ constexpr int kMaxSplitParts = 4;
 hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts,
                                 hipStream_t stream);
 
+// Token dispatch / combine around the grouped MLP (mx_moe.hip).
+constexpr int kMoeBlock = 256;      // entries per workgroup in the counting passes
+struct MoeDispatchArgs {
+  const void* x;                    // bf16 [tokens, hidden]
+  const int32_t* topk_idx;          // [tokens, topk]
+  const float* topk_w;              // [tokens, topk] or null
+  int64_t tokens, hidden;
+  int32_t topk, experts;
+  void* x_perm;                     // bf16 [tokens * topk, hidden]
+  float* probs_perm;                // [tokens * topk] or null
+  int32_t* perm;                    // [tokens, topk]
+  int32_t* row_token;               // [tokens * topk]
+  int64_t* counts;                  // [experts]
+  int32_t* workspace;               // ceil(tokens * topk / kMoeBlock) * experts + 1 int32
+};
+hipError_t launch_moe_dispatch(const MoeDispatchArgs& args, hipStream_t stream);
+hipError_t launch_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens, int64_t hidden, int32_t topk,
+                              void* y, hipStream_t stream);
+
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 constexpr int kTileK = 128;

@@ -162,3 +162,23 @@ def test_library_defines_every_kernel_stub(L):
     import subprocess
     out = subprocess.run(["nm", "-C", "--undefined-only", mx.lib_path()], capture_output=True, text=True).stdout
     assert "device_stub" not in out, [l for l in out.splitlines() if "device_stub" in l][:5]
+
+
+def test_moe_dispatch_combine_argument_errors(L):
+    assert L.mx_moe_dispatch_workspace_bytes(100, 2, 8) == ((200 + 255) // 256 * 8 + 1) * 4
+    assert L.mx_moe_dispatch_workspace_bytes(100, 2, 0) == 0
+    ws = ctypes.c_void_p(0x100000)
+
+    def d(x=FAKE, idx=FAKE, w=None, T=100, H=64, k=2, E=8, xp=FAKE, pp=None, wsb=1 << 20):
+        return L.mx_moe_dispatch(x, idx, w, T, H, k, E, xp, pp, FAKE, FAKE, FAKE, ws, wsb, None)
+
+    assert d(H=60) == ESHAPE
+    assert d(k=0) == EINVAL
+    assert d(E=129) == EUNSUPPORTED
+    assert d(x=None) == EINVAL
+    assert d(w=FAKE) == EINVAL                       # weights without probs_perm
+    assert d(x=ctypes.c_void_p(0x100008)) == EALIGN
+    assert d(wsb=16) == EWORKSPACE
+    assert L.mx_moe_combine(FAKE, FAKE, 10, 60, 2, FAKE, None) == ESHAPE
+    assert L.mx_moe_combine(None, FAKE, 10, 64, 2, FAKE, None) == EINVAL
+    assert L.mx_moe_combine(FAKE, FAKE, 10, 64, 2, ctypes.c_void_p(0x100004), None) == EALIGN
