@@ -301,6 +301,24 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
  *   y_perm bf16 [>= sum(counts), hidden]; y bf16 [tokens, hidden].
  */
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
+
+/*
+ * grouped_mlp_fwd_gather -- grouped_mlp_fwd with the token gather fused into
+ * the cast of X: routed row r is row row_token[r] of x_tokens (bf16
+ * [tokens, hidden]), read by the MXFP8 quantize itself, so the routed bf16
+ * copy of X is never written. row_token is device int32 [rows], as
+ * mx_moe_dispatch returns it, and split_sizes are that call's counts. An
+ * index outside [0, tokens) reads as a zero row. Everything else, including
+ * buffer sizes, `saved` for grouped_mlp_bwd, results and errors, is as for
+ * grouped_mlp_fwd, with x = x_tokens[row_token]. The backward's dX is per
+ * routed row; mx_moe_combine sums it back per token.
+ */
+MX_API mx_status grouped_mlp_fwd_gather(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                        const void* x_tokens, int64_t tokens,
+                                        const int32_t* row_token, const float* probs,
+                                        const void* w1, const void* w2, void* y, void* saved,
+                                        size_t saved_bytes, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 MX_API mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* topk_w,
                                  int64_t tokens, int64_t hidden, int32_t topk, int32_t num_experts,
                                  void* x_perm, float* probs_perm, int32_t* perm, int32_t* row_token,

@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
     L.mx_moe_dispatch.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mx_moe_combine.restype = ctypes.c_int
     L.mx_moe_combine.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.grouped_mlp_fwd_gather.restype = ctypes.c_int
+    L.grouped_mlp_fwd_gather.argtypes = [ctypes.POINTER(_Dims), p64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -227,6 +229,29 @@ def grouped_mlp_fwd(x, probs, w1, w2, split_sizes, *, training: bool = True, wor
                              _ptr(probs), _ptr(w1), _ptr(w2), _ptr(y), _ptr(saved),
                              0 if saved is None else saved.numel(), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
+    state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
+    return y, state
+
+
+def grouped_mlp_fwd_gather(x_tokens, row_token, probs, w1, w2, split_sizes, *, training: bool = True,
+                           workspace=None, out=None, stream=None):
+    """grouped_mlp_fwd on the routed rows x_tokens[row_token] (row_token as
+    mx_moe_dispatch returns it; split_sizes its counts), gathered by the X
+    cast itself. Returns (y [R,H] bf16, MLPState or None)."""
+    L = load()
+    T, H = x_tokens.shape
+    E, F2, _ = w1.shape
+    F = F2 // 2
+    R = int(sum(int(m) for m in split_sizes))
+    fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
+    if workspace is None or workspace.numel() < fws:
+        workspace = _byte_buffer(fws, x_tokens.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x_tokens.device) if out is None else out
+    saved = _byte_buffer(sv, x_tokens.device) if training else None
+    _check(L.grouped_mlp_fwd_gather(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes), _ptr(x_tokens), T,
+                                    _ptr(row_token), _ptr(probs), _ptr(w1), _ptr(w2), _ptr(y), _ptr(saved),
+                                    0 if saved is None else saved.numel(), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
     state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
     return y, state
 

@@ -112,7 +112,8 @@ mx_status check_groups(const int64_t* sizes, int32_t n, int64_t rows, const char
 // internal buffers; needs cols % 128 == 0 for the rowwise copy).
 mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
                         int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
-                        hipStream_t stream, bool tiled = false) {
+                        hipStream_t stream, bool tiled = false, const int32_t* row_index = nullptr,
+                        int64_t index_rows = 0) {
   const char* who = "mx_quantize";
   if (x == nullptr) return fail(MX_EINVAL, "%s: x is null", who);
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return fail(MX_EINVAL, "%s: unsupported dtype %d", who, x_dtype);
@@ -160,6 +161,8 @@ mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t co
     a.nq_col = (int32_t)q0[n];
     a.rows = (int32_t)rows;
   }
+  a.row_index = row_index;
+  a.index_rows = (int32_t)index_rows;
   if (p0 > kI32Max) return fail(MX_EUNSUPPORTED, "%s: padded rows exceed 2^31-1", who);
   a.ld_col = p0;
   a.n_col_tiles = (int32_t)cdiv(cols, mx::quant_tile_cols(x_dtype));
@@ -524,7 +527,8 @@ namespace {
 // are cast from w1/w2 into the workspace (rowwise) and saved (columnwise)
 // copies; otherwise the cached copies are used and w1/w2 are not read.
 mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const void* w1, const void* w2,
-                   const WeightCopies* wc_cached, void* y, void* saved, void* workspace, hipStream_t stream) {
+                   const WeightCopies* wc_cached, void* y, void* saved, void* workspace, hipStream_t stream,
+                   const int32_t* row_token = nullptr, int64_t tokens = 0) {
   const int64_t R = L.R, H = L.H, F = L.F;
   const int E = L.E;
   const WeightCopies wc = wc_cached ? *wc_cached
@@ -556,8 +560,11 @@ mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const 
   a1.R = (int32_t)R;
 
   stage_mark(0, stream);
+  // (with row_token: routed row r is token row row_token[r] of x, gathered
+  // by the cast itself)
   st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
-                     saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true);
+                     saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true,
+                     row_token, tokens);
   if (st != MX_OK) return st;
   // (running the W2 cast on the side stream beside GEMM1 was measured: it
   // slows GEMM1 by more than the cast takes, so the forward stays serial)
@@ -623,6 +630,25 @@ mx_status grouped_mlp_fwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument", who);
   if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
   return fwd_impl(L, x, probs, w1, w2, nullptr, y, saved, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_fwd_gather(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x_tokens,
+                                 int64_t tokens, const int32_t* row_token, const float* probs, const void* w1,
+                                 const void* w2, void* y, void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd_gather";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = fwd_checks(L, x_tokens, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  if (!w1 || !w2 || (L.R > 0 && !row_token)) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (tokens < 0 || tokens > kI32Max) return fail(MX_ESHAPE, "%s: bad token count %lld", who, (long long)tokens);
+  if (!aligned(w1, 16) || !aligned(w2, 16) || !aligned(row_token, 4))
+    return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte and row_token 4-byte aligned", who);
+  return fwd_impl(L, x_tokens, probs, w1, w2, nullptr, y, saved, workspace, reinterpret_cast<hipStream_t>(stream),
+                  row_token, tokens);
 }
 
 mx_status grouped_mlp_weight_cache_bytes(const mx_mlp_dims* dims, size_t* bytes) {

@@ -52,6 +52,10 @@ struct QuantArgs {
   int32_t nq_row;                   // k-tiled rowwise scales: cols / 128
   int32_t nq_col;                   // k-tiled columnwise scales: steps over all groups
   int32_t rows;                     // total rows (k-tiled rowwise: pad rows up to a multiple of 32 get 0)
+  // optional gather: row r of the (routed) input is row row_index[r] of x,
+  // which has index_rows rows; an index outside [0, index_rows) reads zeros
+  const int32_t* row_index;
+  int32_t index_rows;
   QuantGroups groups;
 };
 

@@ -100,8 +100,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
     for (int p = 0; p < TR / 16; ++p) {
       const int r = p * 16 + (tid >> 4);
       raw[p] = make_uint4(0, 0, 0, 0);
-      if ((L.tile_r0 + r) < L.m_g && col < cols)
-        raw[p] = *reinterpret_cast<const uint4*>(x + (L.grow0 + L.tile_r0 + r) * cols + col);
+      if ((L.tile_r0 + r) < L.m_g && col < cols) {
+        int64_t src = L.grow0 + L.tile_r0 + r;
+        if (args.row_index != nullptr) {
+          src = args.row_index[src];
+          if (src < 0 || src >= args.index_rows) continue;
+        }
+        raw[p] = *reinterpret_cast<const uint4*>(x + src * cols + col);
+      }
     }
   };
   auto process = [&](const Loc& L, const uint4 (&raw)[TR / 16]) __attribute__((always_inline)) {

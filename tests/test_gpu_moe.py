@@ -66,3 +66,40 @@ def test_dispatch_and_combine_full_size(gpu_lib):
     y = gpu_lib.mx_moe_combine(_dev_bits(c["y_perm"]), perm)
     torch.cuda.synchronize()
     assert np.array_equal(to_np(y), orc.moe_combine(c["y_perm"], want["perm"]))
+
+
+@pytest.mark.parametrize("T,E,H,F", [(300, 4, 256, 384), (2048, 8, 512, 256)])
+def test_mlp_forward_with_fused_gather_equals_dispatch_then_forward(gpu_lib, T, E, H, F):
+    """grouped_mlp_fwd_gather (the X cast reads token rows through row_token)
+    is bit-identical to mx_moe_dispatch followed by grouped_mlp_fwd on the
+    routed copy, forward and backward (saved state), with one expert empty
+    and a few dropped entries; and the combine of the forward output matches
+    the oracle's combine of the same routed output."""
+    mx = gpu_lib
+    rng = np.random.default_rng(70 + T)
+    x = wl.normal_bf16(rng, (T, H), 1.0)
+    logits = rng.standard_normal((T, E))
+    logits[:, 1] = -50.0                                   # expert 1 gets no tokens
+    idx, w = wl.top2_picks(logits, np.zeros(E))
+    idx[5, 1] = -1
+    w1 = wl.normal_bf16(rng, (E, 2 * F, H), 0.02)
+    w2 = wl.normal_bf16(rng, (E, H, F), 0.02)
+    xt, w1t, w2t = _dev_bits(x), _dev_bits(w1), _dev_bits(w2)
+    x_perm, probs, perm, row_token, counts = mx.mx_moe_dispatch(xt, torch.from_numpy(idx).cuda(),
+                                                                torch.from_numpy(w).cuda(), E)
+    split = counts.cpu().tolist()
+    R = sum(split)
+    assert split[1] == 0 and R == 2 * T - 1
+    y_ref, st_ref = mx.grouped_mlp_fwd(x_perm[:R].contiguous(), probs[:R].contiguous(), w1t, w2t, split)
+    y, st = mx.grouped_mlp_fwd_gather(xt, row_token[:R].contiguous(), probs[:R].contiguous(), w1t, w2t, split)
+    dy = _dev_bits(wl.normal_bf16(rng, (R, H), 1e-3))
+    ref = mx.grouped_mlp_bwd(dy, probs[:R].contiguous(), st_ref)
+    got = mx.grouped_mlp_bwd(dy, probs[:R].contiguous(), st)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    out = mx.mx_moe_combine(y, perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), orc.moe_combine(_bits(y), perm.cpu().numpy()))
