@@ -273,8 +273,10 @@ def main():
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
-        log(f"dispatch {out['dispatch_combine']['dispatch_gbps']:.0f} GB/s, "
-            f"combine {out['dispatch_combine']['combine_gbps']:.0f} GB/s")
+        dc = out["dispatch_combine"]
+        log(f"dispatch {dc['dispatch_gbps']:.0f} GB/s (routing only {dc['routing_only_ms'] * 1e3:.0f} us), "
+            f"combine {dc['combine_gbps']:.0f} GB/s; MoE block fwd {dc['moe_block_fwd']['ms']:.3f} ms "
+            f"-> {dc['moe_block_fwd']['tflops']:.0f} TFLOP/s")
 
     # free device memory before the forward-only workloads and the CPU leg
     del runner, dw1, dw2, x, w1, w2, dy
@@ -316,7 +318,7 @@ def measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step
     log(f"qinit-style step {q_ms:.3f} ms -> {out['qinit_style']['tflops']:.1f} TFLOP/s")
 
 
-def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096):
+def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096, ffn=14336):
     """Token dispatch and combine for 8192 tokens, top-2 of 8 experts, hidden
     4096 (the Mixtral-shaped forward workload's routing shape). Algorithmic
     bytes: dispatch reads x once and writes the 2T routed rows; combine reads
@@ -344,14 +346,43 @@ def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096):
         return e0.elapsed_time(e1) / iters
 
     d_ms = timed(lambda: mx.mx_moe_dispatch(x, idx, w, E))
+    r_ms = timed(lambda: mx.mx_moe_dispatch(x, idx, w, E, gather=False))
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     c_ms = timed(lambda: mx.mx_moe_combine(y_perm, perm, out=y))
     d_bytes = (T + 2 * T) * H * 2
     c_bytes = (2 * T + T) * H * 2
-    return {"tokens": T, "topk": 2, "experts": E, "hidden": H,
-            "dispatch_ms": round(d_ms, 4), "dispatch_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
-            "combine_ms": round(c_ms, 4), "combine_gbps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
-            "note": "dispatch time includes the binding's output allocation per call (torch caching allocator)"}
+    out = {"tokens": T, "topk": 2, "experts": E, "hidden": H,
+           "dispatch_ms": round(d_ms, 4), "dispatch_gbps": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+           "routing_only_ms": round(r_ms, 4),
+           "combine_ms": round(c_ms, 4), "combine_gbps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
+           "note": "dispatch time includes the binding's output allocation per call (torch caching allocator)"}
+    # the whole MoE MLP block forward (inference) on these tokens: routing-only
+    # dispatch, the fused forward gathering X through row_token, combine;
+    # weights are seeded N(0, 0.02) draws made on the device
+    F = ffn
+    g = torch.Generator(device=dev)
+    g.manual_seed(61)
+    w1 = (torch.randn((E, 2 * F, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((E, H, F), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    _, probs, perm, row_token, counts = mx.mx_moe_dispatch(x, idx, w, E, gather=False)
+    split = counts.cpu().tolist()
+    R = sum(split)
+    runner_ws = mx._byte_buffer(mx.mlp_sizes(E, R, H, F, split)[0], dev)
+    y_r = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+
+    def block():
+        _, p_, pm, rt, _ = mx.mx_moe_dispatch(x, idx, w, E, gather=False)
+        mx.grouped_mlp_fwd_gather(x, rt, p_, w1, w2, split, training=False, workspace=runner_ws, out=y_r)
+        mx.mx_moe_combine(y_r, pm, out=y)
+
+    b_ms = timed(block)
+    out["moe_block_fwd"] = {"ms": round(b_ms, 4), "rows": R, "ffn": F,
+                            "tflops": round(6.0 * R * H * F / (b_ms * 1e-3) / 1e12, 1),
+                            "step": "mx_moe_dispatch (routing only) + grouped_mlp_fwd_gather (inference, "
+                                    "weights cast in the call) + mx_moe_combine; split_sizes taken from "
+                                    "the routing before the timed region"}
+    del w1, w2, runner_ws
+    return out
 
 
 def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup):

@@ -281,7 +281,9 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
  *   topk_w     f32 [tokens, topk] routing weights, or NULL (then probs_perm
  *              must be NULL too).
  *   x_perm     bf16 [tokens * topk, hidden]: routed row r holds the row of its
- *              token. Only the first sum(counts) rows are written.
+ *              token. Only the first sum(counts) rows are written. x and
+ *              x_perm may both be NULL: routing only, no row copy (for
+ *              grouped_mlp_fwd_gather, which reads the token rows itself).
  *   probs_perm f32 [tokens * topk]: routing weight of each routed row.
  *   perm       int32 [tokens, topk]: routed row of entry (t, j), or -1.
  *   row_token  int32 [tokens * topk]: token of each routed row.

@@ -358,22 +358,24 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
     return dx, dprobs, dw1, dw2
 
 
-def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None):
+def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None, gather: bool = True):
     """Token dispatch (mx_moe_dispatch): x bf16 [T, H], topk_idx int32 [T, k],
-    topk_w fp32 [T, k] or None. Returns (x_perm bf16 [T*k, H], probs_perm fp32
-    [T*k] or None, perm int32 [T, k], row_token int32 [T*k], counts int64 [E]);
-    the first counts.sum() routed rows are valid."""
+    topk_w fp32 [T, k] or None. Returns (x_perm bf16 [T*k, H] or None,
+    probs_perm fp32 [T*k] or None, perm int32 [T, k], row_token int32 [T*k],
+    counts int64 [E]); the first counts.sum() routed rows are valid.
+    gather=False: routing only (no row copy; x_perm is None)."""
     L = load()
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
-    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev)
+    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None
     probs_perm = torch.empty((T * k,), dtype=torch.float32, device=dev) if topk_w is not None else None
     perm = torch.empty((T, k), dtype=torch.int32, device=dev)
     row_token = torch.empty((T * k,), dtype=torch.int32, device=dev)
     counts = torch.empty((num_experts,), dtype=torch.int64, device=dev)
     ws = _byte_buffer(L.mx_moe_dispatch_workspace_bytes(T, k, num_experts), dev)
-    _check(L.mx_moe_dispatch(_ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, num_experts, _ptr(x_perm),
+    _check(L.mx_moe_dispatch(_ptr(x) if gather else None, _ptr(topk_idx), _ptr(topk_w), T, H, k, num_experts,
+                             _ptr(x_perm),
                              _ptr(probs_perm), _ptr(perm), _ptr(row_token), _ptr(counts), _ptr(ws), ws.numel(),
                              _stream(stream)))
     return x_perm, probs_perm, perm, row_token, counts

@@ -879,8 +879,10 @@ mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* t
     return fail(MX_EUNSUPPORTED, "%s: %d experts outside [1, %d]", who, num_experts, mx::kMaxGroups);
   if (tokens * topk > kI32Max || tokens * hidden > ((int64_t)1 << 40))
     return fail(MX_EUNSUPPORTED, "%s: too many routed rows", who);
-  if (!counts || !workspace || (tokens > 0 && (!x || !topk_idx || !x_perm || !perm || !row_token)))
+  if (!counts || !workspace || (tokens > 0 && (!topk_idx || !perm || !row_token)))
     return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MX_EINVAL, "%s: x and x_perm must both be given or both be null (routing only)", who);
   if ((topk_w == nullptr) != (probs_perm == nullptr))
     return fail(MX_EINVAL, "%s: topk_w and probs_perm must both be given or both be null", who);
   if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_idx, 4) || !aligned(perm, 4) ||

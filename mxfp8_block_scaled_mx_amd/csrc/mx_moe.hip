@@ -12,7 +12,8 @@
 //      (block, expert) and writes the per-expert counts and the total;
 //   3. each entry's routed row = its (block, expert) base + its rank among the
 //      block's earlier entries of the same expert;
-//   4. the token rows are copied to their routed rows, 16 bytes per lane.
+//   4. the token rows are copied to their routed rows, 16 bytes per lane
+//      (skipped in routing-only mode, where the MLP's X cast gathers).
 // Entries whose expert lies outside [0, E) are dropped (perm -1).
 // Combine: y[t] = sum over slots of the routed output rows of token t, in
 // fp32 in slot order, rounded once to bf16.
@@ -134,6 +135,7 @@ hipError_t launch_moe_dispatch(const MoeDispatchArgs& a, hipStream_t stream) {
   if (nblk == 0) return hipGetLastError();
   hipLaunchKernelGGL(moe_place_kernel, dim3(nblk), dim3(256), 0, stream, a.topk_idx, a.topk_w, n, a.topk,
                      a.experts, a.workspace, a.perm, a.row_token, a.probs_perm);
+  if (a.x_perm == nullptr) return hipGetLastError();     // routing only
   hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)n), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(a.x), a.row_token, a.workspace + (int64_t)nblk * a.experts,
                      row_vec, reinterpret_cast<uint4*>(a.x_perm));

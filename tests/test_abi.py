@@ -175,7 +175,8 @@ def test_moe_dispatch_combine_argument_errors(L):
     assert d(H=60) == ESHAPE
     assert d(k=0) == EINVAL
     assert d(E=129) == EUNSUPPORTED
-    assert d(x=None) == EINVAL
+    assert d(x=None) == EINVAL                       # x without x_perm
+    assert d(xp=None) == EINVAL
     assert d(w=FAKE) == EINVAL                       # weights without probs_perm
     assert d(x=ctypes.c_void_p(0x100008)) == EALIGN
     assert d(wsb=16) == EWORKSPACE

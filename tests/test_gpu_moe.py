@@ -35,6 +35,16 @@ def _check_dispatch(mx, x_bits, idx, w, E):
     assert np.array_equal(_bits(x_perm)[:R], want["x_perm"])
     if w is not None:
         assert np.array_equal(probs.cpu().numpy()[:R], want["probs_perm"])
+    # routing only (no row copy): the same routing outputs
+    none, probs2, perm2, row_token2, counts2 = mx.mx_moe_dispatch(
+        _dev_bits(x_bits), torch.from_numpy(idx).cuda(),
+        None if w is None else torch.from_numpy(w).cuda(), E, gather=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(perm2, perm) and torch.equal(counts2, counts)
+    assert torch.equal(row_token2[:R], row_token[:R])
+    if w is not None:
+        assert torch.equal(probs2[:R], probs[:R])
     return perm, want
 
 
