@@ -784,24 +784,35 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
                      at(workspace, L.dycq), at(workspace, L.dycs), stream, true);
   if (st != MX_OK) return st;
+  // once work is on the side stream, an error return still joins it first,
+  // so nothing enqueued by this call runs unordered with the caller's stream
+  auto fail_joined = [&](mx_status s) {
+    if (sd != nullptr) {
+      char keep[sizeof(g_err)];
+      memcpy(keep, g_err, sizeof(g_err));
+      (void)wait_for(stream, sd->s, sd->ev[2]);
+      memcpy(g_err, keep, sizeof(g_err));
+    }
+    return s;
+  };
   if (sd != nullptr) {
     st = wait_for(sd->s, stream, sd->ev[0]);
     if (st == MX_OK) st = run_gemm(pw2, MX_GROUP_K, mx::EPI_F32, sd->s, "grouped_mlp_bwd wgrad2");
-    if (st != MX_OK) return st;
+    if (st != MX_OK) return fail_joined(st);
   }
   stage_mark(1, stream);
   st = run_gemm(pd2, MX_GROUP_M, mx::EPI_SWIGLU_BWD, stream, "grouped_mlp_bwd dgrad2");
-  if (st != MX_OK) return st;
+  if (st != MX_OK) return fail_joined(st);
   stage_mark(2, stream);
   if (dprobs) {
     hipError_t e = mx::launch_dprobs_reduce(reinterpret_cast<const float*>(at(workspace, L.part)), dprobs,
                                             (int32_t)R, (int32_t)L.n_tiles_f, stream);
-    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dprobs");
+    if (e != hipSuccess) return fail_joined(hip_fail(e, "grouped_mlp_bwd dprobs"));
   }
   if (sd != nullptr) {
     st = wait_for(sd->s, stream, sd->ev[1]);
     if (st == MX_OK) st = run_gemm(pw1, MX_GROUP_K, mx::EPI_F32, sd->s, "grouped_mlp_bwd wgrad1");
-    if (st != MX_OK) return st;
+    if (st != MX_OK) return fail_joined(st);
   }
   stage_mark(3, stream);
   if (sd == nullptr) {
@@ -812,9 +823,9 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   {
     const int tail = plan_split_tail(pd1, 2 * F, reinterpret_cast<float*>(at(workspace, L.split1)), L.split1_bytes);
     st = run_gemm(pd1, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_bwd dgrad1");
-    if (st != MX_OK) return st;
+    if (st != MX_OK) return fail_joined(st);
     hipError_t e = mx::launch_split_reduce(mx::EPI_BF16, pd1.args, tail, stream);
-    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd dgrad1 split reduce");
+    if (e != hipSuccess) return fail_joined(hip_fail(e, "grouped_mlp_bwd dgrad1 split reduce"));
   }
   stage_mark(5, stream);
   if (sd != nullptr) return wait_for(stream, sd->s, sd->ev[2]);
