@@ -11,10 +11,14 @@ fwd+bwd (4096 tokens, top-2 of 8 experts = 8192 routed rows, hidden 4096,
 ffn 14336). Inputs are resident in HBM before the timed region; no host
 transfer or allocation happens inside it.
 
-Prints ONE JSON line: metric/value (GEMM FLOP of the step per second),
-per-stage times from HIP events recorded on the launch stream, the roofline
-of the dominant kernel, the standalone quantize GB/s (16384 x 4096 bf16,
-both layouts) and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line: metric/value (GEMM FLOP of the step per second, the
+backward's wgrad GEMMs overlapping dgrad on the library's side stream),
+per-stage times from a second pass with HIP events recorded on the launch
+stream (stages in order), the roofline of the dominant kernel, the step on
+weights cast once into the weight cache (qinit-style), the standalone
+quantize GB/s (16384 x 4096 bf16, both layouts), token dispatch / combine and
+the MoE block forward (8192 tokens, top-2 of 8), the forward-only Llama-3.1-8B
+dense and Mixtral-shaped MLPs, and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -137,7 +141,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md but not run.", file=sys.stderr)
+              "sharding over several GPUs (expert parallelism) is designed but not run here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
