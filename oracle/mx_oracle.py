@@ -48,6 +48,13 @@ R12 token dispatch: the routed rows are the (token, slot) entries of the
     top-k choices, ordered by expert, then token (the per-expert groups that
     GroupedLinear takes, item 1); counts per expert are the split_sizes; an
     entry whose expert lies outside [0, E) is dropped (its perm is -1).
+R14 MXFP4 (the other block-scaled MX format the pages name, run on MI355X):
+    E2M1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN) with one
+    E8M0 scale per 32 consecutive values; e = floor(log2 amax) - 2 (2 =
+    exponent of E2M1's largest value), clamped to [-127, 127]; element =
+    nearest E2M1 value of v / 2^e, ties to the even code, saturating at 6,
+    sign kept (-0 -> 0x8); two codes per byte, element 2i in the low nibble.
 R13 token combine: y[t] = sum over slots j of the routed output row of
     (t, j), slots with perm -1 skipped, summed in float64 and rounded once to
     bf16. The routing weight is already applied inside the MLP (R8), so the
@@ -66,7 +73,8 @@ __all__ = [
     "scale_exponent", "e4m3_encode", "quantize_blocks", "quantize_rowwise",
     "dequantize_rowwise", "padded_sizes", "quantize_colwise", "gemm_group_m",
     "gemm_group_k", "round_to_bf16", "sigmoid", "silu", "mlp_forward",
-    "moe_dispatch", "moe_combine",
+    "moe_dispatch", "moe_combine", "e2m1_value", "e2m1_encode", "quantize_rowwise_fp4",
+    "dequantize_rowwise_fp4",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
     "mlp_backward_wgrad_entries",
 ]
@@ -578,3 +586,64 @@ def moe_combine(y_perm_bits, perm):
             if perm[t, j] >= 0:
                 out[t] += y[perm[t, j]]
     return round_to_bf16(out)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (R14): E2M1 elements with one E8M0 scale per 32 values
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """E2M1 code (4 bits) -> value: exponent field 0 is subnormal (m * 0.5),
+    otherwise (1 + m/2) * 2^(field - 1); bit 3 is the sign."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    ef = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(ef == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2((ef - 1).astype(np.float64)))
+    return np.where((c >> 3) == 1, -mag, mag)
+
+
+def e2m1_encode(t) -> np.ndarray:
+    """Nearest E2M1 value of t (already divided by the block scale), ties to
+    the even code, saturating at 6; the sign bit follows t (R14). Written as
+    the definition: distance to each of the 8 magnitudes, smallest wins, an
+    equal distance goes to the even code."""
+    t = np.asarray(t, dtype=np.float64)
+    a = np.abs(t)[..., None]
+    d = np.abs(a - E2M1_VALUES)
+    best = np.argmin(d, axis=-1)                        # first (lower) code on a tie
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    nxt = np.minimum(best + 1, 7)
+    tie = (np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0] == dmin) & (nxt != best)
+    code = np.where(tie & (best % 2 == 1), nxt, best)
+    return (code | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+
+
+def quantize_rowwise_fp4(x):
+    """Rowwise MXFP4 of [rows, cols] (cols % 32 == 0) -> (packed codes
+    [rows, cols/2] uint8, scales [rows, cols/32] uint8)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the quantizer's contract")
+    v = x.reshape(rows, cols // BLOCK, BLOCK)
+    amax = np.max(np.abs(v), axis=-1)
+    _, ex = np.frexp(amax)
+    e = np.where(amax == 0.0, -127, (ex.astype(np.int64) - 1) - 2)
+    e = np.clip(e, -127, 127)
+    codes = e2m1_encode(np.ldexp(v, (-e)[..., None])).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + E8M0_BIAS).astype(np.uint8)
+
+
+def dequantize_rowwise_fp4(q, s):
+    """value = E2M1(code) * 2^(scale code - 127); low nibble = even element."""
+    q = np.asarray(q, dtype=np.uint8)
+    codes = np.empty((q.shape[0], q.shape[1] * 2), dtype=np.uint8)
+    codes[:, 0::2] = q & 0xF
+    codes[:, 1::2] = q >> 4
+    scale = np.repeat(e8m0_value(s), BLOCK, axis=1)
+    return e2m1_value(codes) * scale
