@@ -273,7 +273,7 @@ def main():
 
     if not args.no_quantize:
         out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
-        log(f"quantize {out['quantize']['gbps']:.0f} GB/s")
+        log(f"quantize {out['quantize']['gbps']:.0f} GB/s; rowwise MXFP4 {out['quantize']['fp4_rowwise']['gbps']:.0f} GB/s")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -479,12 +479,32 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
         evs[b + 1].record()
     torch.cuda.synchronize()
     times = [evs[b].elapsed_time(evs[b + 1]) / iters for b in range(batches)]
+    # rowwise MXFP4 of the same tensor: 2 bytes read, 0.5 + 1/32 written per element
+    q4 = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s4 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+
+    def call4(t):
+        mx._check(L.mx_quantize_fp4(mx._ptr(t), rows, cols, mx._ptr(q4), mx._ptr(s4), stream))
+
+    for i in range(8):
+        call4(xs[i % copies])
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(iters):
+        call4(xs[i % copies])
+    evs[1].record()
+    torch.cuda.synchronize()
+    ms4 = evs[0].elapsed_time(evs[1]) / iters
+    algo4 = rows * cols * 2 + rows * cols // 2 + rows * cols // 32
+    fp4 = {"layouts": "rowwise MXFP4 (E2M1 + E8M0)", "bytes": algo4, "ms": round(ms4, 4),
+           "gbps": round(algo4 / (ms4 * 1e-3) / 1e9, 1), "frac_hbm_peak": round(algo4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     algo = rows * cols * 2 + 2 * (rows * cols + rows * cols // 32)
     med = float(np.median(times))
     gbps = algo / (med * 1e-3) / 1e9
     return {"workload": "quantize_16384x4096", "layouts": "rowwise+columnwise", "bytes": algo,
             "median_ms": round(med, 4), "min_ms": round(float(np.min(times)), 4),
             "timing": f"median over {batches} batches of the mean of {iters} back-to-back launches",
+            "fp4_rowwise": fp4,
             "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(gbps / PEAK_HBM_GBPS, 4)}}

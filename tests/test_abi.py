@@ -183,3 +183,10 @@ def test_moe_dispatch_combine_argument_errors(L):
     assert L.mx_moe_combine(FAKE, FAKE, 10, 60, 2, FAKE, None) == ESHAPE
     assert L.mx_moe_combine(None, FAKE, 10, 64, 2, FAKE, None) == EINVAL
     assert L.mx_moe_combine(FAKE, FAKE, 10, 64, 2, ctypes.c_void_p(0x100004), None) == EALIGN
+
+
+def test_quantize_fp4_argument_errors(L):
+    assert L.mx_quantize_fp4(FAKE, 4, 48, FAKE, FAKE, None) == ESHAPE
+    assert L.mx_quantize_fp4(FAKE, -1, 64, FAKE, FAKE, None) == ESHAPE
+    assert L.mx_quantize_fp4(None, 4, 64, FAKE, FAKE, None) == EINVAL
+    assert L.mx_quantize_fp4(FAKE, 4, 64, ctypes.c_void_p(0x100008), FAKE, None) == EALIGN
