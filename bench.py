@@ -273,7 +273,9 @@ def main():
 
     if not args.no_quantize:
         out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
-        log(f"quantize {out['quantize']['gbps']:.0f} GB/s; rowwise MXFP4 {out['quantize']['fp4_rowwise']['gbps']:.0f} GB/s")
+        f4 = out["quantize"]["fp4_rowwise"]
+        log(f"quantize {out['quantize']['gbps']:.0f} GB/s; MXFP4 rowwise {f4['gbps']:.0f} GB/s, "
+            f"both layouts {f4['both_layouts_gbps']:.0f} GB/s")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -484,7 +486,7 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
     s4 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
 
     def call4(t):
-        mx._check(L.mx_quantize_fp4(mx._ptr(t), rows, cols, mx._ptr(q4), mx._ptr(s4), stream))
+        mx._check(L.mx_quantize_fp4(mx._ptr(t), rows, cols, mx._ptr(q4), mx._ptr(s4), None, None, stream))
 
     for i in range(8):
         call4(xs[i % copies])
@@ -498,6 +500,23 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
     algo4 = rows * cols * 2 + rows * cols // 2 + rows * cols // 32
     fp4 = {"layouts": "rowwise MXFP4 (E2M1 + E8M0)", "bytes": algo4, "ms": round(ms4, 4),
            "gbps": round(algo4 / (ms4 * 1e-3) / 1e9, 1), "frac_hbm_peak": round(algo4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    # both layouts (two kernels, each reading x)
+    q4c = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+    s4c = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    for i in range(8):
+        mx._check(L.mx_quantize_fp4(mx._ptr(xs[i % copies]), rows, cols, mx._ptr(q4), mx._ptr(s4), mx._ptr(q4c),
+                                    mx._ptr(s4c), stream))
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(iters):
+        mx._check(L.mx_quantize_fp4(mx._ptr(xs[i % copies]), rows, cols, mx._ptr(q4), mx._ptr(s4), mx._ptr(q4c),
+                                    mx._ptr(s4c), stream))
+    evs[1].record()
+    torch.cuda.synchronize()
+    ms4b = evs[0].elapsed_time(evs[1]) / iters
+    algo4b = rows * cols * 2 + 2 * (rows * cols // 2 + rows * cols // 32)
+    fp4["both_layouts_ms"] = round(ms4b, 4)
+    fp4["both_layouts_gbps"] = round(algo4b / (ms4b * 1e-3) / 1e9, 1)
     algo = rows * cols * 2 + 2 * (rows * cols + rows * cols // 32)
     med = float(np.median(times))
     gbps = algo / (med * 1e-3) / 1e9

@@ -303,7 +303,7 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
  *   y_perm bf16 [>= sum(counts), hidden]; y bf16 [tokens, hidden].
  */
 /*
- * mx_quantize_fp4 -- rowwise MXFP4 cast of a bf16 [rows, cols] tensor. MX
+ * mx_quantize_fp4 -- MXFP4 cast of a bf16 [rows, cols] tensor. MX
  * block scaling at 4 bits, the format of the MI355X mxfp4 runs on the ROCm
  * Megatron page ("examples/llama: default-on fusion & DP-comm perf toggles"),
  * following the OCP MX rules as for MXFP8. Each 32-value block along a row
@@ -311,14 +311,18 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
  * [-127, 127]. Each element becomes the nearest E2M1 value (0, 0.5, 1, 1.5,
  * 2, 3, 4, 6 and negatives) of v / 2^e, ties to the even code, saturating at
  * 6, with the sign of v kept.
- *   q  uint8 [rows, cols/2]: two codes per byte, element 2i in the low nibble.
- *   s  uint8 [rows, cols/32]: scale codes, row-major.
- * Requires cols % 32 == 0; x and q 16-byte aligned. Non-finite inputs are
- * outside the contract. Errors: MX_EINVAL, MX_ESHAPE, MX_EALIGN,
- * MX_EUNSUPPORTED.
+ *   q      uint8 [rows, cols/2]: rowwise codes, two per byte, element 2i in
+ *          the low nibble.
+ *   s      uint8 [rows, cols/32]: rowwise scale codes, row-major.
+ *   q_col  uint8 [cols, rows/2]: columnwise codes (rowwise of the transpose).
+ *   s_col  uint8 [cols, rows/32]: columnwise scale codes.
+ * Either pair may be NULL (not both). Requires cols % 32 == 0, and
+ * rows % 32 == 0 for the columnwise pair; x, q, q_col 16-byte aligned.
+ * Non-finite inputs are outside the contract. Errors: MX_EINVAL, MX_ESHAPE,
+ * MX_EALIGN, MX_EUNSUPPORTED.
  */
 MX_API mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
-                                 void* stream);
+                                 uint8_t* q_col, uint8_t* s_col, void* stream);
 
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
 

@@ -105,7 +105,7 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_fwd_gather.restype = ctypes.c_int
     L.grouped_mlp_fwd_gather.argtypes = [ctypes.POINTER(_Dims), p64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.mx_quantize_fp4.restype = ctypes.c_int
-    L.mx_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.mx_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -360,15 +360,18 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
     return dx, dprobs, dw1, dw2
 
 
-def mx_quantize_fp4(x: torch.Tensor, stream=None):
-    """Rowwise MXFP4 of bf16 x [rows, cols]: (codes uint8 [rows, cols/2], two
-    per byte, element 2i in the low nibble; scales uint8 [rows, cols/32])."""
+def mx_quantize_fp4(x: torch.Tensor, colwise: bool = False, stream=None):
+    """MXFP4 of bf16 x [rows, cols]: (q [rows, cols/2], s [rows, cols/32]) rowwise
+    (two codes per byte, element 2i in the low nibble), plus (q_col [cols,
+    rows/2], s_col [cols, rows/32]) when colwise."""
     L = load()
     rows, cols = x.shape
     q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
-    _check(L.mx_quantize_fp4(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(stream)))
-    return q, s
+    qc = torch.empty((cols, rows // 2), dtype=torch.uint8, device=x.device) if colwise else None
+    sc = torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device) if colwise else None
+    _check(L.mx_quantize_fp4(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(qc), _ptr(sc), _stream(stream)))
+    return (q, s, qc, sc) if colwise else (q, s)
 
 
 def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None, gather: bool = True):

@@ -928,14 +928,20 @@ mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens
   return MX_OK;
 }
 
-mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, void* stream) {
+mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                          uint8_t* s_col, void* stream) {
   g_err[0] = 0;
   const char* who = "mx_quantize_fp4";
   if (rows < 0 || cols <= 0 || cols % 32) return fail(MX_ESHAPE, "%s: need rows >= 0 and cols a positive multiple of 32", who);
+  if (q_col != nullptr && rows % 32) return fail(MX_ESHAPE, "%s: the columnwise copy needs rows % 32 == 0", who);
   if (rows * (cols / 32) > kI32Max * (int64_t)256) return fail(MX_EUNSUPPORTED, "%s: tensor too large", who);
-  if (rows > 0 && (!x || !q || !s)) return fail(MX_EINVAL, "%s: null pointer argument", who);
-  if (!aligned(x, 16) || !aligned(q, 16)) return fail(MX_EALIGN, "%s: x and q must be 16-byte aligned", who);
-  hipError_t e = mx::launch_quantize_fp4(x, rows, cols, q, s, reinterpret_cast<hipStream_t>(stream));
+  if ((q == nullptr) != (s == nullptr) || (q_col == nullptr) != (s_col == nullptr))
+    return fail(MX_EINVAL, "%s: codes and scales of a layout must both be given or both be null", who);
+  if (q == nullptr && q_col == nullptr) return fail(MX_EINVAL, "%s: no output requested", who);
+  if (rows > 0 && !x) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(q_col, 16))
+    return fail(MX_EALIGN, "%s: x, q and q_col must be 16-byte aligned", who);
+  hipError_t e = mx::launch_quantize_fp4(x, rows, cols, q, s, q_col, s_col, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mx_quantize_fp4 launch");
   return MX_OK;
 }

@@ -6,10 +6,11 @@
 // the even code, saturating at 6; two codes per byte, element 2i in the low
 // nibble.
 //
-// One thread per 32-value block: four 16-byte loads, a local amax, the scale
-// code from the amax exponent bits, the elements scaled by 2^-e (exact) and
-// rounded by comparing against the midpoints of the E2M1 grid, 16 bytes of
-// codes stored at once. HBM-bound.
+// Rowwise: one thread per 32-value block: four 16-byte loads, a local amax,
+// the scale code from the amax exponent bits, the elements scaled by 2^-e
+// (exact) and rounded by comparing against the midpoints of the E2M1 grid, 16
+// bytes of codes stored at once. Columnwise: see the columnwise kernel.
+// HBM-bound.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -62,12 +63,70 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
   s[r * nb + b] = (uint8_t)sc;
 }
 
-hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
-                               hipStream_t stream) {
-  const int64_t blocks = rows * (cols / 32);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_fp4_rowwise_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(x), rows, cols, q, s);
+// Columnwise MXFP4 (= rowwise of the transpose): codes [cols, rows/2] and
+// scales [cols, rows/32]; rows % 32 == 0. A workgroup stages a 128-row x
+// 64-column tile in LDS (rows loaded as coalesced 16-byte pieces); thread t
+// then takes column t % 64 and the 32-row block t / 64, reduces the block's
+// amax locally and stores its 16 code bytes as one piece of the column's run.
+constexpr int kFp4ColTileRows = 128, kFp4ColTileCols = 64;
+__global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+                                                                   uint8_t* q, uint8_t* s) {
+  // [row][column] bf16 with a 2-element pad so that the column reads of a
+  // wave (64 columns of one row) spread over the banks
+  __shared__ uint16_t tile[kFp4ColTileRows][kFp4ColTileCols + 2];
+  const int64_t n_ct = (cols + kFp4ColTileCols - 1) / kFp4ColTileCols;
+  const int64_t r0 = (int64_t)(blockIdx.x / n_ct) * kFp4ColTileRows;
+  const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * kFp4ColTileCols;
+  const int tid = threadIdx.x;
+  // 128 rows x 8 pieces of 16 bytes (8 columns each): 4 pieces per thread
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int p = it * 256 + tid, rr = p >> 3, cp = (p & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + rr < rows && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
+    const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
+  }
+  __syncthreads();
+  const int c = tid % kFp4ColTileCols, rb = tid / kFp4ColTileCols;
+  const int64_t col = c0 + c, row = r0 + 32 * rb;
+  if (col >= cols || row >= rows) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[32 * rb + i][c] << 16);
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
+  const uint32_t eb = am >> 23;
+  const uint32_t sc = eb > 2u ? eb - 2u : 0u;
+  const float inv = inv_scale_from_code(sc);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
+    w[i] = word;
+  }
+  *reinterpret_cast<uint4*>(q + col * (rows / 2) + row / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  s[col * (rows / 32) + row / 32] = (uint8_t)sc;
+}
+
+hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                               uint8_t* s_col, hipStream_t stream) {
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  const int64_t blocks = q != nullptr ? rows * (cols / 32) : 0;
+  if (blocks > 0)
+    hipLaunchKernelGGL(quantize_fp4_rowwise_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream,
+                       xb, rows, cols, q, s);
+  if (q_col != nullptr && rows > 0) {
+    const int64_t tiles = ((rows + kFp4ColTileRows - 1) / kFp4ColTileRows) *
+                          ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
+    hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows, cols,
+                       q_col, s_col);
+  }
   return hipGetLastError();
 }
 

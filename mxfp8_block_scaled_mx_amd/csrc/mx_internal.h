@@ -158,8 +158,8 @@ hipError_t launch_moe_combine(const void* y_perm, const int32_t* perm, int64_t t
                               void* y, hipStream_t stream);
 
 // Rowwise MXFP4 cast (mx_fp4.hip).
-hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
-                               hipStream_t stream);
+hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                               uint8_t* s_col, hipStream_t stream);
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;

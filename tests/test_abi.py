@@ -186,7 +186,10 @@ def test_moe_dispatch_combine_argument_errors(L):
 
 
 def test_quantize_fp4_argument_errors(L):
-    assert L.mx_quantize_fp4(FAKE, 4, 48, FAKE, FAKE, None) == ESHAPE
-    assert L.mx_quantize_fp4(FAKE, -1, 64, FAKE, FAKE, None) == ESHAPE
-    assert L.mx_quantize_fp4(None, 4, 64, FAKE, FAKE, None) == EINVAL
-    assert L.mx_quantize_fp4(FAKE, 4, 64, ctypes.c_void_p(0x100008), FAKE, None) == EALIGN
+    assert L.mx_quantize_fp4(FAKE, 4, 48, FAKE, FAKE, None, None, None) == ESHAPE
+    assert L.mx_quantize_fp4(FAKE, -1, 64, FAKE, FAKE, None, None, None) == ESHAPE
+    assert L.mx_quantize_fp4(FAKE, 40, 64, None, None, FAKE, FAKE, None) == ESHAPE   # rows % 32
+    assert L.mx_quantize_fp4(None, 4, 64, FAKE, FAKE, None, None, None) == EINVAL
+    assert L.mx_quantize_fp4(FAKE, 4, 64, None, None, None, None, None) == EINVAL   # nothing requested
+    assert L.mx_quantize_fp4(FAKE, 4, 64, FAKE, None, None, None, None) == EINVAL   # half a pair
+    assert L.mx_quantize_fp4(FAKE, 4, 64, ctypes.c_void_p(0x100008), FAKE, None, None, None) == EALIGN

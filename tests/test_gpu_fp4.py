@@ -60,3 +60,32 @@ def test_fp4_full_size_sampled(gpu_lib):
     rows = np.random.default_rng(1).choice(bits.shape[0], size=256, replace=False)
     wq, ws = orc.quantize_rowwise_fp4(orc.bf16_bits_to_f64(bits[rows]))
     assert np.array_equal(s[rows], ws) and np.array_equal(q[rows], wq)
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 32), (96, 160), (384, 4096)])
+def test_fp4_colwise_is_rowwise_of_transpose(gpu_lib, rows, cols):
+    """The columnwise copy equals the oracle's rowwise MXFP4 of x transposed,
+    with ragged column tiles and zero blocks; the rowwise pair of the same
+    call is unchanged."""
+    rng = np.random.default_rng(95 + rows)
+    x = rng.standard_t(3, size=(rows, cols)) * np.exp2(rng.integers(-10, 10, size=(1, cols)))
+    x[:32, rng.random(cols) < 0.2] = 0.0
+    xb = wl.bf16_bits_from_f32(x.astype(np.float32))
+    q, s, qc, sc = gpu_lib.mx_quantize_fp4(dev_bf16(xb), colwise=True)
+    torch.cuda.synchronize()
+    xf = orc.bf16_bits_to_f64(xb)
+    wq, ws = orc.quantize_rowwise_fp4(xf)
+    wqc, wsc = orc.quantize_rowwise_fp4(xf.T)
+    assert np.array_equal(q.cpu().numpy(), wq) and np.array_equal(s.cpu().numpy(), ws)
+    assert np.array_equal(sc.cpu().numpy(), wsc)
+    assert np.array_equal(qc.cpu().numpy(), wqc)
+
+
+def test_fp4_colwise_full_size_sampled(gpu_lib):
+    bits = wl.quantize_tensor_c2()
+    _, _, qc, sc = gpu_lib.mx_quantize_fp4(dev_bf16(bits), colwise=True)
+    torch.cuda.synchronize()
+    cols = np.random.default_rng(2).choice(bits.shape[1], size=128, replace=False)
+    wqc, wsc = orc.quantize_rowwise_fp4(orc.bf16_bits_to_f64(bits[:, cols]).T)
+    assert np.array_equal(sc.cpu().numpy()[cols], wsc)
+    assert np.array_equal(qc.cpu().numpy()[cols], wqc)
