@@ -282,7 +282,8 @@ def main():
         dc = out["dispatch_combine"]
         log(f"dispatch {dc['dispatch_gbps']:.0f} GB/s (routing only {dc['routing_only_ms'] * 1e3:.0f} us), "
             f"combine {dc['combine_gbps']:.0f} GB/s; MoE block fwd {dc['moe_block_fwd']['ms']:.3f} ms "
-            f"-> {dc['moe_block_fwd']['tflops']:.0f} TFLOP/s")
+            f"-> {dc['moe_block_fwd']['tflops']:.0f} TFLOP/s; MoE layer train step "
+            f"{dc['moe_layer_train_step']['ms']:.3f} ms -> {dc['moe_layer_train_step']['tflops']:.0f} TFLOP/s")
 
     # free device memory before the forward-only workloads and the CPU leg
     del runner, dw1, dw2, x, w1, w2, dy
@@ -387,7 +388,30 @@ def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096, ffn=14
                             "step": "mx_moe_dispatch (routing only) + grouped_mlp_fwd_gather (inference, "
                                     "weights cast in the call) + mx_moe_combine; split_sizes taken from "
                                     "the routing before the timed region"}
-    del w1, w2, runner_ws
+    # the MoE layer training step (no router): routing-only dispatch, the
+    # fused forward (training), combine, the fused backward with dY gathered
+    # from the tokens' output gradient, combine of dX; fp32 main grads
+    dy_tok = (torch.randn((T, H), generator=g, device=dev) * 1e-3).to(torch.bfloat16)
+    dw1 = torch.zeros((E, 2 * F, H), dtype=torch.float32, device=dev)
+    dw2 = torch.zeros((E, H, F), dtype=torch.float32, device=dev)
+    _, _, bws = mx.mlp_sizes(E, R, H, F, split)
+    bwd_ws = mx._byte_buffer(bws, dev)
+    dx_t = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def layer_step():
+        _, p_, pm, rt, _ = mx.mx_moe_dispatch(x, idx, w, E, gather=False)
+        yr, st = mx.grouped_mlp_fwd_gather(x, rt, p_, w1, w2, split, training=True, workspace=runner_ws, out=y_r)
+        mx.mx_moe_combine(yr, pm, out=y)
+        dxr, _, _, _ = mx.grouped_mlp_bwd_gather(dy_tok, rt, p_, st, dw1=dw1, dw2=dw2, accumulate=True,
+                                                 workspace=bwd_ws)
+        mx.mx_moe_combine(dxr, pm, out=dx_t)
+
+    t_ms = timed(layer_step)
+    out["moe_layer_train_step"] = {"ms": round(t_ms, 4), "rows": R,
+                                   "tflops": round(18.0 * R * H * F / (t_ms * 1e-3) / 1e12, 1),
+                                   "step": "routing-only dispatch + grouped_mlp_fwd_gather (training) + combine + "
+                                           "grouped_mlp_bwd_gather (fp32 wgrad accumulate) + combine of dX"}
+    del w1, w2, runner_ws, dw1, dw2, bwd_ws
     return out
 
 

@@ -327,6 +327,14 @@ MX_API mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
 
 /*
+ * grouped_mlp_bwd_gather -- grouped_mlp_bwd with dY read the same way: routed
+ * row r of dY is row row_token[r] of dy_tokens (bf16 [tokens, hidden]), the
+ * gradient of the combine (each token's output is the sum of its routed
+ * rows, so every routed row receives its token's output gradient). dx is
+ * per routed row ([rows, hidden]); mx_moe_combine sums it per token (the
+ * gradient of the dispatch). Same buffers, results and errors as
+ * grouped_mlp_bwd with dy = dy_tokens[row_token].
+ *
  * grouped_mlp_fwd_gather -- grouped_mlp_fwd with the token gather fused into
  * the cast of X: routed row r is row row_token[r] of x_tokens (bf16
  * [tokens, hidden]), read by the MXFP8 quantize itself, so the routed bf16
@@ -337,6 +345,13 @@ MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int3
  * grouped_mlp_fwd, with x = x_tokens[row_token]. The backward's dX is per
  * routed row; mx_moe_combine sums it back per token.
  */
+MX_API mx_status grouped_mlp_bwd_gather(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                        const void* dy_tokens, int64_t tokens,
+                                        const int32_t* row_token, const float* probs,
+                                        const void* saved, size_t saved_bytes, void* dx,
+                                        float* dprobs, float* dw1, float* dw2,
+                                        int32_t accumulate_wgrad, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 MX_API mx_status grouped_mlp_fwd_gather(const mx_mlp_dims* dims, const int64_t* split_sizes,
                                         const void* x_tokens, int64_t tokens,
                                         const int32_t* row_token, const float* probs,

@@ -102,6 +102,9 @@ def load() -> ctypes.CDLL:
     L.mx_moe_dispatch.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mx_moe_combine.restype = ctypes.c_int
     L.mx_moe_combine.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.grouped_mlp_bwd_gather.restype = ctypes.c_int
+    L.grouped_mlp_bwd_gather.argtypes = [ctypes.POINTER(_Dims), p64, vp, i64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
+                                         vp, sz, vp]
     L.grouped_mlp_fwd_gather.restype = ctypes.c_int
     L.grouped_mlp_fwd_gather.argtypes = [ctypes.POINTER(_Dims), p64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.mx_quantize_fp4.restype = ctypes.c_int
@@ -256,6 +259,31 @@ def grouped_mlp_fwd_gather(x_tokens, row_token, probs, w1, w2, split_sizes, *, t
                                     _stream(stream)))
     state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
     return y, state
+
+
+def grouped_mlp_bwd_gather(dy_tokens, row_token, probs, state: MLPState, *, dw1=None, dw2=None,
+                           accumulate: bool = False, want_dprobs: bool = True, workspace=None, stream=None):
+    """grouped_mlp_bwd with dY gathered from dy_tokens [T, H] through row_token
+    by its cast. Returns (dx [R, H] bf16 per routed row, dprobs, dw1, dw2)."""
+    L = load()
+    E, R, H, F = state.dims
+    T = dy_tokens.shape[0]
+    _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
+    if workspace is None or workspace.numel() < bws:
+        workspace = _byte_buffer(bws, dy_tokens.device)
+    dev = dy_tokens.device
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dprobs = torch.empty((R,), dtype=torch.float32, device=dev) if want_dprobs else None
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, H), dtype=torch.float32, device=dev)
+        accumulate = False if dw2 is None else accumulate
+    if dw2 is None:
+        dw2 = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    _check(L.grouped_mlp_bwd_gather(ctypes.byref(_dims(E, R, H, F)), _i64_array(state.split_sizes), _ptr(dy_tokens),
+                                    T, _ptr(row_token), _ptr(probs), _ptr(state.saved), state.saved.numel(),
+                                    _ptr(dx), _ptr(dprobs), _ptr(dw1), _ptr(dw2), int(accumulate), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+    return dx, dprobs, dw1, dw2
 
 
 def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulate: bool = False,

@@ -726,7 +726,8 @@ mx_status bwd_checks(const MlpLayout& L, const void* dy, const float* probs, con
 // come from saved (w1c/w2c null) or from a weight cache.
 mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const void* saved,
                    const WeightCopies* wc_cached, void* dx, float* dprobs, float* dw1, float* dw2,
-                   int32_t accumulate_wgrad, void* workspace, hipStream_t stream) {
+                   int32_t accumulate_wgrad, void* workspace, hipStream_t stream,
+                   const int32_t* row_token = nullptr, int64_t tokens = 0) {
   const int64_t R = L.R, H = L.H, F = L.F, P = L.sumP;
   const int E = L.E;
   const uint8_t* w1cq = wc_cached ? wc_cached->w1cq : at(saved, L.w1cq);
@@ -781,8 +782,9 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
     if (st != MX_OK) return st;
   }
   stage_mark(0, stream);
+  // (with row_token: routed row r of dY is token row row_token[r] of dy)
   st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
-                     at(workspace, L.dycq), at(workspace, L.dycs), stream, true);
+                     at(workspace, L.dycq), at(workspace, L.dycs), stream, true, row_token, tokens);
   if (st != MX_OK) return st;
   // once work is on the side stream, an error return still joins it first,
   // so nothing enqueued by this call runs unordered with the caller's stream
@@ -851,6 +853,24 @@ mx_status grouped_mlp_bwd(const mx_mlp_dims* dims, const int64_t* split_sizes, c
   if (st != MX_OK) return st;
   return bwd_impl(L, dy, probs, saved, nullptr, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
                   reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_bwd_gather(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy_tokens,
+                                 int64_t tokens, const int32_t* row_token, const float* probs, const void* saved,
+                                 size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                                 int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd_gather";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = bwd_checks(L, dy_tokens, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  if (L.R > 0 && !row_token) return fail(MX_EINVAL, "%s: row_token is null", who);
+  if (tokens < 0 || tokens > kI32Max) return fail(MX_ESHAPE, "%s: bad token count %lld", who, (long long)tokens);
+  if (!aligned(row_token, 4)) return fail(MX_EALIGN, "%s: row_token must be 4-byte aligned", who);
+  return bwd_impl(L, dy_tokens, probs, saved, nullptr, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
+                  reinterpret_cast<hipStream_t>(stream), row_token, tokens);
 }
 
 mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy,

@@ -113,3 +113,13 @@ def test_mlp_forward_with_fused_gather_equals_dispatch_then_forward(gpu_lib, T, 
     out = mx.mx_moe_combine(y, perm)
     torch.cuda.synchronize()
     assert np.array_equal(to_np(out), orc.moe_combine(_bits(y), perm.cpu().numpy()))
+    # backward with dY gathered from the tokens' output gradient by the dY cast
+    # (the gradient of the combine) equals the backward on the gathered copy
+    dy_tok = _dev_bits(wl.normal_bf16(rng, (T, H), 1e-3))
+    dy_perm = dy_tok[row_token[:R].long()].contiguous()
+    ref = mx.grouped_mlp_bwd(dy_perm, probs[:R].contiguous(), st)
+    got = mx.grouped_mlp_bwd_gather(dy_tok, row_token[:R].contiguous(), probs[:R].contiguous(), st)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
