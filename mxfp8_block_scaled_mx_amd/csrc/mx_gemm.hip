@@ -57,7 +57,7 @@ static_assert(sizeof(GemmArgs) <= 4096, "kernel arguments must fit the 4 KB kern
 constexpr int kWavesN = 2;
 constexpr int kWaves = 2 * kWavesN;
 constexpr int kThreads = 64 * kWaves;
-constexpr int NS = 8 / kWavesN;             // n sub-tiles of 32 per wave
+[[maybe_unused]] constexpr int NS = 8 / kWavesN;   // n sub-tiles of 32 per wave
 [[maybe_unused]] constexpr int kWaveN = 256 / kWavesN;      // n columns per wave
 [[maybe_unused]] constexpr int kDmaPerWave = 32 / kWaves;    // 1 KB blocks of A (and of B) per wave per k-step
 // m-tiles per band of the raster: 8 for group-M (fprop, dgrad); 4 for
