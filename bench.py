@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MXFP8 grouped-MLP TFLOP/s (fwd+bwd) and % of MXFP8 MFMA peak; quantize GB/s"
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+NOMINAL_SCLK_MHZ = 2400.0         # the clock the MFMA peak is quoted at
 GEMM_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_gemm.hip")
 QUANT_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_quantize.hip")
 
@@ -265,6 +266,17 @@ def main():
         "roofline": roofline,
     }
 
+    clk = measure_clock(step, torch)
+    if clk.get("sclk_mhz"):
+        scale = NOMINAL_SCLK_MHZ / clk["sclk_mhz"]
+        out["clock"] = dict(clk, gemm_only_frac_mfma_peak_at_clock=round(out["gemm_only"]["frac_mfma_peak"] * scale, 4))
+        for k, v in out["stages"].items():
+            if v["bound"] == "mfma":
+                v["frac_at_measured_clock"] = round(v["frac"] * scale, 4)
+        log(f"sclk {clk['sclk_mhz']:.0f} MHz under the step loop")
+    else:
+        out["clock"] = clk
+
     # qinit-style variant: the weights are cast into the MXFP8 weight cache
     # once, outside the timed region (as after an optimizer update), and the
     # step runs grouped_mlp_fwd_cached + grouped_mlp_bwd_cached
@@ -301,6 +313,42 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, wl)
         log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
+
+
+def measure_clock(step, torch, seconds=2.0, samples=3):
+    """Shader clock while the step runs: `rocm-smi --showclocks --json` sampled
+    from a helper thread during about `seconds` of untimed steps. The MXFP8
+    peak (5.0 PFLOP/s) is quoted at 2.4 GHz; the fractions at the measured
+    clock rescale by 2.4 GHz / sclk."""
+    import re
+    import subprocess
+    import threading
+    vals = []
+
+    def sample():
+        time.sleep(seconds / (samples + 1))
+        for _ in range(samples):
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', r.stdout)
+                if m:
+                    vals.append(int(m.group(1)))
+            except Exception:
+                pass
+            time.sleep(seconds / (samples + 1))
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < 4 * seconds:
+        step()
+        torch.cuda.synchronize()
+    th.join()
+    if not vals:
+        return {"sclk_mhz": None, "source": "rocm-smi --showclocks (not available)"}
+    return {"sclk_mhz": round(sum(vals) / len(vals), 1), "samples_mhz": vals, "nominal_mhz": NOMINAL_SCLK_MHZ,
+            "source": "rocm-smi --showclocks during untimed steps"}
 
 
 def measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step_flops, out, torch):
