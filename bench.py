@@ -135,6 +135,7 @@ def main():
     ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--no-qinit", action="store_true", help="skip the cached-weight (qinit-style) step")
     ap.add_argument("--no-moe", action="store_true", help="skip token dispatch / combine")
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward-only Llama dense and Mixtral-shaped workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -266,7 +267,7 @@ def main():
         "roofline": roofline,
     }
 
-    clk = measure_clock(step, torch)
+    clk = measure_clock(step, torch) if not args.no_clock else {"sclk_mhz": None, "source": "not sampled"}
     if clk.get("sclk_mhz"):
         scale = NOMINAL_SCLK_MHZ / clk["sclk_mhz"]
         out["clock"] = dict(clk, gemm_only_frac_mfma_peak_at_clock=round(out["gemm_only"]["frac_mfma_peak"] * scale, 4))
