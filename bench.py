@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP8 grouped-MLP TFLOP/s (fwd+bwd) and % of MXFP8 MFMA peak; quantize GB/s"
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 / MXFP8 MFMA
+PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 / MXFP4 MFMA
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 NOMINAL_SCLK_MHZ = 2400.0         # the clock the MFMA peak is quoted at
 GEMM_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_gemm.hip")
@@ -136,6 +137,7 @@ def main():
     ap.add_argument("--no-qinit", action="store_true", help="skip the cached-weight (qinit-style) step")
     ap.add_argument("--no-moe", action="store_true", help="skip token dispatch / combine")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock")
+    ap.add_argument("--no-gemm-fp4", action="store_true", help="skip the MXFP4 GEMM")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward-only Llama dense and Mixtral-shaped workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,6 +291,12 @@ def main():
         f4 = out["quantize"]["fp4_rowwise"]
         log(f"quantize {out['quantize']['gbps']:.0f} GB/s; MXFP4 rowwise {f4['gbps']:.0f} GB/s, "
             f"both layouts {f4['both_layouts_gbps']:.0f} GB/s")
+
+    if not args.no_gemm_fp4:
+        out["gemm_fp4"] = measure_gemm_fp4(mx, torch, dev)
+        g4 = out["gemm_fp4"]
+        log(f"MXFP4 GEMM {g4['workload']}: {g4['ms']:.3f} ms -> {g4['tflops']:.0f} TFLOP/s "
+            f"({g4['roofline']['frac']:.3f} of the FP4 peak)")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -518,6 +526,33 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}}),
           flush=True)
+
+
+def measure_gemm_fp4(mx, torch, dev, iters=10, m=16384, n=28672, k=4096):
+    """mx_gemm_fp4 (C = A . B^T, bf16 out) on random MXFP4 operands of the
+    Mixtral MLP's first GEMM taken as one group: 16384 rows, 28672 columns,
+    k = 4096. 2 m n k flops per call, priced at the FP4 MFMA peak."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    aq = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    bq = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    as_ = torch.randint(122, 133, (m, k // 32), dtype=torch.uint8, device=dev, generator=g)
+    bs = torch.randint(122, 133, (n, k // 32), dtype=torch.uint8, device=dev, generator=g)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        mx.mx_gemm_fp4(aq, as_, bq, bs, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        mx.mx_gemm_fp4(aq, as_, bq, bs, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    return {"workload": f"gemm_fp4_{m}x{n}x{k}", "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP4_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}}
 
 
 def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):

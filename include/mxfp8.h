@@ -324,6 +324,23 @@ MX_API mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* 
 MX_API mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
                                  uint8_t* q_col, uint8_t* s_col, void* stream);
 
+/*
+ * mx_gemm_fp4 -- C[m, n] = A[m, k] . B[n, k]^T on MXFP4 operands, the GEMM of
+ * the 4-bit MX runs (same page as mx_quantize_fp4), on the scaled MFMA with
+ * E2M1 operands: element value = E2M1(code) * 2^(scale code - 127), products
+ * summed in fp32.
+ *   a, a_s  uint8 [m, k/2] codes and uint8 [m, k/32] scales (the rowwise
+ *           layout of mx_quantize_fp4: element 2i in the low nibble);
+ *   b, b_s  the same for B [n, k];
+ *   c       [m, n] row-major, bf16 (rounded to nearest even) or fp32 per
+ *           c_dtype; written, never read.
+ * Caller-owned device memory; nothing is allocated. Requires k a positive
+ * multiple of 64 (at most 2^26); a, b, c 16-byte aligned. m or n zero is a
+ * no-op. Errors: MX_EINVAL, MX_ESHAPE, MX_EALIGN, MX_EUNSUPPORTED, MX_EHIP.
+ */
+MX_API mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s, int64_t m,
+                             int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream);
+
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
 
 /*

@@ -22,7 +22,7 @@ __all__ = [
     "load", "lib_path", "MXError", "MX_BF16", "MX_F32", "MX_GROUP_M", "MX_GROUP_K",
     "MAX_GROUPS", "padded_sizes", "quantize", "grouped_gemm", "mlp_sizes",
     "grouped_mlp_fwd", "grouped_mlp_bwd", "GroupedMLP", "MLPState", "MLPRunner",
-    "set_stage_events", "FWD_STAGES", "BWD_STAGES",
+    "set_stage_events", "FWD_STAGES", "BWD_STAGES", "mx_quantize_fp4", "mx_gemm_fp4",
 ]
 
 FWD_STAGES = ("quantize_x", "quantize_w1", "quantize_w2", "gemm1_swiglu", "gemm2")
@@ -109,6 +109,8 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_fwd_gather.argtypes = [ctypes.POINTER(_Dims), p64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.mx_quantize_fp4.restype = ctypes.c_int
     L.mx_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.mx_gemm_fp4.restype = ctypes.c_int
+    L.mx_gemm_fp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -400,6 +402,27 @@ def mx_quantize_fp4(x: torch.Tensor, colwise: bool = False, stream=None):
     sc = torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device) if colwise else None
     _check(L.mx_quantize_fp4(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(qc), _ptr(sc), _stream(stream)))
     return (q, s, qc, sc) if colwise else (q, s)
+
+
+def mx_gemm_fp4(a_q, a_s, b_q, b_s, out_dtype=torch.bfloat16, out=None, stream=None):
+    """C [m, n] = A . B^T on rowwise MXFP4 operands (a_q [m, k/2], a_s [m, k/32],
+    b_q [n, k/2], b_s [n, k/32]: the layout of mx_quantize_fp4), bf16 or fp32."""
+    L = load()
+    m, n, k = a_q.shape[0], b_q.shape[0], a_q.shape[1] * 2
+    for t in (a_q, a_s, b_q, b_s):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError("mx_gemm_fp4: codes and scales must be contiguous 2-D uint8 tensors")
+    if b_q.shape[1] != a_q.shape[1] or tuple(a_s.shape) != (m, k // 32) or tuple(b_s.shape) != (n, k // 32):
+        raise ValueError(f"mx_gemm_fp4: operand shapes {tuple(a_q.shape)}, {tuple(a_s.shape)}, "
+                         f"{tuple(b_q.shape)}, {tuple(b_s.shape)} do not describe A [m, k] and B [n, k]")
+    if out is not None and (tuple(out.shape) != (m, n) or not out.is_contiguous()
+                            or out.dtype not in (torch.bfloat16, torch.float32)):
+        raise ValueError("mx_gemm_fp4: out must be a contiguous bf16 or fp32 [m, n] tensor")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    dt = MX_F32 if out.dtype == torch.float32 else MX_BF16
+    _check(L.mx_gemm_fp4(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), m, n, k, _ptr(out), dt, _stream(stream)))
+    return out
 
 
 def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None, gather: bool = True):

@@ -966,4 +966,23 @@ mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q,
   return MX_OK;
 }
 
+mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s, int64_t m, int64_t n,
+                      int64_t k, void* c, mx_dtype c_dtype, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_gemm_fp4";
+  if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
+  if (m < 0 || n < 0 || k <= 0 || k % 64) return fail(MX_ESHAPE, "%s: need m, n >= 0 and k a positive multiple of 64", who);
+  if (k > ((int64_t)1 << 26)) return fail(MX_EUNSUPPORTED, "%s: k above 2^26", who);
+  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+  if (tiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many output tiles", who);
+  if (m == 0 || n == 0) return MX_OK;
+  if (!a || !a_s || !b || !b_s || !c) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
+    return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
+  hipError_t e = mx::launch_gemm_fp4(a, a_s, b, b_s, m, n, k, c, c_dtype == MX_F32 ? 1 : 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_gemm_fp4 launch");
+  return MX_OK;
+}
+
 }  // extern "C"

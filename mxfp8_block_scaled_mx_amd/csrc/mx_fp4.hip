@@ -130,4 +130,143 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 GEMM: C[M, N] = A[M, K] . B[N, K]^T with both operands in the rowwise
+// MXFP4 layout of the cast above (codes [rows, K/2], scales [rows, K/32]), on
+// gfx950's scaled MFMA with both operand formats set to E2M1. Every product
+// of two E2M1 values is exact; the instruction accumulates in fp32.
+//
+// Workgroup tile 128 x 128: four waves of 64 x 64, each 2 x 2 MFMA tiles of
+// 32 x 32 x 64. Operand fragments go straight from global memory to registers
+// through buffer resources (rows past M or N read as zeros), one k-step of 64
+// ahead of the MFMAs; there is no LDS staging. E2M1 operand layout (pinned on
+// hardware): lane l holds row l % 32 and, with h = l / 32, the 32 values
+// k [32h, 32h+32) of the k-step in the 16 bytes of its first four operand
+// registers, in memory order; its scale register scales that block. (The FP8
+// operand splits each lane's 32 values into two 16-value halves instead.)
+
+// buffer resource over [base, base + bytes), all fields wave-uniform
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fp4_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes)));
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+
+__global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                                       const uint8_t* bs, int64_t M, int64_t N, int64_t K,
+                                                       int64_t n_tiles_n, void* c, int32_t c_f32) {
+  constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
+  const int64_t m0 = mt * kFp4GemmTile + 64 * (wave >> 1);
+  const int64_t n0 = nt * kFp4GemmTile + 64 * (wave & 1);
+  const int64_t mv = min<int64_t>(64, M - m0), nv = min<int64_t>(64, N - n0);
+  if (mv <= 0 || nv <= 0) return;             // wave-uniform; no barriers in this kernel
+  const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
+  const __amdgpu_buffer_rsrc_t ra = fp4_rsrc(a + m0 * ldq, mv * ldq);
+  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + n0 * ldq, nv * ldq);
+  const __amdgpu_buffer_rsrc_t rsa = fp4_rsrc(as + m0 * lds, mv * lds);
+  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + n0 * lds, nv * lds);
+  uint32_t vq[2], vs[2];                      // per-lane offsets of sub-tile rows 32 i + l32
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    vq[i] = (uint32_t)((32 * i + l32) * ldq + 16 * h);
+    vs[i] = (uint32_t)((32 * i + l32) * lds + h);
+  }
+  auto frag = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off) __attribute__((always_inline)) -> v8i {
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    v8i f;
+    f[0] = q.x; f[1] = q.y; f[2] = q.z; f[3] = q.w;
+    f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
+    return f;
+  };
+  // operands and scales of k-step s (64 values); past the last k-step the
+  // loads read the next row's bytes or zeros and are never used
+  v8i fa[2], fb[2], na[2], nb[2];
+  int sa[2], sb[2], nsa[2], nsb[2];
+  auto load_step = [&](int s, v8i (&xa)[2], v8i (&xb)[2], int (&ya)[2], int (&yb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xa[i] = frag(ra, vq[i] + 32 * s);
+      xb[i] = frag(rb, vq[i] + 32 * s);
+      ya[i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsa, vs[i] + 2 * s, 0, 0);
+      yb[i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsb, vs[i] + 2 * s, 0, 0);
+    }
+  };
+  v16f acc[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  const int ksteps = (int)(K / 64);
+  load_step(0, fa, fb, sa, sb);
+  for (int s = 0; s < ksteps; ++s) {
+    load_step(s + 1, na, nb, nsa, nsb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], kE2M1, kE2M1, 0, sb[j],
+                                                                    0, sa[i]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa[i] = na[i]; fb[i] = nb[i]; sa[i] = nsa[i]; sb[i] = nsb[i];
+    }
+  }
+  // lane l holds row 32 i + l32 and, per MFMA tile, columns 8 g + 4 h .. +3
+  // (g = 0..3) in accumulator elements 4 g .. 4 g + 3
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = m0 + 32 * i + l32;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + 32 * j + 8 * g + 4 * h;
+        const float x0 = acc[j][i][4 * g], x1 = acc[j][i][4 * g + 1];
+        const float x2 = acc[j][i][4 * g + 2], x3 = acc[j][i][4 * g + 3];
+        if (c_f32) {
+          float* cp = reinterpret_cast<float*>(c) + row * N + col;
+          if (vec && col + 3 < N) {
+            *reinterpret_cast<float4*>(cp) = make_float4(x0, x1, x2, x3);
+          } else {
+            if (col < N) cp[0] = x0;
+            if (col + 1 < N) cp[1] = x1;
+            if (col + 2 < N) cp[2] = x2;
+            if (col + 3 < N) cp[3] = x3;
+          }
+        } else {
+          uint16_t* cp = reinterpret_cast<uint16_t*>(c) + row * N + col;
+          if (vec && col + 3 < N) {
+            *reinterpret_cast<uint2*>(cp) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+          } else {
+            if (col < N) cp[0] = (uint16_t)bf16_rne(x0);
+            if (col + 1 < N) cp[1] = (uint16_t)bf16_rne(x1);
+            if (col + 2 < N) cp[2] = (uint16_t)bf16_rne(x2);
+            if (col + 3 < N) cp[3] = (uint16_t)bf16_rne(x3);
+          }
+        }
+      }
+  }
+}
+
+hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
+                           int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
+  const int64_t tm = (M + kFp4GemmTile - 1) / kFp4GemmTile, tn = (N + kFp4GemmTile - 1) / kFp4GemmTile;
+  if (tm * tn == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_fp4_kernel, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, M, N, K, tn, c,
+                     c_f32);
+  return hipGetLastError();
+}
+
 }  // namespace mx

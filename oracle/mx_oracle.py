@@ -74,7 +74,7 @@ __all__ = [
     "dequantize_rowwise", "padded_sizes", "quantize_colwise", "gemm_group_m",
     "gemm_group_k", "round_to_bf16", "sigmoid", "silu", "mlp_forward",
     "moe_dispatch", "moe_combine", "e2m1_value", "e2m1_encode", "quantize_rowwise_fp4",
-    "dequantize_rowwise_fp4",
+    "dequantize_rowwise_fp4", "gemm_fp4", "E2M1_VALUES",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
     "mlp_backward_wgrad_entries",
 ]
@@ -647,3 +647,11 @@ def dequantize_rowwise_fp4(q, s):
     codes[:, 1::2] = q >> 4
     scale = np.repeat(e8m0_value(s), BLOCK, axis=1)
     return e2m1_value(codes) * scale
+
+
+def gemm_fp4(a_q, a_s, b_q, b_s):
+    """C = A . B^T (float64) for rowwise MXFP4 operands A [m, k], B [n, k]:
+    each operand dequantized by the MX rule (element times its block's
+    2^(scale code - 127)), then one matmul. The GEMM of the 4-bit MX runs
+    ("examples/llama: default-on fusion & DP-comm perf toggles")."""
+    return dequantize_rowwise_fp4(a_q, a_s) @ dequantize_rowwise_fp4(b_q, b_s).T

@@ -193,3 +193,16 @@ def test_quantize_fp4_argument_errors(L):
     assert L.mx_quantize_fp4(FAKE, 4, 64, None, None, None, None, None) == EINVAL   # nothing requested
     assert L.mx_quantize_fp4(FAKE, 4, 64, FAKE, None, None, None, None) == EINVAL   # half a pair
     assert L.mx_quantize_fp4(FAKE, 4, 64, ctypes.c_void_p(0x100008), FAKE, None, None, None) == EALIGN
+
+
+def test_gemm_fp4_errors(L):
+    g = L.mx_gemm_fp4
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 96, FAKE, 0, None) == ESHAPE      # k % 64
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 0, FAKE, 0, None) == ESHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 4, 64, FAKE, 0, None) == ESHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 2, None) == EINVAL      # dtype
+    assert g(None, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 0, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, None, 4, 4, 64, FAKE, 1, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, ctypes.c_void_p(0x100008), 0, None) == EALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 1 << 27, FAKE, 0, None) == EUNSUPPORTED
+    assert g(None, None, None, None, 0, 4, 64, None, 0, None) == OK             # empty: no-op

@@ -9,7 +9,7 @@ import torch
 
 import oracle as orc
 import workloads as wl
-from tests.gpu_util import dev_bf16
+from tests.gpu_util import canaries_intact, dev_bf16, dev_u8, guarded, mfma_gemm_bound, rel_norm, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +89,98 @@ def test_fp4_colwise_full_size_sampled(gpu_lib):
     wqc, wsc = orc.quantize_rowwise_fp4(orc.bf16_bits_to_f64(bits[:, cols]).T)
     assert np.array_equal(sc.cpu().numpy()[cols], wsc)
     assert np.array_equal(qc.cpu().numpy()[cols], wqc)
+
+
+# ---- MXFP4 GEMM (mx_gemm_fp4) against the oracle's gemm_fp4 on the same codes
+
+def _fp4_operand(rng, rows, k, lo, hi):
+    """Random MXFP4 operand: every byte value (all 16 codes per nibble, -0
+    included) and block scale codes in [lo, hi]."""
+    q = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    s = rng.integers(lo, hi + 1, size=(rows, k // 32), dtype=np.uint8)
+    return q, s
+
+
+def _gemm_fp4(mx, aq, as_, bq, bs, dtype):
+    m, n = aq.shape[0], bq.shape[0]
+    buf, c = guarded((m, n), dtype)
+    mx.mx_gemm_fp4(dev_u8(aq), dev_u8(as_), dev_u8(bq), dev_u8(bs), out=c)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf), "mx_gemm_fp4 wrote outside C"
+    return to_np(c)
+
+
+@pytest.mark.parametrize("m,n", [(300, 200), (257, 130), (1, 1), (128, 128)])
+def test_gemm_fp4_exact(gpu_lib, m, n):
+    # scale codes 126..128 and k = 256 keep every partial sum a multiple of
+    # 2^-4 below 2^16: the fp32 result is exact whatever the summation order,
+    # so any mispaired element, nibble or scale shows as a mismatch
+    rng = np.random.default_rng(1000 + m)
+    k = 256
+    aq, as_ = _fp4_operand(rng, m, k, 126, 128)
+    bq, bs = _fp4_operand(rng, n, k, 126, 128)
+    got = _gemm_fp4(gpu_lib, aq, as_, bq, bs, torch.float32)
+    want = orc.gemm_fp4(aq, as_, bq, bs)
+    assert np.array_equal(got, want), f"max |diff| {np.max(np.abs(got - want))}"
+
+
+@pytest.mark.parametrize("m,n,k", [(257, 130, 512), (96, 300, 64), (512, 256, 1024)])
+def test_gemm_fp4_wide_scales_within_bound(gpu_lib, m, n, k):
+    # scale codes over 2^-7 .. 2^7: inexact sums, checked against the MFMA's
+    # error bound (fp32) and bound plus one bf16 rounding (bf16 output)
+    rng = np.random.default_rng(2000 + k)
+    aq, as_ = _fp4_operand(rng, m, k, 120, 134)
+    bq, bs = _fp4_operand(rng, n, k, 120, 134)
+    A = orc.dequantize_rowwise_fp4(aq, as_)
+    B = orc.dequantize_rowwise_fp4(bq, bs)
+    want = orc.gemm_fp4(aq, as_, bq, bs)
+    bound = mfma_gemm_bound(A, B)
+    got = _gemm_fp4(gpu_lib, aq, as_, bq, bs, torch.float32)
+    assert np.all(np.abs(got - want) <= bound)
+    got16 = _gemm_fp4(gpu_lib, aq, as_, bq, bs, torch.bfloat16)
+    assert np.all(np.abs(got16 - want) <= bound + 2.0 ** -8 * np.abs(want))
+    assert rel_norm(got, want) <= 1e-5
+
+
+def test_gemm_fp4_of_oracle_cast(gpu_lib):
+    # operands cast from normal bf16 data by the oracle's MXFP4 quantizer
+    rng = np.random.default_rng(31)
+    m, n, k = 384, 320, 768
+    a = orc.bf16_bits_to_f64(wl.normal_bf16(rng, (m, k)))
+    b = orc.bf16_bits_to_f64(wl.normal_bf16(rng, (n, k), std=0.02))
+    aq, as_ = orc.quantize_rowwise_fp4(a)
+    bq, bs = orc.quantize_rowwise_fp4(b)
+    want = orc.gemm_fp4(aq, as_, bq, bs)
+    got = _gemm_fp4(gpu_lib, aq, as_, bq, bs, torch.float32)
+    bound = mfma_gemm_bound(orc.dequantize_rowwise_fp4(aq, as_), orc.dequantize_rowwise_fp4(bq, bs))
+    assert np.all(np.abs(got - want) <= bound)
+
+
+def test_gemm_fp4_empty_is_noop(gpu_lib):
+    z = torch.empty((0, 32), dtype=torch.uint8, device="cuda")
+    zs = torch.empty((0, 2), dtype=torch.uint8, device="cuda")
+    bq = torch.zeros((4, 32), dtype=torch.uint8, device="cuda")
+    bs = torch.full((4, 2), 127, dtype=torch.uint8, device="cuda")
+    out = gpu_lib.mx_gemm_fp4(z, zs, bq, bs)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 4)
+
+
+def test_gemm_fp4_full_size_sampled(gpu_lib):
+    # the shape of the Mixtral MLP's first GEMM as one group at MXFP4: 16384
+    # routed rows, 28672 gate and up columns, k = 4096, bf16 output; sampled
+    # rows and columns recomputed by the oracle
+    m, n, k = 16384, 28672, 4096
+    rng = np.random.default_rng(77)
+    aq, as_ = _fp4_operand(rng, m, k, 122, 132)
+    bq, bs = _fp4_operand(rng, n, k, 122, 132)
+    c = gpu_lib.mx_gemm_fp4(dev_u8(aq), dev_u8(as_), dev_u8(bq), dev_u8(bs), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, m - 1], rng.choice(m, 14, replace=False)]))
+    cols = np.sort(np.concatenate([[0, n - 1], rng.choice(n, 254, replace=False)]))
+    got = to_np(c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    A = orc.dequantize_rowwise_fp4(aq[rows], as_[rows])
+    B = orc.dequantize_rowwise_fp4(bq[cols], bs[cols])
+    want = A @ B.T
+    bound = mfma_gemm_bound(A, B) + 2.0 ** -8 * np.abs(want)
+    assert np.all(np.abs(got - want) <= bound)

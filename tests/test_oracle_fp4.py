@@ -67,3 +67,78 @@ def test_scale_equivariance_round_trip_and_zero():
     assert np.array_equal(q3, q) and np.array_equal(s3, s)
     qz, sz = orc.quantize_rowwise_fp4(np.zeros((1, 32)))
     assert qz.tolist() == [[0] * 16] and sz.tolist() == [[0]]
+
+
+# ---- the MXFP4 GEMM of the oracle (gemm_fp4): closed forms
+
+def _fill(rows, k, code, scale):
+    """rows x k operand whose every element has E2M1 code `code` (per row) and
+    every block scale code `scale` (per row)."""
+    code = np.asarray(code, dtype=np.uint8).reshape(-1, 1)
+    q = np.repeat(code | (code << 4), k // 2, axis=1).astype(np.uint8)
+    s = np.repeat(np.asarray(scale, dtype=np.uint8).reshape(-1, 1), k // 32, axis=1)
+    return q, s
+
+
+def test_gemm_fp4_constant_rows():
+    # row i of A is the constant v_i, row j of B is w_j: C[i, j] = k v_i w_j.
+    # m != n, so a transposed operand or output changes the shape or values.
+    k = 128
+    a_codes, a_vals = [2, 7, 10, 5], [1.0, 6.0, -1.0, 3.0]          # 1, 6, -1, 3
+    b_codes, b_vals = [1, 12, 3], [0.5, -2.0, 1.5]
+    aq, as_ = _fill(4, k, a_codes, [127, 128, 126, 127])            # scales 1, 2, 1/2, 1
+    bq, bs = _fill(3, k, b_codes, [127, 127, 129])                  # scales 1, 1, 4
+    C = orc.gemm_fp4(aq, as_, bq, bs)
+    av = np.array(a_vals) * np.array([1.0, 2.0, 0.5, 1.0])
+    bv = np.array(b_vals) * np.array([1.0, 1.0, 4.0])
+    assert C.shape == (4, 3)
+    assert np.array_equal(C, k * np.outer(av, bv))
+
+
+def test_gemm_fp4_single_nonzero_element():
+    # one nonzero element per operand row at chosen k: C[i, j] is their product
+    # when the positions match and 0 otherwise; checks the nibble -> k order
+    # (element 2i in the low nibble) and the block -> scale pairing
+    k = 64
+    aq = np.zeros((2, k // 2), dtype=np.uint8)
+    bq = np.zeros((2, k // 2), dtype=np.uint8)
+    as_ = np.full((2, 2), 127, dtype=np.uint8)
+    bs = np.full((2, 2), 127, dtype=np.uint8)
+    aq[0, 20] = 0x07         # A[0, 40] = 6 (low nibble = even element 40), block 1
+    aq[1, 20] = 0x70         # A[1, 41] = 6 (high nibble = odd element 41)
+    bq[0, 20] = 0x05         # B[0, 40] = 3
+    bq[1, 20] = 0x30         # B[1, 41] = 1.5
+    as_[0, 1] = 129          # block 1 of A row 0 scaled by 4
+    bs[1, 0] = 140           # block 0 of B row 1: no nonzero element there
+    C = orc.gemm_fp4(aq, as_, bq, bs)
+    assert C.tolist() == [[6 * 4 * 3, 0.0], [0.0, 6 * 1.5]]
+
+
+def test_gemm_fp4_matches_blockwise_sum():
+    # C equals the sum over 32-blocks of 2^(sa + sb) times the integer-grid
+    # dot product of the block's E2M1 values (values doubled to integers)
+    rng = np.random.default_rng(7)
+    m, n, k = 5, 6, 128
+    aq = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    bq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    as_ = rng.integers(120, 135, size=(m, k // 32), dtype=np.uint8)
+    bs = rng.integers(120, 135, size=(n, k // 32), dtype=np.uint8)
+    twice = {c: int(round(2 * v)) for c, v in enumerate(orc.E2M1_VALUES)}   # 0..12
+
+    def ints(q):
+        out = np.empty((q.shape[0], q.shape[1] * 2), dtype=np.int64)
+        for r in range(q.shape[0]):
+            for j in range(q.shape[1]):
+                for half, c in enumerate((int(q[r, j]) & 0xF, int(q[r, j]) >> 4)):
+                    v = twice[c & 7]
+                    out[r, 2 * j + half] = -v if c & 8 else v
+        return out
+
+    ai, bi = ints(aq), ints(bq)
+    want = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            for b in range(k // 32):
+                dot = int(np.dot(ai[i, 32 * b:32 * b + 32], bi[j, 32 * b:32 * b + 32]))
+                want[i, j] += dot * 2.0 ** (int(as_[i, b]) + int(bs[j, b]) - 254 - 2)
+    assert np.array_equal(orc.gemm_fp4(aq, as_, bq, bs), want)
