@@ -335,7 +335,7 @@ MX_API mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint
  *   c       [m, n] row-major, bf16 (rounded to nearest even) or fp32 per
  *           c_dtype; written, never read.
  * Caller-owned device memory; nothing is allocated. Requires k a positive
- * multiple of 64 (at most 2^26); a, b, c 16-byte aligned. m or n zero is a
+ * multiple of 64 (at most 2^24); a, b, c 16-byte aligned. m or n zero is a
  * no-op. Errors: MX_EINVAL, MX_ESHAPE, MX_EALIGN, MX_EUNSUPPORTED, MX_EHIP.
  */
 MX_API mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s, int64_t m,

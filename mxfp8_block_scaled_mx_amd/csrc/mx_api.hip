@@ -972,8 +972,8 @@ mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, co
   const char* who = "mx_gemm_fp4";
   if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
   if (m < 0 || n < 0 || k <= 0 || k % 64) return fail(MX_ESHAPE, "%s: need m, n >= 0 and k a positive multiple of 64", who);
-  if (k > ((int64_t)1 << 26)) return fail(MX_EUNSUPPORTED, "%s: k above 2^26", who);
-  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+  if (k > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: k above 2^24", who);
+  const int64_t tiles = ((m + mx::kFp4GemmTileM - 1) / mx::kFp4GemmTileM) * ((n + mx::kFp4GemmTileN - 1) / mx::kFp4GemmTileN);
   if (tiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many output tiles", who);
   if (m == 0 || n == 0) return MX_OK;
   if (!a || !a_s || !b || !b_s || !c) return fail(MX_EINVAL, "%s: null pointer argument", who);

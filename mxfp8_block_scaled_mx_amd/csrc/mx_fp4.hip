@@ -136,10 +136,9 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
 // gfx950's scaled MFMA with both operand formats set to E2M1. Every product
 // of two E2M1 values is exact; the instruction accumulates in fp32.
 //
-// Workgroup tile 128 x 128: four waves of 64 x 64, each 2 x 2 MFMA tiles of
-// 32 x 32 x 64. Operand fragments go straight from global memory to registers
-// through buffer resources (rows past M or N read as zeros), one k-step of 64
-// ahead of the MFMAs; there is no LDS staging. E2M1 operand layout (pinned on
+// Workgroup tile 256 x 128: four waves in 2 x 2, each 4 x 2 MFMA tiles of
+// 32 x 32 x 64. Operands are read through buffer resources, so rows past M
+// or N read as zeros. E2M1 operand layout (pinned on
 // hardware): lane l holds row l % 32 and, with h = l / 32, the 32 values
 // k [32h, 32h+32) of the k-step in the 16 bytes of its first four operand
 // registers, in memory order; its scale register scales that block. (The FP8
@@ -156,80 +155,156 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t fp4_rsrc(const void* base, int
                                            0x00020000);
 }
 
+// A k-tile is 256 values (128 bytes of codes) of every row of the workgroup
+// tile; A and B k-tiles are staged in LDS, double-buffered. Global loads are
+// coalesced (8 lanes per 128-byte row) and stored with 16-byte chunk c of row
+// r at chunk c ^ (r & 7), so that fragment reads (32 rows, one chunk) spread
+// over the LDS banks. One barrier per k-tile: the next k-tile's loads are in
+// flight during this one's MFMAs and are written to the other buffer after.
+constexpr int kF4SubM = 4, kF4SubN = 2;     // wave tile: MFMA tiles of 32 x 32
+constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
+static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
+
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                                        const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                                                        int64_t n_tiles_n, void* c, int32_t c_f32) {
+  constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
+  constexpr int LA = TM * KT / (16 * 256), LB = TN * KT / (16 * 256);   // 16-byte loads per thread
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][TN * KT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
-  const int64_t m0 = mt * kFp4GemmTile + 64 * (wave >> 1);
-  const int64_t n0 = nt * kFp4GemmTile + 64 * (wave & 1);
-  const int64_t mv = min<int64_t>(64, M - m0), nv = min<int64_t>(64, N - n0);
-  if (mv <= 0 || nv <= 0) return;             // wave-uniform; no barriers in this kernel
+  const int64_t am0 = mt * TM, bn0 = nt * TN;
+  const int64_t amv = min<int64_t>(TM, M - am0), bnv = min<int64_t>(TN, N - bn0);
   const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
-  const __amdgpu_buffer_rsrc_t ra = fp4_rsrc(a + m0 * ldq, mv * ldq);
-  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + n0 * ldq, nv * ldq);
-  const __amdgpu_buffer_rsrc_t rsa = fp4_rsrc(as + m0 * lds, mv * lds);
-  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + n0 * lds, nv * lds);
-  uint32_t vq[2], vs[2];                      // per-lane offsets of sub-tile rows 32 i + l32
+  const __amdgpu_buffer_rsrc_t ra = fp4_rsrc(a + am0 * ldq, amv * ldq);
+  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + bn0 * ldq, bnv * ldq);
+  const __amdgpu_buffer_rsrc_t rsa = fp4_rsrc(as + am0 * lds, amv * lds);
+  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + bn0 * lds, bnv * lds);
+  const int ksteps = (int)(K / 64), ktiles = (ksteps + 3) / 4;
+  const bool sc_dword = (lds & 7) == 0;       // a row's 8 scales of a k-tile: one aligned 8-byte load
+
+  // global -> registers: chunk q = p * 256 + tid is row q / 8, chunk q % 8.
+  // Bytes past K in the last k-tile come from the next row (or read zero)
+  // and feed only skipped k-steps.
+  u32x4 ga[LA], gb[LB];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    vq[i] = (uint32_t)((32 * i + l32) * ldq + 16 * h);
-    vs[i] = (uint32_t)((32 * i + l32) * lds + h);
-  }
-  auto frag = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off) __attribute__((always_inline)) -> v8i {
-    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    for (int p = 0; p < LA; ++p) {
+      const int q = p * 256 + tid;
+      ga[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((q >> 3) * ldq + KT * t + 16 * (q & 7)), 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < LB; ++p) {
+      const int q = p * 256 + tid;
+      gb[p] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)((q >> 3) * ldq + KT * t + 16 * (q & 7)), 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < LA; ++p) {
+      const int q = p * 256 + tid, r = q >> 3;
+      *reinterpret_cast<u32x4*>(&sA[buf][r * KT + (((q & 7) ^ (r & 7)) << 4)]) = ga[p];
+    }
+#pragma unroll
+    for (int p = 0; p < LB; ++p) {
+      const int q = p * 256 + tid, r = q >> 3;
+      *reinterpret_cast<u32x4*>(&sB[buf][r * KT + (((q & 7) ^ (r & 7)) << 4)]) = gb[p];
+    }
+  };
+  // scales of k-tile t for this lane's rows: blocks 8 t .. 8 t + 7
+  u32x2 sca[SM], scb[SN];
+  auto scale_pair = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off) __attribute__((always_inline)) -> u32x2 {
+    if (sc_dword) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u32x2 v;
+    v.x = 0; v.y = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(r, off + e, 0, 0);
+      if (e < 4) v.x |= byte << (8 * e); else v.y |= byte << (8 * (e - 4));
+    }
+    return v;
+  };
+  auto load_scales = [&](int t, u32x2 (&xa)[SM], u32x2 (&xb)[SN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) xa[i] = scale_pair(rsa, (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + 8 * t));
+#pragma unroll
+    for (int j = 0; j < SN; ++j) xb[j] = scale_pair(rsb, (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + 8 * t));
+  };
+  auto frag = [&](const uint8_t* base, int r, int s) __attribute__((always_inline)) -> v8i {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ (r & 7)) << 4));
     v8i f;
     f[0] = q.x; f[1] = q.y; f[2] = q.z; f[3] = q.w;
     f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
     return f;
   };
-  // operands and scales of k-step s (64 values); past the last k-step the
-  // loads read the next row's bytes or zeros and are never used
-  v8i fa[2], fb[2], na[2], nb[2];
-  int sa[2], sb[2], nsa[2], nsb[2];
-  auto load_step = [&](int s, v8i (&xa)[2], v8i (&xb)[2], int (&ya)[2], int (&yb)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xa[i] = frag(ra, vq[i] + 32 * s);
-      xb[i] = frag(rb, vq[i] + 32 * s);
-      ya[i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsa, vs[i] + 2 * s, 0, 0);
-      yb[i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rsb, vs[i] + 2 * s, 0, 0);
-    }
+  auto pick = [&](const u32x2& v, int s) __attribute__((always_inline)) -> int {
+    const int blk = 2 * s + h;               // this lane's block of k-step s
+    return (int)(((blk < 4 ? v.x : v.y) >> (8 * (blk & 3))) & 0xFFu);
   };
-  v16f acc[2][2];
+
+  v16f acc[SN][SM];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SM; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
-  const int ksteps = (int)(K / 64);
-  load_step(0, fa, fb, sa, sb);
-  for (int s = 0; s < ksteps; ++s) {
-    load_step(s + 1, na, nb, nsa, nsb);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], kE2M1, kE2M1, 0, sb[j],
-                                                                    0, sa[i]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      fa[i] = na[i]; fb[i] = nb[i]; sa[i] = nsa[i]; sb[i] = nsb[i];
+
+  u32x2 nsa[SM], nsb[SN];
+  load_tile(0);
+  load_scales(0, sca, scb);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ktiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ktiles;         // uniform over the workgroup
+    if (more) {
+      load_tile(t + 1);
+      load_scales(t + 1, nsa, nsb);
     }
+    const uint8_t* A = sA[buf] + (TM / 2 * wm) * KT;
+    const uint8_t* B = sB[buf] + (TN / 2 * wn) * KT;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (4 * t + s < ksteps) {
+        v8i fa[SM], fb[SN];
+#pragma unroll
+        for (int i = 0; i < SM; ++i) fa[i] = frag(A, 32 * i + l32, s);
+#pragma unroll
+        for (int j = 0; j < SN; ++j) fb[j] = frag(B, 32 * j + l32, s);
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+#pragma unroll
+          for (int i = 0; i < SM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], kE2M1, kE2M1, 0,
+                                                                        pick(scb[j], s), 0, pick(sca[i], s));
+      }
+    }
+    if (more) {
+      store_tile(buf ^ 1);
+#pragma unroll
+      for (int i = 0; i < SM; ++i) sca[i] = nsa[i];
+#pragma unroll
+      for (int j = 0; j < SN; ++j) scb[j] = nsb[j];
+    }
+    __syncthreads();
   }
+
   // lane l holds row 32 i + l32 and, per MFMA tile, columns 8 g + 4 h .. +3
   // (g = 0..3) in accumulator elements 4 g .. 4 g + 3
+  const int64_t m0 = am0 + TM / 2 * wm, n0 = bn0 + TN / 2 * wn;
   const bool vec = (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < SM; ++i) {
     const int64_t row = m0 + 32 * i + l32;
     if (row >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t col = n0 + 32 * j + 8 * g + 4 * h;
@@ -262,7 +337,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
                            int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
-  const int64_t tm = (M + kFp4GemmTile - 1) / kFp4GemmTile, tn = (N + kFp4GemmTile - 1) / kFp4GemmTile;
+  const int64_t tm = (M + kFp4GemmTileM - 1) / kFp4GemmTileM, tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
   if (tm * tn == 0) return hipSuccess;
   hipLaunchKernelGGL(gemm_fp4_kernel, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, M, N, K, tn, c,
                      c_f32);

@@ -160,9 +160,9 @@ hipError_t launch_moe_combine(const void* y_perm, const int32_t* perm, int64_t t
 // Rowwise MXFP4 cast (mx_fp4.hip).
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
                                uint8_t* s_col, hipStream_t stream);
-// MXFP4 GEMM C = A . B^T (mx_fp4.hip): 128 x 128 tiles, c_f32 selects fp32
-// (else bf16) output.
-constexpr int kFp4GemmTile = 128;
+// MXFP4 GEMM C = A . B^T (mx_fp4.hip): kFp4GemmTileM x kFp4GemmTileN tiles,
+// c_f32 selects fp32 (else bf16) output.
+constexpr int kFp4GemmTileM = 256, kFp4GemmTileN = 128;
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
                            int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
 
