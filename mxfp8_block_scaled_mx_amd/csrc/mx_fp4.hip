@@ -136,8 +136,8 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
 // gfx950's scaled MFMA with both operand formats set to E2M1. Every product
 // of two E2M1 values is exact; the instruction accumulates in fp32.
 //
-// Workgroup tile 256 x 128: four waves in 2 x 2, each 4 x 2 MFMA tiles of
-// 32 x 32 x 64. Operands are read through buffer resources, so rows past M
+// Workgroup tile 256 x 256: four waves in 2 x 2, each 4 x 4 MFMA tiles of
+// 32 x 32 x 64 (128 x 128 fp32 accumulators in AGPRs). Operands are read through buffer resources, so rows past M
 // or N read as zeros. E2M1 operand layout (pinned on
 // hardware): lane l holds row l % 32 and, with h = l / 32, the 32 values
 // k [32h, 32h+32) of the k-step in the 16 bytes of its first four operand
@@ -156,12 +156,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t fp4_rsrc(const void* base, int
 }
 
 // A k-tile is 256 values (128 bytes of codes) of every row of the workgroup
-// tile; A and B k-tiles are staged in LDS, double-buffered. Global loads are
-// coalesced (8 lanes per 128-byte row) and stored with 16-byte chunk c of row
-// r at chunk c ^ (r & 7), so that fragment reads (32 rows, one chunk) spread
-// over the LDS banks. One barrier per k-tile: the next k-tile's loads are in
-// flight during this one's MFMAs and are written to the other buffer after.
-constexpr int kF4SubM = 4, kF4SubN = 2;     // wave tile: MFMA tiles of 32 x 32
+// tile; A and B k-tiles are staged in LDS, double-buffered, by buffer->LDS DMA
+// (8 lanes per 128-byte row), with 16-byte chunk c of row r at chunk
+// c ^ (r & 7) so that fragment reads (32 rows, one chunk) spread over the LDS
+// banks. One barrier per k-tile: the next k-tile's DMA is in flight during
+// this one's MFMAs.
+typedef __attribute__((address_space(3))) void fp4_lds_void;
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left open
+constexpr int kF4WaitVmcnt0 = 0x0F70;
+constexpr int kF4SubM = 4, kF4SubN = 4;     // wave tile: MFMA tiles of 32 x 32
 constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
 static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
 
@@ -169,7 +172,6 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
                                                        const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                                                        int64_t n_tiles_n, void* c, int32_t c_f32) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
-  constexpr int LA = TM * KT / (16 * 256), LB = TN * KT / (16 * 256);   // 16-byte loads per thread
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][TN * KT];
@@ -188,32 +190,24 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int ksteps = (int)(K / 64), ktiles = (ksteps + 3) / 4;
   const bool sc_dword = (lds & 7) == 0;       // a row's 8 scales of a k-tile: one aligned 8-byte load
 
-  // global -> registers: chunk q = p * 256 + tid is row q / 8, chunk q % 8.
-  // Bytes past K in the last k-tile come from the next row (or read zero)
-  // and feed only skipped k-steps.
-  u32x4 ga[LA], gb[LB];
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
+  // global -> LDS by buffer DMA, 1 KB (8 rows) per instruction: lane L
+  // fills chunk L % 8 of row L / 8 of the block with global chunk
+  // (L % 8) ^ (L / 8), which is the swizzle above since the block starts at a
+  // multiple of 8 rows. Bytes past K in the last k-tile come from the next row
+  // (or read zero) and feed only skipped k-steps.
+  const uint32_t dma_off = (uint32_t)((lane >> 3) * ldq + 16 * ((lane & 7) ^ (lane >> 3)));
+  auto dma_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < LA; ++p) {
-      const int q = p * 256 + tid;
-      ga[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((q >> 3) * ldq + KT * t + 16 * (q & 7)), 0, 0);
+    for (int p = 0; p < TM / 32; ++p) {
+      const int blk = 4 * p + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (fp4_lds_void*)(&sA[buf][blk * 1024]), 16, dma_off,
+                                               (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < LB; ++p) {
-      const int q = p * 256 + tid;
-      gb[p] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)((q >> 3) * ldq + KT * t + 16 * (q & 7)), 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < LA; ++p) {
-      const int q = p * 256 + tid, r = q >> 3;
-      *reinterpret_cast<u32x4*>(&sA[buf][r * KT + (((q & 7) ^ (r & 7)) << 4)]) = ga[p];
-    }
-#pragma unroll
-    for (int p = 0; p < LB; ++p) {
-      const int q = p * 256 + tid, r = q >> 3;
-      *reinterpret_cast<u32x4*>(&sB[buf][r * KT + (((q & 7) ^ (r & 7)) << 4)]) = gb[p];
+    for (int p = 0; p < TN / 32; ++p) {
+      const int blk = 4 * p + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (fp4_lds_void*)(&sB[buf][blk * 1024]), 16, dma_off,
+                                               (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
   };
   // scales of k-tile t for this lane's rows: blocks 8 t .. 8 t + 7
@@ -256,15 +250,15 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
   u32x2 nsa[SM], nsb[SN];
-  load_tile(0);
+  dma_tile(0, 0);
   load_scales(0, sca, scb);
-  store_tile(0);
+  __builtin_amdgcn_s_waitcnt(kF4WaitVmcnt0);
   __syncthreads();
   for (int t = 0; t < ktiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ktiles;         // uniform over the workgroup
     if (more) {
-      load_tile(t + 1);
+      dma_tile(t + 1, buf ^ 1);
       load_scales(t + 1, nsa, nsb);
     }
     const uint8_t* A = sA[buf] + (TM / 2 * wm) * KT;
@@ -272,21 +266,24 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (4 * t + s < ksteps) {
-        v8i fa[SM], fb[SN];
-#pragma unroll
-        for (int i = 0; i < SM; ++i) fa[i] = frag(A, 32 * i + l32, s);
+        // B fragments of the k-step stay in registers; each A fragment is
+        // read just before its row of MFMAs
+        v8i fb[SN];
 #pragma unroll
         for (int j = 0; j < SN; ++j) fb[j] = frag(B, 32 * j + l32, s);
 #pragma unroll
-        for (int j = 0; j < SN; ++j)
+        for (int i = 0; i < SM; ++i) {
+          const v8i fa = frag(A, 32 * i + l32, s);
+          const int sai = pick(sca[i], s);
 #pragma unroll
-          for (int i = 0; i < SM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], kE2M1, kE2M1, 0,
-                                                                        pick(scb[j], s), 0, pick(sca[i], s));
+          for (int j = 0; j < SN; ++j)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa, acc[j][i], kE2M1, kE2M1, 0,
+                                                                        pick(scb[j], s), 0, sai);
+        }
       }
     }
     if (more) {
-      store_tile(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kF4WaitVmcnt0);   // this wave's DMA and scales landed
 #pragma unroll
       for (int i = 0; i < SM; ++i) sca[i] = nsa[i];
 #pragma unroll
@@ -308,8 +305,9 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t col = n0 + 32 * j + 8 * g + 4 * h;
-        const float x0 = acc[j][i][4 * g], x1 = acc[j][i][4 * g + 1];
-        const float x2 = acc[j][i][4 * g + 2], x3 = acc[j][i][4 * g + 3];
+        // through a VALU move, so the accumulators stay AGPR-only operands
+        const float x0 = vgpr_hop(acc[j][i][4 * g]), x1 = vgpr_hop(acc[j][i][4 * g + 1]);
+        const float x2 = vgpr_hop(acc[j][i][4 * g + 2]), x3 = vgpr_hop(acc[j][i][4 * g + 3]);
         if (c_f32) {
           float* cp = reinterpret_cast<float*>(c) + row * N + col;
           if (vec && col + 3 < N) {

@@ -162,7 +162,7 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
                                uint8_t* s_col, hipStream_t stream);
 // MXFP4 GEMM C = A . B^T (mx_fp4.hip): kFp4GemmTileM x kFp4GemmTileN tiles,
 // c_f32 selects fp32 (else bf16) output.
-constexpr int kFp4GemmTileM = 256, kFp4GemmTileN = 128;
+constexpr int kFp4GemmTileM = 256, kFp4GemmTileN = 256;
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
                            int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
 
