@@ -59,6 +59,10 @@ R13 token combine: y[t] = sum over slots j of the routed output row of
     (t, j), slots with perm -1 skipped, summed in float64 and rounded once to
     bf16. The routing weight is already applied inside the MLP (R8), so the
     combine is unweighted.
+R15 MXFP4 GEMM: C = A . B^T with A [m, k] and B [n, k] both rowwise MXFP4
+    (R14), each element taken at its value E2M1(code) * 2^(scale - 127); the
+    pages name the format's GEMMs (mxfp4 runs) but not their arithmetic, so
+    the plain product of the dequantized operands is the definition.
 """
 from __future__ import annotations
 
