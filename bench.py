@@ -293,10 +293,11 @@ def main():
             f"both layouts {f4['both_layouts_gbps']:.0f} GB/s")
 
     if not args.no_gemm_fp4:
-        out["gemm_fp4"] = measure_gemm_fp4(mx, torch, dev)
+        out["gemm_fp4"] = measure_gemm_fp4(mx, torch, dev, split)
         g4 = out["gemm_fp4"]
         log(f"MXFP4 GEMM {g4['workload']}: {g4['ms']:.3f} ms -> {g4['tflops']:.0f} TFLOP/s "
-            f"({g4['roofline']['frac']:.3f} of the FP4 peak)")
+            f"({g4['roofline']['frac']:.3f} of the FP4 peak); grouped over the step's split_sizes "
+            f"{g4['grouped']['ms']:.3f} ms -> {g4['grouped']['tflops']:.0f} TFLOP/s")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -528,10 +529,12 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
           flush=True)
 
 
-def measure_gemm_fp4(mx, torch, dev, iters=10, m=16384, n=28672, k=4096):
+def measure_gemm_fp4(mx, torch, dev, split, iters=10, m=16384, n=28672, k=4096):
     """mx_gemm_fp4 (C = A . B^T, bf16 out) on random MXFP4 operands of the
     Mixtral MLP's first GEMM taken as one group: 16384 rows, 28672 columns,
-    k = 4096. 2 m n k flops per call, priced at the FP4 MFMA peak."""
+    k = 4096; and mx_grouped_gemm_fp4 on the step's routed rows over its
+    split_sizes (one 28672 x 4096 weight per expert). 2 m n k flops per call,
+    priced at the FP4 MFMA peak."""
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     aq = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device=dev, generator=g)
@@ -550,7 +553,26 @@ def measure_gemm_fp4(mx, torch, dev, iters=10, m=16384, n=28672, k=4096):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    # grouped: the step's routed rows (sum of split) over its experts
+    G, mg = len(split), int(sum(split))
+    ag, ags = aq[:mg], as_[:mg]
+    bgq = torch.randint(0, 256, (G, n, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    bgs = torch.randint(122, 133, (G, n, k // 32), dtype=torch.uint8, device=dev, generator=g)
+    cg = torch.empty((mg, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        mx.mx_grouped_gemm_fp4(ag, ags, bgq, bgs, split, out=cg)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        mx.mx_grouped_gemm_fp4(ag, ags, bgq, bgs, split, out=cg)
+    e1.record()
+    torch.cuda.synchronize()
+    msg = e0.elapsed_time(e1) / iters
+    tfg = 2.0 * mg * n * k / (msg * 1e-3) / 1e12
+    grouped = {"workload": f"grouped_gemm_fp4_{mg}x{n}x{k}_{G}experts", "split_sizes": [int(v) for v in split],
+               "ms": round(msg, 4), "tflops": round(tfg, 1), "frac_fp4_peak": round(tfg / PEAK_FP4_TFLOPS, 4)}
     return {"workload": f"gemm_fp4_{m}x{n}x{k}", "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "grouped": grouped,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP4_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}}
 

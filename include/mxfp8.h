@@ -341,6 +341,24 @@ MX_API mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint
 MX_API mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s, int64_t m,
                              int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream);
 
+/*
+ * mx_grouped_gemm_fp4 -- the grouped (GroupedLinear) form of mx_gemm_fp4 over
+ * per-expert split_sizes ("Efficient MoE training for biological foundation
+ * models", Key technical approaches item 1): the rows of A are split into
+ * `groups` consecutive groups of group_sizes[g] rows, and the rows of group g
+ * get C = A_g . B_g^T.
+ *   a, a_s       rowwise MXFP4 A [sum(group_sizes), k] (codes, scales);
+ *   b, b_s       rowwise MXFP4 weights, groups x [n, k], group after group
+ *                (codes [groups, n, k/2], scales [groups, n, k/32]);
+ *   group_sizes  host int64 [groups], each >= 0 (empty groups allowed);
+ *   c            [sum(group_sizes), n] row-major, bf16 or fp32 per c_dtype.
+ * 1 <= groups <= MX_MAX_GROUPS. Same requirements, ownership and errors as
+ * mx_gemm_fp4, which is this call with one group.
+ */
+MX_API mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                                     const int64_t* group_sizes, int32_t groups, int64_t n, int64_t k, void* c,
+                                     mx_dtype c_dtype, void* stream);
+
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
 
 /*

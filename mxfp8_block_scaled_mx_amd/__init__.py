@@ -22,7 +22,7 @@ __all__ = [
     "load", "lib_path", "MXError", "MX_BF16", "MX_F32", "MX_GROUP_M", "MX_GROUP_K",
     "MAX_GROUPS", "padded_sizes", "quantize", "grouped_gemm", "mlp_sizes",
     "grouped_mlp_fwd", "grouped_mlp_bwd", "GroupedMLP", "MLPState", "MLPRunner",
-    "set_stage_events", "FWD_STAGES", "BWD_STAGES", "mx_quantize_fp4", "mx_gemm_fp4",
+    "set_stage_events", "FWD_STAGES", "BWD_STAGES", "mx_quantize_fp4", "mx_gemm_fp4", "mx_grouped_gemm_fp4",
 ]
 
 FWD_STAGES = ("quantize_x", "quantize_w1", "quantize_w2", "gemm1_swiglu", "gemm2")
@@ -111,6 +111,8 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.mx_gemm_fp4.restype = ctypes.c_int
     L.mx_gemm_fp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+    L.mx_grouped_gemm_fp4.restype = ctypes.c_int
+    L.mx_grouped_gemm_fp4.argtypes = [vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L
@@ -422,6 +424,31 @@ def mx_gemm_fp4(a_q, a_s, b_q, b_s, out_dtype=torch.bfloat16, out=None, stream=N
         out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
     dt = MX_F32 if out.dtype == torch.float32 else MX_BF16
     _check(L.mx_gemm_fp4(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), m, n, k, _ptr(out), dt, _stream(stream)))
+    return out
+
+
+def mx_grouped_gemm_fp4(a_q, a_s, b_q, b_s, group_sizes, out_dtype=torch.bfloat16, out=None, stream=None):
+    """Grouped MXFP4 GEMM over split_sizes: rows of group g of A (a_q [M, k/2],
+    a_s [M, k/32], M = sum(group_sizes)) times B_g^T with b_q [G, n, k/2],
+    b_s [G, n, k/32]; returns C [M, n] (bf16 or fp32)."""
+    L = load()
+    sizes = [int(v) for v in group_sizes]
+    G, n, k = len(sizes), b_q.shape[1], a_q.shape[1] * 2
+    m = a_q.shape[0]
+    for t in (a_q, a_s, b_q, b_s):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("mx_grouped_gemm_fp4: codes and scales must be contiguous uint8 tensors")
+    if (sum(sizes) != m or tuple(a_s.shape) != (m, k // 32) or tuple(b_q.shape) != (G, n, k // 2)
+            or tuple(b_s.shape) != (G, n, k // 32)):
+        raise ValueError("mx_grouped_gemm_fp4: operand shapes do not match the group sizes")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    if tuple(out.shape) != (m, n) or not out.is_contiguous() or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("mx_grouped_gemm_fp4: out must be a contiguous bf16 or fp32 [M, n] tensor")
+    dt = MX_F32 if out.dtype == torch.float32 else MX_BF16
+    arr = (ctypes.c_int64 * max(G, 1))(*sizes)
+    _check(L.mx_grouped_gemm_fp4(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), arr, G, n, k, _ptr(out), dt,
+                                 _stream(stream)))
     return out
 
 

@@ -458,6 +458,39 @@ mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, con
 
 }  // namespace
 
+// MXFP4 (grouped) GEMM: validation, group table, launch.
+static mx_status gemm_fp4_impl(const char* who, const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
+                               const uint8_t* b_s, const int64_t* sizes, int32_t groups, int64_t n, int64_t k,
+                               void* c, mx_dtype c_dtype, void* stream) {
+  if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
+  if (groups < 1 || groups > MX_MAX_GROUPS) return fail(MX_EINVAL, "%s: need 1 <= groups <= %d", who, MX_MAX_GROUPS);
+  if (!sizes) return fail(MX_EINVAL, "%s: null group sizes", who);
+  if (n < 0 || k <= 0 || k % 64) return fail(MX_ESHAPE, "%s: need n >= 0 and k a positive multiple of 64", who);
+  if (k > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: k above 2^24", who);
+  mx::Fp4Groups gr{};
+  gr.n = groups;
+  int64_t rows = 0, mtiles = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (sizes[g] < 0) return fail(MX_ESHAPE, "%s: negative group size", who);
+    gr.row0[g] = rows;
+    gr.tile0[g] = (int32_t)(mtiles < kI32Max ? mtiles : kI32Max);
+    rows += sizes[g];
+    mtiles += (sizes[g] + mx::kFp4GemmTileM - 1) / mx::kFp4GemmTileM;
+  }
+  gr.row0[groups] = rows;
+  const int64_t ntiles = (n + mx::kFp4GemmTileN - 1) / mx::kFp4GemmTileN;
+  if (mtiles * ntiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many output tiles", who);
+  gr.tile0[groups] = (int32_t)mtiles;
+  if (rows == 0 || n == 0) return MX_OK;
+  if (!a || !a_s || !b || !b_s || !c) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
+    return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
+  hipError_t e = mx::launch_gemm_fp4(a, a_s, b, b_s, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, who);
+  return MX_OK;
+}
+
 extern "C" {
 
 const char* mx_status_string(int s) {
@@ -969,20 +1002,15 @@ mx_status mx_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q,
 mx_status mx_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s, int64_t m, int64_t n,
                       int64_t k, void* c, mx_dtype c_dtype, void* stream) {
   g_err[0] = 0;
-  const char* who = "mx_gemm_fp4";
-  if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
-  if (m < 0 || n < 0 || k <= 0 || k % 64) return fail(MX_ESHAPE, "%s: need m, n >= 0 and k a positive multiple of 64", who);
-  if (k > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: k above 2^24", who);
-  const int64_t tiles = ((m + mx::kFp4GemmTileM - 1) / mx::kFp4GemmTileM) * ((n + mx::kFp4GemmTileN - 1) / mx::kFp4GemmTileN);
-  if (tiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many output tiles", who);
-  if (m == 0 || n == 0) return MX_OK;
-  if (!a || !a_s || !b || !b_s || !c) return fail(MX_EINVAL, "%s: null pointer argument", who);
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
-    return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
-  hipError_t e = mx::launch_gemm_fp4(a, a_s, b, b_s, m, n, k, c, c_dtype == MX_F32 ? 1 : 0,
-                                     reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mx_gemm_fp4 launch");
-  return MX_OK;
+  if (m < 0) return fail(MX_ESHAPE, "mx_gemm_fp4: need m >= 0");
+  return gemm_fp4_impl("mx_gemm_fp4", a, a_s, b, b_s, &m, 1, n, k, c, c_dtype, stream);
+}
+
+mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                              const int64_t* group_sizes, int32_t groups, int64_t n, int64_t k, void* c,
+                              mx_dtype c_dtype, void* stream) {
+  g_err[0] = 0;
+  return gemm_fp4_impl("mx_grouped_gemm_fp4", a, a_s, b, b_s, group_sizes, groups, n, k, c, c_dtype, stream);
 }
 
 }  // extern "C"

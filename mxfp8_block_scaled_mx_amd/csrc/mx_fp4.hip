@@ -131,10 +131,13 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 GEMM: C[M, N] = A[M, K] . B[N, K]^T with both operands in the rowwise
-// MXFP4 layout of the cast above (codes [rows, K/2], scales [rows, K/32]), on
-// gfx950's scaled MFMA with both operand formats set to E2M1. Every product
-// of two E2M1 values is exact; the instruction accumulates in fp32.
+// MXFP4 grouped GEMM: the rows of A [M, K] are split into groups (per-expert
+// split_sizes, GroupedLinear); the rows of group g get C = A_g . B_g^T with
+// B_g [N, K] the group's weight. Both operands are in the rowwise MXFP4 layout
+// of the cast above (codes [rows, K/2], scales [rows, K/32]). One group is
+// the plain GEMM. Runs on gfx950's scaled MFMA with both operand formats set
+// to E2M1; every product of two E2M1 values is exact, the instruction
+// accumulates in fp32. M-tiles restart at each group's first row.
 //
 // Workgroup tile 256 x 256: four waves in 2 x 2, each 4 x 4 MFMA tiles of
 // 32 x 32 x 64 (128 x 128 fp32 accumulators in AGPRs). Operands are read through buffer resources, so rows past M
@@ -169,7 +172,7 @@ constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
 static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
 
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
-                                                       const uint8_t* bs, int64_t M, int64_t N, int64_t K,
+                                                       const uint8_t* bs, Fp4Groups gr, int64_t N, int64_t K,
                                                        int64_t n_tiles_n, void* c, int32_t c_f32) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
@@ -180,13 +183,22 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
-  const int64_t am0 = mt * TM, bn0 = nt * TN;
-  const int64_t amv = min<int64_t>(TM, M - am0), bnv = min<int64_t>(TN, N - bn0);
+  // group of m-tile mt: the last group whose first m-tile is <= mt (empty
+  // groups own no m-tile)
+  int lo = 0, hi = gr.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gr.tile0[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int64_t row_end = gr.row0[g + 1];     // rows of the group end here
+  const int64_t am0 = gr.row0[g] + (mt - gr.tile0[g]) * TM, bn0 = nt * TN;
+  const int64_t amv = min<int64_t>(TM, row_end - am0), bnv = min<int64_t>(TN, N - bn0);
   const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
   const __amdgpu_buffer_rsrc_t ra = fp4_rsrc(a + am0 * ldq, amv * ldq);
-  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + bn0 * ldq, bnv * ldq);
+  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + (g * N + bn0) * ldq, bnv * ldq);
   const __amdgpu_buffer_rsrc_t rsa = fp4_rsrc(as + am0 * lds, amv * lds);
-  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + bn0 * lds, bnv * lds);
+  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + (g * N + bn0) * lds, bnv * lds);
   const int ksteps = (int)(K / 64), ktiles = (ksteps + 3) / 4;
   const bool sc_dword = (lds & 7) == 0;       // a row's 8 scales of a k-tile: one aligned 8-byte load
 
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
     const int64_t row = m0 + 32 * i + l32;
-    if (row >= M) continue;
+    if (row >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
@@ -333,11 +345,11 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   }
 }
 
-hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
-                           int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
-  const int64_t tm = (M + kFp4GemmTileM - 1) / kFp4GemmTileM, tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
+hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
+  const int64_t tm = gr.tile0[gr.n], tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
   if (tm * tn == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_fp4_kernel, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, M, N, K, tn, c,
+  hipLaunchKernelGGL(gemm_fp4_kernel, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, gr, N, K, tn, c,
                      c_f32);
   return hipGetLastError();
 }

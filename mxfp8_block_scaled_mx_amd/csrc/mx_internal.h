@@ -160,11 +160,17 @@ hipError_t launch_moe_combine(const void* y_perm, const int32_t* perm, int64_t t
 // Rowwise MXFP4 cast (mx_fp4.hip).
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
                                uint8_t* s_col, hipStream_t stream);
-// MXFP4 GEMM C = A . B^T (mx_fp4.hip): kFp4GemmTileM x kFp4GemmTileN tiles,
-// c_f32 selects fp32 (else bf16) output.
+// MXFP4 grouped GEMM C_g = A_g . B_g^T (mx_fp4.hip): kFp4GemmTileM x
+// kFp4GemmTileN tiles, m-tiles restarting at each group; c_f32 selects fp32
+// (else bf16) output.
 constexpr int kFp4GemmTileM = 256, kFp4GemmTileN = 256;
-hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
-                           int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
+struct Fp4Groups {
+  int32_t n;                         // groups
+  int32_t tile0[kMaxGroups + 1];     // first m-tile of group g; tile0[n] = all m-tiles
+  int64_t row0[kMaxGroups + 1];      // first row of group g; row0[n] = M
+};
+hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;

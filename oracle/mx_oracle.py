@@ -78,7 +78,7 @@ __all__ = [
     "dequantize_rowwise", "padded_sizes", "quantize_colwise", "gemm_group_m",
     "gemm_group_k", "round_to_bf16", "sigmoid", "silu", "mlp_forward",
     "moe_dispatch", "moe_combine", "e2m1_value", "e2m1_encode", "quantize_rowwise_fp4",
-    "dequantize_rowwise_fp4", "gemm_fp4", "E2M1_VALUES",
+    "dequantize_rowwise_fp4", "gemm_fp4", "gemm_fp4_grouped", "E2M1_VALUES",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
     "mlp_backward_wgrad_entries",
 ]
@@ -659,3 +659,19 @@ def gemm_fp4(a_q, a_s, b_q, b_s):
     2^(scale code - 127)), then one matmul. The GEMM of the 4-bit MX runs
     ("examples/llama: default-on fusion & DP-comm perf toggles")."""
     return dequantize_rowwise_fp4(a_q, a_s) @ dequantize_rowwise_fp4(b_q, b_s).T
+
+
+def gemm_fp4_grouped(a_q, a_s, b_q, b_s, sizes):
+    """GroupedLinear at MXFP4 (R15 per group): the rows of A split into
+    consecutive groups of sizes[g] rows ("Efficient MoE training for
+    biological foundation models", Key technical approaches item 1); group g's
+    rows times B_g^T, b_q [G, n, k/2]. Returns float64 [sum(sizes), n]."""
+    sizes = [int(v) for v in sizes]
+    G, n = b_q.shape[0], b_q.shape[1]
+    C = np.zeros((sum(sizes), n))
+    r0 = 0
+    for g in range(G):
+        if sizes[g]:
+            C[r0:r0 + sizes[g]] = gemm_fp4(a_q[r0:r0 + sizes[g]], a_s[r0:r0 + sizes[g]], b_q[g], b_s[g])
+        r0 += sizes[g]
+    return C

@@ -206,3 +206,18 @@ def test_gemm_fp4_errors(L):
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, ctypes.c_void_p(0x100008), 0, None) == EALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 1 << 27, FAKE, 0, None) == EUNSUPPORTED
     assert g(None, None, None, None, 0, 4, 64, None, 0, None) == OK             # empty: no-op
+
+
+def test_grouped_gemm_fp4_errors(L):
+    g = L.mx_grouped_gemm_fp4
+    sz = (ctypes.c_int64 * 3)(4, 0, 8)
+    neg = (ctypes.c_int64 * 2)(4, -1)
+    assert g(FAKE, FAKE, FAKE, FAKE, sz, 0, 4, 64, FAKE, 0, None) == EINVAL      # no groups
+    assert g(FAKE, FAKE, FAKE, FAKE, sz, 129, 4, 64, FAKE, 0, None) == EINVAL    # > MX_MAX_GROUPS
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 3, 4, 64, FAKE, 0, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, neg, 2, 4, 64, FAKE, 0, None) == ESHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, sz, 3, 4, 32, FAKE, 0, None) == ESHAPE     # k % 64
+    assert g(FAKE, FAKE, None, FAKE, sz, 3, 4, 64, FAKE, 0, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, sz, 3, 4, 64, ctypes.c_void_p(0x100008), 1, None) == EALIGN
+    zero = (ctypes.c_int64 * 2)(0, 0)
+    assert g(None, None, None, None, zero, 2, 4, 64, None, 0, None) == OK        # no rows: no-op

@@ -184,3 +184,43 @@ def test_gemm_fp4_full_size_sampled(gpu_lib):
     want = A @ B.T
     bound = mfma_gemm_bound(A, B) + 2.0 ** -8 * np.abs(want)
     assert np.all(np.abs(got - want) <= bound)
+
+
+@pytest.mark.parametrize("sizes", [[300, 0, 1, 257, 64], [0, 513], [17]])
+def test_grouped_gemm_fp4_exact(gpu_lib, sizes):
+    # GroupedLinear at MXFP4: ragged groups (an empty one, a single row, tails
+    # inside a 256-row tile), per-group weights; exact regime as above, fp32
+    # out, canaries around C
+    rng = np.random.default_rng(3000 + len(sizes))
+    m, n, k, G = sum(sizes), 200, 256, len(sizes)
+    aq, as_ = _fp4_operand(rng, m, k, 126, 128)
+    bq = rng.integers(0, 256, size=(G, n, k // 2), dtype=np.uint8)
+    bs = rng.integers(126, 129, size=(G, n, k // 32), dtype=np.uint8)
+    buf, c = guarded((m, n), torch.float32)
+    gpu_lib.mx_grouped_gemm_fp4(dev_u8(aq), dev_u8(as_), dev_u8(bq), dev_u8(bs), sizes, out=c)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf), "mx_grouped_gemm_fp4 wrote outside C"
+    want = orc.gemm_fp4_grouped(aq, as_, bq, bs, sizes)
+    assert np.array_equal(to_np(c), want)
+
+
+def test_grouped_gemm_fp4_mixtral_sampled(gpu_lib):
+    # the Mixtral MLP's first GEMM at MXFP4: 8192 routed rows over 8 experts
+    # (ragged), n = 28672, k = 4096, bf16 out; sampled rows of every expert
+    rng = np.random.default_rng(78)
+    sizes = [157, 574, 1914, 3333, 1056, 506, 71, 581]
+    m, n, k, G = sum(sizes), 28672, 4096, len(sizes)
+    aq, as_ = _fp4_operand(rng, m, k, 122, 132)
+    bq = rng.integers(0, 256, size=(G, n, k // 2), dtype=np.uint8)
+    bs = rng.integers(122, 133, size=(G, n, k // 32), dtype=np.uint8)
+    c = gpu_lib.mx_grouped_gemm_fp4(dev_u8(aq), dev_u8(as_), dev_u8(bq), dev_u8(bs), sizes)
+    torch.cuda.synchronize()
+    row0 = np.concatenate([[0], np.cumsum(sizes)])
+    cols = np.sort(rng.choice(n, 128, replace=False))
+    for g in range(G):
+        rows = np.unique(np.concatenate([[row0[g], row0[g + 1] - 1], rng.integers(row0[g], row0[g + 1], 4)]))
+        got = to_np(c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+        A = orc.dequantize_rowwise_fp4(aq[rows], as_[rows])
+        B = orc.dequantize_rowwise_fp4(bq[g][cols], bs[g][cols])
+        want = A @ B.T
+        assert np.all(np.abs(got - want) <= mfma_gemm_bound(A, B) + 2.0 ** -8 * np.abs(want)), f"expert {g}"

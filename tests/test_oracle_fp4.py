@@ -142,3 +142,26 @@ def test_gemm_fp4_matches_blockwise_sum():
                 dot = int(np.dot(ai[i, 32 * b:32 * b + 32], bi[j, 32 * b:32 * b + 32]))
                 want[i, j] += dot * 2.0 ** (int(as_[i, b]) + int(bs[j, b]) - 254 - 2)
     assert np.array_equal(orc.gemm_fp4(aq, as_, bq, bs), want)
+
+
+def test_gemm_fp4_grouped_reduces_to_dense_and_routes_rows():
+    # groups of one shared weight equal the dense GEMM; with per-group
+    # constant weights w_g each output row carries its own group's w_g, so a
+    # row credited to the wrong group (or an empty group taking rows) fails
+    rng = np.random.default_rng(11)
+    sizes = [3, 0, 5, 1, 0]
+    m, n, k = sum(sizes), 4, 64
+    aq = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    as_ = rng.integers(124, 131, size=(m, k // 32), dtype=np.uint8)
+    bq1 = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    bs1 = rng.integers(124, 131, size=(n, k // 32), dtype=np.uint8)
+    G = len(sizes)
+    same = orc.gemm_fp4_grouped(aq, as_, np.stack([bq1] * G), np.stack([bs1] * G), sizes)
+    assert np.array_equal(same, orc.gemm_fp4(aq, as_, bq1, bs1))
+    # B_g all ones times 2^g: C[r, j] = 2^g(r) * sum_k A[r, k]
+    bq = np.full((G, n, k // 2), 0x22, dtype=np.uint8)
+    bs = np.stack([np.full((n, k // 32), 127 + g, dtype=np.uint8) for g in range(G)])
+    C = orc.gemm_fp4_grouped(aq, as_, bq, bs, sizes)
+    rowsum = orc.dequantize_rowwise_fp4(aq, as_).sum(axis=1)
+    owner = np.repeat(np.arange(G), sizes)
+    assert np.array_equal(C, (rowsum * 2.0 ** owner)[:, None] * np.ones((1, n)))
