@@ -221,3 +221,20 @@ def test_grouped_gemm_fp4_errors(L):
     assert g(FAKE, FAKE, FAKE, FAKE, sz, 3, 4, 64, ctypes.c_void_p(0x100008), 1, None) == EALIGN
     zero = (ctypes.c_int64 * 2)(0, 0)
     assert g(None, None, None, None, zero, 2, 4, 64, None, 0, None) == OK        # no rows: no-op
+
+
+def test_fp4_gemm_wrappers_reject_mismatched_shapes():
+    # the C ABI takes plain pointers; the binding checks the operand shapes
+    # before any call, so a narrower B can never be read past its end
+    import torch
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mx.mx_gemm_fp4(u8(4, 32), u8(4, 2), u8(8, 16), u8(8, 1))          # B narrower than A
+    with pytest.raises(ValueError):
+        mx.mx_gemm_fp4(u8(4, 32), u8(4, 1), u8(8, 32), u8(8, 2))          # A scales too short
+    with pytest.raises(ValueError):
+        mx.mx_gemm_fp4(u8(4, 32), u8(4, 2), u8(8, 32), u8(8, 2), out=torch.zeros(4, 7))
+    with pytest.raises(ValueError):
+        mx.mx_grouped_gemm_fp4(u8(5, 32), u8(5, 2), u8(2, 8, 32), u8(2, 8, 2), [2, 2])   # sizes != rows
+    with pytest.raises(ValueError):
+        mx.mx_grouped_gemm_fp4(u8(4, 32), u8(4, 2), u8(3, 8, 32), u8(3, 8, 2), [2, 2])   # groups != weights
