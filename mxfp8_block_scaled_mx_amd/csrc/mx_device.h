@@ -107,6 +107,28 @@ __device__ __forceinline__ float vgpr_hop(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xE4, 0xF, 0xF, false));
 }
 
+// ---- buffer resources and LDS DMA
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and never fault, which replaces per-lane row clamping at tile edges.
+// Every field is made wave-uniform explicitly so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0xFFFFFFFFll;
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
+}
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) (resp. vmcnt(1)) with
+// expcnt/lgkmcnt left open; issued through the builtin so the compiler's own
+// waitcnt tracking knows the loads (and buffer->LDS DMA) have landed.
+[[maybe_unused]] constexpr int kWaitVmcnt0 = 0x0F70;
+[[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
+
 // Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps
 // register-array indices constant however large the body is.
 template <int I, int N, typename Fn>

@@ -147,26 +147,12 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
 // registers, in memory order; its scale register scales that block. (The FP8
 // operand splits each lane's 32 values into two 16-value halves instead.)
 
-// buffer resource over [base, base + bytes), all fields wave-uniform
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t fp4_rsrc(const void* base, int64_t bytes) {
-  const uint32_t n = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes)));
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), (short)0, (int)n,
-                                           0x00020000);
-}
-
 // A k-tile is 256 values (128 bytes of codes) of every row of the workgroup
 // tile; A and B k-tiles are staged in LDS, double-buffered, by buffer->LDS DMA
 // (8 lanes per 128-byte row), with 16-byte chunk c of row r at chunk
 // c ^ (r & 7) so that fragment reads (32 rows, one chunk) spread over the LDS
 // banks. One barrier per k-tile: the next k-tile's DMA is in flight during
 // this one's MFMAs.
-typedef __attribute__((address_space(3))) void fp4_lds_void;
-// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left open
-constexpr int kF4WaitVmcnt0 = 0x0F70;
 constexpr int kF4SubM = 4, kF4SubN = 4;     // wave tile: MFMA tiles of 32 x 32
 constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
 static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
@@ -195,10 +181,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int64_t am0 = gr.row0[g] + (mt - gr.tile0[g]) * TM, bn0 = nt * TN;
   const int64_t amv = min<int64_t>(TM, row_end - am0), bnv = min<int64_t>(TN, N - bn0);
   const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
-  const __amdgpu_buffer_rsrc_t ra = fp4_rsrc(a + am0 * ldq, amv * ldq);
-  const __amdgpu_buffer_rsrc_t rb = fp4_rsrc(b + (g * N + bn0) * ldq, bnv * ldq);
-  const __amdgpu_buffer_rsrc_t rsa = fp4_rsrc(as + am0 * lds, amv * lds);
-  const __amdgpu_buffer_rsrc_t rsb = fp4_rsrc(bs + (g * N + bn0) * lds, bnv * lds);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + am0 * ldq, amv * ldq);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + (g * N + bn0) * ldq, bnv * ldq);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds, amv * lds);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + (g * N + bn0) * lds, bnv * lds);
   const int ksteps = (int)(K / 64), ktiles = (ksteps + 3) / 4;
   const bool sc_dword = (lds & 7) == 0;       // a row's 8 scales of a k-tile: one aligned 8-byte load
 
@@ -212,13 +198,13 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
     for (int p = 0; p < TM / 32; ++p) {
       const int blk = 4 * p + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (fp4_lds_void*)(&sA[buf][blk * 1024]), 16, dma_off,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(&sA[buf][blk * 1024]), 16, dma_off,
                                                (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < TN / 32; ++p) {
       const int blk = 4 * p + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (fp4_lds_void*)(&sB[buf][blk * 1024]), 16, dma_off,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(&sB[buf][blk * 1024]), 16, dma_off,
                                                (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
   };
@@ -264,7 +250,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   u32x2 nsa[SM], nsb[SN];
   dma_tile(0, 0);
   load_scales(0, sca, scb);
-  __builtin_amdgcn_s_waitcnt(kF4WaitVmcnt0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   for (int t = 0; t < ktiles; ++t) {
     const int buf = t & 1;
@@ -295,7 +281,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       }
     }
     if (more) {
-      __builtin_amdgcn_s_waitcnt(kF4WaitVmcnt0);   // this wave's DMA and scales landed
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's DMA and scales landed
 #pragma unroll
       for (int i = 0; i < SM; ++i) sca[i] = nsa[i];
 #pragma unroll

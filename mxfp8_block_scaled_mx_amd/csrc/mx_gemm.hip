@@ -64,11 +64,6 @@ constexpr int kThreads = 64 * kWaves;
 // group-K (wgrad), measured faster there (wgrad1 of the Mixtral-shaped
 // backward 1.99 -> 1.90 ms) while slower for group-M
 __host__ __device__ constexpr int band_m(int mode) { return mode == MX_GROUP_K ? 4 : 8; }
-// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left
-// open; issued through the builtin so the compiler's own waitcnt tracking
-// knows the loads have landed.
-[[maybe_unused]] constexpr int kWaitVmcnt0 = 0x0F70;
-[[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
 // L2 prefetch distance in k-steps (see kstep)
 [[maybe_unused]] constexpr int kPrefetchAhead = 3;
 // Epilogue transpose area of a 32 x 32 fp32 block in a wave's LDS slice:
@@ -140,21 +135,6 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmGroups& gt, int id, i
   t.mt = band_m0 + in_band % band_h;
   t.nt = in_band / band_h;
   return t;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0
-// and never fault, which replaces per-lane row clamping at tile edges.
-// Every field is made wave-uniform explicitly so the descriptor lives in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t cap = 0xFFFFFFFFll;
-  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, 0x00020000);
 }
 
 // Scale sources: per-lane byte loads (any layout), per-lane dword loads (row
