@@ -68,12 +68,15 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
 // 64-column tile in LDS (rows loaded as coalesced 16-byte pieces); thread t
 // then takes column t % 64 and the 32-row block t / 64, reduces the block's
 // amax locally and stores its 16 code bytes as one piece of the column's run.
+// With q_row given, the same tile also yields the rowwise copy (thread t takes
+// row t / 2, 32-column block t % 2), so both layouts cost one read of x.
 constexpr int kFp4ColTileRows = 128, kFp4ColTileCols = 64;
 __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_t* x, int64_t rows, int64_t cols,
-                                                                   uint8_t* q, uint8_t* s) {
+                                                                   uint8_t* q, uint8_t* s, uint8_t* q_row,
+                                                                   uint8_t* s_row) {
   // [row][column] bf16 with a 2-element pad so that the column reads of a
   // wave (64 columns of one row) spread over the banks
-  __shared__ uint16_t tile[kFp4ColTileRows][kFp4ColTileCols + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kFp4ColTileRows][kFp4ColTileCols + 2];
   const int64_t n_ct = (cols + kFp4ColTileCols - 1) / kFp4ColTileCols;
   const int64_t r0 = (int64_t)(blockIdx.x / n_ct) * kFp4ColTileRows;
   const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * kFp4ColTileCols;
@@ -90,6 +93,35 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
     for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
   }
   __syncthreads();
+  if (q_row != nullptr) {
+    const int rr = tid >> 1, bb = tid & 1;
+    const int64_t row = r0 + rr, col = c0 + 32 * bb;
+    if (row < rows && col < cols) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t pair = *reinterpret_cast<const uint32_t*>(&tile[rr][32 * bb + 2 * i]);
+        v[2 * i] = bf16_lo(pair);
+        v[2 * i + 1] = bf16_hi(pair);
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
+      const uint32_t eb = am >> 23;
+      const uint32_t sc = eb > 2u ? eb - 2u : 0u;
+      const float inv = inv_scale_from_code(sc);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
+        w[i] = word;
+      }
+      *reinterpret_cast<uint4*>(q_row + row * (cols / 2) + col / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      s_row[row * (cols / 32) + col / 32] = (uint8_t)sc;
+    }
+  }
   const int c = tid % kFp4ColTileCols, rb = tid / kFp4ColTileCols;
   const int64_t col = c0 + c, row = r0 + 32 * rb;
   if (col >= cols || row >= rows) return;
@@ -117,7 +149,9 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
                                uint8_t* s_col, hipStream_t stream) {
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-  const int64_t blocks = q != nullptr ? rows * (cols / 32) : 0;
+  // both layouts: one pass (the columnwise kernel writes the rowwise pair too)
+  const bool fused = q != nullptr && q_col != nullptr;
+  const int64_t blocks = q != nullptr && !fused ? rows * (cols / 32) : 0;
   if (blocks > 0)
     hipLaunchKernelGGL(quantize_fp4_rowwise_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream,
                        xb, rows, cols, q, s);
@@ -125,7 +159,7 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
     const int64_t tiles = ((rows + kFp4ColTileRows - 1) / kFp4ColTileRows) *
                           ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows, cols,
-                       q_col, s_col);
+                       q_col, s_col, fused ? q : nullptr, fused ? s : nullptr);
   }
   return hipGetLastError();
 }

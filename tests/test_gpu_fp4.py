@@ -82,13 +82,18 @@ def test_fp4_colwise_is_rowwise_of_transpose(gpu_lib, rows, cols):
 
 
 def test_fp4_colwise_full_size_sampled(gpu_lib):
+    # both layouts in one call (one pass over x): sampled columns of the
+    # columnwise copy and sampled rows of the rowwise copy
     bits = wl.quantize_tensor_c2()
-    _, _, qc, sc = gpu_lib.mx_quantize_fp4(dev_bf16(bits), colwise=True)
+    q, s, qc, sc = gpu_lib.mx_quantize_fp4(dev_bf16(bits), colwise=True)
     torch.cuda.synchronize()
     cols = np.random.default_rng(2).choice(bits.shape[1], size=128, replace=False)
     wqc, wsc = orc.quantize_rowwise_fp4(orc.bf16_bits_to_f64(bits[:, cols]).T)
     assert np.array_equal(sc.cpu().numpy()[cols], wsc)
     assert np.array_equal(qc.cpu().numpy()[cols], wqc)
+    rows = np.random.default_rng(3).choice(bits.shape[0], size=256, replace=False)
+    wq, ws = orc.quantize_rowwise_fp4(orc.bf16_bits_to_f64(bits[rows]))
+    assert np.array_equal(s.cpu().numpy()[rows], ws) and np.array_equal(q.cpu().numpy()[rows], wq)
 
 
 # ---- MXFP4 GEMM (mx_gemm_fp4) against the oracle's gemm_fp4 on the same codes
