@@ -148,8 +148,10 @@ def quantize(x: torch.Tensor, group_sizes=None, rowwise: bool = True, colwise: b
 
     Rowwise: codes [rows, cols], scales [rows, cols/32]. Columnwise (with
     optional row groups): codes [cols, sumP], scales [cols, sumP/32]."""
+    if not (isinstance(x, torch.Tensor) and x.dtype in (torch.bfloat16, torch.float32) and x.dim() == 2
+            and x.is_contiguous() and x.is_cuda):
+        raise ValueError("quantize: x must be a contiguous 2-D bfloat16 or float32 CUDA tensor")
     L = load()
-    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
     dt = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}[x.dtype]
     rows, cols = x.shape
     dev = x.device
@@ -396,6 +398,9 @@ def mx_quantize_fp4(x: torch.Tensor, colwise: bool = False, stream=None):
     """MXFP4 of bf16 x [rows, cols]: (q [rows, cols/2], s [rows, cols/32]) rowwise
     (two codes per byte, element 2i in the low nibble), plus (q_col [cols,
     rows/2], s_col [cols, rows/32]) when colwise."""
+    if not (isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+            and x.is_cuda):
+        raise ValueError("mx_quantize_fp4: x must be a contiguous 2-D bfloat16 CUDA tensor")
     L = load()
     rows, cols = x.shape
     q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)

@@ -238,3 +238,19 @@ def test_fp4_gemm_wrappers_reject_mismatched_shapes():
         mx.mx_grouped_gemm_fp4(u8(5, 32), u8(5, 2), u8(2, 8, 32), u8(2, 8, 2), [2, 2])   # sizes != rows
     with pytest.raises(ValueError):
         mx.mx_grouped_gemm_fp4(u8(4, 32), u8(4, 2), u8(3, 8, 32), u8(3, 8, 2), [2, 2])   # groups != weights
+
+
+def test_cast_wrappers_reject_bad_inputs():
+    # a float32, strided, 1-D or host x would be read as packed bf16 from its
+    # data pointer; the bindings refuse it before any device call
+    import torch
+    bad = [torch.zeros(4, 64, dtype=torch.float32),                 # fp32 (FP4 cast takes bf16 only)
+           torch.zeros(64, 8, dtype=torch.bfloat16).t(),            # strided
+           torch.zeros(256, dtype=torch.bfloat16),                  # 1-D
+           torch.zeros(4, 64, dtype=torch.bfloat16)]                # host memory
+    for x in bad:
+        with pytest.raises(ValueError):
+            mx.mx_quantize_fp4(x)
+    for x in bad[1:] + [torch.zeros(4, 64, dtype=torch.float16)]:
+        with pytest.raises(ValueError):
+            mx.quantize(x)
