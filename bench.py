@@ -98,32 +98,96 @@ def traffic_from_profiles(workload, stage):
         return None
 
 
-def cpu_baseline(inputs, wl, rows_sample=256):
-    """The oracle (float64 numpy) on a bounded sample of the same workload: the
-    fwd+bwd of one expert restricted to its first rows_sample rows."""
+def oracle_sample(inp, wl, rows=256, ffn_cols=1024):
+    """A bounded slice of one MLP workload for timing the oracle: the first
+    `rows` routed rows of its largest expert and the first `ffn_cols` ffn
+    columns of that expert (gate rows [0, Fs), up rows [F, F + Fs) of W1, the
+    columns [0, Fs) of W2). The sliced MLP is the same computation at a
+    smaller F, so its algorithmic FLOP rate stands for the workload's."""
+    import numpy as np
+    split = inp["split_sizes"]
+    e = int(np.argmax(split))
+    r0 = int(split[:e].sum())
+    S = int(min(rows, split[e]))
+    F, Fs = wl.ffn, min(ffn_cols, wl.ffn)
+    w1 = inp["w1"][e]
+    out = {"x": inp["x"][r0:r0 + S].copy(), "probs": inp["probs"][r0:r0 + S].copy(),
+           "w1": np.ascontiguousarray(np.concatenate([w1[:Fs], w1[F:F + Fs]])[None]),
+           "w2": np.ascontiguousarray(inp["w2"][e][:, :Fs][None]), "rows": S, "ffn": Fs, "expert": e,
+           "hidden": wl.hidden}
+    if "dy" in inp:
+        out["dy"] = inp["dy"][r0:r0 + S].copy()
+    return out
+
+
+def cpu_baseline(samples, tiny, c2_rows, reps=3):
+    """The oracle (float64 numpy, per-expert loops) as it stands, timed on the
+    host: median of `reps` wall times per configuration, on all BLAS threads;
+    the tiny MoE forward and the quantize sample also on one thread.
+
+    samples: oracle_sample() slices of the Llama dense forward, the
+    Mixtral-shaped forward and the Mixtral-shaped forward+backward; tiny: the
+    whole tiny MoE workload; c2_rows: the first rows of the 16384 x 4096
+    quantize tensor (bf16 bits), both layouts."""
     import numpy as np
     import oracle as orc
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    split = inputs["split_sizes"]
-    e = int(np.argmax(split))
-    r0 = int(split[:e].sum())
-    S = int(min(rows_sample, split[e]))
-    sl = slice(r0, r0 + S)
-    x, dy, p = inputs["x"][sl], inputs["dy"][sl], inputs["probs"][sl]
-    w1, w2 = inputs["w1"][e:e + 1], inputs["w2"][e:e + 1]
-    t0 = time.perf_counter()
-    fwd = orc.mlp_forward(x, p, w1, w2, [S])
-    orc.mlp_backward(x, p, w1, w2, [S], dy, fwd)
-    dt = time.perf_counter() - t0
-    flops = 18.0 * S * wl.hidden * wl.ffn
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fwd+bwd of expert {e} on its first {S} routed rows (H={wl.hidden}, F={wl.ffn}), "
-                      f"{flops / 1e12:.3f} TFLOP in {dt:.1f} s",
-            "seconds": dt}
+    except Exception:                              # threadpoolctl missing: report the core count
+        threadpool_limits, threads = None, os.cpu_count()
+
+    def med(fn):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def single(fn):
+        if threadpool_limits is None:
+            return None
+        with threadpool_limits(limits=1):
+            return med(fn)
+
+    res = {}
+    # tiny MoE MLP forward, whole workload
+    fl = 6.0 * tiny["x"].shape[0] * tiny["w1"].shape[2] * (tiny["w1"].shape[1] // 2)
+    f1 = lambda: orc.mlp_forward(tiny["x"], tiny["probs"], tiny["w1"], tiny["w2"], tiny["split_sizes"])
+    t, t1 = med(f1), single(f1)
+    res["tiny_moe_fwd"] = {"sample": "whole workload (512 routed rows, 4 experts, H=256, F=512)",
+                           "seconds": round(t, 4), "gflops": round(fl / t / 1e9, 3),
+                           "single_thread_seconds": None if t1 is None else round(t1, 4),
+                           "single_thread_gflops": None if t1 is None else round(fl / t1 / 1e9, 3)}
+    # standalone quantize, both layouts
+    nb = c2_rows.shape[0] * c2_rows.shape[1] * (2 + 2 * (1 + 1 / 32))
+    xq = orc.bf16_bits_to_f64(c2_rows)
+    f2 = lambda: (orc.quantize_rowwise(xq), orc.quantize_colwise(xq))
+    t, t1 = med(f2), single(f2)
+    res["quantize_16384x4096"] = {"sample": f"rows 0..{c2_rows.shape[0] - 1} of the tensor, both layouts",
+                                  "seconds": round(t, 4), "gbps": round(nb / t / 1e9, 4),
+                                  "single_thread_seconds": None if t1 is None else round(t1, 4),
+                                  "single_thread_gbps": None if t1 is None else round(nb / t1 / 1e9, 4)}
+    for name, smp in samples.items():
+        S, H, Fs = smp["rows"], smp["hidden"], smp["ffn"]
+        bwd = "dy" in smp
+
+        def fn(smp=smp, bwd=bwd):
+            f = orc.mlp_forward(smp["x"], smp["probs"], smp["w1"], smp["w2"], [smp["rows"]])
+            if bwd:
+                orc.mlp_backward(smp["x"], smp["probs"], smp["w1"], smp["w2"], [smp["rows"]], smp["dy"], f)
+
+        fl = (18.0 if bwd else 6.0) * S * H * Fs
+        t = med(fn)
+        res[name] = {"sample": f"{'fwd+bwd' if bwd else 'fwd'} of expert {smp['expert']} on its first {S} "
+                               f"routed rows, H={H}, ffn columns 0..{Fs - 1}",
+                     "seconds": round(t, 4), "gflops": round(fl / t / 1e9, 3)}
+    head = res["mixtral_moe_fwd_bwd"]
+    return {"value": round(head["gflops"] / 1e3, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": head["sample"] + f" (median of {reps}); per-configuration samples under 'configs'",
+            "configs": res}
 
 
 def main():
@@ -140,6 +204,8 @@ def main():
     ap.add_argument("--no-gemm-fp4", action="store_true", help="skip the MXFP4 GEMM")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward-only Llama dense and Mixtral-shaped workloads")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="only time the standalone 16384 x 4096 quantize (for profiling it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of a known size (reference for HBM counters)")
     args = ap.parse_args()
@@ -160,6 +226,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(torch, dev)
+        return
+    if args.quantize_only:
+        q, _ = measure_quantize(mx, torch, np, wlmod, dev)
+        print(json.dumps({"quantize": q}), flush=True)
         return
     wl = wlmod.WORKLOADS[args.workload]
     if not wl.backward:
@@ -199,13 +269,20 @@ def main():
         for e in evs:
             e.record()
     log(f"timing {args.steps} steps")
+    # one event before each step and one after the last, on the launch stream
+    ev_step = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in ev_step:
+        e.record()
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        ev_step[i].record()
         step()
+    ev_step[args.steps].record()
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    per_step = [ev_step[i].elapsed_time(ev_step[i + 1]) for i in range(args.steps)]
     # per-stage times: the same steps with stage events set, which runs every
     # stage on the launch stream in order (no side-stream overlap)
     log(f"timing {args.steps} steps stage by stage")
@@ -262,6 +339,10 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.tokens, "topk": wl.topk, "experts": E,
                    "rows": R, "hidden": H, "ffn": F, "split_sizes": split,
                    "step": "grouped_mlp_fwd(training) + grouped_mlp_bwd(fp32 wgrad accumulate)"},
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(float(np.median(per_step)), 4),
+                    "min": round(float(np.min(per_step)), 4), "max": round(float(np.max(per_step)), 4),
+                    "timing": "HIP events on the launch stream: one pair around the timed steps (mean) and "
+                              "one event between consecutive steps (median, min, max)"},
         "serial_ms_per_step": round(serial_ms, 4),
         "gemm_only": {"tflops": round(gemm_tflops, 1),
                       "frac_mfma_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "ms": round(gemm_ms, 4)},
@@ -286,8 +367,9 @@ def main():
     if not args.no_qinit:
         measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step_flops, out, torch)
 
+    samples, c2_rows = {}, None
     if not args.no_quantize:
-        out["quantize"] = measure_quantize(mx, torch, np, wlmod, dev)
+        out["quantize"], c2_rows = measure_quantize(mx, torch, np, wlmod, dev)
         f4 = out["quantize"]["fp4_rowwise"]
         log(f"quantize {out['quantize']['gbps']:.0f} GB/s; MXFP4 rowwise {f4['gbps']:.0f} GB/s, "
             f"both layouts {f4['both_layouts_gbps']:.0f} GB/s")
@@ -312,15 +394,23 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_forward:
         out["forward_only"] = {}
-        for name in ("llama8b_dense_fwd", "mixtral_moe_fwd"):
-            r = measure_forward(mx, torch, np, wlmod, dev, wlmod.WORKLOADS[name], args.steps, args.warmup)
+        for name in ("tiny_moe_fwd", "llama8b_dense_fwd", "mixtral_moe_fwd"):
+            r = measure_forward(mx, torch, np, wlmod, dev, wlmod.WORKLOADS[name], args.steps, args.warmup,
+                                samples if not args.no_cpu_baseline else None)
             out["forward_only"][name] = r
             log(f"{name}: forward {r['ms']:.3f} ms -> {r['tflops']:.1f} TFLOP/s; "
                 f"cached weights {r['qinit_style_ms']:.3f} ms -> {r['qinit_style_tflops']:.1f} TFLOP/s")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(inp, wl)
+        log("timing the CPU oracle on bounded samples")
+        samples[wl.name] = oracle_sample(inp, wl)
+        for name in ("llama8b_dense_fwd", "mixtral_moe_fwd"):
+            if name not in samples:
+                samples[name] = oracle_sample(wlmod.make_mlp_inputs(wlmod.WORKLOADS[name]), wlmod.WORKLOADS[name])
+        if c2_rows is None:
+            c2_rows = wlmod.quantize_tensor_c2()[:1024].copy()
+        tiny = wlmod.make_mlp_inputs(wlmod.WORKLOADS["tiny_moe_fwd"])
+        out["cpu_baseline"] = cpu_baseline(samples, tiny, c2_rows)
         log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
 
@@ -473,7 +563,7 @@ def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096, ffn=14
     return out
 
 
-def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup):
+def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup, samples=None):
     """Inference forward (grouped_mlp_fwd without a saved buffer: quantize X
     and the weights rowwise, GEMM1 + SwiGLU epilogue, GEMM2) on a forward-only
     workload, then the same with the weights cast once into the weight cache
@@ -481,6 +571,8 @@ def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup):
     6 R H F."""
     log(f"generating inputs for {wl.name} (seed {wl.seed})")
     inp = wlmod.make_mlp_inputs(wl)
+    if samples is not None and wl.name != "tiny_moe_fwd":
+        samples[wl.name] = oracle_sample(inp, wl)
 
     def to_dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -582,6 +674,7 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
     rotating over 4 distinct 128 MiB inputs so re-reads cannot hit the 256 MB
     Infinity Cache. Algorithmic bytes: 2 read + 2 * (1 + 1/32) written per element."""
     bits = wlmod.quantize_tensor_c2()
+    first_rows = bits[:1024].copy()
     rows, cols = bits.shape
     base = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     xs = [base.clone() for _ in range(copies)]
@@ -656,7 +749,7 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
             "fp4_rowwise": fp4,
             "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4)}}, first_rows
 
 
 if __name__ == "__main__":

@@ -174,6 +174,37 @@ MX_API mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split
                             size_t* fwd_workspace, size_t* saved, size_t* bwd_workspace);
 
 /*
+ * grouped_mlp_intermediates -- where the fused ops leave the intermediates
+ * they requantize inside the call: A = w*silu(g)*u of the forward epilogue
+ * and dH1 = [dg | du] of the backward epilogue (the intermediates the fused
+ * op keeps out of HBM in bf16/fp32 form, article item 3), plus the saved H1.
+ * All values are byte offsets into the buffers of one call with the same
+ * dims and split_sizes; they are valid after the call that writes them and
+ * until the buffer is reused:
+ *   forward workspace:  A rowwise codes [R, F] and scales;
+ *   saved:              H1 bf16 [R, 2F], A columnwise codes [F, sumP] and scales;
+ *   backward workspace: dH1 rowwise codes [R, 2F] and scales, dH1 columnwise
+ *                       codes [2F, sumP] and scales.
+ * Codes are in the public layouts above. Scales are k-tiled: the scales of a
+ * [rows, K] code matrix split K into steps of 128 columns numbered q, and
+ * the four block scales of row r in step q are the bytes
+ *     ((r / 32) * nq + q) * 128 + (r % 32) * 4 + {0, 1, 2, 3};
+ * rowwise: q = column / 128, nq = K / 128 (rows padded to a multiple of 32);
+ * columnwise: expert e's padded rows P_e are its own steps starting at
+ * q0_e = sum_{e' < e} ceil(P_e' / 128), nq = nq_col = q0_E, and the bytes of
+ * blocks past P_e in its last step are unspecified.
+ * Errors: as grouped_mlp_sizes; MX_EINVAL if out is NULL.
+ */
+typedef struct mx_mlp_intermediates {
+  size_t a_row_codes, a_row_scales;                        /* forward workspace */
+  size_t h1, a_col_codes, a_col_scales;                    /* saved */
+  size_t dh1_row_codes, dh1_row_scales, dh1_col_codes, dh1_col_scales;  /* backward workspace */
+  int64_t nq_col;
+} mx_mlp_intermediates;
+MX_API mx_status grouped_mlp_intermediates(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                           mx_mlp_intermediates* out);
+
+/*
  * grouped_mlp_fwd -- fused GroupedLinear -> ScaledSwiGLU -> GroupedLinear
  * forward (article item 3). For expert e and its rows X_e (routing weight w
  * per row):

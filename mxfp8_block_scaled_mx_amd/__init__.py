@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_sizes.restype = ctypes.c_int
     L.grouped_mlp_sizes.argtypes = [ctypes.POINTER(_Dims), p64, ctypes.POINTER(sz),
                                     ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.grouped_mlp_intermediates.restype = ctypes.c_int
+    L.grouped_mlp_intermediates.argtypes = [ctypes.POINTER(_Dims), p64, ctypes.c_void_p]
     L.grouped_mlp_fwd.restype = ctypes.c_int
     L.grouped_mlp_fwd.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     L.grouped_mlp_bwd.restype = ctypes.c_int
@@ -207,6 +209,23 @@ def mlp_sizes(E: int, R: int, H: int, F: int, split_sizes):
     _check(L.grouped_mlp_sizes(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes),
                                ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)))
     return f.value, s.value, b.value
+
+
+class _Intermediates(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "a_row_codes", "a_row_scales", "h1", "a_col_codes", "a_col_scales",
+        "dh1_row_codes", "dh1_row_scales", "dh1_col_codes", "dh1_col_scales")] + [("nq_col", ctypes.c_int64)]
+
+
+def mlp_intermediates(E: int, R: int, H: int, F: int, split_sizes) -> dict:
+    """Byte offsets of the requantized intermediates (A, dH1) and of H1 inside
+    the forward workspace, saved and backward workspace buffers, plus nq_col
+    (grouped_mlp_intermediates)."""
+    L = load()
+    out = _Intermediates()
+    _check(L.grouped_mlp_intermediates(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes),
+                                       ctypes.byref(out)))
+    return {n: int(getattr(out, n)) for n, _ in _Intermediates._fields_}
 
 
 class MLPState:

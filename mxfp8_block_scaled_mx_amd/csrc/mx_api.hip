@@ -552,6 +552,26 @@ mx_status grouped_mlp_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes,
   return MX_OK;
 }
 
+mx_status grouped_mlp_intermediates(const mx_mlp_dims* dims, const int64_t* split_sizes, mx_mlp_intermediates* out) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_intermediates";
+  if (!out) return fail(MX_EINVAL, "%s: out is null", who);
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  out->a_row_codes = L.aq;
+  out->a_row_scales = L.as;
+  out->h1 = L.h1;
+  out->a_col_codes = L.acq;
+  out->a_col_scales = L.acs;
+  out->dh1_row_codes = L.dhq;
+  out->dh1_row_scales = L.dhs;
+  out->dh1_col_codes = L.dhcq;
+  out->dh1_col_scales = L.dhcs;
+  out->nq_col = L.nq;
+  return MX_OK;
+}
+
 }  // extern "C"
 
 namespace {

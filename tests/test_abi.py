@@ -254,3 +254,30 @@ def test_cast_wrappers_reject_bad_inputs():
     for x in bad[1:] + [torch.zeros(4, 64, dtype=torch.float16)]:
         with pytest.raises(ValueError):
             mx.quantize(x)
+
+
+def test_mlp_intermediates_offsets(L):
+    # the intermediates lie inside the buffers grouped_mlp_sizes sizes, in
+    # disjoint regions large enough for their layouts
+    E, R, H, F = 3, 100, 256, 384
+    split = [37, 0, 63]
+    fws, sv, bws = mx.mlp_sizes(E, R, H, F, split)
+    o = mx.mlp_intermediates(E, R, H, F, split)
+    P = sum((m + 31) // 32 * 32 for m in split)
+    nq = sum(-(-((m + 31) // 32 * 32) // 128) for m in split)
+    assert o["nq_col"] == nq
+    R32 = -(-R // 32) * 32
+    regions = {
+        "fwd": [(o["a_row_codes"], R * F), (o["a_row_scales"], R32 * F // 32)],
+        "saved": [(o["h1"], R * 2 * F * 2), (o["a_col_codes"], F * P), (o["a_col_scales"], F // 32 * nq * 128)],
+        "bwd": [(o["dh1_row_codes"], R * 2 * F), (o["dh1_row_scales"], R32 * 2 * F // 32),
+                (o["dh1_col_codes"], 2 * F * P), (o["dh1_col_scales"], 2 * F // 32 * nq * 128)],
+    }
+    for key, total in (("fwd", fws), ("saved", sv), ("bwd", bws)):
+        spans = sorted(regions[key])
+        for (a, n), (b, _) in zip(spans, spans[1:]):
+            assert a + n <= b, key
+        assert all(a % 256 == 0 and a + n <= total for a, n in spans), key
+    with pytest.raises(mx.MXError):
+        mx.mlp_intermediates(E, R, H, F, [37, 0, 62])           # split does not sum to R
+    assert L.grouped_mlp_intermediates(ctypes.byref(_dims()), mx._i64_array([40, 24]), None) == EINVAL
