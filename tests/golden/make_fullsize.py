@@ -2,16 +2,18 @@
 
 For each full-size workload (inputs regenerated from the workload's seed by
 workloads.make_mlp_inputs) the oracle evaluates a sample of outputs it can
-compute one by one: Y at a few rows of two experts (the largest and the
-smallest non-empty one; the only one for a dense MLP) and, for a workload
-with a backward, dX and dprobs at the same rows and entries of those
-experts' dW1 and dW2 (from a zero start). The sample and the values go to
+compute one by one, for EVERY non-empty expert: Y at its first row, its last
+row, a row inside its last partial 32-row block (the block that the grouped
+columnwise layouts zero-pad) and one random row; for a workload with a
+backward, dX and dprobs at the same rows and entries of every non-empty
+expert's dW1 and dW2 (from a zero start; each expert's contraction runs over
+its own columnwise blocks). The sample and the values go to
 fullsize_<workload>.npz beside this script.
 
     python tests/golden/make_fullsize.py [workload ...]
 
 Each workload takes minutes of CPU (the exact float64 quantizer runs over
-whole expert weight matrices for the sampled rows).
+whole expert weight matrices for the sampled rows of every expert).
 """
 from __future__ import annotations
 
@@ -30,7 +32,6 @@ import oracle as orc  # noqa: E402
 import workloads as wl  # noqa: E402
 
 FULLSIZE = ("llama8b_dense_fwd", "mixtral_moe_fwd", "mixtral_moe_fwd_bwd")
-ROWS_PER_EXPERT = 3
 ENTRIES_PER_EXPERT = 24
 
 
@@ -45,15 +46,15 @@ def make(name: str) -> str:
     split = np.asarray(c["split_sizes"], dtype=np.int64)
     off = np.concatenate([[0], np.cumsum(split)])
     F, H = w.ffn, w.hidden
-    nonempty = [e for e in range(w.experts) if split[e] > 0]
-    experts = sorted({max(nonempty, key=lambda e: split[e]), min(nonempty, key=lambda e: split[e])})
+    experts = [e for e in range(w.experts) if split[e] > 0]
     rng = np.random.default_rng(1000 + w.seed)
     rows = []
     for e in experts:
         r0, r1 = int(off[e]), int(off[e + 1])
-        pick = {r0, r1 - 1}
-        while len(pick) < min(ROWS_PER_EXPERT, r1 - r0):
-            pick.add(int(rng.integers(r0, r1)))
+        pick = {r0, r1 - 1, int(rng.integers(r0, r1))}
+        m = r1 - r0
+        if m % 32:                                   # a row inside the last, partial 32-row block
+            pick.add(int(rng.integers(r0 + m // 32 * 32, r1)))
         rows += sorted(pick)
     rows = np.asarray(rows, dtype=np.int64)
     out = dict(workload=np.array(name), split=split, experts=np.asarray(experts, dtype=np.int64), rows=rows)
