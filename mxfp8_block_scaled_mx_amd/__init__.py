@@ -192,6 +192,22 @@ def grouped_gemm(mode: int, sizes, a_q, a_s, b_q, b_s, *, N: int, K: int, M: int
     cdt = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}[out.dtype]
     if c_group_stride is None:
         c_group_stride = M * N if mode == MX_GROUP_K else 0
+    # the extents the kernel reads and writes must lie inside the tensors
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (b_q, "b_q"), (b_s, "b_s")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError(f"grouped_gemm: {nm} must be a contiguous uint8 CUDA tensor")
+    if not out.is_cuda or not out.is_contiguous():
+        raise ValueError("grouped_gemm: out must be a contiguous CUDA tensor")
+    ldc = out.shape[-1]
+    # (row r of a [rows, ld] operand spans [r * ld, r * ld + K); scales 1/32 of that)
+    b_end = (G - 1) * b_group_stride + (N - 1) * ldb + K if mode == MX_GROUP_M else (N - 1) * ldb + K
+    need = {"a_q": (M - 1) * lda + K, "a_s": ((M - 1) * lda + K) // 32, "b_q": b_end, "b_s": b_end // 32,
+            "out": (M - 1) * ldc + N if mode == MX_GROUP_M else (G - 1) * c_group_stride + (M - 1) * ldc + N}
+    if M == 0:
+        need.update(a_q=0, a_s=0, out=0)
+    for t, nm in ((a_q, "a_q"), (a_s, "a_s"), (b_q, "b_q"), (b_s, "b_s"), (out, "out")):
+        if t.numel() < need[nm]:
+            raise ValueError(f"grouped_gemm: {nm} has {t.numel()} elements, the call addresses {need[nm]}")
     _check(L.mx_grouped_gemm(mode, G, _i64_array(sizes), M, N, K, _ptr(a_q), _ptr(a_s), lda,
                              _ptr(b_q), _ptr(b_s), ldb, b_group_stride, _ptr(out), cdt,
                              out.shape[-1], c_group_stride, int(accumulate), _stream(stream)))
@@ -237,6 +253,56 @@ class MLPState:
         self.split_sizes = list(int(s) for s in split_sizes)
 
 
+def _expect_all(items):
+    """items: (tensor or None, shape, dtype, name, optional). Raise ValueError
+    unless every given tensor has its shape and dtype (checked for all first)
+    and is a contiguous CUDA tensor. The C ABI takes plain pointers and trusts
+    the sizes it is given, so a tensor smaller than the dims would be read or
+    written past its end; the bindings check every buffer first."""
+    for t, shape, dtype, name, optional in items:
+        if t is None:
+            if not optional:
+                raise ValueError(f"{name} is required")
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a tensor")
+        want = tuple(int(v) for v in shape)
+        if tuple(t.shape) != want or t.dtype != dtype:
+            raise ValueError(f"{name}: expected {dtype} {want}, got {t.dtype} {tuple(t.shape)}")
+    for t, _, _, name, _ in items:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+
+
+def _expect(t, shape, dtype, name, optional=False):
+    _expect_all([(t, shape, dtype, name, optional)])
+
+
+def _mlp_items(E, R, H, F, x=None, w1=None, w2=None, probs=None, x_rows=None):
+    items = [(probs, (R,), torch.float32, "probs", True)]
+    if x is not None:
+        items.append((x, (R if x_rows is None else x_rows, H), torch.bfloat16, "x", False))
+    if w1 is not None:
+        items.append((w1, (E, 2 * F, H), torch.bfloat16, "w1", False))
+    if w2 is not None:
+        items.append((w2, (E, H, F), torch.bfloat16, "w2", False))
+    return items
+
+
+def _check_split(E, R, split_sizes):
+    if len(split_sizes) != E or sum(int(m) for m in split_sizes) != R:
+        raise ValueError(f"split_sizes {list(split_sizes)} must have {E} entries summing to {R}")
+
+
+def _mlp_inputs(E, R, H, F, split_sizes, x=None, w1=None, w2=None, probs=None, x_rows=None, extra=()):
+    _check_split(E, R, split_sizes)
+    _expect_all(_mlp_items(E, R, H, F, x, w1, w2, probs, x_rows) + list(extra))
+
+
+def _mlp_grads(E, R, H, F, dw1=None, dw2=None):
+    return [(dw1, (E, 2 * F, H), torch.float32, "dw1", True), (dw2, (E, H, F), torch.float32, "dw2", True)]
+
+
 def _byte_buffer(nbytes: int, device):
     # 256-byte aligned (the caching allocator aligns to at least 512 bytes)
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -247,9 +313,12 @@ def grouped_mlp_fwd(x, probs, w1, w2, split_sizes, *, training: bool = True, wor
     """Fused grouped MLP forward. x [R,H] bf16, w1 [E,2F,H] bf16, w2 [E,H,F] bf16,
     probs [R] fp32 or None. Returns (y [R,H] bf16, MLPState or None)."""
     L = load()
+    if x.dim() != 2 or w1.dim() != 3:
+        raise ValueError("grouped_mlp_fwd: x must be [R, H] and w1 [E, 2F, H]")
     R, H = x.shape
     E, F2, _ = w1.shape
     F = F2 // 2
+    _mlp_inputs(E, R, H, F, split_sizes, x, w1, w2, probs, extra=[(out, (R, H), torch.bfloat16, "out", True)])
     fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
     if workspace is None or workspace.numel() < fws:
         workspace = _byte_buffer(fws, x.device)
@@ -269,10 +338,15 @@ def grouped_mlp_fwd_gather(x_tokens, row_token, probs, w1, w2, split_sizes, *, t
     mx_moe_dispatch returns it; split_sizes its counts), gathered by the X
     cast itself. Returns (y [R,H] bf16, MLPState or None)."""
     L = load()
+    if x_tokens.dim() != 2 or w1.dim() != 3:
+        raise ValueError("grouped_mlp_fwd_gather: x_tokens must be [T, H] and w1 [E, 2F, H]")
     T, H = x_tokens.shape
     E, F2, _ = w1.shape
     F = F2 // 2
     R = int(sum(int(m) for m in split_sizes))
+    _mlp_inputs(E, R, H, F, split_sizes, x_tokens, w1, w2, probs, x_rows=T,
+                extra=[(row_token, (R,), torch.int32, "row_token", R == 0),
+                       (out, (R, H), torch.bfloat16, "out", True)])
     fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
     if workspace is None or workspace.numel() < fws:
         workspace = _byte_buffer(fws, x_tokens.device)
@@ -292,7 +366,12 @@ def grouped_mlp_bwd_gather(dy_tokens, row_token, probs, state: MLPState, *, dw1=
     by its cast. Returns (dx [R, H] bf16 per routed row, dprobs, dw1, dw2)."""
     L = load()
     E, R, H, F = state.dims
+    if dy_tokens.dim() != 2:
+        raise ValueError("grouped_mlp_bwd_gather: dy_tokens must be [T, H]")
     T = dy_tokens.shape[0]
+    _expect_all([(dy_tokens, (T, H), torch.bfloat16, "dy_tokens", False),
+                 (row_token, (R,), torch.int32, "row_token", R == 0),
+                 (probs, (R,), torch.float32, "probs", True)] + _mlp_grads(E, R, H, F, dw1, dw2))
     _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
     if workspace is None or workspace.numel() < bws:
         workspace = _byte_buffer(bws, dy_tokens.device)
@@ -317,6 +396,8 @@ def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulat
     With accumulate=True, dw1/dw2 (fp32 main grads) are added into."""
     L = load()
     E, R, H, F = state.dims
+    _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
+                + _mlp_grads(E, R, H, F, dw1, dw2))
     _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
     if workspace is None or workspace.numel() < bws:
         workspace = _byte_buffer(bws, dy.device)
@@ -356,8 +437,11 @@ def grouped_mlp_quantize_weights(w1, w2, cache: WeightCache | None = None, strea
     """Cast the bf16 master weights into `cache` (allocated when None); run
     once after each optimizer update, then use the *_cached calls."""
     L = load()
+    if w1.dim() != 3:
+        raise ValueError("grouped_mlp_quantize_weights: w1 must be [E, 2F, H]")
     E, F2, H = w1.shape
     F = F2 // 2
+    _expect_all([(w1, (E, 2 * F, H), torch.bfloat16, "w1", False), (w2, (E, H, F), torch.bfloat16, "w2", False)])
     if cache is None:
         cache = WeightCache(E, H, F, device=w1.device)
     if cache.ehf != (E, H, F):
@@ -371,10 +455,13 @@ def grouped_mlp_fwd_cached(x, probs, cache: WeightCache, split_sizes, *, trainin
                            workspace=None, out=None, stream=None):
     """grouped_mlp_fwd on the cached MXFP8 weights. Returns (y, MLPState or None)."""
     L = load()
+    if x.dim() != 2:
+        raise ValueError("grouped_mlp_fwd_cached: x must be [R, H]")
     R, H = x.shape
     E, Hc, F = cache.ehf
     if Hc != H:
         raise ValueError(f"x has hidden {H}, the weight cache {Hc}")
+    _mlp_inputs(E, R, H, F, split_sizes, x, probs=probs, extra=[(out, (R, H), torch.bfloat16, "out", True)])
     fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
     if workspace is None or workspace.numel() < fws:
         workspace = _byte_buffer(fws, x.device)
@@ -394,6 +481,8 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
     Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
     L = load()
     E, R, H, F = state.dims
+    _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
+                + _mlp_grads(E, R, H, F, dw1, dw2))
     _, _, bws = mlp_sizes(E, R, H, F, state.split_sizes)
     if workspace is None or workspace.numel() < bws:
         workspace = _byte_buffer(bws, dy.device)
@@ -483,8 +572,12 @@ def mx_moe_dispatch(x, topk_idx, topk_w, num_experts: int, stream=None, gather: 
     counts int64 [E]); the first counts.sum() routed rows are valid.
     gather=False: routing only (no row copy; x_perm is None)."""
     L = load()
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("mx_moe_dispatch: x must be [T, H] and topk_idx [T, k]")
     T, H = x.shape
     k = topk_idx.shape[1]
+    _expect_all([(x, (T, H), torch.bfloat16, "x", False), (topk_idx, (T, k), torch.int32, "topk_idx", False),
+                 (topk_w, (T, k), torch.float32, "topk_w", True)])
     dev = x.device
     x_perm = torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None
     probs_perm = torch.empty((T * k,), dtype=torch.float32, device=dev) if topk_w is not None else None
@@ -503,8 +596,16 @@ def mx_moe_combine(y_perm, perm, out=None, stream=None):
     """Token combine (mx_moe_combine): y [T, H] bf16, the fp32 sum of each
     token's routed rows, rounded once to bf16."""
     L = load()
+    if perm.dim() != 2 or y_perm.dim() != 2:
+        raise ValueError("mx_moe_combine: perm must be [T, k] and y_perm [rows, H]")
     T, k = perm.shape
     H = y_perm.shape[1]
+    # y_perm holds the routed rows: at most T * k (the rows perm points at)
+    if not 1 <= y_perm.shape[0] <= max(T * k, 1):
+        raise ValueError(f"mx_moe_combine: y_perm has {y_perm.shape[0]} rows, expected 1 .. {max(T * k, 1)}")
+    _expect_all([(perm, (T, k), torch.int32, "perm", False),
+                 (y_perm, (y_perm.shape[0], H), torch.bfloat16, "y_perm", False),
+                 (out, (T, H), torch.bfloat16, "out", True)])
     y = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device) if out is None else out
     _check(L.mx_moe_combine(_ptr(y_perm), _ptr(perm), T, H, k, _ptr(y), _stream(stream)))
     return y
@@ -550,8 +651,18 @@ class MLPRunner:
         self._c_dims = _dims(E, R, H, F)
         self._c_split = _i64_array(self.split)
 
+    def _inputs(self, x, probs, w1=None, w2=None):
+        E, R, H, F = self.dims
+        _mlp_inputs(E, R, H, F, self.split, x, w1, w2, probs)
+
+    def _grads(self, dy, probs, dw1, dw2):
+        E, R, H, F = self.dims
+        _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True),
+                     (dw1, (E, 2 * F, H), torch.float32, "dw1", False), (dw2, (E, H, F), torch.float32, "dw2", False)])
+
     def forward(self, x, probs, w1, w2, training=True, stream=None):
         L = load()
+        self._inputs(x, probs, w1, w2)
         saved = self.saved if training else None
         _check(L.grouped_mlp_fwd(ctypes.byref(self._c_dims), self._c_split, _ptr(x), _ptr(probs),
                                  _ptr(w1), _ptr(w2), _ptr(self.y), _ptr(saved),
@@ -569,6 +680,7 @@ class MLPRunner:
 
     def forward_cached(self, x, probs, training=True, stream=None):
         L = load()
+        self._inputs(x, probs)
         saved = self.saved if training else None
         _check(L.grouped_mlp_fwd_cached(ctypes.byref(self._c_dims), self._c_split, _ptr(x), _ptr(probs),
                                         _ptr(self.cache.buf), self.cache.buf.numel(), _ptr(self.y),
@@ -578,6 +690,7 @@ class MLPRunner:
 
     def backward_cached(self, dy, probs, dw1, dw2, accumulate=True, want_dprobs=True, stream=None):
         L = load()
+        self._grads(dy, probs, dw1, dw2)
         _check(L.grouped_mlp_bwd_cached(ctypes.byref(self._c_dims), self._c_split, _ptr(dy), _ptr(probs),
                                         _ptr(self.cache.buf), self.cache.buf.numel(), _ptr(self.saved),
                                         self.saved.numel(), _ptr(self.dx),
@@ -588,6 +701,7 @@ class MLPRunner:
 
     def backward(self, dy, probs, dw1, dw2, accumulate=True, want_dprobs=True, stream=None):
         L = load()
+        self._grads(dy, probs, dw1, dw2)
         _check(L.grouped_mlp_bwd(ctypes.byref(self._c_dims), self._c_split, _ptr(dy), _ptr(probs),
                                  _ptr(self.saved), self.saved.numel(), _ptr(self.dx),
                                  _ptr(self.dprobs) if want_dprobs else None, _ptr(dw1), _ptr(dw2),

@@ -221,8 +221,10 @@ mx_status gemm_plan(int32_t mode, int32_t G, const int64_t* sizes, int64_t M, in
   A.sa = mx::row_major_scales(lda);
   A.sb = mx::row_major_scales(ldb);
   A.as_bytes = M * (lda / 32);
-  // extent of the B scale array: all G groups in group-M, B itself in group-K
-  A.bs_bytes = mode == MX_GROUP_M ? ((int64_t)(G - 1) * b_group_stride + n_rows_b * ldb) / 32
+  // extent of the B scale array: up to the last valid scale of the last row
+  // of the last group in group-M (row r of group g spans K codes from
+  // g * b_group_stride + r * ldb), B itself in group-K
+  A.bs_bytes = mode == MX_GROUP_M ? ((int64_t)(G - 1) * b_group_stride + (n_rows_b - 1) * ldb + K) / 32
                                   : n_rows_b * (ldb / 32);
   A.c_group_stride = c_group_stride;
   A.M = (int32_t)M; A.N = (int32_t)N; A.K = (int32_t)K;

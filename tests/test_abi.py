@@ -281,3 +281,31 @@ def test_mlp_intermediates_offsets(L):
     with pytest.raises(mx.MXError):
         mx.mlp_intermediates(E, R, H, F, [37, 0, 62])           # split does not sum to R
     assert L.grouped_mlp_intermediates(ctypes.byref(_dims()), mx._i64_array([40, 24]), None) == EINVAL
+
+
+def test_mlp_bindings_reject_tensors_that_disagree_with_the_dims():
+    # the C ABI trusts the sizes it is given, so a smaller tensor would be read
+    # past its end; the bindings compare every tensor with the dims first
+    # (shapes and dtypes before the device, so these checks run on the CPU)
+    import torch
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    E, R, H, F = 2, 64, 256, 64
+    x, w1, w2 = bf(R, H), bf(E, 2 * F, H), bf(E, H, F)
+    with pytest.raises(ValueError, match="w1"):
+        mx.grouped_mlp_fwd(x, None, bf(E, H, 2 * F), w2, [32, 32])          # W1 given as [E, H, 2F]
+    with pytest.raises(ValueError, match="w2"):
+        mx.grouped_mlp_fwd(x, None, w1, bf(E, F, H), [32, 32])
+    with pytest.raises(ValueError, match="split_sizes"):
+        mx.grouped_mlp_fwd(x, None, w1, w2, [32, 31])
+    with pytest.raises(ValueError, match="probs"):
+        mx.grouped_mlp_fwd(x, torch.zeros(R + 1), w1, w2, [32, 32])
+    with pytest.raises(ValueError, match="CUDA"):
+        mx.grouped_mlp_fwd(x, None, w1, w2, [32, 32])                      # consistent, but host memory
+    with pytest.raises(ValueError, match="dy"):
+        mx.grouped_mlp_bwd(bf(R, H + 32), None, mx.MLPState(None, (E, R, H, F), [32, 32]))
+    with pytest.raises(ValueError, match="topk_idx"):
+        mx.mx_moe_dispatch(x, torch.zeros((R, 2), dtype=torch.int64), None, E)
+    with pytest.raises(ValueError, match="a_q"):
+        u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+        mx.grouped_gemm(mx.MX_GROUP_M, [64], u8(64, 128), u8(64, 4), u8(32, 128), u8(32, 4), N=32, K=128,
+                        out=torch.zeros((64, 32)))

@@ -25,7 +25,7 @@ import torch
 
 import oracle as orc
 import workloads as wl
-from tests.gpu_util import dev_bf16, dev_f32
+from tests.gpu_util import dev_bf16, dev_f32, mfma_gemm_bound
 
 pytestmark = pytest.mark.gpu
 MAX_RATE = 1e-3
@@ -109,7 +109,7 @@ def _compare(tag, q_gpu, s_gpu, q_ref, s_ref):
 def test_requantized_intermediates_match_oracle(gpu_lib, name):
     c = _inputs(name)
     split = [int(s) for s in c["split_sizes"]]
-    E, H, F2 = c["w1"].shape
+    E, F2, H = c["w1"].shape                      # W1 is [E, 2F, H]
     F = F2 // 2
     R = sum(split)
     print(f"[intermediates] {name}: E={E} R={R} H={H} F={F} split={split}", flush=True)
@@ -128,12 +128,22 @@ def test_requantized_intermediates_match_oracle(gpu_lib, name):
     fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split)
     bwd = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], split, c["dy"], fwd)
 
-    # saved H1 (bf16): equal, or one bf16 step apart where fp32 and float64 straddle a rounding point
+    # saved H1 (bf16): within the GEMM's own error bound plus one bf16
+    # rounding on each side (outputs that cancel to near zero keep the
+    # GEMM's absolute error, so a relative bf16 bar alone does not hold)
     h1_bits = _bytes(runner.saved, o["h1"], R * 2 * F * 2).view(np.uint16).reshape(R, 2 * F)
     h1_gpu = orc.bf16_bits_to_f64(h1_bits)
+    xh = orc.dequantize_rowwise(*orc.quantize_rowwise(orc.bf16_bits_to_f64(c["x"])))
+    off = np.concatenate([[0], np.cumsum(split)])
+    bound = np.zeros((R, 2 * F))
+    for e in range(E):
+        if split[e]:
+            w1h = orc.dequantize_rowwise(*orc.quantize_rowwise(orc.bf16_bits_to_f64(c["w1"][e])))
+            bound[off[e]:off[e + 1]] = mfma_gemm_bound(xh[off[e]:off[e + 1]], w1h)
     dh = np.abs(h1_gpu - fwd["h1_bf16"])
-    assert np.all(dh <= 2.0 ** -7 * np.abs(fwd["h1_bf16"]) + 1e-30), "H1 off by more than one bf16 step"
-    print(f"[intermediates] {name}: H1 bf16 mismatch rate {np.mean(dh > 0):.2e}", flush=True)
+    lim = bound + 2.0 ** -8 * (np.abs(fwd["h1"]) + np.abs(h1_gpu))
+    assert np.all(dh <= lim), f"H1 off by {float(np.max(dh / np.maximum(lim, 1e-300))):.2f}x the bound"
+    print(f"[intermediates] {name}: H1 bf16 differs at a rate of {np.mean(dh > 0):.2e}", flush=True)
 
     # A: rowwise [R, F] and grouped columnwise [F, sumP]
     a_q = _bytes(runner.fwd_ws, o["a_row_codes"], R * F).reshape(R, F)
