@@ -433,6 +433,28 @@ MX_API mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t
                                 int64_t hidden, int32_t topk, void* y, void* stream);
 
 /*
+ * mx_moe_dispatch_noalloc -- mx_moe_dispatch for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results without
+ * the workspace. Its scratch (the per-block expert histograms and row bases)
+ * is a library-owned array of 65536 int32 (256 KiB) per GPU, created with the
+ * library's device code and held until the process ends; the call allocates
+ * nothing. The caller still provides every input and output.
+ *   Limit: ceil(tokens * topk / 256) * num_experts + 1 <= 65536 (for example
+ *   16384 tokens, top-2 of 128 experts); larger requests return
+ *   MX_EUNSUPPORTED and enqueue nothing.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, different threads) race and must be ordered by
+ * the caller. The array needs no clearing between calls. Other errors as
+ * mx_moe_dispatch; MX_EHIP if the array's device address cannot be found.
+ */
+MX_API mx_status mx_moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, const float* topk_w,
+                                         int64_t tokens, int64_t hidden, int32_t topk,
+                                         int32_t num_experts, void* x_perm, float* probs_perm,
+                                         int32_t* perm, int32_t* row_token, int64_t* counts,
+                                         void* stream);
+
+/*
  * mx_set_stage_events -- optional per-stage timing of the fused MLP calls
  * (observability only; the results are the same). While events are set, the
  * fused MLP calls run every stage on the caller's stream in order, without

@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
     L.mx_moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
     L.mx_moe_dispatch.restype = ctypes.c_int
     L.mx_moe_dispatch.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.mx_moe_dispatch_noalloc.restype = ctypes.c_int
+    L.mx_moe_dispatch_noalloc.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
     L.mx_moe_combine.restype = ctypes.c_int
     L.mx_moe_combine.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     L.grouped_mlp_bwd_gather.restype = ctypes.c_int

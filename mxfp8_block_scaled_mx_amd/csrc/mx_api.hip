@@ -953,19 +953,24 @@ size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num
   return (size_t)((nblk * num_experts + 1) * 4);
 }
 
-mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* topk_w, int64_t tokens,
-                          int64_t hidden, int32_t topk, int32_t num_experts, void* x_perm, float* probs_perm,
-                          int32_t* perm, int32_t* row_token, int64_t* counts, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  const char* who = "mx_moe_dispatch";
+}  // extern "C"
+
+namespace {
+
+// Token dispatch after the size checks; workspace null = the library's
+// per-device scratch array (allocation-free variant).
+mx_status moe_dispatch_impl(const char* who, const void* x, const int32_t* topk_idx, const float* topk_w,
+                            int64_t tokens, int64_t hidden, int32_t topk, int32_t num_experts, void* x_perm,
+                            float* probs_perm, int32_t* perm, int32_t* row_token, int64_t* counts, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (tokens < 0 || hidden <= 0 || hidden % 8) return fail(MX_ESHAPE, "%s: need tokens >= 0 and hidden a positive multiple of 8", who);
   if (topk < 1 || topk > 64) return fail(MX_EINVAL, "%s: topk %d outside [1, 64]", who, topk);
   if (num_experts < 1 || num_experts > mx::kMaxGroups)
     return fail(MX_EUNSUPPORTED, "%s: %d experts outside [1, %d]", who, num_experts, mx::kMaxGroups);
   if (tokens * topk > kI32Max || tokens * hidden > ((int64_t)1 << 40))
     return fail(MX_EUNSUPPORTED, "%s: too many routed rows", who);
-  if (!counts || !workspace || (tokens > 0 && (!topk_idx || !perm || !row_token)))
+  const bool own_scratch = workspace == nullptr && workspace_bytes == SIZE_MAX;
+  if (!counts || (!workspace && !own_scratch) || (tokens > 0 && (!topk_idx || !perm || !row_token)))
     return fail(MX_EINVAL, "%s: null pointer argument", who);
   if ((x == nullptr) != (x_perm == nullptr))
     return fail(MX_EINVAL, "%s: x and x_perm must both be given or both be null (routing only)", who);
@@ -976,8 +981,19 @@ mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* t
       (probs_perm && !aligned(probs_perm, 4)))
     return fail(MX_EALIGN, "%s: x and x_perm must be 16-byte aligned, the index arrays 4-byte", who);
   const size_t need = mx_moe_dispatch_workspace_bytes(tokens, topk, num_experts);
-  if (workspace_bytes < need)
+  if (own_scratch) {
+    if (need > (size_t)mx::kDispatchScratchWords * 4)
+      return fail(MX_EUNSUPPORTED, "%s: %lld tokens x top-%d over %d experts need %zu bytes of scratch, above the "
+                  "allocation-free limit of %lld bytes (ceil(tokens*topk/256)*experts + 1 <= %lld)", who,
+                  (long long)tokens, topk, num_experts, need, (long long)mx::kDispatchScratchWords * 4,
+                  (long long)mx::kDispatchScratchWords);
+    int32_t* p = nullptr;
+    hipError_t e = mx::dispatch_scratch(&p);
+    if (e != hipSuccess) return hip_fail(e, "dispatch scratch address");
+    workspace = p;
+  } else if (workspace_bytes < need) {
     return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, need);
+  }
   mx::MoeDispatchArgs a;
   a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w;
   a.tokens = tokens; a.hidden = hidden; a.topk = topk; a.experts = num_experts;
@@ -986,6 +1002,29 @@ mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* t
   hipError_t e = mx::launch_moe_dispatch(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mx_moe_dispatch launch");
   return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_moe_dispatch(const void* x, const int32_t* topk_idx, const float* topk_w, int64_t tokens,
+                          int64_t hidden, int32_t topk, int32_t num_experts, void* x_perm, float* probs_perm,
+                          int32_t* perm, int32_t* row_token, int64_t* counts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (workspace == nullptr) return fail(MX_EINVAL, "mx_moe_dispatch: null pointer argument");
+  return moe_dispatch_impl("mx_moe_dispatch", x, topk_idx, topk_w, tokens, hidden, topk, num_experts, x_perm,
+                           probs_perm, perm, row_token, counts, workspace, workspace_bytes, stream);
+}
+
+mx_status mx_moe_dispatch_noalloc(const void* x, const int32_t* topk_idx, const float* topk_w, int64_t tokens,
+                                  int64_t hidden, int32_t topk, int32_t num_experts, void* x_perm,
+                                  float* probs_perm, int32_t* perm, int32_t* row_token, int64_t* counts,
+                                  void* stream) {
+  g_err[0] = 0;
+  return moe_dispatch_impl("mx_moe_dispatch_noalloc", x, topk_idx, topk_w, tokens, hidden, topk, num_experts,
+                           x_perm, probs_perm, perm, row_token, counts, nullptr, SIZE_MAX, stream);
 }
 
 mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens, int64_t hidden, int32_t topk,

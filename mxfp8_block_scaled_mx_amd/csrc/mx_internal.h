@@ -154,6 +154,10 @@ struct MoeDispatchArgs {
   int32_t* workspace;               // ceil(tokens * topk / kMoeBlock) * experts + 1 int32
 };
 hipError_t launch_moe_dispatch(const MoeDispatchArgs& args, hipStream_t stream);
+// Device address of the current device's dispatch scratch array (looked up
+// once per device).
+constexpr int64_t kDispatchScratchWords = 1 << 16;
+hipError_t dispatch_scratch(int32_t** out);
 hipError_t launch_moe_combine(const void* y_perm, const int32_t* perm, int64_t tokens, int64_t hidden, int32_t topk,
                               void* y, hipStream_t stream);
 

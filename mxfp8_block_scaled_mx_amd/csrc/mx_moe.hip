@@ -17,10 +17,40 @@
 // Entries whose expert lies outside [0, E) are dropped (perm -1).
 // Combine: y[t] = sum over slots of the routed output rows of token t, in
 // fp32 in slot order, rounded once to bf16.
+#include <mutex>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
 namespace mx {
+
+// Scratch of the allocation-free dispatch (mx_moe_dispatch_noalloc): the
+// per-block expert histograms, then the per-(block, expert) first routed rows,
+// and the routed-row total, kDispatchScratchWords int32 at most. Every word
+// the dispatch reads is written earlier in the same call, so the array needs
+// no clearing. One copy per GPU, held until the process ends; calls that
+// overlap on one GPU share it and race.
+static __device__ __align__(256) int32_t scratch[kDispatchScratchWords];
+
+hipError_t dispatch_scratch(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* ptr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    // the device address of this device's copy (the host-side name is only a
+    // stand-in and must never reach a kernel)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 __global__ __launch_bounds__(256) void moe_hist_kernel(const int32_t* idx, int64_t n, int32_t E, int32_t* hist) {
   __shared__ int32_t h[kMaxGroups];

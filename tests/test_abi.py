@@ -283,6 +283,19 @@ def test_mlp_intermediates_offsets(L):
     assert L.grouped_mlp_intermediates(ctypes.byref(_dims()), mx._i64_array([40, 24]), None) == EINVAL
 
 
+def test_moe_dispatch_noalloc_limits(L):
+    # validated before the scratch array is touched: sizes past its 65536
+    # words, and the usual argument errors
+    def d(T=100, H=64, k=2, E=8, x=FAKE, xp=FAKE):
+        return L.mx_moe_dispatch_noalloc(x, FAKE, None, T, H, k, E, xp, None, FAKE, FAKE, FAKE, None)
+
+    assert d(T=65536, E=128) == EUNSUPPORTED          # ceil(131072 / 256) * 128 + 1 words
+    assert d(H=60) == ESHAPE
+    assert d(E=129) == EUNSUPPORTED
+    assert d(x=None) == EINVAL
+    assert d(x=ctypes.c_void_p(0x100008)) == EALIGN
+
+
 def test_mlp_bindings_reject_tensors_that_disagree_with_the_dims():
     # the C ABI trusts the sizes it is given, so a smaller tensor would be read
     # past its end; the bindings compare every tensor with the dims first
