@@ -225,7 +225,7 @@ def main():
     mx.load()
     dev = torch.device("cuda:0")
     if args.copy_calibration:
-        copy_calibration(torch, dev)
+        copy_calibration(mx, torch, dev)
         return
     if args.quantize_only:
         q, _ = measure_quantize(mx, torch, np, wlmod, dev)
@@ -371,6 +371,7 @@ def main():
     if not args.no_quantize:
         out["quantize"], c2_rows = measure_quantize(mx, torch, np, wlmod, dev)
         f4 = out["quantize"]["fp4_rowwise"]
+        log(f"device copy {out['quantize']['copy_reference']['gbps']:.0f} GB/s")
         log(f"quantize {out['quantize']['gbps']:.0f} GB/s; MXFP4 rowwise {f4['gbps']:.0f} GB/s, "
             f"both layouts {f4['both_layouts_gbps']:.0f} GB/s")
 
@@ -607,15 +608,17 @@ def measure_forward(mx, torch, np, wlmod, dev, wl, steps, warmup, samples=None):
             "step": "grouped_mlp_fwd (inference; weights cast in the call) / grouped_mlp_fwd_cached"}
 
 
-def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
-    """A plain device-to-device copy of nbytes (read nbytes, write nbytes),
-    reps times: the HBM counters (FETCH_SIZE, WRITE_SIZE) of these dispatches
-    give the factor between counter units and bytes on this machine."""
+def copy_calibration(mx, torch, dev, nbytes=1 << 30, reps=3):
+    """The library's plain device copy (mx_device_copy) of nbytes (read
+    nbytes, write nbytes), reps times: the HBM counters (FETCH_SIZE,
+    WRITE_SIZE) of these dispatches give the factor between counter units and
+    bytes on this machine."""
+    L = mx.load()
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(reps):
-        dst.copy_(src)
+        mx._check(L.mx_device_copy(mx._ptr(dst), mx._ptr(src), nbytes, mx._stream()))
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}}),
           flush=True)
@@ -704,6 +707,29 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
         evs[b + 1].record()
     torch.cuda.synchronize()
     times = [evs[b].elapsed_time(evs[b + 1]) / iters for b in range(batches)]
+    # the hand-written device copy of the same inputs (read 128 MiB, write
+    # 128 MiB), timed the same way: the practical HBM rate of a cast-shaped
+    # read-then-write stream on this device
+    dst = torch.empty_like(xs[0])
+    nb = xs[0].numel() * 2
+
+    def copy(t):
+        mx._check(L.mx_device_copy(mx._ptr(dst), mx._ptr(t), nb, stream))
+
+    for i in range(8):
+        copy(xs[i % copies])
+    torch.cuda.synchronize()
+    evs[0].record()
+    for b in range(batches):
+        for i in range(iters):
+            copy(xs[i % copies])
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    ctimes = [evs[b].elapsed_time(evs[b + 1]) / iters for b in range(batches)]
+    cms = float(np.median(ctimes))
+    copy_ref = {"kernel": "mx_device_copy", "bytes": 2 * nb, "median_ms": round(cms, 4),
+                "gbps": round(2 * nb / (cms * 1e-3) / 1e9, 1)}
+    del dst
     # rowwise MXFP4 of the same tensor: 2 bytes read, 0.5 + 1/32 written per element
     q4 = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
     s4 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
@@ -746,6 +772,8 @@ def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
     return {"workload": "quantize_16384x4096", "layouts": "rowwise+columnwise", "bytes": algo,
             "median_ms": round(med, 4), "min_ms": round(float(np.min(times)), 4),
             "timing": f"median over {batches} batches of the mean of {iters} back-to-back launches",
+            "copy_reference": dict(copy_ref, quantize_frac_of_copy_rate=round(
+                algo / (med * 1e-3) / 1e9 / copy_ref["gbps"], 4)),
             "fp4_rowwise": fp4,
             "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

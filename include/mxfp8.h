@@ -101,6 +101,15 @@ MX_API const char* mx_last_error(void);
 MX_API int mx_version(void);
 
 /*
+ * mx_device_copy -- a plain device-to-device copy of `bytes` bytes (a
+ * multiple of 16; dst and src 16-byte aligned, not overlapping), enqueued on
+ * `stream`. It is the measured HBM reference for the memory-bound casts (the
+ * same read-then-write traffic without the arithmetic), not part of the MLP.
+ * Errors: MX_ESHAPE, MX_EINVAL (null pointer), MX_EALIGN, MX_EHIP.
+ */
+MX_API mx_status mx_device_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
  * mx_quantize -- MXFP8 quantization of a [rows, cols] matrix (row-major,
  * contiguous, ld = cols) into the rowwise and/or columnwise layouts.
  *

@@ -117,6 +117,8 @@ def load() -> ctypes.CDLL:
     L.mx_gemm_fp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     L.mx_grouped_gemm_fp4.restype = ctypes.c_int
     L.mx_grouped_gemm_fp4.argtypes = [vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
+    L.mx_device_copy.restype = ctypes.c_int
+    L.mx_device_copy.argtypes = [vp, vp, i64, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
     L.mx_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     _lib = L

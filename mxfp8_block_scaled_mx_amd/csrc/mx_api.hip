@@ -521,6 +521,17 @@ mx_status mx_set_stage_events(void* const* events, int32_t count) {
 
 int mx_version(void) { return 1; }
 
+mx_status mx_device_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_device_copy";
+  if (bytes < 0 || bytes % 16) return fail(MX_ESHAPE, "%s: bytes must be a non-negative multiple of 16", who);
+  if (bytes > 0 && (!dst || !src)) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(dst, 16) || !aligned(src, 16)) return fail(MX_EALIGN, "%s: dst and src must be 16-byte aligned", who);
+  hipError_t e = mx::launch_device_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_device_copy launch");
+  return MX_OK;
+}
+
 mx_status mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
                       int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                       void* stream) {

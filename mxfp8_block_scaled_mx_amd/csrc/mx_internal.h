@@ -62,6 +62,8 @@ struct QuantArgs {
 // Launch the quantize kernel (arguments already validated).
 hipError_t launch_quantize(const QuantArgs& args, int x_dtype, int total_row_tiles, hipStream_t stream);
 constexpr int kQuantTileRows = 128;
+// Plain device copy of `bytes` (a multiple of 16; 16-byte aligned pointers).
+hipError_t launch_device_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 inline int quant_tile_cols(int x_dtype) { return x_dtype == MX_BF16 ? 128 : 64; }
 
 // Epilogues of the grouped GEMM.

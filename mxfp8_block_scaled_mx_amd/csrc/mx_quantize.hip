@@ -21,6 +21,8 @@
 #include "mx_device.h"
 #include "mx_internal.h"
 
+#include <algorithm>
+
 namespace mx {
 
 template <typename T>
@@ -268,6 +270,32 @@ hipError_t launch_quantize(const QuantArgs& args, int x_dtype, int total_row_til
     hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, args);
   else
     hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+// Plain device copy (the HBM reference of the casts): every thread moves 4 x 16
+// bytes per pass, all loads issued before the stores; loads and stores are
+// non-temporal (each byte is touched once).
+__global__ __launch_bounds__(256) void device_copy_kernel(const v4i* __restrict__ src, v4i* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t step = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x; base < n16; base += step) {
+    v4i v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (base + 256 * i < n16) v[i] = __builtin_nontemporal_load(src + base + 256 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (base + 256 * i < n16) __builtin_nontemporal_store(v[i], dst + base + 256 * i);
+  }
+}
+
+hipError_t launch_device_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + 1023) / 1024, 256 * 16);
+  hipLaunchKernelGGL(device_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const v4i*>(src), reinterpret_cast<v4i*>(dst), n16);
   return hipGetLastError();
 }
 

@@ -296,6 +296,15 @@ def test_moe_dispatch_noalloc_limits(L):
     assert d(x=ctypes.c_void_p(0x100008)) == EALIGN
 
 
+def test_device_copy_argument_errors(L):
+    # checked before any launch; a zero-byte copy enqueues nothing
+    assert L.mx_device_copy(FAKE, FAKE, 24, None) == ESHAPE
+    assert L.mx_device_copy(FAKE, FAKE, -16, None) == ESHAPE
+    assert L.mx_device_copy(None, FAKE, 16, None) == EINVAL
+    assert L.mx_device_copy(ctypes.c_void_p(0x100008), FAKE, 16, None) == EALIGN
+    assert L.mx_device_copy(None, None, 0, None) == 0
+
+
 def test_mlp_bindings_reject_tensors_that_disagree_with_the_dims():
     # the C ABI trusts the sizes it is given, so a smaller tensor would be read
     # past its end; the bindings compare every tensor with the dims first
