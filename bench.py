@@ -389,6 +389,9 @@ def main():
             f"combine {dc['combine_gbps']:.0f} GB/s; MoE block fwd {dc['moe_block_fwd']['ms']:.3f} ms "
             f"-> {dc['moe_block_fwd']['tflops']:.0f} TFLOP/s; MoE layer train step "
             f"{dc['moe_layer_train_step']['ms']:.3f} ms -> {dc['moe_layer_train_step']['tflops']:.0f} TFLOP/s")
+        log(f"MoE layer train step with this step's counts: host copy "
+            f"{dc['moe_layer_train_step_host_counts']['ms']:.3f} ms, device-resident "
+            f"{dc['moe_layer_train_step_device_counts']['ms']:.3f} ms")
 
     # free device memory before the forward-only workloads and the CPU leg
     del runner, dw1, dw2, x, w1, w2, dy
@@ -560,7 +563,40 @@ def measure_moe(mx, torch, np, wlmod, dev, iters=20, T=8192, E=8, H=4096, ffn=14
                                    "tflops": round(18.0 * R * H * F / (t_ms * 1e-3) / 1e12, 1),
                                    "step": "routing-only dispatch + grouped_mlp_fwd_gather (training) + combine + "
                                            "grouped_mlp_bwd_gather (fp32 wgrad accumulate) + combine of dX"}
-    del w1, w2, runner_ws, dw1, dw2, bwd_ws
+    # the same step as a real layer runs it, where the counts come from this
+    # step's routing: (a) copied to the host before the MLP calls (a host
+    # round trip and a wait each step), (b) left on the device and read by the
+    # device-split calls (no copy, no wait)
+    def layer_step_host_counts():
+        _, p_, pm, rt, cnt = mx.mx_moe_dispatch(x, idx, w, E, gather=False)
+        sp = cnt.cpu().tolist()
+        yr, st = mx.grouped_mlp_fwd_gather(x, rt, p_, w1, w2, sp, training=True, workspace=runner_ws, out=y_r)
+        mx.mx_moe_combine(yr, pm, out=y)
+        dxr, _, _, _ = mx.grouped_mlp_bwd_gather(dy_tok, rt, p_, st, dw1=dw1, dw2=dw2, accumulate=True,
+                                                 workspace=bwd_ws)
+        mx.mx_moe_combine(dxr, pm, out=dx_t)
+
+    h_ms = timed(layer_step_host_counts)
+    dev_run = mx.DeviceSplitMLPRunner(E, R, H, F, device=dev)
+
+    def layer_step_device_counts():
+        _, p_, pm, rt, cnt = mx.mx_moe_dispatch(x, idx, w, E, gather=False)
+        yr = dev_run.forward(cnt, x, p_, w1, w2, row_token=rt)
+        mx.mx_moe_combine(yr, pm, out=y)
+        dxr, _ = dev_run.backward(cnt, dy_tok, p_, dw1, dw2, accumulate=True, row_token=rt)
+        mx.mx_moe_combine(dxr, pm, out=dx_t)
+
+    v_ms = timed(layer_step_device_counts)
+    flop = 18.0 * R * H * F
+    out["moe_layer_train_step_host_counts"] = {
+        "ms": round(h_ms, 4), "tflops": round(flop / (h_ms * 1e-3) / 1e12, 1),
+        "step": "as moe_layer_train_step, with this step's counts copied to the host (counts.cpu()) before "
+                "the MLP calls"}
+    out["moe_layer_train_step_device_counts"] = {
+        "ms": round(v_ms, 4), "tflops": round(flop / (v_ms * 1e-3) / 1e12, 1),
+        "step": "as moe_layer_train_step, with this step's counts read on the device by "
+                "grouped_mlp_fwd_device_split / grouped_mlp_bwd_device_split (no host copy, no wait)"}
+    del w1, w2, runner_ws, dw1, dw2, bwd_ws, dev_run
     return out
 
 

@@ -442,6 +442,69 @@ MX_API mx_status mx_moe_combine(const void* y_perm, const int32_t* perm, int64_t
                                 int64_t hidden, int32_t topk, void* y, void* stream);
 
 /*
+ * Device-resident split_sizes (sync-free). GroupedLinear takes the per-expert
+ * row counts, split_sizes ("Efficient MoE training for biological foundation
+ * models", Key technical approaches item 1); when they are produced on the
+ * GPU, for example as mx_moe_dispatch's counts, these calls read them there:
+ * the call's first kernel turns them into the group tables of every cast and
+ * GEMM of the call, so the host never copies them back nor waits for them,
+ * and the counts may still be in flight on `stream` when the call is made.
+ *
+ * grouped_mlp_sizes_device_split -- buffer sizes (bytes) for the two calls
+ * below, valid for every split of dims->rows routed rows over the experts:
+ * the columnwise copies and their k-tiled scales are laid out for the
+ * largest padded total any split can reach (rows + 31 * min(experts, rows)
+ * columns), and each workspace holds the device-built tables. These layouts
+ * are not those of grouped_mlp_sizes: `saved` of grouped_mlp_fwd_device_split
+ * is read by grouped_mlp_bwd_device_split only.
+ *
+ * grouped_mlp_fwd_device_split -- grouped_mlp_fwd (article item 3) with
+ *   split_sizes  device int64 [num_experts], read when the call's first
+ *                kernel runs (stream order). Expert e owns routed rows
+ *                [sum_{e'<e} m_e', + m_e). The counts are clamped on the
+ *                device: a negative count reads as 0, and a count that would
+ *                take the running sum past dims->rows is cut there (later
+ *                experts get no rows). The clamped sum S may be below
+ *                dims->rows, as when the dispatch drops entries: routed rows
+ *                S .. rows-1 are not read, and their rows of y are not
+ *                written.
+ *   row_token    optional gather as in grouped_mlp_fwd_gather (routed row r
+ *                is row row_token[r] of x, which has `tokens` rows); null:
+ *                x is the routed rows [rows, hidden] and tokens is ignored.
+ *   cache        optional weight cache of grouped_mlp_quantize_weights; null:
+ *                the weights are cast from w1, w2 inside the call (as
+ *                grouped_mlp_fwd); given: w1 and w2 are not read.
+ * Results for the first S rows are those of grouped_mlp_fwd (or _gather /
+ * _cached) on the clamped split, except that no split-K tail is used, so
+ * GEMM2 may sum a tile's k range in another order.
+ * Errors: as grouped_mlp_fwd; MX_EINVAL for a null split_sizes, MX_EALIGN if
+ * it is not 8-byte aligned. A count's value is never an error.
+ *
+ * grouped_mlp_bwd_device_split -- the corresponding backward, with the same
+ * split_sizes (the same values the forward read), optional row_token gather
+ * of dY as in grouped_mlp_bwd_gather, and optional weight cache (null: the
+ * columnwise weight copies that the forward left in `saved`). Rows S ..
+ * rows-1 of dx are not written and dprobs is 0 there; dw1 / dw2 of experts
+ * with no rows are zeroed (accumulate_wgrad == 0) or left as they are.
+ * Errors as grouped_mlp_bwd, plus those of split_sizes above.
+ */
+MX_API mx_status grouped_mlp_sizes_device_split(const mx_mlp_dims* dims, size_t* fwd_workspace,
+                                                size_t* saved, size_t* bwd_workspace);
+MX_API mx_status grouped_mlp_fwd_device_split(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                              const void* x, int64_t tokens, const int32_t* row_token,
+                                              const float* probs, const void* w1, const void* w2,
+                                              const void* cache, size_t cache_bytes, void* y,
+                                              void* saved, size_t saved_bytes, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+MX_API mx_status grouped_mlp_bwd_device_split(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                              const void* dy, int64_t tokens, const int32_t* row_token,
+                                              const float* probs, const void* cache, size_t cache_bytes,
+                                              const void* saved, size_t saved_bytes, void* dx,
+                                              float* dprobs, float* dw1, float* dw2,
+                                              int32_t accumulate_wgrad, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
+/*
  * mx_moe_dispatch_noalloc -- mx_moe_dispatch for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same arguments and results without

@@ -117,6 +117,15 @@ def load() -> ctypes.CDLL:
     L.mx_gemm_fp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     L.mx_grouped_gemm_fp4.restype = ctypes.c_int
     L.mx_grouped_gemm_fp4.argtypes = [vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
+    L.grouped_mlp_sizes_device_split.restype = ctypes.c_int
+    L.grouped_mlp_sizes_device_split.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                                 ctypes.POINTER(sz)]
+    L.grouped_mlp_fwd_device_split.restype = ctypes.c_int
+    L.grouped_mlp_fwd_device_split.argtypes = [ctypes.POINTER(_Dims), vp, vp, i64, vp, vp, vp, vp, vp, sz, vp, vp,
+                                               sz, vp, sz, vp]
+    L.grouped_mlp_bwd_device_split.restype = ctypes.c_int
+    L.grouped_mlp_bwd_device_split.argtypes = [ctypes.POINTER(_Dims), vp, vp, i64, vp, vp, vp, sz, vp, sz, vp, vp,
+                                               vp, vp, i32, vp, sz, vp]
     L.mx_device_copy.restype = ctypes.c_int
     L.mx_device_copy.argtypes = [vp, vp, i64, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
@@ -711,6 +720,89 @@ class MLPRunner:
                                  _ptr(self.dprobs) if want_dprobs else None, _ptr(dw1), _ptr(dw2),
                                  int(accumulate), _ptr(self.bwd_ws), self.bwd_ws.numel(),
                                  _stream(stream)))
+        return self.dx, (self.dprobs if want_dprobs else None)
+
+
+def mlp_sizes_device_split(E: int, R: int, H: int, F: int):
+    """(fwd workspace, saved, bwd workspace) byte sizes of the device-split
+    calls: valid for every split of R routed rows over E experts."""
+    L = load()
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.grouped_mlp_sizes_device_split(ctypes.byref(_dims(E, R, H, F)), ctypes.byref(f), ctypes.byref(s),
+                                            ctypes.byref(b)))
+    return f.value, s.value, b.value
+
+
+class DeviceSplitMLPRunner:
+    """Fused-MLP training step whose per-expert row counts stay on the device
+    (e.g. mx_moe_dispatch's counts): no host round trip, no wait. Owns the
+    workspaces (sized for every split of R rows), the saved buffer and the
+    outputs. Rows past the sum of the (clamped) counts are not read; y and dx
+    are not written there and dprobs is 0 there."""
+
+    def __init__(self, E: int, R: int, H: int, F: int, device="cuda"):
+        self.dims = (int(E), int(R), int(H), int(F))
+        fws, sv, bws = mlp_sizes_device_split(E, R, H, F)
+        self.fwd_ws = _byte_buffer(fws, device)
+        self.saved = _byte_buffer(sv, device)
+        self.bwd_ws = _byte_buffer(bws, device)
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.dx = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.dprobs = torch.empty((R,), dtype=torch.float32, device=device)
+        self._c_dims = _dims(E, R, H, F)
+
+    def _rows(self, x, row_token, name):
+        """Rows x must have: R without a gather, else its own (tokens)."""
+        E, R, H, F = self.dims
+        if row_token is None:
+            return R, []
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
+        return int(x.shape[0]), [(row_token, (R,), torch.int32, "row_token", False)]
+
+    def _cache(self, cache):
+        E, _, H, F = self.dims
+        if cache is None:
+            return None, 0
+        if not isinstance(cache, WeightCache) or cache.ehf != (E, H, F):
+            raise ValueError("cache must be a WeightCache of this runner's E, H, F")
+        return _ptr(cache.buf), cache.buf.numel()
+
+    def forward(self, counts, x, probs, w1=None, w2=None, *, cache=None, row_token=None, training=True,
+                stream=None):
+        L = load()
+        E, R, H, F = self.dims
+        rows, extra = self._rows(x, row_token, "x")
+        items = [(counts, (E,), torch.int64, "counts", False)] + extra
+        items += _mlp_items(E, R, H, F, x, None if cache is not None else w1,
+                            None if cache is not None else w2, probs, x_rows=rows)
+        if cache is None and (w1 is None or w2 is None):
+            raise ValueError("w1 and w2 (or a weight cache) are required")
+        _expect_all(items)
+        cp, cb = self._cache(cache)
+        saved = self.saved if training else None
+        _check(L.grouped_mlp_fwd_device_split(
+            ctypes.byref(self._c_dims), _ptr(counts), _ptr(x), rows if row_token is not None else 0,
+            _ptr(row_token), _ptr(probs), None if cache is not None else _ptr(w1),
+            None if cache is not None else _ptr(w2), cp, cb, _ptr(self.y), _ptr(saved),
+            0 if saved is None else saved.numel(), _ptr(self.fwd_ws), self.fwd_ws.numel(), _stream(stream)))
+        return self.y
+
+    def backward(self, counts, dy, probs, dw1, dw2, *, accumulate=True, want_dprobs=True, cache=None,
+                 row_token=None, stream=None):
+        L = load()
+        E, R, H, F = self.dims
+        rows, extra = self._rows(dy, row_token, "dy")
+        _expect_all([(counts, (E,), torch.int64, "counts", False), (dy, (rows, H), torch.bfloat16, "dy", False),
+                     (probs, (R,), torch.float32, "probs", True),
+                     (dw1, (E, 2 * F, H), torch.float32, "dw1", False),
+                     (dw2, (E, H, F), torch.float32, "dw2", False)] + extra)
+        cp, cb = self._cache(cache)
+        _check(L.grouped_mlp_bwd_device_split(
+            ctypes.byref(self._c_dims), _ptr(counts), _ptr(dy), rows if row_token is not None else 0,
+            _ptr(row_token), _ptr(probs), cp, cb, _ptr(self.saved), self.saved.numel(), _ptr(self.dx),
+            _ptr(self.dprobs) if want_dprobs else None, _ptr(dw1), _ptr(dw2), int(accumulate),
+            _ptr(self.bwd_ws), self.bwd_ws.numel(), _stream(stream)))
         return self.dx, (self.dprobs if want_dprobs else None)
 
 

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmxfp8.so")
-SOURCES = ["mx_api.hip", "mx_quantize.hip", "mx_gemm.hip", "mx_moe.hip", "mx_fp4.hip"]
+SOURCES = ["mx_api.hip", "mx_quantize.hip", "mx_gemm.hip", "mx_moe.hip", "mx_fp4.hip", "mx_plan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

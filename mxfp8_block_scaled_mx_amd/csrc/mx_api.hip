@@ -110,10 +110,19 @@ mx_status check_groups(const int64_t* sizes, int32_t n, int64_t rows, const char
 
 // tiled: scales of both copies in the k-tiled layout (the fused MLP's
 // internal buffers; needs cols % 128 == 0 for the rowwise copy).
+// Device-built row groups for an activation cast of the fused MLP: the table,
+// the worst-case layout of the columnwise copy and the worst-case row tiles.
+struct DevQuant {
+  const mx::QuantGroups* groups;
+  int64_t ld_col;
+  int32_t nq_col;
+  int64_t row_tiles;
+};
+
 mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const int64_t* group_sizes,
                         int32_t num_groups, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                         hipStream_t stream, bool tiled = false, const int32_t* row_index = nullptr,
-                        int64_t index_rows = 0) {
+                        int64_t index_rows = 0, const DevQuant* dq = nullptr) {
   const char* who = "mx_quantize";
   if (x == nullptr) return fail(MX_EINVAL, "%s: x is null", who);
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return fail(MX_EINVAL, "%s: unsupported dtype %d", who, x_dtype);
@@ -166,6 +175,12 @@ mx_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t co
   if (p0 > kI32Max) return fail(MX_EUNSUPPORTED, "%s: padded rows exceed 2^31-1", who);
   a.ld_col = p0;
   a.n_col_tiles = (int32_t)cdiv(cols, mx::quant_tile_cols(x_dtype));
+  if (dq != nullptr) {
+    a.groups_dev = dq->groups;
+    a.ld_col = dq->ld_col;
+    a.nq_col = dq->nq_col;
+    t0 = dq->row_tiles;
+  }
   if (t0 * a.n_col_tiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many tiles", who);
   hipError_t e = mx::launch_quantize(a, x_dtype, (int)t0, stream);
   if (e != hipSuccess) return hip_fail(e, "mx_quantize launch");
@@ -340,7 +355,17 @@ struct MlpLayout {
   int64_t n_tiles_f;
   std::vector<int64_t> q0;   // k-tiled steps of the per-expert columnwise layouts
   int64_t nq;                // total steps (q0[E])
+  // device-resident split sizes: the layout holds every split of R rows
+  // (split above is a placeholder that passes the host checks), the group
+  // tables are built by the call's first kernel into plan_fwd / plan_bwd
+  bool dev = false;
+  const int64_t* counts_dev = nullptr;
+  size_t plan_fwd = 0, plan_bwd = 0;
 };
+
+// Worst-case sums over any split of R rows into E groups (at most min(E, R)
+// of them non-empty): sum of ceil(m_g / b) <= floor((R + (b-1) * min(E, R)) / b).
+int64_t worst_blocks(int64_t R, int64_t E, int64_t b) { return (R + (b - 1) * std::min(E, R)) / b; }
 
 size_t take(size_t& cur, size_t bytes) {
   const size_t at = cur;
@@ -348,10 +373,17 @@ size_t take(size_t& cur, size_t bytes) {
   return at;
 }
 
-mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, const char* who) {
+mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, const char* who,
+                     bool device_split = false) {
   if (!d) return fail(MX_EINVAL, "%s: dims is null", who);
   if (d->num_experts < 1) return fail(MX_EINVAL, "%s: need at least one expert", who);
   if (d->num_experts > mx::kMaxGroups) return fail(MX_EUNSUPPORTED, "%s: %d experts exceeds the maximum %d", who, d->num_experts, mx::kMaxGroups);
+  std::vector<int64_t> placeholder;
+  if (device_split) {
+    placeholder.assign(d->num_experts, 0);
+    placeholder[0] = d->rows > 0 ? d->rows : 0;
+    split = placeholder.data();
+  }
   if (!split) return fail(MX_EINVAL, "%s: split_sizes is null", who);
   if (d->rows < 0 || d->hidden <= 0 || d->ffn <= 0) return fail(MX_ESHAPE, "%s: bad dims", who);
   if (d->hidden % 128 || d->ffn % 128) return fail(MX_ESHAPE, "%s: hidden and ffn must be multiples of 128", who);
@@ -367,9 +399,17 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   L->split.assign(split, split + d->num_experts);
   L->sumP = 0;
   for (int e = 0; e < L->E; ++e) L->sumP += pad32(split[e]);
-  const int64_t R = L->R, H = L->H, F = L->F, E = L->E, P = L->sumP;
   L->q0 = group_steps(split, d->num_experts, d->rows);
-  L->nq = L->q0[E];
+  L->nq = L->q0[L->E];
+  L->dev = device_split;
+  if (device_split) {
+    L->sumP = worst_blocks(L->R, L->E, 32) * 32;
+    L->nq = worst_blocks(L->R, L->E, 128);
+    if (worst_blocks(L->R, L->E, mx::kTileM) * cdiv(L->H, mx::kTileN) > kI32Max ||
+        worst_blocks(L->R, L->E, mx::kQuantTileRows) * (L->H / 128) > kI32Max || L->sumP > kI32Max)
+      return fail(MX_EUNSUPPORTED, "%s: too many tiles", who);
+  }
+  const int64_t R = L->R, H = L->H, F = L->F, E = L->E, P = L->sumP;
   // all scales are k-tiled: a rowwise [rows, K] matrix takes ceil(rows/32)*32*K/32
   // bytes, a per-expert columnwise [cols, P] one cols/32 * nq * 128
   const int64_t R32 = cdiv(R, 32) * 32, NQ = L->nq;
@@ -382,8 +422,10 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   int64_t m_tiles = 0;
   for (int e = 0; e < L->E; ++e) m_tiles += cdiv(split[e], mx::kTileM);
   const int64_t h_tiles = m_tiles * cdiv(H, mx::kTileN);
-  L->split2_bytes = L->split1_bytes = split_ws_bytes(h_tiles);
+  // (no split-K tail with device-built tables: its plan needs the tile count)
+  L->split2_bytes = L->split1_bytes = device_split ? 0 : split_ws_bytes(h_tiles);
   L->split2 = take(c, L->split2_bytes);
+  if (device_split) L->plan_fwd = take(c, sizeof(mx::MlpDevPlan));
   L->fwd_total = c;
   c = 0;
   L->xcq = take(c, H * P); L->xcs = take(c, H / 32 * NQ * 128);
@@ -400,6 +442,7 @@ mx_status mlp_layout(const mx_mlp_dims* d, const int64_t* split, MlpLayout* L, c
   L->dhcq = take(c, 2 * F * P); L->dhcs = take(c, 2 * F / 32 * NQ * 128);
   L->part = take(c, L->n_tiles_f * R * 4);
   L->split1 = take(c, L->split1_bytes);
+  if (device_split) L->plan_bwd = take(c, sizeof(mx::MlpDevPlan));
   L->bwd_total = c;
   return MX_OK;
 }
@@ -450,6 +493,49 @@ mx_status quantize_weights_into(const MlpLayout& L, const void* w1, const void* 
   if (st != MX_OK) return st;
   if (marks) stage_mark(2, stream);
   return quantize_impl(w2, MX_BF16, E * H, F, g_w2.data(), E, wc.w2q, wc.w2s, wc.w2cq, wc.w2cs, stream, true);
+}
+
+// Device-built group tables (device-resident split sizes): tile counts of
+// the tables in mx::MlpDevPlan, from the dims alone.
+enum : int { kDevGemm1 = 0, kDevNH = 1, kDevNF = 2 };     // group-M tables
+enum : int { kDevWgrad2 = 0, kDevWgrad1 = 1 };            // group-K tables
+
+mx::MlpDevPlanArgs dev_plan_args(const MlpLayout& L, mx::MlpDevPlan* plan) {
+  mx::MlpDevPlanArgs a;
+  memset(&a, 0, sizeof(a));
+  a.counts = L.counts_dev;
+  a.plan = plan;
+  a.E = L.E;
+  a.R = (int32_t)L.R;
+  a.m_tiles_n[kDevGemm1] = (int32_t)cdiv(L.F, mx::kTileN / 2);
+  a.m_tiles_n[kDevNH] = (int32_t)cdiv(L.H, mx::kTileN);
+  a.m_tiles_n[kDevNF] = (int32_t)cdiv(L.F, mx::kTileN);
+  a.k_slot_tiles[kDevWgrad2] = (int32_t)(cdiv(L.H, mx::kTileM) * cdiv(L.F, mx::kTileN));
+  a.k_slot_tiles[kDevWgrad1] = (int32_t)(cdiv(2 * L.F, mx::kTileM) * cdiv(L.H, mx::kTileN));
+  for (int j = 0; j < 2; ++j) a.k_interleave[j] = L.E > 1 && a.k_slot_tiles[j] % 32 == 0 ? 1 : 0;
+  return a;
+}
+
+// Switch a plan built on the placeholder split to device table j of plan:
+// worst-case grid, no split-K tail. The table's tile counts must be the
+// plan's own (an internal consistency check).
+mx_status use_dev_groups(GemmPlan& p, int mode, const MlpLayout& L, mx::MlpDevPlan* plan, int j) {
+  const mx::MlpDevPlanArgs a = dev_plan_args(L, plan);
+  mx::GemmArgs& A = p.args;
+  int64_t worst;
+  if (mode == MX_GROUP_M) {
+    if (A.n_tiles_n != a.m_tiles_n[j]) return fail(MX_EUNSUPPORTED, "internal: device table %d tile count", j);
+    A.groups_dev = &plan->m[j];
+    worst = worst_blocks(L.R, L.E, mx::kTileM) * A.n_tiles_n;
+  } else {
+    if (cdiv(A.M, mx::kTileM) * A.n_tiles_n != a.k_slot_tiles[j] || A.groups.interleave != a.k_interleave[j])
+      return fail(MX_EUNSUPPORTED, "internal: device table %d tile count", j);
+    A.groups_dev = &plan->k[j];
+    worst = (int64_t)L.E * a.k_slot_tiles[j];
+  }
+  A.split_s = 0;
+  p.total_tiles = (int)worst;
+  return MX_OK;
 }
 
 mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, const char* what) {
@@ -624,13 +710,25 @@ mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const 
   a1.q_col = saved ? at(saved, L.acq) : nullptr;
   a1.s_col = saved ? at(saved, L.acs) : nullptr;
   a1.R = (int32_t)R;
+  mx::MlpDevPlan* plan = L.dev ? reinterpret_cast<mx::MlpDevPlan*>(at(workspace, L.plan_fwd)) : nullptr;
+  DevQuant dq{};
+  if (L.dev) {
+    st = use_dev_groups(p1, MX_GROUP_M, L, plan, kDevGemm1);
+    if (st == MX_OK) st = use_dev_groups(p2, MX_GROUP_M, L, plan, kDevNH);
+    if (st != MX_OK) return st;
+    dq = DevQuant{&plan->act, L.sumP, (int32_t)L.nq, worst_blocks(R, E, mx::kQuantTileRows)};
+  }
 
   stage_mark(0, stream);
+  if (L.dev) {
+    hipError_t e = mx::launch_mlp_dev_plan(dev_plan_args(L, plan), stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_fwd device plan");
+  }
   // (with row_token: routed row r is token row row_token[r] of x, gathered
   // by the cast itself)
   st = quantize_impl(x, MX_BF16, R, H, L.split.data(), E, at(workspace, L.xq), at(workspace, L.xs),
                      saved ? at(saved, L.xcq) : nullptr, saved ? at(saved, L.xcs) : nullptr, stream, true,
-                     row_token, tokens);
+                     row_token, tokens, L.dev ? &dq : nullptr);
   if (st != MX_OK) return st;
   // (running the W2 cast on the side stream beside GEMM1 was measured: it
   // slows GEMM1 by more than the cast takes, so the forward stays serial)
@@ -646,7 +744,8 @@ mx_status fwd_impl(const MlpLayout& L, const void* x, const float* probs, const 
   if (st != MX_OK) return st;
   stage_mark(4, stream);
   {
-    const int tail = plan_split_tail(p2, F, reinterpret_cast<float*>(at(workspace, L.split2)), L.split2_bytes);
+    const int tail = L.dev ? 0 : plan_split_tail(p2, F, reinterpret_cast<float*>(at(workspace, L.split2)),
+                                                 L.split2_bytes);
     st = run_gemm(p2, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_fwd gemm2");
     if (st != MX_OK) return st;
     hipError_t e = mx::launch_split_reduce(mx::EPI_BF16, p2.args, tail, stream);
@@ -806,7 +905,10 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
                            w2cq, w2cs, E * H, H, dx, MX_BF16, F, 0, 0, mx::EPI_SWIGLU_BWD, F, &pd2);
   if (st != MX_OK) return st;
   // dW2_e = colwise(dY_e) . colwise(A_e)^T
-  st = gemm_plan(MX_GROUP_K, E, L.split.data(), H, F, P, at(workspace, L.dycq), at(workspace, L.dycs), P,
+  // (the contraction of the group-K plans is the padded split; with device
+  // split sizes the placeholder's, inside the worst-case pitch P)
+  const int64_t Kk = L.dev ? pad32(R) : P;
+  st = gemm_plan(MX_GROUP_K, E, L.split.data(), H, F, Kk, at(workspace, L.dycq), at(workspace, L.dycs), P,
                  at(saved, L.acq), at(saved, L.acs), P, 0, dw2, MX_F32, F, H * F, accumulate_wgrad, mx::EPI_F32, F, &pw2);
   if (st != MX_OK) return st;
   // dX = dH1_row . colwise(W1_e): B_e = w1 columnwise [H, E*2F] at column e*2F
@@ -814,7 +916,7 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
                  w1cq, w1cs, E * 2 * F, 2 * F, dx, MX_BF16, H, 0, 0, mx::EPI_BF16, H, &pd1);
   if (st != MX_OK) return st;
   // dW1_e = colwise(dH1_e) . colwise(X_e)^T
-  st = gemm_plan(MX_GROUP_K, E, L.split.data(), 2 * F, H, P, at(workspace, L.dhcq), at(workspace, L.dhcs), P,
+  st = gemm_plan(MX_GROUP_K, E, L.split.data(), 2 * F, H, Kk, at(workspace, L.dhcq), at(workspace, L.dhcs), P,
                  at(saved, L.xcq), at(saved, L.xcs), P, 0, dw1, MX_F32, H, 2 * F * H, accumulate_wgrad, mx::EPI_F32,
                  H, &pw1);
   if (st != MX_OK) return st;
@@ -838,6 +940,16 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   a.s_col = at(workspace, L.dhcs);
   a.dprobs_part = dprobs ? reinterpret_cast<float*>(at(workspace, L.part)) : nullptr;
   a.R = (int32_t)R;
+  mx::MlpDevPlan* plan = L.dev ? reinterpret_cast<mx::MlpDevPlan*>(at(workspace, L.plan_bwd)) : nullptr;
+  DevQuant dq{};
+  if (L.dev) {
+    st = use_dev_groups(pd2, MX_GROUP_M, L, plan, kDevNF);
+    if (st == MX_OK) st = use_dev_groups(pd1, MX_GROUP_M, L, plan, kDevNH);
+    if (st == MX_OK) st = use_dev_groups(pw2, MX_GROUP_K, L, plan, kDevWgrad2);
+    if (st == MX_OK) st = use_dev_groups(pw1, MX_GROUP_K, L, plan, kDevWgrad1);
+    if (st != MX_OK) return st;
+    dq = DevQuant{&plan->act, P, (int32_t)L.nq, worst_blocks(R, E, mx::kQuantTileRows)};
+  }
 
   // stages overlap on the side stream unless per-stage timing is on: the
   // wgrad GEMMs (HBM-bound fp32 read-modify-write) run there, wgrad2 beside
@@ -848,9 +960,14 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
     if (st != MX_OK) return st;
   }
   stage_mark(0, stream);
+  if (L.dev) {
+    hipError_t e = mx::launch_mlp_dev_plan(dev_plan_args(L, plan), stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped_mlp_bwd device plan");
+  }
   // (with row_token: routed row r of dY is token row row_token[r] of dy)
   st = quantize_impl(dy, MX_BF16, R, H, L.split.data(), E, at(workspace, L.dyq), at(workspace, L.dys),
-                     at(workspace, L.dycq), at(workspace, L.dycs), stream, true, row_token, tokens);
+                     at(workspace, L.dycq), at(workspace, L.dycs), stream, true, row_token, tokens,
+                     L.dev ? &dq : nullptr);
   if (st != MX_OK) return st;
   // once work is on the side stream, an error return still joins it first,
   // so nothing enqueued by this call runs unordered with the caller's stream
@@ -874,7 +991,8 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   stage_mark(2, stream);
   if (dprobs) {
     hipError_t e = mx::launch_dprobs_reduce(reinterpret_cast<const float*>(at(workspace, L.part)), dprobs,
-                                            (int32_t)R, (int32_t)L.n_tiles_f, stream);
+                                            (int32_t)R, (int32_t)L.n_tiles_f, L.dev ? &plan->rows : nullptr,
+                                            stream);
     if (e != hipSuccess) return fail_joined(hip_fail(e, "grouped_mlp_bwd dprobs"));
   }
   if (sd != nullptr) {
@@ -889,7 +1007,8 @@ mx_status bwd_impl(const MlpLayout& L, const void* dy, const float* probs, const
   }
   stage_mark(4, stream);
   {
-    const int tail = plan_split_tail(pd1, 2 * F, reinterpret_cast<float*>(at(workspace, L.split1)), L.split1_bytes);
+    const int tail = L.dev ? 0 : plan_split_tail(pd1, 2 * F, reinterpret_cast<float*>(at(workspace, L.split1)),
+                                                 L.split1_bytes);
     st = run_gemm(pd1, MX_GROUP_M, mx::EPI_BF16, stream, "grouped_mlp_bwd dgrad1");
     if (st != MX_OK) return fail_joined(st);
     hipError_t e = mx::launch_split_reduce(mx::EPI_BF16, pd1.args, tail, stream);
@@ -956,6 +1075,82 @@ mx_status grouped_mlp_bwd_cached(const mx_mlp_dims* dims, const int64_t* split_s
   const WeightCopies wc = weight_cache_copies(W, const_cast<void*>(cache));
   return bwd_impl(L, dy, probs, saved, &wc, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
                   reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_sizes_device_split(const mx_mlp_dims* dims, size_t* fwd_workspace, size_t* saved,
+                                         size_t* bwd_workspace) {
+  g_err[0] = 0;
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, nullptr, &L, "grouped_mlp_sizes_device_split", true);
+  if (st != MX_OK) return st;
+  if (fwd_workspace) *fwd_workspace = L.fwd_total;
+  if (saved) *saved = L.saved_total;
+  if (bwd_workspace) *bwd_workspace = L.bwd_total;
+  return MX_OK;
+}
+
+mx_status grouped_mlp_fwd_device_split(const mx_mlp_dims* dims, const int64_t* split_sizes_dev, const void* x,
+                                       int64_t tokens, const int32_t* row_token, const float* probs,
+                                       const void* w1, const void* w2, const void* cache, size_t cache_bytes,
+                                       void* y, void* saved, size_t saved_bytes, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd_device_split";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, nullptr, &L, who, true);
+  if (st != MX_OK) return st;
+  if (!split_sizes_dev) return fail(MX_EINVAL, "%s: split_sizes is null", who);
+  if (!aligned(split_sizes_dev, 8)) return fail(MX_EALIGN, "%s: split_sizes must be 8-byte aligned", who);
+  L.counts_dev = split_sizes_dev;
+  st = fwd_checks(L, x, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  if (row_token) {
+    if (tokens < 0 || tokens > kI32Max) return fail(MX_ESHAPE, "%s: bad token count %lld", who, (long long)tokens);
+    if (!aligned(row_token, 4)) return fail(MX_EALIGN, "%s: row_token must be 4-byte aligned", who);
+  }
+  WeightCopies wc{};
+  if (cache) {
+    WeightCacheLayout W;
+    st = cache_checks(L, cache, cache_bytes, &W, who);
+    if (st != MX_OK) return st;
+    wc = weight_cache_copies(W, const_cast<void*>(cache));
+  } else {
+    if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument (w1, w2 or a weight cache)", who);
+    if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
+  }
+  return fwd_impl(L, x, probs, w1, w2, cache ? &wc : nullptr, y, saved, workspace,
+                  reinterpret_cast<hipStream_t>(stream), row_token, row_token ? tokens : 0);
+}
+
+mx_status grouped_mlp_bwd_device_split(const mx_mlp_dims* dims, const int64_t* split_sizes_dev, const void* dy,
+                                       int64_t tokens, const int32_t* row_token, const float* probs,
+                                       const void* cache, size_t cache_bytes, const void* saved,
+                                       size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                                       int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd_device_split";
+  MlpLayout L;
+  mx_status st = mlp_layout(dims, nullptr, &L, who, true);
+  if (st != MX_OK) return st;
+  if (!split_sizes_dev) return fail(MX_EINVAL, "%s: split_sizes is null", who);
+  if (!aligned(split_sizes_dev, 8)) return fail(MX_EALIGN, "%s: split_sizes must be 8-byte aligned", who);
+  L.counts_dev = split_sizes_dev;
+  st = bwd_checks(L, dy, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  if (row_token) {
+    if (tokens < 0 || tokens > kI32Max) return fail(MX_ESHAPE, "%s: bad token count %lld", who, (long long)tokens);
+    if (!aligned(row_token, 4)) return fail(MX_EALIGN, "%s: row_token must be 4-byte aligned", who);
+  }
+  WeightCopies wc{};
+  if (cache) {
+    WeightCacheLayout W;
+    st = cache_checks(L, cache, cache_bytes, &W, who);
+    if (st != MX_OK) return st;
+    wc = weight_cache_copies(W, const_cast<void*>(cache));
+  }
+  return bwd_impl(L, dy, probs, saved, cache ? &wc : nullptr, dx, dprobs, dw1, dw2, accumulate_wgrad, workspace,
+                  reinterpret_cast<hipStream_t>(stream), row_token, row_token ? tokens : 0);
 }
 
 size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts) {

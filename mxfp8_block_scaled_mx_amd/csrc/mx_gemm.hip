@@ -142,7 +142,16 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmGroups& gt, int id, i
 // layout through LDS (one DMA per 256 rows and k-step).
 enum ScaleSource : int { kScByte = 0, kScDword = 1, kScLds = 2 };
 
-template <int MODE, int EPI, int SC>
+template <bool DEVG>
+__device__ __forceinline__ const GemmGroups& gemm_groups(const GemmArgs& a) {
+  if constexpr (DEVG) return *a.groups_dev;
+  else return a.groups;
+}
+
+// DEVG: the group table is in device memory (args.groups_dev), built there
+// from device-resident group sizes; the grid is sized for the worst case and
+// the workgroups past the table's tile count exit at once.
+template <int MODE, int EPI, int SC, bool DEVG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_kernel(GemmArgs args, int total_tiles) {
   // The body uses gfx950-only types and builtins (buffer resources, LDS DMA);
@@ -169,17 +178,22 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 
   // Work unit of this workgroup: a whole tile, or (split-K tail) part
   // `part` of tile id's k-steps, written as an fp32 partial tile.
+  const GemmGroups& gt = gemm_groups<DEVG>(args);
+  if constexpr (DEVG) {
+    total_tiles = gt.tile0[gt.n];
+    if ((int)blockIdx.x >= total_tiles) return;
+  }
   int id, part = 0, split_unit = -1;
-  if (args.split_s > 1 && (int)blockIdx.x >= args.split_f) {
+  if (!DEVG && args.split_s > 1 && (int)blockIdx.x >= args.split_f) {
     split_unit = (int)blockIdx.x - args.split_f;
     id = args.split_f + split_unit / args.split_s;
     part = split_unit % args.split_s;
   } else {
     id = xcd_remap(blockIdx.x, args.split_s > 1 ? args.split_f : total_tiles);
   }
-  const TileCoord tc = locate_tile(args.groups, id, MODE, args.M, args.n_tiles_n);
+  const TileCoord tc = locate_tile(gt, id, MODE, args.M, args.n_tiles_n);
   const int slot = tc.slot;
-  const int g = args.groups.gid[slot];
+  const int g = gt.gid[slot];
 
   // ---- geometry of this tile
   int64_t a_row0;     // first global A row of the tile
@@ -190,8 +204,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const uint8_t* bq = args.b;
   const uint8_t* bsc = args.bs;
   if constexpr (MODE == MX_GROUP_M) {
-    a_row0 = (int64_t)args.groups.a0[slot] + (int64_t)tc.mt * BM;
-    a_rows_valid = args.groups.len[slot] - tc.mt * BM;
+    a_row0 = (int64_t)gt.a0[slot] + (int64_t)tc.mt * BM;
+    a_rows_valid = gt.len[slot] - tc.mt * BM;
     kbeg = 0;
     klen = args.K;
     bq += (int64_t)g * args.b_group_stride;
@@ -199,8 +213,8 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   } else {
     a_row0 = (int64_t)tc.mt * BM;
     a_rows_valid = args.M - tc.mt * BM;
-    kbeg = args.groups.a0[slot];
-    klen = args.groups.len[slot];
+    kbeg = gt.a0[slot];
+    klen = gt.len[slot];
   }
   b_rows = EPI == EPI_SWIGLU_FWD ? 2 * args.F : args.N;
   if (a_rows_valid > BM) a_rows_valid = BM;
@@ -260,7 +274,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
   const uint32_t vsa_off = (la >> 5) * (uint32_t)sa.grp + (la & 31) * (uint32_t)sa.row;
   const uint32_t vsb_off = (uint32_t)l32 * (uint32_t)sb.row;
   // first 128-column step of this tile's k range in the scale layout
-  const int q_base = MODE == MX_GROUP_K ? (args.k_tiled ? args.groups.q0[slot] : (int)(kbeg >> 7)) : 0;
+  const int q_base = MODE == MX_GROUP_K ? (args.k_tiled ? gt.q0[slot] : (int)(kbeg >> 7)) : 0;
 
   // valid A rows of this wave's 128 (wave-uniform; <= 0: none)
   const int wave_rows = __builtin_amdgcn_readfirstlane(a_rows_valid - (BM / 2) * wm);
@@ -720,9 +734,9 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const uint32_t F = (uint32_t)args.F;
     const int jw0 = tc.nt * (BN / 2) + (NS / 2) * 32 * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;       // first row of the wave inside its group
-    const int len = args.groups.len[slot];
+    const int len = gt.len[slot];
     const uint32_t ldq = (uint32_t)args.ld_col;
-    const int64_t crow0 = args.groups.pc0[slot] + wrow0;   // columnwise position of the wave's first row
+    const int64_t crow0 = gt.pc0[slot] + wrow0;   // columnwise position of the wave's first row
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
     const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 ? args.h1 + m0 * 2 * F : nullptr, args.h1 ? (int64_t)wrows * 4 * F : 0);
     const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * F, (int64_t)wrows * F);
@@ -732,7 +746,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
                                                  col_out ? (int64_t)(NS / 2) * 32 * ldq : 0);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col : nullptr,
                                                  col_out ? (int64_t)(F >> 5) * args.nq_col * 128 : 0);
-    const uint32_t q0 = (uint32_t)args.groups.q0[slot];
+    const uint32_t q0 = (uint32_t)gt.q0[slot];
     float w[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -800,9 +814,9 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const uint32_t F = (uint32_t)args.F;
     const int jw0 = tc.nt * BN + kWaveN * wn;
     const int wrow0 = tc.mt * BM + (BM / 2) * wm;
-    const int len = args.groups.len[slot];
+    const int len = gt.len[slot];
     const uint32_t ldq = (uint32_t)args.ld_col;
-    const int64_t crow0 = args.groups.pc0[slot] + wrow0;
+    const int64_t crow0 = gt.pc0[slot] + wrow0;
     const __amdgpu_buffer_rsrc_t rprob = make_rsrc(args.probs ? args.probs + m0 : nullptr, args.probs ? (int64_t)wrows * 4 : 0);
     const __amdgpu_buffer_rsrc_t rh1 = make_rsrc(args.h1 + m0 * 2 * F, (int64_t)wrows * 4 * F);
     const __amdgpu_buffer_rsrc_t rqr = make_rsrc(args.q_row + m0 * 2 * F, (int64_t)wrows * 2 * F);
@@ -811,7 +825,7 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rqc_g = make_rsrc(args.q_col + (int64_t)jw0 * ldq + crow0, (int64_t)kWaveN * ldq);
     const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)kWaveN * ldq);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(args.s_col, (int64_t)(2 * F >> 5) * args.nq_col * 128);
-    const uint32_t q0 = (uint32_t)args.groups.q0[slot];
+    const uint32_t q0 = (uint32_t)gt.q0[slot];
     float w[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -925,9 +939,14 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-__global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* part, float* out, int32_t R, int32_t n_parts) {
+__global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* part, float* out, int32_t R, int32_t n_parts,
+                                                            const int32_t* rows_dev) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= R) return;
+  if (rows_dev != nullptr && r >= *rows_dev) {   // rows past the routed ones
+    out[r] = 0.0f;
+    return;
+  }
   float s = 0.0f;
   for (int p = 0; p < n_parts; ++p) s += part[(int64_t)p * R + r];
   out[r] = s;
@@ -974,14 +993,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs args) {
 
 template <int MODE, int EPI>
 static hipError_t launch_mode_epi(bool svec, const GemmArgs& args, int total, hipStream_t stream) {
-  if (args.k_tiled) {
-    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScLds>), dim3(total), dim3(kThreads), 0, stream, args, total);
+  if (args.groups_dev != nullptr) {
+    // device-built group tables: k-tiled scales, no split-K tail
+    if (!args.k_tiled || args.split_s > 1) return hipErrorInvalidValue;
+    if constexpr ((MODE == MX_GROUP_M && EPI != EPI_F32) || (MODE == MX_GROUP_K && EPI == EPI_F32))
+      hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScLds, true>), dim3(total), dim3(kThreads), 0, stream, args, total);
+    else
+      return hipErrorInvalidValue;
+  } else if (args.k_tiled) {
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScLds, false>), dim3(total), dim3(kThreads), 0, stream, args, total);
   } else if constexpr (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
     return hipErrorInvalidValue;       // the fused epilogues run on k-tiled scales only
   } else if (svec) {
-    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScDword>), dim3(total), dim3(kThreads), 0, stream, args, total);
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScDword, false>), dim3(total), dim3(kThreads), 0, stream, args, total);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScByte>), dim3(total), dim3(kThreads), 0, stream, args, total);
+    hipLaunchKernelGGL((gemm_kernel<MODE, EPI, kScByte, false>), dim3(total), dim3(kThreads), 0, stream, args, total);
   }
   return hipGetLastError();
 }
@@ -1016,9 +1042,11 @@ hipError_t launch_split_reduce(int epi, const GemmArgs& args, int tail_tiles, hi
   return hipGetLastError();
 }
 
-hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts, hipStream_t stream) {
+hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts, const int32_t* rows_dev,
+                                hipStream_t stream) {
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, part, dprobs, R, n_parts);
+  hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, part, dprobs, R, n_parts,
+                     rows_dev);
   return hipGetLastError();
 }
 

@@ -57,6 +57,10 @@ struct QuantArgs {
   const int32_t* row_index;
   int32_t index_rows;
   QuantGroups groups;
+  // non-null: the group table lives in device memory (built there from
+  // per-group sizes held on the device) and replaces `groups`; the grid is
+  // sized for the worst case and row tiles past the table's last one exit
+  const QuantGroups* groups_dev;
 };
 
 // Launch the quantize kernel (arguments already validated).
@@ -126,6 +130,10 @@ struct GemmArgs {
   int32_t split_f, split_s;
   float* split_ws;
   GemmGroups groups;
+  // non-null: the group table lives in device memory and replaces `groups`
+  // (k-tiled scales only, no split-K tail); the grid is sized for the worst
+  // case and workgroups past the table's tile count exit
+  const GemmGroups* groups_dev;
 };
 
 hipError_t launch_gemm(int mode, int epi, bool scale_dword, const GemmArgs& args, int total_tiles,
@@ -137,8 +145,32 @@ hipError_t launch_split_reduce(int epi, const GemmArgs& args, int tail_tiles, hi
 constexpr int kMaxSplitTiles = 128;
 constexpr int kMaxSplitParts = 4;
 
+// dprobs[r] = sum of the n_parts partials of row r; with rows_dev, rows at
+// or past *rows_dev are written 0.
 hipError_t launch_dprobs_reduce(const float* part, float* dprobs, int32_t R, int32_t n_parts,
-                                hipStream_t stream);
+                                const int32_t* rows_dev, hipStream_t stream);
+
+// Group tables of the fused MLP built on the device from per-expert row
+// counts held in device memory (no host round trip). The counts are clamped:
+// a negative count reads as 0 and a count that would take the running sum
+// past R is cut there, so every table stays inside the buffers sized for R
+// rows.
+struct MlpDevPlan {
+  int32_t rows;                     // sum of the clamped counts (<= R)
+  int32_t pad_;
+  QuantGroups act;                  // activation row groups (X, dY casts)
+  GemmGroups m[3];                  // group-M tables, one per n-tile count below
+  GemmGroups k[2];                  // group-K tables, one per tile count per slot below
+};
+struct MlpDevPlanArgs {
+  const int64_t* counts;            // [E] device
+  MlpDevPlan* plan;                 // device, written
+  int32_t E, R;
+  int32_t m_tiles_n[3];             // n-tiles per m-tile of each group-M table
+  int32_t k_slot_tiles[2];          // tiles per slot of each group-K table
+  int32_t k_interleave[2];          // interleave flag of each group-K table
+};
+hipError_t launch_mlp_dev_plan(const MlpDevPlanArgs& args, hipStream_t stream);
 
 // Token dispatch / combine around the grouped MLP (mx_moe.hip).
 constexpr int kMoeBlock = 256;      // entries per workgroup in the counting passes

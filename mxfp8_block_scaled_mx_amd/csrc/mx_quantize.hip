@@ -53,7 +53,13 @@ __device__ __forceinline__ void unpack16<float>(const uint4& raw, float* v) {
   v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
 }
 
-template <typename T>
+template <bool DEVG>
+__device__ __forceinline__ const QuantGroups& quant_groups(const QuantArgs& a) {
+  if constexpr (DEVG) return *a.groups_dev;
+  else return a.groups;
+}
+
+template <typename T, bool DEVG>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
   constexpr int VPT = QTraits<T>::kVals;
   constexpr int TC = QTraits<T>::kCols;
@@ -70,6 +76,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
   __shared__ uint8_t rs_t[TR * 4];           // rowwise scales [row][block]
   __shared__ uint8_t cs_t[TC * 4];           // columnwise scales [column][block]
 
+  const QuantGroups& G = quant_groups<DEVG>(args);
+  // a device-built table covers fewer row tiles than the worst-case grid
+  if constexpr (DEVG)
+    if ((int)blockIdx.x / args.n_col_tiles >= G.tile0[G.n]) return;
   const int tid = threadIdx.x;
   const int cc = tid & 15;                     // 16-byte chunk within the row segment
   const int64_t cols = args.cols;
@@ -83,15 +93,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
     Loc L;
     const int ct = t % args.n_col_tiles;
     const int rt_global = t / args.n_col_tiles;
-    int lo = 0, hi = args.groups.n - 1;        // last group with tile0 <= rt_global
+    int lo = 0, hi = G.n - 1;        // last group with tile0 <= rt_global
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (args.groups.tile0[mid] <= rt_global) lo = mid; else hi = mid - 1;
+      if (G.tile0[mid] <= rt_global) lo = mid; else hi = mid - 1;
     }
     L.g = lo;
-    L.tile_r0 = (rt_global - args.groups.tile0[lo]) * TR;   // first row of the tile within the group
-    L.grow0 = args.groups.row0[lo];
-    L.m_g = args.groups.row0[lo + 1] - args.groups.row0[lo];
+    L.tile_r0 = (rt_global - G.tile0[lo]) * TR;   // first row of the tile within the group
+    L.grow0 = G.row0[lo];
+    L.m_g = G.row0[lo + 1] - G.row0[lo];
     L.col_base = ct * TC;
     return L;
   };
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
     // Columnwise codes: each column's 128 tile rows are one contiguous run of the
     // layout; 8 lanes x 16 bytes per column. Blocks past the group's end are not
     // part of the layout (the next group's columns start there).
-    const int64_t qc0 = args.groups.pcol0[g] + tile_r0;
+    const int64_t qc0 = G.pcol0[g] + tile_r0;
 #pragma unroll
     for (int it = 0; it < TC * 8 / 256; ++it) {
       const int c = it * 256 + tid;
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
           // blocks past the group's end in its last step are cleared
           const int nvalid = (m_g - tile_r0 + 31) >> 5;
           if (nvalid < 4) word &= (1u << (8 * nvalid)) - 1u;
-          *reinterpret_cast<uint32_t*>(args.s_col + ((colc >> 5) * args.nq_col + args.groups.q0[g] + (tile_r0 >> 7)) * 128 +
+          *reinterpret_cast<uint32_t*>(args.s_col + ((colc >> 5) * args.nq_col + G.q0[g] + (tile_r0 >> 7)) * 128 +
                                        (colc & 31) * 4) = word;
         } else if (tile_r0 + 96 < m_g && ((args.ld_col | qc0) & 127) == 0 &&
                    (reinterpret_cast<uintptr_t>(args.s_col) & 3) == 0) {
@@ -266,10 +276,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs args) {
 hipError_t launch_quantize(const QuantArgs& args, int x_dtype, int total_row_tiles, hipStream_t stream) {
   const int64_t blocks = (int64_t)total_row_tiles * args.n_col_tiles;
   if (blocks == 0) return hipSuccess;
-  if (x_dtype == MX_BF16)
-    hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, args);
-  else
-    hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, args);
+  if (args.groups_dev != nullptr) {
+    if (x_dtype != MX_BF16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quantize_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, stream, args);
+  } else if (x_dtype == MX_BF16) {
+    hipLaunchKernelGGL((quantize_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((quantize_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, stream, args);
+  }
   return hipGetLastError();
 }
 

@@ -296,6 +296,48 @@ def test_moe_dispatch_noalloc_limits(L):
     assert d(x=ctypes.c_void_p(0x100008)) == EALIGN
 
 
+def test_device_split_sizes_cover_every_split(L):
+    # the device-split layout holds the largest padded total any split of R
+    # rows can reach, so it is at least the host-split size of each split
+    E, R, H, F = 4, 100, 128, 128
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.grouped_mlp_sizes_device_split(ctypes.byref(_dims(E, R, H, F)), ctypes.byref(f), ctypes.byref(s),
+                                            ctypes.byref(b)) == OK
+    for split in ([100, 0, 0, 0], [25, 25, 25, 25], [1, 1, 1, 97], [33, 33, 33, 1], [0, 0, 0, 100]):
+        hf, hs, hb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert L.grouped_mlp_sizes(ctypes.byref(_dims(E, R, H, F)), mx._i64_array(split), ctypes.byref(hf),
+                                   ctypes.byref(hs), ctypes.byref(hb)) == OK
+        # (less the host call's split-K partials, which the device-split call does not use)
+        split_k = min(sum(-(-m // 256) for m in split) * -(-H // 256), 128) * 4 * 256 * 256 * 4
+        assert hs.value <= s.value, split
+        assert hf.value - split_k <= f.value and hb.value - split_k <= b.value, split
+    assert L.grouped_mlp_sizes_device_split(ctypes.byref(_dims(E, R, 96, F)), None, None, None) == ESHAPE
+    assert L.grouped_mlp_sizes_device_split(None, None, None, None) == EINVAL
+
+
+def test_device_split_argument_errors(L):
+    E, R, H, F = 2, 64, 128, 128
+    d = _dims(E, R, H, F)
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    L.grouped_mlp_sizes_device_split(ctypes.byref(d), ctypes.byref(f), ctypes.byref(s), ctypes.byref(b))
+    ws = ctypes.c_void_p(0x100000)
+
+    def fwd(split=FAKE, w1=FAKE, cache=None, fb=f.value, rt=None, tokens=0):
+        return L.grouped_mlp_fwd_device_split(ctypes.byref(d), split, FAKE, tokens, rt, None, w1, FAKE, cache, 0,
+                                              FAKE, None, 0, ws, fb, None)
+
+    assert fwd(split=None) == EINVAL
+    assert fwd(split=ctypes.c_void_p(0x100004)) == EALIGN
+    assert fwd(fb=f.value - 1) == EWORKSPACE
+    assert fwd(w1=None) == EINVAL                                   # no weights and no cache
+    assert fwd(cache=ws) == EWORKSPACE                              # cache of 0 bytes
+    assert fwd(rt=FAKE, tokens=-1) == ESHAPE
+    assert L.grouped_mlp_bwd_device_split(ctypes.byref(d), None, FAKE, 0, None, None, None, 0, ws, s.value, FAKE,
+                                          None, FAKE, FAKE, 0, ws, b.value, None) == EINVAL
+    assert L.grouped_mlp_bwd_device_split(ctypes.byref(d), FAKE, FAKE, 0, None, None, None, 0, ws, s.value - 1,
+                                          FAKE, None, FAKE, FAKE, 0, ws, b.value, None) == EWORKSPACE
+
+
 def test_device_copy_argument_errors(L):
     # checked before any launch; a zero-byte copy enqueues nothing
     assert L.mx_device_copy(FAKE, FAKE, 24, None) == ESHAPE
