@@ -63,6 +63,13 @@ R15 MXFP4 GEMM: C = A . B^T with A [m, k] and B [n, k] both rowwise MXFP4
     (R14), each element taken at its value E2M1(code) * 2^(scale - 127); the
     pages name the format's GEMMs (mxfp4 runs) but not their arithmetic, so
     the plain product of the dequantized operands is the definition.
+R16 MXFP4 weight gradient: the columnwise MXFP4 layout pads each group
+    (expert) to a multiple of 32 rows exactly as R6 does for MXFP8, and the
+    group-K product C_g = A[:, K_g] . B[:, K_g]^T is R15 over group g's
+    padded range; fp32 accumulation into an existing main gradient adds C_g.
+    This is the wgrad the ROCm page says its FP4 GEMM library lacks (BF16
+    output only); its arithmetic is the MXFP8 group-K form with R15's
+    element values.
 """
 from __future__ import annotations
 
@@ -80,7 +87,7 @@ __all__ = [
     "moe_dispatch", "moe_combine", "e2m1_value", "e2m1_encode", "quantize_rowwise_fp4",
     "dequantize_rowwise_fp4", "gemm_fp4", "gemm_fp4_grouped", "E2M1_VALUES",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
-    "mlp_backward_wgrad_entries",
+    "mlp_backward_wgrad_entries", "quantize_colwise_fp4", "gemm_fp4_group_k",
 ]
 
 
@@ -675,3 +682,51 @@ def gemm_fp4_grouped(a_q, a_s, b_q, b_s, sizes):
             C[r0:r0 + sizes[g]] = gemm_fp4(a_q[r0:r0 + sizes[g]], a_s[r0:r0 + sizes[g]], b_q[g], b_s[g])
         r0 += sizes[g]
     return C
+
+
+def quantize_colwise_fp4(x, group_sizes=None):
+    """Columnwise MXFP4 with per-group padding, the 4-bit form of R6: each
+    group's rows are zero-padded to a multiple of 32, transposed and quantized
+    rowwise (R14); group g occupies columns [sum of earlier padded sizes,
+    + its padded size) of the [cols, sum P] result. Returns (packed codes
+    [cols, sum P / 2], scales [cols, sum P / 32])."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if group_sizes is None:
+        group_sizes = [rows]
+    sizes = np.asarray(group_sizes, dtype=np.int64)
+    if sizes.sum() != rows:
+        raise ValueError("group sizes must sum to rows")
+    P = padded_sizes(sizes)
+    q = np.zeros((cols, int(P.sum()) // 2), dtype=np.uint8)
+    s = np.zeros((cols, int(P.sum()) // BLOCK), dtype=np.uint8)
+    r0 = 0
+    c0 = 0
+    for m, p in zip(sizes.tolist(), P.tolist()):
+        if p:
+            padded = np.zeros((p, cols))
+            padded[:m] = x[r0:r0 + m]
+            qg, sg = quantize_rowwise_fp4(padded.T)
+            q[:, c0 // 2:(c0 + p) // 2] = qg
+            s[:, c0 // BLOCK:(c0 + p) // BLOCK] = sg
+        r0 += m
+        c0 += p
+    return q, s
+
+
+def gemm_fp4_group_k(a_q, a_s, b_q, b_s, sizes):
+    """The weight-gradient form at MXFP4: C_g = A[:, K_g] . B[:, K_g]^T with
+    K_g group g's padded column range (the columnwise layout above), for
+    A [M, sum P] and B [N, sum P] packed MXFP4 operands. Returns float64
+    [G, M, N]; a group with no rows gives zeros."""
+    A = dequantize_rowwise_fp4(a_q, a_s)
+    B = dequantize_rowwise_fp4(b_q, b_s)
+    P = padded_sizes(sizes)
+    C = np.zeros((len(P), A.shape[0], B.shape[0]))
+    k0 = 0
+    for g, p in enumerate(P.tolist()):
+        if p:
+            C[g] = A[:, k0:k0 + p] @ B[:, k0:k0 + p].T
+        k0 += p
+    return C
+
