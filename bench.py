@@ -380,7 +380,8 @@ def main():
         g4 = out["gemm_fp4"]
         log(f"MXFP4 GEMM {g4['workload']}: {g4['ms']:.3f} ms -> {g4['tflops']:.0f} TFLOP/s "
             f"({g4['roofline']['frac']:.3f} of the FP4 peak); grouped over the step's split_sizes "
-            f"{g4['grouped']['ms']:.3f} ms -> {g4['grouped']['tflops']:.0f} TFLOP/s")
+            f"{g4['grouped']['ms']:.3f} ms -> {g4['grouped']['tflops']:.0f} TFLOP/s; weight gradient "
+            f"{g4['wgrad']['ms']:.3f} ms -> {g4['wgrad']['tflops']:.0f} TFLOP/s")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -664,8 +665,11 @@ def measure_gemm_fp4(mx, torch, dev, split, iters=10, m=16384, n=28672, k=4096):
     """mx_gemm_fp4 (C = A . B^T, bf16 out) on random MXFP4 operands of the
     Mixtral MLP's first GEMM taken as one group: 16384 rows, 28672 columns,
     k = 4096; and mx_grouped_gemm_fp4 on the step's routed rows over its
-    split_sizes (one 28672 x 4096 weight per expert). 2 m n k flops per call,
-    priced at the FP4 MFMA peak."""
+    split_sizes (one 28672 x 4096 weight per expert); and
+    mx_grouped_gemm_fp4_wgrad for the same experts' first weight gradient
+    (28672 x 4096 per expert, summed over its routed rows). 2 m n k flops per
+    call (k = routed rows for the weight gradient), priced at the FP4 MFMA
+    peak."""
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     aq = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device=dev, generator=g)
@@ -702,8 +706,29 @@ def measure_gemm_fp4(mx, torch, dev, split, iters=10, m=16384, n=28672, k=4096):
     tfg = 2.0 * mg * n * k / (msg * 1e-3) / 1e12
     grouped = {"workload": f"grouped_gemm_fp4_{mg}x{n}x{k}_{G}experts", "split_sizes": [int(v) for v in split],
                "ms": round(msg, 4), "tflops": round(tfg, 1), "frac_fp4_peak": round(tfg / PEAK_FP4_TFLOPS, 4)}
+    del bgq, bgs, cg
+    # weight gradient: dW1[e] = dH[e]^T X[e] (m = n_ffn rows of dH's columnwise
+    # copy, n = k = hidden), summed over each expert's routed rows padded to 32
+    kw = sum(-(-int(v) // 32) * 32 for v in split)
+    wq = torch.randint(0, 256, (n, kw // 2), dtype=torch.uint8, device=dev, generator=g)
+    ws = torch.randint(122, 133, (n, kw // 32), dtype=torch.uint8, device=dev, generator=g)
+    xq = torch.randint(0, 256, (k, kw // 2), dtype=torch.uint8, device=dev, generator=g)
+    xs = torch.randint(122, 133, (k, kw // 32), dtype=torch.uint8, device=dev, generator=g)
+    cw = torch.empty((G, n, k), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        mx.mx_grouped_gemm_fp4_wgrad(wq, ws, xq, xs, split, out=cw)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        mx.mx_grouped_gemm_fp4_wgrad(wq, ws, xq, xs, split, out=cw)
+    e1.record()
+    torch.cuda.synchronize()
+    msw = e0.elapsed_time(e1) / iters
+    tfw = 2.0 * mg * n * k / (msw * 1e-3) / 1e12
+    wgrad = {"workload": f"grouped_gemm_fp4_wgrad_{n}x{k}x{mg}_{G}experts", "ms": round(msw, 4),
+             "tflops": round(tfw, 1), "frac_fp4_peak": round(tfw / PEAK_FP4_TFLOPS, 4)}
     return {"workload": f"gemm_fp4_{m}x{n}x{k}", "ms": round(ms, 4), "tflops": round(tflops, 1),
-            "grouped": grouped,
+            "grouped": grouped, "wgrad": wgrad,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP4_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}}
 

@@ -399,6 +399,50 @@ MX_API mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const
                                      const int64_t* group_sizes, int32_t groups, int64_t n, int64_t k, void* c,
                                      mx_dtype c_dtype, void* stream);
 
+/*
+ * mx_quantize_fp4_colwise_grouped -- columnwise MXFP4 of a routed activation
+ * with per-expert padding, the layout of the 4-bit weight gradient (the
+ * MXFP4 form of the grouped columnwise MXFP8 layout above; MXFP4 as in
+ * mx_quantize_fp4): the rows of x (bf16 [rows, cols], contiguous) are split
+ * into `groups` consecutive groups of group_sizes[g] rows; each group's rows
+ * are zero-padded to P_g = a multiple of 32 and, transposed, quantized in
+ * blocks of 32 along the rows.
+ *   q_col  codes [cols, sum P_g / 2] (two per byte, low nibble first),
+ *          group g at bytes [sum_{g'<g} P_g' / 2, + P_g / 2) of every row;
+ *   s_col  E8M0 scales [cols, sum P_g / 32].
+ * Every byte of both outputs is written (padding rows give code 0).
+ * Errors: MX_ESHAPE (cols not a positive multiple of 32, negative sizes or
+ * sizes not summing to rows), MX_EINVAL (groups outside 1..MX_MAX_GROUPS,
+ * null pointers), MX_EALIGN (x or q_col not 16-byte aligned),
+ * MX_EUNSUPPORTED (too large), MX_EHIP.
+ *
+ * mx_grouped_gemm_fp4_wgrad -- the weight-gradient (group-K) GEMM at MXFP4
+ * with fp32 accumulation into a main gradient:
+ *   C_g (+)= A[:, K_g] . B[:, K_g]^T   for every group g,
+ * K_g = group g's padded range [sum_{g'<g} P_g', + P_g) of the contraction
+ * (P_g = group_sizes[g] rounded up to a multiple of 32), with A [m, K] and
+ * B [n, K] (K = sum P_g) in the layout mx_quantize_fp4_colwise_grouped
+ * writes (codes [m, K/2], scales [m, K/32]; likewise B). Elements are
+ * E2M1(code) * 2^(scale - 127) and the products are exact; the sums are fp32
+ * on the scaled MFMA. c is fp32 [groups, m, n] (group g at c + g*m*n,
+ * row-major); accumulate != 0 adds into it (a group with no rows leaves its
+ * C_g unchanged), else C_g is overwritten (zeros for a group with no rows).
+ * The ROCm MI355X recipe notes that its 4-bit wgrad GEMM emits BF16 only,
+ * which breaks fp32 main-gradient accumulation ("examples/llama: default-on
+ * fusion & DP-comm perf toggles - #141", the GRAD_REDUCE_IN_BF16 guard);
+ * this call is that fp32-accumulating form.
+ * Errors: MX_EINVAL (groups outside 1..MX_MAX_GROUPS, null pointers),
+ * MX_ESHAPE (negative sizes), MX_EALIGN (a, b, c not 16-byte aligned),
+ * MX_EUNSUPPORTED (K above 2^24 or too many tiles), MX_EHIP.
+ */
+MX_API mx_status mx_quantize_fp4_colwise_grouped(const void* x, int64_t rows, int64_t cols,
+                                                 const int64_t* group_sizes, int32_t groups,
+                                                 uint8_t* q_col, uint8_t* s_col, void* stream);
+MX_API mx_status mx_grouped_gemm_fp4_wgrad(const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
+                                           const uint8_t* b_s, const int64_t* group_sizes, int32_t groups,
+                                           int64_t m, int64_t n, float* c, int32_t accumulate,
+                                           void* stream);
+
 MX_API size_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int32_t topk, int32_t num_experts);
 
 /*

@@ -126,6 +126,10 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_bwd_device_split.restype = ctypes.c_int
     L.grouped_mlp_bwd_device_split.argtypes = [ctypes.POINTER(_Dims), vp, vp, i64, vp, vp, vp, sz, vp, sz, vp, vp,
                                                vp, vp, i32, vp, sz, vp]
+    L.mx_quantize_fp4_colwise_grouped.restype = ctypes.c_int
+    L.mx_quantize_fp4_colwise_grouped.argtypes = [vp, i64, i64, p64, i32, vp, vp, vp]
+    L.mx_grouped_gemm_fp4_wgrad.restype = ctypes.c_int
+    L.mx_grouped_gemm_fp4_wgrad.argtypes = [vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
     L.mx_device_copy.restype = ctypes.c_int
     L.mx_device_copy.argtypes = [vp, vp, i64, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
@@ -575,6 +579,47 @@ def mx_grouped_gemm_fp4(a_q, a_s, b_q, b_s, group_sizes, out_dtype=torch.bfloat1
     arr = (ctypes.c_int64 * max(G, 1))(*sizes)
     _check(L.mx_grouped_gemm_fp4(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), arr, G, n, k, _ptr(out), dt,
                                  _stream(stream)))
+    return out
+
+
+def mx_quantize_fp4_colwise_grouped(x, group_sizes, stream=None):
+    """Columnwise MXFP4 of bf16 x [rows, cols] with per-group padding to 32
+    rows: (q_col [cols, sum P / 2], s_col [cols, sum P / 32])."""
+    if not (isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+            and x.is_cuda):
+        raise ValueError("mx_quantize_fp4_colwise_grouped: x must be a contiguous 2-D bfloat16 CUDA tensor")
+    sizes = [int(v) for v in group_sizes]
+    rows, cols = x.shape
+    if not sizes or sum(sizes) != rows or min(sizes) < 0:
+        raise ValueError(f"mx_quantize_fp4_colwise_grouped: group sizes {sizes} must be >= 0 and sum to {rows}")
+    P = sum(padded_sizes(sizes))
+    L = load()
+    qc = torch.empty((cols, P // 2), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((cols, P // 32), dtype=torch.uint8, device=x.device)
+    _check(L.mx_quantize_fp4_colwise_grouped(_ptr(x), rows, cols, _i64_array(sizes), len(sizes), _ptr(qc), _ptr(sc),
+                                             _stream(stream)))
+    return qc, sc
+
+
+def mx_grouped_gemm_fp4_wgrad(a_q, a_s, b_q, b_s, group_sizes, out=None, accumulate=False, stream=None):
+    """Weight-gradient GEMM at MXFP4: C_g (+)= A[:, K_g] . B[:, K_g]^T per
+    group, A (a_q [m, K/2], a_s [m, K/32]) and B [n, K] in the grouped
+    columnwise layout, K = sum of the padded group sizes; returns fp32
+    C [G, m, n] (out, accumulated into when accumulate)."""
+    sizes = [int(v) for v in group_sizes]
+    G = len(sizes)
+    K = sum(padded_sizes(sizes))
+    m, n = a_q.shape[0], b_q.shape[0]
+    _expect_all([(a_q, (m, K // 2), torch.uint8, "a_q", False), (a_s, (m, K // 32), torch.uint8, "a_s", False),
+                 (b_q, (n, K // 2), torch.uint8, "b_q", False), (b_s, (n, K // 32), torch.uint8, "b_s", False),
+                 (out, (G, m, n), torch.float32, "out", True)])
+    if accumulate and out is None:
+        raise ValueError("mx_grouped_gemm_fp4_wgrad: accumulate needs out")
+    if out is None:
+        out = torch.empty((G, m, n), dtype=torch.float32, device=a_q.device)
+    L = load()
+    _check(L.mx_grouped_gemm_fp4_wgrad(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _i64_array(sizes), G, m, n,
+                                       _ptr(out), int(bool(accumulate)), _stream(stream)))
     return out
 
 

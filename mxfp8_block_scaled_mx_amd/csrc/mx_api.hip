@@ -1280,4 +1280,66 @@ mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const uint8_
   return gemm_fp4_impl("mx_grouped_gemm_fp4", a, a_s, b, b_s, group_sizes, groups, n, k, c, c_dtype, stream);
 }
 
+mx_status mx_quantize_fp4_colwise_grouped(const void* x, int64_t rows, int64_t cols, const int64_t* group_sizes,
+                                          int32_t groups, uint8_t* q_col, uint8_t* s_col, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_quantize_fp4_colwise_grouped";
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MX_ESHAPE, "%s: need rows >= 0 and cols a positive multiple of 32", who);
+  if (groups < 1 || groups > mx::kMaxGroups) return fail(MX_EINVAL, "%s: need 1 <= groups <= %d", who, mx::kMaxGroups);
+  mx_status st = check_groups(group_sizes, groups, rows, who);
+  if (st != MX_OK) return st;
+  if (!q_col || !s_col || (rows > 0 && !x)) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(q_col, 16)) return fail(MX_EALIGN, "%s: x and q_col must be 16-byte aligned", who);
+  mx::Fp4ColGroups gr{};
+  gr.n = groups;
+  int64_t r0 = 0, p0 = 0, t0 = 0;
+  for (int g = 0; g < groups; ++g) {
+    gr.row0[g] = r0;
+    gr.pcol0[g] = p0;
+    gr.tile0[g] = (int32_t)t0;
+    r0 += group_sizes[g];
+    p0 += pad32(group_sizes[g]);
+    t0 += cdiv(group_sizes[g], 128);
+  }
+  gr.row0[groups] = r0;
+  gr.pcol0[groups] = p0;
+  gr.tile0[groups] = (int32_t)t0;
+  if (t0 * cdiv(cols, 64) > kI32Max || p0 * cols > ((int64_t)1 << 40))
+    return fail(MX_EUNSUPPORTED, "%s: tensor too large", who);
+  hipError_t e = mx::launch_quantize_fp4_grouped(x, rows, cols, gr, q_col, s_col, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_quantize_fp4_colwise_grouped launch");
+  return MX_OK;
+}
+
+mx_status mx_grouped_gemm_fp4_wgrad(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                                    const int64_t* group_sizes, int32_t groups, int64_t m, int64_t n, float* c,
+                                    int32_t accumulate, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_grouped_gemm_fp4_wgrad";
+  if (groups < 1 || groups > mx::kMaxGroups) return fail(MX_EINVAL, "%s: need 1 <= groups <= %d", who, mx::kMaxGroups);
+  if (!group_sizes) return fail(MX_EINVAL, "%s: null group sizes", who);
+  if (m < 0 || n < 0) return fail(MX_ESHAPE, "%s: need m >= 0 and n >= 0", who);
+  mx::Fp4KGroups kg{};
+  kg.n = groups;
+  int64_t k = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (group_sizes[g] < 0) return fail(MX_ESHAPE, "%s: negative group size", who);
+    kg.k0[g] = k;
+    k += pad32(group_sizes[g]);
+  }
+  kg.k0[groups] = k;
+  if (k > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: padded rows above 2^24", who);
+  const int64_t tiles = (int64_t)groups * cdiv(m, mx::kFp4GemmTileM) * cdiv(n, mx::kFp4GemmTileN);
+  if (tiles > kI32Max || (int64_t)groups * m * n > ((int64_t)1 << 40))
+    return fail(MX_EUNSUPPORTED, "%s: output too large", who);
+  if (m == 0 || n == 0) return MX_OK;
+  if (!c || (k > 0 && (!a || !a_s || !b || !b_s))) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
+    return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
+  hipError_t e = mx::launch_gemm_fp4_group_k(a, a_s, b, b_s, kg, m, n, c, accumulate ? 1 : 0,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, who);
+  return MX_OK;
+}
+
 }  // extern "C"

@@ -70,23 +70,36 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
 // amax locally and stores its 16 code bytes as one piece of the column's run.
 // With q_row given, the same tile also yields the rowwise copy (thread t takes
 // row t / 2, 32-column block t % 2), so both layouts cost one read of x.
+// Grouped (per-expert) columnwise layout: row tiles restart at each group's
+// first row, rows past the group's end read as zeros, and group g's padded
+// rows land at columns [pcol0[g], + pad32(m_g)) of the [cols, sum P] result.
+// One group of all rows is the plain columnwise cast.
 constexpr int kFp4ColTileRows = 128, kFp4ColTileCols = 64;
 __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s, uint8_t* q_row,
-                                                                   uint8_t* s_row) {
+                                                                   uint8_t* s_row, Fp4ColGroups gr, int64_t ldp) {
   // [row][column] bf16 with a 2-element pad so that the column reads of a
   // wave (64 columns of one row) spread over the banks
   __shared__ __attribute__((aligned(16))) uint16_t tile[kFp4ColTileRows][kFp4ColTileCols + 2];
   const int64_t n_ct = (cols + kFp4ColTileCols - 1) / kFp4ColTileCols;
-  const int64_t r0 = (int64_t)(blockIdx.x / n_ct) * kFp4ColTileRows;
+  const int rt = (int)(blockIdx.x / n_ct);
   const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * kFp4ColTileCols;
+  int lo = 0, hi = gr.n - 1;                  // last group whose first tile is <= rt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gr.tile0[mid] <= rt) lo = mid; else hi = mid - 1;
+  }
+  const int64_t lr0 = (int64_t)(rt - gr.tile0[lo]) * kFp4ColTileRows;   // first row of the tile in its group
+  const int64_t r0 = gr.row0[lo] + lr0;                                  // its global row
+  const int64_t m_g = gr.row0[lo + 1] - gr.row0[lo];
+  const int64_t p_g = (m_g + 31) / 32 * 32;
   const int tid = threadIdx.x;
   // 128 rows x 8 pieces of 16 bytes (8 columns each): 4 pieces per thread
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int p = it * 256 + tid, rr = p >> 3, cp = (p & 7) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < rows && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
+    if (lr0 + rr < m_g && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
     const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
                            (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
 #pragma unroll
@@ -96,7 +109,7 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
   if (q_row != nullptr) {
     const int rr = tid >> 1, bb = tid & 1;
     const int64_t row = r0 + rr, col = c0 + 32 * bb;
-    if (row < rows && col < cols) {
+    if (lr0 + rr < m_g && col < cols) {
       float v[32];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -123,8 +136,9 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
     }
   }
   const int c = tid % kFp4ColTileCols, rb = tid / kFp4ColTileCols;
-  const int64_t col = c0 + c, row = r0 + 32 * rb;
-  if (col >= cols || row >= rows) return;
+  const int64_t col = c0 + c, lrow = lr0 + 32 * rb;          // block's first row in the group
+  if (col >= cols || lrow >= p_g) return;
+  const int64_t pcol = gr.pcol0[lo] + lrow;                   // its position in the columnwise layout
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[32 * rb + i][c] << 16);
@@ -142,8 +156,8 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
     for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
     w[i] = word;
   }
-  *reinterpret_cast<uint4*>(q + col * (rows / 2) + row / 2) = make_uint4(w[0], w[1], w[2], w[3]);
-  s[col * (rows / 32) + row / 32] = (uint8_t)sc;
+  *reinterpret_cast<uint4*>(q + col * (ldp / 2) + pcol / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  s[col * (ldp / 32) + pcol / 32] = (uint8_t)sc;
 }
 
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
@@ -156,11 +170,28 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
     hipLaunchKernelGGL(quantize_fp4_rowwise_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream,
                        xb, rows, cols, q, s);
   if (q_col != nullptr && rows > 0) {
-    const int64_t tiles = ((rows + kFp4ColTileRows - 1) / kFp4ColTileRows) *
-                          ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
+    Fp4ColGroups gr{};
+    gr.n = 1;
+    gr.row0[0] = 0;
+    gr.row0[1] = rows;
+    gr.pcol0[0] = 0;
+    gr.pcol0[1] = rows;
+    gr.tile0[0] = 0;
+    gr.tile0[1] = (int32_t)((rows + kFp4ColTileRows - 1) / kFp4ColTileRows);
+    const int64_t tiles = (int64_t)gr.tile0[1] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows, cols,
-                       q_col, s_col, fused ? q : nullptr, fused ? s : nullptr);
+                       q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp4_grouped(const void* x, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
+                                       uint8_t* q_col, uint8_t* s_col, hipStream_t stream) {
+  const int64_t tiles = (int64_t)gr.tile0[gr.n] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), rows, cols, q_col, s_col, nullptr, nullptr, gr,
+                     (int64_t)gr.pcol0[gr.n]);
   return hipGetLastError();
 }
 
@@ -191,9 +222,17 @@ constexpr int kF4SubM = 4, kF4SubN = 4;     // wave tile: MFMA tiles of 32 x 32
 constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
 static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
 
+// GK: the group-K (weight-gradient) form. The workgroup takes tile (mt, nt)
+// of group g's output C_g [M, N] (all groups' tiles in group order), over
+// group g's k range [k0[g], k0[g+1]) of A [M, K] and B [N, K]; a last k-step
+// that holds only 32 valid values gets scale code 0 for the invalid half on
+// both operands, so its products (at most 36 * 2^-254) add exact zeros
+// whatever codes lie past the group; C_g is fp32, stored or accumulated.
+template <bool GK>
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
-                                                       const uint8_t* bs, Fp4Groups gr, int64_t N, int64_t K,
-                                                       int64_t n_tiles_n, void* c, int32_t c_f32) {
+                                                       const uint8_t* bs, Fp4Groups gr, Fp4KGroups kg, int64_t M,
+                                                       int64_t N, int64_t K, int64_t n_tiles_n, void* c,
+                                                       int32_t c_f32, int32_t accumulate) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
@@ -202,25 +241,45 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
-  const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
-  // group of m-tile mt: the last group whose first m-tile is <= mt (empty
-  // groups own no m-tile)
-  int lo = 0, hi = gr.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (gr.tile0[mid] <= mt) lo = mid; else hi = mid - 1;
+  int grp;   // the group (expert) of this tile
+  int64_t row_end, am0, bn0, kbeg = 0, klen = K;
+  if constexpr (GK) {
+    const int64_t per_group = ((M + TM - 1) / TM) * n_tiles_n;
+    grp = (int)(blockIdx.x / per_group);
+    const int64_t rem = blockIdx.x - grp * per_group;
+    const int64_t mt = rem / n_tiles_n, nt = rem - mt * n_tiles_n;
+    row_end = M;
+    am0 = mt * TM;
+    bn0 = nt * TN;
+    kbeg = kg.k0[grp];
+    klen = kg.k0[grp + 1] - kbeg;
+  } else {
+    const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
+    // group of m-tile mt: the last group whose first m-tile is <= mt (empty
+    // groups own no m-tile)
+    int lo = 0, hi = gr.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gr.tile0[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    grp = lo;
+    row_end = gr.row0[grp + 1];               // rows of the group end here
+    am0 = gr.row0[grp] + (mt - gr.tile0[grp]) * TM;
+    bn0 = nt * TN;
   }
-  const int g = lo;
-  const int64_t row_end = gr.row0[g + 1];     // rows of the group end here
-  const int64_t am0 = gr.row0[g] + (mt - gr.tile0[g]) * TM, bn0 = nt * TN;
   const int64_t amv = min<int64_t>(TM, row_end - am0), bnv = min<int64_t>(TN, N - bn0);
   const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + am0 * ldq, amv * ldq);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + (g * N + bn0) * ldq, bnv * ldq);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds, amv * lds);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + (g * N + bn0) * lds, bnv * lds);
-  const int ksteps = (int)(K / 64), ktiles = (ksteps + 3) / 4;
-  const bool sc_dword = (lds & 7) == 0;       // a row's 8 scales of a k-tile: one aligned 8-byte load
+  // group-M: B_g is rows [g N, g N + N) of b; group-K: one B, the group's k range
+  const int64_t brow0 = GK ? bn0 : grp * N + bn0;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + am0 * ldq + kbeg / 2, (amv - 1) * ldq + klen / 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + brow0 * ldq + kbeg / 2, (bnv - 1) * ldq + klen / 2);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds + kbeg / 32, (amv - 1) * lds + klen / 32);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + brow0 * lds + kbeg / 32, (bnv - 1) * lds + klen / 32);
+  const int ksteps = (int)((klen + 63) / 64), ktiles = (ksteps + 3) / 4;
+  // a row's 8 scales of a k-tile: one aligned 8-byte load. The k range must
+  // also be whole k-tiles: the last row's load would otherwise reach past
+  // the resource's extent and come back as zero scales.
+  const bool sc_dword = (lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0;
 
   // global -> LDS by buffer DMA, 1 KB (8 rows) per instruction: lane L
   // fills chunk L % 8 of row L / 8 of the block with global chunk
@@ -303,14 +362,16 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
         v8i fb[SN];
 #pragma unroll
         for (int j = 0; j < SN; ++j) fb[j] = frag(B, 32 * j + l32, s);
+        // group-K: this lane's block past the group's k range scales to 0
+        const bool blk_ok = !GK || (int64_t)(8 * t + 2 * s + h) * 32 < klen;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
           const v8i fa = frag(A, 32 * i + l32, s);
-          const int sai = pick(sca[i], s);
+          const int sai = blk_ok ? pick(sca[i], s) : 0;
 #pragma unroll
           for (int j = 0; j < SN; ++j)
             acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa, acc[j][i], kE2M1, kE2M1, 0,
-                                                                        pick(scb[j], s), 0, sai);
+                                                                        blk_ok ? pick(scb[j], s) : 0, 0, sai);
         }
       }
     }
@@ -341,14 +402,20 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
         const float x0 = vgpr_hop(acc[j][i][4 * g]), x1 = vgpr_hop(acc[j][i][4 * g + 1]);
         const float x2 = vgpr_hop(acc[j][i][4 * g + 2]), x3 = vgpr_hop(acc[j][i][4 * g + 3]);
         if (c_f32) {
-          float* cp = reinterpret_cast<float*>(c) + row * N + col;
+          float* cp = reinterpret_cast<float*>(c) + (GK ? (int64_t)grp * M * N : 0) + row * N + col;
           if (vec && col + 3 < N) {
-            *reinterpret_cast<float4*>(cp) = make_float4(x0, x1, x2, x3);
+            float4 v = make_float4(x0, x1, x2, x3);
+            if (GK && accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(cp);
+              v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+            }
+            *reinterpret_cast<float4*>(cp) = v;
           } else {
-            if (col < N) cp[0] = x0;
-            if (col + 1 < N) cp[1] = x1;
-            if (col + 2 < N) cp[2] = x2;
-            if (col + 3 < N) cp[3] = x3;
+            const bool add = GK && accumulate;
+            if (col < N) cp[0] = add ? cp[0] + x0 : x0;
+            if (col + 1 < N) cp[1] = add ? cp[1] + x1 : x1;
+            if (col + 2 < N) cp[2] = add ? cp[2] + x2 : x2;
+            if (col + 3 < N) cp[3] = add ? cp[3] + x3 : x3;
           }
         } else {
           uint16_t* cp = reinterpret_cast<uint16_t*>(c) + row * N + col;
@@ -369,8 +436,21 @@ hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b
                            const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
   const int64_t tm = gr.tile0[gr.n], tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
   if (tm * tn == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_fp4_kernel, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, gr, N, K, tn, c,
-                     c_f32);
+  Fp4KGroups kg{};
+  hipLaunchKernelGGL(gemm_fp4_kernel<false>, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, gr, kg,
+                     (int64_t)0, N, K, tn, c, c_f32, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp4_group_k(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                   const Fp4KGroups& kg, int64_t M, int64_t N, float* c, int32_t accumulate,
+                                   hipStream_t stream) {
+  const int64_t tm = (M + kFp4GemmTileM - 1) / kFp4GemmTileM, tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
+  const int64_t tiles = (int64_t)kg.n * tm * tn;
+  if (tiles == 0) return hipSuccess;
+  Fp4Groups gr{};
+  hipLaunchKernelGGL(gemm_fp4_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs, gr, kg, M, N,
+                     kg.k0[kg.n], tn, c, 1, accumulate);
   return hipGetLastError();
 }
 

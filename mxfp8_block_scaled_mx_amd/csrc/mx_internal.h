@@ -209,6 +209,28 @@ struct Fp4Groups {
 };
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                            const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
+// Groups of the columnwise MXFP4 cast: group g's rows [row0[g], row0[g+1]),
+// padded to a multiple of 32 at columns [pcol0[g], pcol0[g+1]) of the
+// result; its 128-row tiles are tile0[g] .. tile0[g+1] - 1.
+struct Fp4ColGroups {
+  int32_t n;
+  int32_t tile0[kMaxGroups + 1];
+  int64_t row0[kMaxGroups + 1];
+  int64_t pcol0[kMaxGroups + 1];
+};
+hipError_t launch_quantize_fp4_grouped(const void* x, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
+                                       uint8_t* q_col, uint8_t* s_col, hipStream_t stream);
+// MXFP4 group-K product C_g (+)= A[:, K_g] . B[:, K_g]^T (fp32), K_g =
+// [k0[g], k0[g+1]) in values (multiples of 32): A [M, k0[n]] and B
+// [N, k0[n]] rowwise-packed MXFP4 (the columnwise layouts of two routed
+// activations); C_g at c + g * M * N, row-major [M, N].
+struct Fp4KGroups {
+  int32_t n;
+  int64_t k0[kMaxGroups + 1];
+};
+hipError_t launch_gemm_fp4_group_k(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                   const Fp4KGroups& gr, int64_t M, int64_t N, float* c, int32_t accumulate,
+                                   hipStream_t stream);
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;

@@ -338,6 +338,26 @@ def test_device_split_argument_errors(L):
                                           FAKE, None, FAKE, FAKE, 0, ws, b.value, None) == EWORKSPACE
 
 
+def test_fp4_wgrad_and_grouped_cast_argument_errors(L):
+    sizes = mx._i64_array([20, 44])
+    def cast(rows=64, cols=64, sz=sizes, g=2, x=FAKE, q=FAKE):
+        return L.mx_quantize_fp4_colwise_grouped(x, rows, cols, sz, g, q, FAKE, None)
+    assert cast(cols=48) == ESHAPE
+    assert cast(rows=63) == ESHAPE                       # sizes do not sum to rows
+    assert cast(g=0) == EINVAL
+    assert cast(q=None) == EINVAL
+    assert cast(x=ctypes.c_void_p(0x100008)) == EALIGN
+    def wg(g=2, m=64, n=64, sz=sizes, c=FAKE, a=FAKE):
+        return L.mx_grouped_gemm_fp4_wgrad(a, FAKE, FAKE, FAKE, sz, g, m, n, c, 0, None)
+    assert wg(g=0) == EINVAL
+    assert wg(g=129, sz=mx._i64_array([1] * 129)) == EINVAL
+    assert wg(m=-1) == ESHAPE
+    assert wg(sz=mx._i64_array([20, -4])) == ESHAPE
+    assert wg(c=None) == EINVAL
+    assert wg(a=ctypes.c_void_p(0x100008)) == EALIGN
+    assert wg(m=0) == OK                                 # nothing to compute, nothing enqueued
+
+
 def test_device_copy_argument_errors(L):
     # checked before any launch; a zero-byte copy enqueues nothing
     assert L.mx_device_copy(FAKE, FAKE, 24, None) == ESHAPE
