@@ -70,6 +70,16 @@ R16 MXFP4 weight gradient: the columnwise MXFP4 layout pads each group
     This is the wgrad the ROCm page says its FP4 GEMM library lacks (BF16
     output only); its arithmetic is the MXFP8 group-K form with R15's
     element values.
+R17 MXFP4 MLP: the MLP of R7-R11 with every MXFP8 copy replaced by the MXFP4
+    copy (R14) along the same axis -- rowwise along each forward GEMM's
+    contraction axis, the straight-through backward's copies as R9 names
+    them, columnwise copies padded per expert as R16 -- and every other step
+    unchanged (A formed before requantization, H1 saved in bf16, Y and dX
+    rounded to bf16, dW and dprobs unrounded). The Llama 3 recipe page
+    assigns whole layers to FP8 or to FP4 and the ROCm page runs every layer
+    of its mxfp4 model in FP4, so an FP4 layer's MLP runs its GEMMs on MXFP4
+    copies; that the recipe is otherwise the MXFP8 one is the plainest
+    reading. Selected by quantize="mxfp4" in the MLP functions below.
 """
 from __future__ import annotations
 
@@ -297,9 +307,24 @@ def silu(x):
     return x * sigmoid(x)
 
 
+def _fmt(quantize):
+    """The block format an MLP function's `quantize` argument names: False
+    (none, float64), True or "mxfp8" (R1-R6), "mxfp4" (R14, R16, R17)."""
+    if quantize is False or quantize is None:
+        return None
+    if quantize is True or quantize == "mxfp8":
+        return "mxfp8"
+    if quantize == "mxfp4":
+        return "mxfp4"
+    raise ValueError(f"unknown block format {quantize!r}")
+
+
 def _qdq_row(x, quantize):
-    if not quantize:
+    f = _fmt(quantize)
+    if f is None:
         return np.asarray(x, dtype=np.float64)
+    if f == "mxfp4":
+        return dequantize_rowwise_fp4(*quantize_rowwise_fp4(x))
     return dequantize_rowwise(*quantize_rowwise(x))
 
 
@@ -307,9 +332,13 @@ def _qdq_col(x, quantize):
     """Columnwise quantize-dequantize of one group's [m, cols] matrix, returned
     in the original [m, cols] orientation."""
     x = np.asarray(x, dtype=np.float64)
-    if not quantize:
+    f = _fmt(quantize)
+    if f is None:
         return x
     m = x.shape[0]
+    if f == "mxfp4":
+        q, s = quantize_colwise_fp4(x)
+        return dequantize_rowwise_fp4(q, s)[:, :m].T
     q, s = quantize_colwise(x)
     return dequantize_rowwise(q, s)[:, :m].T
 
@@ -333,7 +362,9 @@ def mlp_forward(x, probs, w1, w2, split_sizes, *, quantize=True):
       H1 = Xq_e . W1q_e^T; g = H1[:, :F], u = H1[:, F:];
       A  = w * silu(g) * u   (R8);   Y = Aq . W2q_e^T  (rounded to bf16).
     x [R,H], w1 [E,2F,H], w2 [E,H,F] as bf16 bits or float; probs [R].
-    quantize=False gives the unquantized float64 MLP (for derivative checks).
+    quantize=True (or "mxfp8") runs the GEMMs on MXFP8 copies, "mxfp4" on
+    MXFP4 copies (R17); False gives the unquantized float64 MLP (for
+    derivative checks).
     Returns dict(y, y_exact, h1, h1_bf16, a)."""
     X = _as_f64(x)
     p = np.asarray(probs, dtype=np.float64)
@@ -388,7 +419,7 @@ def mlp_backward(x, probs, w1, w2, split_sizes, dy, fwd, *, quantize=True,
     F = w1.shape[1] // 2
     R, H = X.shape
     off = _offsets(split_sizes)
-    h1 = fwd["h1_bf16"] if quantize else fwd["h1"]
+    h1 = fwd["h1_bf16"] if _fmt(quantize) else fwd["h1"]
     A = fwd["a"]
     dX = np.zeros((R, H))
     dP = np.zeros(R)
@@ -424,8 +455,9 @@ def _expert_of_rows(split_sizes, rows):
     return np.searchsorted(off, np.asarray(rows), side="right") - 1
 
 
-def mlp_forward_rows(x, probs, w1, w2, split_sizes, rows):
-    """Y (bf16-rounded) and A for the selected rows only.
+def mlp_forward_rows(x, probs, w1, w2, split_sizes, rows, quantize=True):
+    """Y (bf16-rounded) and A for the selected rows only (quantize names the
+    block format as in mlp_forward).
 
     Rowwise quantization acts on one row at a time, so a row's Y depends only
     on that row, its routing weight and its expert's weights."""
@@ -440,19 +472,19 @@ def mlp_forward_rows(x, probs, w1, w2, split_sizes, rows):
     for e in np.unique(ex):
         sel = np.nonzero(ex == e)[0]
         r = rows[sel]
-        Xh = _qdq_row(_as_f64(x[r]), True)
-        W1h = _qdq_row(_as_f64(w1[e]), True)
+        Xh = _qdq_row(_as_f64(x[r]), quantize)
+        W1h = _qdq_row(_as_f64(w1[e]), quantize)
         h1 = Xh @ W1h.T
         del W1h
         a = p[r, None] * silu(h1[:, :F]) * h1[:, F:]
-        W2h = _qdq_row(_as_f64(w2[e]), True)
-        Y[sel] = _qdq_row(a, True) @ W2h.T
+        W2h = _qdq_row(_as_f64(w2[e]), quantize)
+        Y[sel] = _qdq_row(a, quantize) @ W2h.T
         A[sel] = a
         H1[sel] = h1
     return dict(y=round_to_bf16(Y), a=A, h1_bf16=round_to_bf16(H1))
 
 
-def _expert_dh1(x, probs, w1, w2, split_sizes, dy, e, r_sel=None):
+def _expert_dh1(x, probs, w1, w2, split_sizes, dy, e, r_sel=None, quantize=True):
     """dH1 rows of expert e (all its rows, or the positions r_sel within it),
     from the fwd's bf16 H1 and the straight-through dA.  Also returns dprobs of
     those rows and the unrounded H1 (from which the forward formed A)."""
@@ -460,18 +492,18 @@ def _expert_dh1(x, probs, w1, w2, split_sizes, dy, e, r_sel=None):
     r0, r1 = int(off[e]), int(off[e + 1])
     F = w1.shape[1] // 2
     idx = np.arange(r0, r1) if r_sel is None else r0 + np.asarray(r_sel)
-    Xh = _qdq_row(_as_f64(x[idx]), True)
-    W1h = _qdq_row(_as_f64(w1[e]), True)
+    Xh = _qdq_row(_as_f64(x[idx]), quantize)
+    W1h = _qdq_row(_as_f64(w1[e]), quantize)
     h1 = Xh @ W1h.T
     del W1h
     hb = round_to_bf16(h1)
-    dA = _qdq_row(_as_f64(dy[idx]), True) @ _qdq_col(_as_f64(w2[e]), True)
+    dA = _qdq_row(_as_f64(dy[idx]), quantize) @ _qdq_col(_as_f64(w2[e]), quantize)
     p = np.asarray(probs, dtype=np.float64)[idx]
     dg, du, dw = _swiglu_backward(dA, hb[:, :F], hb[:, F:], p)
     return np.concatenate([dg, du], axis=1), dw, h1
 
 
-def mlp_backward_rows(x, probs, w1, w2, split_sizes, dy, rows):
+def mlp_backward_rows(x, probs, w1, w2, split_sizes, dy, rows, quantize=True):
     """dX (bf16-rounded) and dprobs for the selected rows only."""
     rows = np.asarray(rows, dtype=np.int64)
     off = _offsets(split_sizes)
@@ -482,14 +514,14 @@ def mlp_backward_rows(x, probs, w1, w2, split_sizes, dy, rows):
     for e in np.unique(ex):
         sel = np.nonzero(ex == e)[0]
         dh, dw, _ = _expert_dh1(x, probs, w1, w2, split_sizes, dy, e,
-                                rows[sel] - int(off[e]))
-        dX[sel] = _qdq_row(dh, True) @ _qdq_col(_as_f64(w1[e]), True)
+                                rows[sel] - int(off[e]), quantize)
+        dX[sel] = _qdq_row(dh, quantize) @ _qdq_col(_as_f64(w1[e]), quantize)
         dP[sel] = dw
     return dict(dx=round_to_bf16(dX), dprobs=dP)
 
 
 def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
-                               dw1_idx, dw2_idx):
+                               dw1_idx, dw2_idx, quantize=True):
     """Selected entries of one expert's dW1 (indices (n, h)) and dW2 ((h, f)),
     from a zero start.
 
@@ -507,27 +539,27 @@ def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
     if r1 == r0:
         return np.zeros(len(dw1_idx)), np.zeros(len(dw2_idx))
     p = np.asarray(probs, dtype=np.float64)[r0:r1]
-    Xh = _qdq_row(_as_f64(x[r0:r1]), True)
-    dYh = _qdq_row(_as_f64(dy[r0:r1]), True)
+    Xh = _qdq_row(_as_f64(x[r0:r1]), quantize)
+    dYh = _qdq_row(_as_f64(dy[r0:r1]), quantize)
 
     def h1_cols(cs):
         """Unrounded gate and up columns cs of H1 = Xh . W1h^T."""
-        W1h_g = _qdq_row(_as_f64(w1[expert][cs]), True)
-        W1h_u = _qdq_row(_as_f64(w1[expert][F + cs]), True)
+        W1h_g = _qdq_row(_as_f64(w1[expert][cs]), quantize)
+        W1h_u = _qdq_row(_as_f64(w1[expert][F + cs]), quantize)
         return Xh @ W1h_g.T, Xh @ W1h_u.T
 
     # dW1[n, h] = sum_r dH1c[r, n] * Xc[r, h]
     c1 = np.unique(dw1_idx[:, 0] % F)
     g, u = h1_cols(c1)
-    dA = dYh @ _qdq_col(_as_f64(w2[expert][:, c1]), True)
+    dA = dYh @ _qdq_col(_as_f64(w2[expert][:, c1]), quantize)
     dg, du, _ = _swiglu_backward(dA, round_to_bf16(g), round_to_bf16(u), p)
     dh = np.concatenate([dg, du], axis=1)                     # columns c1, then F + c1
     dh_pos = {int(c): i for i, c in enumerate(c1.tolist())}
     dh_pos.update({int(F + c): len(c1) + i for i, c in enumerate(c1.tolist())})
     n_sel = np.unique(dw1_idx[:, 0])
-    dhc = _qdq_col(dh[:, [dh_pos[int(n)] for n in n_sel]], True)
+    dhc = _qdq_col(dh[:, [dh_pos[int(n)] for n in n_sel]], quantize)
     h_sel = np.unique(dw1_idx[:, 1])
-    xc = _qdq_col(_as_f64(x[r0:r1][:, h_sel]), True)
+    xc = _qdq_col(_as_f64(x[r0:r1][:, h_sel]), quantize)
     n_map = {int(n): i for i, n in enumerate(n_sel.tolist())}
     h_map = {int(h): i for i, h in enumerate(h_sel.tolist())}
     out1 = np.array([dhc[:, n_map[n]] @ xc[:, h_map[h]] for n, h in dw1_idx.tolist()])
@@ -535,9 +567,9 @@ def mlp_backward_wgrad_entries(x, probs, w1, w2, split_sizes, dy, expert,
     # dW2[h, f] = sum_r dYc[r, h] * Ac[r, f], A = w * silu(gate) * up (unrounded H1)
     f_sel = np.unique(dw2_idx[:, 1])
     g2, u2 = h1_cols(f_sel)
-    ac = _qdq_col(p[:, None] * silu(g2) * u2, True)
+    ac = _qdq_col(p[:, None] * silu(g2) * u2, quantize)
     h2_sel = np.unique(dw2_idx[:, 0])
-    dyc = _qdq_col(_as_f64(dy[r0:r1][:, h2_sel]), True)
+    dyc = _qdq_col(_as_f64(dy[r0:r1][:, h2_sel]), quantize)
     h2_map = {int(h): i for i, h in enumerate(h2_sel.tolist())}
     f_map = {int(f): i for i, f in enumerate(f_sel.tolist())}
     out2 = np.array([dyc[:, h2_map[h]] @ ac[:, f_map[f]] for h, f in dw2_idx.tolist()])
