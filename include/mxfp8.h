@@ -400,6 +400,48 @@ MX_API mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const
                                      mx_dtype c_dtype, void* stream);
 
 /*
+ * MXFP4 MLP -- the grouped MLP of grouped_mlp_fwd / grouped_mlp_bwd with
+ * every GEMM on MXFP4 copies (E2M1 elements, one E8M0 scale per 32 values;
+ * as mx_quantize_fp4) instead of MXFP8: the MLP of a layer assigned to FP4
+ * ("TransformerEngine-accelerated Llama 3 training with native PyTorch
+ * training loop", Layer-Wise Precision; the mxfp4 runs of "examples/llama:
+ * default-on fusion & DP-comm perf toggles - #141", which put every layer in
+ * FP4). Same formulas, straight-through backward and argument meanings as
+ * grouped_mlp_fwd / grouped_mlp_bwd:
+ *     H1 = Xq . W1q^T (fp32);  A = w * silu(g) * u (fp32), requantized;
+ *     Y  = Aq . W2q^T (bf16);
+ *     dA = dYq . colwise(W2) (fp32);  dH1 = [dg | du] from the bf16 H1;
+ *     dX = dH1q . colwise(W1) (bf16);  dW2_e, dW1_e (+)= fp32 group-K products
+ * of the per-expert columnwise copies (mx_quantize_fp4_colwise_grouped's
+ * layout). The bf16 master weights are quantized on every forward call.
+ *
+ * grouped_mlp_fp4_sizes -- byte sizes of the forward workspace, the saved
+ * buffer and the backward workspace for one shape and split (any output
+ * pointer may be NULL). Same dims and split requirements as
+ * grouped_mlp_sizes (H, F multiples of 128, 1 <= E <= MX_MAX_GROUPS, split
+ * summing to R); the padded rows sum P must stay at or below 2^24.
+ * grouped_mlp_fwd_fp4 -- x bf16 [R, H], probs f32 [R] (NULL = all 1), w1 bf16
+ * [E, 2F, H], w2 bf16 [E, H, F], y bf16 [R, H]; saved NULL for inference.
+ * grouped_mlp_bwd_fp4 -- dy bf16 [R, H], saved from grouped_mlp_fwd_fp4 with
+ * the same inputs, dx bf16 [R, H], dprobs f32 [R] or NULL, dw1 f32 [E, 2F, H]
+ * and dw2 f32 [E, H, F] (accumulate_wgrad != 0 adds into them).
+ * Buffers are caller-owned; x, w, y, dy, dx, dw 16-byte aligned, workspace and
+ * saved 256-byte aligned; their layouts are private to the library.
+ * Errors: as grouped_mlp_fwd / grouped_mlp_bwd (MX_EINVAL, MX_ESHAPE,
+ * MX_EALIGN, MX_EWORKSPACE, MX_EUNSUPPORTED, MX_EHIP).
+ */
+MX_API mx_status grouped_mlp_fp4_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                       size_t* fwd_workspace, size_t* saved, size_t* bwd_workspace);
+MX_API mx_status grouped_mlp_fwd_fp4(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                     const void* x, const float* probs, const void* w1, const void* w2,
+                                     void* y, void* saved, size_t saved_bytes,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+MX_API mx_status grouped_mlp_bwd_fp4(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                     const void* dy, const float* probs, const void* saved, size_t saved_bytes,
+                                     void* dx, float* dprobs, float* dw1, float* dw2, int32_t accumulate_wgrad,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mx_quantize_fp4_colwise_grouped -- columnwise MXFP4 of a routed activation
  * with per-expert padding, the layout of the 4-bit weight gradient (the
  * MXFP4 form of the grouped columnwise MXFP8 layout above; MXFP4 as in

@@ -130,6 +130,14 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_fp4_colwise_grouped.argtypes = [vp, i64, i64, p64, i32, vp, vp, vp]
     L.mx_grouped_gemm_fp4_wgrad.restype = ctypes.c_int
     L.mx_grouped_gemm_fp4_wgrad.argtypes = [vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
+    L.grouped_mlp_fp4_sizes.restype = ctypes.c_int
+    L.grouped_mlp_fp4_sizes.argtypes = [ctypes.POINTER(_Dims), p64, ctypes.POINTER(sz),
+                                        ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.grouped_mlp_fwd_fp4.restype = ctypes.c_int
+    L.grouped_mlp_fwd_fp4.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.grouped_mlp_bwd_fp4.restype = ctypes.c_int
+    L.grouped_mlp_bwd_fp4.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
+                                      vp, sz, vp]
     L.mx_device_copy.restype = ctypes.c_int
     L.mx_device_copy.argtypes = [vp, vp, i64, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
@@ -262,12 +270,14 @@ def mlp_intermediates(E: int, R: int, H: int, F: int, split_sizes) -> dict:
 
 
 class MLPState:
-    """What the fused forward keeps for the backward (a caller-owned buffer)."""
+    """What the fused forward keeps for the backward (a caller-owned buffer);
+    fmt is the block format of the forward that filled it."""
 
-    def __init__(self, saved: torch.Tensor, dims, split_sizes):
+    def __init__(self, saved: torch.Tensor, dims, split_sizes, fmt: str = "mxfp8"):
         self.saved = saved
         self.dims = dims
         self.split_sizes = list(int(s) for s in split_sizes)
+        self.fmt = fmt
 
 
 def _expect_all(items):
@@ -382,6 +392,8 @@ def grouped_mlp_bwd_gather(dy_tokens, row_token, probs, state: MLPState, *, dw1=
     """grouped_mlp_bwd with dY gathered from dy_tokens [T, H] through row_token
     by its cast. Returns (dx [R, H] bf16 per routed row, dprobs, dw1, dw2)."""
     L = load()
+    if state.fmt != "mxfp8":
+        raise ValueError("grouped_mlp_bwd_gather needs the state of an MXFP8 forward")
     E, R, H, F = state.dims
     if dy_tokens.dim() != 2:
         raise ValueError("grouped_mlp_bwd_gather: dy_tokens must be [T, H]")
@@ -412,6 +424,8 @@ def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulat
     """Fused grouped MLP backward. Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32).
     With accumulate=True, dw1/dw2 (fp32 main grads) are added into."""
     L = load()
+    if state.fmt != "mxfp8":
+        raise ValueError("grouped_mlp_bwd needs the state of an MXFP8 forward")
     E, R, H, F = state.dims
     _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
                 + _mlp_grads(E, R, H, F, dw1, dw2))
@@ -430,6 +444,68 @@ def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulat
                              _ptr(dy), _ptr(probs), _ptr(state.saved), state.saved.numel(),
                              _ptr(dx), _ptr(dprobs), _ptr(dw1), _ptr(dw2), int(accumulate),
                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dx, dprobs, dw1, dw2
+
+
+def mlp_fp4_sizes(E: int, R: int, H: int, F: int, split_sizes):
+    """(fwd workspace, saved, bwd workspace) byte sizes of the MXFP4 MLP."""
+    L = load()
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.grouped_mlp_fp4_sizes(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes),
+                                   ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)))
+    return f.value, s.value, b.value
+
+
+def grouped_mlp_fwd_fp4(x, probs, w1, w2, split_sizes, *, training: bool = True, workspace=None,
+                        out=None, stream=None):
+    """Grouped MLP forward with every GEMM on MXFP4 copies
+    (grouped_mlp_fwd_fp4). Same arguments and shapes as grouped_mlp_fwd;
+    returns (y [R,H] bf16, MLPState or None)."""
+    L = load()
+    if x.dim() != 2 or w1.dim() != 3:
+        raise ValueError("grouped_mlp_fwd_fp4: x must be [R, H] and w1 [E, 2F, H]")
+    R, H = x.shape
+    E, F2, _ = w1.shape
+    F = F2 // 2
+    _mlp_inputs(E, R, H, F, split_sizes, x, w1, w2, probs, extra=[(out, (R, H), torch.bfloat16, "out", True)])
+    fws, sv, _ = mlp_fp4_sizes(E, R, H, F, split_sizes)
+    if workspace is None or workspace.numel() < fws:
+        workspace = _byte_buffer(fws, x.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x.device) if out is None else out
+    saved = _byte_buffer(sv, x.device) if training else None
+    _check(L.grouped_mlp_fwd_fp4(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes), _ptr(x),
+                                 _ptr(probs), _ptr(w1), _ptr(w2), _ptr(y), _ptr(saved),
+                                 0 if saved is None else saved.numel(), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    state = MLPState(saved, (E, R, H, F), split_sizes, fmt="mxfp4") if training else None
+    return y, state
+
+
+def grouped_mlp_bwd_fp4(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulate: bool = False,
+                        want_dprobs: bool = True, workspace=None, stream=None):
+    """Backward of grouped_mlp_fwd_fp4 (grouped_mlp_bwd_fp4). Returns
+    (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
+    L = load()
+    if state.fmt != "mxfp4":
+        raise ValueError("grouped_mlp_bwd_fp4 needs the state of grouped_mlp_fwd_fp4")
+    E, R, H, F = state.dims
+    _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
+                + _mlp_grads(E, R, H, F, dw1, dw2))
+    _, _, bws = mlp_fp4_sizes(E, R, H, F, state.split_sizes)
+    if workspace is None or workspace.numel() < bws:
+        workspace = _byte_buffer(bws, dy.device)
+    dev = dy.device
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dprobs = torch.empty((R,), dtype=torch.float32, device=dev) if want_dprobs else None
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, H), dtype=torch.float32, device=dev)
+        accumulate = False if dw2 is None else accumulate
+    if dw2 is None:
+        dw2 = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    _check(L.grouped_mlp_bwd_fp4(ctypes.byref(_dims(E, R, H, F)), _i64_array(state.split_sizes),
+                                 _ptr(dy), _ptr(probs), _ptr(state.saved), state.saved.numel(),
+                                 _ptr(dx), _ptr(dprobs), _ptr(dw1), _ptr(dw2), int(accumulate),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
     return dx, dprobs, dw1, dw2
 
 
@@ -497,6 +573,8 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
     """grouped_mlp_bwd after grouped_mlp_fwd_cached (same cache).
     Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
     L = load()
+    if state.fmt != "mxfp8":
+        raise ValueError("grouped_mlp_bwd_cached needs the state of an MXFP8 forward")
     E, R, H, F = state.dims
     _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
                 + _mlp_grads(E, R, H, F, dw1, dw2))

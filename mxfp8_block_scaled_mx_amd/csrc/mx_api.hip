@@ -1306,7 +1306,8 @@ mx_status mx_quantize_fp4_colwise_grouped(const void* x, int64_t rows, int64_t c
   gr.tile0[groups] = (int32_t)t0;
   if (t0 * cdiv(cols, 64) > kI32Max || p0 * cols > ((int64_t)1 << 40))
     return fail(MX_EUNSUPPORTED, "%s: tensor too large", who);
-  hipError_t e = mx::launch_quantize_fp4_grouped(x, rows, cols, gr, q_col, s_col, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = mx::launch_quantize_fp4_grouped(x, false, rows, cols, gr, q_col, s_col, nullptr, nullptr,
+                                                 reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mx_quantize_fp4_colwise_grouped launch");
   return MX_OK;
 }
@@ -1340,6 +1341,246 @@ mx_status mx_grouped_gemm_fp4_wgrad(const uint8_t* a, const uint8_t* a_s, const 
                                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, who);
   return MX_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ MXFP4 MLP
+// GroupedLinear -> ScaledSwiGLU -> GroupedLinear with every GEMM on MXFP4
+// copies (the MLP of an FP4 layer: "TransformerEngine-accelerated Llama 3
+// training with native PyTorch training loop", Layer-Wise Precision; the
+// mxfp4 runs of "examples/llama: default-on fusion & DP-comm perf toggles").
+// The steps are the MXFP8 MLP's; GEMM1 and dgrad2 leave fp32 results that
+// the SwiGLU kernels turn into the requantized A / dH1.
+namespace {
+
+struct Fp4MlpLayout {
+  int64_t E = 0, R = 0, H = 0, F = 0, P = 0;
+  std::vector<int64_t> split;
+  mx::Fp4ColGroups cg{};   // per-expert row tiles of the columnwise casts
+  mx::Fp4KGroups kg{};     // per-expert padded k ranges of the weight gradients
+  // forward workspace: rowwise X, W1, W2, H1 (fp32), rowwise A, A (fp32)
+  size_t xq, xs, w1q, w1s, w2q, w2s, h1f, aq, as, a32, fwd_total;
+  // saved: H1 (bf16), columnwise A, X, and per-expert columnwise W1, W2
+  size_t h1, acq, acs, xcq, xcs, w1cq, w1cs, w2cq, w2cs, saved_total;
+  // backward workspace: dY both layouts, dA (fp32), dH1 (fp32), dH1 both layouts
+  size_t dyq, dys, dycq, dycs, da32, dh1f, dhq, dhs, dhcq, dhcs, bwd_total;
+};
+
+mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayout* L, const char* who) {
+  MlpLayout M;   // the MXFP8 MLP's checks of dims and split (shapes, limits, sums)
+  mx_status st = mlp_layout(d, split, &M, who);
+  if (st != MX_OK) return st;
+  L->E = M.E;
+  L->R = M.R;
+  L->H = M.H;
+  L->F = M.F;
+  L->split = M.split;
+  const int64_t E = L->E, R = L->R, H = L->H, F = L->F;
+  L->cg.n = (int32_t)E;
+  L->kg.n = (int32_t)E;
+  int64_t r0 = 0, p0 = 0, t0 = 0;
+  for (int g = 0; g < E; ++g) {
+    L->cg.row0[g] = r0;
+    L->cg.pcol0[g] = p0;
+    L->cg.tile0[g] = (int32_t)t0;
+    L->kg.k0[g] = p0;
+    r0 += L->split[g];
+    p0 += pad32(L->split[g]);
+    t0 += cdiv(L->split[g], 128);
+  }
+  L->cg.row0[E] = r0;
+  L->cg.pcol0[E] = p0;
+  L->cg.tile0[E] = (int32_t)t0;
+  L->kg.k0[E] = p0;
+  L->P = p0;
+  if (p0 > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: padded rows above 2^24", who);
+  const int64_t P = L->P;
+  size_t c = 0;
+  L->xq = take(c, R * H / 2);
+  L->xs = take(c, R * H / 32);
+  L->w1q = take(c, E * 2 * F * H / 2);
+  L->w1s = take(c, E * 2 * F * H / 32);
+  L->w2q = take(c, E * H * F / 2);
+  L->w2s = take(c, E * H * F / 32);
+  L->h1f = take(c, R * 2 * F * 4);
+  L->aq = take(c, R * F / 2);
+  L->as = take(c, R * F / 32);
+  L->a32 = take(c, R * F * 4);
+  L->fwd_total = c;
+  c = 0;
+  L->h1 = take(c, R * 2 * F * 2);
+  L->acq = take(c, F * P / 2);
+  L->acs = take(c, F * P / 32);
+  L->xcq = take(c, H * P / 2);
+  L->xcs = take(c, H * P / 32);
+  L->w1cq = take(c, E * H * 2 * F / 2);
+  L->w1cs = take(c, E * H * 2 * F / 32);
+  L->w2cq = take(c, E * F * H / 2);
+  L->w2cs = take(c, E * F * H / 32);
+  L->saved_total = c;
+  c = 0;
+  L->dyq = take(c, R * H / 2);
+  L->dys = take(c, R * H / 32);
+  L->dycq = take(c, H * P / 2);
+  L->dycs = take(c, H * P / 32);
+  L->da32 = take(c, R * F * 4);
+  L->dh1f = take(c, R * 2 * F * 4);
+  L->dhq = take(c, R * 2 * F / 2);
+  L->dhs = take(c, R * 2 * F / 32);
+  L->dhcq = take(c, 2 * F * P / 2);
+  L->dhcs = take(c, 2 * F * P / 32);
+  L->bwd_total = c;
+  return MX_OK;
+}
+
+mx_status fp4_step(hipError_t e, const char* what) { return e == hipSuccess ? MX_OK : hip_fail(e, what); }
+
+mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs, const void* w1, const void* w2,
+                       void* y, void* saved, void* workspace, hipStream_t stream) {
+  const char* who = "grouped_mlp_fwd_fp4";
+  uint8_t* W = static_cast<uint8_t*>(workspace);
+  uint8_t* S = static_cast<uint8_t*>(saved);
+  const bool train = saved != nullptr;
+  const int64_t E = L.E, R = L.R, H = L.H, F = L.F;
+  mx_status st;
+  // X: rowwise (and, for the backward, the per-expert columnwise copy in the same pass)
+  if (train)
+    st = fp4_step(mx::launch_quantize_fp4_grouped(x, false, R, H, L.cg, S + L.xcq, S + L.xcs, W + L.xq, W + L.xs,
+                                                  stream), who);
+  else
+    st = fp4_step(mx::launch_quantize_fp4(x, R, H, W + L.xq, W + L.xs, nullptr, nullptr, stream), who);
+  if (st != MX_OK) return st;
+  // weights: rowwise along H (W1) and F (W2); in training also each expert's
+  // columnwise copy, [H, 2F] and [F, H], from the same pass
+  const uint8_t* w1b = static_cast<const uint8_t*>(w1);
+  const uint8_t* w2b = static_cast<const uint8_t*>(w2);
+  if (train) {
+    for (int64_t e = 0; e < E; ++e) {
+      st = fp4_step(mx::launch_quantize_fp4(w1b + e * 2 * F * H * 2, 2 * F, H, W + L.w1q + e * 2 * F * H / 2,
+                                            W + L.w1s + e * 2 * F * H / 32, S + L.w1cq + e * H * 2 * F / 2,
+                                            S + L.w1cs + e * H * 2 * F / 32, stream), who);
+      if (st != MX_OK) return st;
+      st = fp4_step(mx::launch_quantize_fp4(w2b + e * H * F * 2, H, F, W + L.w2q + e * H * F / 2,
+                                            W + L.w2s + e * H * F / 32, S + L.w2cq + e * F * H / 2,
+                                            S + L.w2cs + e * F * H / 32, stream), who);
+      if (st != MX_OK) return st;
+    }
+  } else {
+    st = fp4_step(mx::launch_quantize_fp4(w1, E * 2 * F, H, W + L.w1q, W + L.w1s, nullptr, nullptr, stream), who);
+    if (st != MX_OK) return st;
+    st = fp4_step(mx::launch_quantize_fp4(w2, E * H, F, W + L.w2q, W + L.w2s, nullptr, nullptr, stream), who);
+    if (st != MX_OK) return st;
+  }
+  // GEMM1 -> H1 (fp32)
+  st = gemm_fp4_impl(who, W + L.xq, W + L.xs, W + L.w1q, W + L.w1s, L.split.data(), (int32_t)E, 2 * F, H,
+                     W + L.h1f, MX_F32, stream);
+  if (st != MX_OK) return st;
+  // ScaledSwiGLU: H1 (bf16, saved), A rowwise MXFP4 (and fp32 for its columnwise copy)
+  st = fp4_step(mx::launch_swiglu_fwd_fp4(reinterpret_cast<const float*>(W + L.h1f), probs, R, F,
+                                          train ? reinterpret_cast<uint16_t*>(S + L.h1) : nullptr,
+                                          train ? reinterpret_cast<float*>(W + L.a32) : nullptr, W + L.aq, W + L.as,
+                                          stream), who);
+  if (st != MX_OK) return st;
+  if (train) {
+    st = fp4_step(mx::launch_quantize_fp4_grouped(W + L.a32, true, R, F, L.cg, S + L.acq, S + L.acs, nullptr, nullptr,
+                                                  stream), who);
+    if (st != MX_OK) return st;
+  }
+  // GEMM2 -> Y (bf16)
+  return gemm_fp4_impl(who, W + L.aq, W + L.as, W + L.w2q, W + L.w2s, L.split.data(), (int32_t)E, H, F, y, MX_BF16,
+                       stream);
+}
+
+mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs, const void* saved, void* dx,
+                       float* dprobs, float* dw1, float* dw2, int32_t accumulate, void* workspace,
+                       hipStream_t stream) {
+  const char* who = "grouped_mlp_bwd_fp4";
+  uint8_t* W = static_cast<uint8_t*>(workspace);
+  const uint8_t* S = static_cast<const uint8_t*>(saved);
+  const int64_t E = L.E, R = L.R, H = L.H, F = L.F;
+  // dY: rowwise (dgrad2) and per-expert columnwise (wgrad2) in one pass
+  mx_status st = fp4_step(mx::launch_quantize_fp4_grouped(dy, false, R, H, L.cg, W + L.dycq, W + L.dycs, W + L.dyq,
+                                                          W + L.dys, stream), who);
+  if (st != MX_OK) return st;
+  // dgrad2: dA = dY . W2 (fp32) on the columnwise W2 copies [F, H]
+  st = gemm_fp4_impl(who, W + L.dyq, W + L.dys, S + L.w2cq, S + L.w2cs, L.split.data(), (int32_t)E, F, H, W + L.da32,
+                     MX_F32, stream);
+  if (st != MX_OK) return st;
+  // SwiGLU backward: dH1 (fp32 and rowwise MXFP4), dprobs
+  st = fp4_step(mx::launch_swiglu_bwd_fp4(reinterpret_cast<const float*>(W + L.da32),
+                                          reinterpret_cast<const uint16_t*>(S + L.h1), probs, R, F,
+                                          reinterpret_cast<float*>(W + L.dh1f), W + L.dhq, W + L.dhs, dprobs, stream),
+                who);
+  if (st != MX_OK) return st;
+  st = fp4_step(mx::launch_quantize_fp4_grouped(W + L.dh1f, true, R, 2 * F, L.cg, W + L.dhcq, W + L.dhcs, nullptr,
+                                                nullptr, stream), who);
+  if (st != MX_OK) return st;
+  // dgrad1: dX = dH1 . W1 (bf16) on the columnwise W1 copies [H, 2F]
+  st = gemm_fp4_impl(who, W + L.dhq, W + L.dhs, S + L.w1cq, S + L.w1cs, L.split.data(), (int32_t)E, H, 2 * F, dx,
+                     MX_BF16, stream);
+  if (st != MX_OK) return st;
+  // weight gradients (fp32, stored or accumulated): dW2_e = dY_e^T A_e, dW1_e = dH1_e^T X_e
+  st = fp4_step(mx::launch_gemm_fp4_group_k(W + L.dycq, W + L.dycs, S + L.acq, S + L.acs, L.kg, H, F, dw2, accumulate,
+                                            stream), who);
+  if (st != MX_OK) return st;
+  return fp4_step(mx::launch_gemm_fp4_group_k(W + L.dhcq, W + L.dhcs, S + L.xcq, S + L.xcs, L.kg, 2 * F, H, dw1,
+                                              accumulate, stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status grouped_mlp_fp4_sizes(const mx_mlp_dims* dims, const int64_t* split_sizes, size_t* fwd_workspace,
+                                size_t* saved, size_t* bwd_workspace) {
+  g_err[0] = 0;
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(dims, split_sizes, &L, "grouped_mlp_fp4_sizes");
+  if (st != MX_OK) return st;
+  if (fwd_workspace) *fwd_workspace = L.fwd_total;
+  if (saved) *saved = L.saved_total;
+  if (bwd_workspace) *bwd_workspace = L.bwd_total;
+  return MX_OK;
+}
+
+mx_status grouped_mlp_fwd_fp4(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x, const float* probs,
+                              const void* w1, const void* w2, void* y, void* saved, size_t saved_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd_fp4";
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  if (!x || !w1 || !w2 || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+      (saved && !aligned(saved, 256)) || (probs && !aligned(probs, 4)))
+    return fail(MX_EALIGN, "%s: x, w1, w2, y must be 16-byte and workspace/saved 256-byte aligned", who);
+  if (workspace_bytes < L.fwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
+  if (saved && saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  return fwd_fp4_impl(L, x, probs, w1, w2, y, saved, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+mx_status grouped_mlp_bwd_fp4(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy, const float* probs,
+                              const void* saved, size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                              int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd_fp4";
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  if (!dy || !saved || !dx || !dw1 || !dw2 || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(saved, 256) ||
+      !aligned(workspace, 256) || (probs && !aligned(probs, 4)) || (dprobs && !aligned(dprobs, 4)))
+    return fail(MX_EALIGN, "%s: dy, dx, dw1, dw2 must be 16-byte and saved/workspace 256-byte aligned", who);
+  if (saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  if (workspace_bytes < L.bwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.bwd_total);
+  return bwd_fp4_impl(L, dy, probs, saved, dx, dprobs, dw1, dw2, accumulate_wgrad ? 1 : 0, workspace,
+                      reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -25,6 +25,28 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
   return c | ((__float_as_uint(t) >> 28) & 8u);
 }
 
+// One 32-value MXFP4 block: scale code (floor(log2 amax) - 2 + 127 = biased
+// exponent - 2, clamped at 0 for a zero or subnormal amax or a biased
+// exponent below 3) and the 16 code bytes, element 2i in the low nibble.
+__device__ __forceinline__ uint32_t fp4_block(const float (&v)[32], uint4& codes) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
+  const uint32_t eb = am >> 23;
+  const uint32_t sc = eb > 2u ? eb - 2u : 0u;
+  const float inv = inv_scale_from_code(sc);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
+    w[i] = word;
+  }
+  codes = make_uint4(w[0], w[1], w[2], w[3]);
+  return sc;
+}
+
 __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s) {
   const int64_t nb = cols / 32;
@@ -43,23 +65,9 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
     v[8 * i + 4] = bf16_lo(raw[i].z); v[8 * i + 5] = bf16_hi(raw[i].z);
     v[8 * i + 6] = bf16_lo(raw[i].w); v[8 * i + 7] = bf16_hi(raw[i].w);
   }
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
-  // code = floor(log2 amax) - 2 + 127 = biased exponent - 2, clamped at 0
-  // (zero or subnormal amax, or a biased exponent below 3)
-  const uint32_t eb = am >> 23;
-  const uint32_t sc = eb > 2u ? eb - 2u : 0u;
-  const float inv = inv_scale_from_code(sc);
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
-    w[i] = word;
-  }
-  *reinterpret_cast<uint4*>(q + r * (cols / 2) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  uint4 codes;
+  const uint32_t sc = fp4_block(v, codes);
+  *reinterpret_cast<uint4*>(q + r * (cols / 2) + b * 16) = codes;
   s[r * nb + b] = (uint8_t)sc;
 }
 
@@ -73,14 +81,24 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
 // Grouped (per-expert) columnwise layout: row tiles restart at each group's
 // first row, rows past the group's end read as zeros, and group g's padded
 // rows land at columns [pcol0[g], + pad32(m_g)) of the [cols, sum P] result.
-// One group of all rows is the plain columnwise cast.
+// One group of all rows is the plain columnwise cast. T is the input type:
+// bf16 bits (uint16_t) or fp32 (the fp32 intermediates of the MXFP4 MLP).
 constexpr int kFp4ColTileRows = 128, kFp4ColTileCols = 64;
-__global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s, uint8_t* q_row,
                                                                    uint8_t* s_row, Fp4ColGroups gr, int64_t ldp) {
-  // [row][column] bf16 with a 2-element pad so that the column reads of a
-  // wave (64 columns of one row) spread over the banks
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kFp4ColTileRows][kFp4ColTileCols + 2];
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int EP = 16 / (int)sizeof(T);               // elements per 16-byte piece
+  constexpr int kPiecesPerRow = kFp4ColTileCols / EP;
+  constexpr int kIters = kFp4ColTileRows * kPiecesPerRow / 256;
+  // [row][column] with a pad so that the column reads of a wave (64 columns
+  // of one row) spread over the banks
+  __shared__ __attribute__((aligned(16))) T tile[kFp4ColTileRows][kFp4ColTileCols + (kBf16 ? 2 : 1)];
+  auto val = [&](int r, int c) __attribute__((always_inline)) -> float {
+    if constexpr (kBf16) return __uint_as_float((uint32_t)tile[r][c] << 16);
+    else return tile[r][c];
+  };
   const int64_t n_ct = (cols + kFp4ColTileCols - 1) / kFp4ColTileCols;
   const int rt = (int)(blockIdx.x / n_ct);
   const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * kFp4ColTileCols;
@@ -94,16 +112,24 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
   const int64_t m_g = gr.row0[lo + 1] - gr.row0[lo];
   const int64_t p_g = (m_g + 31) / 32 * 32;
   const int tid = threadIdx.x;
-  // 128 rows x 8 pieces of 16 bytes (8 columns each): 4 pieces per thread
+  // 128 rows of 16-byte pieces (cols % 32 == 0: a piece is wholly inside or
+  // wholly past the last column)
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int p = it * 256 + tid, rr = p >> 3, cp = (p & 7) * 8;
+  for (int it = 0; it < kIters; ++it) {
+    const int p = it * 256 + tid, rr = p / kPiecesPerRow, cp = (p % kPiecesPerRow) * EP;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (lr0 + rr < m_g && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
-    const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+    if constexpr (kBf16) {
+      const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
+      for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
+    } else {
+      tile[rr][cp + 0] = __uint_as_float(v.x);
+      tile[rr][cp + 1] = __uint_as_float(v.y);
+      tile[rr][cp + 2] = __uint_as_float(v.z);
+      tile[rr][cp + 3] = __uint_as_float(v.w);
+    }
   }
   __syncthreads();
   if (q_row != nullptr) {
@@ -112,26 +138,10 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
     if (lr0 + rr < m_g && col < cols) {
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t pair = *reinterpret_cast<const uint32_t*>(&tile[rr][32 * bb + 2 * i]);
-        v[2 * i] = bf16_lo(pair);
-        v[2 * i + 1] = bf16_hi(pair);
-      }
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
-      const uint32_t eb = am >> 23;
-      const uint32_t sc = eb > 2u ? eb - 2u : 0u;
-      const float inv = inv_scale_from_code(sc);
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
-        w[i] = word;
-      }
-      *reinterpret_cast<uint4*>(q_row + row * (cols / 2) + col / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int i = 0; i < 32; ++i) v[i] = val(rr, 32 * bb + i);
+      uint4 codes;
+      const uint32_t sc = fp4_block(v, codes);
+      *reinterpret_cast<uint4*>(q_row + row * (cols / 2) + col / 2) = codes;
       s_row[row * (cols / 32) + col / 32] = (uint8_t)sc;
     }
   }
@@ -141,22 +151,10 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const uint16_
   const int64_t pcol = gr.pcol0[lo] + lrow;                   // its position in the columnwise layout
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tile[32 * rb + i][c] << 16);
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
-  const uint32_t eb = am >> 23;
-  const uint32_t sc = eb > 2u ? eb - 2u : 0u;
-  const float inv = inv_scale_from_code(sc);
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
-    w[i] = word;
-  }
-  *reinterpret_cast<uint4*>(q + col * (ldp / 2) + pcol / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int i = 0; i < 32; ++i) v[i] = val(32 * rb + i, c);
+  uint4 codes;
+  const uint32_t sc = fp4_block(v, codes);
+  *reinterpret_cast<uint4*>(q + col * (ldp / 2) + pcol / 2) = codes;
   s[col * (ldp / 32) + pcol / 32] = (uint8_t)sc;
 }
 
@@ -179,19 +177,167 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
     gr.tile0[0] = 0;
     gr.tile0[1] = (int32_t)((rows + kFp4ColTileRows - 1) / kFp4ColTileRows);
     const int64_t tiles = (int64_t)gr.tile0[1] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
-    hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows, cols,
-                       q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows);
+    hipLaunchKernelGGL(quantize_fp4_colwise_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows,
+                       cols, q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_fp4_grouped(const void* x, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
-                                       uint8_t* q_col, uint8_t* s_col, hipStream_t stream) {
+hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
+                                       uint8_t* q_col, uint8_t* s_col, uint8_t* q_row, uint8_t* s_row,
+                                       hipStream_t stream) {
   const int64_t tiles = (int64_t)gr.tile0[gr.n] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_fp4_colwise_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(x), rows, cols, q_col, s_col, nullptr, nullptr, gr,
-                     (int64_t)gr.pcol0[gr.n]);
+  if (x_f32)
+    hipLaunchKernelGGL(quantize_fp4_colwise_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(x), rows, cols, q_col, s_col, q_row, s_row, gr,
+                       (int64_t)gr.pcol0[gr.n]);
+  else
+    hipLaunchKernelGGL(quantize_fp4_colwise_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(x), rows, cols, q_col, s_col, q_row, s_row, gr,
+                       (int64_t)gr.pcol0[gr.n]);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// ScaledSwiGLU around the MXFP4 GEMMs of the MLP ("Efficient MoE training for
+// biological foundation models", Key technical approaches item 3, at the 4-bit
+// MX format): GEMM1 leaves H1 = [g | u] in fp32, the forward forms
+// A = w * silu(g) * u in fp32 and requantizes it rowwise; the backward takes
+// dA in fp32 from dgrad2 and forms dH1 = [dg | du] and dprobs. silu and its
+// derivative use the same fp32 expressions as the MXFP8 epilogues.
+
+// Forward: one thread per (row, 32-column block of F). Writes H1 in bf16
+// (h1, when the forward is kept for the backward), A in fp32 (a32, the input
+// of the columnwise cast; or null) and A's rowwise MXFP4 copy.
+__global__ __launch_bounds__(256) void swiglu_fwd_fp4_kernel(const float* h1f, const float* probs, int64_t R,
+                                                             int64_t F, uint16_t* h1, float* a32, uint8_t* aq,
+                                                             uint8_t* as) {
+  const int64_t nb = F / 32;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= R * nb) return;
+  const int64_t r = blk / nb, b = blk - r * nb;
+  const float4* gp = reinterpret_cast<const float4*>(h1f + r * 2 * F + 32 * b);
+  const float4* up = reinterpret_cast<const float4*>(h1f + r * 2 * F + F + 32 * b);
+  float g[32], u[32], a[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 gv = gp[i], uv = up[i];
+    g[4 * i] = gv.x; g[4 * i + 1] = gv.y; g[4 * i + 2] = gv.z; g[4 * i + 3] = gv.w;
+    u[4 * i] = uv.x; u[4 * i + 1] = uv.y; u[4 * i + 2] = uv.z; u[4 * i + 3] = uv.w;
+  }
+  const float w = probs != nullptr ? probs[r] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+    a[i] = w * (g[i] * sig) * u[i];
+  }
+  if (h1 != nullptr) {
+    uint4* hg = reinterpret_cast<uint4*>(h1 + r * 2 * F + 32 * b);
+    uint4* hu = reinterpret_cast<uint4*>(h1 + r * 2 * F + F + 32 * b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hg[i] = make_uint4(pack_bf16x2(g[8 * i], g[8 * i + 1]), pack_bf16x2(g[8 * i + 2], g[8 * i + 3]),
+                         pack_bf16x2(g[8 * i + 4], g[8 * i + 5]), pack_bf16x2(g[8 * i + 6], g[8 * i + 7]));
+      hu[i] = make_uint4(pack_bf16x2(u[8 * i], u[8 * i + 1]), pack_bf16x2(u[8 * i + 2], u[8 * i + 3]),
+                         pack_bf16x2(u[8 * i + 4], u[8 * i + 5]), pack_bf16x2(u[8 * i + 6], u[8 * i + 7]));
+    }
+  }
+  if (a32 != nullptr) {
+    float4* ap = reinterpret_cast<float4*>(a32 + r * F + 32 * b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ap[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
+  }
+  uint4 codes;
+  const uint32_t sc = fp4_block(a, codes);
+  *reinterpret_cast<uint4*>(aq + r * (F / 2) + 16 * b) = codes;
+  as[r * nb + b] = (uint8_t)sc;
+}
+
+// Backward: one workgroup per row; thread t takes the row's 32-column blocks
+// t, t + 256, ... of F. dg = dA*w*u*s*(1 + g*(1 - s)), du = dA*w*g*s with
+// s = sigmoid(g) and g, u from the saved bf16 H1; dprobs = sum_f dA*g*s*u
+// (partial sums per thread, then a tree over the workgroup). Writes dH1 in
+// fp32 (dh1f, the input of the columnwise cast; or null) and its rowwise
+// MXFP4 copy (dg blocks at columns [0, F), du blocks at [F, 2F)).
+__global__ __launch_bounds__(256) void swiglu_bwd_fp4_kernel(const float* da, const uint16_t* h1, const float* probs,
+                                                             int64_t F, float* dh1f, uint8_t* dq, uint8_t* ds,
+                                                             float* dprobs) {
+  __shared__ float red[256];
+  const int64_t r = blockIdx.x, nb = F / 32;
+  const float w = probs != nullptr ? probs[r] : 1.0f;
+  float dp = 0.0f;
+  for (int64_t b = threadIdx.x; b < nb; b += 256) {
+    const float4* dap = reinterpret_cast<const float4*>(da + r * F + 32 * b);
+    const uint4* gp = reinterpret_cast<const uint4*>(h1 + r * 2 * F + 32 * b);
+    const uint4* up = reinterpret_cast<const uint4*>(h1 + r * 2 * F + F + 32 * b);
+    float d[32], g[32], u[32], dg[32], du[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = dap[i];
+      d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 gv = gp[i], uv = up[i];
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g[8 * i + 2 * j] = bf16_lo(gw[j]);
+        g[8 * i + 2 * j + 1] = bf16_hi(gw[j]);
+        u[8 * i + 2 * j] = bf16_lo(uw[j]);
+        u[8 * i + 2 * j + 1] = bf16_hi(uw[j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+      const float sl = g[i] * sg;
+      dg[i] = d[i] * w * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
+      du[i] = d[i] * w * sl;
+      dp += d[i] * sl * u[i];
+    }
+    if (dh1f != nullptr) {
+      float4* pg = reinterpret_cast<float4*>(dh1f + r * 2 * F + 32 * b);
+      float4* pu = reinterpret_cast<float4*>(dh1f + r * 2 * F + F + 32 * b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pg[i] = make_float4(dg[4 * i], dg[4 * i + 1], dg[4 * i + 2], dg[4 * i + 3]);
+        pu[i] = make_float4(du[4 * i], du[4 * i + 1], du[4 * i + 2], du[4 * i + 3]);
+      }
+    }
+    uint4 codes;
+    uint32_t sc = fp4_block(dg, codes);
+    *reinterpret_cast<uint4*>(dq + r * F + 16 * b) = codes;
+    ds[r * 2 * nb + b] = (uint8_t)sc;
+    sc = fp4_block(du, codes);
+    *reinterpret_cast<uint4*>(dq + r * F + F / 2 + 16 * b) = codes;
+    ds[r * 2 * nb + nb + b] = (uint8_t)sc;
+  }
+  red[threadIdx.x] = dp;
+  __syncthreads();
+#pragma unroll
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && dprobs != nullptr) dprobs[r] = red[0];
+}
+
+hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint16_t* h1, float* a32,
+                                 uint8_t* aq, uint8_t* as, hipStream_t stream) {
+  const int64_t blocks = R * (F / 32);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_fwd_fp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream, h1f, probs,
+                     R, F, h1, a32, aq, as);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_fp4(const float* da, const uint16_t* h1, const float* probs, int64_t R, int64_t F,
+                                 float* dh1f, uint8_t* dq, uint8_t* ds, float* dprobs, hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_fp4_kernel, dim3((unsigned)R), dim3(256), 0, stream, da, h1, probs, F, dh1f, dq, ds,
+                     dprobs);
   return hipGetLastError();
 }
 

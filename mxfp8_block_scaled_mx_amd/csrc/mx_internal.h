@@ -218,8 +218,20 @@ struct Fp4ColGroups {
   int64_t row0[kMaxGroups + 1];
   int64_t pcol0[kMaxGroups + 1];
 };
-hipError_t launch_quantize_fp4_grouped(const void* x, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
-                                       uint8_t* q_col, uint8_t* s_col, hipStream_t stream);
+// x is bf16 or (x_f32) fp32 [rows, cols]; q_row / s_row (or null) receive the
+// rowwise copy of the same pass.
+hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
+                                       uint8_t* q_col, uint8_t* s_col, uint8_t* q_row, uint8_t* s_row,
+                                       hipStream_t stream);
+// ScaledSwiGLU of the MXFP4 MLP (mx_fp4.hip). Forward: H1 fp32 [R, 2F] ->
+// H1 bf16 (h1, or null), A fp32 (a32, or null) and A's rowwise MXFP4 copy
+// [R, F/2] + [R, F/32]. Backward: dA fp32 [R, F], H1 bf16 -> dH1 fp32 (dh1f,
+// or null), dH1's rowwise MXFP4 copy [R, F] + [R, F/16], dprobs (or null).
+// F % 32 == 0; probs null = all 1.
+hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint16_t* h1, float* a32,
+                                 uint8_t* aq, uint8_t* as, hipStream_t stream);
+hipError_t launch_swiglu_bwd_fp4(const float* da, const uint16_t* h1, const float* probs, int64_t R, int64_t F,
+                                 float* dh1f, uint8_t* dq, uint8_t* ds, float* dprobs, hipStream_t stream);
 // MXFP4 group-K product C_g (+)= A[:, K_g] . B[:, K_g]^T (fp32), K_g =
 // [k0[g], k0[g+1]) in values (multiples of 32): A [M, k0[n]] and B
 // [N, k0[n]] rowwise-packed MXFP4 (the columnwise layouts of two routed

@@ -393,3 +393,49 @@ def test_mlp_bindings_reject_tensors_that_disagree_with_the_dims():
         u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
         mx.grouped_gemm(mx.MX_GROUP_M, [64], u8(64, 128), u8(64, 4), u8(32, 128), u8(32, 4), N=32, K=128,
                         out=torch.zeros((64, 32)))
+
+
+def test_fp4_mlp_sizes_and_argument_errors(L):
+    E, R, H, F = 3, 300, 256, 384
+    split = mx._i64_array([100, 0, 200])
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    d = _dims(E, R, H, F)
+    assert L.grouped_mlp_fp4_sizes(ctypes.byref(d), split, ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)) == OK
+    P = 128 + 0 + 224                                   # per-expert rows padded to 32
+    # the forward holds at least H1 in fp32 and A in fp32, the saved buffer at
+    # least H1 in bf16 and the 4-bit columnwise copies of A, X, W1 and W2
+    assert f.value >= R * 2 * F * 4 + R * F * 4
+    assert s.value >= R * 2 * F * 2 + (F + H) * P // 2 + E * 3 * F * H // 2
+    assert b.value >= R * F * 4 + R * 2 * F * 4
+    assert L.grouped_mlp_fp4_sizes(ctypes.byref(_dims(E, R, 96, F)), split, None, None, None) == ESHAPE
+    assert L.grouped_mlp_fp4_sizes(ctypes.byref(d), mx._i64_array([100, 0, 199]), None, None, None) == ESHAPE
+    assert L.grouped_mlp_fp4_sizes(None, split, None, None, None) == EINVAL
+    ws = f.value
+
+    def fwd(x=FAKE, w=FAKE, y=FAKE, wsb=ws, saved=None, sb=0):
+        return L.grouped_mlp_fwd_fp4(ctypes.byref(d), split, x, None, w, FAKE, y, saved, sb, FAKE, wsb, None)
+    assert fwd(x=None) == EINVAL
+    assert fwd(w=None) == EINVAL
+    assert fwd(y=ctypes.c_void_p(0x100008)) == EALIGN
+    assert fwd(wsb=ws - 1) == EWORKSPACE
+    assert fwd(saved=FAKE, sb=s.value - 1) == EWORKSPACE
+
+    def bwd(saved=FAKE, sb=s.value, wsb=b.value, dw1=FAKE):
+        return L.grouped_mlp_bwd_fp4(ctypes.byref(d), split, FAKE, None, saved, sb, FAKE, None, dw1, FAKE, 0,
+                                     FAKE, wsb, None)
+    assert bwd(saved=None) == EINVAL
+    assert bwd(dw1=None) == EINVAL
+    assert bwd(sb=s.value - 1) == EWORKSPACE
+    assert bwd(wsb=b.value - 1) == EWORKSPACE
+
+
+def test_fp4_mlp_bindings_check_state_and_shapes():
+    import torch
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    E, R, H, F = 2, 64, 256, 64
+    with pytest.raises(ValueError, match="w1"):
+        mx.grouped_mlp_fwd_fp4(bf(R, H), None, bf(E, H, 2 * F), bf(E, H, F), [32, 32])
+    with pytest.raises(ValueError, match="grouped_mlp_fwd_fp4"):
+        mx.grouped_mlp_bwd_fp4(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32]))     # an MXFP8 state
+    with pytest.raises(ValueError, match="MXFP8"):
+        mx.grouped_mlp_bwd(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32], fmt="mxfp4"))

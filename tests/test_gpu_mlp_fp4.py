@@ -1,0 +1,133 @@
+"""GPU parity of the MXFP4 grouped MLP (grouped_mlp_fwd_fp4 /
+grouped_mlp_bwd_fp4) against the oracle's MLP at quantize="mxfp4" (reading
+R17: the MXFP8 MLP of "Efficient MoE training for biological foundation
+models", Key technical approaches item 3, with every GEMM on MXFP4 copies).
+
+Bar: as for the MXFP8 MLP, normwise relative error <= 2e-2 for Y, dX, dW1,
+dW2 and dprobs, over the whole output and per expert with rows. The GPU forms
+A and dH1 in fp32 and the oracle in float64, so a requantized code can differ
+by one E2M1 step where the two straddle a rounding boundary; such flips are
+rare, and the measured errors are printed. An expert with no rows gets zero
+dW (overwrite) or keeps its dW (accumulate)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads as wl
+from tests.gpu_util import dev_bf16, dev_f32, rel_norm, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+CASES = {
+    "ragged4": dict(seed=130, E=4, H=256, F=384, split=(300, 0, 17, 200)),
+    "two_tiles_ffn": dict(seed=131, E=3, H=512, F=768, split=(257, 33, 190)),
+    "dense_one_expert": dict(seed=132, E=1, H=256, F=512, split=(384,)),
+    "many_small": dict(seed=134, E=12, H=128, F=256,
+                       split=(1, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129)),
+}
+
+
+def _rows(got, want, split, what):
+    err = rel_norm(got, want)
+    print(f"  {what}: normwise {err:.2e}", flush=True)
+    assert err <= TOL, what
+    r0 = 0
+    for e, m in enumerate(split):
+        if m:
+            ee = rel_norm(got[r0:r0 + m], want[r0:r0 + m])
+            assert ee <= TOL, f"{what} expert {e}: {ee}"
+        r0 += m
+
+
+def _experts(got, want, split, what):
+    err = rel_norm(got, want)
+    print(f"  {what}: normwise {err:.2e}", flush=True)
+    assert err <= TOL, what
+    for e, m in enumerate(split):
+        if m:
+            ee = rel_norm(got[e], want[e])
+            assert ee <= TOL, f"{what} expert {e}: {ee}"
+
+
+def _fwd(mx, c, training):
+    p = dev_f32(c["probs"])
+    y, st = mx.grouped_mlp_fwd_fp4(dev_bf16(c["x"]), p, dev_bf16(c["w1"]), dev_bf16(c["w2"]),
+                                   c["split_sizes"].tolist(), training=training)
+    torch.cuda.synchronize()
+    return y, st, p
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp4_mlp_forward_backward(gpu_lib, name):
+    k = CASES[name]
+    print(f"[mlp_fp4] {name}: E={k['E']} H={k['H']} F={k['F']} split={k['split']}", flush=True)
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    split = list(k["split"])
+    y, st, p = _fwd(gpu_lib, c, training=True)
+    fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split, quantize="mxfp4")
+    _rows(to_np(y), fwd["y"], split, "y")
+    E, H, F = k["E"], k["H"], k["F"]
+    dw1 = torch.full((E, 2 * F, H), 5.0, dtype=torch.float32, device="cuda")   # overwritten
+    dw2 = torch.full((E, H, F), 5.0, dtype=torch.float32, device="cuda")
+    dx, dp, dw1, dw2 = gpu_lib.grouped_mlp_bwd_fp4(dev_bf16(c["dy"]), p, st, dw1=dw1, dw2=dw2, accumulate=False)
+    torch.cuda.synchronize()
+    bwd = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], split, c["dy"], fwd, quantize="mxfp4")
+    _rows(to_np(dx), bwd["dx"], split, "dx")
+    _rows(to_np(dp)[:, None], bwd["dprobs"][:, None], split, "dprobs")
+    _experts(to_np(dw1), bwd["dw1"], split, "dw1")
+    _experts(to_np(dw2), bwd["dw2"], split, "dw2")
+    for e, m in enumerate(split):
+        if m == 0:
+            assert torch.all(dw1[e] == 0) and torch.all(dw2[e] == 0), f"empty expert {e}"
+
+
+def test_fp4_mlp_inference_matches_training(gpu_lib):
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    y1, st1, _ = _fwd(gpu_lib, c, training=False)
+    y2, st2, _ = _fwd(gpu_lib, c, training=True)
+    assert st1 is None and st2 is not None
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_fp4_mlp_accumulate_and_no_probs(gpu_lib):
+    """accumulate=True adds into the fp32 main gradients (an empty expert keeps
+    its values); probs None means routing weights 1."""
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"], probs="one")
+    split = list(k["split"])
+    E, H, F = k["E"], k["H"], k["F"]
+    y, st = gpu_lib.grouped_mlp_fwd_fp4(dev_bf16(c["x"]), None, dev_bf16(c["w1"]), dev_bf16(c["w2"]), split)
+    rng = np.random.default_rng(7)
+    i1 = rng.standard_normal((E, 2 * F, H)).astype(np.float32) * 1e-3
+    i2 = rng.standard_normal((E, H, F)).astype(np.float32) * 1e-3
+    dw1, dw2 = torch.from_numpy(i1).cuda(), torch.from_numpy(i2).cuda()
+    _, dp, dw1, dw2 = gpu_lib.grouped_mlp_bwd_fp4(dev_bf16(c["dy"]), None, st, dw1=dw1, dw2=dw2, accumulate=True)
+    torch.cuda.synchronize()
+    fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split, quantize="mxfp4")
+    bwd = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], split, c["dy"], fwd, quantize="mxfp4",
+                           dw1_in=i1, dw2_in=i2)
+    _rows(to_np(y), fwd["y"], split, "y")
+    _experts(to_np(dw1) - i1, bwd["dw1"] - i1, split, "dw1 increment")
+    _experts(to_np(dw2) - i2, bwd["dw2"] - i2, split, "dw2 increment")
+    assert np.array_equal(to_np(dw1)[1], i1[1]) and np.array_equal(to_np(dw2)[1], i2[1]), "empty expert changed"
+
+
+def test_fp4_mlp_differs_from_mxfp8(gpu_lib):
+    """The MXFP4 forward is not the MXFP8 one: on the same inputs the two
+    outputs differ by about the MXFP4 quantization error, and each matches its
+    own oracle."""
+    k = CASES["ragged4"]
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    split = list(k["split"])
+    y4, _, _ = _fwd(gpu_lib, c, training=False)
+    y8, _ = gpu_lib.grouped_mlp_fwd(dev_bf16(c["x"]), dev_f32(c["probs"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]),
+                                    split, training=False)
+    torch.cuda.synchronize()
+    w4 = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split, quantize="mxfp4")["y"]
+    w8 = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split)["y"]
+    gap = rel_norm(w4, w8)
+    assert gap > 5 * TOL                      # the formats really differ on these inputs
+    assert rel_norm(to_np(y4), w4) <= TOL and rel_norm(to_np(y8), w8) <= TOL
