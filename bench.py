@@ -202,6 +202,7 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip token dispatch / combine")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock")
     ap.add_argument("--no-gemm-fp4", action="store_true", help="skip the MXFP4 GEMM")
+    ap.add_argument("--no-fp4-step", action="store_true", help="skip the MXFP4 MLP step")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward-only Llama dense and Mixtral-shaped workloads")
     ap.add_argument("--quantize-only", action="store_true",
@@ -367,6 +368,14 @@ def main():
     if not args.no_qinit:
         measure_qinit(args, runner, x, probs, w1, w2, dy, dw1, dw2, start, end, step_flops, out, torch)
 
+    # the same step with every GEMM on MXFP4 copies (the MLP of an FP4 layer)
+    if not args.no_fp4_step:
+        out["mxfp4_step"] = measure_fp4_step(mx, torch, args, x, probs, w1, w2, dy, dw1, dw2, split, step_flops,
+                                             ms_per_step)
+        f4s = out["mxfp4_step"]
+        log(f"MXFP4 step {f4s['ms']:.3f} ms -> {f4s['tflops']:.1f} TFLOP/s "
+            f"({f4s['speedup_vs_mxfp8']:.2f}x the MXFP8 step)")
+
     samples, c2_rows = {}, None
     if not args.no_quantize:
         out["quantize"], c2_rows = measure_quantize(mx, torch, np, wlmod, dev)
@@ -418,6 +427,39 @@ def main():
         out["cpu_baseline"] = cpu_baseline(samples, tiny, c2_rows)
         log(f"oracle {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s on {out['cpu_baseline']['cores']} threads")
     print(json.dumps(out), flush=True)
+
+
+def measure_fp4_step(mx, torch, args, x, probs, w1, w2, dy, dw1, dw2, split, step_flops, ms_mxfp8):
+    """grouped_mlp_fwd_fp4 (training) + grouped_mlp_bwd_fp4 (accumulating into
+    the fp32 gradients) on the step's inputs: the same work as the MXFP8 step
+    (18 R H F flops) with every GEMM on MXFP4 copies; workspaces allocated
+    once, outside the timed region."""
+    R, H = x.shape
+    E, F2, _ = w1.shape
+    F = F2 // 2
+    fws, _, bws = mx.mlp_fp4_sizes(E, R, H, F, split)
+    wsf = torch.empty(fws, dtype=torch.uint8, device=x.device)
+    wsb = torch.empty(bws, dtype=torch.uint8, device=x.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
+
+    def step():
+        _, st = mx.grouped_mlp_fwd_fp4(x, probs, w1, w2, split, training=True, workspace=wsf, out=y)
+        mx.grouped_mlp_bwd_fp4(dy, probs, st, dw1=dw1, dw2=dw2, accumulate=True, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"workload": "mixtral_moe_fwd_bwd at MXFP4", "ms": round(ms, 4),
+            "tflops": round(step_flops / (ms * 1e-3) / 1e12, 1), "frac_fp4_peak": round(
+                step_flops / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4),
+            "speedup_vs_mxfp8": round(ms_mxfp8 / ms, 3)}
 
 
 def measure_clock(step, torch, seconds=2.0, samples=3):

@@ -374,11 +374,11 @@ static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4
 // that holds only 32 valid values gets scale code 0 for the invalid half on
 // both operands, so its products (at most 36 * 2^-254) add exact zeros
 // whatever codes lie past the group; C_g is fp32, stored or accumulated.
-template <bool GK>
+template <bool GK, bool F32>
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                                        const uint8_t* bs, Fp4Groups gr, Fp4KGroups kg, int64_t M,
                                                        int64_t N, int64_t K, int64_t n_tiles_n, void* c,
-                                                       int32_t c_f32, int32_t accumulate) {
+                                                       int32_t accumulate) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
@@ -389,10 +389,26 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int l32 = lane & 31, h = lane >> 5;
   int grp;   // the group (expert) of this tile
   int64_t row_end, am0, bn0, kbeg = 0, klen = K;
+  // Tile id. Group-K: consecutive ids (raster neighbours) run together on one
+  // XCD. Group-M keeps the launch order: with a multiple of 8 n-tiles, block
+  // b's n-tile (and its rows of B) stays on XCD b % 8 for every m-tile.
+  const int64_t per_group = GK ? ((M + TM - 1) / TM) * n_tiles_n : 0;
+  const int id = GK ? xcd_remap((int)blockIdx.x, (int)(kg.n * per_group)) : (int)blockIdx.x;
   if constexpr (GK) {
-    const int64_t per_group = ((M + TM - 1) / TM) * n_tiles_n;
-    grp = (int)(blockIdx.x / per_group);
-    const int64_t rem = blockIdx.x - grp * per_group;
+    // Every group has per_group tiles. When that is a multiple of kXcdChunk,
+    // chunk q of kXcdChunk ids goes to group (q % n + q / n) % n as its chunk
+    // q / n: the tiles running at one time mix groups of different k lengths
+    // (k-loops and fp32 stores overlap across CUs) while one XCD's chunk
+    // stays inside one group.
+    int64_t rem;
+    if (per_group % kXcdChunk == 0) {
+      const int64_t q = id / kXcdChunk, r = q / kg.n, pos = q - r * kg.n;
+      grp = (int)((pos + r) % kg.n);
+      rem = r * kXcdChunk + (id - q * kXcdChunk);
+    } else {
+      grp = (int)(id / per_group);
+      rem = id - grp * per_group;
+    }
     const int64_t mt = rem / n_tiles_n, nt = rem - mt * n_tiles_n;
     row_end = M;
     am0 = mt * TM;
@@ -400,7 +416,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     kbeg = kg.k0[grp];
     klen = kg.k0[grp + 1] - kbeg;
   } else {
-    const int64_t mt = blockIdx.x / n_tiles_n, nt = blockIdx.x - mt * n_tiles_n;
+    const int64_t mt = id / n_tiles_n, nt = id - mt * n_tiles_n;
     // group of m-tile mt: the last group whose first m-tile is <= mt (empty
     // groups own no m-tile)
     int lo = 0, hi = gr.n - 1;
@@ -534,6 +550,73 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // lane l holds row 32 i + l32 and, per MFMA tile, columns 8 g + 4 h .. +3
   // (g = 0..3) in accumulator elements 4 g .. 4 g + 3
   const int64_t m0 = am0 + TM / 2 * wm, n0 = bn0 + TN / 2 * wn;
+  if (F32 && (N & 31) == 0 && N <= (1 << 22)) {
+    // fp32 C leaves through the wave's 32 KB LDS slice (the operand stages
+    // are free after the k-loop's last barrier) so that every store covers
+    // whole 128-byte rows: 32 x 32 block (i, j) is staged as [row][16-byte
+    // chunk], chunk c of row r at slot c ^ (r & 7), and read back so that lane
+    // L holds row 8 q + L / 8, chunk L % 8 (q = 0..3). Old values of an
+    // accumulating store are loaded in that layout, two 32-row blocks ahead.
+    const int64_t wrows = min<int64_t>(TM / 2, row_end - m0);
+    if (wrows <= 0) return;
+    uint8_t* const slice = wave < 2 ? sA[0] + wave * 32768 : sB[0] + (wave - 2) * 32768;
+    const char* cb = reinterpret_cast<const char*>(c) + ((GK ? (int64_t)grp * M * N : 0) + m0 * N + n0) * 4;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(cb, wrows * N * 4);
+    const uint32_t ld = (uint32_t)N;
+    const int rr = lane >> 3, cc = lane & 7;
+    const int jv = (int)min<int64_t>(SN, (N - n0) / 32);     // 32-column blocks inside C
+    auto coff = [&](int i, int j, int q) __attribute__((always_inline)) -> uint32_t {
+      return ((uint32_t)(32 * i + 8 * q + rr) * ld + 32 * j + 4 * cc) * 4;
+    };
+    constexpr int kOnce = 2;   // cache policy of memory touched once: non-temporal
+    u32x4 old[2][SN][4];
+    const bool acc_old = GK && accumulate;
+    auto load_old = [&](int i, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) old[buf][j][q] = __builtin_amdgcn_raw_buffer_load_b128(rd, coff(i, j, q), 0, kOnce);
+    };
+    if (acc_old) {
+      load_old(0, 0);
+      load_old(1, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      uint8_t* const st = slice + (i & 1) * (SN * 4096);
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x4 v;
+          v.x = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 0]));
+          v.y = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 1]));
+          v.z = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 2]));
+          v.w = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 3]));
+          const int ch = 2 * g + h;
+          *reinterpret_cast<u32x4*>(st + j * 4096 + l32 * 128 + ((ch ^ (l32 & 7)) << 4)) = v;
+        }
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        if (j < jv) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(st + j * 4096 + (8 * q + rr) * 128 + ((cc ^ rr) << 4));
+            if (acc_old) {
+              const u32x4 o = old[i & 1][j][q];
+              v.x = __float_as_uint(__uint_as_float(v.x) + __uint_as_float(o.x));
+              v.y = __float_as_uint(__uint_as_float(v.y) + __uint_as_float(o.y));
+              v.z = __float_as_uint(__uint_as_float(v.z) + __uint_as_float(o.z));
+              v.w = __float_as_uint(__uint_as_float(v.w) + __uint_as_float(o.w));
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, coff(i, j, q), 0, kOnce);
+          }
+        }
+      }
+      if (acc_old && i + 2 < SM) load_old(i + 2, i & 1);
+    }
+    return;
+  }
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
@@ -547,7 +630,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
         // through a VALU move, so the accumulators stay AGPR-only operands
         const float x0 = vgpr_hop(acc[j][i][4 * g]), x1 = vgpr_hop(acc[j][i][4 * g + 1]);
         const float x2 = vgpr_hop(acc[j][i][4 * g + 2]), x3 = vgpr_hop(acc[j][i][4 * g + 3]);
-        if (c_f32) {
+        if constexpr (F32) {
           float* cp = reinterpret_cast<float*>(c) + (GK ? (int64_t)grp * M * N : 0) + row * N + col;
           if (vec && col + 3 < N) {
             float4 v = make_float4(x0, x1, x2, x3);
@@ -583,8 +666,12 @@ hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b
   const int64_t tm = gr.tile0[gr.n], tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
   if (tm * tn == 0) return hipSuccess;
   Fp4KGroups kg{};
-  hipLaunchKernelGGL(gemm_fp4_kernel<false>, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs, gr, kg,
-                     (int64_t)0, N, K, tn, c, c_f32, 0);
+  if (c_f32)
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs,
+                       gr, kg, (int64_t)0, N, K, tn, c, 0);
+  else
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs,
+                       gr, kg, (int64_t)0, N, K, tn, c, 0);
   return hipGetLastError();
 }
 
@@ -595,8 +682,8 @@ hipError_t launch_gemm_fp4_group_k(const uint8_t* a, const uint8_t* as, const ui
   const int64_t tiles = (int64_t)kg.n * tm * tn;
   if (tiles == 0) return hipSuccess;
   Fp4Groups gr{};
-  hipLaunchKernelGGL(gemm_fp4_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs, gr, kg, M, N,
-                     kg.k0[kg.n], tn, c, 1, accumulate);
+  hipLaunchKernelGGL((gemm_fp4_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs, gr, kg,
+                     M, N, kg.k0[kg.n], tn, c, accumulate);
   return hipGetLastError();
 }
 

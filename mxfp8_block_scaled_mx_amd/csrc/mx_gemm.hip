@@ -80,23 +80,8 @@ struct TileCoord {
   int mt, nt; // tile indices within the group
 };
 
-// Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8). Tile
-// ids are handed out in rounds of 8 x kXcdChunk: in each round XCD x takes
-// kXcdChunk consecutive ids, so the tiles running together on one XCD are
-// raster neighbours (they share A and B rows in that XCD's L2) while all XCDs
-// walk the id space at the same pace, which keeps tiles of unequal cost
-// (group-K slots sorted by size) balanced across XCDs. Blocks of the last,
-// partial round keep their own id.
-constexpr int kXcdChunk = 32;
 // words of k-tiled scales per LDS stage: A 16 row groups, B 8 row groups
 [[maybe_unused]] constexpr int kScStage = 768;
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  constexpr int round = 8 * kXcdChunk;
-  const int full = total / round * round;
-  if (bid >= full) return bid;
-  const int xcd = bid & 7, local = bid >> 3;
-  return (local / kXcdChunk) * round + xcd * kXcdChunk + local % kXcdChunk;
-}
 
 // Slot of a tile id: slots hold consecutive id ranges (tile0), except in an
 // interleaved group-K plan, where chunk q of kXcdChunk ids belongs to slot

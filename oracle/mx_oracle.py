@@ -653,14 +653,19 @@ def e2m1_encode(t) -> np.ndarray:
     the definition: distance to each of the 8 magnitudes, smallest wins, an
     equal distance goes to the even code."""
     t = np.asarray(t, dtype=np.float64)
-    a = np.abs(t)[..., None]
-    d = np.abs(a - E2M1_VALUES)
-    best = np.argmin(d, axis=-1)                        # first (lower) code on a tie
-    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
-    nxt = np.minimum(best + 1, 7)
-    tie = (np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0] == dmin) & (nxt != best)
-    code = np.where(tie & (best % 2 == 1), nxt, best)
-    return (code | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+    flat = t.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 22                                      # elements per pass (bounds the 8-way distance table)
+    for i in range(0, flat.size, step):
+        c = flat[i:i + step]
+        d = np.abs(np.abs(c)[:, None] - E2M1_VALUES)
+        best = np.argmin(d, axis=-1)                    # first (lower) code on a tie
+        dmin = np.take_along_axis(d, best[:, None], axis=-1)[:, 0]
+        nxt = np.minimum(best + 1, 7)
+        tie = (np.take_along_axis(d, nxt[:, None], axis=-1)[:, 0] == dmin) & (nxt != best)
+        code = np.where(tie & (best % 2 == 1), nxt, best)
+        out[i:i + step] = code | np.where(np.signbit(c), 8, 0)
+    return out.reshape(t.shape)
 
 
 def quantize_rowwise_fp4(x):

@@ -131,3 +131,49 @@ def test_fp4_mlp_differs_from_mxfp8(gpu_lib):
     gap = rel_norm(w4, w8)
     assert gap > 5 * TOL                      # the formats really differ on these inputs
     assert rel_norm(to_np(y4), w4) <= TOL and rel_norm(to_np(y8), w8) <= TOL
+
+
+def test_fp4_mlp_fullsize_sampled(gpu_lib):
+    """The Mixtral-8x7B-shaped MoE MLP forward + backward at MXFP4 (4096
+    tokens top-2 of 8: 8192 rows, H = 4096, F = 14336), in the calls the
+    benchmark times (training forward, backward accumulating into zeroed fp32
+    gradients), on the rows and dW entries whose expected values
+    tests/golden/make_fullsize.py --mxfp4 computed from the oracle alone."""
+    import os
+    from tests.golden.make_fullsize import golden_path
+    name = "mixtral_moe_fwd_bwd"
+    path = golden_path(name, "mxfp4")
+    if not os.path.exists(path):
+        pytest.skip(f"{os.path.basename(path)} not generated")
+    g = np.load(path, allow_pickle=False)
+    w = wl.WORKLOADS[name]
+    print(f"[mlp_fp4 fullsize] {name}: generating inputs", flush=True)
+    c = wl.make_mlp_inputs(w, with_dy=True)
+    split = c["split_sizes"].astype(np.int64)
+    assert np.array_equal(split, g["split"]), "input generator drifted from the stored sample"
+    E, H, F = w.experts, w.hidden, w.ffn
+    p = dev_f32(c["probs"])
+    print(f"[mlp_fp4 fullsize] {name}: forward", flush=True)
+    y, st = gpu_lib.grouped_mlp_fwd_fp4(dev_bf16(c["x"]), p, dev_bf16(c["w1"]), dev_bf16(c["w2"]), split.tolist())
+    dw1 = torch.zeros((E, 2 * F, H), dtype=torch.float32, device="cuda")
+    dw2 = torch.zeros((E, H, F), dtype=torch.float32, device="cuda")
+    print(f"[mlp_fp4 fullsize] {name}: backward", flush=True)
+    dx, dp, dw1, dw2 = gpu_lib.grouped_mlp_bwd_fp4(dev_bf16(c["dy"]), p, st, dw1=dw1, dw2=dw2, accumulate=True)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(g["rows"]).cuda()
+    for key, t in (("y", y), ("dx", dx)):
+        got = to_np(t[sel])
+        errs = [rel_norm(got[i], g[key][i]) for i in range(len(g["rows"]))]
+        print(f"[mlp_fp4 fullsize] {key} max row error {max(errs):.2e}", flush=True)
+        assert max(errs) <= TOL, key
+    err = rel_norm(to_np(dp[sel]), g["dprobs"])
+    print(f"[mlp_fp4 fullsize] dprobs error {err:.2e}", flush=True)
+    assert err <= TOL
+    for key, buf in (("dw1", dw1), ("dw2", dw2)):
+        idx = g[f"{key}_idx"]
+        got = buf[tuple(torch.from_numpy(idx[:, k]).cuda() for k in range(3))].cpu().numpy().astype(np.float64)
+        for e in np.unique(idx[:, 0]).tolist():
+            m = idx[:, 0] == e
+            err = rel_norm(got[m], g[key][m])
+            print(f"[mlp_fp4 fullsize] {key} expert {e} error {err:.2e}", flush=True)
+            assert err <= TOL, f"{key} expert {e}: {err}"
