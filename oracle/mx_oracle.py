@@ -80,6 +80,26 @@ R17 MXFP4 MLP: the MLP of R7-R11 with every MXFP8 copy replaced by the MXFP4
     of its mxfp4 model in FP4, so an FP4 layer's MLP runs its GEMMs on MXFP4
     copies; that the recipe is otherwise the MXFP8 one is the plainest
     reading. Selected by quantize="mxfp4" in the MLP functions below.
+R18 NVFP4 (the 4-bit recipe the Llama 3 recipe page lists beside MXFP8, and
+    whose first and last layers the ROCm page keeps in BF16; neither page
+    defines its arithmetic, so this is the published form of the format):
+    E2M1 elements (R14's values) in blocks of 16 consecutive values, one
+    E4M3 scale per block (a positive R3 code) and one float32 scale per
+    tensor. In float32 arithmetic, each step rounded to nearest even:
+      S   = 2688 / amax of the whole tensor (2688 = 448 * 6, the largest
+            E4M3 times the largest E2M1); amax = 0 gives S = 1, and S is
+            capped at 2^64 (so that S over any block scale stays finite);
+      s_b = E4M3 code (R3) of (bmax / 6) * S, bmax the block's largest
+            magnitude;
+      q   = E2M1 code (R14: nearest, ties to even, saturating at 6, sign kept)
+            of x * (S / E4M3(s_b)); a block whose scale code is 0 gets codes
+            0 (0x8 for a negative input).
+    The value of element q with block scale s_b is E2M1(q) * E4M3(s_b) / S.
+    The decisions (codes) are taken in float32 on both sides because they
+    depend on rounding; products and sums of the GEMM are float64 here.
+    Layouts: codes packed as R14 (element 2i in the low nibble), scales
+    [rows, cols / 16] row-major; the columnwise copy is the rowwise copy of
+    the transpose with the same S.
 """
 from __future__ import annotations
 
@@ -98,6 +118,8 @@ __all__ = [
     "dequantize_rowwise_fp4", "gemm_fp4", "gemm_fp4_grouped", "E2M1_VALUES",
     "mlp_backward", "mlp_forward_rows", "mlp_backward_rows",
     "mlp_backward_wgrad_entries", "quantize_colwise_fp4", "gemm_fp4_group_k",
+    "NV_BLOCK", "nvfp4_tensor_scale", "quantize_rowwise_nvfp4", "quantize_colwise_nvfp4",
+    "dequantize_rowwise_nvfp4", "gemm_nvfp4", "gemm_nvfp4_grouped",
 ]
 
 
@@ -767,3 +789,93 @@ def gemm_fp4_group_k(a_q, a_s, b_q, b_s, sizes):
         k0 += p
     return C
 
+
+# ---------------------------------------------------------------------------
+# NVFP4 (R18): E2M1 elements, one E4M3 scale per 16 values, one float32
+# scale per tensor
+
+NV_BLOCK = 16
+NVFP4_RANGE = np.float32(448.0 * 6.0)
+NVFP4_SCALE_CAP = np.float32(2.0 ** 64)
+
+
+def nvfp4_tensor_scale(amax) -> np.float32:
+    """R18: S = 2688 / amax in float32 (one rounding), 1 for amax = 0, at most 2^64."""
+    a = np.float32(amax)
+    if a == 0:
+        return np.float32(1.0)
+    with np.errstate(over="ignore"):
+        q = np.float32(NVFP4_RANGE / a)
+    return np.float32(min(q, NVFP4_SCALE_CAP))
+
+
+def quantize_rowwise_nvfp4(x):
+    """Rowwise NVFP4 of [rows, cols] (cols % 16 == 0; values exact in
+    float32) -> (packed codes [rows, cols/2] uint8, E4M3 block-scale codes
+    [rows, cols/16] uint8, amax float32). The steps of R18 in order, each a
+    float32 operation."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if cols % NV_BLOCK:
+        raise ValueError("cols must be a multiple of 16")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the quantizer's contract")
+    xf = x.astype(np.float32)
+    if not np.array_equal(xf.astype(np.float64), x):
+        raise ValueError("inputs must be exact float32 values")
+    amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0.0)
+    S = nvfp4_tensor_scale(amax)
+    v = xf.reshape(rows, cols // NV_BLOCK, NV_BLOCK)
+    bmax = np.max(np.abs(v), axis=-1)
+    t = (bmax / np.float32(6.0)).astype(np.float32)
+    sb = (t * S).astype(np.float32)
+    sc = e4m3_encode(sb.astype(np.float64))
+    sv = e4m3_value(sc).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        r = np.where(sv > 0, S / np.where(sv > 0, sv, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    y = (v * r[..., None]).astype(np.float32)
+    codes = e2m1_encode(y.astype(np.float64)).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc.astype(np.uint8), amax
+
+
+def quantize_colwise_nvfp4(x):
+    """Columnwise NVFP4 (R18): the rowwise copy of the transpose, blocks of 16
+    consecutive rows per column (rows % 16 == 0), same tensor scale."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[0] % NV_BLOCK:
+        raise ValueError("rows must be a multiple of 16")
+    return quantize_rowwise_nvfp4(x.T)
+
+
+def dequantize_rowwise_nvfp4(q, s, amax):
+    """value = E2M1(code) * E4M3(block scale) / S (float64), S from amax (R18)."""
+    q = np.asarray(q, dtype=np.uint8)
+    codes = np.empty((q.shape[0], q.shape[1] * 2), dtype=np.uint8)
+    codes[:, 0::2] = q & 0xF
+    codes[:, 1::2] = q >> 4
+    scale = np.repeat(e4m3_value(s), NV_BLOCK, axis=1)
+    return e2m1_value(codes) * scale / np.float64(nvfp4_tensor_scale(amax))
+
+
+def gemm_nvfp4(a_q, a_s, a_amax, b_q, b_s, b_amax):
+    """C = A . B^T (float64) for rowwise NVFP4 operands A [m, k], B [n, k],
+    each element at its R18 value; the plain product of the dequantized
+    operands is the definition."""
+    return dequantize_rowwise_nvfp4(a_q, a_s, a_amax) @ dequantize_rowwise_nvfp4(b_q, b_s, b_amax).T
+
+
+def gemm_nvfp4_grouped(a_q, a_s, a_amax, b_q, b_s, b_amax, sizes):
+    """GroupedLinear at NVFP4: consecutive groups of sizes[g] rows of A times
+    B_g^T, each group's weight B_g with its own tensor scale (b_amax[g]).
+    Returns float64 [sum(sizes), n]."""
+    sizes = [int(v) for v in sizes]
+    n = b_q.shape[1]
+    C = np.zeros((sum(sizes), n))
+    A = dequantize_rowwise_nvfp4(a_q, a_s, a_amax)
+    r0 = 0
+    for g, m in enumerate(sizes):
+        if m:
+            C[r0:r0 + m] = A[r0:r0 + m] @ dequantize_rowwise_nvfp4(b_q[g], b_s[g], b_amax[g]).T
+        r0 += m
+    return C
