@@ -400,6 +400,55 @@ MX_API mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const
                                      mx_dtype c_dtype, void* stream);
 
 /*
+ * NVFP4 -- the 4-bit recipe the Llama 3 recipe page lists beside FP8 and
+ * MXFP8 ("TransformerEngine-accelerated Llama 3 training with native PyTorch
+ * training loop", Supported Models and Training Features, and Quantized
+ * Training), and whose first and last layers the MI355X recipe keeps in BF16
+ * ("examples/llama: default-on fusion & DP-comm perf toggles - #141",
+ * Changes). The pages name the format but not its arithmetic; this library
+ * implements its published form: E2M1 elements in blocks of 16 values with
+ * one E4M3 scale per block and one fp32 scale per tensor. In fp32 arithmetic
+ * rounded to nearest:
+ *     S   = 2688 / amax (448 * 6; 1 for amax = 0; at most 2^64)
+ *     s_b = E4M3 code of (bmax / 6) * S, saturating at 448
+ *     q   = E2M1 code of x * (S / E4M3(s_b)) (nearest, ties to even,
+ *           saturating at 6, sign kept; 0 / 0x8 when s_b = 0)
+ * and an element's value is E2M1(q) * E4M3(s_b) / S.
+ *
+ * mx_quantize_nvfp4 -- x bf16 [rows, cols] (contiguous, cols % 16 == 0):
+ *   amax   device fp32, receives max |x| of the whole tensor (the call
+ *          reduces it first; NULL is an error);
+ *   q, s   rowwise codes [rows, cols/2] (two per byte, low nibble first) and
+ *          E4M3 scale codes [rows, cols/16]; or both NULL;
+ *   q_col, s_col  the columnwise copy (rowwise copy of the transpose, blocks
+ *          of 16 rows; rows % 16 == 0) [cols, rows/2] and [cols, rows/16];
+ *          or both NULL. Both copies use the same S.
+ * Errors: MX_ESHAPE, MX_EINVAL (no output, half a layout, null x or amax),
+ * MX_EALIGN (x 16-byte, q/q_col 8-byte, amax 4-byte), MX_EUNSUPPORTED,
+ * MX_EHIP.
+ *
+ * mx_gemm_nvfp4 / mx_grouped_gemm_nvfp4 -- C = A . B^T (grouped: group g's
+ * rows of A times its weight B_g^T) with NVFP4 operands in the rowwise layout
+ * of mx_quantize_nvfp4, A's tensor amax at a_amax and B_g's at b_amax[g]
+ * (device fp32; one per group). gfx950's scaled MFMA takes power-of-two
+ * (E8M0) scales per 32 values only, so NVFP4 runs on the bf16 MFMA: every
+ * element times its E4M3 block scale is exact in bf16 and is formed in
+ * registers; sums are fp32; the product of the two 1/S factors is applied
+ * once to each result (one fp32 rounding). k must be a positive multiple of
+ * 128 (at most 2^24); scales 8-byte aligned; other requirements, outputs and
+ * errors as mx_gemm_fp4 / mx_grouped_gemm_fp4.
+ */
+MX_API mx_status mx_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                                   uint8_t* q_col, uint8_t* s_col, float* amax, void* stream);
+MX_API mx_status mx_gemm_nvfp4(const uint8_t* a, const uint8_t* a_s, const float* a_amax, const uint8_t* b,
+                               const uint8_t* b_s, const float* b_amax, int64_t m, int64_t n, int64_t k, void* c,
+                               mx_dtype c_dtype, void* stream);
+MX_API mx_status mx_grouped_gemm_nvfp4(const uint8_t* a, const uint8_t* a_s, const float* a_amax, const uint8_t* b,
+                                       const uint8_t* b_s, const float* b_amax, const int64_t* group_sizes,
+                                       int32_t groups, int64_t n, int64_t k, void* c, mx_dtype c_dtype,
+                                       void* stream);
+
+/*
  * MXFP4 MLP -- the grouped MLP of grouped_mlp_fwd / grouped_mlp_bwd with
  * every GEMM on MXFP4 copies (E2M1 elements, one E8M0 scale per 32 values;
  * as mx_quantize_fp4) instead of MXFP8: the MLP of a layer assigned to FP4

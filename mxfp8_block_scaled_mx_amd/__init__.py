@@ -138,6 +138,12 @@ def load() -> ctypes.CDLL:
     L.grouped_mlp_bwd_fp4.restype = ctypes.c_int
     L.grouped_mlp_bwd_fp4.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
                                       vp, sz, vp]
+    L.mx_quantize_nvfp4.restype = ctypes.c_int
+    L.mx_quantize_nvfp4.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.mx_gemm_nvfp4.restype = ctypes.c_int
+    L.mx_gemm_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+    L.mx_grouped_gemm_nvfp4.restype = ctypes.c_int
+    L.mx_grouped_gemm_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, p64, i32, i64, i64, vp, i32, vp]
     L.mx_device_copy.restype = ctypes.c_int
     L.mx_device_copy.argtypes = [vp, vp, i64, vp]
     L.mx_set_stage_events.restype = ctypes.c_int
@@ -658,6 +664,65 @@ def mx_grouped_gemm_fp4(a_q, a_s, b_q, b_s, group_sizes, out_dtype=torch.bfloat1
     _check(L.mx_grouped_gemm_fp4(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), arr, G, n, k, _ptr(out), dt,
                                  _stream(stream)))
     return out
+
+
+def mx_quantize_nvfp4(x: torch.Tensor, colwise: bool = False, rowwise: bool = True, stream=None):
+    """NVFP4 of bf16 x [rows, cols] (mx_quantize_nvfp4): returns (q [rows,
+    cols/2], s [rows, cols/16] E4M3 codes, amax [1] fp32) rowwise, and with
+    colwise also (q_col [cols, rows/2], s_col [cols, rows/16]); None for a
+    layout not asked for."""
+    if not (isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+            and x.is_cuda):
+        raise ValueError("mx_quantize_nvfp4: x must be a contiguous 2-D bfloat16 CUDA tensor")
+    L = load()
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if rowwise else None
+    s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if rowwise else None
+    qc = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if colwise else None
+    sc = torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev) if colwise else None
+    amax = torch.empty((1,), dtype=torch.float32, device=dev)
+    _check(L.mx_quantize_nvfp4(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(qc), _ptr(sc), _ptr(amax),
+                               _stream(stream)))
+    return (q, s, amax, qc, sc) if colwise else (q, s, amax)
+
+
+def mx_grouped_gemm_nvfp4(a_q, a_s, a_amax, b_q, b_s, b_amax, group_sizes, out_dtype=torch.bfloat16, out=None,
+                          stream=None):
+    """Grouped NVFP4 GEMM (mx_grouped_gemm_nvfp4): rows of group g of A (a_q
+    [M, k/2], a_s [M, k/16], a_amax [1]) times B_g^T (b_q [G, n, k/2], b_s
+    [G, n, k/16], b_amax [G]); returns C [M, n] (bf16 or fp32)."""
+    L = load()
+    sizes = [int(v) for v in group_sizes]
+    G, n, k = len(sizes), b_q.shape[1], a_q.shape[1] * 2
+    m = a_q.shape[0]
+    for t in (a_q, a_s, b_q, b_s):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("mx_grouped_gemm_nvfp4: codes and scales must be contiguous uint8 tensors")
+    for t, want in ((a_amax, 1), (b_amax, G)):
+        if t.dtype != torch.float32 or t.numel() != want or not t.is_contiguous():
+            raise ValueError("mx_grouped_gemm_nvfp4: a_amax must be 1 and b_amax G fp32 values")
+    if (sum(sizes) != m or tuple(a_s.shape) != (m, k // 16) or tuple(b_q.shape) != (G, n, k // 2)
+            or tuple(b_s.shape) != (G, n, k // 16)):
+        raise ValueError("mx_grouped_gemm_nvfp4: operand shapes do not match the group sizes")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_q.device)
+    if tuple(out.shape) != (m, n) or not out.is_contiguous() or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("mx_grouped_gemm_nvfp4: out must be a contiguous bf16 or fp32 [M, n] tensor")
+    dt = MX_F32 if out.dtype == torch.float32 else MX_BF16
+    arr = (ctypes.c_int64 * max(G, 1))(*sizes)
+    _check(L.mx_grouped_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_amax), _ptr(b_q), _ptr(b_s), _ptr(b_amax), arr, G,
+                                   n, k, _ptr(out), dt, _stream(stream)))
+    return out
+
+
+def mx_gemm_nvfp4(a_q, a_s, a_amax, b_q, b_s, b_amax, out_dtype=torch.bfloat16, out=None, stream=None):
+    """C [m, n] = A . B^T on rowwise NVFP4 operands (mx_gemm_nvfp4): the grouped
+    call with one group."""
+    if b_q.dim() != 2 or b_s.dim() != 2:
+        raise ValueError("mx_gemm_nvfp4: b_q and b_s must be 2-D")
+    return mx_grouped_gemm_nvfp4(a_q, a_s, a_amax, b_q.unsqueeze(0), b_s.unsqueeze(0), b_amax.reshape(1),
+                                 [a_q.shape[0]], out_dtype=out_dtype, out=out, stream=stream)
 
 
 def mx_quantize_fp4_colwise_grouped(x, group_sizes, stream=None):

@@ -546,14 +546,17 @@ mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, con
 
 }  // namespace
 
-// MXFP4 (grouped) GEMM: validation, group table, launch.
-static mx_status gemm_fp4_impl(const char* who, const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
-                               const uint8_t* b_s, const int64_t* sizes, int32_t groups, int64_t n, int64_t k,
-                               void* c, mx_dtype c_dtype, void* stream) {
+// 4-bit (grouped) GEMM, MXFP4 or (nv) NVFP4 operands: validation, group
+// table, launch.
+static mx_status gemm_4bit_impl(const char* who, bool nv, const uint8_t* a, const uint8_t* a_s, const float* a_amax,
+                                const uint8_t* b, const uint8_t* b_s, const float* b_amax, const int64_t* sizes,
+                                int32_t groups, int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream) {
   if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
   if (groups < 1 || groups > MX_MAX_GROUPS) return fail(MX_EINVAL, "%s: need 1 <= groups <= %d", who, MX_MAX_GROUPS);
   if (!sizes) return fail(MX_EINVAL, "%s: null group sizes", who);
-  if (n < 0 || k <= 0 || k % 64) return fail(MX_ESHAPE, "%s: need n >= 0 and k a positive multiple of 64", who);
+  const int64_t kq = nv ? 128 : 64;
+  if (n < 0 || k <= 0 || k % kq)
+    return fail(MX_ESHAPE, "%s: need n >= 0 and k a positive multiple of %lld", who, (long long)kq);
   if (k > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: k above 2^24", who);
   mx::Fp4Groups gr{};
   gr.n = groups;
@@ -570,13 +573,24 @@ static mx_status gemm_fp4_impl(const char* who, const uint8_t* a, const uint8_t*
   if (mtiles * ntiles > kI32Max) return fail(MX_EUNSUPPORTED, "%s: too many output tiles", who);
   gr.tile0[groups] = (int32_t)mtiles;
   if (rows == 0 || n == 0) return MX_OK;
-  if (!a || !a_s || !b || !b_s || !c) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!a || !a_s || !b || !b_s || !c || (nv && (!a_amax || !b_amax)))
+    return fail(MX_EINVAL, "%s: null pointer argument", who);
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16))
     return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
-  hipError_t e = mx::launch_gemm_fp4(a, a_s, b, b_s, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
-                                     reinterpret_cast<hipStream_t>(stream));
+  if (nv && (!aligned(a_s, 8) || !aligned(b_s, 8) || !aligned(a_amax, 4) || !aligned(b_amax, 4)))
+    return fail(MX_EALIGN, "%s: scales must be 8-byte and tensor amax 4-byte aligned", who);
+  hipError_t e = nv ? mx::launch_gemm_nvfp4(a, a_s, a_amax, b, b_s, b_amax, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
+                                            reinterpret_cast<hipStream_t>(stream))
+                    : mx::launch_gemm_fp4(a, a_s, b, b_s, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
+                                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, who);
   return MX_OK;
+}
+
+static mx_status gemm_fp4_impl(const char* who, const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
+                               const uint8_t* b_s, const int64_t* sizes, int32_t groups, int64_t n, int64_t k,
+                               void* c, mx_dtype c_dtype, void* stream) {
+  return gemm_4bit_impl(who, false, a, a_s, nullptr, b, b_s, nullptr, sizes, groups, n, k, c, c_dtype, stream);
 }
 
 extern "C" {
@@ -1341,6 +1355,46 @@ mx_status mx_grouped_gemm_fp4_wgrad(const uint8_t* a, const uint8_t* a_s, const 
                                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, who);
   return MX_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+mx_status mx_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                            uint8_t* s_col, float* amax, void* stream) {
+  g_err[0] = 0;
+  const char* who = "mx_quantize_nvfp4";
+  if (rows < 0 || cols <= 0 || cols % 16)
+    return fail(MX_ESHAPE, "%s: need rows >= 0 and cols a positive multiple of 16", who);
+  if (q_col != nullptr && rows % 16) return fail(MX_ESHAPE, "%s: the columnwise copy needs rows % 16 == 0", who);
+  if ((q == nullptr) != (s == nullptr) || (q_col == nullptr) != (s_col == nullptr))
+    return fail(MX_EINVAL, "%s: codes and scales of a layout must both be given or both be null", who);
+  if (q == nullptr && q_col == nullptr) return fail(MX_EINVAL, "%s: no output requested", who);
+  if (!amax || (rows > 0 && !x)) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(q_col, 8) || !aligned(amax, 4))
+    return fail(MX_EALIGN, "%s: x must be 16-byte, q and q_col 8-byte and amax 4-byte aligned", who);
+  if (cdiv(rows, 128) * cdiv(cols, 64) > kI32Max) return fail(MX_EUNSUPPORTED, "%s: tensor too large", who);
+  hipError_t e = mx::launch_quantize_nvfp4(x, rows, cols, q, s, q_col, s_col, amax,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mx_quantize_nvfp4 launch");
+  return MX_OK;
+}
+
+mx_status mx_gemm_nvfp4(const uint8_t* a, const uint8_t* a_s, const float* a_amax, const uint8_t* b,
+                        const uint8_t* b_s, const float* b_amax, int64_t m, int64_t n, int64_t k, void* c,
+                        mx_dtype c_dtype, void* stream) {
+  g_err[0] = 0;
+  if (m < 0) return fail(MX_ESHAPE, "mx_gemm_nvfp4: need m >= 0");
+  return gemm_4bit_impl("mx_gemm_nvfp4", true, a, a_s, a_amax, b, b_s, b_amax, &m, 1, n, k, c, c_dtype, stream);
+}
+
+mx_status mx_grouped_gemm_nvfp4(const uint8_t* a, const uint8_t* a_s, const float* a_amax, const uint8_t* b,
+                                const uint8_t* b_s, const float* b_amax, const int64_t* group_sizes, int32_t groups,
+                                int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream) {
+  g_err[0] = 0;
+  return gemm_4bit_impl("mx_grouped_gemm_nvfp4", true, a, a_s, a_amax, b, b_s, b_amax, group_sizes, groups, n, k, c,
+                        c_dtype, stream);
 }
 
 }  // extern "C"

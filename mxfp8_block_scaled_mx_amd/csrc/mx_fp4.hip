@@ -11,10 +11,15 @@
 // (exact) and rounded by comparing against the midpoints of the E2M1 grid, 16
 // bytes of codes stored at once. Columnwise: see the columnwise kernel.
 // HBM-bound.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
 namespace mx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // E2M1 code of |t| (exact, already scaled), ties to the even code: the
 // midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 each either belong to the
@@ -200,6 +205,138 @@ hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, 
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4: E2M1 elements in blocks of 16 values, one E4M3 scale per block and
+// one fp32 scale per tensor (the NVFP4 recipe of "TransformerEngine-
+// accelerated Llama 3 training with native PyTorch training loop", Quantized
+// Training; the format's published form). With the tensor's amax, in fp32
+// arithmetic rounded to nearest:
+//   S   = 2688 / amax (448 * 6), 1 for amax = 0, at most 2^64;
+//   s_b = E4M3 code of (bmax / 6) * S, saturating;
+//   q   = E2M1 code of x * (S / E4M3(s_b)) (0, keeping the sign, when s_b = 0).
+// An element's value is E2M1(q) * E4M3(s_b) / S.
+
+__device__ __forceinline__ float nvfp4_tensor_scale(float amax) {
+  if (!(amax > 0.0f)) return 1.0f;
+  return fminf(2688.0f / amax, 18446744073709551616.0f);   // cap 2^64
+}
+
+// 16 values -> 8 code bytes (element 2i in the low nibble) and the E4M3
+// block-scale code.
+__device__ __forceinline__ uint32_t nvfp4_block(const float (&v)[16], float S, uint2& codes) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = umax(am, abs_bits(v[i]));
+  const float t = __uint_as_float(am) / 6.0f;
+  const float sb = t * S;
+  const uint32_t sc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sb, 448.0f), 0.0f, 0, false) & 0xFFu;
+  const float sv = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+  const float r = sv > 0.0f ? S / sv : 0.0f;
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    w0 |= e2m1_code(v[j] * r) << (4 * j);
+    w1 |= e2m1_code(v[8 + j] * r) << (4 * j);
+  }
+  codes = make_uint2(w0, w1);
+  return sc;
+}
+
+__global__ void nvfp4_amax_init_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
+
+// max |x| over the tensor: per-thread maxima of the magnitude bits (bf16 bits
+// shifted into fp32 position order the same way as the values), a wave
+// maximum, one atomic maximum per wave.
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* x, int64_t n8, uint32_t* amax_bits) {
+  uint32_t m = 0;
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const uint4 v = src[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = umax(m, (w[j] << 16) & 0x7FFFFFFFu);
+      m = umax(m, w[j] & 0x7FFF0000u);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, m);
+}
+
+// Rowwise and/or columnwise NVFP4 of bf16 x [rows, cols] from one LDS tile of
+// 128 rows x 64 columns: the rowwise copy takes 16-column blocks of each
+// row, the columnwise copy 16-row blocks of each column (the rowwise copy of
+// the transpose); both use the tensor scale of amax.
+constexpr int kNvTileRows = 128, kNvTileCols = 64;
+__global__ __launch_bounds__(256) void nvfp4_cast_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+                                                         const float* amax, uint8_t* q, uint8_t* s, uint8_t* qc,
+                                                         uint8_t* sc) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kNvTileRows][kNvTileCols + 2];
+  const int64_t n_ct = (cols + kNvTileCols - 1) / kNvTileCols;
+  const int64_t r0 = (int64_t)(blockIdx.x / n_ct) * kNvTileRows, c0 = (int64_t)(blockIdx.x % n_ct) * kNvTileCols;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int p = it * 256 + tid, rr = p >> 3, cp = (p & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + rr < rows && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
+    const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
+  }
+  __syncthreads();
+  const float S = nvfp4_tensor_scale(*amax);
+  if (q != nullptr) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int task = tid + 256 * u, rr = task >> 2, blk = task & 3;
+      const int64_t row = r0 + rr, col = c0 + 16 * blk;
+      if (row < rows && col < cols) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float((uint32_t)tile[rr][16 * blk + i] << 16);
+        uint2 codes;
+        const uint32_t code = nvfp4_block(v, S, codes);
+        *reinterpret_cast<uint2*>(q + row * (cols / 2) + col / 2) = codes;
+        s[row * (cols / 16) + col / 16] = (uint8_t)code;
+      }
+    }
+  }
+  if (qc != nullptr) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int task = tid + 256 * u, cc = task & 63, rb = task >> 6;
+      const int64_t col = c0 + cc, row = r0 + 16 * rb;
+      if (col < cols && row < rows) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float((uint32_t)tile[16 * rb + i][cc] << 16);
+        uint2 codes;
+        const uint32_t code = nvfp4_block(v, S, codes);
+        *reinterpret_cast<uint2*>(qc + col * (rows / 2) + row / 2) = codes;
+        sc[col * (rows / 16) + row / 16] = (uint8_t)code;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                                 uint8_t* s_col, float* amax, hipStream_t stream) {
+  uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, stream, ab);
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipGetLastError();
+  const int64_t grid = std::min<int64_t>((n8 + 255) / 256, 2048);
+  hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), n8, ab);
+  const int64_t tiles = ((rows + kNvTileRows - 1) / kNvTileRows) * ((cols + kNvTileCols - 1) / kNvTileCols);
+  hipLaunchKernelGGL(nvfp4_cast_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), rows, cols, amax, q, s, q_col, s_col);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // ScaledSwiGLU around the MXFP4 GEMMs of the MLP ("Efficient MoE training for
 // biological foundation models", Key technical approaches item 3, at the 4-bit
 // MX format): GEMM1 leaves H1 = [g | u] in fp32, the forward forms
@@ -374,11 +511,12 @@ static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4
 // that holds only 32 valid values gets scale code 0 for the invalid half on
 // both operands, so its products (at most 36 * 2^-254) add exact zeros
 // whatever codes lie past the group; C_g is fp32, stored or accumulated.
-template <bool GK, bool F32>
+template <bool GK, bool F32, bool NV>
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                                        const uint8_t* bs, Fp4Groups gr, Fp4KGroups kg, int64_t M,
                                                        int64_t N, int64_t K, int64_t n_tiles_n, void* c,
-                                                       int32_t accumulate) {
+                                                       int32_t accumulate,
+                                                       const float* a_amax, const float* b_amax) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
@@ -430,18 +568,22 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     bn0 = nt * TN;
   }
   const int64_t amv = min<int64_t>(TM, row_end - am0), bnv = min<int64_t>(TN, N - bn0);
-  const int64_t ldq = K / 2, lds = K / 32;    // bytes per row of codes, of scales
+  // bytes per row of codes, of scales (one per 32 values; NVFP4: per 16)
+  constexpr int kVPS = NV ? 16 : 32;           // values per scale
+  const int64_t ldq = K / 2, lds = K / kVPS;
   // group-M: B_g is rows [g N, g N + N) of b; group-K: one B, the group's k range
   const int64_t brow0 = GK ? bn0 : grp * N + bn0;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + am0 * ldq + kbeg / 2, (amv - 1) * ldq + klen / 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + brow0 * ldq + kbeg / 2, (bnv - 1) * ldq + klen / 2);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds + kbeg / 32, (amv - 1) * lds + klen / 32);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + brow0 * lds + kbeg / 32, (bnv - 1) * lds + klen / 32);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds + kbeg / kVPS, (amv - 1) * lds + klen / kVPS);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + brow0 * lds + kbeg / kVPS, (bnv - 1) * lds + klen / kVPS);
   const int ksteps = (int)((klen + 63) / 64), ktiles = (ksteps + 3) / 4;
   // a row's 8 scales of a k-tile: one aligned 8-byte load. The k range must
   // also be whole k-tiles: the last row's load would otherwise reach past
   // the resource's extent and come back as zero scales.
-  const bool sc_dword = (lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0;
+  // (NVFP4: K is a multiple of 128, so a lane's 8 scales of a k-tile are
+  // always one aligned 8-byte piece)
+  const bool sc_dword = NV || ((lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0);
 
   // global -> LDS by buffer DMA, 1 KB (8 rows) per instruction: lane L
   // fills chunk L % 8 of row L / 8 of the block with global chunk
@@ -463,8 +605,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
                                                (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
   };
-  // scales of k-tile t for this lane's rows: blocks 8 t .. 8 t + 7
+  // scales of k-tile t for this lane's rows: blocks 8 t .. 8 t + 7 (NVFP4:
+  // blocks 16 t + 8 h .. + 7, those of the lane's half of the k-tile)
   u32x2 sca[SM], scb[SN];
+  const uint32_t sc_k = NV ? 8 * h : 0;
   auto scale_pair = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off) __attribute__((always_inline)) -> u32x2 {
     if (sc_dword) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     u32x2 v;
@@ -478,9 +622,11 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   };
   auto load_scales = [&](int t, u32x2 (&xa)[SM], u32x2 (&xb)[SN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i) xa[i] = scale_pair(rsa, (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + 8 * t));
+    for (int i = 0; i < SM; ++i)
+      xa[i] = scale_pair(rsa, (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + (NV ? 16 : 8) * t + sc_k));
 #pragma unroll
-    for (int j = 0; j < SN; ++j) xb[j] = scale_pair(rsb, (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + 8 * t));
+    for (int j = 0; j < SN; ++j)
+      xb[j] = scale_pair(rsb, (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k));
   };
   auto frag = [&](const uint8_t* base, int r, int s) __attribute__((always_inline)) -> v8i {
     const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ (r & 7)) << 4));
@@ -516,6 +662,62 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     }
     const uint8_t* A = sA[buf] + (TM / 2 * wm) * KT;
     const uint8_t* B = sB[buf] + (TN / 2 * wn) * KT;
+    if constexpr (NV) {
+      // NVFP4 on the bf16 MFMA (32 x 32 x 16): the lanes of half h take the
+      // values [128 h, 128 h + 128) of the k-tile, read as chunks 4 h .. 4 h + 3
+      // of their rows, so step 4 q + u pairs values 32 q + 8 u .. + 7 (h = 0)
+      // with 128 + 32 q + 8 u .. + 7 (h = 1) -- the same permutation of k for
+      // A and B, and each lane's 8 values lie in one 16-value block. Each
+      // lane dequantizes its 8 values exactly into bf16 (E2M1 times an E4M3
+      // scale has at most 6 significant bits): a scale-1 E2M1 -> fp32
+      // conversion, an fp32 multiply by the block scale, and the two upper
+      // halves packed by a byte permute. A half past K (K % 256 == 128 in the
+      // last k-tile) gets scale 0.
+      const bool half_ok = (int64_t)(256 * t + 128 * h) < klen;
+      auto chunk = [&](const uint8_t* base, int r, int c) __attribute__((always_inline)) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(base + r * KT + ((c ^ (r & 7)) << 4));
+      };
+      auto dequant = [&](uint32_t w, float sv) __attribute__((always_inline)) -> bf16x8 {
+        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        u32x4 o;
+        o.x = __builtin_amdgcn_perm(__float_as_uint(f0.y * sv), __float_as_uint(f0.x * sv), 0x07060302u);
+        o.y = __builtin_amdgcn_perm(__float_as_uint(f1.y * sv), __float_as_uint(f1.x * sv), 0x07060302u);
+        o.z = __builtin_amdgcn_perm(__float_as_uint(f2.y * sv), __float_as_uint(f2.x * sv), 0x07060302u);
+        o.w = __builtin_amdgcn_perm(__float_as_uint(f3.y * sv), __float_as_uint(f3.x * sv), 0x07060302u);
+        return __builtin_bit_cast(bf16x8, o);
+      };
+      static_for<0, 4>([&](auto qd_c) __attribute__((always_inline)) {
+        constexpr int qd = decltype(qd_c)::value;
+        u32x4 cb[SN], ca[SM];
+#pragma unroll
+        for (int j = 0; j < SN; ++j) cb[j] = chunk(B, 32 * j + l32, qd + 4 * h);
+#pragma unroll
+        for (int i = 0; i < SM; ++i) ca[i] = chunk(A, 32 * i + l32, qd + 4 * h);
+        static_for<0, 4>([&](auto u_c) __attribute__((always_inline)) {
+          constexpr int u = decltype(u_c)::value;
+          constexpr int blk = 2 * qd + u / 2;             // the lane's block (byte of its scale pair)
+          bf16x8 fb[SN];
+#pragma unroll
+          for (int j = 0; j < SN; ++j) {
+            const uint32_t sw = blk < 4 ? scb[j].x : scb[j].y;
+            const float sv = half_ok ? __builtin_amdgcn_cvt_f32_fp8((int)sw, blk & 3) : 0.0f;
+            fb[j] = dequant(cb[j][u], sv);
+          }
+#pragma unroll
+          for (int i = 0; i < SM; ++i) {
+            const uint32_t sw = blk < 4 ? sca[i].x : sca[i].y;
+            const float sv = half_ok ? __builtin_amdgcn_cvt_f32_fp8((int)sw, blk & 3) : 0.0f;
+            const bf16x8 fa = dequant(ca[i][u], sv);
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa, acc[j][i], 0, 0, 0);
+          }
+        });
+      });
+    } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (4 * t + s < ksteps) {
@@ -537,6 +739,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
         }
       }
     }
+    }
     if (more) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's DMA and scales landed
 #pragma unroll
@@ -548,8 +751,12 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   }
 
   // lane l holds row 32 i + l32 and, per MFMA tile, columns 8 g + 4 h .. +3
-  // (g = 0..3) in accumulator elements 4 g .. 4 g + 3
+  // (g = 0..3) in accumulator elements 4 g .. 4 g + 3. NVFP4: every product
+  // still carries 1 / S of each operand's tensor (alpha, one rounding).
   const int64_t m0 = am0 + TM / 2 * wm, n0 = bn0 + TN / 2 * wn;
+  float alpha = 1.0f;
+  if constexpr (NV)
+    alpha = (float)(1.0 / ((double)nvfp4_tensor_scale(*a_amax) * (double)nvfp4_tensor_scale(b_amax[grp])));
   if (F32 && (N & 31) == 0 && N <= (1 << 22)) {
     // fp32 C leaves through the wave's 32 KB LDS slice (the operand stages
     // are free after the k-loop's last barrier) so that every store covers
@@ -589,10 +796,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           u32x4 v;
-          v.x = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 0]));
-          v.y = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 1]));
-          v.z = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 2]));
-          v.w = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 3]));
+          v.x = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 0]) * alpha);
+          v.y = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 1]) * alpha);
+          v.z = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 2]) * alpha);
+          v.w = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 3]) * alpha);
           const int ch = 2 * g + h;
           *reinterpret_cast<u32x4*>(st + j * 4096 + l32 * 128 + ((ch ^ (l32 & 7)) << 4)) = v;
         }
@@ -628,8 +835,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       for (int g = 0; g < 4; ++g) {
         const int64_t col = n0 + 32 * j + 8 * g + 4 * h;
         // through a VALU move, so the accumulators stay AGPR-only operands
-        const float x0 = vgpr_hop(acc[j][i][4 * g]), x1 = vgpr_hop(acc[j][i][4 * g + 1]);
-        const float x2 = vgpr_hop(acc[j][i][4 * g + 2]), x3 = vgpr_hop(acc[j][i][4 * g + 3]);
+        const float x0 = vgpr_hop(acc[j][i][4 * g]) * alpha, x1 = vgpr_hop(acc[j][i][4 * g + 1]) * alpha;
+        const float x2 = vgpr_hop(acc[j][i][4 * g + 2]) * alpha, x3 = vgpr_hop(acc[j][i][4 * g + 3]) * alpha;
         if constexpr (F32) {
           float* cp = reinterpret_cast<float*>(c) + (GK ? (int64_t)grp * M * N : 0) + row * N + col;
           if (vec && col + 3 < N) {
@@ -667,11 +874,26 @@ hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b
   if (tm * tn == 0) return hipSuccess;
   Fp4KGroups kg{};
   if (c_f32)
-    hipLaunchKernelGGL((gemm_fp4_kernel<false, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs,
-                       gr, kg, (int64_t)0, N, K, tn, c, 0);
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, true, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((gemm_fp4_kernel<false, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as, b, bs,
-                       gr, kg, (int64_t)0, N, K, tn, c, 0);
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, false, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a_amax, const uint8_t* b,
+                             const uint8_t* bs, const float* b_amax, const Fp4Groups& gr, int64_t N, int64_t K,
+                             void* c, int32_t c_f32, hipStream_t stream) {
+  const int64_t tm = gr.tile0[gr.n], tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
+  if (tm * tn == 0) return hipSuccess;
+  Fp4KGroups kg{};
+  if (c_f32)
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, true, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax);
+  else
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, false, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax);
   return hipGetLastError();
 }
 
@@ -682,8 +904,8 @@ hipError_t launch_gemm_fp4_group_k(const uint8_t* a, const uint8_t* as, const ui
   const int64_t tiles = (int64_t)kg.n * tm * tn;
   if (tiles == 0) return hipSuccess;
   Fp4Groups gr{};
-  hipLaunchKernelGGL((gemm_fp4_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs, gr, kg,
-                     M, N, kg.k0[kg.n], tn, c, accumulate);
+  hipLaunchKernelGGL((gemm_fp4_kernel<true, true, false>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs,
+                     gr, kg, M, N, kg.k0[kg.n], tn, c, accumulate, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -223,6 +223,17 @@ struct Fp4ColGroups {
 hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
                                        uint8_t* q_col, uint8_t* s_col, uint8_t* q_row, uint8_t* s_row,
                                        hipStream_t stream);
+// NVFP4 (mx_fp4.hip): the cast writes the tensor amax to *amax (device fp32)
+// and rowwise codes [rows, cols/2] + E4M3 scales [rows, cols/16] and/or the
+// columnwise pair [cols, rows/2] + [cols, rows/16]; cols % 16 == 0 (rows % 16
+// for the columnwise copy). The grouped GEMM is launch_gemm_fp4's with NVFP4
+// operands (K % 128 == 0), the tensor scale of A from *a_amax and of group g's
+// weight from b_amax[g].
+hipError_t launch_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
+                                 uint8_t* s_col, float* amax, hipStream_t stream);
+hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a_amax, const uint8_t* b,
+                             const uint8_t* bs, const float* b_amax, const Fp4Groups& gr, int64_t N, int64_t K,
+                             void* c, int32_t c_f32, hipStream_t stream);
 // ScaledSwiGLU of the MXFP4 MLP (mx_fp4.hip). Forward: H1 fp32 [R, 2F] ->
 // H1 bf16 (h1, or null), A fp32 (a32, or null) and A's rowwise MXFP4 copy
 // [R, F/2] + [R, F/32]. Backward: dA fp32 [R, F], H1 bf16 -> dH1 fp32 (dh1f,

@@ -809,11 +809,12 @@ def nvfp4_tensor_scale(amax) -> np.float32:
     return np.float32(min(q, NVFP4_SCALE_CAP))
 
 
-def quantize_rowwise_nvfp4(x):
+def quantize_rowwise_nvfp4(x, amax=None):
     """Rowwise NVFP4 of [rows, cols] (cols % 16 == 0; values exact in
     float32) -> (packed codes [rows, cols/2] uint8, E4M3 block-scale codes
     [rows, cols/16] uint8, amax float32). The steps of R18 in order, each a
-    float32 operation."""
+    float32 operation. amax: the whole tensor's amax when x holds only some
+    of its rows (default: x's own)."""
     x = np.asarray(x, dtype=np.float64)
     rows, cols = x.shape
     if cols % NV_BLOCK:
@@ -823,7 +824,9 @@ def quantize_rowwise_nvfp4(x):
     xf = x.astype(np.float32)
     if not np.array_equal(xf.astype(np.float64), x):
         raise ValueError("inputs must be exact float32 values")
-    amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0.0)
+    if amax is None:
+        amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0.0)
+    amax = np.float32(amax)
     S = nvfp4_tensor_scale(amax)
     v = xf.reshape(rows, cols // NV_BLOCK, NV_BLOCK)
     bmax = np.max(np.abs(v), axis=-1)

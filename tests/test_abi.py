@@ -439,3 +439,24 @@ def test_fp4_mlp_bindings_check_state_and_shapes():
         mx.grouped_mlp_bwd_fp4(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32]))     # an MXFP8 state
     with pytest.raises(ValueError, match="MXFP8"):
         mx.grouped_mlp_bwd(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32], fmt="mxfp4"))
+
+
+def test_nvfp4_argument_errors(L):
+    amax = FAKE
+    def cast(rows=32, cols=64, q=FAKE, qc=None, am=amax, x=FAKE):
+        return L.mx_quantize_nvfp4(x, rows, cols, q, FAKE if q is not None else None, qc,
+                                   FAKE if qc is not None else None, am, None)
+    assert cast(cols=40) == ESHAPE
+    assert cast(rows=24, qc=FAKE) == ESHAPE                # columnwise copy needs rows % 16 == 0
+    assert cast(q=None) == EINVAL                           # no output
+    assert cast(am=None) == EINVAL
+    assert cast(x=ctypes.c_void_p(0x100008)) == EALIGN
+    assert cast(am=ctypes.c_void_p(0x100002)) == EALIGN
+    def gemm(k=256, am=amax, bs=FAKE, n=64):
+        return L.mx_gemm_nvfp4(FAKE, FAKE, am, FAKE, bs, amax, 64, n, k, FAKE, 0, None)
+    assert gemm(k=192) == ESHAPE                            # k must be a multiple of 128
+    assert gemm(am=None) == EINVAL
+    assert gemm(bs=ctypes.c_void_p(0x100004)) == EALIGN    # scales 8-byte aligned
+    assert gemm(n=0) == OK                                  # nothing to compute
+    assert L.mx_grouped_gemm_nvfp4(FAKE, FAKE, amax, FAKE, FAKE, amax, mx._i64_array([1]), 0, 64, 256, FAKE, 0,
+                                   None) == EINVAL
