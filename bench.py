@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP8 grouped-MLP TFLOP/s (fwd+bwd) and % of MXFP8 MFMA peak; quantize GB/s"
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 / MXFP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 / MXFP4 MFMA
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 NOMINAL_SCLK_MHZ = 2400.0         # the clock the MFMA peak is quoted at
@@ -391,6 +392,10 @@ def main():
             f"({g4['roofline']['frac']:.3f} of the FP4 peak); grouped over the step's split_sizes "
             f"{g4['grouped']['ms']:.3f} ms -> {g4['grouped']['tflops']:.0f} TFLOP/s; weight gradient "
             f"{g4['wgrad']['ms']:.3f} ms -> {g4['wgrad']['tflops']:.0f} TFLOP/s")
+        nv = g4["nvfp4"]
+        log(f"NVFP4 cast {nv['cast']['gbps']:.0f} GB/s; GEMM {nv['gemm']['ms']:.3f} ms -> "
+            f"{nv['gemm']['tflops']:.0f} TFLOP/s ({nv['gemm']['frac_bf16_peak']:.3f} of the bf16 peak); grouped "
+            f"{nv['grouped']['ms']:.3f} ms -> {nv['grouped']['tflops']:.0f} TFLOP/s")
 
     if not args.no_moe:
         out["dispatch_combine"] = measure_moe(mx, torch, np, wlmod, dev)
@@ -769,10 +774,57 @@ def measure_gemm_fp4(mx, torch, dev, split, iters=10, m=16384, n=28672, k=4096):
     tfw = 2.0 * mg * n * k / (msw * 1e-3) / 1e12
     wgrad = {"workload": f"grouped_gemm_fp4_wgrad_{n}x{k}x{mg}_{G}experts", "ms": round(msw, 4),
              "tflops": round(tfw, 1), "frac_fp4_peak": round(tfw / PEAK_FP4_TFLOPS, 4)}
+    del wq, ws, xq, xs, cw
+    nv = measure_nvfp4(mx, torch, dev, split, g, iters, m, n, k)
     return {"workload": f"gemm_fp4_{m}x{n}x{k}", "ms": round(ms, 4), "tflops": round(tflops, 1),
-            "grouped": grouped, "wgrad": wgrad,
+            "grouped": grouped, "wgrad": wgrad, "nvfp4": nv,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_FP4_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}}
+
+
+def measure_nvfp4(mx, torch, dev, split, g, iters, m, n, k):
+    """NVFP4 on the same shapes: the cast of a 16384 x 4096 bf16 tensor (amax
+    reduction + both layouts; bytes = 2 read + 2 x (0.5 + 1/16) written per
+    value, plus the amax pass's 2 read), mx_gemm_nvfp4 (16384 x 28672 x 4096)
+    and mx_grouped_gemm_nvfp4 over the step's split_sizes. The GEMMs run on
+    the bf16 MFMA (gfx950 has no scaled MFMA for E4M3 block scales), so they
+    are priced at the bf16 peak."""
+    x = (torch.randn((m, k), generator=g, device=dev, dtype=torch.float32) * 3).to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms_cast = timed(lambda: mx.mx_quantize_nvfp4(x, colwise=True))
+    cast_bytes = m * k * (2 + 2 + 2 * (0.5 + 1.0 / 16))
+    aq, as_, aa = mx.mx_quantize_nvfp4(x)
+    bq = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    bs = torch.randint(0x28, 0x48, (n, k // 16), dtype=torch.uint8, device=dev, generator=g)
+    ba = torch.tensor([1.5], dtype=torch.float32, device=dev)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: mx.mx_gemm_nvfp4(aq, as_, aa, bq, bs, ba, out=c))
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    G, mg = len(split), int(sum(split))
+    bgq = bq.unsqueeze(0).expand(G, n, k // 2).contiguous()
+    bgs = bs.unsqueeze(0).expand(G, n, k // 16).contiguous()
+    bga = torch.full((G,), 1.5, dtype=torch.float32, device=dev)
+    cg = torch.empty((mg, n), dtype=torch.bfloat16, device=dev)
+    msg = timed(lambda: mx.mx_grouped_gemm_nvfp4(aq[:mg], as_[:mg], aa, bgq, bgs, bga, split, out=cg))
+    tfg = 2.0 * mg * n * k / (msg * 1e-3) / 1e12
+    return {"cast": {"workload": f"nvfp4_cast_{m}x{k}_both_layouts", "ms": round(ms_cast, 4),
+                     "gbps": round(cast_bytes / (ms_cast * 1e-3) / 1e9, 1)},
+            "gemm": {"workload": f"gemm_nvfp4_{m}x{n}x{k}", "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "grouped": {"workload": f"grouped_gemm_nvfp4_{mg}x{n}x{k}_{G}experts", "ms": round(msg, 4),
+                        "tflops": round(tfg, 1), "frac_bf16_peak": round(tfg / PEAK_BF16_TFLOPS, 4)}}
 
 
 def measure_quantize(mx, torch, np, wlmod, dev, iters=50, copies=4):
