@@ -244,23 +244,37 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float (&v)[16], float S, u
 __global__ void nvfp4_amax_init_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
 
 // max |x| over the tensor: per-thread maxima of the magnitude bits (bf16 bits
-// shifted into fp32 position order the same way as the values), a wave
-// maximum, one atomic maximum per wave.
+// shifted into fp32 position order the same way as the values), wave and
+// workgroup maxima, one atomic maximum per workgroup.
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* x, int64_t n8, uint32_t* amax_bits) {
   uint32_t m = 0;
   const uint4* src = reinterpret_cast<const uint4*>(x);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-    const uint4 v = src[i];
+  auto take = [&](const uint4& v) __attribute__((always_inline)) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       m = umax(m, (w[j] << 16) & 0x7FFFFFFFu);
       m = umax(m, w[j] & 0x7FFF0000u);
     }
+  };
+  // four independent 16-byte loads in flight per thread, then the remainder
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    take(v0);
+    take(v1);
+    take(v2);
+    take(v3);
   }
+  for (; i < n8; i += stride) take(src[i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, m);
+  // one atomic per workgroup: atomics on one address serialize
+  __shared__ uint32_t wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax_bits, umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3])));
 }
 
 // Rowwise and/or columnwise NVFP4 of bf16 x [rows, cols] from one LDS tile of
@@ -327,7 +341,7 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint
   hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, stream, ab);
   const int64_t n8 = rows * cols / 8;
   if (n8 == 0) return hipGetLastError();
-  const int64_t grid = std::min<int64_t>((n8 + 255) / 256, 2048);
+  const int64_t grid = std::min<int64_t>((n8 + 255) / 256, 512);
   hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(x), n8, ab);
   const int64_t tiles = ((rows + kNvTileRows - 1) / kNvTileRows) * ((cols + kNvTileCols - 1) / kNvTileCols);
