@@ -18,8 +18,8 @@
 
 namespace mx {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // E2M1 code of |t| (exact, already scaled), ties to the even code: the
 // midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 each either belong to the
@@ -677,31 +677,33 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     const uint8_t* A = sA[buf] + (TM / 2 * wm) * KT;
     const uint8_t* B = sB[buf] + (TN / 2 * wn) * KT;
     if constexpr (NV) {
-      // NVFP4 on the bf16 MFMA (32 x 32 x 16): the lanes of half h take the
+      // NVFP4 on the fp16 MFMA (32 x 32 x 16): the lanes of half h take the
       // values [128 h, 128 h + 128) of the k-tile, read as chunks 4 h .. 4 h + 3
       // of their rows, so step 4 q + u pairs values 32 q + 8 u .. + 7 (h = 0)
       // with 128 + 32 q + 8 u .. + 7 (h = 1) -- the same permutation of k for
       // A and B, and each lane's 8 values lie in one 16-value block. Each
-      // lane dequantizes its 8 values exactly into bf16 (E2M1 times an E4M3
-      // scale has at most 6 significant bits): a scale-1 E2M1 -> fp32
-      // conversion, an fp32 multiply by the block scale, and the two upper
-      // halves packed by a byte permute. A half past K (K % 256 == 128 in the
-      // last k-tile) gets scale 0.
+      // lane dequantizes its 8 values exactly into fp16 (E2M1 times an E4M3
+      // scale has at most 6 significant bits). A half past K (K % 256 == 128
+      // in the last k-tile) gets scale 0.
       const bool half_ok = (int64_t)(256 * t + 128 * h) < klen;
       auto chunk = [&](const uint8_t* base, int r, int c) __attribute__((always_inline)) -> u32x4 {
         return *reinterpret_cast<const u32x4*>(base + r * KT + ((c ^ (r & 7)) << 4));
       };
-      auto dequant = [&](uint32_t w, float sv) __attribute__((always_inline)) -> bf16x8 {
-        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+      auto dequant = [&](uint32_t w, float sv) __attribute__((always_inline)) -> f16x8 {
+        // sv = 2^E * m with m in [1, 2) holding at most 3 fraction bits: the
+        // scaled conversion applies 2^E exactly, one packed fp16 multiply per
+        // pair applies m (exact: at most 6 significant bits, within fp16's
+        // normal range 2^-10 .. 2688)
+        const uint32_t sb = __float_as_uint(sv);
+        const float pe = __uint_as_float(sb & 0x7F800000u);
+        const uint32_t mb = 0x3C00u | ((sb >> 13) & 0x3FFu);
+        const f16x2 mh = __builtin_bit_cast(f16x2, mb | (mb << 16));
         u32x4 o;
-        o.x = __builtin_amdgcn_perm(__float_as_uint(f0.y * sv), __float_as_uint(f0.x * sv), 0x07060302u);
-        o.y = __builtin_amdgcn_perm(__float_as_uint(f1.y * sv), __float_as_uint(f1.x * sv), 0x07060302u);
-        o.z = __builtin_amdgcn_perm(__float_as_uint(f2.y * sv), __float_as_uint(f2.x * sv), 0x07060302u);
-        o.w = __builtin_amdgcn_perm(__float_as_uint(f3.y * sv), __float_as_uint(f3.x * sv), 0x07060302u);
-        return __builtin_bit_cast(bf16x8, o);
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pe, 0) * mh);
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pe, 1) * mh);
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pe, 2) * mh);
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pe, 3) * mh);
+        return __builtin_bit_cast(f16x8, o);
       };
       static_for<0, 4>([&](auto qd_c) __attribute__((always_inline)) {
         constexpr int qd = decltype(qd_c)::value;
@@ -713,7 +715,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
         static_for<0, 4>([&](auto u_c) __attribute__((always_inline)) {
           constexpr int u = decltype(u_c)::value;
           constexpr int blk = 2 * qd + u / 2;             // the lane's block (byte of its scale pair)
-          bf16x8 fb[SN];
+          f16x8 fb[SN];
 #pragma unroll
           for (int j = 0; j < SN; ++j) {
             const uint32_t sw = blk < 4 ? scb[j].x : scb[j].y;
@@ -724,10 +726,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
           for (int i = 0; i < SM; ++i) {
             const uint32_t sw = blk < 4 ? sca[i].x : sca[i].y;
             const float sv = half_ok ? __builtin_amdgcn_cvt_f32_fp8((int)sw, blk & 3) : 0.0f;
-            const bf16x8 fa = dequant(ca[i][u], sv);
+            const f16x8 fa = dequant(ca[i][u], sv);
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa, acc[j][i], 0, 0, 0);
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa, acc[j][i], 0, 0, 0);
           }
         });
       });
