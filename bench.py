@@ -787,8 +787,8 @@ def measure_nvfp4(mx, torch, dev, split, g, iters, m, n, k):
     reduction + both layouts; bytes = 2 read + 2 x (0.5 + 1/16) written per
     value, plus the amax pass's 2 read), mx_gemm_nvfp4 (16384 x 28672 x 4096)
     and mx_grouped_gemm_nvfp4 over the step's split_sizes. The GEMMs run on
-    the bf16 MFMA (gfx950 has no scaled MFMA for E4M3 block scales), so they
-    are priced at the bf16 peak."""
+    the fp16 MFMA (gfx950 has no scaled MFMA for E4M3 block scales), so they
+    are priced at the 16-bit (bf16 / fp16) peak."""
     x = (torch.randn((m, k), generator=g, device=dev, dtype=torch.float32) * 3).to(torch.bfloat16)
 
     def timed(fn):

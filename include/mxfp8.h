@@ -431,8 +431,8 @@ MX_API mx_status mx_grouped_gemm_fp4(const uint8_t* a, const uint8_t* a_s, const
  * rows of A times its weight B_g^T) with NVFP4 operands in the rowwise layout
  * of mx_quantize_nvfp4, A's tensor amax at a_amax and B_g's at b_amax[g]
  * (device fp32; one per group). gfx950's scaled MFMA takes power-of-two
- * (E8M0) scales per 32 values only, so NVFP4 runs on the bf16 MFMA: every
- * element times its E4M3 block scale is exact in bf16 and is formed in
+ * (E8M0) scales per 32 values only, so NVFP4 runs on the fp16 MFMA: every
+ * element times its E4M3 block scale is exact in fp16 and is formed in
  * registers; sums are fp32; the product of the two 1/S factors is applied
  * once to each result (one fp32 rounding). k must be a positive multiple of
  * 128 (at most 2^24); scales 8-byte aligned; other requirements, outputs and
