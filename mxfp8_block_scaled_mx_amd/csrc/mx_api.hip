@@ -1449,6 +1449,11 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
   L->kg.k0[E] = p0;
   L->P = p0;
   if (p0 > ((int64_t)1 << 24)) return fail(MX_EUNSUPPORTED, "%s: padded rows above 2^24", who);
+  // launch grids: columnwise-cast tiles (widest input 2F), SwiGLU blocks, GEMM tiles
+  const int64_t cast_tiles = t0 * cdiv(2 * L->F, 64), swiglu_blocks = cdiv(L->R * (L->F / 32), 256);
+  const int64_t gemm_tiles = (cdiv(L->R, mx::kFp4GemmTileM) + L->E) * cdiv(2 * L->F, mx::kFp4GemmTileN);
+  if (cast_tiles > kI32Max || swiglu_blocks > kI32Max || gemm_tiles > kI32Max)
+    return fail(MX_EUNSUPPORTED, "%s: launch grid above 2^31", who);
   const int64_t P = L->P;
   size_t c = 0;
   L->xq = take(c, R * H / 2);

@@ -460,3 +460,12 @@ def test_nvfp4_argument_errors(L):
     assert gemm(n=0) == OK                                  # nothing to compute
     assert L.mx_grouped_gemm_nvfp4(FAKE, FAKE, amax, FAKE, FAKE, amax, mx._i64_array([1]), 0, 64, 256, FAKE, 0,
                                    None) == EINVAL
+
+
+def test_fp4_mlp_rejects_grids_past_32_bits(L):
+    # 2^24 rows of one expert and F = 2^20: every dimension and the padded row
+    # count are in range, but the columnwise cast of the [R, 2F] gradient takes
+    # 2^17 row tiles x 2^15 column tiles = 2^32 workgroups
+    E, R, H, F = 1, 1 << 24, 4096, 1 << 20
+    split = mx._i64_array([R // E] * E)
+    assert L.grouped_mlp_fp4_sizes(ctypes.byref(_dims(E, R, H, F)), split, None, None, None) == EUNSUPPORTED
