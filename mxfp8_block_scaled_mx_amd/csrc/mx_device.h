@@ -129,8 +129,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 [[maybe_unused]] constexpr int kWaitVmcnt0 = 0x0F70;
 [[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
 
-// Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps
-// register-array indices constant however large the body is.
 // Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8). Tile
 // ids are handed out in rounds of 8 x kXcdChunk: in each round XCD x takes
 // kXcdChunk consecutive ids, so the tiles running together on one XCD are
@@ -147,6 +145,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (local / kXcdChunk) * round + xcd * kXcdChunk + local % kXcdChunk;
 }
 
+// Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps
+// register-array indices constant however large the body is.
 template <int I, int N, typename Fn>
 __device__ __forceinline__ void static_for(Fn&& fn) {
   if constexpr (I < N) {
