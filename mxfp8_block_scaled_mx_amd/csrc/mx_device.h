@@ -130,19 +130,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 [[maybe_unused]] constexpr int kWaitVmcnt1 = 0x0F71;
 
 // Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8). Tile
-// ids are handed out in rounds of 8 x kXcdChunk: in each round XCD x takes
-// kXcdChunk consecutive ids, so the tiles running together on one XCD are
+// ids are handed out in rounds of 8 x CHUNK: in each round XCD x takes
+// CHUNK consecutive ids, so the tiles running together on one XCD are
 // raster neighbours (they share A and B rows in that XCD's L2) while all XCDs
 // walk the id space at the same pace, which keeps tiles of unequal cost
 // (group-K slots sorted by size) balanced across XCDs. Blocks of the last,
 // partial round keep their own id.
 constexpr int kXcdChunk = 32;
+template <int CHUNK = kXcdChunk>
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
-  constexpr int round = 8 * kXcdChunk;
+  constexpr int round = 8 * CHUNK;
   const int full = total / round * round;
   if (bid >= full) return bid;
   const int xcd = bid & 7, local = bid >> 3;
-  return (local / kXcdChunk) * round + xcd * kXcdChunk + local % kXcdChunk;
+  return (local / CHUNK) * round + xcd * CHUNK + local % CHUNK;
 }
 
 // Compile-time loop: fn(std::integral_constant<int, i>) for i in [I, N). Keeps

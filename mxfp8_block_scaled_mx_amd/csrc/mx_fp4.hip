@@ -7,10 +7,9 @@
 // nibble.
 //
 // Rowwise: one thread per 32-value block: four 16-byte loads, a local amax,
-// the scale code from the amax exponent bits, the elements scaled by 2^-e
-// (exact) and rounded by comparing against the midpoints of the E2M1 grid, 16
-// bytes of codes stored at once. Columnwise: see the columnwise kernel.
-// HBM-bound.
+// the scale code from the amax exponent bits, the elements divided by 2^e and
+// rounded by the hardware's scaled E2M1 convert, 16 bytes of codes stored at
+// once. Columnwise: see the columnwise kernel. HBM-bound.
 #include <algorithm>
 
 #include "mx_device.h"
@@ -20,14 +19,35 @@ namespace mx {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// E2M1 code of |t| (exact, already scaled), ties to the even code: the
-// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 each either belong to the
-// lower code (its code is even) or the upper one.
-__device__ __forceinline__ uint32_t e2m1_code(float t) {
-  const float a = fabsf(t);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(t) >> 28) & 8u);
+// E2M1 codes of 8 values, value i in nibble i of the word. The scaled convert
+// (v_cvt_scalef32_pk_fp4_*) divides each value by 2^E, E the exponent field
+// of `scale` read as an E8M0 code (so code 0 means 2^-127), rounds to the
+// nearest E2M1 value with ties to the even code (the midpoints 0.25, 0.75,
+// 1.25, 1.75, 2.5, 3.5 and 5 go to the neighbour whose code is even),
+// saturates at 6 and keeps the sign of zero. Checked on hardware against that
+// rule written out: every bf16 value under scale codes 0..253, every tie point
+// and its neighbouring fp32 values at scale 1, signed zeros and values whose
+// quotient is an fp32 subnormal, both operand positions; NaN inputs differ
+// and lie outside the casts' contract.
+__device__ __forceinline__ float e8m0_as_scale(uint32_t code) { return __uint_as_float(code << 23); }
+__device__ __forceinline__ uint32_t e2m1x8(const float* v, float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
+}
+// the same for 8 bf16 values as loaded (value 2i in the low half of dword i)
+__device__ __forceinline__ uint32_t e2m1x8_bf16(const uint4& raw, float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, raw.x), scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, raw.y), scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, raw.z), scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, raw.w), scale, 3);
+  return w;
 }
 
 // One 32-value MXFP4 block: scale code (floor(log2 amax) - 2 + 127 = biased
@@ -39,16 +59,8 @@ __device__ __forceinline__ uint32_t fp4_block(const float (&v)[32], uint4& codes
   for (int i = 0; i < 32; ++i) am = umax(am, abs_bits(v[i]));
   const uint32_t eb = am >> 23;
   const uint32_t sc = eb > 2u ? eb - 2u : 0u;
-  const float inv = inv_scale_from_code(sc);
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
-    w[i] = word;
-  }
-  codes = make_uint4(w[0], w[1], w[2], w[3]);
+  const float scale = e8m0_as_scale(sc);
+  codes = make_uint4(e2m1x8(&v[0], scale), e2m1x8(&v[8], scale), e2m1x8(&v[16], scale), e2m1x8(&v[24], scale));
   return sc;
 }
 
@@ -76,91 +88,188 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
   s[r * nb + b] = (uint8_t)sc;
 }
 
-// Columnwise MXFP4 (= rowwise of the transpose): codes [cols, rows/2] and
-// scales [cols, rows/32]; rows % 32 == 0. A workgroup stages a 128-row x
-// 64-column tile in LDS (rows loaded as coalesced 16-byte pieces); thread t
-// then takes column t % 64 and the 32-row block t / 64, reduces the block's
-// amax locally and stores its 16 code bytes as one piece of the column's run.
-// With q_row given, the same tile also yields the rowwise copy (thread t takes
-// row t / 2, 32-column block t % 2), so both layouts cost one read of x.
-// Grouped (per-expert) columnwise layout: row tiles restart at each group's
-// first row, rows past the group's end read as zeros, and group g's padded
-// rows land at columns [pcol0[g], + pad32(m_g)) of the [cols, sum P] result.
-// One group of all rows is the plain columnwise cast. T is the input type:
-// bf16 bits (uint16_t) or fp32 (the fp32 intermediates of the MXFP4 MLP).
-constexpr int kFp4ColTileRows = 128, kFp4ColTileCols = 64;
+// Columnwise MXFP4 (= rowwise of the transpose): codes [cols, ldp/2] and
+// scales [cols, ldp/32]; with q_row given, the rowwise pair [rows, cols/2] +
+// [rows, cols/32] from the same read of x. Grouped (per-expert) columnwise
+// layout: row tiles restart at each group's first row, rows past the group's
+// end read as zeros, and group g's padded rows land at columns
+// [pcol0[g], + pad32(m_g)) of the result. One group of all rows is the plain
+// columnwise cast. T is the input type: bf16 bits (uint16_t) or fp32 (the
+// fp32 intermediates of the MXFP4 MLP).
+//
+// Tile: 128 rows x 256 bytes (128 bf16 or 64 fp32 columns), 256 threads.
+// Thread t issues its 8 row pieces (row 16 p + t / 16, 16-byte chunk t % 16)
+// first; the rowwise copy comes from registers (the 4 or 8 threads of a
+// 32-block reduce its amax with xor shuffles; one scale word per row and
+// tile). The tile is staged in LDS unchanged; thread t then reads 32 dwords
+// down rows 32 (t / 64) .. + 31 (one or two columns), forms each column's
+// block, and the codes are staged as [column][64 bytes] (16-byte piece j of
+// column c at piece j ^ ((c >> 2) & 3), spreading the writes over the banks)
+// and leave as each column's 64-byte run of the tile's 128 rows.
+// Order: a 128-byte output line holds 256 values, two tiles' worth in both
+// layouts, so tile ids pair consecutive row tiles inside each column tile
+// (id = 2 (row pair) n_ct + 2 ct + (row tile & 1)) and go to the XCDs in
+// chunks of 64: the two halves of every line are written by workgroups that
+// run at the same time on the same XCD and meet in its L2.
+constexpr int kFp4ColTileRows = 128, kFp4CastChunk = 64;
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s, uint8_t* q_row,
                                                                    uint8_t* s_row, Fp4ColGroups gr, int64_t ldp) {
   constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int EP = 16 / (int)sizeof(T);               // elements per 16-byte piece
-  constexpr int kPiecesPerRow = kFp4ColTileCols / EP;
-  constexpr int kIters = kFp4ColTileRows * kPiecesPerRow / 256;
-  // [row][column] with a pad so that the column reads of a wave (64 columns
-  // of one row) spread over the banks
-  __shared__ __attribute__((aligned(16))) T tile[kFp4ColTileRows][kFp4ColTileCols + (kBf16 ? 2 : 1)];
-  auto val = [&](int r, int c) __attribute__((always_inline)) -> float {
-    if constexpr (kBf16) return __uint_as_float((uint32_t)tile[r][c] << 16);
-    else return tile[r][c];
-  };
-  const int64_t n_ct = (cols + kFp4ColTileCols - 1) / kFp4ColTileCols;
-  const int rt = (int)(blockIdx.x / n_ct);
-  const int64_t c0 = (int64_t)(blockIdx.x % n_ct) * kFp4ColTileCols;
-  int lo = 0, hi = gr.n - 1;                  // last group whose first tile is <= rt
+  constexpr int VPT = 16 / (int)sizeof(T);   // values per 16-byte chunk
+  constexpr int TC = 16 * VPT;               // tile columns
+  constexpr int TR = kFp4ColTileRows;
+  constexpr int TPB = 32 / VPT;              // threads per 32-block along a row
+  constexpr int NB = TC / 32;                // 32-blocks per tile row
+  constexpr int CPS = kBf16 ? 2 : 1;         // columns per dword
+  // the input tile as loaded, then (once every column is in registers) the
+  // columnwise codes [column][64 bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TR * 256];
+  __shared__ uint32_t cs_t[TC];              // columnwise scale bytes [column][block]
+  static_assert(TC * 64 <= TR * 256, "columnwise staging must fit the input tile");
+
+  const int64_t n_ct = (cols + TC - 1) / TC;
+  const int n_rt = gr.tile0[gr.n];
+  const int total = (int)((int64_t)((n_rt + 1) / 2) * 2 * n_ct);
+  const int id = xcd_remap<kFp4CastChunk>((int)blockIdx.x, total);
+  const int64_t pair = id / (2 * n_ct), rem = id - pair * 2 * n_ct;
+  const int rt = (int)(2 * pair + (rem & 1));
+  if (rt >= n_rt) return;                    // the missing half of an odd last pair
+  const int64_t c0 = (rem >> 1) * TC;
+  int lo = 0, hi = gr.n - 1;                 // last group whose first tile is <= rt
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (gr.tile0[mid] <= rt) lo = mid; else hi = mid - 1;
   }
-  const int64_t lr0 = (int64_t)(rt - gr.tile0[lo]) * kFp4ColTileRows;   // first row of the tile in its group
-  const int64_t r0 = gr.row0[lo] + lr0;                                  // its global row
+  const int64_t lr0 = (int64_t)(rt - gr.tile0[lo]) * TR;   // first row of the tile in its group
+  const int64_t r0 = gr.row0[lo] + lr0;                     // its global row
   const int64_t m_g = gr.row0[lo + 1] - gr.row0[lo];
   const int64_t p_g = (m_g + 31) / 32 * 32;
   const int tid = threadIdx.x;
-  // 128 rows of 16-byte pieces (cols % 32 == 0: a piece is wholly inside or
-  // wholly past the last column)
+  const int cc = tid & 15;
+  const int64_t col = c0 + cc * VPT;
+  const bool col_ok = col < cols;              // cols % 32 == 0: a chunk is wholly in or out
+
+  uint4 raw[TR / 16];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int p = it * 256 + tid, rr = p / kPiecesPerRow, cp = (p % kPiecesPerRow) * EP;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (lr0 + rr < m_g && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + c0 + cp);
-    if constexpr (kBf16) {
-      const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+  for (int p = 0; p < TR / 16; ++p) {
+    const int rr = 16 * p + (tid >> 4);
+    raw[p] = make_uint4(0, 0, 0, 0);
+    if (lr0 + rr < m_g && col_ok) raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + col);
+  }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tile[rr][cp + j] = e[j];
-    } else {
-      tile[rr][cp + 0] = __uint_as_float(v.x);
-      tile[rr][cp + 1] = __uint_as_float(v.y);
-      tile[rr][cp + 2] = __uint_as_float(v.z);
-      tile[rr][cp + 3] = __uint_as_float(v.w);
+  for (int p = 0; p < TR / 16; ++p) {
+    const int rr = 16 * p + (tid >> 4);
+    *reinterpret_cast<uint4*>(tile + rr * 256 + cc * 16) = raw[p];
+    if (q_row != nullptr) {
+      float v[VPT];
+      if constexpr (kBf16) {
+        v[0] = bf16_lo(raw[p].x); v[1] = bf16_hi(raw[p].x); v[2] = bf16_lo(raw[p].y); v[3] = bf16_hi(raw[p].y);
+        v[4] = bf16_lo(raw[p].z); v[5] = bf16_hi(raw[p].z); v[6] = bf16_lo(raw[p].w); v[7] = bf16_hi(raw[p].w);
+      } else {
+        v[0] = __uint_as_float(raw[p].x); v[1] = __uint_as_float(raw[p].y);
+        v[2] = __uint_as_float(raw[p].z); v[3] = __uint_as_float(raw[p].w);
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) am = umax(am, abs_bits(v[i]));
+#pragma unroll
+      for (int sh = 1; sh < TPB; sh <<= 1) am = umax(am, xor_u32(am, sh));
+      const uint32_t eb = am >> 23;
+      const uint32_t sc = eb > 2u ? eb - 2u : 0u;
+      uint32_t codes;
+      if constexpr (kBf16) {
+        codes = e2m1x8_bf16(raw[p], e8m0_as_scale(sc));
+      } else {
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], e8m0_as_scale(sc), 0);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[2], v[3], e8m0_as_scale(sc), 1);
+      }
+      const int64_t row = r0 + rr;
+      const bool row_ok = lr0 + rr < m_g;
+      if (row_ok && col_ok) {
+        if constexpr (kBf16) *reinterpret_cast<uint32_t*>(q_row + row * (cols / 2) + col / 2) = codes;
+        else *reinterpret_cast<uint16_t*>(q_row + row * (cols / 2) + col / 2) = (uint16_t)codes;
+      }
+      // the row's scale bytes of this tile, gathered into one word
+      uint32_t word = sc << (8 * (cc / TPB));
+#pragma unroll
+      for (int sh = TPB; sh < 16; sh <<= 1) word |= xor_u32(word, sh);
+      if (cc == 0 && row_ok) {
+        uint8_t* sd = s_row + row * (cols / 32) + c0 / 32;
+        const bool whole = c0 + TC <= cols && (reinterpret_cast<uintptr_t>(sd) & (NB - 1)) == 0;
+        if (whole) {
+          if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = word;
+          else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)word;
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            if (c0 + 32 * j < cols) sd[j] = (uint8_t)(word >> (8 * j));
+        }
+      }
     }
   }
   __syncthreads();
-  if (q_row != nullptr) {
-    const int rr = tid >> 1, bb = tid & 1;
-    const int64_t row = r0 + rr, col = c0 + 32 * bb;
-    if (lr0 + rr < m_g && col < cols) {
-      float v[32];
+
+  // columnwise: thread t takes the CPS columns of dword t % 64 and the 32-row
+  // block t / 64 (rows of the group past its end are zeros)
+  const int rb = tid >> 6, slot = tid & 63;
+  float v[CPS][32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = val(rr, 32 * bb + i);
-      uint4 codes;
-      const uint32_t sc = fp4_block(v, codes);
-      *reinterpret_cast<uint4*>(q_row + row * (cols / 2) + col / 2) = codes;
-      s_row[row * (cols / 32) + col / 32] = (uint8_t)sc;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * rb + i) * 256 + slot * 4);
+    if constexpr (kBf16) {
+      v[0][i] = bf16_lo(w);
+      v[CPS - 1][i] = bf16_hi(w);
+    } else {
+      v[0][i] = __uint_as_float(w);
     }
   }
-  const int c = tid % kFp4ColTileCols, rb = tid / kFp4ColTileCols;
-  const int64_t col = c0 + c, lrow = lr0 + 32 * rb;          // block's first row in the group
-  if (col >= cols || lrow >= p_g) return;
-  const int64_t pcol = gr.pcol0[lo] + lrow;                   // its position in the columnwise layout
-  float v[32];
+  __syncthreads();                             // every column read: the tile becomes the code staging
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = val(32 * rb + i, c);
-  uint4 codes;
-  const uint32_t sc = fp4_block(v, codes);
-  *reinterpret_cast<uint4*>(q + col * (ldp / 2) + pcol / 2) = codes;
-  s[col * (ldp / 32) + pcol / 32] = (uint8_t)sc;
+  for (int j = 0; j < CPS; ++j) {
+    uint4 codes;
+    const uint32_t sc = fp4_block(v[j], codes);
+    const int cl = CPS * slot + j;             // column inside the tile
+    *reinterpret_cast<uint4*>(tile + cl * 64 + ((rb ^ ((cl >> 2) & 3)) << 4)) = codes;
+    reinterpret_cast<uint8_t*>(cs_t)[cl * 4 + rb] = (uint8_t)sc;
+  }
+  __syncthreads();
+
+  // each column's 64-byte run; blocks past the group's padded rows are not
+  // part of the layout (the next group's columns start there)
+  const int64_t pc0 = gr.pcol0[lo] + lr0;     // the tile's first position in the columnwise layout
+#pragma unroll
+  for (int it = 0; it < TC * 4 / 256; ++it) {
+    const int u = it * 256 + tid;
+    const int cl = u >> 2, piece = u & 3;
+    const int64_t colc = c0 + cl;
+    if (colc < cols && lr0 + 32 * piece < p_g)
+      *reinterpret_cast<uint4*>(q + colc * (ldp / 2) + pc0 / 2 + 16 * piece) =
+          *reinterpret_cast<const uint4*>(tile + cl * 64 + ((piece ^ ((cl >> 2) & 3)) << 4));
+  }
+  // columnwise scales: the tile's 4 blocks of a column are 4 consecutive bytes
+  if (tid < TC) {
+    const int64_t colc = c0 + tid;
+    if (colc < cols) {
+      const uint32_t word = cs_t[tid];
+      uint8_t* sd = s + colc * (ldp / 32) + pc0 / 32;
+      if (lr0 + 96 < p_g && (reinterpret_cast<uintptr_t>(sd) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(sd) = word;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (lr0 + 32 * j < p_g) sd[j] = (uint8_t)(word >> (8 * j));
+      }
+    }
+  }
+}
+
+// Grid of the columnwise cast: row tiles in pairs, times the column tiles.
+template <typename T>
+int64_t fp4_colwise_grid(const Fp4ColGroups& gr, int64_t cols) {
+  constexpr int TC = 16 * (16 / (int)sizeof(T));
+  return (int64_t)((gr.tile0[gr.n] + 1) / 2) * 2 * ((cols + TC - 1) / TC);
 }
 
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s, uint8_t* q_col,
@@ -181,7 +290,8 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
     gr.pcol0[1] = rows;
     gr.tile0[0] = 0;
     gr.tile0[1] = (int32_t)((rows + kFp4ColTileRows - 1) / kFp4ColTileRows);
-    const int64_t tiles = (int64_t)gr.tile0[1] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
+    const int64_t tiles = fp4_colwise_grid<uint16_t>(gr, cols);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows,
                        cols, q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows);
   }
@@ -191,8 +301,9 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
 hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
                                        uint8_t* q_col, uint8_t* s_col, uint8_t* q_row, uint8_t* s_row,
                                        hipStream_t stream) {
-  const int64_t tiles = (int64_t)gr.tile0[gr.n] * ((cols + kFp4ColTileCols - 1) / kFp4ColTileCols);
+  const int64_t tiles = x_f32 ? fp4_colwise_grid<float>(gr, cols) : fp4_colwise_grid<uint16_t>(gr, cols);
   if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (x_f32)
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, stream,
                        reinterpret_cast<const float*>(x), rows, cols, q_col, s_col, q_row, s_row, gr,
@@ -231,13 +342,11 @@ __device__ __forceinline__ uint32_t nvfp4_block(const float (&v)[16], float S, u
   const uint32_t sc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sb, 448.0f), 0.0f, 0, false) & 0xFFu;
   const float sv = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
   const float r = sv > 0.0f ? S / sv : 0.0f;
-  uint32_t w0 = 0, w1 = 0;
+  // q = E2M1 of fl32(v * r): the convert at scale 1 (E8M0 code 127)
+  float vr[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w0 |= e2m1_code(v[j] * r) << (4 * j);
-    w1 |= e2m1_code(v[8 + j] * r) << (4 * j);
-  }
-  codes = make_uint2(w0, w1);
+  for (int j = 0; j < 16; ++j) vr[j] = v[j] * r;
+  codes = make_uint2(e2m1x8(&vr[0], 1.0f), e2m1x8(&vr[8], 1.0f));
   return sc;
 }
 
