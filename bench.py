@@ -42,6 +42,8 @@ PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 NOMINAL_SCLK_MHZ = 2400.0         # the clock the MFMA peak is quoted at
 GEMM_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_gemm.hip")
 QUANT_KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", "mx_quantize.hip")
+# headers compiled into both kernels (device helpers, argument structs)
+KERNEL_HEADERS = [os.path.join(ROOT, "mxfp8_block_scaled_mx_amd", "csrc", h) for h in ("mx_device.h", "mx_internal.h")]
 
 
 def log(msg):
@@ -93,6 +95,8 @@ def traffic_from_profiles(workload, stage):
     for key, src in (("source_sha256", GEMM_KERNEL_SRC), ("quantize_source_sha256", QUANT_KERNEL_SRC)):
         if vals.get(key) != hashlib.sha256(open(src, "rb").read()).hexdigest():
             return None
+    if vals.get("headers_sha256") != hashlib.sha256(b"".join(open(h, "rb").read() for h in KERNEL_HEADERS)).hexdigest():
+        return None
     try:
         return float(vals[f"{stage}.hbm_bytes_per_launch"])
     except (KeyError, ValueError):

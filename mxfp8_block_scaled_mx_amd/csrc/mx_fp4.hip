@@ -621,8 +621,9 @@ hipError_t launch_swiglu_bwd_fp4(const float* da, const uint16_t* h1, const floa
 // A k-tile is 256 values (128 bytes of codes) of every row of the workgroup
 // tile; A and B k-tiles are staged in LDS, double-buffered, by buffer->LDS DMA
 // (8 lanes per 128-byte row), with 16-byte chunk c of row r at chunk
-// c ^ (r & 7) so that fragment reads (32 rows, one chunk) spread over the LDS
-// banks. One barrier per k-tile: the next k-tile's DMA is in flight during
+// c ^ ((r >> 1) & 7): two 128-byte rows share one 256-byte line of the 64 LDS
+// banks, so this puts a fragment read's 16 consecutive rows (one chunk each)
+// on 16 different 16-byte bank groups. One barrier per k-tile: the next k-tile's DMA is in flight during
 // this one's MFMAs.
 constexpr int kF4SubM = 4, kF4SubN = 4;     // wave tile: MFMA tiles of 32 x 32
 constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
@@ -709,11 +710,12 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const bool sc_dword = NV || ((lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0);
 
   // global -> LDS by buffer DMA, 1 KB (8 rows) per instruction: lane L
-  // fills chunk L % 8 of row L / 8 of the block with global chunk
-  // (L % 8) ^ (L / 8), which is the swizzle above since the block starts at a
-  // multiple of 8 rows. Bytes past K in the last k-tile come from the next row
-  // (or read zero) and feed only skipped k-steps.
-  const uint32_t dma_off = (uint32_t)((lane >> 3) * ldq + 16 * ((lane & 7) ^ (lane >> 3)));
+  // fills chunk L % 8 of row 8 blk + L / 8 with global chunk
+  // (L % 8) ^ (((8 blk + L / 8) >> 1) & 7) = (L % 8) ^ (L / 16) ^ 4 (blk & 1),
+  // the swizzle above; blk = 4 p + wave, so blk & 1 = wave & 1. Bytes past K
+  // in the last k-tile come from the next row (or read zero) and feed only
+  // skipped k-steps.
+  const uint32_t dma_off = (uint32_t)((lane >> 3) * ldq + 16 * ((lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1))));
   auto dma_tile = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < TM / 32; ++p) {
@@ -752,7 +754,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       xb[j] = scale_pair(rsb, (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k));
   };
   auto frag = [&](const uint8_t* base, int r, int s) __attribute__((always_inline)) -> v8i {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ (r & 7)) << 4));
+    const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ ((r >> 1) & 7)) << 4));
     v8i f;
     f[0] = q.x; f[1] = q.y; f[2] = q.z; f[3] = q.w;
     f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
@@ -796,7 +798,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       // in the last k-tile) gets scale 0.
       const bool half_ok = (int64_t)(256 * t + 128 * h) < klen;
       auto chunk = [&](const uint8_t* base, int r, int c) __attribute__((always_inline)) -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(base + r * KT + ((c ^ (r & 7)) << 4));
+        return *reinterpret_cast<const u32x4*>(base + r * KT + ((c ^ ((r >> 1) & 7)) << 4));
       };
       auto dequant = [&](uint32_t w, float sv) __attribute__((always_inline)) -> f16x8 {
         // sv = 2^E * m with m in [1, 2) holding at most 3 fraction bits: the
