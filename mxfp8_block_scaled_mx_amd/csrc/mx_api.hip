@@ -548,9 +548,13 @@ mx_status run_gemm(const GemmPlan& p, int mode, int epi, hipStream_t stream, con
 
 // 4-bit (grouped) GEMM, MXFP4 or (nv) NVFP4 operands: validation, group
 // table, launch.
+// split_ws (MXFP4 only; may be null): room for the fp32 partials of a
+// split-K tail, planned as for the MXFP8 GEMMs (plan_split_tail) with the
+// 4-bit kernel's 256-value k-tiles.
 static mx_status gemm_4bit_impl(const char* who, bool nv, const uint8_t* a, const uint8_t* a_s, const float* a_amax,
                                 const uint8_t* b, const uint8_t* b_s, const float* b_amax, const int64_t* sizes,
-                                int32_t groups, int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream) {
+                                int32_t groups, int64_t n, int64_t k, void* c, mx_dtype c_dtype, void* stream,
+                                float* split_ws = nullptr, size_t split_ws_bytes = 0) {
   if (c_dtype != MX_BF16 && c_dtype != MX_F32) return fail(MX_EINVAL, "%s: bad output dtype", who);
   if (groups < 1 || groups > MX_MAX_GROUPS) return fail(MX_EINVAL, "%s: need 1 <= groups <= %d", who, MX_MAX_GROUPS);
   if (!sizes) return fail(MX_EINVAL, "%s: null group sizes", who);
@@ -579,18 +583,32 @@ static mx_status gemm_4bit_impl(const char* who, bool nv, const uint8_t* a, cons
     return fail(MX_EALIGN, "%s: a, b and c must be 16-byte aligned", who);
   if (nv && (!aligned(a_s, 8) || !aligned(b_s, 8) || !aligned(a_amax, 4) || !aligned(b_amax, 4)))
     return fail(MX_EALIGN, "%s: scales must be 8-byte and tensor amax 4-byte aligned", who);
+  mx::Fp4Split sp{0, 0, nullptr};
+  if (!nv && split_ws != nullptr) {
+    const int n_cu = device_cu_count();
+    const int64_t T = mtiles * ntiles;
+    const int64_t full = n_cu > 0 ? T / n_cu * n_cu : T, tail = T - full;
+    const int64_t nk = (k + 255) / 256;
+    if (n_cu > 0 && tail > 0 && tail <= n_cu / 2 && tail <= mx::kMaxSplitTiles) {
+      const int64_t parts = std::min<int64_t>({mx::kMaxSplitParts, n_cu / tail, nk / 4});
+      if (parts >= 2 && (size_t)(tail * parts) * mx::kFp4GemmTileM * mx::kFp4GemmTileN * 4 <= split_ws_bytes)
+        sp = mx::Fp4Split{(int32_t)full, (int32_t)parts, split_ws};
+    }
+  }
   hipError_t e = nv ? mx::launch_gemm_nvfp4(a, a_s, a_amax, b, b_s, b_amax, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
                                             reinterpret_cast<hipStream_t>(stream))
                     : mx::launch_gemm_fp4(a, a_s, b, b_s, gr, n, k, c, c_dtype == MX_F32 ? 1 : 0,
-                                          reinterpret_cast<hipStream_t>(stream));
+                                          reinterpret_cast<hipStream_t>(stream), sp);
   if (e != hipSuccess) return hip_fail(e, who);
   return MX_OK;
 }
 
 static mx_status gemm_fp4_impl(const char* who, const uint8_t* a, const uint8_t* a_s, const uint8_t* b,
                                const uint8_t* b_s, const int64_t* sizes, int32_t groups, int64_t n, int64_t k,
-                               void* c, mx_dtype c_dtype, void* stream) {
-  return gemm_4bit_impl(who, false, a, a_s, nullptr, b, b_s, nullptr, sizes, groups, n, k, c, c_dtype, stream);
+                               void* c, mx_dtype c_dtype, void* stream, float* split_ws = nullptr,
+                               size_t split_ws_bytes = 0) {
+  return gemm_4bit_impl(who, false, a, a_s, nullptr, b, b_s, nullptr, sizes, groups, n, k, c, c_dtype, stream,
+                        split_ws, split_ws_bytes);
 }
 
 extern "C" {
@@ -1413,12 +1431,15 @@ struct Fp4MlpLayout {
   std::vector<int64_t> split;
   mx::Fp4ColGroups cg{};   // per-expert row tiles of the columnwise casts
   mx::Fp4KGroups kg{};     // per-expert padded k ranges of the weight gradients
-  // forward workspace: rowwise X, W1, W2, H1 (fp32), rowwise A, A (fp32)
-  size_t xq, xs, w1q, w1s, w2q, w2s, h1f, aq, as, a32, fwd_total;
+  // forward workspace: rowwise X, W1, W2, H1 (fp32), rowwise A, A (fp32),
+  // GEMM2's split-K partials
+  size_t xq, xs, w1q, w1s, w2q, w2s, h1f, aq, as, a32, split2, fwd_total;
   // saved: H1 (bf16), columnwise A, X, and per-expert columnwise W1, W2
   size_t h1, acq, acs, xcq, xcs, w1cq, w1cs, w2cq, w2cs, saved_total;
-  // backward workspace: dY both layouts, dA (fp32), dH1 (fp32), dH1 both layouts
-  size_t dyq, dys, dycq, dycs, da32, dh1f, dhq, dhs, dhcq, dhcs, bwd_total;
+  // backward workspace: dY both layouts, dA (fp32), dH1 (fp32), dH1 both
+  // layouts, dgrad1's split-K partials
+  size_t dyq, dys, dycq, dycs, da32, dh1f, dhq, dhs, dhcq, dhcs, split1, bwd_total;
+  size_t split_bytes;        // each of split2 / split1
 };
 
 mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayout* L, const char* who) {
@@ -1466,6 +1487,11 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
   L->aq = take(c, R * F / 2);
   L->as = take(c, R * F / 32);
   L->a32 = take(c, R * F * 4);
+  // GEMM2 and dgrad1 (n = H): sum over experts of ceil(m_e/256) x ceil(H/256) tiles
+  int64_t m_tiles = 0;
+  for (int g = 0; g < E; ++g) m_tiles += cdiv(L->split[g], mx::kFp4GemmTileM);
+  L->split_bytes = split_ws_bytes(m_tiles * cdiv(H, mx::kFp4GemmTileN));
+  L->split2 = take(c, L->split_bytes);
   L->fwd_total = c;
   c = 0;
   L->h1 = take(c, R * 2 * F * 2);
@@ -1489,6 +1515,7 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
   L->dhs = take(c, R * 2 * F / 32);
   L->dhcq = take(c, 2 * F * P / 2);
   L->dhcs = take(c, 2 * F * P / 32);
+  L->split1 = take(c, L->split_bytes);
   L->bwd_total = c;
   return MX_OK;
 }
@@ -1548,7 +1575,7 @@ mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs,
   }
   // GEMM2 -> Y (bf16)
   return gemm_fp4_impl(who, W + L.aq, W + L.as, W + L.w2q, W + L.w2s, L.split.data(), (int32_t)E, H, F, y, MX_BF16,
-                       stream);
+                       stream, reinterpret_cast<float*>(W + L.split2), L.split_bytes);
 }
 
 mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs, const void* saved, void* dx,
@@ -1577,7 +1604,7 @@ mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs
   if (st != MX_OK) return st;
   // dgrad1: dX = dH1 . W1 (bf16) on the columnwise W1 copies [H, 2F]
   st = gemm_fp4_impl(who, W + L.dhq, W + L.dhs, S + L.w1cq, S + L.w1cs, L.split.data(), (int32_t)E, H, 2 * F, dx,
-                     MX_BF16, stream);
+                     MX_BF16, stream, reinterpret_cast<float*>(W + L.split1), L.split_bytes);
   if (st != MX_OK) return st;
   // weight gradients (fp32, stored or accumulated): dW2_e = dY_e^T A_e, dW1_e = dH1_e^T X_e
   st = fp4_step(mx::launch_gemm_fp4_group_k(W + L.dycq, W + L.dycs, S + L.acq, S + L.acs, L.kg, H, F, dw2, accumulate,

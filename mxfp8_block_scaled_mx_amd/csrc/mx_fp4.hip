@@ -635,12 +635,14 @@ static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4
 // that holds only 32 valid values gets scale code 0 for the invalid half on
 // both operands, so its products (at most 36 * 2^-254) add exact zeros
 // whatever codes lie past the group; C_g is fp32, stored or accumulated.
-template <bool GK, bool F32, bool NV>
+// SPLIT: the split-K tail units only (a launch of its own over
+// (tiles - sp.first) * sp.parts workgroups), fp32 partial tiles out.
+template <bool GK, bool F32, bool NV, bool SPLIT = false>
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                                        const uint8_t* bs, Fp4Groups gr, Fp4KGroups kg, int64_t M,
                                                        int64_t N, int64_t K, int64_t n_tiles_n, void* c,
                                                        int32_t accumulate,
-                                                       const float* a_amax, const float* b_amax) {
+                                                       const float* a_amax, const float* b_amax, Fp4Split sp) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
@@ -655,7 +657,14 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // XCD. Group-M keeps the launch order: with a multiple of 8 n-tiles, block
   // b's n-tile (and its rows of B) stays on XCD b % 8 for every m-tile.
   const int64_t per_group = GK ? ((M + TM - 1) / TM) * n_tiles_n : 0;
-  const int id = GK ? xcd_remap((int)blockIdx.x, (int)(kg.n * per_group)) : (int)blockIdx.x;
+  int id = GK ? xcd_remap((int)blockIdx.x, (int)(kg.n * per_group)) : (int)blockIdx.x;
+  // split-K tail units: workgroup u is part u % parts of tile first + u / parts
+  int split_unit = -1, part = 0;
+  if constexpr (SPLIT) {
+    split_unit = (int)blockIdx.x;
+    id = sp.first + split_unit / sp.parts;
+    part = split_unit % sp.parts;
+  }
   if constexpr (GK) {
     // Every group has per_group tiles. When that is a multiple of kXcdChunk,
     // chunk q of kXcdChunk ids goes to group (q % n + q / n) % n as its chunk
@@ -702,6 +711,9 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds + kbeg / kVPS, (amv - 1) * lds + klen / kVPS);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + brow0 * lds + kbeg / kVPS, (bnv - 1) * lds + klen / kVPS);
   const int ksteps = (int)((klen + 63) / 64), ktiles = (ksteps + 3) / 4;
+  // k-tiles [t_lo, t_hi) of this work unit
+  const int t_lo = SPLIT ? part * ktiles / sp.parts : 0;
+  const int t_hi = SPLIT ? (part + 1) * ktiles / sp.parts : ktiles;
   // a row's 8 scales of a k-tile: one aligned 8-byte load. The k range must
   // also be whole k-tiles: the last row's load would otherwise reach past
   // the resource's extent and come back as zero scales.
@@ -774,13 +786,13 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
   u32x2 nsa[SM], nsb[SN];
-  dma_tile(0, 0);
-  load_scales(0, sca, scb);
+  dma_tile(t_lo, 0);
+  load_scales(t_lo, sca, scb);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int t = 0; t < ktiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ktiles;         // uniform over the workgroup
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;           // uniform over the workgroup
     if (more) {
       dma_tile(t + 1, buf ^ 1);
       load_scales(t + 1, nsa, nsb);
@@ -884,6 +896,40 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   float alpha = 1.0f;
   if constexpr (NV)
     alpha = (float)(1.0 / ((double)nvfp4_tensor_scale(*a_amax) * (double)nvfp4_tensor_scale(b_amax[grp])));
+  if constexpr (SPLIT) {
+    // a split-K part: the whole fp32 partial tile, row-major (pitch TN), into
+    // its slot, through the wave's 32 KB LDS slice as whole 128-byte rows
+    // (the staging of the fp32 epilogue below, without old values)
+    uint8_t* const slice = wave < 2 ? sA[0] + wave * 32768 : sB[0] + (wave - 2) * 32768;
+    const float* wp = sp.ws + (int64_t)split_unit * TM * TN + (int64_t)(TM / 2 * wm) * TN + TN / 2 * wn;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(wp, ((int64_t)(TM / 2 - 1) * TN + TN / 2) * 4);
+    const int rr = lane >> 3, cc = lane & 7;
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      uint8_t* const st = slice + (i & 1) * (SN * 4096);
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x4 v;
+          v.x = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 0]));
+          v.y = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 1]));
+          v.z = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 2]));
+          v.w = __float_as_uint(vgpr_hop(acc[j][i][4 * g + 3]));
+          const int ch = 2 * g + h;
+          *reinterpret_cast<u32x4*>(st + j * 4096 + l32 * 128 + ((ch ^ (l32 & 7)) << 4)) = v;
+        }
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(st + j * 4096 + (8 * q + rr) * 128 + ((cc ^ rr) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(v, rd, ((uint32_t)(32 * i + 8 * q + rr) * TN + 32 * j + 4 * cc) * 4,
+                                                 0, 2);
+        }
+    }
+    return;
+  } else {
   if (F32 && (N & 31) == 0 && N <= (1 << 22)) {
     // fp32 C leaves through the wave's 32 KB LDS slice (the operand stages
     // are free after the k-loop's last barrier) so that every store covers
@@ -951,6 +997,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     }
     return;
   }
+  }
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
@@ -995,17 +1042,87 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   }
 }
 
+// Split-K reduce: one workgroup per 16-row slab of a tail tile; a thread
+// issues its loads (4 float4 positions x up to kMaxSplitParts parts) before
+// adding the parts in part order, and writes C for the rows of the tile's
+// group and the columns below N.
+constexpr int kF4RedRows = 16;
+template <bool F32>
+__global__ __launch_bounds__(256) void fp4_split_reduce_kernel(Fp4Split sp, Fp4Groups gr, int64_t N,
+                                                               int64_t n_tiles_n, void* c) {
+  constexpr int TM = kFp4GemmTileM, TN = kFp4GemmTileN, kSlabs = TM / kF4RedRows;
+  static_assert(kF4RedRows * TN == 4 * 4 * 256, "a slab is 4 float4 per thread");
+  const int tile = (int)blockIdx.x / kSlabs, slab = (int)blockIdx.x % kSlabs;
+  const int id = sp.first + tile;
+  const int64_t mt = id / n_tiles_n, nt = id - mt * n_tiles_n;
+  int lo = 0, hi = gr.n - 1;                  // the group of m-tile mt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gr.tile0[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  const int64_t am0 = gr.row0[lo] + (mt - gr.tile0[lo]) * TM, row_end = gr.row0[lo + 1];
+  const int64_t bn0 = nt * TN;
+  const float* ws = sp.ws + (int64_t)tile * sp.parts * TM * TN + slab * kF4RedRows * TN;
+  float4 v[kMaxSplitParts][4];
+#pragma unroll
+  for (int p = 0; p < kMaxSplitParts; ++p)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (p < sp.parts)
+        v[p][k] = *reinterpret_cast<const float4*>(ws + (int64_t)p * TM * TN + (k * 256 + (int)threadIdx.x) * 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = (k * 256 + (int)threadIdx.x) * 4;
+    const int64_t row = am0 + slab * kF4RedRows + e / TN, col = bn0 + e % TN;
+    float4 sum = v[0][k];
+#pragma unroll
+    for (int p = 1; p < kMaxSplitParts; ++p)
+      if (p < sp.parts) { sum.x += v[p][k].x; sum.y += v[p][k].y; sum.z += v[p][k].z; sum.w += v[p][k].w; }
+    if (row >= row_end || col >= N) continue;
+    const float x[4] = {sum.x, sum.y, sum.z, sum.w};
+    if constexpr (F32) {
+      float* cp = reinterpret_cast<float*>(c) + row * N + col;
+      for (int q = 0; q < 4; ++q)
+        if (col + q < N) cp[q] = x[q];
+    } else {
+      uint16_t* cp = reinterpret_cast<uint16_t*>(c) + row * N + col;
+      for (int q = 0; q < 4; ++q)
+        if (col + q < N) cp[q] = (uint16_t)bf16_rne(x[q]);
+    }
+  }
+}
+
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
-                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream) {
+                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream,
+                           const Fp4Split& split_in) {
   const int64_t tm = gr.tile0[gr.n], tn = (N + kFp4GemmTileN - 1) / kFp4GemmTileN;
   if (tm * tn == 0) return hipSuccess;
   Fp4KGroups kg{};
-  if (c_f32)
-    hipLaunchKernelGGL((gemm_fp4_kernel<false, true, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
-                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr);
-  else
-    hipLaunchKernelGGL((gemm_fp4_kernel<false, false, false>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
-                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr);
+  const int64_t tiles = tm * tn;
+  const bool split = split_in.parts > 1 && split_in.parts <= kMaxSplitParts && split_in.first >= 0 &&
+                     split_in.first < tiles && split_in.ws != nullptr;
+  const Fp4Split none{0, 0, nullptr};
+  // whole tiles [0, first); with a split, the tail's parts in a launch of their own, then their sums
+  const int64_t main_tiles = split ? split_in.first : tiles;
+  if (main_tiles > 0) {
+    if (c_f32)
+      hipLaunchKernelGGL((gemm_fp4_kernel<false, true, false>), dim3((unsigned)main_tiles), dim3(256), 0, stream, a,
+                         as, b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr, none);
+    else
+      hipLaunchKernelGGL((gemm_fp4_kernel<false, false, false>), dim3((unsigned)main_tiles), dim3(256), 0, stream, a,
+                         as, b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, nullptr, nullptr, none);
+  }
+  if (split) {
+    const int64_t tail = tiles - split_in.first;
+    hipLaunchKernelGGL((gemm_fp4_kernel<false, true, false, true>), dim3((unsigned)(tail * split_in.parts)),
+                       dim3(256), 0, stream, a, as, b, bs, gr, kg, (int64_t)0, N, K, tn, nullptr, 0, nullptr,
+                       nullptr, split_in);
+    const dim3 rgrid((unsigned)(tail * (kFp4GemmTileM / kF4RedRows)));
+    if (c_f32)
+      hipLaunchKernelGGL(fp4_split_reduce_kernel<true>, rgrid, dim3(256), 0, stream, split_in, gr, N, tn, c);
+    else
+      hipLaunchKernelGGL(fp4_split_reduce_kernel<false>, rgrid, dim3(256), 0, stream, split_in, gr, N, tn, c);
+  }
   return hipGetLastError();
 }
 
@@ -1017,10 +1134,10 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a
   Fp4KGroups kg{};
   if (c_f32)
     hipLaunchKernelGGL((gemm_fp4_kernel<false, true, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
-                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax);
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax, Fp4Split{0, 0, nullptr});
   else
     hipLaunchKernelGGL((gemm_fp4_kernel<false, false, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, stream, a, as,
-                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax);
+                       b, bs, gr, kg, (int64_t)0, N, K, tn, c, 0, a_amax, b_amax, Fp4Split{0, 0, nullptr});
   return hipGetLastError();
 }
 
@@ -1032,7 +1149,7 @@ hipError_t launch_gemm_fp4_group_k(const uint8_t* a, const uint8_t* as, const ui
   if (tiles == 0) return hipSuccess;
   Fp4Groups gr{};
   hipLaunchKernelGGL((gemm_fp4_kernel<true, true, false>), dim3((unsigned)tiles), dim3(256), 0, stream, a, as, b, bs,
-                     gr, kg, M, N, kg.k0[kg.n], tn, c, accumulate, nullptr, nullptr);
+                     gr, kg, M, N, kg.k0[kg.n], tn, c, accumulate, nullptr, nullptr, Fp4Split{0, 0, nullptr});
   return hipGetLastError();
 }
 

@@ -940,24 +940,38 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* part, f
 // Split-K tail: tile args.split_f + blockIdx.x is the sum of its
 // args.split_s fp32 partials (added in part order); write it as C (bf16, or
 // fp32 with optional accumulate) over the tile's valid rows and columns.
+// Split-K reduce: one workgroup per kRedRows-row slab of a tail tile. A
+// thread issues all of its loads (4 float4 positions x up to kMaxSplitParts
+// parts) before adding, and adds the parts in part order (then the old value
+// when accumulating), so the sums are those of a plain loop over the parts.
+constexpr int kRedRows = 16;
 template <int EPI>
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs args) {
-  const int id = args.split_f + (int)blockIdx.x;
+  constexpr int kSlabs = BM / kRedRows;
+  static_assert(kRedRows * BN == 4 * 4 * 256, "a slab is 4 float4 per thread");
+  const int tile = (int)blockIdx.x / kSlabs, slab = (int)blockIdx.x % kSlabs;
+  const int id = args.split_f + tile;
   const TileCoord tc = locate_tile(args.groups, id, MX_GROUP_M, args.M, args.n_tiles_n);
   const int slot = tc.slot;
   const int64_t a_row0 = (int64_t)args.groups.a0[slot] + (int64_t)tc.mt * BM;
   const int rows_valid = min(BM, args.groups.len[slot] - tc.mt * BM);
   const int64_t col0 = (int64_t)tc.nt * BN;
   const int S = args.split_s;
-  const float* ws = args.split_ws + (int64_t)blockIdx.x * S * BM * BN;
-  for (int it = 0; it < BM * BN / 1024; ++it) {
-    const int e = it * 1024 + (int)threadIdx.x * 4;
-    const int r = e / BN, c = e % BN;
-    float4 sum = *reinterpret_cast<const float4*>(ws + e);
-    for (int p = 1; p < S; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)p * BM * BN + e);
-      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-    }
+  const float* ws = args.split_ws + (int64_t)tile * S * BM * BN + slab * kRedRows * BN;
+  float4 v[kMaxSplitParts][4];
+#pragma unroll
+  for (int p = 0; p < kMaxSplitParts; ++p)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (p < S) v[p][k] = *reinterpret_cast<const float4*>(ws + (int64_t)p * BM * BN + (k * 256 + (int)threadIdx.x) * 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = (k * 256 + (int)threadIdx.x) * 4;
+    const int r = slab * kRedRows + e / BN, c = e % BN;
+    float4 sum = v[0][k];
+#pragma unroll
+    for (int p = 1; p < kMaxSplitParts; ++p)
+      if (p < S) { sum.x += v[p][k].x; sum.y += v[p][k].y; sum.z += v[p][k].z; sum.w += v[p][k].w; }
     if (r >= rows_valid || col0 + c >= args.N) continue;
     const int64_t o = (a_row0 + r) * args.ldc + col0 + c;
     if constexpr (EPI == EPI_BF16) {
@@ -1018,10 +1032,11 @@ hipError_t launch_gemm(int mode, int epi, bool scale_dword, const GemmArgs& args
 
 hipError_t launch_split_reduce(int epi, const GemmArgs& args, int tail_tiles, hipStream_t stream) {
   if (tail_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)(tail_tiles * (BM / kRedRows)));
   if (epi == EPI_BF16)
-    hipLaunchKernelGGL(split_reduce_kernel<EPI_BF16>, dim3(tail_tiles), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(split_reduce_kernel<EPI_BF16>, grid, dim3(256), 0, stream, args);
   else if (epi == EPI_F32)
-    hipLaunchKernelGGL(split_reduce_kernel<EPI_F32>, dim3(tail_tiles), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(split_reduce_kernel<EPI_F32>, grid, dim3(256), 0, stream, args);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -207,8 +207,18 @@ struct Fp4Groups {
   int32_t tile0[kMaxGroups + 1];     // first m-tile of group g; tile0[n] = all m-tiles
   int64_t row0[kMaxGroups + 1];      // first row of group g; row0[n] = M
 };
+// Split-K tail: the tiles from id `first` on (the last, partial round) each
+// run as `parts` workgroups over consecutive k-tile ranges, writing fp32
+// partial tiles (kFp4GemmTileM x kFp4GemmTileN, row-major, unit
+// (id - first) * parts + part) to ws; a reduce kernel adds each tile's parts
+// in part order and writes C. parts <= 1: no split.
+struct Fp4Split {
+  int32_t first, parts;
+  float* ws;
+};
 hipError_t launch_gemm_fp4(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
-                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream);
+                           const Fp4Groups& gr, int64_t N, int64_t K, void* c, int32_t c_f32, hipStream_t stream,
+                           const Fp4Split& split = Fp4Split{0, 0, nullptr});
 // Groups of the columnwise MXFP4 cast: group g's rows [row0[g], row0[g+1]),
 // padded to a multiple of 32 at columns [pcol0[g], pcol0[g+1]) of the
 // result; its 128-row tiles are tile0[g] .. tile0[g+1] - 1.

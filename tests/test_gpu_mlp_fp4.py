@@ -4,7 +4,8 @@ R17: the MXFP8 MLP of "Efficient MoE training for biological foundation
 models", Key technical approaches item 3, with every GEMM on MXFP4 copies).
 
 Bar: as for the MXFP8 MLP, normwise relative error <= 2e-2 for Y, dX, dW1,
-dW2 and dprobs, over the whole output and per expert with rows. The GPU forms
+dW2 and dprobs, over the whole output and per expert with rows. One case is
+shaped so that GEMM2 and dgrad1 run with a split-K tail. The GPU forms
 A and dH1 in fp32 and the oracle in float64, so a requantized code can differ
 by one E2M1 step where the two straddle a rounding boundary; such flips are
 rare, and the measured errors are printed. An expert with no rows gets zero
@@ -26,6 +27,10 @@ CASES = {
     "dense_one_expert": dict(seed=132, E=1, H=256, F=512, split=(384,)),
     "many_small": dict(seed=134, E=12, H=128, F=256,
                        split=(1, 31, 32, 33, 0, 64, 95, 96, 97, 127, 128, 129)),
+    # 3 output tiles of GEMM2 and dgrad1 (n = H = 256): the whole launch is a
+    # partial last round, so GEMM2 (k = 2048) runs split-K in 2 parts and
+    # dgrad1 (k = 4096) in 4, partials summed by the reduce kernel
+    "split_k_tail": dict(seed=135, E=2, H=256, F=2048, split=(300, 200)),
 }
 
 
