@@ -1431,14 +1431,14 @@ struct Fp4MlpLayout {
   std::vector<int64_t> split;
   mx::Fp4ColGroups cg{};   // per-expert row tiles of the columnwise casts
   mx::Fp4KGroups kg{};     // per-expert padded k ranges of the weight gradients
-  // forward workspace: rowwise X, W1, W2, H1 (fp32), rowwise A, A (fp32),
-  // GEMM2's split-K partials
-  size_t xq, xs, w1q, w1s, w2q, w2s, h1f, aq, as, a32, split2, fwd_total;
+  // forward workspace: rowwise X, W1, W2, H1 (fp32), rowwise A, GEMM2's
+  // split-K partials
+  size_t xq, xs, w1q, w1s, w2q, w2s, h1f, aq, as, split2, fwd_total;
   // saved: H1 (bf16), columnwise A, X, and per-expert columnwise W1, W2
   size_t h1, acq, acs, xcq, xcs, w1cq, w1cs, w2cq, w2cs, saved_total;
-  // backward workspace: dY both layouts, dA (fp32), dH1 (fp32), dH1 both
-  // layouts, dgrad1's split-K partials
-  size_t dyq, dys, dycq, dycs, da32, dh1f, dhq, dhs, dhcq, dhcs, split1, bwd_total;
+  // backward workspace: dY both layouts, dA (fp32), dH1 both layouts,
+  // dprobs partials [F / 64, R], dgrad1's split-K partials
+  size_t dyq, dys, dycq, dycs, da32, dhq, dhs, dhcq, dhcs, dpart, split1, bwd_total;
   size_t split_bytes;        // each of split2 / split1
 };
 
@@ -1486,7 +1486,6 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
   L->h1f = take(c, R * 2 * F * 4);
   L->aq = take(c, R * F / 2);
   L->as = take(c, R * F / 32);
-  L->a32 = take(c, R * F * 4);
   // GEMM2 and dgrad1 (n = H): sum over experts of ceil(m_e/256) x ceil(H/256) tiles
   int64_t m_tiles = 0;
   for (int g = 0; g < E; ++g) m_tiles += cdiv(L->split[g], mx::kFp4GemmTileM);
@@ -1510,11 +1509,11 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
   L->dycq = take(c, H * P / 2);
   L->dycs = take(c, H * P / 32);
   L->da32 = take(c, R * F * 4);
-  L->dh1f = take(c, R * 2 * F * 4);
   L->dhq = take(c, R * 2 * F / 2);
   L->dhs = take(c, R * 2 * F / 32);
   L->dhcq = take(c, 2 * F * P / 2);
   L->dhcs = take(c, 2 * F * P / 32);
+  L->dpart = take(c, F / 64 * R * 4);
   L->split1 = take(c, L->split_bytes);
   L->bwd_total = c;
   return MX_OK;
@@ -1562,17 +1561,21 @@ mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs,
   st = gemm_fp4_impl(who, W + L.xq, W + L.xs, W + L.w1q, W + L.w1s, L.split.data(), (int32_t)E, 2 * F, H,
                      W + L.h1f, MX_F32, stream);
   if (st != MX_OK) return st;
-  // ScaledSwiGLU: H1 (bf16, saved), A rowwise MXFP4 (and fp32 for its columnwise copy)
-  st = fp4_step(mx::launch_swiglu_fwd_fp4(reinterpret_cast<const float*>(W + L.h1f), probs, R, F,
-                                          train ? reinterpret_cast<uint16_t*>(S + L.h1) : nullptr,
-                                          train ? reinterpret_cast<float*>(W + L.a32) : nullptr, W + L.aq, W + L.as,
-                                          stream), who);
-  if (st != MX_OK) return st;
+  // ScaledSwiGLU: A rowwise MXFP4; in training also H1 (bf16, saved) and A's
+  // per-expert columnwise copy, from one pass over H1
   if (train) {
-    st = fp4_step(mx::launch_quantize_fp4_grouped(W + L.a32, true, R, F, L.cg, S + L.acq, S + L.acs, nullptr, nullptr,
-                                                  stream), who);
-    if (st != MX_OK) return st;
+    mx::Fp4SwigluArgs sw{};
+    sw.h1f = reinterpret_cast<const float*>(W + L.h1f);
+    sw.h1_out = reinterpret_cast<uint16_t*>(S + L.h1);
+    sw.probs = probs;
+    sw.R = R;
+    sw.F = F;
+    st = fp4_step(mx::launch_swiglu_fp4_cast(false, sw, L.cg, S + L.acq, S + L.acs, W + L.aq, W + L.as, stream), who);
+  } else {
+    st = fp4_step(mx::launch_swiglu_fwd_fp4(reinterpret_cast<const float*>(W + L.h1f), probs, R, F, W + L.aq, W + L.as,
+                                            stream), who);
   }
+  if (st != MX_OK) return st;
   // GEMM2 -> Y (bf16)
   return gemm_fp4_impl(who, W + L.aq, W + L.as, W + L.w2q, W + L.w2s, L.split.data(), (int32_t)E, H, F, y, MX_BF16,
                        stream, reinterpret_cast<float*>(W + L.split2), L.split_bytes);
@@ -1593,15 +1596,22 @@ mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs
   st = gemm_fp4_impl(who, W + L.dyq, W + L.dys, S + L.w2cq, S + L.w2cs, L.split.data(), (int32_t)E, F, H, W + L.da32,
                      MX_F32, stream);
   if (st != MX_OK) return st;
-  // SwiGLU backward: dH1 (fp32 and rowwise MXFP4), dprobs
-  st = fp4_step(mx::launch_swiglu_bwd_fp4(reinterpret_cast<const float*>(W + L.da32),
-                                          reinterpret_cast<const uint16_t*>(S + L.h1), probs, R, F,
-                                          reinterpret_cast<float*>(W + L.dh1f), W + L.dhq, W + L.dhs, dprobs, stream),
-                who);
+  // SwiGLU backward: dH1 in both MXFP4 layouts from one pass over dA and the
+  // saved H1, and dprobs from per-tile partial sums
+  mx::Fp4SwigluArgs sw{};
+  sw.da = reinterpret_cast<const float*>(W + L.da32);
+  sw.h1 = reinterpret_cast<const uint16_t*>(S + L.h1);
+  sw.dprobs_part = dprobs ? reinterpret_cast<float*>(W + L.dpart) : nullptr;
+  sw.probs = probs;
+  sw.R = R;
+  sw.F = F;
+  st = fp4_step(mx::launch_swiglu_fp4_cast(true, sw, L.cg, W + L.dhcq, W + L.dhcs, W + L.dhq, W + L.dhs, stream), who);
   if (st != MX_OK) return st;
-  st = fp4_step(mx::launch_quantize_fp4_grouped(W + L.dh1f, true, R, 2 * F, L.cg, W + L.dhcq, W + L.dhcs, nullptr,
-                                                nullptr, stream), who);
-  if (st != MX_OK) return st;
+  if (dprobs) {
+    st = fp4_step(mx::launch_dprobs_reduce(reinterpret_cast<const float*>(W + L.dpart), dprobs, (int32_t)R,
+                                           (int32_t)(F / 64), nullptr, stream), who);
+    if (st != MX_OK) return st;
+  }
   // dgrad1: dX = dH1 . W1 (bf16) on the columnwise W1 copies [H, 2F]
   st = gemm_fp4_impl(who, W + L.dhq, W + L.dhs, S + L.w1cq, S + L.w1cs, L.split.data(), (int32_t)E, H, 2 * F, dx,
                      MX_BF16, stream, reinterpret_cast<float*>(W + L.split1), L.split_bytes);

@@ -111,11 +111,17 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
 // (id = 2 (row pair) n_ct + 2 ct + (row tile & 1)) and go to the XCDs in
 // chunks of 64: the two halves of every line are written by workgroups that
 // run at the same time on the same XCD and meet in its L2.
+// SRC: where the values come from -- the input x, or (T = float) the
+// ScaledSwiGLU forward or backward formed from Fp4SwigluArgs (the fused
+// MXFP4 MLP; cols = F resp. 2F). A 64-column tile of the backward lies wholly
+// in the dg half (columns below F) or the du half, F being a multiple of 128.
+enum Fp4Src : int { kSrcX = 0, kSrcSwigluFwd = 1, kSrcSwigluBwd = 2 };
 constexpr int kFp4ColTileRows = 128, kFp4CastChunk = 64;
-template <typename T>
+template <typename T, int SRC = kSrcX>
 __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s, uint8_t* q_row,
-                                                                   uint8_t* s_row, Fp4ColGroups gr, int64_t ldp) {
+                                                                   uint8_t* s_row, Fp4ColGroups gr, int64_t ldp,
+                                                                   Fp4SwigluArgs sw) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int VPT = 16 / (int)sizeof(T);   // values per 16-byte chunk
   constexpr int TC = 16 * VPT;               // tile columns
@@ -152,11 +158,87 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
   const bool col_ok = col < cols;              // cols % 32 == 0: a chunk is wholly in or out
 
   uint4 raw[TR / 16];
+  if constexpr (SRC == kSrcX) {
 #pragma unroll
-  for (int p = 0; p < TR / 16; ++p) {
-    const int rr = 16 * p + (tid >> 4);
-    raw[p] = make_uint4(0, 0, 0, 0);
-    if (lr0 + rr < m_g && col_ok) raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + col);
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      raw[p] = make_uint4(0, 0, 0, 0);
+      if (lr0 + rr < m_g && col_ok) raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + col);
+    }
+  } else if constexpr (SRC == kSrcSwigluFwd) {
+    // A = w * silu(g) * u of 4 columns per row piece, g and u from H1 (fp32)
+    static_assert(sizeof(T) == 4, "the SwiGLU sources are fp32");
+    const int64_t F = sw.F;
+    float4 gv[TR / 16], uv[TR / 16];
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      const float* hp = sw.h1f + (r0 + rr) * 2 * F + col;
+      gv[p] = ok ? *reinterpret_cast<const float4*>(hp) : make_float4(0.f, 0.f, 0.f, 0.f);
+      uv[p] = ok ? *reinterpret_cast<const float4*>(hp + F) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      const float w = ok && sw.probs != nullptr ? sw.probs[r0 + rr] : 1.0f;
+      const float g[4] = {gv[p].x, gv[p].y, gv[p].z, gv[p].w}, u[4] = {uv[p].x, uv[p].y, uv[p].z, uv[p].w};
+      uint32_t ab[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+        ab[i] = __float_as_uint(w * (g[i] * sig) * u[i]);
+      }
+      raw[p] = make_uint4(ab[0], ab[1], ab[2], ab[3]);
+      if (ok && sw.h1_out != nullptr) {
+        uint16_t* hp = sw.h1_out + (r0 + rr) * 2 * F + col;
+        *reinterpret_cast<uint2*>(hp) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+        *reinterpret_cast<uint2*>(hp + F) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+      }
+    }
+  } else {
+    // dg = dA w u s (1 + g (1 - s)) (columns below F) or du = dA w silu(g)
+    // (columns F + j), s = sigmoid(g), g and u from the saved bf16 H1; the
+    // dg tiles also sum dA silu(g) u over the tile's 64 columns of each row
+    static_assert(sizeof(T) == 4, "the SwiGLU sources are fp32");
+    const int64_t F = sw.F;
+    const bool is_g = c0 < F;                   // the tile's half (uniform)
+    const int64_t j = is_g ? col : col - F;
+    float4 dv[TR / 16];
+    uint2 gq[TR / 16], uq[TR / 16];
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      dv[p] = ok ? *reinterpret_cast<const float4*>(sw.da + (r0 + rr) * F + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint16_t* hp = sw.h1 + (r0 + rr) * 2 * F + j;
+      gq[p] = ok ? *reinterpret_cast<const uint2*>(hp) : make_uint2(0, 0);
+      uq[p] = ok && is_g ? *reinterpret_cast<const uint2*>(hp + F) : make_uint2(0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      const float w = ok && sw.probs != nullptr ? sw.probs[r0 + rr] : 1.0f;
+      const float d[4] = {dv[p].x, dv[p].y, dv[p].z, dv[p].w};
+      const float g[4] = {bf16_lo(gq[p].x), bf16_hi(gq[p].x), bf16_lo(gq[p].y), bf16_hi(gq[p].y)};
+      const float u[4] = {bf16_lo(uq[p].x), bf16_hi(uq[p].x), bf16_lo(uq[p].y), bf16_hi(uq[p].y)};
+      uint32_t vb[4];
+      float dp = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+        const float sl = g[i] * sg;
+        vb[i] = __float_as_uint(is_g ? d[i] * w * u[i] * sg * (1.0f + g[i] * (1.0f - sg)) : d[i] * w * sl);
+        dp += d[i] * sl * u[i];
+      }
+      raw[p] = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+      // the row's 16 chunks of this tile (lanes with the same tid / 16)
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) dp += xor_f32(dp, sh);
+      if (is_g && cc == 0 && ok && sw.dprobs_part != nullptr) sw.dprobs_part[(c0 / TC) * sw.R + r0 + rr] = dp;
+    }
   }
 #pragma unroll
   for (int p = 0; p < TR / 16; ++p) {
@@ -293,7 +375,7 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, uint8_
     const int64_t tiles = fp4_colwise_grid<uint16_t>(gr, cols);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, stream, xb, rows,
-                       cols, q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows);
+                       cols, q_col, s_col, fused ? q : nullptr, fused ? s : nullptr, gr, rows, Fp4SwigluArgs{});
   }
   return hipGetLastError();
 }
@@ -307,11 +389,27 @@ hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, 
   if (x_f32)
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, stream,
                        reinterpret_cast<const float*>(x), rows, cols, q_col, s_col, q_row, s_row, gr,
-                       (int64_t)gr.pcol0[gr.n]);
+                       (int64_t)gr.pcol0[gr.n], Fp4SwigluArgs{});
   else
     hipLaunchKernelGGL(quantize_fp4_colwise_kernel<uint16_t>, dim3((unsigned)tiles), dim3(256), 0, stream,
                        reinterpret_cast<const uint16_t*>(x), rows, cols, q_col, s_col, q_row, s_row, gr,
-                       (int64_t)gr.pcol0[gr.n]);
+                       (int64_t)gr.pcol0[gr.n], Fp4SwigluArgs{});
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fp4_cast(bool backward, const Fp4SwigluArgs& sw, const Fp4ColGroups& gr, uint8_t* q_col,
+                                  uint8_t* s_col, uint8_t* q_row, uint8_t* s_row, hipStream_t stream) {
+  const int64_t cols = backward ? 2 * sw.F : sw.F;
+  if (sw.F % 128 != 0) return hipErrorInvalidValue;
+  const int64_t tiles = fp4_colwise_grid<float>(gr, cols);
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (backward)
+    hipLaunchKernelGGL((quantize_fp4_colwise_kernel<float, kSrcSwigluBwd>), dim3((unsigned)tiles), dim3(256), 0,
+                       stream, nullptr, sw.R, cols, q_col, s_col, q_row, s_row, gr, (int64_t)gr.pcol0[gr.n], sw);
+  else
+    hipLaunchKernelGGL((quantize_fp4_colwise_kernel<float, kSrcSwigluFwd>), dim3((unsigned)tiles), dim3(256), 0,
+                       stream, nullptr, sw.R, cols, q_col, s_col, q_row, s_row, gr, (int64_t)gr.pcol0[gr.n], sw);
   return hipGetLastError();
 }
 
@@ -462,17 +560,15 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint
 // ---------------------------------------------------------------------------
 // ScaledSwiGLU around the MXFP4 GEMMs of the MLP ("Efficient MoE training for
 // biological foundation models", Key technical approaches item 3, at the 4-bit
-// MX format): GEMM1 leaves H1 = [g | u] in fp32, the forward forms
-// A = w * silu(g) * u in fp32 and requantizes it rowwise; the backward takes
-// dA in fp32 from dgrad2 and forms dH1 = [dg | du] and dprobs. silu and its
-// derivative use the same fp32 expressions as the MXFP8 epilogues.
+// MX format): GEMM1 leaves H1 = [g | u] in fp32 and dgrad2 leaves dA in fp32.
+// In training the columnwise cast forms A = w * silu(g) * u, resp.
+// dH1 = [dg | du] and dprobs, on the fly (launch_swiglu_fp4_cast); silu and
+// its derivative use the same fp32 expressions as the MXFP8 epilogues.
 
-// Forward: one thread per (row, 32-column block of F). Writes H1 in bf16
-// (h1, when the forward is kept for the backward), A in fp32 (a32, the input
-// of the columnwise cast; or null) and A's rowwise MXFP4 copy.
+// Inference forward: one thread per (row, 32-column block of F), A's rowwise
+// MXFP4 copy only.
 __global__ __launch_bounds__(256) void swiglu_fwd_fp4_kernel(const float* h1f, const float* probs, int64_t R,
-                                                             int64_t F, uint16_t* h1, float* a32, uint8_t* aq,
-                                                             uint8_t* as) {
+                                                             int64_t F, uint8_t* aq, uint8_t* as) {
   const int64_t nb = F / 32;
   const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (blk >= R * nb) return;
@@ -492,112 +588,18 @@ __global__ __launch_bounds__(256) void swiglu_fwd_fp4_kernel(const float* h1f, c
     const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
     a[i] = w * (g[i] * sig) * u[i];
   }
-  if (h1 != nullptr) {
-    uint4* hg = reinterpret_cast<uint4*>(h1 + r * 2 * F + 32 * b);
-    uint4* hu = reinterpret_cast<uint4*>(h1 + r * 2 * F + F + 32 * b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hg[i] = make_uint4(pack_bf16x2(g[8 * i], g[8 * i + 1]), pack_bf16x2(g[8 * i + 2], g[8 * i + 3]),
-                         pack_bf16x2(g[8 * i + 4], g[8 * i + 5]), pack_bf16x2(g[8 * i + 6], g[8 * i + 7]));
-      hu[i] = make_uint4(pack_bf16x2(u[8 * i], u[8 * i + 1]), pack_bf16x2(u[8 * i + 2], u[8 * i + 3]),
-                         pack_bf16x2(u[8 * i + 4], u[8 * i + 5]), pack_bf16x2(u[8 * i + 6], u[8 * i + 7]));
-    }
-  }
-  if (a32 != nullptr) {
-    float4* ap = reinterpret_cast<float4*>(a32 + r * F + 32 * b);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ap[i] = make_float4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
-  }
   uint4 codes;
   const uint32_t sc = fp4_block(a, codes);
   *reinterpret_cast<uint4*>(aq + r * (F / 2) + 16 * b) = codes;
   as[r * nb + b] = (uint8_t)sc;
 }
 
-// Backward: one workgroup per row; thread t takes the row's 32-column blocks
-// t, t + 256, ... of F. dg = dA*w*u*s*(1 + g*(1 - s)), du = dA*w*g*s with
-// s = sigmoid(g) and g, u from the saved bf16 H1; dprobs = sum_f dA*g*s*u
-// (partial sums per thread, then a tree over the workgroup). Writes dH1 in
-// fp32 (dh1f, the input of the columnwise cast; or null) and its rowwise
-// MXFP4 copy (dg blocks at columns [0, F), du blocks at [F, 2F)).
-__global__ __launch_bounds__(256) void swiglu_bwd_fp4_kernel(const float* da, const uint16_t* h1, const float* probs,
-                                                             int64_t F, float* dh1f, uint8_t* dq, uint8_t* ds,
-                                                             float* dprobs) {
-  __shared__ float red[256];
-  const int64_t r = blockIdx.x, nb = F / 32;
-  const float w = probs != nullptr ? probs[r] : 1.0f;
-  float dp = 0.0f;
-  for (int64_t b = threadIdx.x; b < nb; b += 256) {
-    const float4* dap = reinterpret_cast<const float4*>(da + r * F + 32 * b);
-    const uint4* gp = reinterpret_cast<const uint4*>(h1 + r * 2 * F + 32 * b);
-    const uint4* up = reinterpret_cast<const uint4*>(h1 + r * 2 * F + F + 32 * b);
-    float d[32], g[32], u[32], dg[32], du[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = dap[i];
-      d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 gv = gp[i], uv = up[i];
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        g[8 * i + 2 * j] = bf16_lo(gw[j]);
-        g[8 * i + 2 * j + 1] = bf16_hi(gw[j]);
-        u[8 * i + 2 * j] = bf16_lo(uw[j]);
-        u[8 * i + 2 * j + 1] = bf16_hi(uw[j]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
-      const float sl = g[i] * sg;
-      dg[i] = d[i] * w * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
-      du[i] = d[i] * w * sl;
-      dp += d[i] * sl * u[i];
-    }
-    if (dh1f != nullptr) {
-      float4* pg = reinterpret_cast<float4*>(dh1f + r * 2 * F + 32 * b);
-      float4* pu = reinterpret_cast<float4*>(dh1f + r * 2 * F + F + 32 * b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pg[i] = make_float4(dg[4 * i], dg[4 * i + 1], dg[4 * i + 2], dg[4 * i + 3]);
-        pu[i] = make_float4(du[4 * i], du[4 * i + 1], du[4 * i + 2], du[4 * i + 3]);
-      }
-    }
-    uint4 codes;
-    uint32_t sc = fp4_block(dg, codes);
-    *reinterpret_cast<uint4*>(dq + r * F + 16 * b) = codes;
-    ds[r * 2 * nb + b] = (uint8_t)sc;
-    sc = fp4_block(du, codes);
-    *reinterpret_cast<uint4*>(dq + r * F + F / 2 + 16 * b) = codes;
-    ds[r * 2 * nb + nb + b] = (uint8_t)sc;
-  }
-  red[threadIdx.x] = dp;
-  __syncthreads();
-#pragma unroll
-  for (int off = 128; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0 && dprobs != nullptr) dprobs[r] = red[0];
-}
-
-hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint16_t* h1, float* a32,
-                                 uint8_t* aq, uint8_t* as, hipStream_t stream) {
+hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint8_t* aq, uint8_t* as,
+                                 hipStream_t stream) {
   const int64_t blocks = R * (F / 32);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(swiglu_fwd_fp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream, h1f, probs,
-                     R, F, h1, a32, aq, as);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_bwd_fp4(const float* da, const uint16_t* h1, const float* probs, int64_t R, int64_t F,
-                                 float* dh1f, uint8_t* dq, uint8_t* ds, float* dprobs, hipStream_t stream) {
-  if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_bwd_fp4_kernel, dim3((unsigned)R), dim3(256), 0, stream, da, h1, probs, F, dh1f, dq, ds,
-                     dprobs);
+                     R, F, aq, as);
   return hipGetLastError();
 }
 

@@ -228,6 +228,24 @@ struct Fp4ColGroups {
   int64_t row0[kMaxGroups + 1];
   int64_t pcol0[kMaxGroups + 1];
 };
+// ScaledSwiGLU of the MXFP4 MLP fused into the columnwise cast: the values
+// cast are formed on the fly instead of read. Forward: A = w * silu(g) * u
+// [R, F] from GEMM1's fp32 H1 = [g | u] [R, 2F], H1 written in bf16 to h1_out
+// (or not, when null). Backward: dH1 = [dg | du] [R, 2F] from dgrad2's fp32
+// dA [R, F] and the saved bf16 H1, and per-row partial sums of dprobs
+// (sum over f of dA * silu(g) * u) to dprobs_part [F / 64, R] (summed by
+// launch_dprobs_reduce). probs null means routing weights 1.
+struct Fp4SwigluArgs {
+  const float* h1f;          // forward: H1 [R, 2F] fp32
+  uint16_t* h1_out;          // forward: H1 [R, 2F] bf16 (or null)
+  const float* da;           // backward: dA [R, F] fp32
+  const uint16_t* h1;        // backward: saved H1 [R, 2F] bf16
+  float* dprobs_part;        // backward: [F / 64, R] (or null)
+  const float* probs;        // [R] or null
+  int64_t R, F;
+};
+hipError_t launch_swiglu_fp4_cast(bool backward, const Fp4SwigluArgs& sw, const Fp4ColGroups& gr, uint8_t* q_col,
+                                  uint8_t* s_col, uint8_t* q_row, uint8_t* s_row, hipStream_t stream);
 // x is bf16 or (x_f32) fp32 [rows, cols]; q_row / s_row (or null) receive the
 // rowwise copy of the same pass.
 hipError_t launch_quantize_fp4_grouped(const void* x, bool x_f32, int64_t rows, int64_t cols, const Fp4ColGroups& gr,
@@ -244,15 +262,11 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, uint
 hipError_t launch_gemm_nvfp4(const uint8_t* a, const uint8_t* as, const float* a_amax, const uint8_t* b,
                              const uint8_t* bs, const float* b_amax, const Fp4Groups& gr, int64_t N, int64_t K,
                              void* c, int32_t c_f32, hipStream_t stream);
-// ScaledSwiGLU of the MXFP4 MLP (mx_fp4.hip). Forward: H1 fp32 [R, 2F] ->
-// H1 bf16 (h1, or null), A fp32 (a32, or null) and A's rowwise MXFP4 copy
-// [R, F/2] + [R, F/32]. Backward: dA fp32 [R, F], H1 bf16 -> dH1 fp32 (dh1f,
-// or null), dH1's rowwise MXFP4 copy [R, F] + [R, F/16], dprobs (or null).
-// F % 32 == 0; probs null = all 1.
-hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint16_t* h1, float* a32,
-                                 uint8_t* aq, uint8_t* as, hipStream_t stream);
-hipError_t launch_swiglu_bwd_fp4(const float* da, const uint16_t* h1, const float* probs, int64_t R, int64_t F,
-                                 float* dh1f, uint8_t* dq, uint8_t* ds, float* dprobs, hipStream_t stream);
+// ScaledSwiGLU forward of the MXFP4 MLP at inference (mx_fp4.hip): H1 fp32
+// [R, 2F] -> A's rowwise MXFP4 copy [R, F/2] + [R, F/32]; F % 32 == 0; probs
+// null = all 1. (Training runs launch_swiglu_fp4_cast.)
+hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R, int64_t F, uint8_t* aq, uint8_t* as,
+                                 hipStream_t stream);
 // MXFP4 group-K product C_g (+)= A[:, K_g] . B[:, K_g]^T (fp32), K_g =
 // [k0[g], k0[g+1]) in values (multiples of 32): A [M, k0[n]] and B
 // [N, k0[n]] rowwise-packed MXFP4 (the columnwise layouts of two routed
