@@ -628,6 +628,7 @@ hipError_t launch_swiglu_fwd_fp4(const float* h1f, const float* probs, int64_t R
 // on 16 different 16-byte bank groups. One barrier per k-tile: the next k-tile's DMA is in flight during
 // this one's MFMAs.
 constexpr int kF4SubM = 4, kF4SubN = 4;     // wave tile: MFMA tiles of 32 x 32
+constexpr int kF4BandM = 4;                 // group-K: m-tiles per band of the tile raster
 constexpr int kF4KTile = 128;               // bytes of codes per row and k-tile
 static_assert(kFp4GemmTileM == 2 * 32 * kF4SubM && kFp4GemmTileN == 2 * 32 * kF4SubN, "tile = 2 x 2 waves");
 
@@ -682,7 +683,13 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       grp = (int)(id / per_group);
       rem = id - grp * per_group;
     }
-    const int64_t mt = rem / n_tiles_n, nt = rem - mt * n_tiles_n;
+    // bands of kF4BandM m-tiles x all n-tiles, m fastest inside a band: a
+    // chunk of 32 ids is 4 m-tiles x 8 n-tiles, which share their A and B
+    // rows in the XCD's L2
+    const int64_t m_tiles = (M + TM - 1) / TM, per_band = kF4BandM * n_tiles_n;
+    const int64_t band = rem / per_band, in_band = rem - band * per_band;
+    const int64_t band_h = min<int64_t>(kF4BandM, m_tiles - band * kF4BandM);
+    const int64_t mt = band * kF4BandM + in_band % band_h, nt = in_band / band_h;
     row_end = M;
     am0 = mt * TM;
     bn0 = nt * TN;
