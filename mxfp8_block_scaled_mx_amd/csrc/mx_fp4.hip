@@ -717,18 +717,32 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   const int64_t brow0 = GK ? bn0 : grp * N + bn0;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + am0 * ldq + kbeg / 2, (amv - 1) * ldq + klen / 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + brow0 * ldq + kbeg / 2, (bnv - 1) * ldq + klen / 2);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(as + am0 * lds + kbeg / kVPS, (amv - 1) * lds + klen / kVPS);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bs + brow0 * lds + kbeg / kVPS, (bnv - 1) * lds + klen / kVPS);
+  // a row's 8 scales of a k-tile: one aligned 8-byte load (sc_dword). The k
+  // range must also be whole k-tiles: the last row's load would otherwise
+  // reach past the resource's extent and come back as zero scales. (NVFP4: K
+  // is a multiple of 128, so a lane's 8 scales of a k-tile are always one
+  // aligned 8-byte piece.) Group-K ranges start at any multiple of 32 values,
+  // so a group's scales start at any byte: then (sc_shift) the two aligned
+  // 8-byte loads around the 8 bytes and a per-lane byte shift, through
+  // resources over the whole scale arrays (offsets from their bases, which
+  // the range check covers). A load that reaches past the extent reads
+  // zeros, also for its bytes inside it, so a lane whose 16 bytes do not
+  // all lie in the array (the array's last row or two) takes byte loads.
+  // Else byte loads throughout.
+  const bool sc_dword = NV || ((lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0);
+  const bool sc_shift = GK && !sc_dword &&
+                        ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) & 7) == 0 &&
+                        M * lds < ((int64_t)1 << 32) && N * lds < ((int64_t)1 << 32);
+  const int64_t sa_len = sc_shift ? M * lds : (amv - 1) * lds + klen / kVPS;
+  const int64_t sb_len = sc_shift ? N * lds : (bnv - 1) * lds + klen / kVPS;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sc_shift ? as : as + am0 * lds + kbeg / kVPS, sa_len);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sc_shift ? bs : bs + brow0 * lds + kbeg / kVPS, sb_len);
+  const uint32_t sa_off0 = sc_shift ? (uint32_t)(am0 * lds + kbeg / 32) : 0u;
+  const uint32_t sb_off0 = sc_shift ? (uint32_t)(brow0 * lds + kbeg / 32) : 0u;
   const int ksteps = (int)((klen + 63) / 64), ktiles = (ksteps + 3) / 4;
   // k-tiles [t_lo, t_hi) of this work unit
   const int t_lo = SPLIT ? part * ktiles / sp.parts : 0;
   const int t_hi = SPLIT ? (part + 1) * ktiles / sp.parts : ktiles;
-  // a row's 8 scales of a k-tile: one aligned 8-byte load. The k range must
-  // also be whole k-tiles: the last row's load would otherwise reach past
-  // the resource's extent and come back as zero scales.
-  // (NVFP4: K is a multiple of 128, so a lane's 8 scales of a k-tile are
-  // always one aligned 8-byte piece)
-  const bool sc_dword = NV || ((lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0);
 
   // global -> LDS by buffer DMA, 1 KB (8 rows) per instruction: lane L
   // fills chunk L % 8 of row 8 blk + L / 8 with global chunk
@@ -755,8 +769,20 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // blocks 16 t + 8 h .. + 7, those of the lane's half of the k-tile)
   u32x2 sca[SM], scb[SN];
   const uint32_t sc_k = NV ? 8 * h : 0;
-  auto scale_pair = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off) __attribute__((always_inline)) -> u32x2 {
+  auto scale_pair = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int64_t len)
+      __attribute__((always_inline)) -> u32x2 {
     if (sc_dword) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const uint32_t al = off & ~7u, sh = off & 7u;
+    if (sc_shift && (int64_t)al + 16 <= len) {
+      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, al, 0, 0);
+      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(r, al + 8, 0, 0);
+      const bool up = sh >= 4;                // the 8 bytes start in the second dword
+      const uint32_t a0 = up ? lo.y : lo.x, a1 = up ? hi.x : lo.y, a2 = up ? hi.y : hi.x;
+      u32x2 w;
+      w.x = __builtin_amdgcn_alignbyte(a1, a0, sh & 3u);
+      w.y = __builtin_amdgcn_alignbyte(a2, a1, sh & 3u);
+      return w;
+    }
     u32x2 v;
     v.x = 0; v.y = 0;
 #pragma unroll
@@ -769,10 +795,12 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   auto load_scales = [&](int t, u32x2 (&xa)[SM], u32x2 (&xb)[SN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < SM; ++i)
-      xa[i] = scale_pair(rsa, (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + (NV ? 16 : 8) * t + sc_k));
+      xa[i] = scale_pair(rsa, sa_off0 + (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + (NV ? 16 : 8) * t + sc_k),
+                         sa_len);
 #pragma unroll
     for (int j = 0; j < SN; ++j)
-      xb[j] = scale_pair(rsb, (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k));
+      xb[j] = scale_pair(rsb, sb_off0 + (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k),
+                         sb_len);
   };
   auto frag = [&](const uint8_t* base, int r, int s) __attribute__((always_inline)) -> v8i {
     const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ ((r >> 1) & 7)) << 4));
