@@ -491,6 +491,47 @@ MX_API mx_status grouped_mlp_bwd_fp4(const mx_mlp_dims* dims, const int64_t* spl
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Cached MXFP4 weights: the cached-weight form of the MXFP4 MLP, as
+ * grouped_mlp_quantize_weights / grouped_mlp_fwd_cached / grouped_mlp_bwd_cached
+ * are for the MXFP8 MLP (quantized initialization of the Llama 3 recipe
+ * page's MXFP8 throughput section, applied to the 4-bit layer of its
+ * Layer-Wise Precision section). The per-expert weight casts of
+ * grouped_mlp_fwd_fp4 leave the step: a training loop casts its bf16 master
+ * weights once after each optimizer update and runs forward and backward on
+ * the cached copies, which hold exactly the codes and scales
+ * grouped_mlp_fwd_fp4 would make from the same weights, so the results are
+ * bit-identical.
+ *
+ * grouped_mlp_fp4_weight_cache_bytes -- size of the cache for E, H, F (rows
+ * and split are not used; the other dims rules of grouped_mlp_fp4_sizes hold).
+ * grouped_mlp_fp4_quantize_weights -- cast w1 bf16 [E, 2F, H] and w2 bf16
+ * [E, H, F] into `cache` (caller-owned device buffer, 256-byte aligned, at
+ * least grouped_mlp_fp4_weight_cache_bytes), rowwise and each expert's
+ * columnwise copy. Async on `stream`. The cache layout is private to the
+ * library; it stays valid until the weights change. Errors: MX_EINVAL,
+ * MX_ESHAPE, MX_EALIGN, MX_EWORKSPACE (cache too small), MX_EHIP.
+ * grouped_mlp_fwd_fp4_cached / grouped_mlp_bwd_fp4_cached --
+ * grouped_mlp_fwd_fp4 and grouped_mlp_bwd_fp4 with the weights read from a
+ * filled cache instead of being cast; same workspace and saved sizes
+ * (grouped_mlp_fp4_sizes) and errors, plus the cache checks above. The saved
+ * buffer written by grouped_mlp_fwd_fp4_cached holds no weight copies and must
+ * be consumed by grouped_mlp_bwd_fp4_cached with the same cache.
+ */
+MX_API mx_status grouped_mlp_fp4_weight_cache_bytes(const mx_mlp_dims* dims, size_t* bytes);
+MX_API mx_status grouped_mlp_fp4_quantize_weights(const mx_mlp_dims* dims, const void* w1, const void* w2,
+                                                  void* cache, size_t cache_bytes, void* stream);
+MX_API mx_status grouped_mlp_fwd_fp4_cached(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                            const void* x, const float* probs, const void* cache,
+                                            size_t cache_bytes, void* y, void* saved, size_t saved_bytes,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+MX_API mx_status grouped_mlp_bwd_fp4_cached(const mx_mlp_dims* dims, const int64_t* split_sizes,
+                                            const void* dy, const float* probs, const void* cache,
+                                            size_t cache_bytes, const void* saved, size_t saved_bytes,
+                                            void* dx, float* dprobs, float* dw1, float* dw2,
+                                            int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/*
  * mx_quantize_fp4_colwise_grouped -- columnwise MXFP4 of a routed activation
  * with per-expert padding, the layout of the 4-bit weight gradient (the
  * MXFP4 form of the grouped columnwise MXFP8 layout above; MXFP4 as in

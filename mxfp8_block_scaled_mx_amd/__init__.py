@@ -135,6 +135,15 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.grouped_mlp_fwd_fp4.restype = ctypes.c_int
     L.grouped_mlp_fwd_fp4.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.grouped_mlp_fp4_weight_cache_bytes.restype = ctypes.c_int
+    L.grouped_mlp_fp4_weight_cache_bytes.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(sz)]
+    L.grouped_mlp_fp4_quantize_weights.restype = ctypes.c_int
+    L.grouped_mlp_fp4_quantize_weights.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, sz, vp]
+    L.grouped_mlp_fwd_fp4_cached.restype = ctypes.c_int
+    L.grouped_mlp_fwd_fp4_cached.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, sz, vp, sz, vp]
+    L.grouped_mlp_bwd_fp4_cached.restype = ctypes.c_int
+    L.grouped_mlp_bwd_fp4_cached.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp,
+                                             i32, vp, sz, vp]
     L.grouped_mlp_bwd_fp4.restype = ctypes.c_int
     L.grouped_mlp_bwd_fp4.argtypes = [ctypes.POINTER(_Dims), p64, vp, vp, vp, sz, vp, vp, vp, vp, i32,
                                       vp, sz, vp]
@@ -277,13 +286,27 @@ def mlp_intermediates(E: int, R: int, H: int, F: int, split_sizes) -> dict:
 
 class MLPState:
     """What the fused forward keeps for the backward (a caller-owned buffer);
-    fmt is the block format of the forward that filled it."""
+    fmt is the block format of the forward that filled it, cache the weight
+    cache it read (None: it cast the weights itself and saved their
+    columnwise copies, which a cached forward does not)."""
 
-    def __init__(self, saved: torch.Tensor, dims, split_sizes, fmt: str = "mxfp8"):
+    def __init__(self, saved: torch.Tensor, dims, split_sizes, fmt: str = "mxfp8", cache=None):
         self.saved = saved
         self.dims = dims
         self.split_sizes = list(int(s) for s in split_sizes)
         self.fmt = fmt
+        self.cache = cache
+
+
+def _check_state(state: MLPState, fmt: str, cache, who: str):
+    """The backward `who` takes the state of a forward of block format fmt
+    that used the weight cache `cache` (None: the uncached forward)."""
+    if state.fmt != fmt:
+        raise ValueError(f"{who} needs the state of an {fmt.upper()} forward, not {state.fmt.upper()}")
+    if cache is None and state.cache is not None:
+        raise ValueError(f"{who}: the state comes from a cached forward; use the *_cached backward with its cache")
+    if cache is not None and state.cache is not cache:
+        raise ValueError(f"{who}: the state was not made by the cached forward with this weight cache")
 
 
 def _expect_all(items):
@@ -398,8 +421,7 @@ def grouped_mlp_bwd_gather(dy_tokens, row_token, probs, state: MLPState, *, dw1=
     """grouped_mlp_bwd with dY gathered from dy_tokens [T, H] through row_token
     by its cast. Returns (dx [R, H] bf16 per routed row, dprobs, dw1, dw2)."""
     L = load()
-    if state.fmt != "mxfp8":
-        raise ValueError("grouped_mlp_bwd_gather needs the state of an MXFP8 forward")
+    _check_state(state, "mxfp8", None, "grouped_mlp_bwd_gather")
     E, R, H, F = state.dims
     if dy_tokens.dim() != 2:
         raise ValueError("grouped_mlp_bwd_gather: dy_tokens must be [T, H]")
@@ -430,8 +452,7 @@ def grouped_mlp_bwd(dy, probs, state: MLPState, *, dw1=None, dw2=None, accumulat
     """Fused grouped MLP backward. Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32).
     With accumulate=True, dw1/dw2 (fp32 main grads) are added into."""
     L = load()
-    if state.fmt != "mxfp8":
-        raise ValueError("grouped_mlp_bwd needs the state of an MXFP8 forward")
+    _check_state(state, "mxfp8", None, "grouped_mlp_bwd")
     E, R, H, F = state.dims
     _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
                 + _mlp_grads(E, R, H, F, dw1, dw2))
@@ -492,8 +513,7 @@ def grouped_mlp_bwd_fp4(dy, probs, state: MLPState, *, dw1=None, dw2=None, accum
     """Backward of grouped_mlp_fwd_fp4 (grouped_mlp_bwd_fp4). Returns
     (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
     L = load()
-    if state.fmt != "mxfp4":
-        raise ValueError("grouped_mlp_bwd_fp4 needs the state of grouped_mlp_fwd_fp4")
+    _check_state(state, "mxfp4", None, "grouped_mlp_bwd_fp4")
     E, R, H, F = state.dims
     _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
                 + _mlp_grads(E, R, H, F, dw1, dw2))
@@ -524,12 +544,17 @@ def grouped_mlp_weight_cache_bytes(E: int, H: int, F: int) -> int:
 
 
 class WeightCache:
-    """MXFP8 copies of w1 [E,2F,H] and w2 [E,H,F] in both layouts (a
-    caller-owned device buffer filled by grouped_mlp_quantize_weights)."""
+    """MXFP8 (fmt "mxfp8") or MXFP4 ("mxfp4") copies of w1 [E,2F,H] and w2
+    [E,H,F] in both layouts (a caller-owned device buffer filled by
+    grouped_mlp_quantize_weights, resp. grouped_mlp_fp4_quantize_weights)."""
 
-    def __init__(self, E: int, H: int, F: int, device="cuda"):
+    def __init__(self, E: int, H: int, F: int, device="cuda", fmt: str = "mxfp8"):
+        if fmt not in ("mxfp8", "mxfp4"):
+            raise ValueError(f"WeightCache: unknown format {fmt!r}")
         self.ehf = (int(E), int(H), int(F))
-        self.buf = _byte_buffer(grouped_mlp_weight_cache_bytes(E, H, F), device)
+        self.fmt = fmt
+        n = grouped_mlp_weight_cache_bytes(E, H, F) if fmt == "mxfp8" else grouped_mlp_fp4_weight_cache_bytes(E, H, F)
+        self.buf = _byte_buffer(n, device)
 
 
 def grouped_mlp_quantize_weights(w1, w2, cache: WeightCache | None = None, stream=None) -> WeightCache:
@@ -543,8 +568,8 @@ def grouped_mlp_quantize_weights(w1, w2, cache: WeightCache | None = None, strea
     _expect_all([(w1, (E, 2 * F, H), torch.bfloat16, "w1", False), (w2, (E, H, F), torch.bfloat16, "w2", False)])
     if cache is None:
         cache = WeightCache(E, H, F, device=w1.device)
-    if cache.ehf != (E, H, F):
-        raise ValueError(f"weight cache is for (E, H, F) = {cache.ehf}, weights are {(E, H, F)}")
+    if cache.ehf != (E, H, F) or cache.fmt != "mxfp8":
+        raise ValueError(f"weight cache is {cache.fmt} for (E, H, F) = {cache.ehf}, weights are MXFP8 {(E, H, F)}")
     _check(L.grouped_mlp_quantize_weights(ctypes.byref(_dims(E, 0, H, F)), _ptr(w1), _ptr(w2),
                                           _ptr(cache.buf), cache.buf.numel(), _stream(stream)))
     return cache
@@ -558,8 +583,8 @@ def grouped_mlp_fwd_cached(x, probs, cache: WeightCache, split_sizes, *, trainin
         raise ValueError("grouped_mlp_fwd_cached: x must be [R, H]")
     R, H = x.shape
     E, Hc, F = cache.ehf
-    if Hc != H:
-        raise ValueError(f"x has hidden {H}, the weight cache {Hc}")
+    if Hc != H or cache.fmt != "mxfp8":
+        raise ValueError(f"x has hidden {H}; the weight cache is {cache.fmt} with hidden {Hc}")
     _mlp_inputs(E, R, H, F, split_sizes, x, probs=probs, extra=[(out, (R, H), torch.bfloat16, "out", True)])
     fws, sv, _ = mlp_sizes(E, R, H, F, split_sizes)
     if workspace is None or workspace.numel() < fws:
@@ -570,7 +595,7 @@ def grouped_mlp_fwd_cached(x, probs, cache: WeightCache, split_sizes, *, trainin
                                     _ptr(probs), _ptr(cache.buf), cache.buf.numel(), _ptr(y), _ptr(saved),
                                     0 if saved is None else saved.numel(), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
-    state = MLPState(saved, (E, R, H, F), split_sizes) if training else None
+    state = MLPState(saved, (E, R, H, F), split_sizes, cache=cache) if training else None
     return y, state
 
 
@@ -579,8 +604,9 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
     """grouped_mlp_bwd after grouped_mlp_fwd_cached (same cache).
     Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
     L = load()
-    if state.fmt != "mxfp8":
-        raise ValueError("grouped_mlp_bwd_cached needs the state of an MXFP8 forward")
+    if cache.fmt != "mxfp8":
+        raise ValueError("grouped_mlp_bwd_cached needs an MXFP8 weight cache")
+    _check_state(state, "mxfp8", cache, "grouped_mlp_bwd_cached")
     E, R, H, F = state.dims
     _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
                 + _mlp_grads(E, R, H, F, dw1, dw2))
@@ -600,6 +626,87 @@ def grouped_mlp_bwd_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw
                                     _ptr(state.saved), state.saved.numel(), _ptr(dx), _ptr(dprobs),
                                     _ptr(dw1), _ptr(dw2), int(accumulate), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
+    return dx, dprobs, dw1, dw2
+
+
+def grouped_mlp_fp4_weight_cache_bytes(E: int, H: int, F: int) -> int:
+    """Bytes of the MXFP4 weight cache for E experts, hidden H, ffn F."""
+    L = load()
+    n = ctypes.c_size_t()
+    _check(L.grouped_mlp_fp4_weight_cache_bytes(ctypes.byref(_dims(E, 0, H, F)), ctypes.byref(n)))
+    return n.value
+
+
+def grouped_mlp_fp4_quantize_weights(w1, w2, cache: WeightCache | None = None, stream=None) -> WeightCache:
+    """Cast the bf16 master weights into an MXFP4 weight cache (allocated
+    when None); run once after each optimizer update, then use the
+    grouped_mlp_*_fp4_cached calls."""
+    L = load()
+    if w1.dim() != 3:
+        raise ValueError("grouped_mlp_fp4_quantize_weights: w1 must be [E, 2F, H]")
+    E, F2, H = w1.shape
+    F = F2 // 2
+    _expect_all([(w1, (E, 2 * F, H), torch.bfloat16, "w1", False), (w2, (E, H, F), torch.bfloat16, "w2", False)])
+    if cache is None:
+        cache = WeightCache(E, H, F, device=w1.device, fmt="mxfp4")
+    if cache.ehf != (E, H, F) or cache.fmt != "mxfp4":
+        raise ValueError(f"weight cache is {cache.fmt} for (E, H, F) = {cache.ehf}, weights are MXFP4 {(E, H, F)}")
+    _check(L.grouped_mlp_fp4_quantize_weights(ctypes.byref(_dims(E, 0, H, F)), _ptr(w1), _ptr(w2),
+                                              _ptr(cache.buf), cache.buf.numel(), _stream(stream)))
+    return cache
+
+
+def grouped_mlp_fwd_fp4_cached(x, probs, cache: WeightCache, split_sizes, *, training: bool = True,
+                               workspace=None, out=None, stream=None):
+    """grouped_mlp_fwd_fp4 on the cached MXFP4 weights. Returns (y, MLPState or None)."""
+    L = load()
+    if x.dim() != 2:
+        raise ValueError("grouped_mlp_fwd_fp4_cached: x must be [R, H]")
+    R, H = x.shape
+    E, Hc, F = cache.ehf
+    if Hc != H or cache.fmt != "mxfp4":
+        raise ValueError(f"x has hidden {H}; the weight cache is {cache.fmt} with hidden {Hc}")
+    _mlp_inputs(E, R, H, F, split_sizes, x, probs=probs, extra=[(out, (R, H), torch.bfloat16, "out", True)])
+    fws, sv, _ = mlp_fp4_sizes(E, R, H, F, split_sizes)
+    if workspace is None or workspace.numel() < fws:
+        workspace = _byte_buffer(fws, x.device)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=x.device) if out is None else out
+    saved = _byte_buffer(sv, x.device) if training else None
+    _check(L.grouped_mlp_fwd_fp4_cached(ctypes.byref(_dims(E, R, H, F)), _i64_array(split_sizes), _ptr(x),
+                                        _ptr(probs), _ptr(cache.buf), cache.buf.numel(), _ptr(y), _ptr(saved),
+                                        0 if saved is None else saved.numel(), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
+    state = MLPState(saved, (E, R, H, F), split_sizes, fmt="mxfp4", cache=cache) if training else None
+    return y, state
+
+
+def grouped_mlp_bwd_fp4_cached(dy, probs, state: MLPState, cache: WeightCache, *, dw1=None, dw2=None,
+                               accumulate: bool = False, want_dprobs: bool = True, workspace=None, stream=None):
+    """grouped_mlp_bwd_fp4 after grouped_mlp_fwd_fp4_cached (same cache).
+    Returns (dx bf16, dprobs fp32 or None, dw1 fp32, dw2 fp32)."""
+    L = load()
+    if cache.fmt != "mxfp4":
+        raise ValueError("grouped_mlp_bwd_fp4_cached needs an MXFP4 weight cache")
+    _check_state(state, "mxfp4", cache, "grouped_mlp_bwd_fp4_cached")
+    E, R, H, F = state.dims
+    _expect_all([(dy, (R, H), torch.bfloat16, "dy", False), (probs, (R,), torch.float32, "probs", True)]
+                + _mlp_grads(E, R, H, F, dw1, dw2))
+    _, _, bws = mlp_fp4_sizes(E, R, H, F, state.split_sizes)
+    if workspace is None or workspace.numel() < bws:
+        workspace = _byte_buffer(bws, dy.device)
+    dev = dy.device
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dprobs = torch.empty((R,), dtype=torch.float32, device=dev) if want_dprobs else None
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, H), dtype=torch.float32, device=dev)
+        accumulate = False if dw2 is None else accumulate
+    if dw2 is None:
+        dw2 = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    _check(L.grouped_mlp_bwd_fp4_cached(ctypes.byref(_dims(E, R, H, F)), _i64_array(state.split_sizes),
+                                        _ptr(dy), _ptr(probs), _ptr(cache.buf), cache.buf.numel(),
+                                        _ptr(state.saved), state.saved.numel(), _ptr(dx), _ptr(dprobs),
+                                        _ptr(dw1), _ptr(dw2), int(accumulate), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
     return dx, dprobs, dw1, dw2
 
 

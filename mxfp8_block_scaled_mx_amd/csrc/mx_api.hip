@@ -1521,9 +1521,69 @@ mx_status fp4_mlp_layout(const mx_mlp_dims* d, const int64_t* split, Fp4MlpLayou
 
 mx_status fp4_step(hipError_t e, const char* what) { return e == hipSuccess ? MX_OK : hip_fail(e, what); }
 
+// MXFP4 weight copies: rowwise W1 [E*2F, H] and W2 [E*H, F] for the forward
+// GEMMs, and each expert's columnwise W1 [H, 2F] and W2 [F, H] for the dgrad
+// GEMMs (codes two per byte, one scale byte per 32 values).
+struct Fp4WeightCopies {
+  const uint8_t *w1q, *w1s, *w2q, *w2s;
+  const uint8_t *w1cq, *w1cs, *w2cq, *w2cs;
+};
+
+// Layout of an MXFP4 weight cache (grouped_mlp_fp4_quantize_weights): the
+// four copies back to back, 256-byte aligned regions; offsets depend on E, H,
+// F only.
+struct Fp4WeightCacheLayout {
+  size_t w1q, w1s, w2q, w2s, w1cq, w1cs, w2cq, w2cs, total;
+};
+
+Fp4WeightCacheLayout fp4_weight_cache_layout(int64_t E, int64_t H, int64_t F) {
+  Fp4WeightCacheLayout W;
+  size_t c = 0;
+  W.w1q = take(c, E * 2 * F * H / 2); W.w1s = take(c, E * 2 * F * H / 32);
+  W.w2q = take(c, E * H * F / 2); W.w2s = take(c, E * H * F / 32);
+  W.w1cq = take(c, E * H * 2 * F / 2); W.w1cs = take(c, E * H * 2 * F / 32);
+  W.w2cq = take(c, E * F * H / 2); W.w2cs = take(c, E * F * H / 32);
+  W.total = c;
+  return W;
+}
+
+Fp4WeightCopies fp4_weight_cache_copies(const Fp4WeightCacheLayout& W, const void* base) {
+  return {at(base, W.w1q), at(base, W.w1s), at(base, W.w2q), at(base, W.w2s),
+          at(base, W.w1cq), at(base, W.w1cs), at(base, W.w2cq), at(base, W.w2cs)};
+}
+
+// Both MXFP4 layouts of the bf16 master weights, one pass per expert and
+// weight: rowwise into (w1q, w1s, w2q, w2s), columnwise into (w1cq, ...).
+mx_status fp4_quantize_weights_into(int64_t E, int64_t H, int64_t F, const void* w1, const void* w2, uint8_t* w1q,
+                                    uint8_t* w1s, uint8_t* w2q, uint8_t* w2s, uint8_t* w1cq, uint8_t* w1cs,
+                                    uint8_t* w2cq, uint8_t* w2cs, hipStream_t stream, const char* who) {
+  const uint8_t* w1b = static_cast<const uint8_t*>(w1);
+  const uint8_t* w2b = static_cast<const uint8_t*>(w2);
+  for (int64_t e = 0; e < E; ++e) {
+    mx_status st = fp4_step(mx::launch_quantize_fp4(w1b + e * 2 * F * H * 2, 2 * F, H, w1q + e * 2 * F * H / 2,
+                                                    w1s + e * 2 * F * H / 32, w1cq + e * H * 2 * F / 2,
+                                                    w1cs + e * H * 2 * F / 32, stream), who);
+    if (st != MX_OK) return st;
+    st = fp4_step(mx::launch_quantize_fp4(w2b + e * H * F * 2, H, F, w2q + e * H * F / 2, w2s + e * H * F / 32,
+                                          w2cq + e * F * H / 2, w2cs + e * F * H / 32, stream), who);
+    if (st != MX_OK) return st;
+  }
+  return MX_OK;
+}
+
+mx_status fp4_cache_checks(const Fp4MlpLayout& L, const void* cache, size_t cache_bytes, Fp4WeightCacheLayout* W,
+                           const char* who) {
+  *W = fp4_weight_cache_layout(L.E, L.H, L.F);
+  if (!cache) return fail(MX_EINVAL, "%s: weight cache is null", who);
+  if (!aligned(cache, 256)) return fail(MX_EALIGN, "%s: weight cache must be 256-byte aligned", who);
+  if (cache_bytes < W->total)
+    return fail(MX_EWORKSPACE, "%s: weight cache %zu bytes < required %zu", who, cache_bytes, W->total);
+  return MX_OK;
+}
+
 mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs, const void* w1, const void* w2,
-                       void* y, void* saved, void* workspace, hipStream_t stream) {
-  const char* who = "grouped_mlp_fwd_fp4";
+                       const Fp4WeightCopies* wc, void* y, void* saved, void* workspace, hipStream_t stream,
+                       const char* who) {
   uint8_t* W = static_cast<uint8_t*>(workspace);
   uint8_t* S = static_cast<uint8_t*>(saved);
   const bool train = saved != nullptr;
@@ -1537,20 +1597,15 @@ mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs,
     st = fp4_step(mx::launch_quantize_fp4(x, R, H, W + L.xq, W + L.xs, nullptr, nullptr, stream), who);
   if (st != MX_OK) return st;
   // weights: rowwise along H (W1) and F (W2); in training also each expert's
-  // columnwise copy, [H, 2F] and [F, H], from the same pass
-  const uint8_t* w1b = static_cast<const uint8_t*>(w1);
-  const uint8_t* w2b = static_cast<const uint8_t*>(w2);
-  if (train) {
-    for (int64_t e = 0; e < E; ++e) {
-      st = fp4_step(mx::launch_quantize_fp4(w1b + e * 2 * F * H * 2, 2 * F, H, W + L.w1q + e * 2 * F * H / 2,
-                                            W + L.w1s + e * 2 * F * H / 32, S + L.w1cq + e * H * 2 * F / 2,
-                                            S + L.w1cs + e * H * 2 * F / 32, stream), who);
-      if (st != MX_OK) return st;
-      st = fp4_step(mx::launch_quantize_fp4(w2b + e * H * F * 2, H, F, W + L.w2q + e * H * F / 2,
-                                            W + L.w2s + e * H * F / 32, S + L.w2cq + e * F * H / 2,
-                                            S + L.w2cs + e * F * H / 32, stream), who);
-      if (st != MX_OK) return st;
-    }
+  // columnwise copy, [H, 2F] and [F, H], from the same pass. A weight cache
+  // holds all of them already.
+  const uint8_t *w1q = W + L.w1q, *w1s = W + L.w1s, *w2q = W + L.w2q, *w2s = W + L.w2s;
+  if (wc) {
+    w1q = wc->w1q; w1s = wc->w1s; w2q = wc->w2q; w2s = wc->w2s;
+  } else if (train) {
+    st = fp4_quantize_weights_into(E, H, F, w1, w2, W + L.w1q, W + L.w1s, W + L.w2q, W + L.w2s, S + L.w1cq,
+                                   S + L.w1cs, S + L.w2cq, S + L.w2cs, stream, who);
+    if (st != MX_OK) return st;
   } else {
     st = fp4_step(mx::launch_quantize_fp4(w1, E * 2 * F, H, W + L.w1q, W + L.w1s, nullptr, nullptr, stream), who);
     if (st != MX_OK) return st;
@@ -1558,8 +1613,8 @@ mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs,
     if (st != MX_OK) return st;
   }
   // GEMM1 -> H1 (fp32)
-  st = gemm_fp4_impl(who, W + L.xq, W + L.xs, W + L.w1q, W + L.w1s, L.split.data(), (int32_t)E, 2 * F, H,
-                     W + L.h1f, MX_F32, stream);
+  st = gemm_fp4_impl(who, W + L.xq, W + L.xs, w1q, w1s, L.split.data(), (int32_t)E, 2 * F, H, W + L.h1f, MX_F32,
+                     stream);
   if (st != MX_OK) return st;
   // ScaledSwiGLU: A rowwise MXFP4; in training also H1 (bf16, saved) and A's
   // per-expert columnwise copy, from one pass over H1
@@ -1577,24 +1632,28 @@ mx_status fwd_fp4_impl(const Fp4MlpLayout& L, const void* x, const float* probs,
   }
   if (st != MX_OK) return st;
   // GEMM2 -> Y (bf16)
-  return gemm_fp4_impl(who, W + L.aq, W + L.as, W + L.w2q, W + L.w2s, L.split.data(), (int32_t)E, H, F, y, MX_BF16,
-                       stream, reinterpret_cast<float*>(W + L.split2), L.split_bytes);
+  return gemm_fp4_impl(who, W + L.aq, W + L.as, w2q, w2s, L.split.data(), (int32_t)E, H, F, y, MX_BF16, stream,
+                       reinterpret_cast<float*>(W + L.split2), L.split_bytes);
 }
 
-mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs, const void* saved, void* dx,
-                       float* dprobs, float* dw1, float* dw2, int32_t accumulate, void* workspace,
-                       hipStream_t stream) {
-  const char* who = "grouped_mlp_bwd_fp4";
+mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs, const void* saved,
+                       const Fp4WeightCopies* wc, void* dx, float* dprobs, float* dw1, float* dw2, int32_t accumulate,
+                       void* workspace, hipStream_t stream, const char* who) {
   uint8_t* W = static_cast<uint8_t*>(workspace);
   const uint8_t* S = static_cast<const uint8_t*>(saved);
   const int64_t E = L.E, R = L.R, H = L.H, F = L.F;
+  // columnwise weight copies: from saved (the forward cast them) or the cache
+  const uint8_t* w1cq = wc ? wc->w1cq : S + L.w1cq;
+  const uint8_t* w1cs = wc ? wc->w1cs : S + L.w1cs;
+  const uint8_t* w2cq = wc ? wc->w2cq : S + L.w2cq;
+  const uint8_t* w2cs = wc ? wc->w2cs : S + L.w2cs;
   // dY: rowwise (dgrad2) and per-expert columnwise (wgrad2) in one pass
   mx_status st = fp4_step(mx::launch_quantize_fp4_grouped(dy, false, R, H, L.cg, W + L.dycq, W + L.dycs, W + L.dyq,
                                                           W + L.dys, stream), who);
   if (st != MX_OK) return st;
   // dgrad2: dA = dY . W2 (fp32) on the columnwise W2 copies [F, H]
-  st = gemm_fp4_impl(who, W + L.dyq, W + L.dys, S + L.w2cq, S + L.w2cs, L.split.data(), (int32_t)E, F, H, W + L.da32,
-                     MX_F32, stream);
+  st = gemm_fp4_impl(who, W + L.dyq, W + L.dys, w2cq, w2cs, L.split.data(), (int32_t)E, F, H, W + L.da32, MX_F32,
+                     stream);
   if (st != MX_OK) return st;
   // SwiGLU backward: dH1 in both MXFP4 layouts from one pass over dA and the
   // saved H1, and dprobs from per-tile partial sums
@@ -1613,8 +1672,8 @@ mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs
     if (st != MX_OK) return st;
   }
   // dgrad1: dX = dH1 . W1 (bf16) on the columnwise W1 copies [H, 2F]
-  st = gemm_fp4_impl(who, W + L.dhq, W + L.dhs, S + L.w1cq, S + L.w1cs, L.split.data(), (int32_t)E, H, 2 * F, dx,
-                     MX_BF16, stream, reinterpret_cast<float*>(W + L.split1), L.split_bytes);
+  st = gemm_fp4_impl(who, W + L.dhq, W + L.dhs, w1cq, w1cs, L.split.data(), (int32_t)E, H, 2 * F, dx, MX_BF16,
+                     stream, reinterpret_cast<float*>(W + L.split1), L.split_bytes);
   if (st != MX_OK) return st;
   // weight gradients (fp32, stored or accumulated): dW2_e = dY_e^T A_e, dW1_e = dH1_e^T X_e
   st = fp4_step(mx::launch_gemm_fp4_group_k(W + L.dycq, W + L.dycs, S + L.acq, S + L.acs, L.kg, H, F, dw2, accumulate,
@@ -1622,6 +1681,33 @@ mx_status bwd_fp4_impl(const Fp4MlpLayout& L, const void* dy, const float* probs
   if (st != MX_OK) return st;
   return fp4_step(mx::launch_gemm_fp4_group_k(W + L.dhcq, W + L.dhcs, S + L.xcq, S + L.xcs, L.kg, 2 * F, H, dw1,
                                               accumulate, stream), who);
+}
+
+mx_status fp4_fwd_checks(const Fp4MlpLayout& L, const void* x, const float* probs, const void* y, const void* saved,
+                         size_t saved_bytes, const void* workspace, size_t workspace_bytes, const char* who) {
+  if (!x || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) || (saved && !aligned(saved, 256)) ||
+      (probs && !aligned(probs, 4)))
+    return fail(MX_EALIGN, "%s: x, y must be 16-byte and workspace/saved 256-byte aligned", who);
+  if (workspace_bytes < L.fwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
+  if (saved && saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  return MX_OK;
+}
+
+mx_status fp4_bwd_checks(const Fp4MlpLayout& L, const void* dy, const float* probs, const void* saved,
+                         size_t saved_bytes, const void* dx, const float* dprobs, const float* dw1, const float* dw2,
+                         const void* workspace, size_t workspace_bytes, const char* who) {
+  if (!dy || !saved || !dx || !dw1 || !dw2 || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(saved, 256) ||
+      !aligned(workspace, 256) || (probs && !aligned(probs, 4)) || (dprobs && !aligned(dprobs, 4)))
+    return fail(MX_EALIGN, "%s: dy, dx, dw1, dw2 must be 16-byte and saved/workspace 256-byte aligned", who);
+  if (saved_bytes < L.saved_total)
+    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
+  if (workspace_bytes < L.bwd_total)
+    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.bwd_total);
+  return MX_OK;
 }
 
 }  // namespace
@@ -1648,15 +1734,11 @@ mx_status grouped_mlp_fwd_fp4(const mx_mlp_dims* dims, const int64_t* split_size
   Fp4MlpLayout L;
   mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
   if (st != MX_OK) return st;
-  if (!x || !w1 || !w2 || !y || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
-  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
-      (saved && !aligned(saved, 256)) || (probs && !aligned(probs, 4)))
-    return fail(MX_EALIGN, "%s: x, w1, w2, y must be 16-byte and workspace/saved 256-byte aligned", who);
-  if (workspace_bytes < L.fwd_total)
-    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.fwd_total);
-  if (saved && saved_bytes < L.saved_total)
-    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
-  return fwd_fp4_impl(L, x, probs, w1, w2, y, saved, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
+  st = fp4_fwd_checks(L, x, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  return fwd_fp4_impl(L, x, probs, w1, w2, nullptr, y, saved, workspace, reinterpret_cast<hipStream_t>(stream), who);
 }
 
 mx_status grouped_mlp_bwd_fp4(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy, const float* probs,
@@ -1667,16 +1749,84 @@ mx_status grouped_mlp_bwd_fp4(const mx_mlp_dims* dims, const int64_t* split_size
   Fp4MlpLayout L;
   mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
   if (st != MX_OK) return st;
-  if (!dy || !saved || !dx || !dw1 || !dw2 || !workspace) return fail(MX_EINVAL, "%s: null pointer argument", who);
-  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(saved, 256) ||
-      !aligned(workspace, 256) || (probs && !aligned(probs, 4)) || (dprobs && !aligned(dprobs, 4)))
-    return fail(MX_EALIGN, "%s: dy, dx, dw1, dw2 must be 16-byte and saved/workspace 256-byte aligned", who);
-  if (saved_bytes < L.saved_total)
-    return fail(MX_EWORKSPACE, "%s: saved buffer %zu bytes < required %zu", who, saved_bytes, L.saved_total);
-  if (workspace_bytes < L.bwd_total)
-    return fail(MX_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.bwd_total);
-  return bwd_fp4_impl(L, dy, probs, saved, dx, dprobs, dw1, dw2, accumulate_wgrad ? 1 : 0, workspace,
-                      reinterpret_cast<hipStream_t>(stream));
+  st = fp4_bwd_checks(L, dy, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  return bwd_fp4_impl(L, dy, probs, saved, nullptr, dx, dprobs, dw1, dw2, accumulate_wgrad ? 1 : 0, workspace,
+                      reinterpret_cast<hipStream_t>(stream), who);
+}
+
+mx_status grouped_mlp_fp4_weight_cache_bytes(const mx_mlp_dims* dims, size_t* bytes) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fp4_weight_cache_bytes";
+  if (!bytes) return fail(MX_EINVAL, "%s: bytes is null", who);
+  if (!dims) return fail(MX_EINVAL, "%s: dims is null", who);
+  // the cache does not depend on the routed rows: check the rest with R = 0
+  mx_mlp_dims d = *dims;
+  d.rows = 0;
+  std::vector<int64_t> zeros(d.num_experts > 0 && d.num_experts <= mx::kMaxGroups ? d.num_experts : 1, 0);
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(&d, zeros.data(), &L, who);
+  if (st != MX_OK) return st;
+  *bytes = fp4_weight_cache_layout(L.E, L.H, L.F).total;
+  return MX_OK;
+}
+
+mx_status grouped_mlp_fp4_quantize_weights(const mx_mlp_dims* dims, const void* w1, const void* w2, void* cache,
+                                           size_t cache_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fp4_quantize_weights";
+  if (!dims) return fail(MX_EINVAL, "%s: dims is null", who);
+  mx_mlp_dims d = *dims;
+  d.rows = 0;
+  std::vector<int64_t> zeros(d.num_experts > 0 && d.num_experts <= mx::kMaxGroups ? d.num_experts : 1, 0);
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(&d, zeros.data(), &L, who);
+  if (st != MX_OK) return st;
+  Fp4WeightCacheLayout W;
+  st = fp4_cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  if (!w1 || !w2) return fail(MX_EINVAL, "%s: null pointer argument", who);
+  if (!aligned(w1, 16) || !aligned(w2, 16)) return fail(MX_EALIGN, "%s: w1, w2 must be 16-byte aligned", who);
+  uint8_t* c = static_cast<uint8_t*>(cache);
+  return fp4_quantize_weights_into(L.E, L.H, L.F, w1, w2, c + W.w1q, c + W.w1s, c + W.w2q, c + W.w2s, c + W.w1cq,
+                                   c + W.w1cs, c + W.w2cq, c + W.w2cs, reinterpret_cast<hipStream_t>(stream), who);
+}
+
+mx_status grouped_mlp_fwd_fp4_cached(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* x,
+                                     const float* probs, const void* cache, size_t cache_bytes, void* y, void* saved,
+                                     size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_fwd_fp4_cached";
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = fp4_fwd_checks(L, x, probs, y, saved, saved_bytes, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  Fp4WeightCacheLayout W;
+  st = fp4_cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  const Fp4WeightCopies wc = fp4_weight_cache_copies(W, cache);
+  return fwd_fp4_impl(L, x, probs, nullptr, nullptr, &wc, y, saved, workspace, reinterpret_cast<hipStream_t>(stream),
+                      who);
+}
+
+mx_status grouped_mlp_bwd_fp4_cached(const mx_mlp_dims* dims, const int64_t* split_sizes, const void* dy,
+                                     const float* probs, const void* cache, size_t cache_bytes, const void* saved,
+                                     size_t saved_bytes, void* dx, float* dprobs, float* dw1, float* dw2,
+                                     int32_t accumulate_wgrad, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "grouped_mlp_bwd_fp4_cached";
+  Fp4MlpLayout L;
+  mx_status st = fp4_mlp_layout(dims, split_sizes, &L, who);
+  if (st != MX_OK) return st;
+  st = fp4_bwd_checks(L, dy, probs, saved, saved_bytes, dx, dprobs, dw1, dw2, workspace, workspace_bytes, who);
+  if (st != MX_OK) return st;
+  Fp4WeightCacheLayout W;
+  st = fp4_cache_checks(L, cache, cache_bytes, &W, who);
+  if (st != MX_OK) return st;
+  const Fp4WeightCopies wc = fp4_weight_cache_copies(W, cache);
+  return bwd_fp4_impl(L, dy, probs, saved, &wc, dx, dprobs, dw1, dw2, accumulate_wgrad ? 1 : 0, workspace,
+                      reinterpret_cast<hipStream_t>(stream), who);
 }
 
 }  // extern "C"

@@ -438,10 +438,89 @@ def test_fp4_mlp_bindings_check_state_and_shapes():
     E, R, H, F = 2, 64, 256, 64
     with pytest.raises(ValueError, match="w1"):
         mx.grouped_mlp_fwd_fp4(bf(R, H), None, bf(E, H, 2 * F), bf(E, H, F), [32, 32])
-    with pytest.raises(ValueError, match="grouped_mlp_fwd_fp4"):
+    with pytest.raises(ValueError, match="MXFP4 forward"):
         mx.grouped_mlp_bwd_fp4(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32]))     # an MXFP8 state
     with pytest.raises(ValueError, match="MXFP8"):
         mx.grouped_mlp_bwd(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32], fmt="mxfp4"))
+
+
+def _fake_cache(fmt, E=2, H=256, F=64):
+    """A WeightCache object without a device buffer (the bindings' checks
+    below run before any device call)."""
+    c = mx.WeightCache.__new__(mx.WeightCache)
+    c.ehf, c.fmt, c.buf = (E, H, F), fmt, None
+    return c
+
+
+def test_cached_states_pair_with_their_cache():
+    """A state from a cached forward holds no weight copies: the uncached
+    backward refuses it, and a cached backward takes only the cache (and
+    format) that made it."""
+    import torch
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    E, R, H, F = 2, 64, 256, 64
+    c8, c4 = _fake_cache("mxfp8"), _fake_cache("mxfp4")
+    st8 = mx.MLPState(None, (E, R, H, F), [32, 32], cache=c8)
+    st4 = mx.MLPState(None, (E, R, H, F), [32, 32], fmt="mxfp4", cache=c4)
+    with pytest.raises(ValueError, match="cached forward"):
+        mx.grouped_mlp_bwd(bf(R, H), None, st8)
+    with pytest.raises(ValueError, match="cached forward"):
+        mx.grouped_mlp_bwd_fp4(bf(R, H), None, st4)
+    with pytest.raises(ValueError, match="this weight cache"):
+        mx.grouped_mlp_bwd_cached(bf(R, H), None, st8, _fake_cache("mxfp8"))
+    with pytest.raises(ValueError, match="this weight cache"):
+        mx.grouped_mlp_bwd_fp4_cached(bf(R, H), None, st4, _fake_cache("mxfp4"))
+    with pytest.raises(ValueError, match="MXFP4 weight cache"):
+        mx.grouped_mlp_bwd_fp4_cached(bf(R, H), None, st4, c8)
+    with pytest.raises(ValueError, match="MXFP8 weight cache"):
+        mx.grouped_mlp_bwd_cached(bf(R, H), None, st8, c4)
+    with pytest.raises(ValueError, match="MXFP4 forward"):
+        mx.grouped_mlp_bwd_fp4_cached(bf(R, H), None, mx.MLPState(None, (E, R, H, F), [32, 32], cache=c4), c4)
+    with pytest.raises(ValueError, match="mxfp8"):
+        mx.grouped_mlp_fwd_fp4_cached(bf(R, H), None, c8, [32, 32])
+    with pytest.raises(ValueError, match="mxfp4"):
+        mx.grouped_mlp_fwd_cached(bf(R, H), None, c4, [32, 32])
+    with pytest.raises(ValueError, match="unknown format"):
+        mx.WeightCache(E, H, F, fmt="nvfp4")
+
+
+def test_fp4_weight_cache_sizes_and_errors(L):
+    E, H, F = 2, 256, 128
+    n = ctypes.c_size_t()
+    d = _dims(E=E, H=H, F=F)
+    assert L.grouped_mlp_fp4_weight_cache_bytes(ctypes.byref(d), ctypes.byref(n)) == OK
+    codes = (E * 2 * F * H + E * H * F)               # both layouts of W1 and W2, two codes per byte
+    assert codes * (1 + 1 / 16) <= n.value <= codes * (1 + 1 / 16) + 8 * 256
+    assert L.grouped_mlp_fp4_weight_cache_bytes(ctypes.byref(_dims(H=96)), ctypes.byref(n)) == ESHAPE
+    assert L.grouped_mlp_fp4_weight_cache_bytes(None, ctypes.byref(n)) == EINVAL
+    assert L.grouped_mlp_fp4_weight_cache_bytes(ctypes.byref(d), None) == EINVAL
+    cb = ctypes.c_size_t()
+    L.grouped_mlp_fp4_weight_cache_bytes(ctypes.byref(d), ctypes.byref(cb))
+    ws = ctypes.c_void_p(0x100000)
+    assert L.grouped_mlp_fp4_quantize_weights(ctypes.byref(d), FAKE, FAKE, ws, cb.value - 1, None) == EWORKSPACE
+    assert L.grouped_mlp_fp4_quantize_weights(ctypes.byref(d), None, FAKE, ws, cb.value, None) == EINVAL
+    assert L.grouped_mlp_fp4_quantize_weights(ctypes.byref(d), FAKE, FAKE, None, cb.value, None) == EINVAL
+    assert L.grouped_mlp_fp4_quantize_weights(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x100010), cb.value,
+                                              None) == EALIGN
+    assert L.grouped_mlp_fp4_quantize_weights(None, FAKE, FAKE, ws, cb.value, None) == EINVAL
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    split = mx._i64_array([40, 24])
+    d = _dims(E=E, R=64, H=H, F=F)
+    assert L.grouped_mlp_fp4_sizes(ctypes.byref(d), split, ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)) == OK
+    fwd = lambda cache=ws, cbytes=cb.value, wsb=f.value, x=FAKE: L.grouped_mlp_fwd_fp4_cached(
+        ctypes.byref(d), split, x, None, cache, cbytes, FAKE, None, 0, ws, wsb, None)
+    assert fwd(cbytes=cb.value - 1) == EWORKSPACE
+    assert fwd(cache=None) == EINVAL
+    assert fwd(cache=ctypes.c_void_p(0x100010)) == EALIGN
+    assert fwd(wsb=f.value - 1) == EWORKSPACE
+    assert fwd(x=None) == EINVAL
+    bwd = lambda cache=ws, cbytes=cb.value, saved=ws, sb=s.value, wsb=b.value: L.grouped_mlp_bwd_fp4_cached(
+        ctypes.byref(d), split, FAKE, None, cache, cbytes, saved, sb, FAKE, None, FAKE, FAKE, 1, ws, wsb, None)
+    assert bwd(cbytes=cb.value - 1) == EWORKSPACE
+    assert bwd(cache=None) == EINVAL
+    assert bwd(saved=None) == EINVAL
+    assert bwd(sb=s.value - 1) == EWORKSPACE
+    assert bwd(wsb=b.value - 1) == EWORKSPACE
 
 
 def test_nvfp4_argument_errors(L):

@@ -138,6 +138,57 @@ def test_fp4_mlp_differs_from_mxfp8(gpu_lib):
     assert rel_norm(to_np(y4), w4) <= TOL and rel_norm(to_np(y8), w8) <= TOL
 
 
+@pytest.mark.parametrize("name", ["ragged4", "split_k_tail"])
+def test_fp4_cached_weights_match_uncast_path(gpu_lib, name):
+    """grouped_mlp_fwd_fp4_cached / grouped_mlp_bwd_fp4_cached on weights cast
+    once by grouped_mlp_fp4_quantize_weights give bit-identical outputs to the
+    calls that cast the bf16 weights themselves (same codes, same kernels), in
+    training and inference, overwriting and accumulating the weight gradients,
+    and the cache serves a second step with another split; the cached path
+    also meets the oracle's bar on its own."""
+    mx = gpu_lib
+    k = CASES[name]
+    print(f"[mlp_fp4 cached] {name}: E={k['E']} H={k['H']} F={k['F']} split={k['split']}", flush=True)
+    c = wl.small_mlp_case(k["seed"], k["E"], k["H"], k["F"], k["split"])
+    x, w1, w2, dy = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]), dev_bf16(c["dy"])
+    p = dev_f32(c["probs"])
+    split = list(k["split"])
+    E, H, F = k["E"], k["H"], k["F"]
+    cache = mx.grouped_mlp_fp4_quantize_weights(w1, w2)
+
+    def same(a, b):
+        if a.dtype == torch.bfloat16:
+            return torch.equal(a.view(torch.int16), b.view(torch.int16))
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+    rng = np.random.default_rng(11)
+    start1 = torch.from_numpy(rng.standard_normal((E, 2 * F, H)).astype(np.float32) * 1e-3).cuda()
+    start2 = torch.from_numpy(rng.standard_normal((E, H, F)).astype(np.float32) * 1e-3).cuda()
+    for split_now in (split, split[::-1]):
+        y_ref, st_ref = mx.grouped_mlp_fwd_fp4(x, p, w1, w2, split_now, training=True)
+        y_c, st_c = mx.grouped_mlp_fwd_fp4_cached(x, p, cache, split_now, training=True)
+        y_i, _ = mx.grouped_mlp_fwd_fp4_cached(x, p, cache, split_now, training=False)
+        ref = mx.grouped_mlp_bwd_fp4(dy, p, st_ref)
+        got = mx.grouped_mlp_bwd_fp4_cached(dy, p, st_c, cache)
+        acc_ref = mx.grouped_mlp_bwd_fp4(dy, p, st_ref, dw1=start1.clone(), dw2=start2.clone(), accumulate=True)
+        acc_got = mx.grouped_mlp_bwd_fp4_cached(dy, p, st_c, cache, dw1=start1.clone(), dw2=start2.clone(),
+                                                accumulate=True)
+        torch.cuda.synchronize()
+        assert same(y_ref, y_c) and same(y_ref, y_i), "y"
+        for a, b, what in zip(ref + acc_ref, got + acc_got,
+                              ("dx", "dprobs", "dw1", "dw2", "dx (acc)", "dprobs (acc)", "dw1 (acc)", "dw2 (acc)")):
+            assert same(a, b), what
+    fwd = orc.mlp_forward(c["x"], c["probs"], c["w1"], c["w2"], split, quantize="mxfp4")
+    y_c, st_c = mx.grouped_mlp_fwd_fp4_cached(x, p, cache, split, training=True)
+    dx, dp, dw1, dw2 = mx.grouped_mlp_bwd_fp4_cached(dy, p, st_c, cache)
+    torch.cuda.synchronize()
+    bwd = orc.mlp_backward(c["x"], c["probs"], c["w1"], c["w2"], split, c["dy"], fwd, quantize="mxfp4")
+    _rows(to_np(y_c), fwd["y"], split, "y (cached weights)")
+    _rows(to_np(dx), bwd["dx"], split, "dx (cached weights)")
+    _experts(to_np(dw1), bwd["dw1"], split, "dw1 (cached weights)")
+    _experts(to_np(dw2), bwd["dw2"], split, "dw2 (cached weights)")
+
+
 def test_fp4_mlp_fullsize_sampled(gpu_lib):
     """The Mixtral-8x7B-shaped MoE MLP forward + backward at MXFP4 (4096
     tokens top-2 of 8: 8192 rows, H = 4096, F = 14336), in the calls the
