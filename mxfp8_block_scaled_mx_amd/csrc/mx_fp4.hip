@@ -648,8 +648,17 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
                                                        const float* a_amax, const float* b_amax, Fp4Split sp) {
   constexpr int SM = kF4SubM, SN = kF4SubN, TM = kFp4GemmTileM, TN = kFp4GemmTileN, KT = kF4KTile;
   constexpr uint32_t kE2M1 = 4;               // operand format selector of the scaled MFMA
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * KT];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][TN * KT];
+  // The two stages of A and B as four separate LDS objects, the stage of each
+  // k-tile fixed at compile time (the k-loop is unrolled by two): the
+  // compiler then sees that the DMA into one stage never aliases the
+  // fragment reads of the other and does not wait for the next k-tile's
+  // loads before computing on this one.
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[TM * KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sA1[TM * KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB0[TN * KT];
+  __shared__ __attribute__((aligned(16))) uint8_t sB1[TN * KT];
+  static_assert(TM * KT == 2 * SN * 4096 && TN * KT == 2 * SN * 4096,
+                "each wave's fp32 epilogue slice is one whole stage array");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -751,17 +760,17 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // in the last k-tile come from the next row (or read zero) and feed only
   // skipped k-steps.
   const uint32_t dma_off = (uint32_t)((lane >> 3) * ldq + 16 * ((lane & 7) ^ (lane >> 4) ^ (4 * (wave & 1))));
-  auto dma_tile = [&](int t, int buf) __attribute__((always_inline)) {
+  auto dma_tile = [&](int t, uint8_t* dA, uint8_t* dB) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < TM / 32; ++p) {
       const int blk = 4 * p + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(&sA[buf][blk * 1024]), 16, dma_off,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dA + blk * 1024), 16, dma_off,
                                                (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < TN / 32; ++p) {
       const int blk = 4 * p + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(&sB[buf][blk * 1024]), 16, dma_off,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dB + blk * 1024), 16, dma_off,
                                                (uint32_t)(8 * blk * ldq + KT * t), 0, 0);
     }
   };
@@ -822,20 +831,46 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
+  // L2 prefetch (MXFP4): once the loads of k-tile t + 1 are out, each wave
+  // touches one 128-byte line in each of 128 rows of k-tile t + kF4Prefetch
+  // (waves 0-1 the tile's A rows, waves 2-3 its B rows), so that k-tile's
+  // DMA finds its lines in L2. The two words land in a register pair of the
+  // k-tile's parity (the loop is unrolled by two, so the pairs alternate
+  // without moves); the wait at the end of the k-tile leaves them in flight,
+  // and at the end of the next k-tile, when in-order completion has them in,
+  // they are folded into a sink, so the prefetch adds no wait. (A
+  // buffer->LDS touch would not do: the barrier's release fence waits for
+  // every LDS write.) Rows and columns past the resource extents read
+  // nothing.
+  constexpr int kF4Prefetch = 3;
+  constexpr int kWaitVmcnt2 = 0x0F72;         // s_waitcnt vmcnt(2), expcnt/lgkmcnt open
+  const __amdgpu_buffer_rsrc_t rpf = make_rsrc(wave < 2 ? a + am0 * ldq + kbeg / 2 : b + brow0 * ldq + kbeg / 2,
+                                               wave < 2 ? (amv - 1) * ldq + klen / 2 : (bnv - 1) * ldq + klen / 2);
+  const uint32_t pf_off = (uint32_t)((128 * (wave & 1) + lane) * ldq);
+  uint32_t pf_sink = 0, pf_even[2] = {0u, 0u}, pf_odd[2] = {0u, 0u};
+  auto prefetch = [&](int t, uint32_t (&d)[2]) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)(KT * t);
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(rpf, pf_off, k0, 0);
+    d[1] = __builtin_amdgcn_raw_buffer_load_b32(rpf, pf_off + (uint32_t)(64 * ldq), k0, 0);
+  };
+
   u32x2 nsa[SM], nsb[SN];
-  dma_tile(t_lo, 0);
+  dma_tile(t_lo, sA0, sB0);
   load_scales(t_lo, sca, scb);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
+  // k-tile t on stage (cA, cB) while k-tile t + 1 loads into (nA, nB)
+  auto ktile = [&](int t, const uint8_t* cA, const uint8_t* cB, uint8_t* nA, uint8_t* nB, uint32_t (&pf_mine)[2],
+                   const uint32_t (&pf_prev)[2]) __attribute__((always_inline)) {
     const bool more = t + 1 < t_hi;           // uniform over the workgroup
     if (more) {
-      dma_tile(t + 1, buf ^ 1);
+      dma_tile(t + 1, nA, nB);
       load_scales(t + 1, nsa, nsb);
     }
-    const uint8_t* A = sA[buf] + (TM / 2 * wm) * KT;
-    const uint8_t* B = sB[buf] + (TN / 2 * wn) * KT;
+    // unconditional, so that it is the newest load on every path
+    if constexpr (!NV) prefetch(t + kF4Prefetch, pf_mine);
+    const uint8_t* A = cA + (TM / 2 * wm) * KT;
+    const uint8_t* B = cB + (TN / 2 * wn) * KT;
     if constexpr (NV) {
       // NVFP4 on the fp16 MFMA (32 x 32 x 16): the lanes of half h take the
       // values [128 h, 128 h + 128) of the k-tile, read as chunks 4 h .. 4 h + 3
@@ -916,15 +951,29 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       }
     }
     }
+    // this wave's DMA and scales landed (MXFP4: all but this k-tile's two
+    // prefetch loads, so the previous k-tile's are in)
+    if constexpr (NV) {
+      if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
+      // (an asm statement, so that the fold cannot move above the wait)
+      asm volatile("v_add3_u32 %0, %0, %1, %2" : "+v"(pf_sink) : "v"(pf_prev[0]), "v"(pf_prev[1]));
+    }
     if (more) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's DMA and scales landed
 #pragma unroll
       for (int i = 0; i < SM; ++i) sca[i] = nsa[i];
 #pragma unroll
       for (int j = 0; j < SN; ++j) scb[j] = nsb[j];
     }
     __syncthreads();
+  };
+  // k-tile t_lo + j lives in stage j & 1
+  for (int t = t_lo; t < t_hi; t += 2) {
+    ktile(t, sA0, sB0, sA1, sB1, pf_even, pf_odd);
+    if (t + 1 < t_hi) ktile(t + 1, sA1, sB1, sA0, sB0, pf_odd, pf_even);
   }
+  asm volatile("" :: "v"(pf_sink ^ pf_even[0] ^ pf_even[1] ^ pf_odd[0] ^ pf_odd[1]));
 
   // lane l holds row 32 i + l32 and, per MFMA tile, columns 8 g + 4 h .. +3
   // (g = 0..3) in accumulator elements 4 g .. 4 g + 3. NVFP4: every product
@@ -937,7 +986,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     // a split-K part: the whole fp32 partial tile, row-major (pitch TN), into
     // its slot, through the wave's 32 KB LDS slice as whole 128-byte rows
     // (the staging of the fp32 epilogue below, without old values)
-    uint8_t* const slice = wave < 2 ? sA[0] + wave * 32768 : sB[0] + (wave - 2) * 32768;
+    uint8_t* const slice = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
     const float* wp = sp.ws + (int64_t)split_unit * TM * TN + (int64_t)(TM / 2 * wm) * TN + TN / 2 * wn;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(wp, ((int64_t)(TM / 2 - 1) * TN + TN / 2) * 4);
     const int rr = lane >> 3, cc = lane & 7;
@@ -976,7 +1025,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     // accumulating store are loaded in that layout, two 32-row blocks ahead.
     const int64_t wrows = min<int64_t>(TM / 2, row_end - m0);
     if (wrows <= 0) return;
-    uint8_t* const slice = wave < 2 ? sA[0] + wave * 32768 : sB[0] + (wave - 2) * 32768;
+    uint8_t* const slice = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
     const char* cb = reinterpret_cast<const char*>(c) + ((GK ? (int64_t)grp * M * N : 0) + m0 * N + n0) * 4;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(cb, wrows * N * 4);
     const uint32_t ld = (uint32_t)N;
