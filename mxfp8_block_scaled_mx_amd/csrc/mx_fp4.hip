@@ -731,15 +731,17 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // reach past the resource's extent and come back as zero scales. (NVFP4: K
   // is a multiple of 128, so a lane's 8 scales of a k-tile are always one
   // aligned 8-byte piece.) Group-K ranges start at any multiple of 32 values,
-  // so a group's scales start at any byte: then (sc_shift) the two aligned
-  // 8-byte loads around the 8 bytes and a per-lane byte shift, through
-  // resources over the whole scale arrays (offsets from their bases, which
-  // the range check covers). A load that reaches past the extent reads
-  // zeros, also for its bytes inside it, so a lane whose 16 bytes do not
-  // all lie in the array (the array's last row or two) takes byte loads.
-  // Else byte loads throughout.
+  // so a group's scales start at any byte: group-K takes (sc_shift) the
+  // aligned 16 bytes around the 8 and a per-lane byte shift (0 where they are
+  // aligned), through resources over the whole scale arrays (offsets from
+  // their bases, which the range check covers). A load that reaches past the
+  // extent reads zeros, also for its bytes inside it, so a lane whose 16
+  // bytes do not all lie in the array (the array's last row or two) takes
+  // byte loads. One load shape for all group-K tiles also keeps the combine
+  // from waiting (an 8-byte path beside it made the compiler copy its
+  // result, which waits for the load). Else byte loads throughout.
   const bool sc_dword = NV || ((lds & 7) == 0 && ((kbeg / 32) & 7) == 0 && ((klen / 32) & 7) == 0);
-  const bool sc_shift = GK && !sc_dword &&
+  const bool sc_shift = GK &&
                         ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(bs)) & 7) == 0 &&
                         M * lds < ((int64_t)1 << 32) && N * lds < ((int64_t)1 << 32);
   const int64_t sa_len = sc_shift ? M * lds : (amv - 1) * lds + klen / kVPS;
@@ -778,38 +780,68 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
   // blocks 16 t + 8 h .. + 7, those of the lane's half of the k-tile)
   u32x2 sca[SM], scb[SN];
   const uint32_t sc_k = NV ? 8 * h : 0;
-  auto scale_pair = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int64_t len)
-      __attribute__((always_inline)) -> u32x2 {
-    if (sc_dword) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    const uint32_t al = off & ~7u, sh = off & 7u;
-    if (sc_shift && (int64_t)al + 16 <= len) {
+  // A lane's scales of one k-tile in two steps: the loads (scale_load, raw
+  // words: the 8 scale bytes in x, y, or for sc_shift the two aligned pieces
+  // in x, y and z, w), and after the k-tile's wait the byte shift
+  // (scale_take), so that combining the pieces never waits on the loads
+  // issued with them, the next k-tile's DMA among them.
+  auto shifted = [&](uint32_t off, int64_t len) __attribute__((always_inline)) -> bool {
+    return sc_shift && (int64_t)(off & ~7u) + 16 <= len;
+  };
+  auto scale_load = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, int64_t len)
+      __attribute__((always_inline)) -> u32x4 {
+    u32x4 w;
+    w.z = 0; w.w = 0;
+    if (shifted(off, len)) {
+      const uint32_t al = off & ~7u;
       const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, al, 0, 0);
       const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(r, al + 8, 0, 0);
-      const bool up = sh >= 4;                // the 8 bytes start in the second dword
-      const uint32_t a0 = up ? lo.y : lo.x, a1 = up ? hi.x : lo.y, a2 = up ? hi.y : hi.x;
-      u32x2 w;
-      w.x = __builtin_amdgcn_alignbyte(a1, a0, sh & 3u);
-      w.y = __builtin_amdgcn_alignbyte(a2, a1, sh & 3u);
+      w.x = lo.x; w.y = lo.y; w.z = hi.x; w.w = hi.y;
       return w;
     }
-    u32x2 v;
-    v.x = 0; v.y = 0;
+    if (sc_dword) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      w.x = v.x; w.y = v.y;
+      return w;
+    }
+    w.x = 0; w.y = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(r, off + e, 0, 0);
-      if (e < 4) v.x |= byte << (8 * e); else v.y |= byte << (8 * (e - 4));
+      if (e < 4) w.x |= byte << (8 * e); else w.y |= byte << (8 * (e - 4));
+    }
+    return w;
+  };
+  auto scale_take = [&](const u32x4& w, uint32_t off, int64_t len) __attribute__((always_inline)) -> u32x2 {
+    u32x2 v;
+    if (shifted(off, len)) {
+      const uint32_t sh = off & 7u;
+      const bool up = sh >= 4;                // the 8 bytes start in the second dword
+      const uint32_t a0 = up ? w.y : w.x, a1 = up ? w.z : w.y, a2 = up ? w.w : w.z;
+      v.x = __builtin_amdgcn_alignbyte(a1, a0, sh & 3u);
+      v.y = __builtin_amdgcn_alignbyte(a2, a1, sh & 3u);
+    } else {
+      v.x = w.x; v.y = w.y;
     }
     return v;
   };
-  auto load_scales = [&](int t, u32x2 (&xa)[SM], u32x2 (&xb)[SN]) __attribute__((always_inline)) {
+  auto sa_off = [&](int t, int i) __attribute__((always_inline)) -> uint32_t {
+    return sa_off0 + (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + (NV ? 16 : 8) * t + sc_k);
+  };
+  auto sb_off = [&](int t, int j) __attribute__((always_inline)) -> uint32_t {
+    return sb_off0 + (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k);
+  };
+  auto load_scales = [&](int t, u32x4 (&xa)[SM], u32x4 (&xb)[SN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
-      xa[i] = scale_pair(rsa, sa_off0 + (uint32_t)((TM / 2 * wm + 32 * i + l32) * lds + (NV ? 16 : 8) * t + sc_k),
-                         sa_len);
+    for (int i = 0; i < SM; ++i) xa[i] = scale_load(rsa, sa_off(t, i), sa_len);
 #pragma unroll
-    for (int j = 0; j < SN; ++j)
-      xb[j] = scale_pair(rsb, sb_off0 + (uint32_t)((TN / 2 * wn + 32 * j + l32) * lds + (NV ? 16 : 8) * t + sc_k),
-                         sb_len);
+    for (int j = 0; j < SN; ++j) xb[j] = scale_load(rsb, sb_off(t, j), sb_len);
+  };
+  auto take_scales = [&](int t, const u32x4 (&xa)[SM], const u32x4 (&xb)[SN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i) sca[i] = scale_take(xa[i], sa_off(t, i), sa_len);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) scb[j] = scale_take(xb[j], sb_off(t, j), sb_len);
   };
   auto frag = [&](const uint8_t* base, int r, int s) __attribute__((always_inline)) -> v8i {
     const u32x4 q = *reinterpret_cast<const u32x4*>(base + r * KT + (((2 * s + h) ^ ((r >> 1) & 7)) << 4));
@@ -854,10 +886,11 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
     d[1] = __builtin_amdgcn_raw_buffer_load_b32(rpf, pf_off + (uint32_t)(64 * ldq), k0, 0);
   };
 
-  u32x2 nsa[SM], nsb[SN];
+  u32x4 nsa[SM], nsb[SN];
   dma_tile(t_lo, sA0, sB0);
-  load_scales(t_lo, sca, scb);
+  load_scales(t_lo, nsa, nsb);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  take_scales(t_lo, nsa, nsb);
   __syncthreads();
   // k-tile t on stage (cA, cB) while k-tile t + 1 loads into (nA, nB)
   auto ktile = [&](int t, const uint8_t* cA, const uint8_t* cB, uint8_t* nA, uint8_t* nB, uint32_t (&pf_mine)[2],
@@ -961,10 +994,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(const uint8_t* a, const u
       asm volatile("v_add3_u32 %0, %0, %1, %2" : "+v"(pf_sink) : "v"(pf_prev[0]), "v"(pf_prev[1]));
     }
     if (more) {
-#pragma unroll
-      for (int i = 0; i < SM; ++i) sca[i] = nsa[i];
-#pragma unroll
-      for (int j = 0; j < SN; ++j) scb[j] = nsb[j];
+      take_scales(t + 1, nsa, nsb);
     }
     __syncthreads();
   };
