@@ -135,7 +135,9 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
   __shared__ uint32_t cs_t[TC];              // columnwise scale bytes [column][block]
   static_assert(TC * 64 <= TR * 256, "columnwise staging must fit the input tile");
 
-  const int64_t n_ct = (cols + TC - 1) / TC;
+  // column tiles of the grid: the SwiGLU backward covers the dg half (columns
+  // below F) and forms the du half of the same columns in the same tile
+  const int64_t n_ct = ((SRC == kSrcSwigluBwd ? sw.F : cols) + TC - 1) / TC;
   const int n_rt = gr.tile0[gr.n];
   const int total = (int)((int64_t)((n_rt + 1) / 2) * 2 * n_ct);
   const int id = xcd_remap<kFp4CastChunk>((int)blockIdx.x, total);
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
   const bool col_ok = col < cols;              // cols % 32 == 0: a chunk is wholly in or out
 
   uint4 raw[TR / 16];
+  uint4 raw_u[SRC == kSrcSwigluBwd ? TR / 16 : 1];   // the backward's du values
   if constexpr (SRC == kSrcX) {
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
@@ -203,8 +206,7 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
     // dg tiles also sum dA silu(g) u over the tile's 64 columns of each row
     static_assert(sizeof(T) == 4, "the SwiGLU sources are fp32");
     const int64_t F = sw.F;
-    const bool is_g = c0 < F;                   // the tile's half (uniform)
-    const int64_t j = is_g ? col : col - F;
+    const int64_t j = col;                      // c0 < F: the tile's columns of dA, g and u
     float4 dv[TR / 16];
     uint2 gq[TR / 16], uq[TR / 16];
 #pragma unroll
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
       dv[p] = ok ? *reinterpret_cast<const float4*>(sw.da + (r0 + rr) * F + j) : make_float4(0.f, 0.f, 0.f, 0.f);
       const uint16_t* hp = sw.h1 + (r0 + rr) * 2 * F + j;
       gq[p] = ok ? *reinterpret_cast<const uint2*>(hp) : make_uint2(0, 0);
-      uq[p] = ok && is_g ? *reinterpret_cast<const uint2*>(hp + F) : make_uint2(0, 0);
+      uq[p] = ok ? *reinterpret_cast<const uint2*>(hp + F) : make_uint2(0, 0);
     }
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
@@ -224,126 +226,141 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
       const float d[4] = {dv[p].x, dv[p].y, dv[p].z, dv[p].w};
       const float g[4] = {bf16_lo(gq[p].x), bf16_hi(gq[p].x), bf16_lo(gq[p].y), bf16_hi(gq[p].y)};
       const float u[4] = {bf16_lo(uq[p].x), bf16_hi(uq[p].x), bf16_lo(uq[p].y), bf16_hi(uq[p].y)};
-      uint32_t vb[4];
+      uint32_t vb[4], vu[4];
       float dp = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
         const float sl = g[i] * sg;
-        vb[i] = __float_as_uint(is_g ? d[i] * w * u[i] * sg * (1.0f + g[i] * (1.0f - sg)) : d[i] * w * sl);
+        vb[i] = __float_as_uint(d[i] * w * u[i] * sg * (1.0f + g[i] * (1.0f - sg)));
+        vu[i] = __float_as_uint(d[i] * w * sl);
         dp += d[i] * sl * u[i];
       }
       raw[p] = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+      raw_u[p] = make_uint4(vu[0], vu[1], vu[2], vu[3]);
       // the row's 16 chunks of this tile (lanes with the same tid / 16)
 #pragma unroll
       for (int sh = 1; sh < 16; sh <<= 1) dp += xor_f32(dp, sh);
-      if (is_g && cc == 0 && ok && sw.dprobs_part != nullptr) sw.dprobs_part[(c0 / TC) * sw.R + r0 + rr] = dp;
+      if (cc == 0 && ok && sw.dprobs_part != nullptr) sw.dprobs_part[(c0 / TC) * sw.R + r0 + rr] = dp;
     }
   }
-#pragma unroll
-  for (int p = 0; p < TR / 16; ++p) {
-    const int rr = 16 * p + (tid >> 4);
-    *reinterpret_cast<uint4*>(tile + rr * 256 + cc * 16) = raw[p];
-    if (q_row != nullptr) {
-      float v[VPT];
-      if constexpr (kBf16) {
-        v[0] = bf16_lo(raw[p].x); v[1] = bf16_hi(raw[p].x); v[2] = bf16_lo(raw[p].y); v[3] = bf16_hi(raw[p].y);
-        v[4] = bf16_lo(raw[p].z); v[5] = bf16_hi(raw[p].z); v[6] = bf16_lo(raw[p].w); v[7] = bf16_hi(raw[p].w);
-      } else {
-        v[0] = __uint_as_float(raw[p].x); v[1] = __uint_as_float(raw[p].y);
-        v[2] = __uint_as_float(raw[p].z); v[3] = __uint_as_float(raw[p].w);
-      }
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) am = umax(am, abs_bits(v[i]));
-#pragma unroll
-      for (int sh = 1; sh < TPB; sh <<= 1) am = umax(am, xor_u32(am, sh));
-      const uint32_t eb = am >> 23;
-      const uint32_t sc = eb > 2u ? eb - 2u : 0u;
-      uint32_t codes;
-      if constexpr (kBf16) {
-        codes = e2m1x8_bf16(raw[p], e8m0_as_scale(sc));
-      } else {
-        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], e8m0_as_scale(sc), 0);
-        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[2], v[3], e8m0_as_scale(sc), 1);
-      }
-      const int64_t row = r0 + rr;
-      const bool row_ok = lr0 + rr < m_g;
-      if (row_ok && col_ok) {
-        if constexpr (kBf16) *reinterpret_cast<uint32_t*>(q_row + row * (cols / 2) + col / 2) = codes;
-        else *reinterpret_cast<uint16_t*>(q_row + row * (cols / 2) + col / 2) = (uint16_t)codes;
-      }
-      // the row's scale bytes of this tile, gathered into one word
-      uint32_t word = sc << (8 * (cc / TPB));
-#pragma unroll
-      for (int sh = TPB; sh < 16; sh <<= 1) word |= xor_u32(word, sh);
-      if (cc == 0 && row_ok) {
-        uint8_t* sd = s_row + row * (cols / 32) + c0 / 32;
-        const bool whole = c0 + TC <= cols && (reinterpret_cast<uintptr_t>(sd) & (NB - 1)) == 0;
-        if (whole) {
-          if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = word;
-          else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)word;
+  // Both layouts of one tile of values (vals) at output columns c0e ..
+  // c0e + TC - 1: rowwise codes from registers, then the tile through LDS for
+  // the columnwise codes and scales.
+  auto emit = [&](const uint4 (&vals)[TR / 16], int64_t c0e) __attribute__((always_inline)) {
+    const int64_t c0 = c0e;
+    const int64_t col = c0 + cc * VPT;
+    const bool col_ok = col < cols;
+  #pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      *reinterpret_cast<uint4*>(tile + rr * 256 + cc * 16) = vals[p];
+      if (q_row != nullptr) {
+        float v[VPT];
+        if constexpr (kBf16) {
+          v[0] = bf16_lo(vals[p].x); v[1] = bf16_hi(vals[p].x); v[2] = bf16_lo(vals[p].y); v[3] = bf16_hi(vals[p].y);
+          v[4] = bf16_lo(vals[p].z); v[5] = bf16_hi(vals[p].z); v[6] = bf16_lo(vals[p].w); v[7] = bf16_hi(vals[p].w);
         } else {
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            if (c0 + 32 * j < cols) sd[j] = (uint8_t)(word >> (8 * j));
+          v[0] = __uint_as_float(vals[p].x); v[1] = __uint_as_float(vals[p].y);
+          v[2] = __uint_as_float(vals[p].z); v[3] = __uint_as_float(vals[p].w);
+        }
+        uint32_t am = 0;
+  #pragma unroll
+        for (int i = 0; i < VPT; ++i) am = umax(am, abs_bits(v[i]));
+  #pragma unroll
+        for (int sh = 1; sh < TPB; sh <<= 1) am = umax(am, xor_u32(am, sh));
+        const uint32_t eb = am >> 23;
+        const uint32_t sc = eb > 2u ? eb - 2u : 0u;
+        uint32_t codes;
+        if constexpr (kBf16) {
+          codes = e2m1x8_bf16(vals[p], e8m0_as_scale(sc));
+        } else {
+          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], e8m0_as_scale(sc), 0);
+          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, v[2], v[3], e8m0_as_scale(sc), 1);
+        }
+        const int64_t row = r0 + rr;
+        const bool row_ok = lr0 + rr < m_g;
+        if (row_ok && col_ok) {
+          if constexpr (kBf16) *reinterpret_cast<uint32_t*>(q_row + row * (cols / 2) + col / 2) = codes;
+          else *reinterpret_cast<uint16_t*>(q_row + row * (cols / 2) + col / 2) = (uint16_t)codes;
+        }
+        // the row's scale bytes of this tile, gathered into one word
+        uint32_t word = sc << (8 * (cc / TPB));
+  #pragma unroll
+        for (int sh = TPB; sh < 16; sh <<= 1) word |= xor_u32(word, sh);
+        if (cc == 0 && row_ok) {
+          uint8_t* sd = s_row + row * (cols / 32) + c0 / 32;
+          const bool whole = c0 + TC <= cols && (reinterpret_cast<uintptr_t>(sd) & (NB - 1)) == 0;
+          if (whole) {
+            if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(sd) = word;
+            else *reinterpret_cast<uint16_t*>(sd) = (uint16_t)word;
+          } else {
+  #pragma unroll
+            for (int j = 0; j < NB; ++j)
+              if (c0 + 32 * j < cols) sd[j] = (uint8_t)(word >> (8 * j));
+          }
         }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // columnwise: thread t takes the CPS columns of dword t % 64 and the 32-row
-  // block t / 64 (rows of the group past its end are zeros)
-  const int rb = tid >> 6, slot = tid & 63;
-  float v[CPS][32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * rb + i) * 256 + slot * 4);
-    if constexpr (kBf16) {
-      v[0][i] = bf16_lo(w);
-      v[CPS - 1][i] = bf16_hi(w);
-    } else {
-      v[0][i] = __uint_as_float(w);
-    }
-  }
-  __syncthreads();                             // every column read: the tile becomes the code staging
-#pragma unroll
-  for (int j = 0; j < CPS; ++j) {
-    uint4 codes;
-    const uint32_t sc = fp4_block(v[j], codes);
-    const int cl = CPS * slot + j;             // column inside the tile
-    *reinterpret_cast<uint4*>(tile + cl * 64 + ((rb ^ ((cl >> 2) & 3)) << 4)) = codes;
-    reinterpret_cast<uint8_t*>(cs_t)[cl * 4 + rb] = (uint8_t)sc;
-  }
-  __syncthreads();
-
-  // each column's 64-byte run; blocks past the group's padded rows are not
-  // part of the layout (the next group's columns start there)
-  const int64_t pc0 = gr.pcol0[lo] + lr0;     // the tile's first position in the columnwise layout
-#pragma unroll
-  for (int it = 0; it < TC * 4 / 256; ++it) {
-    const int u = it * 256 + tid;
-    const int cl = u >> 2, piece = u & 3;
-    const int64_t colc = c0 + cl;
-    if (colc < cols && lr0 + 32 * piece < p_g)
-      *reinterpret_cast<uint4*>(q + colc * (ldp / 2) + pc0 / 2 + 16 * piece) =
-          *reinterpret_cast<const uint4*>(tile + cl * 64 + ((piece ^ ((cl >> 2) & 3)) << 4));
-  }
-  // columnwise scales: the tile's 4 blocks of a column are 4 consecutive bytes
-  if (tid < TC) {
-    const int64_t colc = c0 + tid;
-    if (colc < cols) {
-      const uint32_t word = cs_t[tid];
-      uint8_t* sd = s + colc * (ldp / 32) + pc0 / 32;
-      if (lr0 + 96 < p_g && (reinterpret_cast<uintptr_t>(sd) & 3) == 0) {
-        *reinterpret_cast<uint32_t*>(sd) = word;
+    // columnwise: thread t takes the CPS columns of dword t % 64 and the 32-row
+    // block t / 64 (rows of the group past its end are zeros)
+    const int rb = tid >> 6, slot = tid & 63;
+    float v[CPS][32];
+  #pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * rb + i) * 256 + slot * 4);
+      if constexpr (kBf16) {
+        v[0][i] = bf16_lo(w);
+        v[CPS - 1][i] = bf16_hi(w);
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (lr0 + 32 * j < p_g) sd[j] = (uint8_t)(word >> (8 * j));
+        v[0][i] = __uint_as_float(w);
       }
     }
+    __syncthreads();                             // every column read: the tile becomes the code staging
+  #pragma unroll
+    for (int j = 0; j < CPS; ++j) {
+      uint4 codes;
+      const uint32_t sc = fp4_block(v[j], codes);
+      const int cl = CPS * slot + j;             // column inside the tile
+      *reinterpret_cast<uint4*>(tile + cl * 64 + ((rb ^ ((cl >> 2) & 3)) << 4)) = codes;
+      reinterpret_cast<uint8_t*>(cs_t)[cl * 4 + rb] = (uint8_t)sc;
+    }
+    __syncthreads();
+
+    // each column's 64-byte run; blocks past the group's padded rows are not
+    // part of the layout (the next group's columns start there)
+    const int64_t pc0 = gr.pcol0[lo] + lr0;     // the tile's first position in the columnwise layout
+  #pragma unroll
+    for (int it = 0; it < TC * 4 / 256; ++it) {
+      const int u = it * 256 + tid;
+      const int cl = u >> 2, piece = u & 3;
+      const int64_t colc = c0 + cl;
+      if (colc < cols && lr0 + 32 * piece < p_g)
+        *reinterpret_cast<uint4*>(q + colc * (ldp / 2) + pc0 / 2 + 16 * piece) =
+            *reinterpret_cast<const uint4*>(tile + cl * 64 + ((piece ^ ((cl >> 2) & 3)) << 4));
+    }
+    // columnwise scales: the tile's 4 blocks of a column are 4 consecutive bytes
+    if (tid < TC) {
+      const int64_t colc = c0 + tid;
+      if (colc < cols) {
+        const uint32_t word = cs_t[tid];
+        uint8_t* sd = s + colc * (ldp / 32) + pc0 / 32;
+        if (lr0 + 96 < p_g && (reinterpret_cast<uintptr_t>(sd) & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(sd) = word;
+        } else {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (lr0 + 32 * j < p_g) sd[j] = (uint8_t)(word >> (8 * j));
+        }
+      }
+    }
+  };
+  emit(raw, c0);
+  if constexpr (SRC == kSrcSwigluBwd) {
+    __syncthreads();                           // the LDS tile and scale words are free again
+    emit(raw_u, sw.F + c0);
   }
 }
 
