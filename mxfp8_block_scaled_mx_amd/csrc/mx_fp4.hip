@@ -418,7 +418,8 @@ hipError_t launch_swiglu_fp4_cast(bool backward, const Fp4SwigluArgs& sw, const 
                                   uint8_t* s_col, uint8_t* q_row, uint8_t* s_row, hipStream_t stream) {
   const int64_t cols = backward ? 2 * sw.F : sw.F;
   if (sw.F % 128 != 0) return hipErrorInvalidValue;
-  const int64_t tiles = fp4_colwise_grid<float>(gr, cols);
+  // the backward's tiles cover the F columns of dA and each writes both dg and du
+  const int64_t tiles = fp4_colwise_grid<float>(gr, sw.F);
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (backward)
