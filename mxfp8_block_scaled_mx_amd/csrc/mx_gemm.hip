@@ -732,13 +732,14 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(col_out ? args.s_col : nullptr,
                                                  col_out ? (int64_t)(F >> 5) * args.nq_col * 128 : 0);
     const uint32_t q0 = (uint32_t)gt.q0[slot];
-    float w[4];
+    // routing weights of the lane's 4 rows: the loads go out together and
+    // unconditionally (without probs the resource is empty and they read 0),
+    // the choice comes after, so no load waits at a branch join
+    float w[4], wl[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = 32 * mi + l32;
-      w[mi] = args.probs ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * r, 0, 0))
-                         : (r < wrows ? 1.0f : 0.0f);
-    }
+    for (int mi = 0; mi < 4; ++mi) wl[mi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * (32 * mi + l32), 0, 0));
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) w[mi] = args.probs ? wl[mi] : (32 * mi + l32 < wrows ? 1.0f : 0.0f);
     // Scale words: the wave's NS/2 column blocks are bytes 2*wn .. of one
     // rowwise word per row, and its 4 row blocks the 4 bytes of one
     // columnwise word per column (bytes of blocks past the group are 0).
@@ -811,13 +812,14 @@ void gemm_kernel(GemmArgs args, int total_tiles) {
     const __amdgpu_buffer_rsrc_t rqc_u = make_rsrc(args.q_col + (int64_t)(F + jw0) * ldq + crow0, (int64_t)kWaveN * ldq);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(args.s_col, (int64_t)(2 * F >> 5) * args.nq_col * 128);
     const uint32_t q0 = (uint32_t)gt.q0[slot];
-    float w[4];
+    // routing weights of the lane's 4 rows: the loads go out together and
+    // unconditionally (without probs the resource is empty and they read 0),
+    // the choice comes after, so no load waits at a branch join
+    float w[4], wl[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = 32 * mi + l32;
-      w[mi] = args.probs ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * r, 0, 0))
-                         : (r < wrows ? 1.0f : 0.0f);
-    }
+    for (int mi = 0; mi < 4; ++mi) wl[mi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rprob, 4 * (32 * mi + l32), 0, 0));
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) w[mi] = args.probs ? wl[mi] : (32 * mi + l32 < wrows ? 1.0f : 0.0f);
     float dpsum[4];
     // Scale words: the wave's NS column blocks of the gate (and of the up)
     // half are the 4 bytes of one rowwise word per row, and its 4 row blocks
