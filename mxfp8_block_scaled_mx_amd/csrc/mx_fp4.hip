@@ -117,6 +117,10 @@ __global__ __launch_bounds__(256) void quantize_fp4_rowwise_kernel(const uint16_
 // in the dg half (columns below F) or the du half, F being a multiple of 128.
 enum Fp4Src : int { kSrcX = 0, kSrcSwigluFwd = 1, kSrcSwigluBwd = 2 };
 constexpr int kFp4ColTileRows = 128, kFp4CastChunk = 64;
+// routing weight 1, read where a cast has no probs (so that the weight loads
+// stay unconditional)
+__device__ const float kUnitWeight = 1.0f;
+
 template <typename T, int SRC = kSrcX>
 __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, int64_t rows, int64_t cols,
                                                                    uint8_t* q, uint8_t* s, uint8_t* q_row,
@@ -162,30 +166,54 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
   uint4 raw[TR / 16];
   uint4 raw_u[SRC == kSrcSwigluBwd ? TR / 16 : 1];   // the backward's du values
   if constexpr (SRC == kSrcX) {
+    // unconditional loads from clamped addresses (the tile's first row and
+    // column), all issued, then zeroed where out of range: a load under the
+    // condition is waited for at the branch join, one latency after another
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
       const int rr = 16 * p + (tid >> 4);
-      raw[p] = make_uint4(0, 0, 0, 0);
-      if (lr0 + rr < m_g && col_ok) raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + rr) * cols + col);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + (ok ? rr : 0)) * cols + (ok ? col : c0));
+    }
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      if (!(lr0 + rr < m_g && col_ok)) raw[p] = make_uint4(0, 0, 0, 0);
     }
   } else if constexpr (SRC == kSrcSwigluFwd) {
     // A = w * silu(g) * u of 4 columns per row piece, g and u from H1 (fp32)
     static_assert(sizeof(T) == 4, "the SwiGLU sources are fp32");
     const int64_t F = sw.F;
     float4 gv[TR / 16], uv[TR / 16];
+    float wv[TR / 16];
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
       const int rr = 16 * p + (tid >> 4);
-      const bool ok = lr0 + rr < m_g && col_ok;
-      const float* hp = sw.h1f + (r0 + rr) * 2 * F + col;
-      gv[p] = ok ? *reinterpret_cast<const float4*>(hp) : make_float4(0.f, 0.f, 0.f, 0.f);
-      uv[p] = ok ? *reinterpret_cast<const float4*>(hp + F) : make_float4(0.f, 0.f, 0.f, 0.f);
+      // routing weight, loaded unconditionally (row clamped; without probs
+      // the unit weight kUnitWeight)
+      wv[p] = *(sw.probs != nullptr ? sw.probs + r0 + (lr0 + rr < m_g ? rr : 0) : &kUnitWeight);
     }
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
       const int rr = 16 * p + (tid >> 4);
       const bool ok = lr0 + rr < m_g && col_ok;
-      const float w = ok && sw.probs != nullptr ? sw.probs[r0 + rr] : 1.0f;
+      const float* hp = sw.h1f + (r0 + (ok ? rr : 0)) * 2 * F + (ok ? col : c0);   // clamped, loaded unconditionally
+      gv[p] = *reinterpret_cast<const float4*>(hp);
+      uv[p] = *reinterpret_cast<const float4*>(hp + F);
+    }
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      if (!(lr0 + rr < m_g && col_ok)) {
+        gv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        uv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < TR / 16; ++p) {
+      const int rr = 16 * p + (tid >> 4);
+      const bool ok = lr0 + rr < m_g && col_ok;
+      const float w = ok ? wv[p] : 1.0f;
       const float g[4] = {gv[p].x, gv[p].y, gv[p].z, gv[p].w}, u[4] = {uv[p].x, uv[p].y, uv[p].z, uv[p].w};
       uint32_t ab[4];
 #pragma unroll
@@ -209,20 +237,27 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
     const int64_t j = col;                      // c0 < F: the tile's columns of dA, g and u
     float4 dv[TR / 16];
     uint2 gq[TR / 16], uq[TR / 16];
+    float wv[TR / 16];
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
+      // loaded unconditionally from clamped addresses (the tile's first row
+      // and column), zeroed after
       const int rr = 16 * p + (tid >> 4);
       const bool ok = lr0 + rr < m_g && col_ok;
-      dv[p] = ok ? *reinterpret_cast<const float4*>(sw.da + (r0 + rr) * F + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const uint16_t* hp = sw.h1 + (r0 + rr) * 2 * F + j;
-      gq[p] = ok ? *reinterpret_cast<const uint2*>(hp) : make_uint2(0, 0);
-      uq[p] = ok ? *reinterpret_cast<const uint2*>(hp + F) : make_uint2(0, 0);
+      const int64_t rc = r0 + (ok ? rr : 0), jc = ok ? j : c0;
+      const float4 dl = *reinterpret_cast<const float4*>(sw.da + rc * F + jc);
+      const uint16_t* hp = sw.h1 + rc * 2 * F + jc;
+      const uint2 gl = *reinterpret_cast<const uint2*>(hp), ul = *reinterpret_cast<const uint2*>(hp + F);
+      wv[p] = *(sw.probs != nullptr ? sw.probs + rc : &kUnitWeight);
+      dv[p] = ok ? dl : make_float4(0.f, 0.f, 0.f, 0.f);
+      gq[p] = ok ? gl : make_uint2(0, 0);
+      uq[p] = ok ? ul : make_uint2(0, 0);
     }
 #pragma unroll
     for (int p = 0; p < TR / 16; ++p) {
       const int rr = 16 * p + (tid >> 4);
       const bool ok = lr0 + rr < m_g && col_ok;
-      const float w = ok && sw.probs != nullptr ? sw.probs[r0 + rr] : 1.0f;
+      const float w = ok ? wv[p] : 1.0f;
       const float d[4] = {dv[p].x, dv[p].y, dv[p].z, dv[p].w};
       const float g[4] = {bf16_lo(gq[p].x), bf16_hi(gq[p].x), bf16_lo(gq[p].y), bf16_hi(gq[p].y)};
       const float u[4] = {bf16_lo(uq[p].x), bf16_hi(uq[p].x), bf16_lo(uq[p].y), bf16_hi(uq[p].y)};
@@ -244,6 +279,9 @@ __global__ __launch_bounds__(256) void quantize_fp4_colwise_kernel(const T* x, i
       if (cc == 0 && ok && sw.dprobs_part != nullptr) sw.dprobs_part[(c0 / TC) * sw.R + r0 + rr] = dp;
     }
   }
+  // every load above is issued before the stores below start (the scheduler
+  // would otherwise pair each load with its LDS store and wait in between)
+  __builtin_amdgcn_sched_barrier(0);
   // Both layouts of one tile of values (vals) at output columns c0e ..
   // c0e + TC - 1: rowwise codes from registers, then the tile through LDS for
   // the columnwise codes and scales.
