@@ -189,6 +189,40 @@ def test_fp4_cached_weights_match_uncast_path(gpu_lib, name):
     _experts(to_np(dw2), bwd["dw2"], split, "dw2 (cached weights)")
 
 
+def test_fp4_cached_weights_bit_identical_fullsize(gpu_lib):
+    """The Mixtral-shaped MXFP4 forward + backward (accumulating into fp32
+    main grads) on weights cast once into the MXFP4 weight cache equals the
+    step that casts the bf16 weights itself, bit for bit, at full size: the
+    cache's per-expert columnwise copies feed dgrad2 and dgrad1 at their
+    real offsets and extents."""
+    mx = gpu_lib
+    w = wl.WORKLOADS["mixtral_moe_fwd_bwd"]
+    print("[mlp_fp4 cached] mixtral_moe_fwd_bwd: generating inputs", flush=True)
+    c = wl.make_mlp_inputs(w, with_dy=True)
+    split = c["split_sizes"].tolist()
+    E, H, F = w.experts, w.hidden, w.ffn
+    x, w1, w2, dy = dev_bf16(c["x"]), dev_bf16(c["w1"]), dev_bf16(c["w2"]), dev_bf16(c["dy"])
+    p = dev_f32(c["probs"])
+    same = lambda a, b: torch.equal(a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32),
+                                    b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32))
+    print("[mlp_fp4 cached] reference step", flush=True)
+    y_ref, st = mx.grouped_mlp_fwd_fp4(x, p, w1, w2, split, training=True)
+    ref = mx.grouped_mlp_bwd_fp4(dy, p, st, dw1=torch.zeros((E, 2 * F, H), dtype=torch.float32, device="cuda"),
+                                 dw2=torch.zeros((E, H, F), dtype=torch.float32, device="cuda"), accumulate=True)
+    del st
+    print("[mlp_fp4 cached] cached step", flush=True)
+    cache = mx.grouped_mlp_fp4_quantize_weights(w1, w2)
+    y, st = mx.grouped_mlp_fwd_fp4_cached(x, p, cache, split, training=True)
+    got = mx.grouped_mlp_bwd_fp4_cached(dy, p, st, cache,
+                                        dw1=torch.zeros((E, 2 * F, H), dtype=torch.float32, device="cuda"),
+                                        dw2=torch.zeros((E, H, F), dtype=torch.float32, device="cuda"),
+                                        accumulate=True)
+    torch.cuda.synchronize()
+    assert same(y, y_ref), "y"
+    for a, b, what in zip(got, ref, ("dx", "dprobs", "dw1", "dw2")):
+        assert same(a, b), what
+
+
 def test_fp4_mlp_fullsize_sampled(gpu_lib):
     """The Mixtral-8x7B-shaped MoE MLP forward + backward at MXFP4 (4096
     tokens top-2 of 8: 8192 rows, H = 4096, F = 14336), in the calls the
